@@ -1,0 +1,455 @@
+/*
+ * qsa_ref.c -- plain, slow, obviously correct CPU oracle of the QSA hot path.
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT: only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg use it. It shares no code with the
+ * HIP library. Arithmetic is double precision throughout; the steps follow the
+ * order in which the pages describe the layer: compress key blocks, score them
+ * with the indexer, keep the best blocks, attend over the kept tokens.
+ *
+ * Readings taken where the pages are silent (each is restated at its step):
+ *   R1 compression of a micro-block = sum of its indexer keys, stored as bf16;
+ *   R2 score = sum_h w[t,h] * relu(q_idx[t,h] . K^[b]) with relu(x) = x>0 ? x : +0;
+ *   R3 order = score descending, ties to the lower block index;
+ *   R4 a block is a candidate once all of its tokens are at or before the query;
+ *      the tokens after the last complete block (0..bs-1 of them) are attended raw,
+ *      on top of the block budget;
+ *   R5 query head h uses key/value head h / (Hq/Hkv) (contiguous groups);
+ *   R6 one selection per query token, shared by every head;
+ *   R7 softmax scale 1/sqrt(D) unless given; output and log-sum-exp per head.
+ */
+#include "qsa_ref.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ bf16 */
+
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round x to the nearest bf16 value, ties to even. bf16 keeps 8 significant bits
+ * and the fp32 exponent range, so the rounding quantum is 2^(e-8) for
+ * x = m * 2^e with 0.5 <= |m| < 1, never finer than the subnormal step 2^-133. */
+uint16_t qsa_ref_bf16_round(double x)
+{
+    if (x == 0.0)
+        return signbit(x) ? 0x8000u : 0x0000u;
+    int e;
+    (void)frexp(x, &e);
+    int qe = (e < -125 ? -125 : e) - 8;
+    double r = ldexp(nearbyint(ldexp(x, -qe)), qe); /* default mode: ties to even */
+    if (fabs(r) >= 0x1p128)
+        return x > 0 ? 0x7f80u : 0xff80u;
+    float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------ bookkeeping */
+
+static int dims_ok(const qsa_ref_dims *d)
+{
+    return d && d->n_q_heads > 0 && d->n_kv_heads > 0 && d->head_dim > 0 &&
+           d->n_q_heads % d->n_kv_heads == 0 && d->n_idx_heads > 0 && d->idx_dim > 0 &&
+           d->block_size > 0 && d->topk_blocks > 0;
+}
+
+static int seqs_ok(int32_t batch, const int32_t *cu_q, const int32_t *cu_k)
+{
+    if (batch < 0 || !cu_k)
+        return 0;
+    if (cu_k[0] != 0 || (cu_q && cu_q[0] != 0))
+        return 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        int32_t L = cu_k[b + 1] - cu_k[b];
+        if (L < 0)
+            return 0;
+        if (cu_q) {
+            int32_t nq = cu_q[b + 1] - cu_q[b];
+            if (nq < 0 || nq > L)
+                return 0;
+        }
+    }
+    return 1;
+}
+
+/* Where query row r lives: its sequence, its absolute position t, the
+ * sequence's first key row and first compressed block. */
+typedef struct {
+    int32_t seq;
+    int64_t t;
+    int64_t key0;
+    int64_t blk0;
+} row_pos;
+
+static row_pos locate_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                          const int32_t *cu_k, int64_t r)
+{
+    row_pos p = {-1, 0, 0, 0};
+    int64_t blk0 = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t L = cu_k[b + 1] - cu_k[b];
+        if (r >= cu_q[b] && r < cu_q[b + 1]) {
+            int64_t nq = cu_q[b + 1] - cu_q[b];
+            p.seq = b;
+            p.t = L - nq + (r - cu_q[b]);
+            p.key0 = cu_k[b];
+            p.blk0 = blk0;
+            return p;
+        }
+        blk0 += L / d->block_size;
+    }
+    return p;
+}
+
+/* Reading R4: blocks whose every token is at or before t. */
+static int64_t visible_blocks(const qsa_ref_dims *d, int64_t t)
+{
+    return (t + 1) / d->block_size;
+}
+
+/* ------------------------------------------------------------- step 1 */
+
+/* Compressed key blocks. The pages say the indexer scores "compressed key
+ * blocks" of 4-token micro-blocks but do not give the operator (elzobrito.github.io,
+ * "Linear attention carries the stream; sparse attention retrieves detail").
+ * Reading R1: the block key is the sum of the block's indexer keys, taken in token
+ * order and stored as bf16. Only complete blocks are compressed; the trailing
+ * L mod bs tokens stay raw. */
+int qsa_ref_compress(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_k,
+                     const uint16_t *k_idx, uint16_t *k_blk)
+{
+    if (!dims_ok(d) || !seqs_ok(batch, NULL, cu_k) ||
+        ((!k_idx || !k_blk) && cu_k[batch] > 0))
+        return -1;
+    const int64_t Di = d->idx_dim, bs = d->block_size;
+    int64_t out_b = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t L = cu_k[b + 1] - cu_k[b];
+        for (int64_t blk = 0; blk < L / bs; ++blk, ++out_b) {
+            for (int64_t j = 0; j < Di; ++j) {
+                double s = 0.0;
+                for (int64_t i = 0; i < bs; ++i)
+                    s += bf16_value(k_idx[(cu_k[b] + blk * bs + i) * Di + j]);
+                k_blk[out_b * Di + j] = qsa_ref_bf16_round(s);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------- step 2 */
+
+static double relu(double x) { return x > 0.0 ? x : 0.0; }
+
+/* Indexer score of block `blk` for one query row. The pages describe a small
+ * indexer whose query heads share one key ("MQA indexer", aiany.app, "Key
+ * Capabilities") scoring compressed blocks. Reading R2:
+ *     s = sum_h w[h] * relu(q_idx[h] . K^[blk]). */
+static double block_score(const qsa_ref_dims *d, const uint16_t *qi_row, const float *w_row,
+                          const uint16_t *kb)
+{
+    const int64_t Hi = d->n_idx_heads, Di = d->idx_dim;
+    double s = 0.0;
+    for (int64_t h = 0; h < Hi; ++h) {
+        double dot = 0.0;
+        for (int64_t j = 0; j < Di; ++j)
+            dot += bf16_value(qi_row[h * Di + j]) * bf16_value(kb[j]);
+        s += (double)w_row[h] * relu(dot);
+    }
+    return s;
+}
+
+int qsa_ref_row_scores(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                       const int32_t *cu_k, const uint16_t *q_idx, const float *w,
+                       const uint16_t *k_blk, int64_t row, double *scores,
+                       int64_t *n_out)
+{
+    if (!dims_ok(d) || !cu_q || !seqs_ok(batch, cu_q, cu_k) || row < 0 ||
+        row >= cu_q[batch] || !n_out)
+        return -1;
+    row_pos p = locate_row(d, batch, cu_q, cu_k, row);
+    int64_t nv = visible_blocks(d, p.t);
+    const int64_t Hi = d->n_idx_heads, Di = d->idx_dim;
+    for (int64_t blk = 0; blk < nv; ++blk)
+        scores[blk] = block_score(d, q_idx + row * Hi * Di, w + row * Hi,
+                                  k_blk + (p.blk0 + blk) * Di);
+    *n_out = nv;
+    return 0;
+}
+
+/* ------------------------------------------------------------- step 3 */
+
+typedef struct {
+    double s;
+    int32_t blk;
+} scored_block;
+
+/* Reading R3: higher score first; equal scores go to the lower block index. */
+static int by_score_then_index(const void *a, const void *b)
+{
+    const scored_block *x = (const scored_block *)a, *y = (const scored_block *)b;
+    if (x->s != y->s)
+        return x->s > y->s ? -1 : 1;
+    return (x->blk > y->blk) - (x->blk < y->blk);
+}
+
+static int by_index(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Keep the budget of best blocks: "the published budget is 512 blocks,
+ * corresponding to 2,048 tokens" (elzobrito.github.io). A query with no more
+ * visible blocks than the budget keeps all of them. The kept ids are written in
+ * ascending order and the row is padded with -1. */
+static void select_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                       const int32_t *cu_k, const uint16_t *q_idx, const float *w,
+                       const uint16_t *k_blk, int64_t row, int32_t *sel_row)
+{
+    const int64_t k = d->topk_blocks, Hi = d->n_idx_heads, Di = d->idx_dim;
+    row_pos p = locate_row(d, batch, cu_q, cu_k, row);
+    int64_t nv = visible_blocks(d, p.t);
+    int64_t kept = nv < k ? nv : k;
+    if (nv <= k) {
+        for (int64_t i = 0; i < nv; ++i)
+            sel_row[i] = (int32_t)i;
+    } else {
+        scored_block *c = (scored_block *)malloc((size_t)nv * sizeof *c);
+        for (int64_t blk = 0; blk < nv; ++blk) {
+            c[blk].s = block_score(d, q_idx + row * Hi * Di, w + row * Hi,
+                                   k_blk + (p.blk0 + blk) * Di);
+            c[blk].blk = (int32_t)blk;
+        }
+        qsort(c, (size_t)nv, sizeof *c, by_score_then_index);
+        for (int64_t i = 0; i < k; ++i)
+            sel_row[i] = c[i].blk;
+        free(c);
+        qsort(sel_row, (size_t)k, sizeof *sel_row, by_index);
+    }
+    for (int64_t i = kept; i < k; ++i)
+        sel_row[i] = -1;
+}
+
+/* ------------------------------------------------------------- step 4 */
+
+/* Attention of one query row. Keys: the tokens of the kept blocks, in ascending
+ * order, then the raw tokens after the last complete block (reading R4: "the
+ * final incomplete block remains uncompressed", elzobrito.github.io). Query head h
+ * reads key/value head h / (Hq/Hkv): "24 query heads paired with only 2 key-value
+ * (KV) heads" (axbrief.com, "Shifting from Tokens to Micro-Blocks"), a 12:1 ratio
+ * (blog.compendialabs.org, "Qwen Sparse Attention -- Full Attention When It
+ * Counts"). Softmax with a max shift, then normalisation; lse = m + ln(l) of the
+ * scaled logits. */
+static void attend_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                       const int32_t *cu_k, const uint16_t *q, const uint16_t *k,
+                       const uint16_t *v, const int32_t *sel_row, int64_t row,
+                       double *out_row, double *lse_row)
+{
+    const int64_t Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
+    const int64_t bs = d->block_size, kb = d->topk_blocks;
+    const double scale = d->softmax_scale > 0 ? d->softmax_scale : 1.0 / sqrt((double)D);
+    row_pos p = locate_row(d, batch, cu_q, cu_k, row);
+    int64_t nv = visible_blocks(d, p.t);
+
+    /* the attended positions J(t), ascending */
+    int64_t n_sel = 0;
+    while (n_sel < kb && sel_row[n_sel] >= 0)
+        ++n_sel;
+    int64_t n_tail = p.t + 1 - nv * bs;
+    int64_t nj = n_sel * bs + n_tail;
+    int64_t *J = (int64_t *)malloc((size_t)nj * sizeof *J);
+    int64_t n = 0;
+    for (int64_t i = 0; i < n_sel; ++i)
+        for (int64_t j = 0; j < bs; ++j)
+            J[n++] = (int64_t)sel_row[i] * bs + j;
+    for (int64_t j = nv * bs; j <= p.t; ++j)
+        J[n++] = j;
+
+    double *z = (double *)malloc((size_t)nj * sizeof *z);
+    for (int64_t h = 0; h < Hq; ++h) {
+        int64_t g = h / (Hq / Hkv);
+        const uint16_t *qh = q + (row * Hq + h) * D;
+        double m = -INFINITY;
+        for (int64_t i = 0; i < nj; ++i) {
+            const uint16_t *kh = k + ((p.key0 + J[i]) * Hkv + g) * D;
+            double dot = 0.0;
+            for (int64_t c = 0; c < D; ++c)
+                dot += bf16_value(qh[c]) * bf16_value(kh[c]);
+            z[i] = dot * scale;
+            if (z[i] > m)
+                m = z[i];
+        }
+        double l = 0.0;
+        for (int64_t i = 0; i < nj; ++i) {
+            z[i] = exp(z[i] - m);
+            l += z[i];
+        }
+        double *o = out_row + h * D;
+        for (int64_t c = 0; c < D; ++c)
+            o[c] = 0.0;
+        for (int64_t i = 0; i < nj; ++i) {
+            const uint16_t *vh = v + ((p.key0 + J[i]) * Hkv + g) * D;
+            for (int64_t c = 0; c < D; ++c)
+                o[c] += z[i] * bf16_value(vh[c]);
+        }
+        for (int64_t c = 0; c < D; ++c)
+            o[c] /= l;
+        if (lse_row)
+            lse_row[h] = m + log(l);
+    }
+    free(z);
+    free(J);
+}
+
+/* ------------------------------------------------------- row-parallel loop */
+
+typedef struct {
+    int op; /* 0 select, 1 attend */
+    const qsa_ref_dims *d;
+    int32_t batch;
+    const int32_t *cu_q, *cu_k;
+    const uint16_t *q, *k, *v, *q_idx, *k_blk;
+    const float *w;
+    int32_t *sel_w;
+    const int32_t *sel_r;
+    double *out, *lse;
+    const int64_t *rows;
+    int64_t lo, hi;
+} row_job;
+
+static void *run_rows(void *arg)
+{
+    row_job *j = (row_job *)arg;
+    const int64_t kb = j->d->topk_blocks, Hq = j->d->n_q_heads, D = j->d->head_dim;
+    for (int64_t i = j->lo; i < j->hi; ++i) {
+        int64_t r = j->rows ? j->rows[i] : i;
+        if (j->op == 0)
+            select_row(j->d, j->batch, j->cu_q, j->cu_k, j->q_idx, j->w, j->k_blk, r,
+                       j->sel_w + r * kb);
+        else
+            attend_row(j->d, j->batch, j->cu_q, j->cu_k, j->q, j->k, j->v,
+                       j->sel_r + r * kb, r, j->out + r * Hq * D,
+                       j->lse ? j->lse + r * Hq : NULL);
+    }
+    return NULL;
+}
+
+static void for_rows(row_job proto, int64_t n_rows, int32_t n_threads)
+{
+    if (n_threads < 1)
+        n_threads = 1;
+    if (n_threads > 256)
+        n_threads = 256;
+    if (n_rows < n_threads)
+        n_threads = n_rows > 0 ? (int32_t)n_rows : 1;
+    pthread_t tid[256];
+    row_job jobs[256];
+    for (int32_t i = 0; i < n_threads; ++i) {
+        jobs[i] = proto;
+        jobs[i].lo = n_rows * i / n_threads;
+        jobs[i].hi = n_rows * (i + 1) / n_threads;
+    }
+    for (int32_t i = 1; i < n_threads; ++i)
+        pthread_create(&tid[i], NULL, run_rows, &jobs[i]);
+    run_rows(&jobs[0]);
+    for (int32_t i = 1; i < n_threads; ++i)
+        pthread_join(tid[i], NULL);
+}
+
+static int rows_ok(const int32_t *cu_q, int32_t batch, const int64_t *rows, int64_t n_rows)
+{
+    if (!rows)
+        return 1;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= cu_q[batch])
+            return 0;
+    return 1;
+}
+
+int qsa_ref_select(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                   const int32_t *cu_k, const uint16_t *q_idx, const float *w,
+                   const uint16_t *k_blk, int32_t *sel, const int64_t *rows,
+                   int64_t n_rows, int32_t n_threads)
+{
+    if (!dims_ok(d) || !cu_q || !seqs_ok(batch, cu_q, cu_k) || !sel ||
+        !rows_ok(cu_q, batch, rows, n_rows))
+        return -1;
+    row_job j;
+    memset(&j, 0, sizeof j);
+    j.op = 0;
+    j.d = d;
+    j.batch = batch;
+    j.cu_q = cu_q;
+    j.cu_k = cu_k;
+    j.q_idx = q_idx;
+    j.w = w;
+    j.k_blk = k_blk;
+    j.sel_w = sel;
+    j.rows = rows;
+    for_rows(j, rows ? n_rows : cu_q[batch], n_threads);
+    return 0;
+}
+
+int qsa_ref_attend(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                   const int32_t *cu_k, const uint16_t *q, const uint16_t *k,
+                   const uint16_t *v, const int32_t *sel, double *out, double *lse,
+                   const int64_t *rows, int64_t n_rows, int32_t n_threads)
+{
+    if (!dims_ok(d) || !cu_q || !seqs_ok(batch, cu_q, cu_k) || !sel || !out ||
+        !rows_ok(cu_q, batch, rows, n_rows))
+        return -1;
+    row_job j;
+    memset(&j, 0, sizeof j);
+    j.op = 1;
+    j.d = d;
+    j.batch = batch;
+    j.cu_q = cu_q;
+    j.cu_k = cu_k;
+    j.q = q;
+    j.k = k;
+    j.v = v;
+    j.sel_r = sel;
+    j.out = out;
+    j.lse = lse;
+    j.rows = rows;
+    for_rows(j, rows ? n_rows : cu_q[batch], n_threads);
+    return 0;
+}
+
+int qsa_ref_forward(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                    const int32_t *cu_k, const uint16_t *q, const uint16_t *k,
+                    const uint16_t *v, const uint16_t *q_idx, const float *w,
+                    const uint16_t *k_idx, uint16_t *k_blk, int32_t *sel,
+                    double *out, double *lse, const int64_t *rows, int64_t n_rows,
+                    int32_t n_threads)
+{
+    if (!dims_ok(d) || !cu_q || !seqs_ok(batch, cu_q, cu_k) || !k_blk || !out ||
+        !rows_ok(cu_q, batch, rows, n_rows))
+        return -1;
+    if (qsa_ref_compress(d, batch, cu_k, k_idx, k_blk) != 0)
+        return -1;
+    int32_t *s = sel;
+    if (!s) {
+        s = (int32_t *)malloc((size_t)cu_q[batch] * (size_t)d->topk_blocks * sizeof *s + 1);
+        if (!s)
+            return -1;
+    }
+    int rc = qsa_ref_select(d, batch, cu_q, cu_k, q_idx, w, k_blk, s, rows, n_rows, n_threads);
+    if (rc == 0)
+        rc = qsa_ref_attend(d, batch, cu_q, cu_k, q, k, v, s, out, lse, rows, n_rows,
+                            n_threads);
+    if (!sel)
+        free(s);
+    return rc;
+}

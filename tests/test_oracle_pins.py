@@ -1,0 +1,350 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test names the mistake it would catch. Sources of truth: hand-worked examples
+(tests/golden), library routines (scipy softmax/logsumexp, torch's bf16 conversion,
+integer arithmetic), closed forms and brute force.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_inputs as gen
+from qsa_inputs import bf16_to_f32, f32_to_bf16_exact
+from tests.refmath import as_f64, attended_mask, causal_mask, masked_gqa_attention
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf(x):
+    return f32_to_bf16_exact(np.asarray(x, dtype=np.float32))
+
+
+def _dims(d):
+    return oracle.Dims(**d)
+
+
+# ----------------------------------------------------------------- bf16 rounding
+
+@pytest.mark.parametrize("x,bits", [
+    (1.0, 0x3F80), (-2.5, 0xC020), (3.0, 0x4040),
+    (1 + 2 ** -8, 0x3F80),                 # halfway, ties to even (down)
+    (1 + 3 * 2 ** -8, 0x3F82),             # halfway, ties to even (up)
+    (1 + 2 ** -8 + 2 ** -20, 0x3F81),      # above halfway rounds up
+    ((2 - 2 ** -7) * 2.0 ** 127, 0x7F7F),  # largest finite bf16
+    (2.0 ** 128 - 2.0 ** 119, 0x7F80),     # halfway to 2^128: ties to even -> inf
+    (2.0 ** -133, 0x0001),                 # smallest subnormal
+    (2.0 ** -134, 0x0000),                 # halfway to zero: even
+    (3 * 2.0 ** -134, 0x0002),             # halfway between 1 and 2 quanta: even
+    (-0.0, 0x8000),
+])
+def test_bf16_round_table(x, bits):
+    """Catches truncation instead of round-to-nearest-even and exponent slips."""
+    assert oracle.bf16_round(x) == bits
+
+
+def test_bf16_round_matches_torch_on_fp32_values():
+    """Library pin: for values exact in fp32, torch's fp32->bf16 is RNE."""
+    rng = np.random.default_rng(7)
+    f = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))).astype(np.float32)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_round(float(x)) for x in f], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------- compress
+
+def test_compress_integer_sums_and_ragged_packing():
+    """Integer data: each block key must equal the exact integer sum of its 4 rows
+    (catches wrong token range, dropped token, packing across sequences); the
+    trailing L mod 4 tokens form no block; a 3-token sequence has none."""
+    lens = [13, 3, 8, 6]
+    p = gen.make_problem(lens, seed=11)
+    got = oracle.compress(oracle.Dims(), p.cu_k, p.k_idx)
+    ints = bf16_to_f32(p.k_idx).astype(np.int64)
+    rows = []
+    for b, L in enumerate(lens):
+        base = int(p.cu_k[b])
+        for blk in range(L // 4):
+            rows.append(ints[base + 4 * blk: base + 4 * blk + 4].sum(axis=0))
+    assert got.shape == (sum(L // 4 for L in lens), 64)
+    assert np.array_equal(bf16_to_f32(got), np.array(rows, dtype=np.float32))
+
+
+def test_compress_float_data_matches_library_rounding():
+    """Normal data: exact double sum, rounded once to bf16 (torch RNE on the exact
+    fp32 value). Catches fp32 accumulation, truncation, reordering that rounds."""
+    lens = [64, 37]
+    p = gen.make_problem(lens, seed=12, float_indexer=True)
+    got = oracle.compress(oracle.Dims(), p.cu_k, p.k_idx)
+    x = as_f64(p.k_idx)
+    sums = []
+    for b, L in enumerate(lens):
+        base = int(p.cu_k[b])
+        for blk in range(L // 4):
+            sums.append(x[base + 4 * blk: base + 4 * blk + 4].sum(axis=0))
+    sums = np.array(sums)
+    f32 = sums.astype(np.float32)
+    exact = f32.astype(np.float64) == sums
+    assert exact.mean() > 0.99
+    ref = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got[exact], ref[exact])
+
+
+# --------------------------------------------------------------- worked examples
+
+def _single_query_problem(k_idx_rows, t, q_idx_row, w_row, dims, kv_zero=True):
+    """One decode row at position t over a sequence of length t+1. V rows are
+    one-hot (V[j] = e_j) and K = 0, so the output is the mean of e_j over J."""
+    L = t + 1
+    Hq, Hkv, D = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    cu_k = np.array([0, L], dtype=np.int32)
+    cu_q = np.array([0, 1], dtype=np.int32)
+    k_idx = bf(np.array(k_idx_rows[:L], dtype=np.float32))
+    q_idx = bf(np.array(q_idx_row, dtype=np.float32).reshape(1, dims.n_idx_heads, dims.idx_dim))
+    w = np.array(w_row, dtype=np.float32).reshape(1, dims.n_idx_heads)
+    q = bf(np.ones((1, Hq, D), dtype=np.float32))
+    k = bf(np.zeros((L, Hkv, D), dtype=np.float32))
+    v = np.zeros((L, Hkv, D), dtype=np.float32)
+    for j in range(L):
+        v[j, :, j] = 1.0
+    return cu_q, cu_k, q, k, bf(v), q_idx, w, k_idx
+
+
+def test_golden_e1_selection_tie_visibility_tail():
+    g = json.load(open(os.path.join(GOLDEN, "e1_micro_blocks.json")))
+    dims = _dims(g["dims"])
+    kb = oracle.compress(dims, np.array([0, 9], dtype=np.int32), bf(np.array(g["k_idx"], np.float32)))
+    assert bf16_to_f32(kb).tolist() == g["k_blk"]
+    for case in g["cases"]:
+        cu_q, cu_k, q, k, v, q_idx, w, k_idx = _single_query_problem(
+            g["k_idx"], case["t"], case["q_idx"], case["w"], dims)
+        k_blk, sel, out, lse = oracle.forward(dims, cu_q, cu_k, q, k, v, q_idx, w, k_idx)
+        s = oracle.row_scores(dims, cu_q, cu_k, q_idx, w, k_blk, 0)
+        assert s.tolist() == case["scores"], case["what"]
+        assert sel[0].tolist() == case["sel"], case["what"]
+        J = case["J"]
+        expect = np.zeros(dims.head_dim)
+        expect[J] = 1.0 / len(J)
+        assert np.allclose(out[0, 0], expect, atol=1e-15), case["what"]
+        assert abs(lse[0, 0] - math.log(len(J))) < 1e-12
+
+
+def test_golden_e2_two_heads_weights_relu():
+    g = json.load(open(os.path.join(GOLDEN, "e2_indexer_scores.json")))
+    dims = _dims(g["dims"])
+    cu_q, cu_k, q, k, v, q_idx, w, k_idx = _single_query_problem(
+        g["k_idx"], g["t"], g["q_idx"], g["w"], dims)
+    k_blk, sel, out, lse = oracle.forward(dims, cu_q, cu_k, q, k, v, q_idx, w, k_idx)
+    assert bf16_to_f32(k_blk).tolist() == g["k_blk"]
+    assert oracle.row_scores(dims, cu_q, cu_k, q_idx, w, k_blk, 0).tolist() == g["scores"]
+    assert sel[0].tolist() == g["sel"]
+    expect = np.zeros(dims.head_dim)
+    expect[g["J"]] = 1.0 / len(g["J"])
+    for h in range(dims.n_q_heads):
+        assert np.allclose(out[0, h], expect, atol=1e-15)
+
+
+# ------------------------------------------------------------------- selection
+
+def _brute_force_topk(scores, k):
+    """Among all k-subsets of maximal total score, the lexicographically smallest
+    sorted index tuple. An optimisation-form definition, independent of sorting."""
+    n = len(scores)
+    if n <= k:
+        return list(range(n))
+    best, best_sum = None, None
+    for comb in itertools.combinations(range(n), k):
+        s = sum(scores[i] for i in comb)
+        if best_sum is None or s > best_sum or (s == best_sum and comb < best):
+            best, best_sum = comb, s
+    return list(best)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_matches_exhaustive_subsets(seed):
+    """Tiny rows with heavy ties (indexer values in {-1,0,1}, 1 head x 2 dims):
+    selection == brute-force best subset; output ascending and -1 padded."""
+    dims = oracle.Dims(n_q_heads=2, n_kv_heads=1, head_dim=8, n_idx_heads=1, idx_dim=2,
+                       topk_blocks=[1, 2, 3, 4, 5, 6][seed])
+    rng = np.random.default_rng(seed)
+    L = 4 * 14 + int(rng.integers(0, 4))
+    cu_k = np.array([0, L], dtype=np.int32)
+    cu_q = np.array([0, L], dtype=np.int32)
+    k_idx = bf(rng.integers(-1, 2, size=(L, 2)).astype(np.float32))
+    q_idx = bf(rng.integers(-1, 2, size=(L, 1, 2)).astype(np.float32))
+    w = rng.integers(1, 3, size=(L, 1)).astype(np.float32)
+    k_blk = oracle.compress(dims, cu_k, k_idx)
+    sel = oracle.select(dims, cu_q, cu_k, q_idx, w, k_blk)
+    ties = 0
+    for t in range(L):
+        s = oracle.row_scores(dims, cu_q, cu_k, q_idx, w, k_blk, t)
+        ties += len(s) - len(set(s.tolist()))
+        expect = _brute_force_topk(s.tolist(), dims.topk_blocks)
+        got = sel[t].tolist()
+        assert got[:len(expect)] == expect
+        assert all(x == -1 for x in got[len(expect):])
+    assert ties > 0
+
+
+def test_select_all_ties_keeps_lowest_blocks():
+    """q_idx = 0: every score is 0, so the first min(nvis, k) blocks are kept."""
+    dims = oracle.Dims(topk_blocks=5)
+    p = gen.make_problem([50], seed=3)
+    q_idx = np.zeros_like(p.q_idx)
+    k_blk = oracle.compress(dims, p.cu_k, p.k_idx)
+    sel = oracle.select(dims, p.cu_q, p.cu_k, q_idx, p.w, k_blk)
+    for t in range(50):
+        nv = (t + 1) // 4
+        n = min(nv, 5)
+        assert sel[t].tolist() == list(range(n)) + [-1] * (5 - n)
+
+
+def test_select_scale_invariance():
+    """Scaling w by 2 or the indexer keys by 2 (exact in bf16) keeps the selection
+    (relu is positively homogeneous). Catches a bias or non-homogeneous step."""
+    dims = oracle.Dims(topk_blocks=7)
+    p = gen.make_problem([203], seed=5)
+    kb = oracle.compress(dims, p.cu_k, p.k_idx)
+    s0 = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb)
+    s1 = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w * 2, kb)
+    k2 = bf(bf16_to_f32(p.k_idx) * 2)
+    s2 = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, oracle.compress(dims, p.cu_k, k2))
+    assert np.array_equal(s0, s1) and np.array_equal(s0, s2)
+
+
+def test_needles_selected_decode_32k():
+    """Config 1: every needle block must be among the 512 kept blocks."""
+    p = gen.config_problem(1)
+    dims = oracle.Dims()
+    kb = oracle.compress(dims, p.cu_k, p.k_idx)
+    sel = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb)
+    assert set(p.needles[0]) <= set(sel[0].tolist())
+    assert (sel[0] >= 0).all() and np.all(np.diff(sel[0]) > 0)
+
+
+# ------------------------------------------------------------------- attention
+
+def _prefill_dense_check(p, dims, rows_t):
+    k_blk, sel, out, lse = oracle.forward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, p.q_idx,
+                                          p.w, p.k_idx, rows=rows_t)
+    L = int(p.cu_k[1])
+    scale = 1 / math.sqrt(dims.head_dim)
+    ref_o, ref_l = masked_gqa_attention(as_f64(p.q[rows_t]), as_f64(p.k), as_f64(p.v),
+                                        causal_mask(rows_t, L), scale)
+    return out[rows_t], lse[rows_t], ref_o, ref_l, sel
+
+
+def test_dense_equality_when_budget_covers_everything():
+    """All blocks fit the budget (L <= 4*512+3): QSA == causal GQA attention
+    (library softmax on dense matrices, heads grouped 12:1)."""
+    dims = oracle.Dims()
+    p = gen.make_problem([300], seed=21)
+    rows = list(range(300))
+    o, l, ro, rl, sel = _prefill_dense_check(p, dims, rows)
+    assert np.max(np.abs(o - ro)) < 1e-12 and np.max(np.abs(l - rl)) < 1e-12
+
+
+def test_dense_equality_config0_sampled_rows():
+    dims = oracle.Dims()
+    p = gen.config_problem(0)
+    rows = [0, 1, 2, 3, 4, 511, 512, 1022, 1023]
+    o, l, ro, rl, _ = _prefill_dense_check(p, dims, rows)
+    assert np.max(np.abs(o - ro)) < 1e-12 and np.max(np.abs(l - rl)) < 1e-12
+
+
+def test_sparse_rows_match_masked_attention():
+    """Budget 3 blocks on a 71-token prefill: rows past 15 tokens are sparse. The
+    output must equal masked attention over the oracle's kept blocks + raw tail."""
+    dims = oracle.Dims(topk_blocks=3)
+    p = gen.make_problem([71], seed=22)
+    k_blk, sel, out, lse = oracle.forward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, p.q_idx,
+                                          p.w, p.k_idx)
+    ts = list(range(71))
+    mask = attended_mask(ts, sel, 71, 4)
+    ro, rl = masked_gqa_attention(as_f64(p.q), as_f64(p.k), as_f64(p.v), mask,
+                                  1 / math.sqrt(128))
+    assert np.max(np.abs(out - ro)) < 1e-12 and np.max(np.abs(lse - rl)) < 1e-12
+    assert mask.sum(axis=1).max() <= 3 * 4 + 3
+    assert (mask.sum(axis=1)[15:] >= 12).all()
+
+
+def test_first_token_attends_only_itself():
+    """t = 0: the output is V[0] of the head's group exactly; lse = q.k0 * scale."""
+    p = gen.make_problem([5], seed=23)
+    _, _, out, lse = oracle.forward(oracle.Dims(), p.cu_q, p.cu_k, p.q, p.k, p.v, p.q_idx,
+                                    p.w, p.k_idx)
+    v = as_f64(p.v)
+    for h in range(24):
+        assert np.array_equal(out[0, h], v[0, h // 12])
+        z = float(as_f64(p.q[0, h]) @ as_f64(p.k[0, h // 12])) / math.sqrt(128)
+        assert abs(lse[0, h] - z) < 1e-12
+
+
+def test_two_keys_logit_gap_ln3():
+    """Two keys whose logits differ by ln 3: weights 3/4 and 1/4 (scale = ln 3,
+    q.k0 = 1, q.k1 = 0). Catches a wrong exponent base or a missing scale."""
+    dims = oracle.Dims(n_q_heads=1, n_kv_heads=1, head_dim=4, softmax_scale=math.log(3))
+    cu = np.array([0, 2], dtype=np.int32)
+    q = bf(np.array([[[1, 0, 0, 0]]], np.float32))
+    k = bf(np.array([[[1, 0, 0, 0]], [[0, 1, 0, 0]]], np.float32))
+    v = bf(np.array([[[4, 0, 8, 1]], [[0, 4, 8, -1]]], np.float32))
+    q_idx = np.zeros((1, 4, 64), np.uint16)
+    w = np.ones((1, 4), np.float32)
+    k_idx = np.zeros((2, 64), np.uint16)
+    _, _, out, lse = oracle.forward(dims, np.array([0, 1], np.int32), cu, q, k, v, q_idx, w,
+                                    k_idx)
+    assert np.allclose(out[0, 0], [3, 1, 8, 0.5], atol=1e-14)
+    assert abs(lse[0, 0] - (math.log(3) + math.log(4 / 3))) < 1e-14
+
+
+def test_attention_shift_invariances():
+    """K + u (fixed u per kv head) leaves O unchanged; V + c shifts O by c. Values
+    are quarter-integers so that every shifted input is exact in bf16."""
+    dims = oracle.Dims(topk_blocks=4)
+    p = gen.make_problem([61], seed=24)
+    rng = np.random.default_rng(0)
+    k = bf(np.clip(np.round(bf16_to_f32(p.k) * 4) / 4, -8, 8))
+    v = bf(np.clip(np.round(bf16_to_f32(p.v) * 4) / 4, -8, 8))
+    u = np.round(rng.standard_normal((1, 2, 128)) * 4).clip(-8, 8).astype(np.float32) / 4
+    k2 = bf(bf16_to_f32(k) + u)
+    v2 = bf(bf16_to_f32(v) + np.float32(3.0))
+    run = lambda kk, vv: oracle.forward(dims, p.cu_q, p.cu_k, p.q, kk, vv, p.q_idx, p.w,
+                                        p.k_idx)[2]
+    o0 = run(k, v)
+    assert np.max(np.abs(run(k2, v) - o0)) < 1e-9
+    assert np.max(np.abs(run(k, v2) - (o0 + 3.0))) < 1e-12
+
+
+def test_decode_equals_last_prefill_row():
+    """A decode call at length L is the last row of the prefill of length L."""
+    dims = oracle.Dims(topk_blocks=6)
+    for L in (1, 3, 4, 29, 40, 77):
+        p = gen.make_problem([L], seed=30 + L)
+        _, sel_p, out_p, lse_p = oracle.forward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v,
+                                                p.q_idx, p.w, p.k_idx)
+        cu_q = np.array([0, 1], np.int32)
+        _, sel_d, out_d, lse_d = oracle.forward(dims, cu_q, p.cu_k, p.q[-1:], p.k, p.v,
+                                                p.q_idx[-1:], p.w[-1:], p.k_idx)
+        assert np.array_equal(sel_d[0], sel_p[-1])
+        assert np.array_equal(out_d[0], out_p[-1]) and np.array_equal(lse_d[0], lse_p[-1])
+
+
+def test_ragged_batch_rows_independent():
+    """Each sequence of a ragged batch gives the same rows as when run alone."""
+    dims = oracle.Dims(topk_blocks=3)
+    lens = [23, 3, 18]
+    p = gen.make_problem(lens, seed=40)
+    _, sel, out, _ = oracle.forward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, p.q_idx, p.w,
+                                    p.k_idx)
+    for b, L in enumerate(lens):
+        k0, k1 = int(p.cu_k[b]), int(p.cu_k[b + 1])
+        cu = np.array([0, L], np.int32)
+        _, sel1, out1, _ = oracle.forward(dims, cu, cu, p.q[k0:k1], p.k[k0:k1], p.v[k0:k1],
+                                          p.q_idx[k0:k1], p.w[k0:k1], p.k_idx[k0:k1])
+        assert np.array_equal(sel[k0:k1], sel1) and np.array_equal(out[k0:k1], out1)
