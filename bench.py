@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the QSA hot path on one MI355X.
+
+A step is one pass of the whole layer (compress of the block the new token completes,
+indexer scoring, top-512 block selection, sparse GQA attention) over one batch of the
+decode workload: 16 sequences at 262,144 tokens of context, one query token each.
+Inputs are seeded and synthetic and sit in HBM before timing starts. Consecutive steps
+rotate over R distinct query sets and R copies of the compressed-key cache, so that a
+step never finds the previous step's 168 MB working set in the 256 MB Infinity Cache.
+
+Prints one JSON line: throughput (query-tokens/s), a roofline entry for the dominant
+kernel (algorithmic bytes / its mean HIP-event duration), the CPU oracle timed on a
+bounded sample, and a secondary prefill measurement (ragged 65,535/40,001/8,190/3).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA query-tokens/s: decode @256K ctx + prefill @64K; % of HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16, 256 CU x 2.4 GHz x 4096 flop/clk
+
+HQ, HKV, D, HI, DI, BS, TOPK = 24, 2, 128, 4, 64, 4, 512
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=4, help="distinct query sets / cache copies")
+    ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--trace-steps", type=int, default=8)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- decode workload
+
+def decode_algorithmic_bytes(batch, ctx):
+    """Bytes the decode step must move (no intermediate spills):
+    score: every visible compressed key (128 B per block) + q_idx and w;
+    attend: 512 blocks x 4 tokens x (K + V, 2 heads x 128 x bf16) + Q (bf16) + O (fp32)."""
+    nblk = ctx // BS
+    score = batch * (nblk * DI * 2 + HI * DI * 2 + HI * 4)
+    attend = batch * (TOPK * BS * HKV * D * 2 * 2 + HQ * D * 2 + HQ * D * 4)
+    return {"score": score, "attend": attend, "total": score + attend}
+
+
+def run_decode(args, torch, qsa, gen):
+    cfg = gen.CONFIGS[3]
+    lens, batch = cfg["lens"], len(cfg["lens"])
+    ctx = lens[0]
+    t0 = time.time()
+    p = gen.config_problem(3)
+    log(f"generated decode inputs in {time.time() - t0:.1f}s")
+    dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    seqs = qsa.Seqs(p.cu_q, p.cu_k)
+    k, v, k_idx = dev16(p.k), dev16(p.v), dev16(p.k_idx)
+    R = max(1, args.rotate)
+    sets = []
+    k_blk0 = torch.empty((seqs.n_blocks, DI), dtype=torch.int16, device="cuda")
+    qsa.compress(seqs, k_idx, k_blk0)
+    for r in range(R):
+        if r == 0:
+            q, q_idx, w = p.q, p.q_idx, p.w
+        else:
+            s2 = 50_000 + r
+            q = gen.normal_bf16(s2, gen.TID_Q, batch * HQ * D).reshape(batch, HQ, D)
+            q_idx = gen.uniform_int_bf16(s2, gen.TID_QIDX, batch * HI * DI, -3, 3).reshape(
+                batch, HI, DI)
+            w = gen.weights(s2, gen.TID_W, batch * HI).reshape(batch, HI)
+        kb = k_blk0 if r == 0 else k_blk0.clone()
+        sets.append(dict(q=dev16(q), q_idx=dev16(q_idx), w=torch.from_numpy(w).cuda(), k_blk=kb,
+                         sel=torch.empty((batch, TOPK), dtype=torch.int32, device="cuda"),
+                         out=torch.empty((batch, HQ, D), dtype=torch.float32, device="cuda"),
+                         lse=torch.empty((batch, HQ), dtype=torch.float32, device="cuda")))
+    ws = qsa.alloc_workspace(seqs, TOPK)
+    torch.cuda.synchronize()
+    log(f"decode inputs resident: K/V {2 * k.numel() * 2 / 2**30:.2f} GiB, "
+        f"{R} cache copies of {k_blk0.numel() * 2 / 2**20:.0f} MiB")
+
+    def step(i):
+        s = sets[i % R]
+        qsa.forward(seqs, s["q"], k, v, s["q_idx"], s["w"], k_idx, s["k_blk"], s["sel"],
+                    s["out"], s["lse"], ws, TOPK)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # correctness guard on the timed configuration: needles of set 0 selected
+    sel0 = sets[0]["sel"].cpu().numpy()
+    for b, needles in p.needles.items():
+        if not set(needles) <= set(sel0[b].tolist()):
+            raise RuntimeError(f"needle blocks of sequence {b} not selected")
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = ev0.elapsed_time(ev1)
+    log(f"decode: {args.steps} steps, wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+
+    # instrumented pass: per-kernel durations with HIP events on the library's stream
+    with qsa.trace(4096) as tr:
+        for i in range(args.trace_steps):
+            step(i)
+    torch.cuda.synchronize()
+    return dict(p=p, batch=batch, ctx=ctx, wall_s=wall, gpu_ms=gpu_ms,
+                kernels=tr.mean_ms(), kernel_total=tr.total_ms(), seqs=seqs, sets=sets)
+
+
+# ---------------------------------------------------------------- prefill workload
+
+def run_prefill(args, torch, qsa, gen):
+    p = gen.config_problem(4)
+    dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    seqs = qsa.Seqs(p.cu_q, p.cu_k)
+    q, k, v, q_idx, k_idx = (dev16(x) for x in (p.q, p.k, p.v, p.q_idx, p.k_idx))
+    w = torch.from_numpy(p.w).cuda()
+    k_blk = torch.empty((seqs.n_blocks, DI), dtype=torch.int16, device="cuda")
+    sel = torch.empty((seqs.n_q, TOPK), dtype=torch.int32, device="cuda")
+    out = torch.empty((seqs.n_q, HQ, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((seqs.n_q, HQ), dtype=torch.float32, device="cuda")
+    ws = qsa.alloc_workspace(seqs, TOPK)
+
+    def step():
+        qsa.forward(seqs, q, k, v, q_idx, w, k_idx, k_blk, sel, out, lse, ws, TOPK)
+
+    step()
+    torch.cuda.synchronize()
+    n = max(1, args.prefill_steps)
+    t0 = time.perf_counter()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    with qsa.trace(64) as tr:
+        step()
+    torch.cuda.synchronize()
+    # algorithmic work: attended (query, key) pairs and scored (query, block) pairs
+    pairs, scored = 0, 0
+    for b in range(len(p.cu_k) - 1):
+        L = int(p.cu_k[b + 1] - p.cu_k[b])
+        for t in range(L):
+            nv = (t + 1) // BS
+            pairs += min(nv, TOPK) * BS + (t + 1 - BS * nv)
+            scored += nv if nv > TOPK else 0
+    att_flop = pairs * HQ * D * 4
+    score_flop = scored * HI * DI * 2
+    km = tr.mean_ms()
+    att_ms = km.get("attend", float("nan")) + km.get("combine", 0.0)
+    return {
+        "workload": "ragged prefill 65,535/40,001/8,190/3 tokens, budget 512 blocks",
+        "ms_per_step": round(ms, 3),
+        "query_tokens_per_s": round(seqs.n_q / (ms / 1e3), 1),
+        "kernel_ms": {k2: round(v2, 4) for k2, v2 in km.items()},
+        "attention_pairs": pairs,
+        "attention_tflops": round(att_flop / (att_ms / 1e3) / 1e12, 2),
+        "attention_mfma_frac": round(att_flop / (att_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "attention_gather_gbs": round(pairs * HKV * D * 2 * 2 / (att_ms / 1e3) / 1e9, 1),
+        "score_tflops": round(score_flop / (km.get("score", float("nan")) / 1e3) / 1e12, 2),
+    }
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def run_cpu_baseline(args, d, oracle):
+    """The oracle timed on host cores: the decode step's select + attend for the 16
+    rows against the prebuilt compressed cache, repeated for a bounded time."""
+    p = d["p"]
+    dims = oracle.Dims()
+    k_blk = oracle.compress(dims, p.cu_k, p.k_idx)
+    threads = min(os.cpu_count() or 1, p.n_q)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        sel = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, k_blk, threads=threads)
+        oracle.attend(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or reps >= 50:
+            break
+    return {"value": round(reps * p.n_q / el, 3), "unit": "query-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} decode step(s) of 16 rows at 262,144 context (score + select + "
+                      f"attend over the prebuilt compressed cache), {el:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs "
+                                   "are not part of this build", "n_gpus": args.gpus}),
+              flush=True)
+        sys.exit(2)
+    import torch
+    import long_context_block_qsa_amd as qsa
+    import qsa_inputs as gen
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    qsa.lib()
+
+    d = run_decode(args, torch, qsa, gen)
+    step_ms = d["wall_s"] * 1e3 / args.steps
+    value = d["batch"] / (step_ms / 1e3)
+    ab = decode_algorithmic_bytes(d["batch"], d["ctx"])
+
+    # dominant kernel (largest total traced time) and its algorithmic bytes per launch
+    kern = d["kernels"]
+    dom = max(d["kernel_total"], key=d["kernel_total"].get)
+    per_launch = {"score": ab["score"],
+                  "attend": ab["attend"] - d["batch"] * HQ * D * 4,
+                  "select": d["batch"] * ((d["ctx"] // BS) * 4 + TOPK * 4),
+                  "combine": d["batch"] * HQ * (D + 1) * 4,
+                  "compress": d["batch"] * (BS * DI * 2 + DI * 2),
+                  "prep": d["batch"] * 40}
+    achieved = per_launch[dom] / (kern[dom] / 1e3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "algorithmic_bytes_per_launch": per_launch[dom],
+                "mean_ms": round(kern[dom], 5)}
+    step_gbs = ab["total"] / (step_ms / 1e3) / 1e9
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode: 16 sequences x 262,144 tokens of context, 1 query "
+                               "token each, budget 512 blocks of 4 tokens",
+                   "batch": d["batch"], "context": d["ctx"], "budget_blocks": TOPK,
+                   "rotation_sets": args.rotate},
+        "roofline": roofline,
+        "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_gbs": round(step_gbs, 1),
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "kernel_mean_ms": {k2: round(v2, 5) for k2, v2 in kern.items()},
+    }
+    if not args.no_prefill:
+        log("prefill workload")
+        line["prefill"] = run_prefill(args, torch, qsa, gen)
+    if not args.no_cpu_baseline:
+        import oracle
+        log("CPU oracle baseline")
+        line["cpu_baseline"] = run_cpu_baseline(args, d, oracle)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,353 @@
+// qsa_api.hip -- the C ABI declared in include/qsa.h: host-side validation,
+// workspace layout and launch orchestration. Nothing is enqueued before every
+// argument has been checked; no device memory is allocated here.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <vector>
+
+#pragma GCC visibility push(default)
+#include "qsa.h"
+#pragma GCC visibility pop
+#include "qsa_device.h"
+#include "qsa_launch.h"
+
+// ------------------------------------------------------------ kernel trace
+namespace qsa {
+namespace {
+struct Trace {
+    bool open = false;
+    bool pending = false;
+    bool failed = false;
+    int cap = 0, n = 0;
+    std::vector<hipEvent_t> ev;   // 2 per kernel
+    std::vector<int> kind;
+};
+thread_local Trace g_trace;
+}  // namespace
+
+void trace_before(int kind, hipStream_t st) {
+    Trace &t = g_trace;
+    t.pending = false;
+    if (!t.open || t.n >= t.cap) return;
+    if (hipEventRecord(t.ev[2 * t.n], st) != hipSuccess) { t.failed = true; return; }
+    t.kind[t.n] = kind;
+    t.pending = true;
+}
+
+hipError_t trace_after(hipStream_t st, hipError_t launch_status) {
+    Trace &t = g_trace;
+    if (t.pending) {
+        t.pending = false;
+        if (hipEventRecord(t.ev[2 * t.n + 1], st) != hipSuccess) t.failed = true;
+        else ++t.n;
+    }
+    return launch_status;
+}
+}  // namespace qsa
+
+namespace {
+
+using qsa::SeqInfo;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxGridY = 65535;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Host mirrors of the device bookkeeping formulas.
+int64_t h_slots_before(int64_t t) {
+    int64_t m = t / 4, r = t % 4;
+    return 2 * m * (m - 1) + m * (r + 1);
+}
+int64_t h_first_scored_pos(int64_t L, int64_t nq, int64_t topk) {
+    return std::max(L - nq, 4 * topk + 3);
+}
+
+struct Plan {
+    int batch = 0;
+    int topk = 0;
+    float scale = 0.f;
+    int64_t tq = 0, tk = 0;
+    int64_t n_tiles = 0;        // score tiles (4 query rows each)
+    int64_t n_slots = 0;        // fp32 score slots
+    int64_t max_score_blocks = 0;
+    int64_t max_cmp_full = 0;   // most complete blocks in a sequence
+    int64_t max_cmp_incr = 0;   // most blocks holding a query token
+    int64_t score_chunk = 0;    // blocks per score workgroup
+    int nsplit = 1;             // attention key splits per row
+    size_t off_tab = 0, off_sel = 0, off_union = 0, ws_bytes = 0;
+};
+
+qsa_status check_dims(const qsa_dims *d) {
+    if (!d) return QSA_ERR_NULL;
+    if (d->n_q_heads != qsa::HQ || d->n_kv_heads != qsa::HKV || d->head_dim != qsa::HD ||
+        d->n_idx_heads != qsa::HI || d->idx_dim != qsa::DI || d->block_size != qsa::BS)
+        return QSA_ERR_UNSUPPORTED;
+    if (d->topk_blocks < 1 || d->topk_blocks > qsa::KMAX) return QSA_ERR_SHAPE;
+    if (!isfinite(d->softmax_scale)) return QSA_ERR_SHAPE;
+    return QSA_OK;
+}
+
+// Validates the sequence description and fills the plan. need_q: cu_q is used.
+qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p) {
+    qsa_status st = check_dims(d);
+    if (st != QSA_OK) return st;
+    if (!s) return QSA_ERR_NULL;
+    if (s->batch < 0) return QSA_ERR_SHAPE;
+    if (s->batch > kMaxGridY) return QSA_ERR_UNSUPPORTED;
+    if (!s->cu_k_host || (need_q && !s->cu_q_host)) return QSA_ERR_NULL;
+    if (s->batch > 0 && (!s->cu_k_dev || (need_q && !s->cu_q_dev))) return QSA_ERR_NULL;
+    const int32_t *ck = s->cu_k_host, *cq = need_q ? s->cu_q_host : nullptr;
+    if (ck[0] != 0 || (cq && cq[0] != 0)) return QSA_ERR_SHAPE;
+    p->batch = s->batch;
+    p->topk = d->topk_blocks;
+    p->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)qsa::HD);
+    for (int b = 0; b < s->batch; ++b) {
+        const int64_t L = (int64_t)ck[b + 1] - ck[b];
+        if (L < 0) return QSA_ERR_SHAPE;
+        int64_t nq = 0;
+        if (cq) {
+            nq = (int64_t)cq[b + 1] - cq[b];
+            if (nq < 0 || nq > L) return QSA_ERR_SHAPE;
+        }
+        p->max_cmp_full = std::max(p->max_cmp_full, L / qsa::BS);
+        if (nq > 0)
+            p->max_cmp_incr = std::max(p->max_cmp_incr, L / qsa::BS - (L - nq) / qsa::BS);
+        const int64_t ts = h_first_scored_pos(L, nq, p->topk);
+        if (cq && ts < L) {
+            p->n_tiles += (L - ts + 3) / 4;
+            p->n_slots += h_slots_before(L) - h_slots_before(ts);
+            p->max_score_blocks = std::max(p->max_score_blocks, L / qsa::BS);
+        }
+    }
+    p->tk = ck[s->batch];
+    p->tq = cq ? cq[s->batch] : 0;
+    if (p->n_tiles > INT32_MAX) return QSA_ERR_UNSUPPORTED;
+
+    // score grid: enough workgroups to fill the chip when few tiles exist
+    if (p->n_tiles > 0) {
+        int64_t gy = std::max<int64_t>(1, (2048 + p->n_tiles - 1) / p->n_tiles);
+        gy = std::min<int64_t>(gy, std::max<int64_t>(1, p->max_score_blocks / 256));
+        int64_t chunk = (p->max_score_blocks + gy - 1) / gy;
+        chunk = (chunk + 63) / 64 * 64;
+        p->score_chunk = chunk;
+        if ((p->max_score_blocks + chunk - 1) / chunk > kMaxGridY) return QSA_ERR_UNSUPPORTED;
+    }
+    // attention splits: aim at ~1024 waves when rows are few
+    if (p->tq > 0) {
+        int64_t ns = (1024 + 2 * p->tq - 1) / (2 * p->tq);
+        p->nsplit = (int)std::min<int64_t>(64, std::max<int64_t>(1, ns));
+    }
+    // workspace: [seq table][selection][scores | attention partials]
+    const size_t tab_b = align_up((size_t)std::max(p->batch, 1) * sizeof(SeqInfo));
+    const size_t sel_b = align_up((size_t)p->tq * (size_t)p->topk * sizeof(int32_t));
+    const size_t score_b = align_up((size_t)p->n_slots * sizeof(uint32_t));
+    const size_t part_b = p->nsplit > 1
+        ? align_up((size_t)p->tq * p->nsplit * qsa::HQ * (qsa::HD + 4) * sizeof(float)) : 0;
+    p->off_tab = 0;
+    p->off_sel = tab_b;
+    p->off_union = tab_b + sel_b;
+    p->ws_bytes = p->off_union + std::max(score_b, part_b);
+    return QSA_OK;
+}
+
+qsa_status check_ws(const Plan &p, void *ws, size_t ws_bytes) {
+    if (!ws) return QSA_ERR_NULL;
+    if (((uintptr_t)ws % kAlign) != 0) return QSA_ERR_WORKSPACE;
+    if (ws_bytes < p.ws_bytes) return QSA_ERR_WORKSPACE;
+    return QSA_OK;
+}
+
+qsa_status device_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_DEVICE; }
+
+#define QSA_TRY(expr)                                  \
+    do {                                               \
+        qsa_status _s = device_status(expr);           \
+        if (_s != QSA_OK) return _s;                   \
+    } while (0)
+
+template <typename T>
+T *ws_at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, const float *w,
+                      const qsa_bf16 *k_blk, int32_t *sel, void *ws, hipStream_t st) {
+    SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
+    uint32_t *keys = ws_at<uint32_t>(ws, p.off_union);
+    QSA_TRY(qsa::launch_score(tab, p.batch, p.topk, q_idx, w, k_blk, keys, p.n_tiles,
+                              p.max_score_blocks, p.score_chunk, st));
+    QSA_TRY(qsa::launch_select(tab, p.batch, p.topk, keys, sel, p.tq, st));
+    (void)s;
+    return QSA_OK;
+}
+
+qsa_status run_attend(const Plan &p, const qsa_bf16 *q, const qsa_bf16 *k, const qsa_bf16 *v,
+                      const int32_t *sel, float *out, float *lse, void *ws, hipStream_t st) {
+    SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
+    float *part = ws_at<float>(ws, p.off_union);
+    QSA_TRY(qsa::launch_attend(tab, p.batch, p.topk, p.scale, q, k, v, sel, out, lse, part,
+                               p.nsplit, p.tq, st));
+    return QSA_OK;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char *qsa_status_string(qsa_status s) {
+    switch (s) {
+    case QSA_OK: return "QSA_OK";
+    case QSA_ERR_NULL: return "QSA_ERR_NULL: a required pointer is NULL";
+    case QSA_ERR_SHAPE: return "QSA_ERR_SHAPE: invalid sequence offsets, budget or alignment";
+    case QSA_ERR_UNSUPPORTED: return "QSA_ERR_UNSUPPORTED: dims or sizes outside the supported set";
+    case QSA_ERR_WORKSPACE: return "QSA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case QSA_ERR_DEVICE: return "QSA_ERR_DEVICE: a kernel launch failed";
+    }
+    return "unknown qsa_status";
+}
+
+qsa_status qsa_workspace_size(const qsa_dims *dims, const qsa_seqs *seqs, size_t *bytes) {
+    if (!bytes) return QSA_ERR_NULL;
+    Plan p;
+    qsa_status st = make_plan(dims, seqs, true, &p);
+    if (st != QSA_OK) return st;
+    *bytes = p.ws_bytes;
+    return QSA_OK;
+}
+
+qsa_status qsa_compress(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *k_idx,
+                        qsa_bf16 *k_blk, void *stream) {
+    Plan p;
+    qsa_status st = make_plan(dims, seqs, false, &p);
+    if (st != QSA_OK) return st;
+    if (p.max_cmp_full == 0) return QSA_OK;
+    if (!k_idx || !k_blk) return QSA_ERR_NULL;
+    if (!aligned16(k_idx) || !aligned16(k_blk)) return QSA_ERR_SHAPE;
+    QSA_TRY(qsa::launch_compress(nullptr, seqs->cu_k_dev, p.batch, p.max_cmp_full, k_idx, k_blk,
+                                 0, (hipStream_t)stream));
+    return QSA_OK;
+}
+
+qsa_status qsa_select(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q_idx,
+                      const float *w, const qsa_bf16 *k_blk, int32_t *sel, void *ws,
+                      size_t ws_bytes, void *stream) {
+    Plan p;
+    qsa_status st = make_plan(dims, seqs, true, &p);
+    if (st != QSA_OK) return st;
+    if (p.tq == 0) return QSA_OK;
+    if (!sel) return QSA_ERR_NULL;
+    if (p.n_tiles > 0 && (!q_idx || !w || !k_blk)) return QSA_ERR_NULL;
+    if ((q_idx && !aligned16(q_idx)) || (k_blk && !aligned16(k_blk)) ||
+        (w && !aligned16(w)) || !aligned16(sel))
+        return QSA_ERR_SHAPE;
+    if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
+                             ws_at<SeqInfo>(ws, p.off_tab), hs));
+    return run_select(p, seqs, q_idx, w, k_blk, sel, ws, hs);
+}
+
+qsa_status qsa_attend(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                      const qsa_bf16 *k, const qsa_bf16 *v, const int32_t *sel, float *out,
+                      float *lse, void *ws, size_t ws_bytes, void *stream) {
+    Plan p;
+    qsa_status st = make_plan(dims, seqs, true, &p);
+    if (st != QSA_OK) return st;
+    if (p.tq == 0) return QSA_OK;
+    if (!q || !k || !v || !sel || !out) return QSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(sel))
+        return QSA_ERR_SHAPE;
+    if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
+                             ws_at<SeqInfo>(ws, p.off_tab), hs));
+    return run_attend(p, q, k, v, sel, out, lse, ws, hs);
+}
+
+qsa_status qsa_forward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                       const qsa_bf16 *k, const qsa_bf16 *v, const qsa_bf16 *q_idx,
+                       const float *w, const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel,
+                       float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    Plan p;
+    qsa_status st = make_plan(dims, seqs, true, &p);
+    if (st != QSA_OK) return st;
+    if (p.tq == 0) return QSA_OK;
+    if (!q || !k || !v || !out) return QSA_ERR_NULL;
+    if (p.n_tiles > 0 && (!q_idx || !w)) return QSA_ERR_NULL;
+    if ((p.n_tiles > 0 || (k_idx && p.max_cmp_incr > 0)) && !k_blk) return QSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (q_idx && !aligned16(q_idx)) || (w && !aligned16(w)) || (k_idx && !aligned16(k_idx)) ||
+        (k_blk && !aligned16(k_blk)) || (sel && !aligned16(sel)))
+        return QSA_ERR_SHAPE;
+    if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    int32_t *sel_use = sel ? sel : ws_at<int32_t>(ws, p.off_sel);
+    if (k_idx && p.max_cmp_incr > 0)
+        QSA_TRY(qsa::launch_compress(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.max_cmp_incr,
+                                     k_idx, k_blk, 1, hs));
+    QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
+                             ws_at<SeqInfo>(ws, p.off_tab), hs));
+    if ((st = run_select(p, seqs, q_idx, w, k_blk, sel_use, ws, hs)) != QSA_OK) return st;
+    return run_attend(p, q, k, v, sel_use, out, lse, ws, hs);
+}
+
+qsa_status qsa_trace_begin(int32_t max_kernels) {
+    qsa::Trace &t = qsa::g_trace;
+    if (t.open || max_kernels < 1 || max_kernels > (1 << 20)) return QSA_ERR_SHAPE;
+    t.ev.assign(2 * (size_t)max_kernels, nullptr);
+    t.kind.assign((size_t)max_kernels, -1);
+    for (auto &e : t.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (auto &x : t.ev)
+                if (x) hipEventDestroy(x);
+            t.ev.clear();
+            return QSA_ERR_DEVICE;
+        }
+    }
+    t.cap = max_kernels;
+    t.n = 0;
+    t.failed = false;
+    t.pending = false;
+    t.open = true;
+    return QSA_OK;
+}
+
+int32_t qsa_trace_end(int32_t max_out, int32_t *kind_out, float *ms_out) {
+    qsa::Trace &t = qsa::g_trace;
+    if (!t.open) return -1;
+    int32_t n = t.n;
+    bool ok = !t.failed;
+    for (int i = 0; i < n && ok; ++i) {
+        float ms = 0.f;
+        if (hipEventSynchronize(t.ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess) {
+            ok = false;
+            break;
+        }
+        if (i < max_out) {
+            if (kind_out) kind_out[i] = t.kind[i];
+            if (ms_out) ms_out[i] = ms;
+        }
+    }
+    for (auto &e : t.ev) hipEventDestroy(e);
+    t.ev.clear();
+    t.kind.clear();
+    t.open = false;
+    t.n = 0;
+    return ok ? n : -1;
+}
+
+const char *qsa_kernel_name(int32_t kind) {
+    static const char *names[] = {"prep", "compress", "score", "select", "attend", "combine"};
+    return (kind >= 0 && kind < 6) ? names[kind] : "unknown";
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,31 @@
+// qsa_launch.h -- host-side launchers of the QSA kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct SeqInfo;
+
+// Optional per-kernel event trace (thread-local; see qsa_trace_begin).
+void trace_before(int kind, hipStream_t st);
+hipError_t trace_after(hipStream_t st, hipError_t launch_status);
+
+hipError_t launch_prep(const int32_t *cu_q, const int32_t *cu_k, int batch, int topk,
+                       SeqInfo *tab, hipStream_t st);
+hipError_t launch_compress(const int32_t *cu_q, const int32_t *cu_k, int batch,
+                           int64_t max_blocks, const uint16_t *k_idx, uint16_t *k_blk,
+                           int incremental, hipStream_t st);
+hipError_t launch_score(const SeqInfo *tab, int batch, int topk, const uint16_t *q_idx,
+                        const float *w, const uint16_t *k_blk, uint32_t *keys,
+                        int64_t n_tiles, int64_t max_blocks, int64_t chunk_blocks,
+                        hipStream_t st);
+hipError_t launch_select(const SeqInfo *tab, int batch, int topk, const uint32_t *keys,
+                         int32_t *sel, int64_t n_rows, hipStream_t st);
+hipError_t launch_attend(const SeqInfo *tab, int batch, int topk, float scale,
+                         const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const int32_t *sel, float *out, float *lse, float *part, int nsplit,
+                         int64_t n_rows, hipStream_t st);
+
+}  // namespace qsa

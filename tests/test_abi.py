@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads, exports what include/qsa.h declares,
+and every validation error returns before anything touches a device."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import long_context_block_qsa_amd as qsa
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def _seqs(cu_q, cu_k, batch=None, dev=True):
+    cq = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int32))
+    ck = np.ascontiguousarray(np.asarray(cu_k, dtype=np.int32))
+    s = qsa.qsa_seqs(len(ck) - 1 if batch is None else batch, cq.ctypes.data, ck.ctypes.data,
+                     FAKE if dev else None, FAKE if dev else None)
+    s._keep = (cq, ck)
+    return s
+
+
+def _ws(dims, seqs):
+    n = ctypes.c_size_t(0)
+    st = qsa.lib().qsa_workspace_size(ctypes.byref(dims), ctypes.byref(seqs), ctypes.byref(n))
+    return st, n.value
+
+
+def test_exports_every_declared_symbol():
+    names = qsa.header_functions()
+    assert set(names) == {"qsa_abi_version", "qsa_status_string", "qsa_workspace_size",
+                          "qsa_compress", "qsa_select", "qsa_attend", "qsa_forward",
+                          "qsa_trace_begin", "qsa_trace_end", "qsa_kernel_name"}
+    out = subprocess.run(["nm", "-D", "--defined-only", qsa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+    for n in names:
+        assert hasattr(qsa.lib(), n)
+
+
+def test_version_and_status_strings():
+    assert qsa.lib().qsa_abi_version() == 1
+    for s in range(6):
+        assert qsa.status_string(s).startswith(("QSA_OK", "QSA_ERR"))
+    assert "unknown" in qsa.status_string(99)
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("n_q_heads", 32, qsa.QSA_ERR_UNSUPPORTED), ("n_kv_heads", 4, qsa.QSA_ERR_UNSUPPORTED),
+    ("head_dim", 64, qsa.QSA_ERR_UNSUPPORTED), ("n_idx_heads", 8, qsa.QSA_ERR_UNSUPPORTED),
+    ("idx_dim", 128, qsa.QSA_ERR_UNSUPPORTED), ("block_size", 8, qsa.QSA_ERR_UNSUPPORTED),
+    ("topk_blocks", 0, qsa.QSA_ERR_SHAPE), ("topk_blocks", 513, qsa.QSA_ERR_SHAPE),
+    ("softmax_scale", float("nan"), qsa.QSA_ERR_SHAPE),
+])
+def test_dims_rejected(field, value, expect):
+    d = qsa.make_dims()
+    setattr(d, field, value)
+    s = _seqs([0, 1], [0, 10])
+    assert _ws(d, s)[0] == expect
+
+
+@pytest.mark.parametrize("cu_q,cu_k,expect", [
+    ([1, 2], [0, 10], qsa.QSA_ERR_SHAPE),            # cu_q not starting at 0
+    ([0, 1], [2, 10], qsa.QSA_ERR_SHAPE),            # cu_k not starting at 0
+    ([0, 11], [0, 10], qsa.QSA_ERR_SHAPE),           # more queries than tokens
+    ([0, 1, 0], [0, 5, 9], qsa.QSA_ERR_SHAPE),       # decreasing cu_q
+    ([0, 1, 2], [0, 5, 4], qsa.QSA_ERR_SHAPE),       # decreasing cu_k
+])
+def test_bad_offsets_rejected(cu_q, cu_k, expect):
+    assert _ws(qsa.make_dims(), _seqs(cu_q, cu_k))[0] == expect
+
+
+def test_null_pointers_rejected():
+    d = qsa.make_dims()
+    n = ctypes.c_size_t(0)
+    L = qsa.lib()
+    assert L.qsa_workspace_size(None, ctypes.byref(_seqs([0, 1], [0, 4])), ctypes.byref(n)) == 1
+    assert L.qsa_workspace_size(ctypes.byref(d), None, ctypes.byref(n)) == 1
+    assert L.qsa_workspace_size(ctypes.byref(d), ctypes.byref(_seqs([0, 1], [0, 4])), None) == 1
+    no_dev = _seqs([0, 1], [0, 4], dev=False)
+    assert L.qsa_workspace_size(ctypes.byref(d), ctypes.byref(no_dev), ctypes.byref(n)) == 1
+    s = _seqs([0, 1], [0, 40])
+    st, nbytes = _ws(d, s)
+    assert st == 0
+    f = ctypes.c_void_p(FAKE)
+    # forward: missing q / out / workspace
+    assert L.qsa_forward(ctypes.byref(d), ctypes.byref(s), None, f, f, f, f, f, f, f, f, f, f,
+                         nbytes, None) == qsa.QSA_ERR_NULL
+    assert L.qsa_forward(ctypes.byref(d), ctypes.byref(s), f, f, f, f, f, f, f, f, None, f, f,
+                         nbytes, None) == qsa.QSA_ERR_NULL
+    assert L.qsa_forward(ctypes.byref(d), ctypes.byref(s), f, f, f, f, f, f, f, f, f, f, None,
+                         nbytes, None) == qsa.QSA_ERR_NULL
+    assert L.qsa_attend(ctypes.byref(d), ctypes.byref(s), f, f, f, None, f, f, f, nbytes,
+                        None) == qsa.QSA_ERR_NULL
+    assert L.qsa_select(ctypes.byref(d), ctypes.byref(s), f, f, f, None, f, nbytes,
+                        None) == qsa.QSA_ERR_NULL
+    assert L.qsa_compress(ctypes.byref(d), ctypes.byref(s), None, f, None) == qsa.QSA_ERR_NULL
+
+
+def test_workspace_checks():
+    d = qsa.make_dims()
+    s = _seqs([0, 40000], [0, 40000])
+    L = qsa.lib()
+    st, nbytes = _ws(d, s)
+    assert st == 0 and nbytes > 0
+    f = ctypes.c_void_p(FAKE)
+    assert L.qsa_select(ctypes.byref(d), ctypes.byref(s), f, f, f, f, f, nbytes - 1,
+                        None) == qsa.QSA_ERR_WORKSPACE
+    assert L.qsa_select(ctypes.byref(d), ctypes.byref(s), f, f, f, f,
+                        ctypes.c_void_p(FAKE + 16), nbytes, None) == qsa.QSA_ERR_WORKSPACE
+    assert L.qsa_attend(ctypes.byref(d), ctypes.byref(s), f, f, f, f, f, f, None, nbytes,
+                        None) == qsa.QSA_ERR_NULL
+
+
+def test_misaligned_tensor_rejected():
+    d = qsa.make_dims()
+    s = _seqs([0, 1], [0, 40])
+    st, nbytes = _ws(d, s)
+    f, g = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 2)
+    assert qsa.lib().qsa_attend(ctypes.byref(d), ctypes.byref(s), g, f, f, f, f, f, f, nbytes,
+                                None) == qsa.QSA_ERR_SHAPE
+
+
+def test_empty_work_is_a_no_op():
+    """batch 0, or sequences with no query rows: success, nothing enqueued."""
+    d = qsa.make_dims()
+    L = qsa.lib()
+    for cu_q, cu_k in (([0], [0]), ([0, 0, 0], [0, 0, 7])):
+        s = _seqs(cu_q, cu_k)
+        st, nbytes = _ws(d, s)
+        assert st == 0
+        assert L.qsa_forward(ctypes.byref(d), ctypes.byref(s), None, None, None, None, None,
+                             None, None, None, None, None, None, 0, None) == 0
+
+
+def test_workspace_size_grows_with_scored_rows():
+    """Rows within the budget need no score slots; longer prefills need more."""
+    d = qsa.make_dims(topk=512)
+    small = _ws(d, _seqs([0, 2051], [0, 2051]))[1]
+    large = _ws(d, _seqs([0, 4096], [0, 4096]))[1]
+    assert large > small
+    # scores of a 4096-token prefill: positions 2051..4095, F(4096) - F(2051) slots
+    F = lambda t: 2 * (t // 4) * (t // 4 - 1) + (t // 4) * (t % 4 + 1)
+    assert large >= 4 * (F(4096) - F(2051))
+
+
+def test_trace_end_without_begin_and_names():
+    L = qsa.lib()
+    assert L.qsa_trace_end(0, None, None) == -1
+    assert qsa.lib().qsa_kernel_name(2) == b"score"
+    assert qsa.lib().qsa_kernel_name(42) == b"unknown"
+    assert L.qsa_trace_begin(0) == qsa.QSA_ERR_SHAPE

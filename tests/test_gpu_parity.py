@@ -1,0 +1,228 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by element.
+
+Bars: compressed keys and selected block ids bit-identical (indexer inputs are small
+integers, so every score is exact in fp32); attention outputs within max-abs 2e-3 and
+mean-abs 2e-4 of the oracle, lse within 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_inputs as gen
+from tests.gpu_helpers import LSE_ABS, MAX_ABS, MEAN_ABS, DeviceProblem, errs
+
+pytestmark = pytest.mark.gpu
+
+
+def _banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _check_rows(name, dp, rows, topk, threads=None, gpu=None):
+    p = dp.p
+    dims = oracle.Dims(topk_blocks=topk)
+    k_blk_r, sel_r, out_r, lse_r = oracle.forward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, p.q_idx,
+                                                  p.w, p.k_idx, rows=rows, threads=threads)
+    k_blk, sel, out, lse = gpu if gpu is not None else dp.forward()
+    assert np.array_equal(k_blk, k_blk_r), f"{name}: compressed keys differ"
+    rows = np.arange(p.n_q) if rows is None else np.asarray(rows)
+    bad = [r for r in rows if not np.array_equal(sel[r], sel_r[r])]
+    assert not bad, f"{name}: selection differs on rows {bad[:10]}"
+    mx, mean = errs(out[rows], out_r[rows])
+    lmx, _ = errs(lse[rows], lse_r[rows])
+    print(f"[{name}] rows={len(rows)} max_abs={mx:.3e} mean_abs={mean:.3e} lse={lmx:.3e}",
+          flush=True)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and lmx <= LSE_ABS
+    return sel, out
+
+
+# ----------------------------------------------------------------- small shapes
+
+SMALL = [
+    ([1], 1), ([2], 1), ([3], 2), ([4], 1), ([5], 1), ([7, 8], 1), ([13], 2), ([64], 3),
+    ([64, 3, 0, 29], 8), ([203], 8), ([130, 77], 16), ([1000, 600], 64),
+]
+
+
+@pytest.mark.parametrize("lens,topk", SMALL)
+def test_small_prefill(lens, topk):
+    _banner(f"small prefill lens={lens} topk={topk}")
+    p = gen.make_problem(lens, seed=100 + sum(lens) + topk)
+    _check_rows(f"prefill{lens}/k{topk}", DeviceProblem(p, topk), None, topk)
+
+
+@pytest.mark.parametrize("lens,topk", [([33], 2), ([64, 61, 4, 1], 3), ([4099], 512),
+                                       ([2000, 1999, 6], 100)])
+def test_small_decode(lens, topk):
+    _banner(f"small decode lens={lens} topk={topk}")
+    p = gen.make_problem(lens, q_lens=[1] * len(lens), seed=200 + sum(lens))
+    _check_rows(f"decode{lens}/k{topk}", DeviceProblem(p, topk), None, topk)
+
+
+def test_multi_query_rows_per_sequence():
+    """2-4 query tokens per sequence (the last tokens), ragged lengths."""
+    _banner("multi-query decode")
+    lens, q_lens = [3000, 2500, 777, 16], [4, 2, 3, 1]
+    p = gen.make_problem(lens, q_lens=q_lens, seed=301)
+    _check_rows("multi-query", DeviceProblem(p, 64), None, 64)
+
+
+# ----------------------------------------------------------------- configurations
+
+def test_config0_prefill_1k_dense():
+    _banner("config 0: prefill 1x1024")
+    p = gen.config_problem(0)
+    _check_rows("cfg0", DeviceProblem(p), None, 512)
+
+
+def test_config1_decode_32k_needles():
+    _banner("config 1: decode 1x32768")
+    p = gen.config_problem(1)
+    sel, _ = _check_rows("cfg1", DeviceProblem(p), None, 512)
+    assert set(p.needles[0]) <= set(sel[0].tolist())
+
+
+def test_config2_prefill_16k_sampled():
+    _banner("config 2: prefill 1x16384")
+    p = gen.config_problem(2)
+    rows = sorted(set([0, 1, 2, 3, 4, 2047, 2048, 2049, 2050, 2051, 2052, 2053, 2054, 2055]
+                      + list(range(16384 - 40, 16384))
+                      + np.random.default_rng(2).integers(0, 16384, 200).tolist()))
+    _check_rows("cfg2", DeviceProblem(p), rows, 512)
+
+
+def test_config3_decode_256k_x16_full():
+    _banner("config 3: decode 16x262144")
+    p = gen.config_problem(3)
+    sel, _ = _check_rows("cfg3", DeviceProblem(p), None, 512)
+    for b, needles in p.needles.items():
+        assert set(needles) <= set(sel[b].tolist()), f"needles of sequence {b} missing"
+
+
+def test_config4_ragged_prefill_sampled():
+    _banner("config 4: ragged prefill 65535/40001/8190/3")
+    p = gen.config_problem(4)
+    cu = p.cu_q
+    rng = np.random.default_rng(4)
+    rows = set()
+    for b in range(4):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        rows.update(range(lo, min(hi, lo + 6)))
+        rows.update(range(max(lo, hi - 6), hi))
+        for t in (2049, 2050, 2051, 2052):
+            if lo + t < hi:
+                rows.add(lo + t)
+        if hi - lo > 10:
+            rows.update(rng.integers(lo, hi, 60).tolist())
+    _check_rows("cfg4", DeviceProblem(p), sorted(rows), 512)
+
+
+# ----------------------------------------------------------------- edge cases / properties
+
+def test_all_ties_keep_lowest_blocks():
+    _banner("all-tie scores")
+    p = gen.make_problem([5000, 2100], q_lens=[3, 2100], seed=7)
+    p.q_idx[:] = 0
+    dp = DeviceProblem(p, 512)
+    _, sel, _, _ = dp.forward()
+    for r in range(p.n_q):
+        seq = 0 if r < 3 else 1
+        t = (5000 - 3 + r) if seq == 0 else (r - 3)
+        n = min((t + 1) // 4, 512)
+        assert sel[r].tolist() == list(range(n)) + [-1] * (512 - n)
+
+
+def test_float_indexer_tie_tolerant():
+    """Non-integer indexer data: fp32 GPU scores may round differently from the
+    double oracle, so each kept block must score within 1e-5 relative of the
+    oracle's budget threshold; attention is compared on the GPU's own selection."""
+    _banner("float indexer")
+    p = gen.make_problem([3000, 2500], q_lens=[5, 40], seed=8, float_indexer=True)
+    topk = 128
+    dp = DeviceProblem(p, topk)
+    _, sel, out, lse = dp.forward()
+    dims = oracle.Dims(topk_blocks=topk)
+    kb = oracle.compress(dims, p.cu_k, p.k_idx)
+    for r in range(p.n_q):
+        s = oracle.row_scores(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb, r)
+        kth = np.sort(s)[::-1][topk - 1]
+        kept = sel[r][sel[r] >= 0]
+        assert len(kept) == topk and np.all(np.diff(kept) > 0)
+        assert np.all(s[kept] >= kth - 1e-5 * max(1.0, abs(kth)))
+    out_r, lse_r = oracle.attend(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel)
+    mx, mean = errs(out, out_r)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+    assert errs(lse, lse_r)[0] <= LSE_ABS
+
+
+def test_deterministic_bitwise():
+    _banner("determinism")
+    p = gen.make_problem([9000, 4000], q_lens=[1, 1], seed=9)
+    dp = DeviceProblem(p, 512)
+    a = dp.forward()
+    b = dp.forward()
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_decode_equals_last_prefill_row():
+    _banner("decode == last prefill row")
+    L = 2600
+    p = gen.make_problem([L], seed=10)
+    _, sel_p, out_p, lse_p = DeviceProblem(p, 256).forward()
+    pd = gen.make_problem([L], seed=10)
+    pd.cu_q = np.array([0, 1], np.int32)
+    pd.q, pd.q_idx, pd.w = p.q[-1:].copy(), p.q_idx[-1:].copy(), p.w[-1:].copy()
+    _, sel_d, out_d, lse_d = DeviceProblem(pd, 256).forward()
+    assert np.array_equal(sel_d[0], sel_p[-1])
+    assert errs(out_d[0], out_p[-1])[0] < 1e-5 and errs(lse_d[0], lse_p[-1])[0] < 1e-5
+
+
+def test_incremental_compress_completes_cache():
+    """forward() with k_idx recompresses only the blocks holding query tokens; with a
+    cache built by compress() for the rest, the result equals a full compress."""
+    _banner("incremental compress")
+    p = gen.make_problem([4096, 1203, 8], q_lens=[1, 7, 8], seed=11)
+    dp = DeviceProblem(p, 512)
+    full = dp.compress()
+    dp.k_blk.zero_()
+    # rebuild the prefix cache only: blocks before each sequence's first query token
+    dims = oracle.Dims()
+    ref = oracle.compress(dims, p.cu_k, p.k_idx)
+    assert np.array_equal(full, ref)
+    pref = ref.copy()
+    nb0 = 0
+    for b in range(3):
+        L = int(p.cu_k[b + 1] - p.cu_k[b])
+        nq = int(p.cu_q[b + 1] - p.cu_q[b])
+        first_new = (L - nq) // 4
+        pref[nb0 + first_new: nb0 + L // 4] = 0x7FC0  # garbage where forward must write
+        nb0 += L // 4
+    dp.k_blk.copy_(torch.from_numpy(pref.view(np.int16)).cuda())
+    k_blk, _, _, _ = dp.forward(with_k_idx=True)
+    assert np.array_equal(k_blk, ref)
+
+
+def test_select_and_attend_entry_points():
+    """qsa_select then qsa_attend equal qsa_forward; attend accepts a caller selection."""
+    _banner("separate entry points")
+    p = gen.make_problem([3333, 100], q_lens=[2, 100], seed=12)
+    dp = DeviceProblem(p, 32)
+    kb, sel_f, out_f, lse_f = dp.forward()
+    dp.sel.fill_(-9)
+    sel_s = dp.select()
+    assert np.array_equal(sel_s, sel_f)
+    out_a, lse_a = dp.attend()
+    assert np.array_equal(out_a, out_f) and np.array_equal(lse_a, lse_f)
+    # a hand-made selection: every other visible block, capped at 32, -1 padded
+    custom = np.full_like(sel_f, -1)
+    dims = oracle.Dims(topk_blocks=32)
+    for r in range(p.n_q):
+        t = (3333 - 2 + r) if r < 2 else r - 2
+        ids = list(range(0, (t + 1) // 4, 2))[:32]
+        custom[r, :len(ids)] = ids
+    out_c, lse_c = dp.attend(custom)
+    out_r, lse_r = oracle.attend(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, custom)
+    mx, mean = errs(out_c, out_r)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
