@@ -78,9 +78,11 @@ struct Plan {
     int64_t max_score_blocks = 0;
     int64_t max_cmp_full = 0;   // most complete blocks in a sequence
     int64_t max_cmp_incr = 0;   // most blocks holding a query token
-    int64_t score_chunk = 0;    // blocks per score workgroup
+    int64_t score_chunk = 0;    // blocks per score workgroup (whole-row path)
+    int local_ch = 0;           // > 0: decode path, blocks per chunk
+    int max_chunks = 0;         // chunks of the longest scored row (decode path)
     int nsplit = 1;             // attention key splits per row
-    size_t off_tab = 0, off_sel = 0, off_union = 0, ws_bytes = 0;
+    size_t off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, ws_bytes = 0;
 };
 
 qsa_status check_dims(const qsa_dims *d) {
@@ -129,8 +131,20 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     p->tq = cq ? cq[s->batch] : 0;
     if (p->n_tiles > INT32_MAX) return QSA_ERR_UNSUPPORTED;
 
+    // decode path: few score tiles over long rows -> chunked scoring with local
+    // candidates; the chunk shrinks until the longest row has 16 full chunks
+    constexpr int kKP = 32;
+    if (p->n_tiles > 0 && p->n_tiles <= 64) {
+        int ch = 1024;
+        while (ch > 64 && (p->max_score_blocks / ch) * kKP < p->topk) ch /= 2;
+        if ((p->max_score_blocks / ch) * kKP >= p->topk) {
+            p->local_ch = ch;
+            p->max_chunks = (int)((p->max_score_blocks + ch - 1) / ch);
+            if (p->max_chunks > kMaxGridY) return QSA_ERR_UNSUPPORTED;
+        }
+    }
     // score grid: enough workgroups to fill the chip when few tiles exist
-    if (p->n_tiles > 0) {
+    if (p->n_tiles > 0 && p->local_ch == 0) {
         int64_t gy = std::max<int64_t>(1, (2048 + p->n_tiles - 1) / p->n_tiles);
         gy = std::min<int64_t>(gy, std::max<int64_t>(1, p->max_score_blocks / 256));
         int64_t chunk = (p->max_score_blocks + gy - 1) / gy;
@@ -147,12 +161,15 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     const size_t tab_b = align_up((size_t)std::max(p->batch, 1) * sizeof(SeqInfo));
     const size_t sel_b = align_up((size_t)p->tq * (size_t)p->topk * sizeof(int32_t));
     const size_t score_b = align_up((size_t)p->n_slots * sizeof(uint32_t));
+    const size_t cand_b = p->local_ch > 0
+        ? align_up((size_t)p->tq * p->max_chunks * kKP * 2 * sizeof(uint32_t)) : 0;
     const size_t part_b = p->nsplit > 1
         ? align_up((size_t)p->tq * p->nsplit * qsa::HQ * (qsa::HD + 4) * sizeof(float)) : 0;
     p->off_tab = 0;
     p->off_sel = tab_b;
-    p->off_union = tab_b + sel_b;
-    p->ws_bytes = p->off_union + std::max(score_b, part_b);
+    p->off_union = tab_b + sel_b;     // scores (+ candidates) while selecting, then partials
+    p->off_cand = p->off_union + score_b;
+    p->ws_bytes = p->off_union + std::max(score_b + cand_b, part_b);
     return QSA_OK;
 }
 
@@ -178,9 +195,19 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
                       const qsa_bf16 *k_blk, int32_t *sel, void *ws, hipStream_t st) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
     uint32_t *keys = ws_at<uint32_t>(ws, p.off_union);
-    QSA_TRY(qsa::launch_score(tab, p.batch, p.topk, q_idx, w, k_blk, keys, p.n_tiles,
-                              p.max_score_blocks, p.score_chunk, st));
-    QSA_TRY(qsa::launch_select(tab, p.batch, p.topk, keys, sel, p.tq, st));
+    uint32_t *cand_key = nullptr;
+    int32_t *cand_idx = nullptr;
+    if (p.local_ch > 0) {
+        cand_key = ws_at<uint32_t>(ws, p.off_cand);
+        cand_idx = reinterpret_cast<int32_t *>(cand_key + (size_t)p.tq * p.max_chunks * 32);
+        QSA_TRY(qsa::launch_score_local(tab, p.batch, p.topk, q_idx, w, k_blk, keys, cand_key,
+                                        cand_idx, p.n_tiles, p.local_ch, p.max_chunks, st));
+    } else {
+        QSA_TRY(qsa::launch_score(tab, p.batch, p.topk, q_idx, w, k_blk, keys, p.n_tiles,
+                                  p.max_score_blocks, p.score_chunk, st));
+    }
+    QSA_TRY(qsa::launch_select(tab, p.batch, p.topk, keys, cand_key, cand_idx, p.local_ch,
+                               p.max_chunks, sel, p.tq, p.max_score_blocks, st));
     (void)s;
     return QSA_OK;
 }
@@ -231,7 +258,7 @@ qsa_status qsa_compress(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf
     if (!k_idx || !k_blk) return QSA_ERR_NULL;
     if (!aligned16(k_idx) || !aligned16(k_blk)) return QSA_ERR_SHAPE;
     QSA_TRY(qsa::launch_compress(nullptr, seqs->cu_k_dev, p.batch, p.max_cmp_full, k_idx, k_blk,
-                                 0, (hipStream_t)stream));
+                                 0, nullptr, p.topk, (hipStream_t)stream));
     return QSA_OK;
 }
 
@@ -289,11 +316,12 @@ qsa_status qsa_forward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf1
     if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
     int32_t *sel_use = sel ? sel : ws_at<int32_t>(ws, p.off_sel);
-    if (k_idx && p.max_cmp_incr > 0)
+    SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
+    if (k_idx && p.max_cmp_incr > 0)   // compress the new blocks and build the table
         QSA_TRY(qsa::launch_compress(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.max_cmp_incr,
-                                     k_idx, k_blk, 1, hs));
-    QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
-                             ws_at<SeqInfo>(ws, p.off_tab), hs));
+                                     k_idx, k_blk, 1, tab, p.topk, hs));
+    else
+        QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk, tab, hs));
     if ((st = run_select(p, seqs, q_idx, w, k_blk, sel_use, ws, hs)) != QSA_OK) return st;
     return run_attend(p, q, k, v, sel_use, out, lse, ws, hs);
 }

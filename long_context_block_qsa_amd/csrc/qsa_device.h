@@ -66,6 +66,24 @@ __device__ __forceinline__ int upper_index(int n, int64_t x, F key) {
     return lo;
 }
 
+// Same, with one round of loads: lane i reads entry i, i+64, ... (up to 1024
+// entries) and the count of entries <= x comes from ballots. Wave-uniform result.
+template <typename F>
+__device__ __forceinline__ int find_seq(int n, int64_t x, F key) {
+    if (n > 1024) return upper_index(n, x, key);
+    const int l = __lane_id();
+    int cnt = 0;
+    for (int j0 = 0; j0 < n; j0 += 256) {   // 4 unconditional loads per round
+        int64_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = key(min(j0 + 64 * j + l, n - 1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            cnt += __popcll(__ballot(j0 + 64 * j + l < n && v[j] <= x));
+    }
+    return cnt - 1;
+}
+
 // ---------------------------------------------------------------- bf16
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
@@ -144,6 +162,141 @@ __device__ __forceinline__ T block_excl_scan(T v, T *scratch, T *total) {
     *total = scratch[NW];
     __syncthreads();
     return r;
+}
+
+// ---------------------------------------------------------------- selection
+
+// Digit plans of the radix select over 32-bit order keys (most significant first).
+// WIDE: 11 + 11 + 10 bits (2048-bin histograms) for long rows; NARROW: 4 x 8 bits.
+struct DigitPlan {
+    int n;
+    int shift[4];
+    int width[4];
+};
+constexpr DigitPlan kWide = {3, {21, 10, 0, 0}, {11, 11, 10, 0}};
+constexpr int kHistBins = 2048;
+constexpr DigitPlan kNarrow = {4, {24, 16, 8, 0}, {8, 8, 8, 8}};
+
+// The k-th largest of n keys (1 <= k <= n) by a most-significant-digit radix select
+// with LDS histograms. Returns theta (that key) and `need`, how many keys equal to
+// theta belong to the k largest (ties go to the lowest positions). All NT threads
+// of the workgroup must call it. hist: LDS, 2^max(width) entries; scan_sh: LDS,
+// NT/64+1 entries; found: LDS, 2 entries.
+template <int NT>
+__device__ __forceinline__ void radix_kth(const uint32_t *keys, int64_t n, int64_t k,
+                                          const DigitPlan &plan, uint32_t *hist,
+                                          int64_t *scan_sh, uint32_t *found,
+                                          uint32_t *theta_out, int64_t *need_out) {
+    static_assert(NT == 256, "bin ownership assumes 256 threads");
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, pmask = 0;
+    int64_t need = k;
+#pragma unroll 1
+    for (int pass = 0; pass < plan.n; ++pass) {
+        const int shift = plan.shift[pass], nb = 1 << plan.width[pass];
+        const uint32_t dmask = (uint32_t)nb - 1u;
+        for (int i = tid; i < nb; i += NT) hist[i] = 0u;
+        if (tid == 0) { found[0] = 0u; found[1] = 0u; }
+        __syncthreads();
+        // keys are read in batches of 8 before their atomics, so the loads overlap
+        for (int64_t i0 = tid; i0 < n; i0 += 8 * NT) {
+            uint32_t kk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t i = i0 + (int64_t)e * NT;
+                kk[e] = i < n ? keys[i] : 0u;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t i = i0 + (int64_t)e * NT;
+                if (i < n && (kk[e] & pmask) == prefix)
+                    atomicAdd(&hist[(kk[e] >> shift) & dmask], 1u);
+            }
+        }
+        __syncthreads();
+        // thread j owns `per` consecutive bins ending at nb - per*j (highest bins first)
+        const int per = nb / NT;
+        const int top = nb - per * tid;
+        int64_t local = 0;
+        for (int i = 1; i <= per; ++i) local += hist[top - i];
+        int64_t tot;
+        const int64_t above = block_excl_scan<int64_t, NT>(local, scan_sh, &tot);
+        if (above < need && need <= above + local) {
+            int64_t run = above;
+            for (int i = 1; i <= per; ++i) {
+                const int bin = top - i;
+                if (run + hist[bin] >= need) {
+                    found[0] = (uint32_t)bin;
+                    found[1] = (uint32_t)run;
+                    break;
+                }
+                run += hist[bin];
+            }
+        }
+        __syncthreads();
+        need -= (int64_t)found[1];
+        prefix |= found[0] << shift;
+        pmask |= dmask << shift;
+        __syncthreads();
+    }
+    *theta_out = prefix;
+    *need_out = need;
+}
+
+// Ordered pass after radix_kth: walks the n keys in position order and keeps every
+// key above theta and the first `need` keys equal to it, writing their ids
+// (idx[i], or i when idx is null, plus idx_base) and optionally keys to consecutive
+// output slots
+// (at most cap). Optionally counts kept entries per group of `group` positions in
+// LDS (group_cnt). Returns the number kept. All NT threads must call it.
+template <int NT, int PER>
+__device__ __forceinline__ int64_t emit_kept(const uint32_t *keys, const int32_t *idx,
+                                             int64_t n, uint32_t theta, int64_t need,
+                                             int32_t *out_idx, uint32_t *out_key, int64_t cap,
+                                             int64_t *scan_sh, uint32_t *group_cnt,
+                                             int group, int32_t idx_base = 0) {
+    const int tid = threadIdx.x;
+    int64_t run_eq = 0, run_sel = 0;
+#pragma unroll 1
+    for (int64_t base = 0; base < n; base += (int64_t)NT * PER) {
+        const int64_t i0 = base + (int64_t)tid * PER;
+        uint32_t kk[PER];
+        int n_eq = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const bool valid = i0 + e < n;
+            kk[e] = valid ? keys[i0 + e] : 0u;
+            n_eq += (valid && kk[e] == theta);
+        }
+        int64_t tot_eq;
+        int64_t eq_run = run_eq + block_excl_scan<int64_t, NT>(n_eq, scan_sh, &tot_eq);
+        int n_take = 0;
+        uint32_t take_mask = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const bool valid = i0 + e < n;
+            const bool eq = valid && kk[e] == theta;
+            const bool take = (valid && kk[e] > theta) || (eq && eq_run < need);
+            eq_run += eq;
+            if (take) { take_mask |= 1u << e; ++n_take; }
+        }
+        int64_t tot_take;
+        int64_t pos = run_sel + block_excl_scan<int64_t, NT>(n_take, scan_sh, &tot_take);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            if (take_mask & (1u << e)) {
+                if (pos < cap) {
+                    out_idx[pos] = (idx ? idx[i0 + e] : (int32_t)(i0 + e)) + idx_base;
+                    if (out_key) out_key[pos] = kk[e];
+                }
+                if (group_cnt) atomicAdd(&group_cnt[(i0 + e) / group], 1u);
+                ++pos;
+            }
+        }
+        run_eq += tot_eq;
+        run_sel += tot_take;
+    }
+    return run_sel;
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {

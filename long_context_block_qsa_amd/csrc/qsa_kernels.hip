@@ -1,27 +1,27 @@
 // qsa_kernels.hip -- gfx950 kernels of the QSA hot path:
-//   prep     per-sequence bookkeeping table (one workgroup)
-//   compress micro-block key compression (HBM stream)
-//   score    indexer scores, bf16 MFMA 16x16x32 with fp32 accumulation
-//   select   exact per-row top-k by radix select in LDS
-//   attend   sparse GQA attention over gathered micro-blocks (MFMA, online softmax)
-//   combine  split-K merge of attention partials
+//   prep / compress   per-sequence bookkeeping; micro-block key compression (HBM stream)
+//   score             indexer scores of whole rows, 4 query rows per tile (prefill)
+//   score_local       indexer scores of one block chunk + the chunk's exact local
+//                     top-KP candidates (decode: few rows, long contexts)
+//   select            exact top-k per row: from a chunk-candidate union when valid,
+//                     else from the full row (radix select, LDS histograms)
+//   attend            sparse GQA attention over gathered micro-blocks (MFMA, online
+//                     softmax), split over keys when rows are few
+//   combine           log-sum-exp merge of the key splits
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
 namespace qsa {
 
 // =============================================================== prep
-// One workgroup scans the sequences: first compressed block, first score tile and
-// first score slot of each. Score rows are the positions t >= max(L-nq, 4*topk+3)
-// (more visible blocks than the budget); they are tiled 4 rows at a time.
-constexpr int PREP_NT = 1024;
-
-__global__ void __launch_bounds__(PREP_NT)
-prep_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int batch,
-            int topk, SeqInfo *__restrict__ tab) {
-    __shared__ int64_t sh[PREP_NT / WAVE + 1];
+// Per-sequence table: first compressed block, first score tile and first score slot.
+// Score rows are the positions t >= max(L-nq, 4*topk+3) (more visible blocks than the
+// budget); they are tiled 4 rows at a time.
+template <int NT>
+__device__ void prep_body(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
+                          int batch, int topk, SeqInfo *__restrict__ tab, int64_t *sh) {
     int64_t carry_blk = 0, carry_tile = 0, carry_slot = 0;
-    for (int base = 0; base < batch; base += PREP_NT) {
+    for (int base = 0; base < batch; base += NT) {
         const int b = base + threadIdx.x;
         int32_t q0 = 0, nq = 0, k0 = 0, L = 0;
         int64_t nblk = 0, ntile = 0, nslot = 0;
@@ -29,19 +29,16 @@ prep_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, 
             q0 = cu_q[b]; nq = cu_q[b + 1] - q0;
             k0 = cu_k[b]; L = cu_k[b + 1] - k0;
             nblk = L / BS;
-            int64_t ts = first_scored_pos(L, nq, topk);
+            const int64_t ts = first_scored_pos(L, nq, topk);
             if (ts < L) {
                 ntile = (L - ts + 3) / 4;
                 nslot = slots_before(L) - slots_before(ts);
             }
         }
-        int64_t tot;
-        int64_t eb = block_excl_scan<int64_t, PREP_NT>(nblk, sh, &tot);
-        int64_t sum_blk = tot;
-        int64_t et = block_excl_scan<int64_t, PREP_NT>(ntile, sh, &tot);
-        int64_t sum_tile = tot;
-        int64_t es = block_excl_scan<int64_t, PREP_NT>(nslot, sh, &tot);
-        int64_t sum_slot = tot;
+        int64_t tot_b, tot_t, tot_s;
+        const int64_t eb = block_excl_scan<int64_t, NT>(nblk, sh, &tot_b);
+        const int64_t et = block_excl_scan<int64_t, NT>(ntile, sh, &tot_t);
+        const int64_t es = block_excl_scan<int64_t, NT>(nslot, sh, &tot_s);
         if (b < batch) {
             SeqInfo s;
             s.q0 = q0; s.nq = nq; s.k0 = k0; s.L = L;
@@ -50,22 +47,37 @@ prep_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, 
             s.s0 = carry_slot + es;
             tab[b] = s;
         }
-        carry_blk += sum_blk; carry_tile += sum_tile; carry_slot += sum_slot;
+        carry_blk += tot_b; carry_tile += tot_t; carry_slot += tot_s;
     }
+}
+
+constexpr int PREP_NT = 256;
+
+__global__ void __launch_bounds__(PREP_NT)
+prep_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int batch,
+            int topk, SeqInfo *__restrict__ tab) {
+    __shared__ int64_t sh[PREP_NT / WAVE + 1];
+    prep_body<PREP_NT>(cu_q, cu_k, batch, topk, tab, sh);
 }
 
 // =============================================================== compress
 // Sum of the 4 indexer keys of each micro-block, exactly (double), rounded once to
 // bf16. Thread = (block, 8 consecutive dims): 4 x 16-byte reads, one 16-byte write,
 // so a wave streams 8 whole blocks (4 KiB in, 1 KiB out) with full coalescing.
+// Grid: x = block group, y = sequence. When `tab` is given, the workgroup at
+// (gridDim.x - 1, 0) also builds the per-sequence table (fused prep).
 constexpr int CMP_NT = 256;
 constexpr int CMP_BLOCKS_PER_WG = CMP_NT / 8;
 
 __global__ void __launch_bounds__(CMP_NT)
 compress_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
                 const uint16_t *__restrict__ k_idx, uint16_t *__restrict__ k_blk,
-                int incremental) {
+                int incremental, SeqInfo *__restrict__ tab, int batch, int topk) {
     __shared__ int64_t red[CMP_NT / WAVE + 1];
+    if (tab && blockIdx.x == gridDim.x - 1) {
+        if (blockIdx.y == 0) prep_body<CMP_NT>(cu_q, cu_k, batch, topk, tab, red);
+        return;
+    }
     const int b = blockIdx.y;
     const int32_t k0 = cu_k[b], L = cu_k[b + 1] - k0;
     const int64_t nblk = L / BS;
@@ -74,230 +86,360 @@ compress_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu
         const int32_t nq = cu_q[b + 1] - cu_q[b];
         lo = (int64_t)(L - nq) / BS;
     }
-    const int64_t blk = lo + (int64_t)blockIdx.x * CMP_BLOCKS_PER_WG + threadIdx.x / 8;
-    if (lo + (int64_t)blockIdx.x * CMP_BLOCKS_PER_WG >= nblk) return;  // whole WG idle
+    const int64_t first = lo + (int64_t)blockIdx.x * CMP_BLOCKS_PER_WG;
+    if (first >= nblk) return;  // whole workgroup idle
 
     // first block row of this sequence: sum of floor(L_i/4) over earlier sequences
     int64_t part = 0;
     for (int i = threadIdx.x; i < b; i += CMP_NT) part += (cu_k[i + 1] - cu_k[i]) / BS;
-    int64_t tot;
-    (void)block_excl_scan<int64_t, CMP_NT>(part, red, &tot);
-    const int64_t blk0 = tot;
+    int64_t blk0;
+    (void)block_excl_scan<int64_t, CMP_NT>(part, red, &blk0);
 
+    const int64_t blk = first + threadIdx.x / 8;
     if (blk >= nblk) return;
     const int c = threadIdx.x % 8;
     const uint16_t *src = k_idx + ((int64_t)k0 + blk * BS) * DI + c * 8;
-    u32x4 r0 = load16(src), r1 = load16(src + DI), r2 = load16(src + 2 * DI),
-          r3 = load16(src + 3 * DI);
+    const u32x4 r0 = load16(src), r1 = load16(src + DI), r2 = load16(src + 2 * DI),
+                r3 = load16(src + 3 * DI);
     u32x4 out;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        double s_lo = (((double)bf16_lo(r0[q]) + (double)bf16_lo(r1[q])) + (double)bf16_lo(r2[q])) +
-                      (double)bf16_lo(r3[q]);
-        double s_hi = (((double)bf16_hi(r0[q]) + (double)bf16_hi(r1[q])) + (double)bf16_hi(r2[q])) +
-                      (double)bf16_hi(r3[q]);
+        const double s_lo = (((double)bf16_lo(r0[q]) + (double)bf16_lo(r1[q])) +
+                             (double)bf16_lo(r2[q])) + (double)bf16_lo(r3[q]);
+        const double s_hi = (((double)bf16_hi(r0[q]) + (double)bf16_hi(r1[q])) +
+                             (double)bf16_hi(r2[q])) + (double)bf16_hi(r3[q]);
         out[q] = f64_to_bf16_rne(s_lo) | (f64_to_bf16_rne(s_hi) << 16);
     }
     *reinterpret_cast<u32x4 *>(k_blk + (blk0 + blk) * DI + c * 8) = out;
 }
 
-// =============================================================== score
-// Tile = 4 consecutive score rows of one sequence; MFMA rows = (row, indexer head)
-// pairs (16 = 4 x 4), columns = 16 blocks, K = 64 indexer dims in two 16x16x32
-// steps. The contraction order of the dims is permuted so that each lane reads
-// 16 contiguous bytes of a block key per step (A and B use the same permutation):
-// step m, lane group g holds dims 32m + 8g .. 32m + 8g + 7.
-// Output lane (g, c) holds the 4 head dot products of row g and block c, so the
-// score sum_h w_h relu(dot_h) is formed in-lane and stored as an order key.
+// =============================================================== scoring core
+// Tile = up to 4 consecutive query rows of one sequence. MFMA rows = (row, indexer
+// head) pairs (16 = 4 x 4), columns = 16 blocks, K = 64 indexer dims in two
+// 16x16x32 bf16 steps. The contraction order of the dims is permuted so each lane
+// reads 16 contiguous bytes of a block key per step (A and B share the permutation):
+// step m, lane group g holds dims 32m + 8g .. 32m + 8g + 7. Output lane (g, c) holds
+// the 4 head dot products of row g and block c; the score sum_h w_h relu(dot_h) is
+// formed in-lane and turned into an order key.
+struct TileInfo {
+    SeqInfo s;
+    int64_t ts, t0, row0, nv_max;
+    int nrows;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const SeqInfo *tab, int batch, int topk,
+                                              int64_t tile) {
+    TileInfo ti;
+    const int sb = find_seq(batch, tile, [&](int i) { return (int64_t)tab[i].tile0; });
+    ti.s = tab[sb];
+    ti.ts = first_scored_pos(ti.s.L, ti.s.nq, topk);
+    ti.t0 = ti.ts + 4 * (tile - ti.s.tile0);
+    ti.nrows = (int)min<int64_t>(4, ti.s.L - ti.t0);
+    ti.row0 = ti.s.q0 + (ti.t0 - (ti.s.L - ti.s.nq));
+    ti.nv_max = nvis_of(ti.t0 + ti.nrows - 1);
+    return ti;
+}
+
+struct ScoreLane {
+    u32x4 qa[2];
+    float wr[HI];
+    int64_t slot, nv_row;
+};
+
+__device__ __forceinline__ ScoreLane score_lane_setup(const TileInfo &ti,
+                                                      const uint16_t *__restrict__ q_idx,
+                                                      const float *__restrict__ w) {
+    ScoreLane sl;
+    const int l = lane_id(), g = l >> 4, c = l & 15;
+    const int rr = c >> 2, hh = c & 3;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+        sl.qa[m] = rr < ti.nrows
+            ? load16(q_idx + ((ti.row0 + rr) * HI + hh) * DI + 32 * m + 8 * g)
+            : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < HI; ++h) sl.wr[h] = 0.f;
+    sl.slot = 0;
+    sl.nv_row = 0;
+    if (g < ti.nrows) {
+#pragma unroll
+        for (int h = 0; h < HI; ++h) sl.wr[h] = w[(ti.row0 + g) * HI + h];
+        sl.slot = ti.s.s0 + slots_before(ti.t0 + g) - slots_before(ti.ts);
+        sl.nv_row = nvis_of(ti.t0 + g);
+    }
+    return sl;
+}
+
+// Keys of NB groups of 16 consecutive blocks starting at b0, b0 + step, ...; all
+// loads are issued before the first MFMA (loads past hi are clamped to block hi-1).
+template <int NB>
+__device__ __forceinline__ void score_groups(const ScoreLane &sl, const uint16_t *kb,
+                                             int64_t b0, int64_t step, int64_t hi,
+                                             uint32_t (&key)[NB]) {
+    const int l = lane_id(), g = l >> 4, c = l & 15;
+    u32x4 b[NB][2];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const int64_t blk = b0 + u * step + c;
+        const uint16_t *src = kb + (blk < hi ? blk : hi - 1) * DI + 8 * g;
+        b[u][0] = load16(src);
+        b[u][1] = load16(src + 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the MFMAs
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma_bf16_16x16x32(sl.qa[0], b[u][0], acc);
+        acc = mfma_bf16_16x16x32(sl.qa[1], b[u][1], acc);
+        float sc = sl.wr[0] * fmaxf(acc[0], 0.f);
+        sc += sl.wr[1] * fmaxf(acc[1], 0.f);
+        sc += sl.wr[2] * fmaxf(acc[2], 0.f);
+        sc += sl.wr[3] * fmaxf(acc[3], 0.f);
+        key[u] = score_key(sc);
+    }
+}
+
+constexpr int SCORE_BATCH = 8;  // 16-block groups per wave in flight
+
 constexpr int SCORE_NT = 256;
 
+// Whole rows: grid x = tile, y = chunk of `chunk_blocks` blocks.
 __global__ void __launch_bounds__(SCORE_NT)
 score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
              const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
              const uint16_t *__restrict__ k_blk, uint32_t *__restrict__ keys,
              int64_t chunk_blocks) {
-    const int64_t tile = blockIdx.x;
-    const int sb = upper_index(batch, tile, [&](int i) { return (int64_t)tab[i].tile0; });
-    const SeqInfo s = tab[sb];
-    const int64_t ts = first_scored_pos(s.L, s.nq, topk);
-    const int64_t t0 = ts + 4 * (tile - s.tile0);
-    const int nrows = (int)min<int64_t>(4, s.L - t0);
-    const int64_t row0 = s.q0 + (t0 - (s.L - s.nq));
-    const int64_t nv_max = nvis_of(t0 + nrows - 1);
+    const TileInfo ti = tile_info(tab, batch, topk, blockIdx.x);
     const int64_t lo = (int64_t)blockIdx.y * chunk_blocks;
-    const int64_t hi = min<int64_t>(nv_max, lo + chunk_blocks);
+    const int64_t hi = min<int64_t>(ti.nv_max, lo + chunk_blocks);
     if (lo >= hi) return;
-
-    const int l = lane_id(), g = l >> 4, c = l & 15;
-    // A operand: q_idx of (row (c>>2), head (c&3)), dims of lane group g
-    u32x4 qa[2];
-    {
-        const int rr = c >> 2, hh = c & 3;
+    const ScoreLane sl = score_lane_setup(ti, q_idx, w);
+    const uint16_t *kb = k_blk + (int64_t)ti.s.blk0 * DI;
+    const int c = lane_id() & 15;
+    constexpr int64_t step = 16 * (SCORE_NT / WAVE);
+    for (int64_t b0 = lo + 16 * (threadIdx.x / WAVE); b0 < hi; b0 += step * SCORE_BATCH) {
+        uint32_t key[SCORE_BATCH];
+        score_groups<SCORE_BATCH>(sl, kb, b0, step, hi, key);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            if (rr < nrows)
-                qa[m] = load16(q_idx + ((row0 + rr) * HI + hh) * DI + 32 * m + 8 * g);
-            else
-                qa[m] = u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < SCORE_BATCH; ++u) {
+            const int64_t blk = b0 + u * step + c;
+            if (blk < hi && blk < sl.nv_row) keys[sl.slot + blk] = key[u];
         }
     }
-    // output side: row g of the tile
-    float wr[HI] = {0.f, 0.f, 0.f, 0.f};
-    int64_t slot = 0, nv_row = 0;
-    if (g < nrows) {
+}
+
+// =============================================================== score_local
+// Decode-shaped launches: grid x = tile, y = chunk of CH blocks. Besides writing
+// every key (needed by the exact fallback), each workgroup keeps its chunk's keys in
+// LDS and, for each row of the tile whose selection can come from chunk candidates,
+// writes the chunk's KP best (key, block) pairs in ascending block order to
+// cand[row][chunk][0..KP), padded with key 0 (below every real key).
+constexpr int LOC_NT = 256;
+constexpr int LOC_MAX_CH = 1024;
+constexpr int KP = 32;
+
+// A row may be selected from chunk candidates when its full chunks alone provide at
+// least topk candidates (so the union always holds topk real keys).
+__device__ __forceinline__ bool cand_eligible(int64_t nv, int topk, int ch) {
+    return nv > topk && (nv / ch) * KP >= topk;
+}
+
+__global__ void __launch_bounds__(LOC_NT)
+score_local_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
+                   const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
+                   const uint16_t *__restrict__ k_blk, uint32_t *__restrict__ keys,
+                   uint32_t *__restrict__ cand_key, int32_t *__restrict__ cand_idx,
+                   int ch, int max_chunks) {
+    __shared__ uint32_t lk[4][LOC_MAX_CH];
+    __shared__ uint32_t hist[256];
+    __shared__ int64_t scan_sh[LOC_NT / WAVE + 1];
+    __shared__ uint32_t found[2];
+
+    const TileInfo ti = tile_info(tab, batch, topk, blockIdx.x);
+    const int64_t lo = (int64_t)blockIdx.y * ch;
+    const int64_t hi = min<int64_t>(ti.nv_max, lo + ch);
+    if (lo >= hi) return;
+    const ScoreLane sl = score_lane_setup(ti, q_idx, w);
+    const uint16_t *kb = k_blk + (int64_t)ti.s.blk0 * DI;
+    const int l = lane_id(), g = l >> 4, c = l & 15;
+    constexpr int64_t step = 16 * (LOC_NT / WAVE);
+    for (int64_t b0 = lo + 16 * (threadIdx.x / WAVE); b0 < hi; b0 += step * SCORE_BATCH) {
+        uint32_t key[SCORE_BATCH];
+        score_groups<SCORE_BATCH>(sl, kb, b0, step, hi, key);
 #pragma unroll
-        for (int h = 0; h < HI; ++h) wr[h] = w[(row0 + g) * HI + h];
-        slot = s.s0 + slots_before(t0 + g) - slots_before(ts);
-        nv_row = nvis_of(t0 + g);
+        for (int u = 0; u < SCORE_BATCH; ++u) {
+            const int64_t blk = b0 + u * step + c;
+            if (blk < hi && blk < sl.nv_row) {
+                keys[sl.slot + blk] = key[u];
+                lk[g][blk - lo] = key[u];
+            }
+        }
     }
-    const uint16_t *kb = k_blk + (int64_t)s.blk0 * DI;
-    const int wv = threadIdx.x / WAVE;
-    for (int64_t base = lo + 16 * wv; base < hi; base += 16 * (SCORE_NT / WAVE)) {
-        const int64_t blk = base + c;
-        const int64_t blk_ld = blk < hi ? blk : hi - 1;
-        const uint16_t *src = kb + blk_ld * DI + 8 * g;
-        u32x4 b0 = load16(src), b1 = load16(src + 32);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma_bf16_16x16x32(qa[0], b0, acc);
-        acc = mfma_bf16_16x16x32(qa[1], b1, acc);
-        float sc = wr[0] * fmaxf(acc[0], 0.f);
-        sc += wr[1] * fmaxf(acc[1], 0.f);
-        sc += wr[2] * fmaxf(acc[2], 0.f);
-        sc += wr[3] * fmaxf(acc[3], 0.f);
-        if (blk < nv_row) keys[slot + blk] = score_key(sc);
+    __syncthreads();
+
+    for (int rr = 0; rr < ti.nrows; ++rr) {
+        const int64_t t = ti.t0 + rr;
+        const int64_t nv = nvis_of(t);
+        if (!cand_eligible(nv, topk, ch)) continue;       // uniform over the workgroup
+        const int64_t n = min<int64_t>(nv, hi) - lo;      // this row's blocks in the chunk
+        uint32_t *ck = cand_key + ((ti.row0 + rr) * max_chunks + blockIdx.y) * KP;
+        int32_t *ci = cand_idx + ((ti.row0 + rr) * max_chunks + blockIdx.y) * KP;
+        int64_t kept = 0;
+        if (n > KP) {
+            uint32_t theta;
+            int64_t need;
+            radix_kth<LOC_NT>(lk[rr], n, KP, kNarrow, hist, scan_sh, found, &theta, &need);
+            kept = emit_kept<LOC_NT, 4>(lk[rr], nullptr, n, theta, need, ci, ck, KP, scan_sh,
+                                        nullptr, 1, (int32_t)lo);
+        } else if (n > 0) {
+            if (threadIdx.x < n) {
+                ck[threadIdx.x] = lk[rr][threadIdx.x];
+                ci[threadIdx.x] = (int32_t)(lo + threadIdx.x);
+            }
+            kept = n;
+        }
+        for (int64_t i = kept + threadIdx.x; i < KP; i += LOC_NT) {
+            ck[i] = 0u;
+            ci[i] = -1;
+        }
+        __syncthreads();
     }
 }
 
 // =============================================================== select
 // One workgroup per query row. Rows within the budget keep blocks 0..nvis-1. Other
-// rows: exact radix select of the topk-th largest key over 3 digit passes
-// (12 + 12 + 8 bits) with LDS histograms, then one ordered pass that keeps every key
-// above the threshold and the lowest-index keys equal to it, written in ascending
-// block order through block-wide prefix counts.
+// rows: radix_kth + emit_kept over either the union of chunk candidates (when the
+// row was eligible and no chunk had all KP of its candidates kept: only then can a
+// chunk hide a better block, so the union result is exact) or the full row of keys.
+// Keys are staged in dynamic LDS when they fit (lds_cap keys), else read from the
+// workspace in each pass.
 constexpr int SEL_NT = 256;
-constexpr int SEL_PER = 16;  // keys per thread per sweep (contiguous)
+
+struct SelectArgs {
+    const SeqInfo *tab;
+    int batch, topk;
+    const uint32_t *keys;
+    const uint32_t *cand_key;
+    const int32_t *cand_idx;
+    int ch, max_chunks;  // ch = 0: no candidates
+    int32_t *sel;
+    int64_t lds_cap;     // keys that fit the dynamic LDS
+};
+
+// Top-k of n keys at `kk` (LDS or global; the caller passes a pointer of known
+// address space), ids from `ii` (or positions), written to out in ascending order.
+template <int PER, typename KP_T, typename IP_T>
+__device__ __forceinline__ void select_keys(KP_T kk, IP_T ii, int64_t n, int topk,
+                                            int32_t *out, uint32_t *hist, int64_t *scan_sh,
+                                            uint32_t *found, uint32_t *grp_cnt, int group,
+                                            int64_t ngroups) {
+    uint32_t theta;
+    int64_t need;
+    radix_kth<SEL_NT>(kk, n, topk, kWide, hist, scan_sh, found, &theta, &need);
+    if (grp_cnt) {
+        for (int64_t i = threadIdx.x; i < ngroups; i += SEL_NT) grp_cnt[i] = 0u;
+        __syncthreads();
+    }
+    emit_kept<SEL_NT, PER>(kk, ii, n, theta, need, out, nullptr, topk, scan_sh, grp_cnt, group);
+}
 
 __global__ void __launch_bounds__(SEL_NT)
-select_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
-              const uint32_t *__restrict__ keys, int32_t *__restrict__ sel) {
-    __shared__ uint32_t hist[4096];
+select_kernel(SelectArgs a) {
+    extern __shared__ uint32_t dyn[];   // lds_cap words
+    __shared__ uint32_t hist[kHistBins];  // histograms; then per-chunk kept counts
     __shared__ int64_t scan_sh[SEL_NT / WAVE + 1];
     __shared__ uint32_t found[2];
+    __shared__ int viol;
 
     const int64_t row = blockIdx.x;
-    const int sb = upper_index(batch, row, [&](int i) { return (int64_t)tab[i].q0; });
-    const SeqInfo s = tab[sb];
+    const int sb = find_seq(a.batch, row, [&](int i) { return (int64_t)a.tab[i].q0; });
+    const SeqInfo s = a.tab[sb];
     const int64_t t = (int64_t)s.L - s.nq + (row - s.q0);
     const int64_t nv = nvis_of(t);
-    int32_t *out = sel + row * topk;
+    int32_t *out = a.sel + row * a.topk;
     const int tid = threadIdx.x;
-    if (tid == 0) { found[0] = 0; found[1] = 0; }
 
-    if (nv <= topk) {
-        for (int i = tid; i < topk; i += SEL_NT) out[i] = i < nv ? i : -1;
+    if (nv <= a.topk) {
+        for (int i = tid; i < a.topk; i += SEL_NT) out[i] = i < nv ? i : -1;
         return;
     }
-    const int64_t ts = first_scored_pos(s.L, s.nq, topk);
-    const uint32_t *rk = keys + s.s0 + slots_before(t) - slots_before(ts);
-    const int64_t n = nv;
 
-    uint32_t prefix = 0, pmask = 0;
-    int64_t need = topk;
-    const int shifts[3] = {20, 8, 0};
-    const int widths[3] = {12, 12, 8};
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = shifts[pass], nb = 1 << widths[pass];
-        const uint32_t dmask = (uint32_t)nb - 1;
-        for (int i = tid; i < nb; i += SEL_NT) hist[i] = 0;
-        __syncthreads();
-        for (int64_t i = tid; i < n; i += SEL_NT) {
-            uint32_t kk = rk[i];
-            if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & dmask], 1u);
+    if (a.ch > 0 && cand_eligible(nv, a.topk, a.ch)) {
+        const int64_t nchunk = (nv + a.ch - 1) / a.ch;
+        const int64_t n = nchunk * KP;
+        const uint32_t *ck = a.cand_key + row * a.max_chunks * KP;
+        const int32_t *ci = a.cand_idx + row * a.max_chunks * KP;
+        uint32_t *cnt = nchunk <= kHistBins ? hist : nullptr;
+        if (tid == 0) viol = 0;
+        if (2 * n <= a.lds_cap) {
+            uint32_t *lk = dyn;
+            int32_t *li = reinterpret_cast<int32_t *>(dyn + n);
+            for (int64_t i = tid; i < n; i += SEL_NT) { lk[i] = ck[i]; li[i] = ci[i]; }
+            __syncthreads();
+            select_keys<8>(lk, li, n, a.topk, out, hist, scan_sh, found, cnt, KP, nchunk);
+        } else {
+            __syncthreads();
+            select_keys<8>(ck, ci, n, a.topk, out, hist, scan_sh, found, cnt, KP, nchunk);
         }
         __syncthreads();
-        // thread j owns the per consecutive bins ending at nb - per*j (highest first)
-        const int per = nb / SEL_NT;
-        const int top = nb - per * tid;
-        int64_t local = 0;
-        for (int i = 1; i <= per; ++i) local += hist[top - i];
-        int64_t tot;
-        int64_t above = block_excl_scan<int64_t, SEL_NT>(local, scan_sh, &tot);
-        if (above < need && need <= above + local) {
-            int64_t run = above;
-            for (int i = 1; i <= per; ++i) {
-                const int bin = top - i;
-                if (run + hist[bin] >= need) {
-                    found[0] = (uint32_t)bin;
-                    found[1] = (uint32_t)(run);
-                    break;
-                }
-                run += hist[bin];
+        // a full chunk (more than KP blocks) with every candidate kept may hide more
+        if (!cnt) {
+            if (tid == 0) viol = 1;   // cannot check: take the exact path
+        } else {
+            for (int64_t c = tid; c < nchunk; c += SEL_NT) {
+                const int64_t nc = min<int64_t>(a.ch, nv - c * a.ch);
+                if (nc > KP && cnt[c] >= (uint32_t)KP) viol = 1;
             }
         }
         __syncthreads();
-        const uint32_t digit = found[0];
-        need -= (int64_t)found[1];
-        prefix |= digit << shift;
-        pmask |= dmask << shift;
-        __syncthreads();
+        if (!viol) return;
     }
-    const uint32_t theta = prefix;  // the topk-th largest key; take `need` equal keys
 
-    int64_t run_eq = 0, run_sel = 0;
-    for (int64_t base = 0; base < n; base += (int64_t)SEL_NT * SEL_PER) {
-        const int64_t i0 = base + (int64_t)tid * SEL_PER;
-        uint32_t kk[SEL_PER];
-        int n_eq = 0;
+    // exact selection over the full row of keys
+    const int64_t ts = first_scored_pos(s.L, s.nq, a.topk);
+    const uint32_t *rk = a.keys + s.s0 + slots_before(t) - slots_before(ts);
+    if (nv <= a.lds_cap) {
+        for (int64_t i0 = tid; i0 < nv; i0 += 8 * SEL_NT) {
+            uint32_t v[8];
 #pragma unroll
-        for (int e = 0; e < SEL_PER; ++e) {
-            kk[e] = (i0 + e < n) ? rk[i0 + e] : 0u;
-            n_eq += (i0 + e < n && kk[e] == theta);
-        }
-        int64_t tot_eq;
-        int64_t eq_before = run_eq + block_excl_scan<int64_t, SEL_NT>(n_eq, scan_sh, &tot_eq);
-        int n_take = 0;
-        int64_t eq_run = eq_before;
-        uint32_t take_mask = 0;
-#pragma unroll
-        for (int e = 0; e < SEL_PER; ++e) {
-            bool valid = i0 + e < n;
-            bool gt = valid && kk[e] > theta;
-            bool eq = valid && kk[e] == theta;
-            bool take = gt || (eq && eq_run < need);
-            eq_run += eq;
-            if (take) { take_mask |= 1u << e; ++n_take; }
-        }
-        int64_t tot_take;
-        int64_t pos = run_sel + block_excl_scan<int64_t, SEL_NT>(n_take, scan_sh, &tot_take);
-#pragma unroll
-        for (int e = 0; e < SEL_PER; ++e)
-            if (take_mask & (1u << e)) {
-                if (pos < topk) out[pos] = (int32_t)(i0 + e);
-                ++pos;
+            for (int e = 0; e < 8; ++e) {
+                const int64_t i = i0 + (int64_t)e * SEL_NT;
+                v[e] = i < nv ? rk[i] : 0u;
             }
-        run_eq += tot_eq;
-        run_sel += tot_take;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t i = i0 + (int64_t)e * SEL_NT;
+                if (i < nv) dyn[i] = v[e];
+            }
+        }
+        __syncthreads();
+        select_keys<16>((const uint32_t *)dyn, (const int32_t *)nullptr, nv, a.topk, out, hist,
+                        scan_sh, found, nullptr, 1, 0);
+    } else {
+        select_keys<16>(rk, (const int32_t *)nullptr, nv, a.topk, out, hist, scan_sh, found,
+                        nullptr, 1, 0);
     }
 }
 
 // =============================================================== attend
 // One wave per (query row, key/value head g, key split). The row's keys are the
-// tokens of its kept blocks in ascending order, then its raw tail (treated as one
-// more block slot with 0..3 valid tokens). A wave walks them 32 at a time:
-//   S^T[32 keys x 16 heads] = K (A operand, 2 x 16 keys) * Q^T (B operand, 12 live
-//   heads of group g): 4 MFMA 16x16x32 steps per 16 keys over the 128 dims, with the
-//   dims permuted so each lane reads 16 contiguous bytes (step m, group gr holds
-//   dims 32m + 8gr .. +7).
+// tokens of its kept blocks in ascending order, then its raw tail (one more block
+// slot with 0..3 valid tokens). A wave walks them 32 at a time:
+//   S^T[32 keys x 16 heads] = K (A operand, 2 x 16 keys) * Q^T (B operand, the 12 live
+//   heads of group g): 4 MFMA 16x16x32 steps per 16 keys over the 128 dims, the dims
+//   permuted so each lane reads 16 contiguous bytes (step m, group gr holds dims
+//   32m + 8gr .. +7).
 //   Online softmax per head in base 2; each lane owns one head (its column).
-//   O^T[128 dims x 16 heads] += V^T * P^T: P^T is the lane's own 8 probabilities
-//   (keys 4gr..4gr+3 and 16+4gr..16+4gr+3, the k-slots of its lane group), split
-//   into bf16 hi + lo parts (2 MFMAs) to keep ~16 bits; V^T rows are permuted so row
-//   r of dim-tile mt is dim 8r + mt, which lets each lane load 16 contiguous bytes of
-//   V per key.
-// S = 1: final output. S > 1: unnormalised partial (m, l, acc) for the combine.
+//   O^T[128 dims x 16 heads] += V^T * P^T: P^T is the lane's own 8 probabilities (keys
+//   4gr..4gr+3 and 16+4gr..16+4gr+3, the k-slots of its lane group), split into bf16
+//   hi + lo parts (2 MFMAs) to keep ~16 bits; V^T rows are permuted so row r of
+//   dim-tile mt is dim 8r + mt, which lets each lane load 16 contiguous bytes of V per
+//   key.
+// Block ids of the row are held in registers (lane i: slot 64j + i) and broadcast with
+// shuffles, and each tile's K/V loads are issued one tile ahead of its MFMAs.
+// nsplit = 1: final output. nsplit > 1: unnormalised partial (acc, m, l) per split.
 constexpr int ATT_NT = 256;
-// split partial record per (row, split, head): acc[128], m, l, 2 pad (16-byte aligned)
-constexpr int PREC = HD + 4;
+constexpr int PREC = HD + 4;  // partial record per (row, split, head): acc[128], m, l, pad
 
 struct AttnArgs {
     const SeqInfo *tab;
@@ -307,7 +449,7 @@ struct AttnArgs {
     const uint16_t *q, *k, *v;
     const int32_t *sel;
     float *out, *lse;
-    float *part;       // split partials (S > 1)
+    float *part;
     int nsplit;
     int64_t nrows;
 };
@@ -315,6 +457,12 @@ struct AttnArgs {
 __device__ __forceinline__ int64_t part_stride_row(int nsplit) {
     return (int64_t)nsplit * HQ * PREC;
 }
+
+struct KVTile {
+    u32x4 kr[2][4];  // K rows of keys j0 + 16u + col, dims 32m + 8gr
+    u32x4 vr[8];     // V rows of the lane's 8 P keys, dims 8col .. 8col+7
+    uint32_t valid;  // bit 4u+i: key j0 + 16u + 4gr + i is attended
+};
 
 __global__ void __launch_bounds__(ATT_NT)
 attend_kernel(AttnArgs a) {
@@ -324,22 +472,25 @@ attend_kernel(AttnArgs a) {
     const int rem = (int)(item % (HKV * a.nsplit));
     const int g = rem / a.nsplit, sp = rem % a.nsplit;
 
-    const int sb = upper_index(a.batch, row, [&](int i) { return (int64_t)a.tab[i].q0; });
+    const int sb = find_seq(a.batch, row, [&](int i) { return (int64_t)a.tab[i].q0; });
     const SeqInfo s = a.tab[sb];
     const int64_t t = (int64_t)s.L - s.nq + (row - s.q0);
     const int64_t nv = nvis_of(t);
     const int ntail = (int)(t + 1 - BS * nv);
     const int32_t *srow = a.sel + row * a.topk;
-
     const int l = lane_id(), gr = l >> 4, col = l & 15;
 
-    // number of leading selected entries (stop at the first -1)
+    // number of leading selected entries: 8 unconditional loads in flight, then ballots
     int nsel = a.topk;
-    for (int i0 = 0; i0 < a.topk; i0 += WAVE) {
-        int i = i0 + l;
-        bool neg = i < a.topk && srow[i] < 0;
-        unsigned long long bal = __ballot(neg);
-        if (bal) { nsel = i0 + __builtin_ctzll(bal); break; }
+    {
+        int32_t v[KMAX / WAVE];
+#pragma unroll
+        for (int j = 0; j < KMAX / WAVE; ++j) v[j] = srow[min(64 * j + l, a.topk - 1)];
+#pragma unroll
+        for (int j = KMAX / WAVE - 1; j >= 0; --j) {
+            const unsigned long long bal = __ballot(64 * j + l < a.topk && v[j] < 0);
+            if (bal) nsel = 64 * j + __builtin_ctzll(bal);
+        }
     }
     const int nslot = nsel + (ntail > 0 ? 1 : 0);
     const int npos = 4 * nslot;
@@ -348,75 +499,95 @@ attend_kernel(AttnArgs a) {
     const int p_lo = sp * chunk;
     const int p_hi = min(npos, p_lo + chunk);
 
-    // Q^T operand: head g*12 + col, dims of lane group gr
     const int head = g * GQ + col;
     u32x4 qb[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        if (col < GQ)
-            qb[m] = load16(a.q + (row * HQ + head) * HD + 32 * m + 8 * gr);
-        else
-            qb[m] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int m = 0; m < 4; ++m)
+        qb[m] = col < GQ ? load16(a.q + (row * HQ + head) * HD + 32 * m + 8 * gr)
+                         : u32x4{0u, 0u, 0u, 0u};
 
     f32x4 acc[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int64_t kvrow0 = (int64_t)s.k0;
-    const int64_t safe_tok = kvrow0 + t;  // always a valid key row
-    auto slot_block = [&](int slot, bool &ok) -> int64_t {
-        if (slot < nsel) {
-            int32_t bid = srow[slot];
-            ok = bid >= 0 && bid < nv;
-            return bid;
-        }
-        ok = (slot == nsel && ntail > 0);
-        return nv;
-    };
-    auto key_token = [&](int p, bool &ok) -> int64_t {
-        bool okb;
-        int64_t bid = slot_block(p >> 2, okb);
-        const int i = p & 3;
-        ok = okb && p < p_hi && (p >> 2 < nsel || i < ntail);
-        return ok ? kvrow0 + BS * bid + i : safe_tok;
-    };
+    const int64_t kv0 = (int64_t)s.k0;
+    const int64_t safe_tok = kv0 + t;  // always a valid key row
+    const uint16_t *kbase = a.k + g * HD;
+    const uint16_t *vbase = a.v + g * HD;
 
-    for (int j0 = p_lo; j0 < p_hi; j0 += 32) {
-        // ---- scores S^T for keys j0 .. j0+31
-        f32x4 sc[2];
-        bool kval[2];
+    // first token of slot sl (block ids of the current 64-slot group held in `cur`)
+    auto slot_token0 = [&](int sl, int32_t cur, bool &ok) -> int64_t {
+        const int32_t bid = __shfl(cur, sl & 63);
+        if (sl < nsel) {
+            ok = bid >= 0 && bid < nv;
+            return kv0 + (int64_t)BS * bid;
+        }
+        ok = sl == nsel && ntail > 0;
+        return kv0 + (int64_t)BS * nv;
+    };
+    auto load_tile = [&](int j0, int32_t cur) -> KVTile {
+        KVTile T;
+        T.valid = 0;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
+            const int p = j0 + 16 * u + col;
             bool ok;
-            const int64_t tok = key_token(j0 + 16 * u + col, ok);
-            (void)ok;
-            const uint16_t *kp = a.k + (tok * HKV + g) * HD + 8 * gr;
-            f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
+            int64_t tok = slot_token0(p >> 2, cur, ok) + (p & 3);
+            ok = ok && p < p_hi && ((p >> 2) < nsel || (p & 3) < ntail);
+            if (!ok) tok = safe_tok;
+            const uint16_t *kp = kbase + tok * (HKV * HD) + 8 * gr;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) c4 = mfma_bf16_16x16x32(load16(kp + 32 * m), qb[m], c4);
-            sc[u] = c4;
-            kval[u] = false;
+            for (int m = 0; m < 4; ++m) T.kr[u][m] = load16(kp + 32 * m);
         }
-        (void)kval;
-        // lane (gr, col): sc[u][i] = logit of key j0 + 16u + 4gr + i for head col
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int sl = (j0 >> 2) + 4 * h + gr;
+            bool okb;
+            const int64_t tok0 = slot_token0(sl, cur, okb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = 4 * sl + i;
+                const bool ok = okb && p < p_hi && (sl < nsel || i < ntail);
+                const int64_t tok = ok ? tok0 + i : safe_tok;
+                T.vr[4 * h + i] = load16(vbase + tok * (HKV * HD) + 8 * col);
+                if (ok) T.valid |= 1u << (4 * h + i);
+            }
+        }
+        return T;
+    };
+    // block ids of slots 64*grp .. 64*grp+63 (lane i: slot 64*grp + i), L2-resident
+    auto group_ids = [=](int grp) -> int32_t { return srow[min(64 * grp + l, a.topk - 1)]; };
+
+    int cur_grp = p_lo >> 8;  // 64 slots = 256 key positions per group
+    int32_t cur = group_ids(cur_grp);
+    KVTile nxt;
+    if (p_lo < p_hi) nxt = load_tile(p_lo, cur);
+    for (int j0 = p_lo; j0 < p_hi; j0 += 32) {
+        const KVTile T = nxt;
+        const int jn = j0 + 32;
+        if (jn < p_hi) {
+            if ((jn >> 8) != cur_grp) { cur_grp = jn >> 8; cur = group_ids(cur_grp); }
+            nxt = load_tile(jn, cur);
+        }
+        // ---- logits S^T for keys j0 .. j0+31 (lane: keys j0+16u+4gr+i, head col)
         float z[8];
         float mx = -INFINITY;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
+            f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) c4 = mfma_bf16_16x16x32(T.kr[u][m], qb[m], c4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                bool ok;
-                (void)key_token(j0 + 16 * u + 4 * gr + i, ok);
-                float zz = ok ? sc[u][i] * a.scale_log2 : -INFINITY;
-                z[4 * u + i] = zz;
-                mx = fmaxf(mx, zz);
+                const bool ok = (T.valid >> (4 * u + i)) & 1u;
+                z[4 * u + i] = ok ? c4[i] * a.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, z[4 * u + i]);
             }
         }
         mx = wave_max_xor_16_32(mx);
         const float m_new = fmaxf(m_run, mx);
-        if (m_new == -INFINITY) continue;  // nothing valid yet (whole wave agrees)
+        if (m_new == -INFINITY) continue;  // no attended key yet (uniform over the wave)
         const float alpha = exp2f(m_run - m_new);
         float p[8], rs = 0.f;
 #pragma unroll
@@ -430,24 +601,14 @@ attend_kernel(AttnArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) acc[mt] *= alpha;
 
-        // P^T operand, hi and lo bf16 parts
         u32x4 ph, pl;
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
-            uint32_t h0 = f32_to_bf16_rne(p[2 * q2]), h1 = f32_to_bf16_rne(p[2 * q2 + 1]);
-            float r0 = p[2 * q2] - __uint_as_float(h0 << 16);
-            float r1 = p[2 * q2 + 1] - __uint_as_float(h1 << 16);
+            const uint32_t h0 = f32_to_bf16_rne(p[2 * q2]), h1 = f32_to_bf16_rne(p[2 * q2 + 1]);
+            const float r0 = p[2 * q2] - __uint_as_float(h0 << 16);
+            const float r1 = p[2 * q2 + 1] - __uint_as_float(h1 << 16);
             ph[q2] = h0 | (h1 << 16);
             pl[q2] = f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16);
-        }
-        // V rows of the lane's 8 keys, dims 8*col .. 8*col+7
-        u32x4 vv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bool ok;
-            const int pe = j0 + (e < 4 ? 4 * gr + e : 16 + 4 * gr + (e - 4));
-            const int64_t tok = key_token(pe, ok);
-            vv[e] = load16(a.v + (tok * HKV + g) * HD + 8 * col);
         }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
@@ -455,7 +616,7 @@ attend_kernel(AttnArgs a) {
             u32x4 va;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                uint32_t x0 = vv[2 * kk][q2], x1 = vv[2 * kk + 1][q2];
+                const uint32_t x0 = T.vr[2 * kk][q2], x1 = T.vr[2 * kk + 1][q2];
                 va[kk] = (mt & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u))
                                   : ((x0 & 0xffffu) | (x1 << 16));
             }
@@ -472,8 +633,8 @@ attend_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int d0 = 8 * (4 * gr + i);
-            f32x4 lo4 = {acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
-            f32x4 hi4 = {acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv, acc[7][i] * inv};
+            const f32x4 lo4 = {acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
+            const f32x4 hi4 = {acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv, acc[7][i] * inv};
             *reinterpret_cast<f32x4 *>(o + d0) = lo4;
             *reinterpret_cast<f32x4 *>(o + d0 + 4) = hi4;
         }
@@ -481,13 +642,12 @@ attend_kernel(AttnArgs a) {
             a.lse[row * HQ + head] = l_run > 0.f ? m_run * 0.69314718055994531f + logf(l_run)
                                                  : -INFINITY;
     } else {
-        float *pp = a.part + row * part_stride_row(a.nsplit) +
-                    ((int64_t)sp * HQ + head) * PREC;
+        float *pp = a.part + row * part_stride_row(a.nsplit) + ((int64_t)sp * HQ + head) * PREC;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int d0 = 8 * (4 * gr + i);
-            f32x4 lo4 = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-            f32x4 hi4 = {acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+            const f32x4 lo4 = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+            const f32x4 hi4 = {acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
             *reinterpret_cast<f32x4 *>(pp + d0) = lo4;
             *reinterpret_cast<f32x4 *>(pp + d0 + 4) = hi4;
         }
@@ -496,7 +656,8 @@ attend_kernel(AttnArgs a) {
 }
 
 // =============================================================== combine
-// One wave per (row, head): log-sum-exp merge of the split partials, in split order.
+// One wave per (row, head): lane s reads split s's (m, l); the merged output is the
+// weighted sum of the split accumulators in split order (deterministic).
 constexpr int CMB_NT = 256;
 
 __global__ void __launch_bounds__(CMB_NT)
@@ -509,18 +670,27 @@ combine_kernel(const float *__restrict__ part, int nsplit, int64_t nrows,
     const int l = lane_id();
     const float *pr = part + row * part_stride_row(nsplit) + (int64_t)head * PREC;
     const int64_t sstride = (int64_t)HQ * PREC;
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, pr[sp * sstride + HD]);
-    float Lsum = 0.f, o0 = 0.f, o1 = 0.f;
-    if (M != -INFINITY) {
-        for (int sp = 0; sp < nsplit; ++sp) {
-            const float *ps = pr + sp * sstride;
-            const float ms = ps[HD];
-            if (ms == -INFINITY) continue;
-            const float f = exp2f(ms - M);
-            Lsum += ps[HD + 1] * f;
-            o0 += ps[2 * l] * f;
-            o1 += ps[2 * l + 1] * f;
+    const float ms = l < nsplit ? pr[l * sstride + HD] : -INFINITY;
+    const float ls = l < nsplit ? pr[l * sstride + HD + 1] : 0.f;
+    float M = ms;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
+    const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    float Lsum = ls * f;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) Lsum += __shfl_xor(Lsum, d);
+    float o0 = 0.f, o1 = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += 16) {
+        float2 v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            v[j] = s0 + j < nsplit ? *reinterpret_cast<const float2 *>(pr + (s0 + j) * sstride + 2 * l)
+                                   : float2{0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float fs = __shfl(f, (s0 + j) & 63);
+            o0 += v[j].x * fs;
+            o1 += v[j].y * fs;
         }
     }
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
@@ -542,12 +712,14 @@ hipError_t launch_prep(const int32_t *cu_q, const int32_t *cu_k, int batch, int 
 
 hipError_t launch_compress(const int32_t *cu_q, const int32_t *cu_k, int batch,
                            int64_t max_blocks, const uint16_t *k_idx, uint16_t *k_blk,
-                           int incremental, hipStream_t st) {
-    if (max_blocks <= 0 || batch <= 0) return hipSuccess;
-    const int64_t gx = (max_blocks + CMP_BLOCKS_PER_WG - 1) / CMP_BLOCKS_PER_WG;
+                           int incremental, SeqInfo *tab, int topk, hipStream_t st) {
+    if (batch <= 0) return hipSuccess;
+    int64_t gx = (max_blocks + CMP_BLOCKS_PER_WG - 1) / CMP_BLOCKS_PER_WG;
+    if (tab) gx += 1;  // fused prep workgroup
+    if (gx <= 0) return hipSuccess;
     trace_before(1, st);
     hipLaunchKernelGGL(compress_kernel, dim3((unsigned)gx, (unsigned)batch), dim3(CMP_NT), 0, st,
-                       cu_q, cu_k, k_idx, k_blk, incremental);
+                       cu_q, cu_k, k_idx, k_blk, incremental, tab, batch, topk);
     return trace_after(st, hipGetLastError());
 }
 
@@ -563,12 +735,56 @@ hipError_t launch_score(const SeqInfo *tab, int batch, int topk, const uint16_t 
     return trace_after(st, hipGetLastError());
 }
 
+hipError_t launch_score_local(const SeqInfo *tab, int batch, int topk, const uint16_t *q_idx,
+                              const float *w, const uint16_t *k_blk, uint32_t *keys,
+                              uint32_t *cand_key, int32_t *cand_idx, int64_t n_tiles,
+                              int ch, int max_chunks, hipStream_t st) {
+    if (n_tiles <= 0) return hipSuccess;
+    trace_before(2, st);
+    hipLaunchKernelGGL(score_local_kernel, dim3((unsigned)n_tiles, (unsigned)max_chunks),
+                       dim3(LOC_NT), 0, st, tab, batch, topk, q_idx, w, k_blk, keys, cand_key,
+                       cand_idx, ch, max_chunks);
+    return trace_after(st, hipGetLastError());
+}
+
+int64_t select_lds_cap_keys() {
+    static int64_t cap = -1;
+    if (cap < 0) {
+        int dev = 0, limit = 65536;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&limit, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+                hipSuccess)
+            limit = 65536;
+        // static LDS of select_kernel: histogram + small
+        const int64_t stat = kHistBins * 4 + 128;
+        int64_t c = (limit - stat) / 4;
+        c = c > 16384 ? 16384 : c;
+        cap = c < 0 ? 0 : c & ~(int64_t)255;
+    }
+    return cap;
+}
+
 hipError_t launch_select(const SeqInfo *tab, int batch, int topk, const uint32_t *keys,
-                         int32_t *sel, int64_t n_rows, hipStream_t st) {
+                         const uint32_t *cand_key, const int32_t *cand_idx, int ch,
+                         int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
+                         hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
+    SelectArgs a;
+    a.tab = tab; a.batch = batch; a.topk = topk; a.keys = keys;
+    a.cand_key = cand_key; a.cand_idx = cand_idx; a.ch = ch; a.max_chunks = max_chunks;
+    a.sel = sel;
+    const int64_t cap = select_lds_cap_keys();
+    int64_t want = max_nvis;
+    if (ch > 0) want = want > 2 * (int64_t)max_chunks * KP ? want : 2 * (int64_t)max_chunks * KP;
+    a.lds_cap = want < cap ? want : cap;
+    const size_t shmem = (size_t)a.lds_cap * 4;
+    if (shmem > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void *)select_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        if (e != hipSuccess) return e;
+    }
     trace_before(3, st);
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), 0, st, tab, batch,
-                       topk, keys, sel);
+    hipLaunchKernelGGL(select_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), shmem, st, a);
     return trace_after(st, hipGetLastError());
 }
 
