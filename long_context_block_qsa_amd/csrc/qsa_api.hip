@@ -83,7 +83,42 @@ struct Plan {
     int max_chunks = 0;         // chunks of the longest scored row (decode path)
     int nsplit = 1;             // attention key splits per row
     size_t off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, ws_bytes = 0;
+    bool use_dec = false;       // few rows: row/tile tables travel as kernel arguments
+    bool fuse_compress = false; // decode: scoring workgroups compress the new blocks
+    qsa::DecodeTables dec;
 };
+
+// Row and tile tables of a call with at most DEC_MAX query rows and score tiles.
+void build_decode_tables(const int32_t *cq, const int32_t *ck, int batch, int topk,
+                         qsa::DecodeTables *d) {
+    int64_t blk = 0, slots = 0, tiles = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t L = (int64_t)ck[b + 1] - ck[b], nq = (int64_t)cq[b + 1] - cq[b];
+        const int64_t ts = h_first_scored_pos(L, nq, topk);
+        for (int64_t r = cq[b]; r < cq[b + 1]; ++r) {
+            const int64_t t = L - nq + (r - cq[b]);
+            qsa::DecRow &x = d->row[r];
+            x.k0 = ck[b];
+            x.t = (int32_t)t;
+            x.blk0 = (int32_t)blk;
+            x.pad = 0;
+            x.slot = t >= ts ? slots + h_slots_before(t) - h_slots_before(ts) : 0;
+        }
+        if (ts < L) {
+            const int64_t nt = (L - ts + 3) / 4;
+            for (int64_t i = 0; i < nt; ++i) {
+                qsa::DecTile &y = d->tile[tiles + i];
+                y.row0 = (int32_t)(cq[b] + (ts + 4 * i - (L - nq)));
+                y.nrows = (int32_t)std::min<int64_t>(4, L - (ts + 4 * i));
+                y.new_lo = (int32_t)((L - nq) / qsa::BS);
+                y.new_hi = (int32_t)(L / qsa::BS);
+            }
+            tiles += nt;
+            slots += h_slots_before(L) - h_slots_before(ts);
+        }
+        blk += L / qsa::BS;
+    }
+}
 
 qsa_status check_dims(const qsa_dims *d) {
     if (!d) return QSA_ERR_NULL;
@@ -131,17 +166,28 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     p->tq = cq ? cq[s->batch] : 0;
     if (p->n_tiles > INT32_MAX) return QSA_ERR_UNSUPPORTED;
 
+    p->use_dec = cq && p->tq <= qsa::DEC_MAX && p->n_tiles <= qsa::DEC_MAX;
+    if (p->use_dec) {
+        build_decode_tables(cq, ck, p->batch, p->topk, &p->dec);
+        // new blocks can be compressed by the scoring kernel when every sequence that
+        // has one also has a score tile (its last tile covers all of its blocks)
+        p->fuse_compress = true;
+        for (int b = 0; b < p->batch; ++b) {
+            const int64_t L = (int64_t)ck[b + 1] - ck[b], nq = (int64_t)cq[b + 1] - cq[b];
+            const bool has_new = nq > 0 && L / qsa::BS > (L - nq) / qsa::BS;
+            if (has_new && h_first_scored_pos(L, nq, p->topk) >= L) p->fuse_compress = false;
+        }
+    }
     // decode path: few score tiles over long rows -> chunked scoring with local
     // candidates; the chunk shrinks until the longest row has 16 full chunks
     constexpr int kKP = 32;
-    if (p->n_tiles > 0 && p->n_tiles <= 64) {
+    // (rows with too few chunks for candidates are selected from their full key row)
+    if (p->use_dec && p->n_tiles > 0) {
         int ch = 1024;
         while (ch > 64 && (p->max_score_blocks / ch) * kKP < p->topk) ch /= 2;
-        if ((p->max_score_blocks / ch) * kKP >= p->topk) {
-            p->local_ch = ch;
-            p->max_chunks = (int)((p->max_score_blocks + ch - 1) / ch);
-            if (p->max_chunks > kMaxGridY) return QSA_ERR_UNSUPPORTED;
-        }
+        p->local_ch = ch;
+        p->max_chunks = (int)((p->max_score_blocks + ch - 1) / ch);
+        if (p->max_chunks > kMaxGridY) return QSA_ERR_UNSUPPORTED;
     }
     // score grid: enough workgroups to fill the chip when few tiles exist
     if (p->n_tiles > 0 && p->local_ch == 0) {
@@ -192,7 +238,8 @@ template <typename T>
 T *ws_at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
 
 qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, const float *w,
-                      const qsa_bf16 *k_blk, int32_t *sel, void *ws, hipStream_t st) {
+                      const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel, void *ws,
+                      hipStream_t st) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
     uint32_t *keys = ws_at<uint32_t>(ws, p.off_union);
     uint32_t *cand_key = nullptr;
@@ -200,14 +247,15 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
     if (p.local_ch > 0) {
         cand_key = ws_at<uint32_t>(ws, p.off_cand);
         cand_idx = reinterpret_cast<int32_t *>(cand_key + (size_t)p.tq * p.max_chunks * 32);
-        QSA_TRY(qsa::launch_score_local(tab, p.batch, p.topk, q_idx, w, k_blk, keys, cand_key,
-                                        cand_idx, p.n_tiles, p.local_ch, p.max_chunks, st));
+        QSA_TRY(qsa::launch_score_local(p.dec, p.n_tiles, p.topk, q_idx, w, k_idx, k_blk, keys,
+                                        cand_key, cand_idx, p.local_ch, p.max_chunks, st));
     } else {
         QSA_TRY(qsa::launch_score(tab, p.batch, p.topk, q_idx, w, k_blk, keys, p.n_tiles,
                                   p.max_score_blocks, p.score_chunk, st));
     }
-    QSA_TRY(qsa::launch_select(tab, p.batch, p.topk, keys, cand_key, cand_idx, p.local_ch,
-                               p.max_chunks, sel, p.tq, p.max_score_blocks, st));
+    QSA_TRY(qsa::launch_select(tab, p.use_dec ? &p.dec : nullptr, p.batch, p.topk, keys,
+                               cand_key, cand_idx, p.local_ch, p.max_chunks, sel, p.tq,
+                               p.max_score_blocks, st));
     (void)s;
     return QSA_OK;
 }
@@ -216,8 +264,8 @@ qsa_status run_attend(const Plan &p, const qsa_bf16 *q, const qsa_bf16 *k, const
                       const int32_t *sel, float *out, float *lse, void *ws, hipStream_t st) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
     float *part = ws_at<float>(ws, p.off_union);
-    QSA_TRY(qsa::launch_attend(tab, p.batch, p.topk, p.scale, q, k, v, sel, out, lse, part,
-                               p.nsplit, p.tq, st));
+    QSA_TRY(qsa::launch_attend(tab, p.use_dec ? &p.dec : nullptr, p.batch, p.topk, p.scale, q,
+                               k, v, sel, out, lse, part, p.nsplit, p.tq, st));
     return QSA_OK;
 }
 
@@ -276,9 +324,10 @@ qsa_status qsa_select(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16
         return QSA_ERR_SHAPE;
     if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
-    QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
-                             ws_at<SeqInfo>(ws, p.off_tab), hs));
-    return run_select(p, seqs, q_idx, w, k_blk, sel, ws, hs);
+    if (!p.use_dec)
+        QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
+                                 ws_at<SeqInfo>(ws, p.off_tab), hs));
+    return run_select(p, seqs, q_idx, w, nullptr, const_cast<qsa_bf16 *>(k_blk), sel, ws, hs);
 }
 
 qsa_status qsa_attend(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
@@ -293,8 +342,9 @@ qsa_status qsa_attend(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16
         return QSA_ERR_SHAPE;
     if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
-    QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
-                             ws_at<SeqInfo>(ws, p.off_tab), hs));
+    if (!p.use_dec)
+        QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
+                                 ws_at<SeqInfo>(ws, p.off_tab), hs));
     return run_attend(p, q, k, v, sel, out, lse, ws, hs);
 }
 
@@ -316,13 +366,16 @@ qsa_status qsa_forward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf1
     if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
     int32_t *sel_use = sel ? sel : ws_at<int32_t>(ws, p.off_sel);
-    SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
-    if (k_idx && p.max_cmp_incr > 0)   // compress the new blocks and build the table
+    SeqInfo *tab = p.use_dec ? nullptr : ws_at<SeqInfo>(ws, p.off_tab);
+    const bool fused = p.use_dec && p.fuse_compress && k_idx && p.n_tiles > 0;
+    if (k_idx && p.max_cmp_incr > 0 && !fused)   // compress the new blocks (and build the table)
         QSA_TRY(qsa::launch_compress(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.max_cmp_incr,
                                      k_idx, k_blk, 1, tab, p.topk, hs));
-    else
+    else if (!p.use_dec)
         QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk, tab, hs));
-    if ((st = run_select(p, seqs, q_idx, w, k_blk, sel_use, ws, hs)) != QSA_OK) return st;
+    if ((st = run_select(p, seqs, q_idx, w, fused ? k_idx : nullptr, k_blk, sel_use, ws, hs)) !=
+        QSA_OK)
+        return st;
     return run_attend(p, q, k, v, sel_use, out, lse, ws, hs);
 }
 

@@ -38,6 +38,32 @@ struct SeqInfo {
     int64_t s0;     // first score slot
 };
 
+// Host-computed row and tile tables passed as kernel arguments when a call has few
+// query rows (decode): no table kernel and no device-side sequence lookup.
+constexpr int DEC_MAX = 64;
+struct DecRow {
+    int32_t k0;     // first key row of the row's sequence
+    int32_t t;      // position of the query token
+    int32_t blk0;   // first compressed-block row of the sequence
+    int32_t pad;
+    int64_t slot;   // first score slot of the row (rows with nvis > topk)
+};
+struct DecTile {
+    int32_t row0;   // first query row of the tile
+    int32_t nrows;  // 1..4 consecutive rows of one sequence
+    int32_t new_lo; // sequence-local blocks [new_lo, new_hi) hold a query token
+    int32_t new_hi;
+};
+struct DecodeTables {
+    DecRow row[DEC_MAX];
+    DecTile tile[DEC_MAX];
+};
+
+// What a kernel needs to know about one query row.
+struct RowView {
+    int64_t k0, t, blk0, slot;
+};
+
 // ---------------------------------------------------------------- visibility
 
 // Blocks whose 4 tokens are all at or before position t.
@@ -143,6 +169,40 @@ __device__ __forceinline__ T wave_incl_scan(T v) {
     return v;
 }
 
+// Inclusive prefix sum of int32 over a wave with DPP row shifts and row broadcasts
+// (4 shifts within each 16-lane row, then rows 1/3 add row 0/2's last lane and rows
+// 2/3 add lane 31).
+__device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// Block-wide exclusive prefix sum of int32 with two barriers; scratch: NT/64 ints.
+template <int NT>
+__device__ __forceinline__ int32_t block_excl_scan_i32(int32_t v, int32_t *scratch,
+                                                       int32_t *total) {
+    constexpr int NW = NT / WAVE;
+    const int w = threadIdx.x / WAVE;
+    const int32_t inc = wave_incl_scan_i32(v);
+    if (lane_id() == WAVE - 1) scratch[w] = inc;
+    __syncthreads();
+    int32_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int32_t x = scratch[i];
+        before += i < w ? x : 0;
+        tot += x;
+    }
+    *total = tot;
+    __syncthreads();  // scratch is rewritten by the next call
+    return before + inc - v;
+}
+
 // Block-wide exclusive prefix sum; `scratch` holds >= nwaves+1 elements of T.
 // Returns the exclusive prefix and writes the block total to *total.
 template <typename T, int NT>
@@ -182,10 +242,10 @@ constexpr DigitPlan kNarrow = {4, {24, 16, 8, 0}, {8, 8, 8, 8}};
 // theta belong to the k largest (ties go to the lowest positions). All NT threads
 // of the workgroup must call it. hist: LDS, 2^max(width) entries; scan_sh: LDS,
 // NT/64+1 entries; found: LDS, 2 entries.
-template <int NT>
-__device__ __forceinline__ void radix_kth(const uint32_t *keys, int64_t n, int64_t k,
+template <int NT, typename KeyPtr>
+__device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
                                           const DigitPlan &plan, uint32_t *hist,
-                                          int64_t *scan_sh, uint32_t *found,
+                                          int32_t *scan_sh, uint32_t *found,
                                           uint32_t *theta_out, int64_t *need_out) {
     static_assert(NT == 256, "bin ownership assumes 256 threads");
     const int tid = threadIdx.x;
@@ -217,11 +277,11 @@ __device__ __forceinline__ void radix_kth(const uint32_t *keys, int64_t n, int64
         // thread j owns `per` consecutive bins ending at nb - per*j (highest bins first)
         const int per = nb / NT;
         const int top = nb - per * tid;
-        int64_t local = 0;
-        for (int i = 1; i <= per; ++i) local += hist[top - i];
-        int64_t tot;
-        const int64_t above = block_excl_scan<int64_t, NT>(local, scan_sh, &tot);
-        if (above < need && need <= above + local) {
+        int32_t local = 0;
+        for (int i = 1; i <= per; ++i) local += (int32_t)hist[top - i];
+        int32_t tot;
+        const int64_t above = block_excl_scan_i32<NT>(local, scan_sh, &tot);
+        if (above < need && need <= above + (int64_t)local) {
             int64_t run = above;
             for (int i = 1; i <= per; ++i) {
                 const int bin = top - i;
@@ -249,11 +309,11 @@ __device__ __forceinline__ void radix_kth(const uint32_t *keys, int64_t n, int64
 // output slots
 // (at most cap). Optionally counts kept entries per group of `group` positions in
 // LDS (group_cnt). Returns the number kept. All NT threads must call it.
-template <int NT, int PER>
-__device__ __forceinline__ int64_t emit_kept(const uint32_t *keys, const int32_t *idx,
+template <int NT, int PER, typename KeyPtr, typename IdxPtr>
+__device__ __forceinline__ int64_t emit_kept(KeyPtr keys, IdxPtr idx,
                                              int64_t n, uint32_t theta, int64_t need,
                                              int32_t *out_idx, uint32_t *out_key, int64_t cap,
-                                             int64_t *scan_sh, uint32_t *group_cnt,
+                                             int32_t *scan_sh, uint32_t *group_cnt,
                                              int group, int32_t idx_base = 0) {
     const int tid = threadIdx.x;
     int64_t run_eq = 0, run_sel = 0;
@@ -268,8 +328,8 @@ __device__ __forceinline__ int64_t emit_kept(const uint32_t *keys, const int32_t
             kk[e] = valid ? keys[i0 + e] : 0u;
             n_eq += (valid && kk[e] == theta);
         }
-        int64_t tot_eq;
-        int64_t eq_run = run_eq + block_excl_scan<int64_t, NT>(n_eq, scan_sh, &tot_eq);
+        int32_t tot_eq;
+        int64_t eq_run = run_eq + block_excl_scan_i32<NT>(n_eq, scan_sh, &tot_eq);
         int n_take = 0;
         uint32_t take_mask = 0;
 #pragma unroll
@@ -280,8 +340,8 @@ __device__ __forceinline__ int64_t emit_kept(const uint32_t *keys, const int32_t
             eq_run += eq;
             if (take) { take_mask |= 1u << e; ++n_take; }
         }
-        int64_t tot_take;
-        int64_t pos = run_sel + block_excl_scan<int64_t, NT>(n_take, scan_sh, &tot_take);
+        int32_t tot_take;
+        int64_t pos = run_sel + block_excl_scan_i32<NT>(n_take, scan_sh, &tot_take);
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             if (take_mask & (1u << e)) {

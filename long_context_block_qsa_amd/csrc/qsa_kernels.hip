@@ -69,6 +69,26 @@ prep_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, 
 constexpr int CMP_NT = 256;
 constexpr int CMP_BLOCKS_PER_WG = CMP_NT / 8;
 
+// Dims 8c .. 8c+7 of block `blk` of the sequence starting at key row k0 and block row
+// blk0: exact (double) sum of the 4 token keys, rounded once to bf16.
+__device__ __forceinline__ void compress_one(const uint16_t *__restrict__ k_idx,
+                                             uint16_t *__restrict__ k_blk, int64_t k0,
+                                             int64_t blk0, int64_t blk, int c) {
+    const uint16_t *src = k_idx + (k0 + blk * BS) * DI + c * 8;
+    const u32x4 r0 = load16(src), r1 = load16(src + DI), r2 = load16(src + 2 * DI),
+                r3 = load16(src + 3 * DI);
+    u32x4 out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const double s_lo = (((double)bf16_lo(r0[q]) + (double)bf16_lo(r1[q])) +
+                             (double)bf16_lo(r2[q])) + (double)bf16_lo(r3[q]);
+        const double s_hi = (((double)bf16_hi(r0[q]) + (double)bf16_hi(r1[q])) +
+                             (double)bf16_hi(r2[q])) + (double)bf16_hi(r3[q]);
+        out[q] = f64_to_bf16_rne(s_lo) | (f64_to_bf16_rne(s_hi) << 16);
+    }
+    *reinterpret_cast<u32x4 *>(k_blk + (blk0 + blk) * DI + c * 8) = out;
+}
+
 __global__ void __launch_bounds__(CMP_NT)
 compress_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
                 const uint16_t *__restrict__ k_idx, uint16_t *__restrict__ k_blk,
@@ -97,20 +117,7 @@ compress_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu
 
     const int64_t blk = first + threadIdx.x / 8;
     if (blk >= nblk) return;
-    const int c = threadIdx.x % 8;
-    const uint16_t *src = k_idx + ((int64_t)k0 + blk * BS) * DI + c * 8;
-    const u32x4 r0 = load16(src), r1 = load16(src + DI), r2 = load16(src + 2 * DI),
-                r3 = load16(src + 3 * DI);
-    u32x4 out;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const double s_lo = (((double)bf16_lo(r0[q]) + (double)bf16_lo(r1[q])) +
-                             (double)bf16_lo(r2[q])) + (double)bf16_lo(r3[q]);
-        const double s_hi = (((double)bf16_hi(r0[q]) + (double)bf16_hi(r1[q])) +
-                             (double)bf16_hi(r2[q])) + (double)bf16_hi(r3[q]);
-        out[q] = f64_to_bf16_rne(s_lo) | (f64_to_bf16_rne(s_hi) << 16);
-    }
-    *reinterpret_cast<u32x4 *>(k_blk + (blk0 + blk) * DI + c * 8) = out;
+    compress_one(k_idx, k_blk, k0, blk0, blk, threadIdx.x % 8);
 }
 
 // =============================================================== scoring core
@@ -140,33 +147,42 @@ __device__ __forceinline__ TileInfo tile_info(const SeqInfo *tab, int batch, int
     return ti;
 }
 
+// RowView of query row r from the per-sequence table.
+__device__ __forceinline__ RowView tab_row(const SeqInfo *tab, int batch, int topk, int64_t r) {
+    const int sb = find_seq(batch, r, [&](int i) { return (int64_t)tab[i].q0; });
+    const SeqInfo s = tab[sb];
+    RowView v;
+    v.k0 = s.k0;
+    v.t = (int64_t)s.L - s.nq + (r - s.q0);
+    v.blk0 = s.blk0;
+    v.slot = s.s0 + slots_before(v.t) - slots_before(first_scored_pos(s.L, s.nq, topk));
+    return v;
+}
+
 struct ScoreLane {
     u32x4 qa[2];
     float wr[HI];
     int64_t slot, nv_row;
 };
 
-__device__ __forceinline__ ScoreLane score_lane_setup(const TileInfo &ti,
-                                                      const uint16_t *__restrict__ q_idx,
-                                                      const float *__restrict__ w) {
+// Operands of a tile of nrows query rows starting at row0 (position t0); slot_g is
+// the first score slot of this lane's output row (row0 + lane/16), if it exists.
+__device__ __forceinline__ ScoreLane score_lane_setup(const uint16_t *__restrict__ q_idx,
+                                                      const float *__restrict__ w,
+                                                      int64_t row0, int nrows, int64_t t0,
+                                                      int64_t slot_g) {
     ScoreLane sl;
     const int l = lane_id(), g = l >> 4, c = l & 15;
     const int rr = c >> 2, hh = c & 3;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
-        sl.qa[m] = rr < ti.nrows
-            ? load16(q_idx + ((ti.row0 + rr) * HI + hh) * DI + 32 * m + 8 * g)
-            : u32x4{0u, 0u, 0u, 0u};
+        sl.qa[m] = load16(q_idx + ((row0 + min(rr, nrows - 1)) * HI + hh) * DI + 32 * m + 8 * g);
+    if (rr >= nrows) sl.qa[0] = sl.qa[1] = u32x4{0u, 0u, 0u, 0u};
+    const int gg = min(g, nrows - 1);
 #pragma unroll
-    for (int h = 0; h < HI; ++h) sl.wr[h] = 0.f;
-    sl.slot = 0;
-    sl.nv_row = 0;
-    if (g < ti.nrows) {
-#pragma unroll
-        for (int h = 0; h < HI; ++h) sl.wr[h] = w[(ti.row0 + g) * HI + h];
-        sl.slot = ti.s.s0 + slots_before(ti.t0 + g) - slots_before(ti.ts);
-        sl.nv_row = nvis_of(ti.t0 + g);
-    }
+    for (int h = 0; h < HI; ++h) sl.wr[h] = g < nrows ? w[(row0 + gg) * HI + h] : 0.f;
+    sl.slot = g < nrows ? slot_g : 0;
+    sl.nv_row = g < nrows ? nvis_of(t0 + g) : 0;
     return sl;
 }
 
@@ -204,7 +220,7 @@ constexpr int SCORE_BATCH = 8;  // 16-block groups per wave in flight
 constexpr int SCORE_NT = 256;
 
 // Whole rows: grid x = tile, y = chunk of `chunk_blocks` blocks.
-__global__ void __launch_bounds__(SCORE_NT)
+__global__ void __launch_bounds__(SCORE_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
              const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
              const uint16_t *__restrict__ k_blk, uint32_t *__restrict__ keys,
@@ -213,7 +229,10 @@ score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
     const int64_t lo = (int64_t)blockIdx.y * chunk_blocks;
     const int64_t hi = min<int64_t>(ti.nv_max, lo + chunk_blocks);
     if (lo >= hi) return;
-    const ScoreLane sl = score_lane_setup(ti, q_idx, w);
+    const int g = lane_id() >> 4;
+    const ScoreLane sl = score_lane_setup(
+        q_idx, w, ti.row0, ti.nrows, ti.t0,
+        ti.s.s0 + slots_before(ti.t0 + g) - slots_before(ti.ts));
     const uint16_t *kb = k_blk + (int64_t)ti.s.blk0 * DI;
     const int c = lane_id() & 15;
     constexpr int64_t step = 16 * (SCORE_NT / WAVE);
@@ -244,24 +263,48 @@ __device__ __forceinline__ bool cand_eligible(int64_t nv, int topk, int ch) {
     return nv > topk && (nv / ch) * KP >= topk;
 }
 
-__global__ void __launch_bounds__(LOC_NT)
-score_local_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
-                   const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
-                   const uint16_t *__restrict__ k_blk, uint32_t *__restrict__ keys,
-                   uint32_t *__restrict__ cand_key, int32_t *__restrict__ cand_idx,
-                   int ch, int max_chunks) {
+struct LocalArgs {
+    int topk;
+    const uint16_t *q_idx;
+    const float *w;
+    const uint16_t *k_idx;   // not null: compress each tile's new blocks first
+    uint16_t *k_blk;
+    uint32_t *keys;
+    uint32_t *cand_key;
+    int32_t *cand_idx;
+    int ch, max_chunks;
+};
+
+// 4 waves per SIMD: the whole decode grid (rows x chunks) is resident at once
+__global__ void __launch_bounds__(LOC_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
+score_local_kernel(LocalArgs a, DecodeTables d) {
     __shared__ uint32_t lk[4][LOC_MAX_CH];
-    __shared__ uint32_t hist[256];
-    __shared__ int64_t scan_sh[LOC_NT / WAVE + 1];
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ int32_t scan_sh[LOC_NT / WAVE];
     __shared__ uint32_t found[2];
 
-    const TileInfo ti = tile_info(tab, batch, topk, blockIdx.x);
-    const int64_t lo = (int64_t)blockIdx.y * ch;
-    const int64_t hi = min<int64_t>(ti.nv_max, lo + ch);
+    const DecTile tl = d.tile[blockIdx.x];
+    const int64_t row0 = tl.row0;
+    const int nrows = tl.nrows;
+    const int64_t t0 = d.row[row0].t;
+    const int64_t lo = (int64_t)blockIdx.y * a.ch;
+    const int64_t hi = min<int64_t>(nvis_of(t0 + nrows - 1), lo + a.ch);
     if (lo >= hi) return;
-    const ScoreLane sl = score_lane_setup(ti, q_idx, w);
-    const uint16_t *kb = k_blk + (int64_t)ti.s.blk0 * DI;
     const int l = lane_id(), g = l >> 4, c = l & 15;
+    // blocks of this sequence that hold a query token are (re)compressed here first,
+    // by every workgroup whose chunk contains them (identical values)
+    if (a.k_idx && tl.new_hi > tl.new_lo) {
+        const int64_t c_lo = max<int64_t>(lo, tl.new_lo), c_hi = min<int64_t>(hi, tl.new_hi);
+        const int64_t blk = c_lo + threadIdx.x / 8;
+        if (blk < c_hi)
+            compress_one(a.k_idx, a.k_blk, d.row[row0].k0, d.row[row0].blk0, blk,
+                         threadIdx.x % 8);
+        __threadfence_block();
+        __syncthreads();
+    }
+    const ScoreLane sl = score_lane_setup(a.q_idx, a.w, row0, nrows, t0,
+                                          d.row[row0 + min(g, nrows - 1)].slot);
+    const uint16_t *kb = a.k_blk + (int64_t)d.row[row0].blk0 * DI;
     constexpr int64_t step = 16 * (LOC_NT / WAVE);
     for (int64_t b0 = lo + 16 * (threadIdx.x / WAVE); b0 < hi; b0 += step * SCORE_BATCH) {
         uint32_t key[SCORE_BATCH];
@@ -270,27 +313,28 @@ score_local_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
         for (int u = 0; u < SCORE_BATCH; ++u) {
             const int64_t blk = b0 + u * step + c;
             if (blk < hi && blk < sl.nv_row) {
-                keys[sl.slot + blk] = key[u];
+                a.keys[sl.slot + blk] = key[u];
                 lk[g][blk - lo] = key[u];
             }
         }
     }
     __syncthreads();
 
-    for (int rr = 0; rr < ti.nrows; ++rr) {
-        const int64_t t = ti.t0 + rr;
-        const int64_t nv = nvis_of(t);
-        if (!cand_eligible(nv, topk, ch)) continue;       // uniform over the workgroup
-        const int64_t n = min<int64_t>(nv, hi) - lo;      // this row's blocks in the chunk
-        uint32_t *ck = cand_key + ((ti.row0 + rr) * max_chunks + blockIdx.y) * KP;
-        int32_t *ci = cand_idx + ((ti.row0 + rr) * max_chunks + blockIdx.y) * KP;
+    for (int rr = 0; rr < nrows; ++rr) {
+        const int64_t nv = nvis_of(t0 + rr);
+        if (!cand_eligible(nv, a.topk, a.ch)) continue;   // uniform over the workgroup
+        const int64_t n = min<int64_t>(nv, hi) - lo;       // this row's blocks in the chunk
+        uint32_t *ck = a.cand_key + ((row0 + rr) * a.max_chunks + blockIdx.y) * KP;
+        int32_t *ci = a.cand_idx + ((row0 + rr) * a.max_chunks + blockIdx.y) * KP;
         int64_t kept = 0;
         if (n > KP) {
             uint32_t theta;
             int64_t need;
-            radix_kth<LOC_NT>(lk[rr], n, KP, kNarrow, hist, scan_sh, found, &theta, &need);
-            kept = emit_kept<LOC_NT, 4>(lk[rr], nullptr, n, theta, need, ci, ck, KP, scan_sh,
-                                        nullptr, 1, (int32_t)lo);
+            radix_kth<LOC_NT>((const uint32_t *)lk[rr], n, KP, kWide, hist, scan_sh, found,
+                              &theta, &need);
+            kept = emit_kept<LOC_NT, 4>((const uint32_t *)lk[rr], (const int32_t *)nullptr, n,
+                                        theta, need, ci, ck, KP, scan_sh, nullptr, 1,
+                                        (int32_t)lo);
         } else if (n > 0) {
             if (threadIdx.x < n) {
                 ck[threadIdx.x] = lk[rr][threadIdx.x];
@@ -330,7 +374,7 @@ struct SelectArgs {
 // address space), ids from `ii` (or positions), written to out in ascending order.
 template <int PER, typename KP_T, typename IP_T>
 __device__ __forceinline__ void select_keys(KP_T kk, IP_T ii, int64_t n, int topk,
-                                            int32_t *out, uint32_t *hist, int64_t *scan_sh,
+                                            int32_t *out, uint32_t *hist, int32_t *scan_sh,
                                             uint32_t *found, uint32_t *grp_cnt, int group,
                                             int64_t ngroups) {
     uint32_t theta;
@@ -343,18 +387,10 @@ __device__ __forceinline__ void select_keys(KP_T kk, IP_T ii, int64_t n, int top
     emit_kept<SEL_NT, PER>(kk, ii, n, theta, need, out, nullptr, topk, scan_sh, grp_cnt, group);
 }
 
-__global__ void __launch_bounds__(SEL_NT)
-select_kernel(SelectArgs a) {
-    extern __shared__ uint32_t dyn[];   // lds_cap words
-    __shared__ uint32_t hist[kHistBins];  // histograms; then per-chunk kept counts
-    __shared__ int64_t scan_sh[SEL_NT / WAVE + 1];
-    __shared__ uint32_t found[2];
-    __shared__ int viol;
-
-    const int64_t row = blockIdx.x;
-    const int sb = find_seq(a.batch, row, [&](int i) { return (int64_t)a.tab[i].q0; });
-    const SeqInfo s = a.tab[sb];
-    const int64_t t = (int64_t)s.L - s.nq + (row - s.q0);
+__device__ __forceinline__ void select_body(const SelectArgs &a, const RowView rv, int64_t row,
+                                            uint32_t *dyn, uint32_t *hist, int32_t *scan_sh,
+                                            uint32_t *found, int *viol) {
+    const int64_t t = rv.t;
     const int64_t nv = nvis_of(t);
     int32_t *out = a.sel + row * a.topk;
     const int tid = threadIdx.x;
@@ -370,13 +406,28 @@ select_kernel(SelectArgs a) {
         const uint32_t *ck = a.cand_key + row * a.max_chunks * KP;
         const int32_t *ci = a.cand_idx + row * a.max_chunks * KP;
         uint32_t *cnt = nchunk <= kHistBins ? hist : nullptr;
-        if (tid == 0) viol = 0;
+        if (tid == 0) *viol = 0;
         if (2 * n <= a.lds_cap) {
             uint32_t *lk = dyn;
             int32_t *li = reinterpret_cast<int32_t *>(dyn + n);
-            for (int64_t i = tid; i < n; i += SEL_NT) { lk[i] = ck[i]; li[i] = ci[i]; }
+            for (int64_t i0 = tid; i0 < n; i0 += 8 * SEL_NT) {   // 16 loads in flight
+                uint32_t kv[8];
+                int32_t iv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int64_t i = min<int64_t>(i0 + (int64_t)e * SEL_NT, n - 1);
+                    kv[e] = ck[i];
+                    iv[e] = ci[i];
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int64_t i = i0 + (int64_t)e * SEL_NT;
+                    if (i < n) { lk[i] = kv[e]; li[i] = iv[e]; }
+                }
+            }
             __syncthreads();
-            select_keys<8>(lk, li, n, a.topk, out, hist, scan_sh, found, cnt, KP, nchunk);
+            select_keys<8>((const uint32_t *)lk, (const int32_t *)li, n, a.topk, out, hist,
+                           scan_sh, found, cnt, KP, nchunk);
         } else {
             __syncthreads();
             select_keys<8>(ck, ci, n, a.topk, out, hist, scan_sh, found, cnt, KP, nchunk);
@@ -384,28 +435,24 @@ select_kernel(SelectArgs a) {
         __syncthreads();
         // a full chunk (more than KP blocks) with every candidate kept may hide more
         if (!cnt) {
-            if (tid == 0) viol = 1;   // cannot check: take the exact path
+            if (tid == 0) *viol = 1;   // cannot check: take the exact path
         } else {
             for (int64_t c = tid; c < nchunk; c += SEL_NT) {
                 const int64_t nc = min<int64_t>(a.ch, nv - c * a.ch);
-                if (nc > KP && cnt[c] >= (uint32_t)KP) viol = 1;
+                if (nc > KP && cnt[c] >= (uint32_t)KP) *viol = 1;
             }
         }
         __syncthreads();
-        if (!viol) return;
+        if (!*viol) return;
     }
 
     // exact selection over the full row of keys
-    const int64_t ts = first_scored_pos(s.L, s.nq, a.topk);
-    const uint32_t *rk = a.keys + s.s0 + slots_before(t) - slots_before(ts);
+    const uint32_t *rk = a.keys + rv.slot;
     if (nv <= a.lds_cap) {
         for (int64_t i0 = tid; i0 < nv; i0 += 8 * SEL_NT) {
             uint32_t v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t i = i0 + (int64_t)e * SEL_NT;
-                v[e] = i < nv ? rk[i] : 0u;
-            }
+            for (int e = 0; e < 8; ++e) v[e] = rk[min<int64_t>(i0 + (int64_t)e * SEL_NT, nv - 1)];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int64_t i = i0 + (int64_t)e * SEL_NT;
@@ -419,6 +466,30 @@ select_kernel(SelectArgs a) {
         select_keys<16>(rk, (const int32_t *)nullptr, nv, a.topk, out, hist, scan_sh, found,
                         nullptr, 1, 0);
     }
+}
+
+__global__ void __launch_bounds__(SEL_NT)
+select_kernel(SelectArgs a) {
+    extern __shared__ uint32_t dyn[];   // lds_cap words
+    __shared__ uint32_t hist[kHistBins];  // histograms; then per-chunk kept counts
+    __shared__ int32_t scan_sh[SEL_NT / WAVE];
+    __shared__ uint32_t found[2];
+    __shared__ int viol;
+    const int64_t row = blockIdx.x;
+    select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, dyn, hist, scan_sh, found, &viol);
+}
+
+__global__ void __launch_bounds__(SEL_NT)
+select_dec_kernel(SelectArgs a, DecodeTables d) {
+    extern __shared__ uint32_t dyn[];
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ int32_t scan_sh[SEL_NT / WAVE];
+    __shared__ uint32_t found[2];
+    __shared__ int viol;
+    const int64_t row = blockIdx.x;
+    const DecRow r = d.row[row];
+    const RowView rv = {r.k0, r.t, r.blk0, r.slot};
+    select_body(a, rv, row, dyn, hist, scan_sh, found, &viol);
 }
 
 // =============================================================== attend
@@ -464,17 +535,9 @@ struct KVTile {
     uint32_t valid;  // bit 4u+i: key j0 + 16u + 4gr + i is attended
 };
 
-__global__ void __launch_bounds__(ATT_NT)
-attend_kernel(AttnArgs a) {
-    const int64_t item = (int64_t)blockIdx.x * (ATT_NT / WAVE) + threadIdx.x / WAVE;
-    const int64_t row = item / (HKV * a.nsplit);
-    if (row >= a.nrows) return;
-    const int rem = (int)(item % (HKV * a.nsplit));
-    const int g = rem / a.nsplit, sp = rem % a.nsplit;
-
-    const int sb = find_seq(a.batch, row, [&](int i) { return (int64_t)a.tab[i].q0; });
-    const SeqInfo s = a.tab[sb];
-    const int64_t t = (int64_t)s.L - s.nq + (row - s.q0);
+__device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv, int64_t row,
+                                            int g, int sp) {
+    const int64_t t = rv.t;
     const int64_t nv = nvis_of(t);
     const int ntail = (int)(t + 1 - BS * nv);
     const int32_t *srow = a.sel + row * a.topk;
@@ -482,15 +545,13 @@ attend_kernel(AttnArgs a) {
 
     // number of leading selected entries: 8 unconditional loads in flight, then ballots
     int nsel = a.topk;
-    {
-        int32_t v[KMAX / WAVE];
+    int32_t v[KMAX / WAVE];
 #pragma unroll
-        for (int j = 0; j < KMAX / WAVE; ++j) v[j] = srow[min(64 * j + l, a.topk - 1)];
+    for (int j = 0; j < KMAX / WAVE; ++j) v[j] = srow[min(64 * j + l, a.topk - 1)];
 #pragma unroll
-        for (int j = KMAX / WAVE - 1; j >= 0; --j) {
-            const unsigned long long bal = __ballot(64 * j + l < a.topk && v[j] < 0);
-            if (bal) nsel = 64 * j + __builtin_ctzll(bal);
-        }
+    for (int j = KMAX / WAVE - 1; j >= 0; --j) {
+        const unsigned long long bal = __ballot(64 * j + l < a.topk && v[j] < 0);
+        if (bal) nsel = 64 * j + __builtin_ctzll(bal);
     }
     const int nslot = nsel + (ntail > 0 ? 1 : 0);
     const int npos = 4 * nslot;
@@ -511,7 +572,7 @@ attend_kernel(AttnArgs a) {
     for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int64_t kv0 = (int64_t)s.k0;
+    const int64_t kv0 = rv.k0;
     const int64_t safe_tok = kv0 + t;  // always a valid key row
     const uint16_t *kbase = a.k + g * HD;
     const uint16_t *vbase = a.v + g * HD;
@@ -560,7 +621,10 @@ attend_kernel(AttnArgs a) {
     auto group_ids = [=](int grp) -> int32_t { return srow[min(64 * grp + l, a.topk - 1)]; };
 
     int cur_grp = p_lo >> 8;  // 64 slots = 256 key positions per group
-    int32_t cur = group_ids(cur_grp);
+    int32_t cur = v[0];
+#pragma unroll
+    for (int j = 1; j < KMAX / WAVE; ++j)
+        if (cur_grp == j) cur = v[j];
     KVTile nxt;
     if (p_lo < p_hi) nxt = load_tile(p_lo, cur);
     for (int j0 = p_lo; j0 < p_hi; j0 += 32) {
@@ -655,6 +719,35 @@ attend_kernel(AttnArgs a) {
     }
 }
 
+// wave -> (row, kv head, split)
+__device__ __forceinline__ bool attend_item(const AttnArgs &a, int64_t &row, int &g, int &sp) {
+    const int64_t item = __builtin_amdgcn_readfirstlane(
+        (int)((int64_t)blockIdx.x * (ATT_NT / WAVE) + threadIdx.x / WAVE));
+    row = item / (HKV * a.nsplit);
+    const int rem = (int)(item % (HKV * a.nsplit));
+    g = rem / a.nsplit;
+    sp = rem % a.nsplit;
+    return row < a.nrows;
+}
+
+__global__ void __launch_bounds__(ATT_NT)
+attend_kernel(AttnArgs a) {
+    int64_t row;
+    int g, sp;
+    if (!attend_item(a, row, g, sp)) return;
+    attend_body(a, tab_row(a.tab, a.batch, a.topk, row), row, g, sp);
+}
+
+__global__ void __launch_bounds__(ATT_NT)
+attend_dec_kernel(AttnArgs a, DecodeTables d) {
+    int64_t row;
+    int g, sp;
+    if (!attend_item(a, row, g, sp)) return;
+    const DecRow r = d.row[row];
+    const RowView rv = {r.k0, r.t, r.blk0, r.slot};
+    attend_body(a, rv, row, g, sp);
+}
+
 // =============================================================== combine
 // One wave per (row, head): lane s reads split s's (m, l); the merged output is the
 // weighted sum of the split accumulators in split order (deterministic).
@@ -735,15 +828,17 @@ hipError_t launch_score(const SeqInfo *tab, int batch, int topk, const uint16_t 
     return trace_after(st, hipGetLastError());
 }
 
-hipError_t launch_score_local(const SeqInfo *tab, int batch, int topk, const uint16_t *q_idx,
-                              const float *w, const uint16_t *k_blk, uint32_t *keys,
-                              uint32_t *cand_key, int32_t *cand_idx, int64_t n_tiles,
-                              int ch, int max_chunks, hipStream_t st) {
+hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
+                              const uint16_t *q_idx, const float *w, const uint16_t *k_idx,
+                              uint16_t *k_blk, uint32_t *keys, uint32_t *cand_key,
+                              int32_t *cand_idx, int ch, int max_chunks, hipStream_t st) {
     if (n_tiles <= 0) return hipSuccess;
+    LocalArgs a;
+    a.topk = topk; a.q_idx = q_idx; a.w = w; a.k_idx = k_idx; a.k_blk = k_blk; a.keys = keys;
+    a.cand_key = cand_key; a.cand_idx = cand_idx; a.ch = ch; a.max_chunks = max_chunks;
     trace_before(2, st);
     hipLaunchKernelGGL(score_local_kernel, dim3((unsigned)n_tiles, (unsigned)max_chunks),
-                       dim3(LOC_NT), 0, st, tab, batch, topk, q_idx, w, k_blk, keys, cand_key,
-                       cand_idx, ch, max_chunks);
+                       dim3(LOC_NT), 0, st, a, d);
     return trace_after(st, hipGetLastError());
 }
 
@@ -764,9 +859,9 @@ int64_t select_lds_cap_keys() {
     return cap;
 }
 
-hipError_t launch_select(const SeqInfo *tab, int batch, int topk, const uint32_t *keys,
-                         const uint32_t *cand_key, const int32_t *cand_idx, int ch,
-                         int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
+hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
+                         const uint32_t *keys, const uint32_t *cand_key, const int32_t *cand_idx,
+                         int ch, int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
                          hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
     SelectArgs a;
@@ -778,18 +873,21 @@ hipError_t launch_select(const SeqInfo *tab, int batch, int topk, const uint32_t
     if (ch > 0) want = want > 2 * (int64_t)max_chunks * KP ? want : 2 * (int64_t)max_chunks * KP;
     a.lds_cap = want < cap ? want : cap;
     const size_t shmem = (size_t)a.lds_cap * 4;
+    const void *fn = d ? (const void *)select_dec_kernel : (const void *)select_kernel;
     if (shmem > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void *)select_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
         if (e != hipSuccess) return e;
     }
     trace_before(3, st);
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), shmem, st, a);
+    if (d)
+        hipLaunchKernelGGL(select_dec_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), shmem, st, a, *d);
+    else
+        hipLaunchKernelGGL(select_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), shmem, st, a);
     return trace_after(st, hipGetLastError());
 }
 
-hipError_t launch_attend(const SeqInfo *tab, int batch, int topk, float scale,
-                         const uint16_t *q, const uint16_t *k, const uint16_t *v,
+hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
+                         float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const int32_t *sel, float *out, float *lse, float *part, int nsplit,
                          int64_t n_rows, hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
@@ -801,7 +899,10 @@ hipError_t launch_attend(const SeqInfo *tab, int batch, int topk, float scale,
     const int64_t waves = n_rows * HKV * nsplit;
     const int64_t wgs = (waves + ATT_NT / WAVE - 1) / (ATT_NT / WAVE);
     trace_before(4, st);
-    hipLaunchKernelGGL(attend_kernel, dim3((unsigned)wgs), dim3(ATT_NT), 0, st, a);
+    if (d)
+        hipLaunchKernelGGL(attend_dec_kernel, dim3((unsigned)wgs), dim3(ATT_NT), 0, st, a, *d);
+    else
+        hipLaunchKernelGGL(attend_kernel, dim3((unsigned)wgs), dim3(ATT_NT), 0, st, a);
     hipError_t e = trace_after(st, hipGetLastError());
     if (e != hipSuccess || nsplit == 1) return e;
     const int64_t cw = (n_rows * HQ + CMB_NT / WAVE - 1) / (CMB_NT / WAVE);

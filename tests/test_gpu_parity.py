@@ -179,12 +179,17 @@ def test_decode_equals_last_prefill_row():
     assert errs(out_d[0], out_p[-1])[0] < 1e-5 and errs(lse_d[0], lse_p[-1])[0] < 1e-5
 
 
-def test_incremental_compress_completes_cache():
+@pytest.mark.parametrize("lens,q_lens,topk", [
+    ([4096, 1203, 8], [1, 7, 8], 512),   # some sequences have no scored row
+    ([4096, 3000, 2052], [1, 2, 5], 64),  # every sequence scored: fused into scoring
+])
+def test_incremental_compress_completes_cache(lens, q_lens, topk):
     """forward() with k_idx recompresses only the blocks holding query tokens; with a
-    cache built by compress() for the rest, the result equals a full compress."""
-    _banner("incremental compress")
-    p = gen.make_problem([4096, 1203, 8], q_lens=[1, 7, 8], seed=11)
-    dp = DeviceProblem(p, 512)
+    cache built by compress() for the rest, the result equals a full compress and the
+    selection and outputs match the oracle."""
+    _banner(f"incremental compress lens={lens} q_lens={q_lens}")
+    p = gen.make_problem(lens, q_lens=q_lens, seed=11)
+    dp = DeviceProblem(p, topk)
     full = dp.compress()
     dp.k_blk.zero_()
     # rebuild the prefix cache only: blocks before each sequence's first query token
@@ -193,15 +198,16 @@ def test_incremental_compress_completes_cache():
     assert np.array_equal(full, ref)
     pref = ref.copy()
     nb0 = 0
-    for b in range(3):
+    for b in range(len(lens)):
         L = int(p.cu_k[b + 1] - p.cu_k[b])
         nq = int(p.cu_q[b + 1] - p.cu_q[b])
         first_new = (L - nq) // 4
         pref[nb0 + first_new: nb0 + L // 4] = 0x7FC0  # garbage where forward must write
         nb0 += L // 4
     dp.k_blk.copy_(torch.from_numpy(pref.view(np.int16)).cuda())
-    k_blk, _, _, _ = dp.forward(with_k_idx=True)
-    assert np.array_equal(k_blk, ref)
+    gpu = dp.forward(with_k_idx=True)
+    assert np.array_equal(gpu[0], ref)
+    _check_rows(f"incremental{lens}", dp, None, topk, gpu=gpu)
 
 
 def test_select_and_attend_entry_points():
