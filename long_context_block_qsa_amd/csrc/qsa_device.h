@@ -359,6 +359,280 @@ __device__ __forceinline__ int64_t emit_kept(KeyPtr keys, IdxPtr idx,
     return run_sel;
 }
 
+// ---------------------------------------------------------------- wave-level select
+
+// Workgroup barrier that orders LDS only (outstanding global stores are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Orders this wave's LDS accesses (lanes exchange data through LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d));
+    return v;
+}
+
+// Lanes below this one in a ballot mask.
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// One wave finds the k-th largest of the keys it holds in registers: lane j holds
+// positions PER*j .. PER*j+PER-1, of which those below n are valid (1 <= k <= n).
+// Radix select with 8-bit digits that starts at the highest bit where the keys
+// differ, a wave-private 256-bin LDS histogram, no workgroup barrier. Returns theta
+// and `need`, the number of keys equal to theta among the k largest (ties go to the
+// lowest positions).
+template <int PER>
+__device__ __forceinline__ void wave_kth_regs(const uint32_t (&x)[PER], int n, int k,
+                                              uint32_t *__restrict__ hist, uint32_t *theta_out,
+                                              int *need_out) {
+    const int l = lane_id();
+    uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        if (PER * l + e < n) {
+            mx = max(mx, x[e]);
+            mn = min(mn, x[e]);
+        }
+    }
+    mx = wave_max_u32(mx);
+    mn = wave_min_u32(mn);
+    const uint32_t diff = mx ^ mn;
+    int hb = diff ? 32 - __builtin_clz(diff) : 0;  // low bits that vary
+    uint32_t pmask = hb >= 32 ? 0u : ~((1u << hb) - 1u);
+    uint32_t prefix = mx & pmask;
+    int need = k;
+    while (hb > 0) {
+        const int shift = hb > 8 ? hb - 8 : 0;
+        const int nb = 1 << (hb - shift);
+        const uint32_t dmask = (uint32_t)nb - 1u;
+        for (int i = l; i < nb; i += WAVE) hist[i] = 0u;
+        wave_lds_sync();
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            if (PER * l + e < n && (x[e] & pmask) == prefix)
+                atomicAdd(&hist[(x[e] >> shift) & dmask], 1u);
+        wave_lds_sync();
+        // lane j owns the 4 bins ending at nb - 4j (highest bins first)
+        const int top = nb - 4 * l;
+        uint32_t h[4];
+        int local = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = top - 1 - i;
+            h[i] = b >= 0 ? hist[b] : 0u;
+            local += (int)h[i];
+        }
+        const int above = wave_incl_scan_i32(local) - local;
+        const bool cross = above < need && need <= above + local;
+        const unsigned long long bal = __ballot(cross);
+        int digit = 0, run = above;
+        if (cross) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (run + (int)h[i] >= need) { digit = top - 1 - i; break; }
+                run += (int)h[i];
+            }
+        }
+        const int src = (int)__builtin_ctzll(bal);
+        digit = __builtin_amdgcn_readlane(digit, src);
+        run = __builtin_amdgcn_readlane(run, src);
+        need -= run;
+        prefix |= (uint32_t)digit << shift;
+        pmask |= dmask << shift;
+        hb = shift;
+        wave_lds_sync();
+    }
+    *theta_out = prefix;
+    *need_out = need;
+}
+
+// Ordered pass after wave_kth_regs: keeps keys above theta and the first `need` keys
+// equal to it (lowest positions). Each lane marks its kept elements in `kept_mask`
+// (bit e) and gets the output slot of its first kept element; returns the total kept.
+template <int PER>
+__device__ __forceinline__ int wave_keep_regs(const uint32_t (&x)[PER], int n, uint32_t theta,
+                                              int need, uint32_t *kept_mask, int *first_pos,
+                                              int *n_kept) {
+    const int l = lane_id();
+    int n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) n_eq += (PER * l + e < n && x[e] == theta);
+    int eq_run = wave_incl_scan_i32(n_eq) - n_eq;
+    uint32_t mask = 0;
+    int nt = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const bool valid = PER * l + e < n;
+        const bool eq = valid && x[e] == theta;
+        const bool take = (valid && x[e] > theta) || (eq && eq_run < need);
+        eq_run += eq;
+        if (take) { mask |= 1u << e; ++nt; }
+    }
+    const int incl = wave_incl_scan_i32(nt);
+    *kept_mask = mask;
+    *first_pos = incl - nt;
+    *n_kept = nt;
+    return __builtin_amdgcn_readlane(incl, WAVE - 1);
+}
+
+// ---------------------------------------------------------------- block top-k (registers)
+
+// LDS of block_topk_regs.
+struct TopkSmem {
+    uint32_t hist[256];
+    uint32_t red[2][16];
+    int32_t scan[16];
+    int32_t found[4];
+    uint32_t bin_key[64];
+    int32_t bin_pos[64];
+    uint32_t take_bits[64];   // bit p: position p of the final bin is kept (n <= 2048)
+};
+
+// Top-k of n keys (1 <= k <= n <= 2048) that the NT threads of a workgroup hold in
+// registers: thread t holds positions PER*t .. PER*t+PER-1 (positions >= n are
+// ignored). Order: key descending, equal keys by ascending position. Sets bit e of
+// *kept when position PER*t+e is among the k, and *first to this thread's rank
+// among kept positions (kept positions ordered by position); returns k.
+// Method: an 8-bit histogram of the highest bits where the keys differ finds the
+// bin that holds the k-th key; bins above it are kept whole. When that bin holds at
+// most 64 keys they are ranked exactly by one wave (all pairs); otherwise the bin is
+// refined with the next 8 bits, down to single key values, where equal keys are
+// kept by position.
+template <int NT, int PER>
+__device__ __forceinline__ int block_topk_regs(const uint32_t (&x)[PER], int n, int k,
+                                               TopkSmem &sm, uint32_t *kept, int *first) {
+    static_assert(NT == 256, "one histogram bin per thread");
+    constexpr int NW = NT / WAVE;
+    const int tid = threadIdx.x, l = lane_id(), w = tid / WAVE;
+
+    // common high bits of all valid keys
+    uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+        if (PER * tid + e < n) { mx = max(mx, x[e]); mn = min(mn, x[e]); }
+    mx = wave_max_u32(mx);
+    mn = wave_min_u32(mn);
+    if (l == 0) { sm.red[0][w] = mx; sm.red[1][w] = mn; }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) { mx = max(mx, sm.red[0][i]); mn = min(mn, sm.red[1][i]); }
+    const uint32_t diff = mx ^ mn;
+    int hb = diff ? 32 - __builtin_clz(diff) : 0;
+    uint32_t pmask = hb >= 32 ? 0u : ~((1u << hb) - 1u);
+    uint32_t prefix = mx & pmask;
+    int need = k;
+    int mode = 0;   // 1: keep the whole final bin, 2: ranked bitmap, 3: equal keys by position
+
+    while (true) {
+        if (hb == 0) { mode = 3; break; }            // the final bin is one key value
+        const int shift = hb > 8 ? hb - 8 : 0;
+        const int nb = 1 << (hb - shift);
+        const uint32_t dmask = (uint32_t)nb - 1u;
+        if (tid < nb) sm.hist[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            if (PER * tid + e < n && (x[e] & pmask) == prefix)
+                atomicAdd(&sm.hist[(x[e] >> shift) & dmask], 1u);
+        __syncthreads();
+        const int bin = nb - 1 - tid;                 // thread t owns bin nb-1-t
+        const int local = tid < nb ? (int)sm.hist[bin] : 0;
+        int tot;
+        const int above = block_excl_scan_i32<NT>(local, sm.scan, &tot);
+        if (tid < nb && above < need && need <= above + local) {
+            sm.found[0] = bin;
+            sm.found[1] = above;
+            sm.found[2] = local;
+        }
+        __syncthreads();
+        const int T = sm.found[0], A = sm.found[1], m = sm.found[2];
+        need -= A;
+        prefix |= (uint32_t)T << shift;
+        pmask |= dmask << shift;
+        hb = shift;
+        __syncthreads();
+        if (m == need) { mode = 1; break; }
+        if (m <= 64) { mode = 2; break; }
+    }
+
+    if (mode == 2) {
+        // compact the final bin's keys in position order, rank them in one wave
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) c += (PER * tid + e < n && (x[e] & pmask) == prefix);
+        int tot;
+        int off = block_excl_scan_i32<NT>(c, sm.scan, &tot);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            if (PER * tid + e < n && (x[e] & pmask) == prefix) {
+                sm.bin_key[off] = x[e];
+                sm.bin_pos[off] = PER * tid + e;
+                ++off;
+            }
+        }
+        for (int i = tid; i < 64; i += NT) sm.take_bits[i] = 0u;
+        __syncthreads();
+        if (w == 0) {
+            const int m = tot;
+            const uint32_t kj = l < m ? sm.bin_key[l] : 0u;
+            const int pj = l < m ? sm.bin_pos[l] : 0;
+            int rank = 0;
+            for (int i = 0; i < m; ++i) {
+                const uint32_t ki = __builtin_amdgcn_readlane(kj, i);
+                const int pi = __builtin_amdgcn_readlane(pj, i);
+                rank += (ki > kj) || (ki == kj && pi < pj);
+            }
+            if (l < m && rank < need) atomicOr(&sm.take_bits[pj >> 5], 1u << (pj & 31));
+        }
+        __syncthreads();
+    }
+
+    // mode 3: among the (equal) keys of the final bin keep the first `need` by position
+    int eq_before = 0;
+    if (mode == 3) {
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) c += (PER * tid + e < n && (x[e] & pmask) == prefix);
+        int tot;
+        eq_before = block_excl_scan_i32<NT>(c, sm.scan, &tot);
+    }
+    uint32_t mask = 0u;
+    int nt = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int pos = PER * tid + e;
+        if (pos >= n) continue;
+        const uint32_t hi_bits = x[e] & pmask;
+        bool take = hi_bits > prefix;
+        if (hi_bits == prefix) {
+            if (mode == 1) take = true;
+            else if (mode == 2) take = (sm.take_bits[pos >> 5] >> (pos & 31)) & 1u;
+            else { take = eq_before < need; ++eq_before; }
+        }
+        if (take) { mask |= 1u << e; ++nt; }
+    }
+    int tot;
+    *first = block_excl_scan_i32<NT>(nt, sm.scan, &tot);
+    *kept = mask;
+    return tot;
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -279,9 +279,7 @@ struct LocalArgs {
 __global__ void __launch_bounds__(LOC_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 score_local_kernel(LocalArgs a, DecodeTables d) {
     __shared__ uint32_t lk[4][LOC_MAX_CH];
-    __shared__ uint32_t hist[kHistBins];
-    __shared__ int32_t scan_sh[LOC_NT / WAVE];
-    __shared__ uint32_t found[2];
+    __shared__ TopkSmem tsm;
 
     const DecTile tl = d.tile[blockIdx.x];
     const int64_t row0 = tl.row0;
@@ -318,35 +316,41 @@ score_local_kernel(LocalArgs a, DecodeTables d) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
+    // each tile row whose selection can come from chunk candidates gets this chunk's
+    // KP best (key, block) pairs, in ascending block order, padded with key 0
     for (int rr = 0; rr < nrows; ++rr) {
         const int64_t nv = nvis_of(t0 + rr);
         if (!cand_eligible(nv, a.topk, a.ch)) continue;   // uniform over the workgroup
-        const int64_t n = min<int64_t>(nv, hi) - lo;       // this row's blocks in the chunk
+        const int n = (int)(min<int64_t>(nv, hi) - lo);    // this row's blocks in the chunk
         uint32_t *ck = a.cand_key + ((row0 + rr) * a.max_chunks + blockIdx.y) * KP;
         int32_t *ci = a.cand_idx + ((row0 + rr) * a.max_chunks + blockIdx.y) * KP;
-        int64_t kept = 0;
+        int kept_total = n;
         if (n > KP) {
-            uint32_t theta;
-            int64_t need;
-            radix_kth<LOC_NT>((const uint32_t *)lk[rr], n, KP, kWide, hist, scan_sh, found,
-                              &theta, &need);
-            kept = emit_kept<LOC_NT, 4>((const uint32_t *)lk[rr], (const int32_t *)nullptr, n,
-                                        theta, need, ci, ck, KP, scan_sh, nullptr, 1,
-                                        (int32_t)lo);
-        } else if (n > 0) {
-            if (threadIdx.x < n) {
-                ck[threadIdx.x] = lk[rr][threadIdx.x];
-                ci[threadIdx.x] = (int32_t)(lo + threadIdx.x);
+            uint32_t x[4];
+            const u32x4 q4 = *reinterpret_cast<const u32x4 *>(&lk[rr][4 * threadIdx.x]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = q4[e];
+            uint32_t kept;
+            int first;
+            kept_total = block_topk_regs<LOC_NT, 4>(x, n, KP, tsm, &kept, &first);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (kept & (1u << e)) {
+                    ck[first] = x[e];
+                    ci[first] = (int32_t)(lo + 4 * threadIdx.x + e);
+                    ++first;
+                }
             }
-            kept = n;
+        } else if (threadIdx.x < n) {
+            ck[threadIdx.x] = lk[rr][threadIdx.x];
+            ci[threadIdx.x] = (int32_t)(lo + threadIdx.x);
         }
-        for (int64_t i = kept + threadIdx.x; i < KP; i += LOC_NT) {
-            ck[i] = 0u;
-            ci[i] = -1;
+        if (threadIdx.x < KP && (int)threadIdx.x >= kept_total) {
+            ck[threadIdx.x] = 0u;
+            ci[threadIdx.x] = -1;
         }
-        __syncthreads();
     }
 }
 
@@ -389,7 +393,7 @@ __device__ __forceinline__ void select_keys(KP_T kk, IP_T ii, int64_t n, int top
 
 __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView rv, int64_t row,
                                             uint32_t *dyn, uint32_t *hist, int32_t *scan_sh,
-                                            uint32_t *found, int *viol) {
+                                            uint32_t *found, int *viol, TopkSmem *tsm) {
     const int64_t t = rv.t;
     const int64_t nv = nvis_of(t);
     int32_t *out = a.sel + row * a.topk;
@@ -400,50 +404,45 @@ __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView r
         return;
     }
 
-    if (a.ch > 0 && cand_eligible(nv, a.topk, a.ch)) {
-        const int64_t nchunk = (nv + a.ch - 1) / a.ch;
-        const int64_t n = nchunk * KP;
-        const uint32_t *ck = a.cand_key + row * a.max_chunks * KP;
-        const int32_t *ci = a.cand_idx + row * a.max_chunks * KP;
-        uint32_t *cnt = nchunk <= kHistBins ? hist : nullptr;
+    if (a.ch > 0 && cand_eligible(nv, a.topk, a.ch) && (nv + a.ch - 1) / a.ch <= WAVE) {
+        // thread t holds candidate positions 8t .. 8t+7 (chunk t/4) in registers
+        const int nchunk = (int)((nv + a.ch - 1) / a.ch);
+        const int n = nchunk * KP;   // padding entries carry key 0, never kept
+        const int c = min(tid / 4, nchunk - 1), part = tid % 4;
+        const uint32_t *ck = a.cand_key + (row * a.max_chunks + c) * KP + 8 * part;
+        const int32_t *ci = a.cand_idx + (row * a.max_chunks + c) * KP + 8 * part;
+        uint32_t x[8];
+        int32_t id[8];
+#pragma unroll
+        for (int v4 = 0; v4 < 2; ++v4) {
+            const u32x4 kq = load16(ck + 4 * v4);
+            const u32x4 iq = load16(ci + 4 * v4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[4 * v4 + e] = kq[e];
+                id[4 * v4 + e] = (int32_t)iq[e];
+            }
+        }
         if (tid == 0) *viol = 0;
-        if (2 * n <= a.lds_cap) {
-            uint32_t *lk = dyn;
-            int32_t *li = reinterpret_cast<int32_t *>(dyn + n);
-            for (int64_t i0 = tid; i0 < n; i0 += 8 * SEL_NT) {   // 16 loads in flight
-                uint32_t kv[8];
-                int32_t iv[8];
+        uint32_t kept;
+        int first;
+        block_topk_regs<SEL_NT, 8>(x, n, a.topk, *tsm, &kept, &first);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int64_t i = min<int64_t>(i0 + (int64_t)e * SEL_NT, n - 1);
-                    kv[e] = ck[i];
-                    iv[e] = ci[i];
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int64_t i = i0 + (int64_t)e * SEL_NT;
-                    if (i < n) { lk[i] = kv[e]; li[i] = iv[e]; }
-                }
+        for (int e = 0; e < 8; ++e) {
+            if (kept & (1u << e)) {
+                if (first < a.topk) out[first] = id[e];
+                ++first;
             }
-            __syncthreads();
-            select_keys<8>((const uint32_t *)lk, (const int32_t *)li, n, a.topk, out, hist,
-                           scan_sh, found, cnt, KP, nchunk);
-        } else {
-            __syncthreads();
-            select_keys<8>(ck, ci, n, a.topk, out, hist, scan_sh, found, cnt, KP, nchunk);
         }
-        __syncthreads();
         // a full chunk (more than KP blocks) with every candidate kept may hide more
-        if (!cnt) {
-            if (tid == 0) *viol = 1;   // cannot check: take the exact path
-        } else {
-            for (int64_t c = tid; c < nchunk; c += SEL_NT) {
-                const int64_t nc = min<int64_t>(a.ch, nv - c * a.ch);
-                if (nc > KP && cnt[c] >= (uint32_t)KP) *viol = 1;
-            }
-        }
+        int kc = __popc(kept);
+        kc += __shfl_xor(kc, 1);
+        kc += __shfl_xor(kc, 2);
+        const int64_t nc = tid / 4 < nchunk ? min<int64_t>(a.ch, nv - (int64_t)(tid / 4) * a.ch) : 0;
+        if (nc > KP && kc >= KP) *viol = 1;
         __syncthreads();
         if (!*viol) return;
+        // otherwise the exact path below decides
     }
 
     // exact selection over the full row of keys
@@ -475,8 +474,10 @@ select_kernel(SelectArgs a) {
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
     __shared__ uint32_t found[2];
     __shared__ int viol;
+    __shared__ TopkSmem tsm;
     const int64_t row = blockIdx.x;
-    select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, dyn, hist, scan_sh, found, &viol);
+    select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, dyn, hist, scan_sh, found, &viol,
+                &tsm);
 }
 
 __global__ void __launch_bounds__(SEL_NT)
@@ -486,10 +487,11 @@ select_dec_kernel(SelectArgs a, DecodeTables d) {
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
     __shared__ uint32_t found[2];
     __shared__ int viol;
+    __shared__ TopkSmem tsm;
     const int64_t row = blockIdx.x;
     const DecRow r = d.row[row];
     const RowView rv = {r.k0, r.t, r.blk0, r.slot};
-    select_body(a, rv, row, dyn, hist, scan_sh, found, &viol);
+    select_body(a, rv, row, dyn, hist, scan_sh, found, &viol, &tsm);
 }
 
 // =============================================================== attend
