@@ -45,8 +45,12 @@
  *   status, enqueues nothing and leaves every output untouched. On success it
  *   enqueues its kernels on `stream` (a hipStream_t; NULL = the null stream) and
  *   returns; results are valid once the stream has reached that point. Outputs must
- *   not alias inputs. Workspace contents are undefined before and after a call.
- *   Calls on different streams must not share a workspace. The only mutable state is
+ *   not alias inputs. The workspace starts with a 4 KiB control block (counters
+ *   through which the workgroups of one kernel hand work to each other): it must be
+ *   zero-filled before the workspace is first used (e.g. one hipMemset at
+ *   allocation), and every call leaves it zero when its kernels complete. The rest of
+ *   the workspace is undefined before and after a call. Calls on different streams
+ *   must not share a workspace, and calls that overlap in time must not either. The only mutable state is
  *   the optional, thread-local kernel trace (diagnostics below); the library is
  *   thread-safe. No exceptions cross this interface.
  */

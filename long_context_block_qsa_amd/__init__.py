@@ -154,10 +154,11 @@ def workspace_size(seqs: Seqs, topk: int = KMAX) -> int:
 
 
 def alloc_workspace(seqs: Seqs, topk: int = KMAX, device="cuda"):
-    """A device buffer of qsa_workspace_size() bytes, 256-byte aligned."""
+    """A zero-filled device buffer of qsa_workspace_size() bytes, 256-byte aligned (the
+    library expects the workspace's control block to be zero before its first use)."""
     import torch
     n = workspace_size(seqs, topk)
-    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    buf = torch.zeros(n + 256, dtype=torch.uint8, device=device)
     off = (-buf.data_ptr()) % 256
     return buf[off:off + n] if n > 0 else buf[off:off + 1]
 

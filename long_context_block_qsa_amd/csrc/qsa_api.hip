@@ -82,7 +82,8 @@ struct Plan {
     int local_ch = 0;           // > 0: decode path, blocks per chunk
     int max_chunks = 0;         // chunks of the longest scored row (decode path)
     int nsplit = 1;             // attention key splits per row
-    size_t off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, ws_bytes = 0;
+    int64_t n_dense = 0;        // query rows with at most topk visible blocks
+    size_t off_ctl = 0, off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, ws_bytes = 0;
     bool use_dec = false;       // few rows: row/tile tables travel as kernel arguments
     bool fuse_compress = false; // decode: scoring workgroups compress the new blocks
     qsa::DecodeTables dec;
@@ -156,6 +157,7 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
         if (nq > 0)
             p->max_cmp_incr = std::max(p->max_cmp_incr, L / qsa::BS - (L - nq) / qsa::BS);
         const int64_t ts = h_first_scored_pos(L, nq, p->topk);
+        if (cq) p->n_dense += std::min(nq, std::max<int64_t>(0, ts - (L - nq)));
         if (cq && ts < L) {
             p->n_tiles += (L - ts + 3) / 4;
             p->n_slots += h_slots_before(L) - h_slots_before(ts);
@@ -203,7 +205,8 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
         int64_t ns = (1024 + 2 * p->tq - 1) / (2 * p->tq);
         p->nsplit = (int)std::min<int64_t>(64, std::max<int64_t>(1, ns));
     }
-    // workspace: [seq table][selection][scores | attention partials]
+    // workspace: [control block][seq table][selection][scores | attention partials]
+    const size_t ctl_b = (size_t)qsa::CTL_WORDS * sizeof(uint32_t);
     const size_t tab_b = align_up((size_t)std::max(p->batch, 1) * sizeof(SeqInfo));
     const size_t sel_b = align_up((size_t)p->tq * (size_t)p->topk * sizeof(int32_t));
     const size_t score_b = align_up((size_t)p->n_slots * sizeof(uint32_t));
@@ -211,9 +214,10 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
         ? align_up((size_t)p->tq * p->max_chunks * kKP * 2 * sizeof(uint32_t)) : 0;
     const size_t part_b = p->nsplit > 1
         ? align_up((size_t)p->tq * p->nsplit * qsa::HQ * (qsa::HD + 4) * sizeof(float)) : 0;
-    p->off_tab = 0;
-    p->off_sel = tab_b;
-    p->off_union = tab_b + sel_b;     // scores (+ candidates) while selecting, then partials
+    p->off_ctl = 0;
+    p->off_tab = ctl_b;
+    p->off_sel = ctl_b + tab_b;
+    p->off_union = ctl_b + tab_b + sel_b;  // scores (+ candidates) while selecting, then partials
     p->off_cand = p->off_union + score_b;
     p->ws_bytes = p->off_union + std::max(score_b + cand_b, part_b);
     return QSA_OK;
@@ -247,15 +251,23 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
     if (p.local_ch > 0) {
         cand_key = ws_at<uint32_t>(ws, p.off_cand);
         cand_idx = reinterpret_cast<int32_t *>(cand_key + (size_t)p.tq * p.max_chunks * 32);
+        // scoring selects the scored rows itself; a select launch remains only for rows
+        // within the budget
         QSA_TRY(qsa::launch_score_local(p.dec, p.n_tiles, p.topk, q_idx, w, k_idx, k_blk, keys,
-                                        cand_key, cand_idx, p.local_ch, p.max_chunks, st));
-    } else {
+                                        cand_key, cand_idx, p.local_ch, p.max_chunks, sel,
+                                        ws_at<uint32_t>(ws, p.off_ctl), st));
+        if (p.n_dense > 0)
+            QSA_TRY(qsa::launch_select(tab, &p.dec, p.batch, p.topk, keys, cand_key, cand_idx,
+                                       p.local_ch, p.max_chunks, sel, p.tq, p.max_score_blocks,
+                                       1, st));
+        return QSA_OK;
+    }
+    if (p.n_tiles > 0)
         QSA_TRY(qsa::launch_score(tab, p.batch, p.topk, q_idx, w, k_blk, keys, p.n_tiles,
                                   p.max_score_blocks, p.score_chunk, st));
-    }
     QSA_TRY(qsa::launch_select(tab, p.use_dec ? &p.dec : nullptr, p.batch, p.topk, keys,
                                cand_key, cand_idx, p.local_ch, p.max_chunks, sel, p.tq,
-                               p.max_score_blocks, st));
+                               p.max_score_blocks, 0, st));
     (void)s;
     return QSA_OK;
 }

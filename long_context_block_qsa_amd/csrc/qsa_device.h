@@ -41,6 +41,12 @@ struct SeqInfo {
 // Host-computed row and tile tables passed as kernel arguments when a call has few
 // query rows (decode): no table kernel and no device-side sequence lookup.
 constexpr int DEC_MAX = 64;
+
+// Control block at the start of the workspace: counters through which workgroups of
+// one kernel hand work to each other. Zero before a call; every call leaves it zero.
+//   words [0, 64): score tiles, chunks scored so far
+constexpr int CTL_TILE = 0;
+constexpr int CTL_WORDS = 1024;
 struct DecRow {
     int32_t k0;     // first key row of the row's sequence
     int32_t t;      // position of the query token
@@ -391,105 +397,173 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// One wave finds the k-th largest of the keys it holds in registers: lane j holds
-// positions PER*j .. PER*j+PER-1, of which those below n are valid (1 <= k <= n).
-// Radix select with 8-bit digits that starts at the highest bit where the keys
-// differ, a wave-private 256-bin LDS histogram, no workgroup barrier. Returns theta
-// and `need`, the number of keys equal to theta among the k largest (ties go to the
-// lowest positions).
-template <int PER>
-__device__ __forceinline__ void wave_kth_regs(const uint32_t (&x)[PER], int n, int k,
-                                              uint32_t *__restrict__ hist, uint32_t *theta_out,
-                                              int *need_out) {
+// Wave-wide max / min of uint32 with DPP row shifts and row broadcasts (the result is
+// complete in lane 63 and read from there).
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
+}
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xa, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
+}
+
+// Exact top-k (1 <= k) of the valid keys one wave holds in registers, with no
+// workgroup barrier: lane l holds positions PER*l .. PER*l+PER-1 (REG_MAJOR: positions
+// e*64 + l), ok[e] marks the valid ones. Order: key descending, equal keys by
+// ascending position. Radix select with
+// 8-bit digits over a wave-private 256-bin LDS histogram (`hist`), starting at the
+// highest bit where the keys differ and stopping as soon as the bin that holds the
+// k-th key is kept whole; when the digits run out, that bin is one key value and its
+// keys are kept by position. Returns this lane's kept mask (bit e); all valid keys
+// when there are at most k.
+template <int PER, bool REG_MAJOR = false>
+__device__ __forceinline__ uint32_t wave_topk_hist(const uint32_t (&x)[PER],
+                                                   const bool (&ok)[PER], int k,
+                                                   uint32_t *__restrict__ hist) {
     const int l = lane_id();
-    uint32_t mx = 0u, mn = 0xffffffffu;
+    int nvalid = 0;
+    uint32_t mx = 0u, mn = 0xffffffffu, all = 0u;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        if (PER * l + e < n) {
-            mx = max(mx, x[e]);
-            mn = min(mn, x[e]);
-        }
+        nvalid += __popcll(__ballot(ok[e]));
+        if (ok[e]) { mx = max(mx, x[e]); mn = min(mn, x[e]); all |= 1u << e; }
     }
-    mx = wave_max_u32(mx);
-    mn = wave_min_u32(mn);
+    if (nvalid <= k) return all;
+    mx = wave_max_dpp(mx);
+    mn = wave_min_dpp(mn);
     const uint32_t diff = mx ^ mn;
-    int hb = diff ? 32 - __builtin_clz(diff) : 0;  // low bits that vary
+    int hb = diff ? 32 - __builtin_clz(diff) : 0;   // low bits that vary
     uint32_t pmask = hb >= 32 ? 0u : ~((1u << hb) - 1u);
     uint32_t prefix = mx & pmask;
     int need = k;
+    bool whole = false;   // the final bin is kept whole
     while (hb > 0) {
         const int shift = hb > 8 ? hb - 8 : 0;
         const int nb = 1 << (hb - shift);
         const uint32_t dmask = (uint32_t)nb - 1u;
-        for (int i = l; i < nb; i += WAVE) hist[i] = 0u;
+        *reinterpret_cast<u32x4 *>(&hist[4 * l]) = u32x4{0u, 0u, 0u, 0u};
         wave_lds_sync();
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-            if (PER * l + e < n && (x[e] & pmask) == prefix)
+            if (ok[e] && (x[e] & pmask) == prefix)
                 atomicAdd(&hist[(x[e] >> shift) & dmask], 1u);
         wave_lds_sync();
-        // lane j owns the 4 bins ending at nb - 4j (highest bins first)
-        const int top = nb - 4 * l;
-        uint32_t h[4];
-        int local = 0;
+        // lane l owns bins nb-1-4l .. nb-4-4l (highest first)
+        int h[4], local = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int b = top - 1 - i;
-            h[i] = b >= 0 ? hist[b] : 0u;
-            local += (int)h[i];
+            const int b = nb - 1 - 4 * l - i;
+            h[i] = b >= 0 ? (int)hist[b] : 0;
+            local += h[i];
         }
-        const int above = wave_incl_scan_i32(local) - local;
-        const bool cross = above < need && need <= above + local;
-        const unsigned long long bal = __ballot(cross);
-        int digit = 0, run = above;
+        const int incl = wave_incl_scan_i32(local);
+        const int above = incl - local;
+        const bool cross = above < need && need <= incl;
+        int digit = 0, run = above, m = 0;
         if (cross) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (run + (int)h[i] >= need) { digit = top - 1 - i; break; }
-                run += (int)h[i];
+                if (run + h[i] >= need) { digit = nb - 1 - 4 * l - i; m = h[i]; break; }
+                run += h[i];
             }
         }
-        const int src = (int)__builtin_ctzll(bal);
+        const int src = (int)__builtin_ctzll(__ballot(cross));
         digit = __builtin_amdgcn_readlane(digit, src);
         run = __builtin_amdgcn_readlane(run, src);
+        m = __builtin_amdgcn_readlane(m, src);
         need -= run;
         prefix |= (uint32_t)digit << shift;
         pmask |= dmask << shift;
         hb = shift;
-        wave_lds_sync();
+        wave_lds_sync();  // the histogram is cleared again by the next pass
+        if (m == need) { whole = true; break; }
     }
-    *theta_out = prefix;
-    *need_out = need;
-}
-
-// Ordered pass after wave_kth_regs: keeps keys above theta and the first `need` keys
-// equal to it (lowest positions). Each lane marks its kept elements in `kept_mask`
-// (bit e) and gets the output slot of its first kept element; returns the total kept.
-template <int PER>
-__device__ __forceinline__ int wave_keep_regs(const uint32_t (&x)[PER], int n, uint32_t theta,
-                                              int need, uint32_t *kept_mask, int *first_pos,
-                                              int *n_kept) {
-    const int l = lane_id();
-    int n_eq = 0;
+    uint32_t mask = 0u;
+    if (REG_MAJOR) {
+        // equal keys before (e, l): all lanes at e' < e, then lanes below l at e
+        int eq_run = 0;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) n_eq += (PER * l + e < n && x[e] == theta);
-    int eq_run = wave_incl_scan_i32(n_eq) - n_eq;
-    uint32_t mask = 0;
-    int nt = 0;
+        for (int e = 0; e < PER; ++e) {
+            const uint32_t hi_bits = x[e] & pmask;
+            const bool eq = ok[e] && !whole && hi_bits == prefix;
+            const unsigned long long b = __ballot(eq);
+            if (ok[e] && (hi_bits > prefix || (whole && hi_bits == prefix))) mask |= 1u << e;
+            else if (eq && eq_run + lanes_below(b) < need) mask |= 1u << e;
+            eq_run += __popcll(b);
+        }
+        return mask;
+    }
+    int eq_below = 0;
+    if (!whole) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) eq_below += lanes_below(__ballot(ok[e] && x[e] == prefix));
+    }
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const bool valid = PER * l + e < n;
-        const bool eq = valid && x[e] == theta;
-        const bool take = (valid && x[e] > theta) || (eq && eq_run < need);
-        eq_run += eq;
-        if (take) { mask |= 1u << e; ++nt; }
+        if (!ok[e]) continue;
+        const uint32_t hi_bits = x[e] & pmask;
+        if (hi_bits > prefix || (whole && hi_bits == prefix)) mask |= 1u << e;
+        else if (hi_bits == prefix) {
+            if (eq_below < need) mask |= 1u << e;
+            ++eq_below;
+        }
     }
-    const int incl = wave_incl_scan_i32(nt);
-    *kept_mask = mask;
-    *first_pos = incl - nt;
-    *n_kept = nt;
-    return __builtin_amdgcn_readlane(incl, WAVE - 1);
+    return mask;
 }
+
+// Exclusive prefix over the wave of small per-lane counts (0 <= cnt <= MAXC).
+template <int MAXC>
+__device__ __forceinline__ int wave_excl_small(int cnt) {
+    int pre = 0;
+#pragma unroll
+    for (int c = 1; c <= MAXC; ++c) pre += lanes_below(__ballot(cnt >= c));
+    return pre;
+}
+
+// ---------------------------------------------------------------- write-through access
+// Data handed from one workgroup to another inside a kernel (possibly on another
+// XCD, whose L2 is not coherent with this one) is stored and loaded at agent scope:
+// the stores write through to the coherence point and the loads read from it. The
+// producer waits for its stores to complete before it signals (s_waitcnt), so no
+// cache-wide release fence is needed.
+__device__ __forceinline__ void store_wt(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_wt(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_wt(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_wt(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_wt(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes as two 8-byte agent-scope loads (p 16-byte aligned)
+__device__ __forceinline__ u32x4 load16_wt(const void *p) {
+    const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+// Waits until every vector memory operation this wave issued has completed (stores
+// included); the "memory" clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 
 // ---------------------------------------------------------------- block top-k (registers)
 
@@ -509,15 +583,18 @@ struct TopkSmem {
 // ignored). Order: key descending, equal keys by ascending position. Sets bit e of
 // *kept when position PER*t+e is among the k, and *first to this thread's rank
 // among kept positions (kept positions ordered by position); returns k.
-// Method: an 8-bit histogram of the highest bits where the keys differ finds the
-// bin that holds the k-th key; bins above it are kept whole. When that bin holds at
-// most 64 keys they are ranked exactly by one wave (all pairs); otherwise the bin is
-// refined with the next 8 bits, down to single key values, where equal keys are
-// kept by position.
-template <int NT, int PER>
+// Method: a histogram of up to DB bits (the highest bits where the keys differ; DB
+// = 8 uses sm.hist, DB = 11 the caller's 2048-word `wide` array) finds the bin that
+// holds the k-th key; bins above it are kept whole. When that bin holds at most 64
+// keys they are ranked exactly by one wave (all pairs); otherwise the bin is refined
+// with the next 8 bits, down to single key values, where equal keys are kept by
+// position.
+template <int NT, int PER, int DB = 8>
 __device__ __forceinline__ int block_topk_regs(const uint32_t (&x)[PER], int n, int k,
-                                               TopkSmem &sm, uint32_t *kept, int *first) {
-    static_assert(NT == 256, "one histogram bin per thread");
+                                               TopkSmem &sm, uint32_t *kept, int *first,
+                                               uint32_t *wide = nullptr) {
+    static_assert(NT == 256, "bins are owned by threads in groups of nb / 256");
+    static_assert(DB == 8 || DB == 11, "digit widths: 8 or 11 bits");
     constexpr int NW = NT / WAVE;
     const int tid = threadIdx.x, l = lane_id(), w = tid / WAVE;
 
@@ -526,8 +603,8 @@ __device__ __forceinline__ int block_topk_regs(const uint32_t (&x)[PER], int n, 
 #pragma unroll
     for (int e = 0; e < PER; ++e)
         if (PER * tid + e < n) { mx = max(mx, x[e]); mn = min(mn, x[e]); }
-    mx = wave_max_u32(mx);
-    mn = wave_min_u32(mn);
+    mx = wave_max_dpp(mx);
+    mn = wave_min_dpp(mn);
     if (l == 0) { sm.red[0][w] = mx; sm.red[1][w] = mn; }
     __syncthreads();
 #pragma unroll
@@ -538,27 +615,42 @@ __device__ __forceinline__ int block_topk_regs(const uint32_t (&x)[PER], int n, 
     uint32_t prefix = mx & pmask;
     int need = k;
     int mode = 0;   // 1: keep the whole final bin, 2: ranked bitmap, 3: equal keys by position
+    bool first_pass = true;
 
     while (true) {
         if (hb == 0) { mode = 3; break; }            // the final bin is one key value
-        const int shift = hb > 8 ? hb - 8 : 0;
+        const int width = (DB == 11 && first_pass) ? 11 : 8;
+        uint32_t *hist = (DB == 11 && first_pass) ? wide : sm.hist;
+        const int shift = hb > width ? hb - width : 0;
         const int nb = 1 << (hb - shift);
+        const int bpt = nb > NT ? nb / NT : 1;        // bins per thread
         const uint32_t dmask = (uint32_t)nb - 1u;
-        if (tid < nb) sm.hist[tid] = 0u;
+        for (int i = tid; i < nb; i += NT) hist[i] = 0u;
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < PER; ++e)
             if (PER * tid + e < n && (x[e] & pmask) == prefix)
-                atomicAdd(&sm.hist[(x[e] >> shift) & dmask], 1u);
+                atomicAdd(&hist[(x[e] >> shift) & dmask], 1u);
         __syncthreads();
-        const int bin = nb - 1 - tid;                 // thread t owns bin nb-1-t
-        const int local = tid < nb ? (int)sm.hist[bin] : 0;
+        // thread t owns bins nb-bpt*(t+1) .. nb-1-bpt*t (highest bins first)
+        const int top = nb - bpt * tid;
+        int local = 0;
+        for (int i = 1; i <= bpt; ++i) local += top - i >= 0 ? (int)hist[top - i] : 0;
         int tot;
         const int above = block_excl_scan_i32<NT>(local, sm.scan, &tot);
-        if (tid < nb && above < need && need <= above + local) {
-            sm.found[0] = bin;
-            sm.found[1] = above;
-            sm.found[2] = local;
+        if (top > 0 && above < need && need <= above + local) {
+            int run = above;
+            for (int i = 1; i <= bpt; ++i) {
+                const int b = top - i;
+                const int h = (int)hist[b];
+                if (run + h >= need) {
+                    sm.found[0] = b;
+                    sm.found[1] = run;
+                    sm.found[2] = h;
+                    break;
+                }
+                run += h;
+            }
         }
         __syncthreads();
         const int T = sm.found[0], A = sm.found[1], m = sm.found[2];
@@ -566,6 +658,7 @@ __device__ __forceinline__ int block_topk_regs(const uint32_t (&x)[PER], int n, 
         prefix |= (uint32_t)T << shift;
         pmask |= dmask << shift;
         hb = shift;
+        first_pass = false;
         __syncthreads();
         if (m == need) { mode = 1; break; }
         if (m <= 64) { mode = 2; break; }

@@ -247,121 +247,29 @@ score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
     }
 }
 
-// =============================================================== score_local
-// Decode-shaped launches: grid x = tile, y = chunk of CH blocks. Besides writing
-// every key (needed by the exact fallback), each workgroup keeps its chunk's keys in
-// LDS and, for each row of the tile whose selection can come from chunk candidates,
-// writes the chunk's KP best (key, block) pairs in ascending block order to
-// cand[row][chunk][0..KP), padded with key 0 (below every real key).
+// =============================================================== score_local + select
+// Decode-shaped launches: grid x = chunk of CH blocks, y = tile, so workgroups are
+// dispatched (and their loads largely served) row by row: a row's chunks complete
+// together and its selection overlaps the scoring of later rows. Each workgroup
+// scores its chunk for the tile's rows into LDS and, for each row whose selection can
+// come from chunk candidates, writes the chunk's KP best (key, block) pairs in
+// ascending block order to cand[row][chunk][0..KP), padded with key 0 (below every
+// real key). The local top-KP is exact and needs no workgroup-wide histogram: each
+// wave takes the top KP of its 256 positions with a wave-private radix select, and
+// one wave takes the top KP of those 4 x KP. Candidates are written through to the
+// coherence point; the workgroup that completes the tile's last chunk (per-tile
+// arrival counter in the control block, reset by that workgroup) then selects every
+// row of the tile (select_tile below).
 constexpr int LOC_NT = 256;
 constexpr int LOC_MAX_CH = 1024;
 constexpr int KP = 32;
+constexpr int SEL_NT = 256;
 
 // A row may be selected from chunk candidates when its full chunks alone provide at
 // least topk candidates (so the union always holds topk real keys).
 __device__ __forceinline__ bool cand_eligible(int64_t nv, int topk, int ch) {
     return nv > topk && (nv / ch) * KP >= topk;
 }
-
-struct LocalArgs {
-    int topk;
-    const uint16_t *q_idx;
-    const float *w;
-    const uint16_t *k_idx;   // not null: compress each tile's new blocks first
-    uint16_t *k_blk;
-    uint32_t *keys;
-    uint32_t *cand_key;
-    int32_t *cand_idx;
-    int ch, max_chunks;
-};
-
-// 4 waves per SIMD: the whole decode grid (rows x chunks) is resident at once
-__global__ void __launch_bounds__(LOC_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
-score_local_kernel(LocalArgs a, DecodeTables d) {
-    __shared__ uint32_t lk[4][LOC_MAX_CH];
-    __shared__ TopkSmem tsm;
-
-    const DecTile tl = d.tile[blockIdx.x];
-    const int64_t row0 = tl.row0;
-    const int nrows = tl.nrows;
-    const int64_t t0 = d.row[row0].t;
-    const int64_t lo = (int64_t)blockIdx.y * a.ch;
-    const int64_t hi = min<int64_t>(nvis_of(t0 + nrows - 1), lo + a.ch);
-    if (lo >= hi) return;
-    const int l = lane_id(), g = l >> 4, c = l & 15;
-    // blocks of this sequence that hold a query token are (re)compressed here first,
-    // by every workgroup whose chunk contains them (identical values)
-    if (a.k_idx && tl.new_hi > tl.new_lo) {
-        const int64_t c_lo = max<int64_t>(lo, tl.new_lo), c_hi = min<int64_t>(hi, tl.new_hi);
-        const int64_t blk = c_lo + threadIdx.x / 8;
-        if (blk < c_hi)
-            compress_one(a.k_idx, a.k_blk, d.row[row0].k0, d.row[row0].blk0, blk,
-                         threadIdx.x % 8);
-        __threadfence_block();
-        __syncthreads();
-    }
-    const ScoreLane sl = score_lane_setup(a.q_idx, a.w, row0, nrows, t0,
-                                          d.row[row0 + min(g, nrows - 1)].slot);
-    const uint16_t *kb = a.k_blk + (int64_t)d.row[row0].blk0 * DI;
-    constexpr int64_t step = 16 * (LOC_NT / WAVE);
-    for (int64_t b0 = lo + 16 * (threadIdx.x / WAVE); b0 < hi; b0 += step * SCORE_BATCH) {
-        uint32_t key[SCORE_BATCH];
-        score_groups<SCORE_BATCH>(sl, kb, b0, step, hi, key);
-#pragma unroll
-        for (int u = 0; u < SCORE_BATCH; ++u) {
-            const int64_t blk = b0 + u * step + c;
-            if (blk < hi && blk < sl.nv_row) {
-                a.keys[sl.slot + blk] = key[u];
-                lk[g][blk - lo] = key[u];
-            }
-        }
-    }
-    lds_barrier();
-
-    // each tile row whose selection can come from chunk candidates gets this chunk's
-    // KP best (key, block) pairs, in ascending block order, padded with key 0
-    for (int rr = 0; rr < nrows; ++rr) {
-        const int64_t nv = nvis_of(t0 + rr);
-        if (!cand_eligible(nv, a.topk, a.ch)) continue;   // uniform over the workgroup
-        const int n = (int)(min<int64_t>(nv, hi) - lo);    // this row's blocks in the chunk
-        uint32_t *ck = a.cand_key + ((row0 + rr) * a.max_chunks + blockIdx.y) * KP;
-        int32_t *ci = a.cand_idx + ((row0 + rr) * a.max_chunks + blockIdx.y) * KP;
-        int kept_total = n;
-        if (n > KP) {
-            uint32_t x[4];
-            const u32x4 q4 = *reinterpret_cast<const u32x4 *>(&lk[rr][4 * threadIdx.x]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = q4[e];
-            uint32_t kept;
-            int first;
-            kept_total = block_topk_regs<LOC_NT, 4>(x, n, KP, tsm, &kept, &first);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (kept & (1u << e)) {
-                    ck[first] = x[e];
-                    ci[first] = (int32_t)(lo + 4 * threadIdx.x + e);
-                    ++first;
-                }
-            }
-        } else if (threadIdx.x < n) {
-            ck[threadIdx.x] = lk[rr][threadIdx.x];
-            ci[threadIdx.x] = (int32_t)(lo + threadIdx.x);
-        }
-        if (threadIdx.x < KP && (int)threadIdx.x >= kept_total) {
-            ck[threadIdx.x] = 0u;
-            ci[threadIdx.x] = -1;
-        }
-    }
-}
-
-// =============================================================== select
-// One workgroup per query row. Rows within the budget keep blocks 0..nvis-1. Other
-// rows: radix_kth + emit_kept over either the union of chunk candidates (when the
-// row was eligible and no chunk had all KP of its candidates kept: only then can a
-// chunk hide a better block, so the union result is exact) or the full row of keys.
-// Keys are staged in dynamic LDS when they fit (lds_cap keys), else read from the
-// workspace in each pass.
-constexpr int SEL_NT = 256;
 
 struct SelectArgs {
     const SeqInfo *tab;
@@ -372,10 +280,11 @@ struct SelectArgs {
     int ch, max_chunks;  // ch = 0: no candidates
     int32_t *sel;
     int64_t lds_cap;     // keys that fit the dynamic LDS
+    int dense_only;      // only rows with at most topk visible blocks
 };
 
-// Top-k of n keys at `kk` (LDS or global; the caller passes a pointer of known
-// address space), ids from `ii` (or positions), written to out in ascending order.
+// Top-k of n keys at `kk` (LDS or global), ids from `ii` (or positions), written to
+// out in ascending order.
 template <int PER, typename KP_T, typename IP_T>
 __device__ __forceinline__ void select_keys(KP_T kk, IP_T ii, int64_t n, int topk,
                                             int32_t *out, uint32_t *hist, int32_t *scan_sh,
@@ -391,61 +300,78 @@ __device__ __forceinline__ void select_keys(KP_T kk, IP_T ii, int64_t n, int top
     emit_kept<SEL_NT, PER>(kk, ii, n, theta, need, out, nullptr, topk, scan_sh, grp_cnt, group);
 }
 
+// Selection of a row from the union of its chunk candidates (rows with nvis > topk
+// that are eligible and have at most 64 chunks). Returns true when the result is
+// exact: no full chunk (more than KP blocks) had all KP of its candidates kept, since
+// only such a chunk can hide a better block. WT: candidates were written by other
+// workgroups of the same kernel and are read with agent-scope loads.
+template <bool WT>
+__device__ __forceinline__ bool select_from_candidates(const SelectArgs &a, int64_t nv,
+                                                       int64_t row, int *viol, TopkSmem *tsm) {
+    int32_t *out = a.sel + row * a.topk;
+    const int tid = threadIdx.x;
+    // thread t holds candidate positions 8t .. 8t+7 (chunk t/4) in registers
+    const int nchunk = (int)((nv + a.ch - 1) / a.ch);
+    const int n = nchunk * KP;   // padding entries carry key 0, never kept
+    const int c = min(tid / 4, nchunk - 1), part = tid % 4;
+    const uint32_t *ck = a.cand_key + (row * a.max_chunks + c) * KP + 8 * part;
+    const int32_t *ci = a.cand_idx + (row * a.max_chunks + c) * KP + 8 * part;
+    uint32_t x[8];
+    int32_t id[8];
+    u32x4 kq[2], iq[2];
+#pragma unroll
+    for (int v4 = 0; v4 < 2; ++v4) {
+        kq[v4] = WT ? load16_wt(ck + 4 * v4) : load16(ck + 4 * v4);
+        iq[v4] = WT ? load16_wt(ci + 4 * v4) : load16(ci + 4 * v4);
+    }
+#pragma unroll
+    for (int v4 = 0; v4 < 2; ++v4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[4 * v4 + e] = kq[v4][e];
+            id[4 * v4 + e] = (int32_t)iq[v4][e];
+        }
+    }
+    if (tid == 0) *viol = 0;
+    uint32_t kept;
+    int first;
+    block_topk_regs<SEL_NT, 8>(x, n, a.topk, *tsm, &kept, &first);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (kept & (1u << e)) {
+            if (first < a.topk) out[first] = id[e];
+            ++first;
+        }
+    }
+    int kc = __popc(kept);
+    kc += __shfl_xor(kc, 1);
+    kc += __shfl_xor(kc, 2);
+    const int64_t nc = tid / 4 < nchunk ? min<int64_t>(a.ch, nv - (int64_t)(tid / 4) * a.ch) : 0;
+    if (nc > KP && kc >= KP) *viol = 1;
+    __syncthreads();
+    return !*viol;
+}
+
+__device__ __forceinline__ bool uses_candidates(const SelectArgs &a, int64_t nv) {
+    return a.ch > 0 && cand_eligible(nv, a.topk, a.ch) && (nv + a.ch - 1) / a.ch <= WAVE;
+}
+
+// One workgroup selects one query row. Rows within the budget keep blocks 0..nvis-1.
+// Other rows: the union of chunk candidates when that is exact, else an exact radix
+// select over the row's full key row (staged in dynamic LDS when it fits).
 __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView rv, int64_t row,
                                             uint32_t *dyn, uint32_t *hist, int32_t *scan_sh,
                                             uint32_t *found, int *viol, TopkSmem *tsm) {
-    const int64_t t = rv.t;
-    const int64_t nv = nvis_of(t);
+    const int64_t nv = nvis_of(rv.t);
     int32_t *out = a.sel + row * a.topk;
     const int tid = threadIdx.x;
-
     if (nv <= a.topk) {
         for (int i = tid; i < a.topk; i += SEL_NT) out[i] = i < nv ? i : -1;
         return;
     }
+    if (a.dense_only) return;
+    if (uses_candidates(a, nv) && select_from_candidates<false>(a, nv, row, viol, tsm)) return;
 
-    if (a.ch > 0 && cand_eligible(nv, a.topk, a.ch) && (nv + a.ch - 1) / a.ch <= WAVE) {
-        // thread t holds candidate positions 8t .. 8t+7 (chunk t/4) in registers
-        const int nchunk = (int)((nv + a.ch - 1) / a.ch);
-        const int n = nchunk * KP;   // padding entries carry key 0, never kept
-        const int c = min(tid / 4, nchunk - 1), part = tid % 4;
-        const uint32_t *ck = a.cand_key + (row * a.max_chunks + c) * KP + 8 * part;
-        const int32_t *ci = a.cand_idx + (row * a.max_chunks + c) * KP + 8 * part;
-        uint32_t x[8];
-        int32_t id[8];
-#pragma unroll
-        for (int v4 = 0; v4 < 2; ++v4) {
-            const u32x4 kq = load16(ck + 4 * v4);
-            const u32x4 iq = load16(ci + 4 * v4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[4 * v4 + e] = kq[e];
-                id[4 * v4 + e] = (int32_t)iq[e];
-            }
-        }
-        if (tid == 0) *viol = 0;
-        uint32_t kept;
-        int first;
-        block_topk_regs<SEL_NT, 8>(x, n, a.topk, *tsm, &kept, &first);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (kept & (1u << e)) {
-                if (first < a.topk) out[first] = id[e];
-                ++first;
-            }
-        }
-        // a full chunk (more than KP blocks) with every candidate kept may hide more
-        int kc = __popc(kept);
-        kc += __shfl_xor(kc, 1);
-        kc += __shfl_xor(kc, 2);
-        const int64_t nc = tid / 4 < nchunk ? min<int64_t>(a.ch, nv - (int64_t)(tid / 4) * a.ch) : 0;
-        if (nc > KP && kc >= KP) *viol = 1;
-        __syncthreads();
-        if (!*viol) return;
-        // otherwise the exact path below decides
-    }
-
-    // exact selection over the full row of keys
     const uint32_t *rk = a.keys + rv.slot;
     if (nv <= a.lds_cap) {
         for (int64_t i0 = tid; i0 < nv; i0 += 8 * SEL_NT) {
@@ -465,6 +391,236 @@ __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView r
         select_keys<16>(rk, (const int32_t *)nullptr, nv, a.topk, out, hist, scan_sh, found,
                         nullptr, 1, 0);
     }
+}
+
+struct LocalArgs {
+    int topk;
+    const uint16_t *q_idx;
+    const float *w;
+    const uint16_t *k_idx;   // not null: compress each tile's new blocks first
+    uint16_t *k_blk;
+    uint32_t *keys;          // full key rows, written only when a row needs the exact path
+    uint32_t *cand_key;
+    int32_t *cand_idx;
+    int ch, max_chunks;
+    int32_t *sel;
+    uint32_t *ctl;           // per-tile arrival counters (zero between calls)
+};
+
+// Scores blocks [lo, hi) of a tile; store(row, blk, key) is called for each block
+// the lane's row sees.
+template <typename Store>
+__device__ __forceinline__ void score_range(const ScoreLane &sl, const uint16_t *kb, int64_t lo,
+                                            int64_t hi, Store store) {
+    const int g = lane_id() >> 4, c = lane_id() & 15;
+    constexpr int64_t step = 16 * (LOC_NT / WAVE);
+    for (int64_t b0 = lo + 16 * (threadIdx.x / WAVE); b0 < hi; b0 += step * SCORE_BATCH) {
+        uint32_t key[SCORE_BATCH];
+        score_groups<SCORE_BATCH>(sl, kb, b0, step, hi, key);
+#pragma unroll
+        for (int u = 0; u < SCORE_BATCH; ++u) {
+            const int64_t blk = b0 + u * step + c;
+            if (blk < hi && blk < sl.nv_row) store(g, blk, key[u]);
+        }
+    }
+}
+
+// Selection of every row of a decode tile by the workgroup that scored its last
+// chunk: from the chunk candidates where that is exact; the other rows get an exact
+// radix select over key rows this workgroup recomputes itself (after recompressing
+// the tile's new blocks, so that it reads only its own writes).
+__device__ __forceinline__ void select_tile(const LocalArgs &a, const DecodeTables &d, int tile,
+                                         uint32_t *hist, int32_t *scan_sh, uint32_t *found,
+                                         int *viol, int *exact, TopkSmem *tsm) {
+    const DecTile tl = d.tile[tile];
+    const int64_t row0 = tl.row0;
+    const int nrows = tl.nrows;
+    const int64_t t0 = d.row[row0].t;
+    SelectArgs sa;
+    sa.tab = nullptr; sa.batch = 0; sa.topk = a.topk; sa.keys = a.keys;
+    sa.cand_key = a.cand_key; sa.cand_idx = a.cand_idx; sa.ch = a.ch;
+    sa.max_chunks = a.max_chunks; sa.sel = a.sel; sa.lds_cap = 0; sa.dense_only = 0;
+    int n_exact = 0;
+    for (int rr = 0; rr < nrows; ++rr) {
+        const int64_t nv = nvis_of(t0 + rr);
+        const bool done = uses_candidates(sa, nv) &&
+                          select_from_candidates<true>(sa, nv, row0 + rr, viol, tsm);
+        if (threadIdx.x == 0) exact[rr] = !done;
+        n_exact += !done;   // uniform
+    }
+    if (n_exact == 0) return;
+    const DecRow r0 = d.row[row0];
+    if (a.k_idx && tl.new_hi > tl.new_lo) {
+        for (int64_t blk = tl.new_lo + threadIdx.x / 8; blk < tl.new_hi; blk += LOC_NT / 8)
+            compress_one(a.k_idx, a.k_blk, r0.k0, r0.blk0, blk, threadIdx.x % 8);
+        wait_vmem();
+        __syncthreads();
+    }
+    const int g = lane_id() >> 4;
+    const ScoreLane sl = score_lane_setup(a.q_idx, a.w, row0, nrows, t0,
+                                          d.row[row0 + min(g, nrows - 1)].slot);
+    uint32_t *keys = a.keys;
+    const int64_t slot = sl.slot;
+    score_range(sl, a.k_blk + (int64_t)r0.blk0 * DI, 0, nvis_of(t0 + nrows - 1),
+                [=](int, int64_t blk, uint32_t key) { keys[slot + blk] = key; });
+    wait_vmem();
+    __syncthreads();
+    for (int rr = 0; rr < nrows; ++rr) {
+        if (!exact[rr]) continue;   // uniform (LDS, after the barrier)
+        const DecRow r = d.row[row0 + rr];
+        select_keys<16>((const uint32_t *)(a.keys + r.slot), (const int32_t *)nullptr,
+                        nvis_of(r.t), a.topk, a.sel + (row0 + rr) * a.topk, hist, scan_sh,
+                        found, nullptr, 1, 0);
+    }
+}
+
+// LDS of one scoring workgroup.
+struct ScoreSmem {
+    uint32_t whist[LOC_NT / WAVE][256];   // per-wave histograms (and key transposes)
+    uint32_t wl_key[LOC_NT / WAVE][KP];
+    int32_t wl_pos[LOC_NT / WAVE][KP];
+    uint32_t hist[kHistBins];
+    int32_t scan_sh[SEL_NT / WAVE];
+    uint32_t found[2];
+    int viol, s_last, exact[4];
+    TopkSmem tsm;
+};
+
+// One scoring workgroup: chunk `chunk` of tile `tile`. Returns true in the workgroup
+// that completed the tile (after it has selected the tile's rows).
+__device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTables &d, int tile,
+                                            int chunk, ScoreSmem &sm) {
+    const DecTile tl = d.tile[tile];
+    const int64_t row0 = tl.row0;
+    const int nrows = tl.nrows;
+    const int64_t t0 = d.row[row0].t;
+    const int64_t nv_max = nvis_of(t0 + nrows - 1);
+    const int64_t lo = (int64_t)chunk * a.ch;
+    const int64_t hi = min<int64_t>(nv_max, lo + a.ch);
+    if (lo >= hi) return false;
+    const int l = lane_id(), g = l >> 4, c = l & 15, w = threadIdx.x / WAVE;
+    // blocks of this sequence that hold a query token are (re)compressed here first,
+    // by every workgroup whose chunk contains them (identical values)
+    if (a.k_idx && tl.new_hi > tl.new_lo) {
+        const int64_t c_lo = max<int64_t>(lo, tl.new_lo), c_hi = min<int64_t>(hi, tl.new_hi);
+        const int64_t blk = c_lo + threadIdx.x / 8;
+        if (blk < c_hi)
+            compress_one(a.k_idx, a.k_blk, d.row[row0].k0, d.row[row0].blk0, blk,
+                         threadIdx.x % 8);
+        __threadfence_block();
+        __syncthreads();
+    }
+    const ScoreLane sl = score_lane_setup(a.q_idx, a.w, row0, nrows, t0,
+                                          d.row[row0 + min(g, nrows - 1)].slot);
+    const uint16_t *kb = a.k_blk + (int64_t)d.row[row0].blk0 * DI;
+
+    // wave w scores the contiguous blocks wlo + 16u + c (u < 16) of its quarter of the
+    // chunk; the keys stay in registers (two batches of 8 groups of 16 blocks)
+    const int span = a.ch / 4;
+    const int64_t wlo = lo + (int64_t)w * span;
+    const int64_t whi = min<int64_t>(hi, wlo + span);
+    uint32_t key[2 * SCORE_BATCH];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t kk[SCORE_BATCH];
+        if (wlo + 16 * SCORE_BATCH * h < whi) {
+            score_groups<SCORE_BATCH>(sl, kb, wlo + 16 * SCORE_BATCH * h, 16, whi, kk);
+        } else {
+#pragma unroll
+            for (int u = 0; u < SCORE_BATCH; ++u) kk[u] = 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < SCORE_BATCH; ++u) key[SCORE_BATCH * h + u] = kk[u];
+    }
+
+    // each tile row whose selection can come from chunk candidates gets this chunk's
+    // KP best (key, block) pairs, in ascending block order, padded with key 0: the top
+    // KP of each wave's blocks, then the top KP of those 4 x KP
+    uint32_t *wk = sm.whist[w];
+    for (int rr = 0; rr < nrows; ++rr) {
+        const int64_t nv = nvis_of(t0 + rr);
+        if (!cand_eligible(nv, a.topk, a.ch)) continue;   // uniform over the workgroup
+        // the row's keys, position 16u + c, move to lanes as positions 4l .. 4l+3
+        if (g == rr) {
+#pragma unroll
+            for (int u = 0; u < 2 * SCORE_BATCH; ++u) wk[16 * u + c] = key[u];
+        }
+        wave_lds_sync();
+        const u32x4 q4 = *reinterpret_cast<const u32x4 *>(&wk[4 * l]);
+        uint32_t x[4];
+        bool ok[4];
+        const int64_t nvw = min<int64_t>(whi, nv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[e] = q4[e]; ok[e] = wlo + 4 * l + e < nvw; }
+        wave_lds_sync();   // the histogram below reuses wk
+        const uint32_t mask = wave_topk_hist<4>(x, ok, KP, wk);
+        const int cnt = __popc(mask);
+        int pos = wave_excl_small<4>(cnt);
+        const int tot = __builtin_amdgcn_readlane(pos + cnt, WAVE - 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (mask & (1u << e)) {
+                sm.wl_key[w][pos] = x[e];
+                sm.wl_pos[w][pos] = (int32_t)(wlo + 4 * l + e - lo);
+                ++pos;
+            }
+        }
+        if (l >= tot && l < KP) sm.wl_key[w][l] = 0u;
+        lds_barrier();
+        if (w == 0) {
+            // entries 2l, 2l+1 of the 4 x KP wave lists (ascending position order)
+            uint32_t y[2];
+            bool oy[2];
+            int py[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * l + e;
+                y[e] = sm.wl_key[i / KP][i % KP];
+                py[e] = sm.wl_pos[i / KP][i % KP];
+                oy[e] = y[e] != 0u;
+            }
+            const uint32_t m2 = wave_topk_hist<2>(y, oy, KP, sm.whist[0]);
+            const int c2 = __popc(m2);
+            int o = wave_excl_small<2>(c2);
+            const int tot2 = __builtin_amdgcn_readlane(o + c2, WAVE - 1);
+            uint32_t *ck = a.cand_key + ((row0 + rr) * a.max_chunks + chunk) * KP;
+            int32_t *ci = a.cand_idx + ((row0 + rr) * a.max_chunks + chunk) * KP;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                if (m2 & (1u << e)) {
+                    store_wt(ck + o, y[e]);
+                    store_wt(ci + o, (int32_t)(lo + py[e]));
+                    ++o;
+                }
+            }
+            if (l >= tot2 && l < KP) {
+                store_wt(ck + l, 0u);
+                store_wt(ci + l, -1);
+            }
+        }
+        if (rr + 1 < nrows) lds_barrier();   // wave lists are reused by the next row
+    }
+
+    // hand over: the workgroup that completes the tile's last chunk selects its rows
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t nch = (uint32_t)((nv_max + a.ch - 1) / a.ch);
+        const uint32_t old = atomicAdd(&a.ctl[CTL_TILE + tile], 1u);
+        sm.s_last = old + 1 == nch;
+        if (sm.s_last) store_wt(&a.ctl[CTL_TILE + tile], 0u);
+    }
+    __syncthreads();
+    if (!sm.s_last) return false;
+    select_tile(a, d, tile, sm.hist, sm.scan_sh, sm.found, &sm.viol, sm.exact, &sm.tsm);
+    return true;
+}
+
+// 4 waves per SIMD: the whole decode grid (rows x chunks) is resident at once
+__global__ void __launch_bounds__(LOC_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
+score_local_kernel(LocalArgs a, DecodeTables d) {
+    __shared__ ScoreSmem sm;
+    (void)score_chunk(a, d, blockIdx.y, blockIdx.x, sm);
 }
 
 __global__ void __launch_bounds__(SEL_NT)
@@ -833,13 +989,15 @@ hipError_t launch_score(const SeqInfo *tab, int batch, int topk, const uint16_t 
 hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
                               const uint16_t *q_idx, const float *w, const uint16_t *k_idx,
                               uint16_t *k_blk, uint32_t *keys, uint32_t *cand_key,
-                              int32_t *cand_idx, int ch, int max_chunks, hipStream_t st) {
+                              int32_t *cand_idx, int ch, int max_chunks, int32_t *sel,
+                              uint32_t *ctl, hipStream_t st) {
     if (n_tiles <= 0) return hipSuccess;
     LocalArgs a;
     a.topk = topk; a.q_idx = q_idx; a.w = w; a.k_idx = k_idx; a.k_blk = k_blk; a.keys = keys;
     a.cand_key = cand_key; a.cand_idx = cand_idx; a.ch = ch; a.max_chunks = max_chunks;
+    a.sel = sel; a.ctl = ctl;
     trace_before(2, st);
-    hipLaunchKernelGGL(score_local_kernel, dim3((unsigned)n_tiles, (unsigned)max_chunks),
+    hipLaunchKernelGGL(score_local_kernel, dim3((unsigned)max_chunks, (unsigned)n_tiles),
                        dim3(LOC_NT), 0, st, a, d);
     return trace_after(st, hipGetLastError());
 }
@@ -864,13 +1022,13 @@ int64_t select_lds_cap_keys() {
 hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          const uint32_t *keys, const uint32_t *cand_key, const int32_t *cand_idx,
                          int ch, int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
-                         hipStream_t st) {
+                         int dense_only, hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
     SelectArgs a;
     a.tab = tab; a.batch = batch; a.topk = topk; a.keys = keys;
     a.cand_key = cand_key; a.cand_idx = cand_idx; a.ch = ch; a.max_chunks = max_chunks;
-    a.sel = sel;
-    const int64_t cap = select_lds_cap_keys();
+    a.sel = sel; a.dense_only = dense_only;
+    const int64_t cap = dense_only ? 0 : select_lds_cap_keys();
     int64_t want = max_nvis;
     if (ch > 0) want = want > 2 * (int64_t)max_chunks * KP ? want : 2 * (int64_t)max_chunks * KP;
     a.lds_cap = want < cap ? want : cap;

@@ -25,11 +25,12 @@ hipError_t launch_score(const SeqInfo *tab, int batch, int topk, const uint16_t 
 hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
                               const uint16_t *q_idx, const float *w, const uint16_t *k_idx,
                               uint16_t *k_blk, uint32_t *keys, uint32_t *cand_key,
-                              int32_t *cand_idx, int ch, int max_chunks, hipStream_t st);
+                              int32_t *cand_idx, int ch, int max_chunks, int32_t *sel,
+                              uint32_t *ctl, hipStream_t st);
 hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          const uint32_t *keys, const uint32_t *cand_key, const int32_t *cand_idx,
                          int ch, int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
-                         hipStream_t st);
+                         int dense_only, hipStream_t st);
 hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const int32_t *sel, float *out, float *lse, float *part, int nsplit,

@@ -133,6 +133,33 @@ def test_all_ties_keep_lowest_blocks():
         assert sel[r].tolist() == list(range(n)) + [-1] * (512 - n)
 
 
+@pytest.mark.parametrize("q_lens", [[1, 1], [3, 2]])
+def test_decode_all_ties_exact_fallback(q_lens):
+    """All-equal scores on decode-shaped calls: the first chunk keeps every one of its
+    candidates, so the chunk union cannot be trusted and the exact path (rows scored
+    again by the selecting workgroup) must give the lowest blocks."""
+    _banner(f"decode all ties q_lens={q_lens}")
+    p = gen.make_problem([9000, 5000], q_lens=q_lens, seed=13)
+    p.q_idx[:] = 0
+    sel, _ = _check_rows(f"decode-ties{q_lens}", DeviceProblem(p, 512), None, 512)
+    assert sel[0].tolist() == list(range(512))
+
+
+def test_decode_clustered_top_blocks_exact_fallback():
+    """The best blocks of a decode row packed into one contiguous run of 300 blocks (far
+    more than one chunk's candidates): exact fallback, bit-exact selection."""
+    _banner("decode clustered top blocks")
+    p = gen.make_problem([60000, 30000], q_lens=[1, 1], seed=14)
+    for b, (k0, t) in enumerate([(0, 59999), (60000, 29999)]):
+        u = (p.w[b][:, None].astype(np.float64) *
+             gen.bf16_to_f32(p.q_idx[b]).astype(np.float64)).sum(axis=0)
+        val = np.where(u >= 0, 0x4040, 0xC040).astype(np.uint16)   # +3 / -3 in bf16
+        first = 2500 if b == 0 else 700
+        p.k_idx[k0 + 4 * first: k0 + 4 * (first + 300)] = val[None, :]
+    sel, _ = _check_rows("decode-cluster", DeviceProblem(p, 512), None, 512)
+    assert set(range(2500, 2800)) <= set(sel[0].tolist())
+
+
 def test_float_indexer_tie_tolerant():
     """Non-integer indexer data: fp32 GPU scores may round differently from the
     double oracle, so each kept block must score within 1e-5 relative of the
