@@ -58,14 +58,16 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--rotate", type=int, default=4, help="distinct query sets / cache copies")
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--trace-steps", type=int, default=8)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 4 plain device copies of MIB MiB (reference for HBM "
                          "byte counters) and exit")
@@ -139,6 +141,20 @@ def run_decode(args, torch, qsa, gen):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # one HIP graph holding R consecutive steps (one per rotation set): a replay runs the
+    # library's kernels for R steps as recorded, with one launch
+    graph = None
+    if not args.no_graph:
+        if args.steps % R:
+            sys.exit(f"--steps must be a multiple of --rotate ({R}) with graph replay")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for r in range(R):
+                step(r)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup // R)):
+            graph.replay()
+        torch.cuda.synchronize()
     # correctness guard on the timed configuration: needles of set 0 selected
     sel0 = sets[0]["sel"].cpu().numpy()
     for b, needles in p.needles.items():
@@ -149,13 +165,18 @@ def run_decode(args, torch, qsa, gen):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
-        step(i)
+    if graph is None:
+        for i in range(args.steps):
+            step(i)
+    else:
+        for _ in range(args.steps // R):
+            graph.replay()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gpu_ms = ev0.elapsed_time(ev1)
-    log(f"decode: {args.steps} steps, wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+    log(f"decode: {args.steps} steps ({'eager' if graph is None else 'graph replay'}), "
+        f"wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
 
     # instrumented pass: per-kernel durations with HIP events on the library's stream
     with qsa.trace(4096) as tr:
@@ -295,7 +316,8 @@ def main():
         "config": {"workload": "decode: 16 sequences x 262,144 tokens of context, 1 query "
                                "token each, budget 512 blocks of 4 tokens",
                    "batch": d["batch"], "context": d["ctx"], "budget_blocks": TOPK,
-                   "rotation_sets": args.rotate},
+                   "rotation_sets": args.rotate,
+                   "launch": "eager" if args.no_graph else "hip graph replay"},
         "roofline": roofline,
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_gbs": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},

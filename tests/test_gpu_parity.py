@@ -8,9 +8,10 @@ import numpy as np
 import pytest
 import torch
 
+import long_context_block_qsa_amd as qsa
 import oracle
 import qsa_inputs as gen
-from tests.gpu_helpers import LSE_ABS, MAX_ABS, MEAN_ABS, DeviceProblem, errs
+from tests.gpu_helpers import LSE_ABS, MAX_ABS, MEAN_ABS, DeviceProblem, errs, host16
 
 pytestmark = pytest.mark.gpu
 
@@ -235,6 +236,38 @@ def test_incremental_compress_completes_cache(lens, q_lens, topk):
     gpu = dp.forward(with_k_idx=True)
     assert np.array_equal(gpu[0], ref)
     _check_rows(f"incremental{lens}", dp, None, topk, gpu=gpu)
+
+
+def test_graph_replay_matches_eager():
+    """A decode forward captured in a HIP graph, replayed several times with eager
+    library work and synchronisations in between: every replay equals the eager
+    result bit for bit (the workspace control block is left zero by every call)."""
+    _banner("graph replay")
+    p = gen.make_problem([20000, 9000], q_lens=[1, 1], seed=15)
+    dp = DeviceProblem(p, 512)
+    eager = dp.forward()
+    other = DeviceProblem(gen.make_problem([5000], q_lens=[1], seed=16), 512)
+    other_ref = other.forward()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qsa.forward(dp.seqs, dp.q, dp.k, dp.v, dp.q_idx, dp.w, dp.k_idx, dp.k_blk, dp.sel,
+                    dp.out, dp.lse, dp.ws, dp.topk)
+    for i in range(4):
+        dp.sel.fill_(-7)
+        dp.out.fill_(float("nan"))
+        dp.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (host16(dp.k_blk), dp.sel.cpu().numpy(), dp.out.cpu().numpy(), dp.lse.cpu().numpy())
+        for x, y in zip(got, eager):
+            assert np.array_equal(x, y), f"replay {i} differs from the eager forward"
+        # eager work on the same workspace between replays
+        qsa.forward(dp.seqs, dp.q, dp.k, dp.v, dp.q_idx, dp.w, dp.k_idx, dp.k_blk, dp.sel,
+                    dp.out, dp.lse, dp.ws, dp.topk)
+        torch.cuda.synchronize()
+        for x, y in zip(other.forward(), other_ref):
+            assert np.array_equal(x, y)
 
 
 def test_select_and_attend_entry_points():
