@@ -63,6 +63,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=4, help="distinct query sets / cache copies")
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context decode line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--trace-steps", type=int, default=8)
@@ -183,8 +184,59 @@ def run_decode(args, torch, qsa, gen):
         for i in range(args.trace_steps):
             step(i)
     torch.cuda.synchronize()
+    long_ctx = None if args.no_1m else run_decode_1m(args, torch, qsa, gen, k, v, k_idx, sets)
     return dict(p=p, batch=batch, ctx=ctx, wall_s=wall, gpu_ms=gpu_ms,
-                kernels=tr.mean_ms(), kernel_total=tr.total_ms(), seqs=seqs, sets=sets)
+                kernels=tr.mean_ms(), kernel_total=tr.total_ms(), seqs=seqs, sets=sets,
+                long_ctx=long_ctx)
+
+
+def run_decode_1m(args, torch, qsa, gen, k, v, k_idx, sets):
+    """Decode at 1,048,576 tokens of context (the extended window): the resident
+    4,194,304-token K/V, indexer keys and compressed caches, read as 4 sequences of
+    1,048,576 tokens with fresh query tokens; same rotation and timing protocol."""
+    L, batch = 1 << 20, 4
+    if k.shape[0] != L * batch:
+        return None
+    dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    cu_k = np.arange(batch + 1, dtype=np.int32) * L
+    cu_q = np.arange(batch + 1, dtype=np.int32)
+    seqs = qsa.Seqs(cu_q, cu_k)
+    R = len(sets)
+    qs = []
+    for r in range(R):
+        s2 = 60_000 + r
+        qs.append(dict(
+            q=dev16(gen.normal_bf16(s2, gen.TID_Q, batch * HQ * D).reshape(batch, HQ, D)),
+            q_idx=dev16(gen.uniform_int_bf16(s2, gen.TID_QIDX, batch * HI * DI, -3, 3).reshape(
+                batch, HI, DI)),
+            w=torch.from_numpy(gen.weights(s2, gen.TID_W, batch * HI).reshape(batch, HI)).cuda(),
+            sel=torch.empty((batch, TOPK), dtype=torch.int32, device="cuda"),
+            out=torch.empty((batch, HQ, D), dtype=torch.float32, device="cuda"),
+            lse=torch.empty((batch, HQ), dtype=torch.float32, device="cuda")))
+    ws = qsa.alloc_workspace(seqs, TOPK)
+
+    def step(i):
+        s, kb = qs[i % R], sets[i % R]["k_blk"]
+        qsa.forward(seqs, s["q"], k, v, s["q_idx"], s["w"], k_idx, kb, s["sel"], s["out"],
+                    s["lse"], ws, TOPK)
+
+    for i in range(max(args.warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(R, args.steps // 2 // R * R)
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    ab = decode_algorithmic_bytes(batch, L)
+    gbs = ab["total"] / (ms / 1e3) / 1e9
+    log(f"decode 1M: {n} steps, {ms * 1e3:.1f} us/step")
+    return {"workload": "decode: 4 sequences x 1,048,576 tokens of context, 1 query token "
+                        "each, budget 512 blocks", "steps": n, "launch": "eager",
+            "ms_per_step": round(ms, 5), "query_tokens_per_s": round(batch / (ms / 1e3), 1),
+            "algorithmic_bytes": ab["total"], "achieved_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 # ---------------------------------------------------------------- prefill workload
@@ -323,6 +375,8 @@ def main():
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "kernel_mean_ms": {k2: round(v2, 5) for k2, v2 in kern.items()},
     }
+    if d["long_ctx"] is not None:
+        line["decode_1m"] = d["long_ctx"]
     if not args.no_prefill:
         log("prefill workload")
         line["prefill"] = run_prefill(args, torch, qsa, gen)

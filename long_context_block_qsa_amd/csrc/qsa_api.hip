@@ -83,7 +83,8 @@ struct Plan {
     int max_chunks = 0;         // chunks of the longest scored row (decode path)
     int nsplit = 1;             // attention key splits per row
     int64_t n_dense = 0;        // query rows with at most topk visible blocks
-    size_t off_ctl = 0, off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, ws_bytes = 0;
+    size_t off_ctl = 0, off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, off_glist = 0;
+    size_t ws_bytes = 0;
     bool use_dec = false;       // few rows: row/tile tables travel as kernel arguments
     bool fuse_compress = false; // decode: scoring workgroups compress the new blocks
     qsa::DecodeTables dec;
@@ -212,6 +213,9 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     const size_t score_b = align_up((size_t)p->n_slots * sizeof(uint32_t));
     const size_t cand_b = p->local_ch > 0
         ? align_up((size_t)p->tq * p->max_chunks * kKP * 2 * sizeof(uint32_t)) : 0;
+    // group merge results of rows with more than 64 chunks (at most 4 groups of topk)
+    const size_t glist_b = p->local_ch > 0 && p->max_chunks > 64
+        ? align_up((size_t)p->tq * 4 * p->topk * 2 * sizeof(uint32_t)) : 0;
     const size_t part_b = p->nsplit > 1
         ? align_up((size_t)p->tq * p->nsplit * qsa::HQ * (qsa::HD + 4) * sizeof(float)) : 0;
     p->off_ctl = 0;
@@ -219,7 +223,8 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     p->off_sel = ctl_b + tab_b;
     p->off_union = ctl_b + tab_b + sel_b;  // scores (+ candidates) while selecting, then partials
     p->off_cand = p->off_union + score_b;
-    p->ws_bytes = p->off_union + std::max(score_b + cand_b, part_b);
+    p->off_glist = p->off_cand + cand_b;
+    p->ws_bytes = p->off_union + std::max(score_b + cand_b + glist_b, part_b);
     return QSA_OK;
 }
 
@@ -253,9 +258,12 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
         cand_idx = reinterpret_cast<int32_t *>(cand_key + (size_t)p.tq * p.max_chunks * 32);
         // scoring selects the scored rows itself; a select launch remains only for rows
         // within the budget
+        uint32_t *glist_key = ws_at<uint32_t>(ws, p.off_glist);
+        int32_t *glist_idx = reinterpret_cast<int32_t *>(glist_key + (size_t)p.tq * 4 * p.topk);
         QSA_TRY(qsa::launch_score_local(p.dec, p.n_tiles, p.topk, q_idx, w, k_idx, k_blk, keys,
                                         cand_key, cand_idx, p.local_ch, p.max_chunks, sel,
-                                        ws_at<uint32_t>(ws, p.off_ctl), st));
+                                        glist_key, glist_idx, ws_at<uint32_t>(ws, p.off_ctl),
+                                        st));
         if (p.n_dense > 0)
             QSA_TRY(qsa::launch_select(tab, &p.dec, p.batch, p.topk, keys, cand_key, cand_idx,
                                        p.local_ch, p.max_chunks, sel, p.tq, p.max_score_blocks,

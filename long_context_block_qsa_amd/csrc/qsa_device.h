@@ -44,8 +44,12 @@ constexpr int DEC_MAX = 64;
 
 // Control block at the start of the workspace: counters through which workgroups of
 // one kernel hand work to each other. Zero before a call; every call leaves it zero.
-//   words [0, 64): score tiles, chunks scored so far
+//   [0, 64)    per score tile: chunks (or chunk groups) merged so far
+//   [64, 320)  per (tile, group of chunks): chunks scored so far
+//   [320, 384) per query row: the row needs the exact selection
 constexpr int CTL_TILE = 0;
+constexpr int CTL_GROUP = 64;
+constexpr int CTL_EXACT = 320;
 constexpr int CTL_WORDS = 1024;
 struct DecRow {
     int32_t k0;     // first key row of the row's sequence

@@ -300,29 +300,34 @@ __device__ __forceinline__ void select_keys(KP_T kk, IP_T ii, int64_t n, int top
     emit_kept<SEL_NT, PER>(kk, ii, n, theta, need, out, nullptr, topk, scan_sh, grp_cnt, group);
 }
 
-// Selection of a row from the union of its chunk candidates (rows with nvis > topk
-// that are eligible and have at most 64 chunks). Returns true when the result is
-// exact: no full chunk (more than KP blocks) had all KP of its candidates kept, since
-// only such a chunk can hide a better block. WT: candidates were written by other
-// workgroups of the same kernel and are read with agent-scope loads.
-template <bool WT>
-__device__ __forceinline__ bool select_from_candidates(const SelectArgs &a, int64_t nv,
-                                                       int64_t row, int *viol, TopkSmem *tsm) {
-    int32_t *out = a.sel + row * a.topk;
+// Level-one merges take at most MERGE_CHUNKS chunk lists (KP candidates each); rows
+// with more chunks first merge groups of MERGE_CHUNKS chunks, then the group lists
+// (topk entries each) of at most MAX_GROUPS groups.
+constexpr int MERGE_CHUNKS = 64;
+constexpr int MAX_GROUPS = 4;
+
+// Top-k of the n <= 2048 candidates (key, id) at ck[0..n) / ci[0..n) (written by other
+// workgroups of this kernel: agent-scope loads); key 0 marks padding, which is never
+// kept because every caller has at least k real candidates. Kept ids go out in
+// position order: to out_idx with plain stores, or (WT_OUT) with their keys through to
+// the coherence point, padded with key 0 / id -1 up to k. When nv > 0 the positions are
+// the KP-entry lists of chunks c0, c0+1, ... of a row with nv visible blocks: returns
+// false if a chunk holding more than KP of the row's blocks had all KP candidates kept
+// (only such a chunk can hide a better block, so only then can the result be inexact).
+template <bool WT_OUT>
+__device__ __forceinline__ bool merge_candidates(const uint32_t *ck, const int32_t *ci, int n,
+                                                 int k, int32_t *out_idx, uint32_t *out_key,
+                                                 int64_t nv, int ch, int c0, int *viol,
+                                                 TopkSmem *tsm) {
     const int tid = threadIdx.x;
-    // thread t holds candidate positions 8t .. 8t+7 (chunk t/4) in registers
-    const int nchunk = (int)((nv + a.ch - 1) / a.ch);
-    const int n = nchunk * KP;   // padding entries carry key 0, never kept
-    const int c = min(tid / 4, nchunk - 1), part = tid % 4;
-    const uint32_t *ck = a.cand_key + (row * a.max_chunks + c) * KP + 8 * part;
-    const int32_t *ci = a.cand_idx + (row * a.max_chunks + c) * KP + 8 * part;
     uint32_t x[8];
     int32_t id[8];
     u32x4 kq[2], iq[2];
+    const bool have = 8 * tid < n;
 #pragma unroll
     for (int v4 = 0; v4 < 2; ++v4) {
-        kq[v4] = WT ? load16_wt(ck + 4 * v4) : load16(ck + 4 * v4);
-        iq[v4] = WT ? load16_wt(ci + 4 * v4) : load16(ci + 4 * v4);
+        kq[v4] = have ? load16_wt(ck + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
+        iq[v4] = have ? load16_wt(ci + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int v4 = 0; v4 < 2; ++v4) {
@@ -335,33 +340,46 @@ __device__ __forceinline__ bool select_from_candidates(const SelectArgs &a, int6
     if (tid == 0) *viol = 0;
     uint32_t kept;
     int first;
-    block_topk_regs<SEL_NT, 8>(x, n, a.topk, *tsm, &kept, &first);
+    const int tot = block_topk_regs<SEL_NT, 8>(x, n, k, *tsm, &kept, &first);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         if (kept & (1u << e)) {
-            if (first < a.topk) out[first] = id[e];
+            if (first < k) {
+                if (WT_OUT) {
+                    store_wt(out_key + first, x[e]);
+                    store_wt(out_idx + first, id[e]);
+                } else {
+                    out_idx[first] = id[e];
+                }
+            }
             ++first;
         }
     }
-    int kc = __popc(kept);
-    kc += __shfl_xor(kc, 1);
-    kc += __shfl_xor(kc, 2);
-    const int64_t nc = tid / 4 < nchunk ? min<int64_t>(a.ch, nv - (int64_t)(tid / 4) * a.ch) : 0;
-    if (nc > KP && kc >= KP) *viol = 1;
+    if (WT_OUT) {
+        for (int i = tot + tid; i < k; i += SEL_NT) {
+            store_wt(out_key + i, 0u);
+            store_wt(out_idx + i, -1);
+        }
+    }
+    if (nv > 0) {
+        int kc = __popc(kept);
+        kc += __shfl_xor(kc, 1);
+        kc += __shfl_xor(kc, 2);
+        static_assert(KP == 32, "4 threads hold one chunk list");
+        const int c = c0 + tid / 4;
+        const int64_t nc = have ? min<int64_t>(ch, nv - (int64_t)c * ch) : 0;
+        if (nc > KP && kc >= KP) *viol = 1;
+    }
     __syncthreads();
     return !*viol;
 }
 
-__device__ __forceinline__ bool uses_candidates(const SelectArgs &a, int64_t nv) {
-    return a.ch > 0 && cand_eligible(nv, a.topk, a.ch) && (nv + a.ch - 1) / a.ch <= WAVE;
-}
-
-// One workgroup selects one query row. Rows within the budget keep blocks 0..nvis-1.
-// Other rows: the union of chunk candidates when that is exact, else an exact radix
-// select over the row's full key row (staged in dynamic LDS when it fits).
+// One workgroup selects one query row from its full key row: rows within the budget
+// keep blocks 0..nvis-1, others get an exact radix select (keys staged in dynamic LDS
+// when they fit).
 __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView rv, int64_t row,
                                             uint32_t *dyn, uint32_t *hist, int32_t *scan_sh,
-                                            uint32_t *found, int *viol, TopkSmem *tsm) {
+                                            uint32_t *found) {
     const int64_t nv = nvis_of(rv.t);
     int32_t *out = a.sel + row * a.topk;
     const int tid = threadIdx.x;
@@ -370,8 +388,6 @@ __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView r
         return;
     }
     if (a.dense_only) return;
-    if (uses_candidates(a, nv) && select_from_candidates<false>(a, nv, row, viol, tsm)) return;
-
     const uint32_t *rk = a.keys + rv.slot;
     if (nv <= a.lds_cap) {
         for (int64_t i0 = tid; i0 < nv; i0 += 8 * SEL_NT) {
@@ -404,7 +420,9 @@ struct LocalArgs {
     int32_t *cand_idx;
     int ch, max_chunks;
     int32_t *sel;
-    uint32_t *ctl;           // per-tile arrival counters (zero between calls)
+    uint32_t *glist_key;     // [row][MAX_GROUPS][topk] group merge results
+    int32_t *glist_idx;
+    uint32_t *ctl;           // arrival counters and flags (zero between calls)
 };
 
 // Scores blocks [lo, hi) of a tile; store(row, blk, key) is called for each block
@@ -425,30 +443,16 @@ __device__ __forceinline__ void score_range(const ScoreLane &sl, const uint16_t 
     }
 }
 
-// Selection of every row of a decode tile by the workgroup that scored its last
-// chunk: from the chunk candidates where that is exact; the other rows get an exact
-// radix select over key rows this workgroup recomputes itself (after recompressing
-// the tile's new blocks, so that it reads only its own writes).
-__device__ __forceinline__ void select_tile(const LocalArgs &a, const DecodeTables &d, int tile,
-                                         uint32_t *hist, int32_t *scan_sh, uint32_t *found,
-                                         int *viol, int *exact, TopkSmem *tsm) {
+// Exact selection of the rows of a tile flagged in exact[] from key rows this
+// workgroup recomputes itself (after recompressing the tile's new blocks, so that it
+// reads only its own writes).
+__device__ __forceinline__ void select_tile_exact(const LocalArgs &a, const DecodeTables &d,
+                                                  int tile, const int *exact, uint32_t *hist,
+                                                  int32_t *scan_sh, uint32_t *found) {
     const DecTile tl = d.tile[tile];
     const int64_t row0 = tl.row0;
     const int nrows = tl.nrows;
     const int64_t t0 = d.row[row0].t;
-    SelectArgs sa;
-    sa.tab = nullptr; sa.batch = 0; sa.topk = a.topk; sa.keys = a.keys;
-    sa.cand_key = a.cand_key; sa.cand_idx = a.cand_idx; sa.ch = a.ch;
-    sa.max_chunks = a.max_chunks; sa.sel = a.sel; sa.lds_cap = 0; sa.dense_only = 0;
-    int n_exact = 0;
-    for (int rr = 0; rr < nrows; ++rr) {
-        const int64_t nv = nvis_of(t0 + rr);
-        const bool done = uses_candidates(sa, nv) &&
-                          select_from_candidates<true>(sa, nv, row0 + rr, viol, tsm);
-        if (threadIdx.x == 0) exact[rr] = !done;
-        n_exact += !done;   // uniform
-    }
-    if (n_exact == 0) return;
     const DecRow r0 = d.row[row0];
     if (a.k_idx && tl.new_hi > tl.new_lo) {
         for (int64_t blk = tl.new_lo + threadIdx.x / 8; blk < tl.new_hi; blk += LOC_NT / 8)
@@ -466,7 +470,7 @@ __device__ __forceinline__ void select_tile(const LocalArgs &a, const DecodeTabl
     wait_vmem();
     __syncthreads();
     for (int rr = 0; rr < nrows; ++rr) {
-        if (!exact[rr]) continue;   // uniform (LDS, after the barrier)
+        if (!exact[rr]) continue;   // uniform (LDS)
         const DecRow r = d.row[row0 + rr];
         select_keys<16>((const uint32_t *)(a.keys + r.slot), (const int32_t *)nullptr,
                         nvis_of(r.t), a.topk, a.sel + (row0 + rr) * a.topk, hist, scan_sh,
@@ -601,18 +605,81 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
         if (rr + 1 < nrows) lds_barrier();   // wave lists are reused by the next row
     }
 
-    // hand over: the workgroup that completes the tile's last chunk selects its rows
+    // hand over: the workgroup that completes the tile's last chunk merges the rows'
+    // candidates; rows with more than MERGE_CHUNKS chunks merge groups of chunks first
+    // (the last chunk of each group), then the group lists (the tile's last group)
     wait_vmem();
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t nch = (uint32_t)((nv_max + a.ch - 1) / a.ch);
+    const int tid = threadIdx.x;
+    const int nch = (int)((nv_max + a.ch - 1) / a.ch);
+    const int ngroups = (nch + MERGE_CHUNKS - 1) / MERGE_CHUNKS;
+    // groups of chunks are merged separately when there are 2 .. MAX_GROUPS of them
+    const bool grouped = ngroups > 1 && ngroups <= MAX_GROUPS;
+    if (grouped) {
+        const int grp = chunk / MERGE_CHUNKS;
+        const int n_in = min(MERGE_CHUNKS, nch - grp * MERGE_CHUNKS);
+        if (tid == 0) {
+            uint32_t *cnt = &a.ctl[CTL_GROUP + tile * MAX_GROUPS + grp];
+            const uint32_t old = atomicAdd(cnt, 1u);
+            sm.s_last = old + 1 == (uint32_t)n_in;
+            if (sm.s_last) store_wt(cnt, 0u);
+        }
+        __syncthreads();
+        if (!sm.s_last) return false;
+        for (int rr = 0; rr < nrows; ++rr) {
+            const int64_t nv = nvis_of(t0 + rr), row = row0 + rr;
+            if (!cand_eligible(nv, a.topk, a.ch)) continue;   // uniform
+            const int64_t cbase = (row * a.max_chunks + grp * MERGE_CHUNKS) * KP;
+            const int64_t gbase = (row * MAX_GROUPS + grp) * a.topk;
+            const bool ok = merge_candidates<true>(
+                a.cand_key + cbase, a.cand_idx + cbase, n_in * KP, a.topk, a.glist_idx + gbase,
+                a.glist_key + gbase, nv, a.ch, grp * MERGE_CHUNKS, &sm.viol, &sm.tsm);
+            if (!ok && tid == 0) store_wt(&a.ctl[CTL_EXACT + row], 1u);
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+    // the tile counter counts merged groups, or chunks when no grouping is used
+    if (tid == 0) {
         const uint32_t old = atomicAdd(&a.ctl[CTL_TILE + tile], 1u);
-        sm.s_last = old + 1 == nch;
+        sm.s_last = old + 1 == (uint32_t)(grouped ? ngroups : nch);
         if (sm.s_last) store_wt(&a.ctl[CTL_TILE + tile], 0u);
     }
     __syncthreads();
     if (!sm.s_last) return false;
-    select_tile(a, d, tile, sm.hist, sm.scan_sh, sm.found, &sm.viol, sm.exact, &sm.tsm);
+
+    // this workgroup selects the tile's rows
+    int n_exact = 0;
+    for (int rr = 0; rr < nrows; ++rr) {
+        const int64_t nv = nvis_of(t0 + rr), row = row0 + rr;
+        bool done = false;
+        if (cand_eligible(nv, a.topk, a.ch) && ngroups <= MAX_GROUPS) {
+            if (grouped) {
+                if (tid == 0) {
+                    sm.exact[rr] = load_wt(&a.ctl[CTL_EXACT + row]) != 0u;
+                    store_wt(&a.ctl[CTL_EXACT + row], 0u);
+                }
+                __syncthreads();
+                if (!sm.exact[rr]) {
+                    const int64_t gbase = row * MAX_GROUPS * a.topk;
+                    done = merge_candidates<false>(a.glist_key + gbase, a.glist_idx + gbase,
+                                                   ngroups * a.topk, a.topk, a.sel + row * a.topk,
+                                                   nullptr, 0, a.ch, 0, &sm.viol, &sm.tsm);
+                }
+            } else {
+                const int64_t cbase = row * a.max_chunks * KP;
+                const int nch_row = (int)((nv + a.ch - 1) / a.ch);
+                done = merge_candidates<false>(a.cand_key + cbase, a.cand_idx + cbase,
+                                               nch_row * KP, a.topk, a.sel + row * a.topk,
+                                               nullptr, nv, a.ch, 0, &sm.viol, &sm.tsm);
+            }
+        }
+        __syncthreads();
+        if (tid == 0) sm.exact[rr] = !done;
+        n_exact += !done;   // uniform
+    }
+    __syncthreads();
+    if (n_exact > 0) select_tile_exact(a, d, tile, sm.exact, sm.hist, sm.scan_sh, sm.found);
     return true;
 }
 
@@ -629,11 +696,8 @@ select_kernel(SelectArgs a) {
     __shared__ uint32_t hist[kHistBins];  // histograms; then per-chunk kept counts
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
     __shared__ uint32_t found[2];
-    __shared__ int viol;
-    __shared__ TopkSmem tsm;
     const int64_t row = blockIdx.x;
-    select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, dyn, hist, scan_sh, found, &viol,
-                &tsm);
+    select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, dyn, hist, scan_sh, found);
 }
 
 __global__ void __launch_bounds__(SEL_NT)
@@ -642,12 +706,10 @@ select_dec_kernel(SelectArgs a, DecodeTables d) {
     __shared__ uint32_t hist[kHistBins];
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
     __shared__ uint32_t found[2];
-    __shared__ int viol;
-    __shared__ TopkSmem tsm;
     const int64_t row = blockIdx.x;
     const DecRow r = d.row[row];
     const RowView rv = {r.k0, r.t, r.blk0, r.slot};
-    select_body(a, rv, row, dyn, hist, scan_sh, found, &viol, &tsm);
+    select_body(a, rv, row, dyn, hist, scan_sh, found);
 }
 
 // =============================================================== attend
@@ -990,12 +1052,13 @@ hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
                               const uint16_t *q_idx, const float *w, const uint16_t *k_idx,
                               uint16_t *k_blk, uint32_t *keys, uint32_t *cand_key,
                               int32_t *cand_idx, int ch, int max_chunks, int32_t *sel,
-                              uint32_t *ctl, hipStream_t st) {
+                              uint32_t *glist_key, int32_t *glist_idx, uint32_t *ctl,
+                              hipStream_t st) {
     if (n_tiles <= 0) return hipSuccess;
     LocalArgs a;
     a.topk = topk; a.q_idx = q_idx; a.w = w; a.k_idx = k_idx; a.k_blk = k_blk; a.keys = keys;
     a.cand_key = cand_key; a.cand_idx = cand_idx; a.ch = ch; a.max_chunks = max_chunks;
-    a.sel = sel; a.ctl = ctl;
+    a.sel = sel; a.glist_key = glist_key; a.glist_idx = glist_idx; a.ctl = ctl;
     trace_before(2, st);
     hipLaunchKernelGGL(score_local_kernel, dim3((unsigned)max_chunks, (unsigned)n_tiles),
                        dim3(LOC_NT), 0, st, a, d);

@@ -26,7 +26,8 @@ hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
                               const uint16_t *q_idx, const float *w, const uint16_t *k_idx,
                               uint16_t *k_blk, uint32_t *keys, uint32_t *cand_key,
                               int32_t *cand_idx, int ch, int max_chunks, int32_t *sel,
-                              uint32_t *ctl, hipStream_t st);
+                              uint32_t *glist_key, int32_t *glist_idx, uint32_t *ctl,
+                              hipStream_t st);
 hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          const uint32_t *keys, const uint32_t *cand_key, const int32_t *cand_idx,
                          int ch, int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,

@@ -119,6 +119,39 @@ def test_config4_ragged_prefill_sampled():
     _check_rows("cfg4", DeviceProblem(p), sorted(rows), 512)
 
 
+# ----------------------------------------------------------------- long contexts
+
+def test_decode_1m_context_grouped_merge():
+    """One decode row at 1,048,576 tokens (262,144 blocks, 256 chunks): candidates are
+    merged in 4 groups of 64 chunks, then across groups; bit-exact selection, needles
+    kept, outputs within tolerance."""
+    _banner("decode 1M context")
+    p = gen.make_problem([1 << 20], q_lens=[1], seed=17, needles=32)
+    sel, _ = _check_rows("decode-1M", DeviceProblem(p, 512), None, 512)
+    assert set(p.needles[0]) <= set(sel[0].tolist())
+
+
+def test_multi_query_long_rows_grouped():
+    """Three query tokens of one 300,001-token sequence (one tile, 74 chunks, 2 groups)
+    plus a short sequence."""
+    _banner("multi-query grouped")
+    p = gen.make_problem([300001, 7000], q_lens=[3, 2], seed=18)
+    _check_rows("mq-grouped", DeviceProblem(p, 512), None, 512)
+
+
+def test_grouped_merge_exact_fallback():
+    """A grouped row (100,000 blocks) whose best blocks form one run of 300 blocks: the
+    group merge finds a chunk with every candidate kept and the row is selected exactly."""
+    _banner("grouped exact fallback")
+    p = gen.make_problem([400000], q_lens=[1], seed=19)
+    u = (p.w[0][:, None].astype(np.float64) *
+         gen.bf16_to_f32(p.q_idx[0]).astype(np.float64)).sum(axis=0)
+    val = np.where(u >= 0, 0x4040, 0xC040).astype(np.uint16)
+    p.k_idx[4 * 70000: 4 * 70300] = val[None, :]
+    sel, _ = _check_rows("grouped-fallback", DeviceProblem(p, 512), None, 512)
+    assert set(range(70000, 70300)) <= set(sel[0].tolist())
+
+
 # ----------------------------------------------------------------- edge cases / properties
 
 def test_all_ties_keep_lowest_blocks():
