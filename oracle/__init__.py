@@ -79,10 +79,18 @@ def _load():
         lib.qsa_ref_attend.argtypes = [dp, i32, P, P, P, P, P, P, P, P, P, i64, i32]
         lib.qsa_ref_forward.argtypes = [dp, i32, P, P, P, P, P, P, P, P, P, P, P, P,
                                         P, i64, i32]
+        lib.qsa_ref_quantize_kv.argtypes = [dp, i32, P, P, P, P, P, P, P]
+        lib.qsa_ref_attend_fp8.argtypes = [dp, i32, P, P, P, P, P, P, P, P, P, P, P, i64,
+                                           i32]
         lib.qsa_ref_bf16_round.argtypes = [ctypes.c_double]
         lib.qsa_ref_bf16_round.restype = ctypes.c_uint16
+        lib.qsa_ref_e4m3_round.argtypes = [ctypes.c_double]
+        lib.qsa_ref_e4m3_round.restype = ctypes.c_uint8
+        lib.qsa_ref_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.qsa_ref_e4m3_value.restype = ctypes.c_double
         for f in ("qsa_ref_compress", "qsa_ref_row_scores", "qsa_ref_select",
-                  "qsa_ref_attend", "qsa_ref_forward"):
+                  "qsa_ref_attend", "qsa_ref_forward", "qsa_ref_quantize_kv",
+                  "qsa_ref_attend_fp8"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -118,6 +126,51 @@ def _check(rc, name):
 def bf16_round(x: float) -> int:
     """The oracle's double -> bf16 rounding (bit pattern)."""
     return int(_load().qsa_ref_bf16_round(float(x)))
+
+
+def e4m3_round(x: float) -> int:
+    """The oracle's double -> OCP FP8 E4M3 rounding (byte)."""
+    return int(_load().qsa_ref_e4m3_round(float(x)))
+
+
+def e4m3_value(b: int) -> float:
+    """The value of an OCP FP8 E4M3 byte."""
+    return float(_load().qsa_ref_e4m3_value(int(b)))
+
+
+def quantize_kv(dims: Dims, cu_k, k, v):
+    """FP8 KV cache of bf16 K and V: (k8, v8, k_scale, v_scale)."""
+    cu_k = _arr(cu_k, np.int32)
+    k, v = _arr(k, np.uint16), _arr(v, np.uint16)
+    tk = int(cu_k[-1])
+    k8 = np.zeros((tk, dims.n_kv_heads, dims.head_dim), dtype=np.uint8)
+    v8 = np.zeros_like(k8)
+    ks = np.zeros((tk, dims.n_kv_heads), dtype=np.float32)
+    vs = np.zeros_like(ks)
+    d = dims._c()
+    _check(_load().qsa_ref_quantize_kv(ctypes.byref(d), len(cu_k) - 1, _ptr(cu_k), _ptr(k),
+                                       _ptr(v), _ptr(k8), _ptr(v8), _ptr(ks), _ptr(vs)),
+           "quantize_kv")
+    return k8, v8, ks, vs
+
+
+def attend_fp8(dims: Dims, cu_q, cu_k, q, k8, v8, k_scale, v_scale, sel, rows=None,
+               threads=None):
+    """Attention over the dequantized FP8 KV cache. Returns (out, lse)."""
+    cu_q, cu_k = _arr(cu_q, np.int32), _arr(cu_k, np.int32)
+    q, k8, v8 = _arr(q, np.uint16), _arr(k8, np.uint8), _arr(v8, np.uint8)
+    ks, vs = _arr(k_scale, np.float32), _arr(v_scale, np.float32)
+    sel = _arr(sel, np.int32)
+    tq = int(cu_q[-1])
+    out = np.full((tq, dims.n_q_heads, dims.head_dim), np.nan, dtype=np.float64)
+    lse = np.full((tq, dims.n_q_heads), np.nan, dtype=np.float64)
+    r, nr = _rows(rows)
+    d = dims._c()
+    _check(_load().qsa_ref_attend_fp8(ctypes.byref(d), len(cu_k) - 1, _ptr(cu_q), _ptr(cu_k),
+                                      _ptr(q), _ptr(k8), _ptr(v8), _ptr(ks), _ptr(vs),
+                                      _ptr(sel), _ptr(out), _ptr(lse), _ptr(r), nr,
+                                      _threads(threads)), "attend_fp8")
+    return out, lse
 
 
 def n_blocks(dims: Dims, cu_k) -> int:

@@ -54,6 +54,50 @@ uint16_t qsa_ref_bf16_round(double x)
     return (uint16_t)(u >> 16);
 }
 
+/* ------------------------------------------------------------------- fp8 */
+
+/* OCP FP8 E4M3 ("e4m3fn"): sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities, S.1111.111 is NaN, largest finite magnitude 448, subnormals m/8 * 2^-6. */
+static double e4m3_value(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(8.0 + m, e - 10);
+    return s ? -v : v;
+}
+
+double qsa_ref_e4m3_value(uint8_t b) { return e4m3_value(b); }
+
+/* Round x to the nearest E4M3 value, ties to even; finite magnitudes beyond 448
+ * saturate to 448. The rounding quantum is 2^(e-4) for |x| = m * 2^e with
+ * 0.5 <= m < 1, never finer than the subnormal step 2^-9. */
+uint8_t qsa_ref_e4m3_round(double x)
+{
+    uint8_t sign = signbit(x) ? 0x80u : 0x00u;
+    double a = fabs(x);
+    if (a == 0.0)
+        return sign;
+    int e;
+    (void)frexp(a, &e);
+    int qe = (e < -5 ? -5 : e) - 4;
+    double r = ldexp(nearbyint(ldexp(a, -qe)), qe); /* default mode: ties to even */
+    if (r > 448.0)
+        r = 448.0;
+    /* encode r exactly */
+    if (r < 0x1p-6)
+        return (uint8_t)(sign | (uint8_t)nearbyint(ldexp(r, 9)));
+    int re;
+    double mr = frexp(r, &re);              /* r = mr * 2^re, 0.5 <= mr < 1 */
+    int m = (int)nearbyint(ldexp(mr, 4)) - 8;  /* 3 mantissa bits */
+    int eb = re - 1 + 7;                    /* biased exponent */
+    return (uint8_t)(sign | (uint8_t)(eb << 3) | (uint8_t)m);
+}
+
 /* ------------------------------------------------------------ bookkeeping */
 
 static int dims_ok(const qsa_ref_dims *d)
@@ -251,9 +295,26 @@ static void select_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
  * (blog.compendialabs.org, "Qwen Sparse Attention -- Full Attention When It
  * Counts"). Softmax with a max shift, then normalisation; lse = m + ln(l) of the
  * scaled logits. */
+/* One element of K or V: bf16, or (FP8 KV cache) an E4M3 byte times the fp32 scale
+ * of its (token, KV head) row. */
+typedef struct {
+    const uint16_t *bf;
+    const uint8_t *f8;
+    const float *scale;
+} kv_src;
+
+static double kv_value(const kv_src *s, int64_t token, int64_t g, int64_t Hkv, int64_t D,
+                       int64_t c)
+{
+    int64_t r = token * Hkv + g;
+    if (s->f8)
+        return e4m3_value(s->f8[r * D + c]) * (double)s->scale[r];
+    return bf16_value(s->bf[r * D + c]);
+}
+
 static void attend_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
-                       const int32_t *cu_k, const uint16_t *q, const uint16_t *k,
-                       const uint16_t *v, const int32_t *sel_row, int64_t row,
+                       const int32_t *cu_k, const uint16_t *q, const kv_src *k,
+                       const kv_src *v, const int32_t *sel_row, int64_t row,
                        double *out_row, double *lse_row)
 {
     const int64_t Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
@@ -282,10 +343,9 @@ static void attend_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
         const uint16_t *qh = q + (row * Hq + h) * D;
         double m = -INFINITY;
         for (int64_t i = 0; i < nj; ++i) {
-            const uint16_t *kh = k + ((p.key0 + J[i]) * Hkv + g) * D;
             double dot = 0.0;
             for (int64_t c = 0; c < D; ++c)
-                dot += bf16_value(qh[c]) * bf16_value(kh[c]);
+                dot += bf16_value(qh[c]) * kv_value(k, p.key0 + J[i], g, Hkv, D, c);
             z[i] = dot * scale;
             if (z[i] > m)
                 m = z[i];
@@ -298,11 +358,9 @@ static void attend_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
         double *o = out_row + h * D;
         for (int64_t c = 0; c < D; ++c)
             o[c] = 0.0;
-        for (int64_t i = 0; i < nj; ++i) {
-            const uint16_t *vh = v + ((p.key0 + J[i]) * Hkv + g) * D;
+        for (int64_t i = 0; i < nj; ++i)
             for (int64_t c = 0; c < D; ++c)
-                o[c] += z[i] * bf16_value(vh[c]);
-        }
+                o[c] += z[i] * kv_value(v, p.key0 + J[i], g, Hkv, D, c);
         for (int64_t c = 0; c < D; ++c)
             o[c] /= l;
         if (lse_row)
@@ -319,7 +377,8 @@ typedef struct {
     const qsa_ref_dims *d;
     int32_t batch;
     const int32_t *cu_q, *cu_k;
-    const uint16_t *q, *k, *v, *q_idx, *k_blk;
+    const uint16_t *q, *q_idx, *k_blk;
+    kv_src k, v;
     const float *w;
     int32_t *sel_w;
     const int32_t *sel_r;
@@ -338,7 +397,7 @@ static void *run_rows(void *arg)
             select_row(j->d, j->batch, j->cu_q, j->cu_k, j->q_idx, j->w, j->k_blk, r,
                        j->sel_w + r * kb);
         else
-            attend_row(j->d, j->batch, j->cu_q, j->cu_k, j->q, j->k, j->v,
+            attend_row(j->d, j->batch, j->cu_q, j->cu_k, j->q, &j->k, &j->v,
                        j->sel_r + r * kb, r, j->out + r * Hq * D,
                        j->lse ? j->lse + r * Hq : NULL);
     }
@@ -417,8 +476,69 @@ int qsa_ref_attend(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
     j.cu_q = cu_q;
     j.cu_k = cu_k;
     j.q = q;
-    j.k = k;
-    j.v = v;
+    j.k.bf = k;
+    j.v.bf = v;
+    j.sel_r = sel;
+    j.out = out;
+    j.lse = lse;
+    j.rows = rows;
+    for_rows(j, rows ? n_rows : cu_q[batch], n_threads);
+    return 0;
+}
+
+/* FP8 KV cache (a variant of the attention's K/V storage; the attention is defined on
+ * the dequantized values): each (token, KV head) row x of K or V gets the fp32 scale
+ * s = amax|x| / 448 (1 for an all-zero row) and the bytes e4m3_round(fp32(x / s)),
+ * both divisions in fp32 (computed here in double and rounded once to fp32, which
+ * gives the correctly rounded fp32 quotient). */
+int qsa_ref_quantize_kv(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_k,
+                        const uint16_t *k, const uint16_t *v, uint8_t *k8, uint8_t *v8,
+                        float *k_scale, float *v_scale)
+{
+    if (!dims_ok(d) || !seqs_ok(batch, NULL, cu_k) || !k || !v || !k8 || !v8 ||
+        !k_scale || !v_scale)
+        return -1;
+    const int64_t rows = (int64_t)cu_k[batch] * d->n_kv_heads, D = d->head_dim;
+    for (int which = 0; which < 2; ++which) {
+        const uint16_t *x = which ? v : k;
+        uint8_t *q8 = which ? v8 : k8;
+        float *sc = which ? v_scale : k_scale;
+        for (int64_t r = 0; r < rows; ++r) {
+            double amax = 0.0;
+            for (int64_t c = 0; c < D; ++c)
+                amax = fmax(amax, fabs(bf16_value(x[r * D + c])));
+            float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+            sc[r] = s;
+            for (int64_t c = 0; c < D; ++c) {
+                float y = (float)(bf16_value(x[r * D + c]) / (double)s);
+                q8[r * D + c] = qsa_ref_e4m3_round((double)y);
+            }
+        }
+    }
+    return 0;
+}
+
+int qsa_ref_attend_fp8(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                       const int32_t *cu_k, const uint16_t *q, const uint8_t *k8,
+                       const uint8_t *v8, const float *k_scale, const float *v_scale,
+                       const int32_t *sel, double *out, double *lse, const int64_t *rows,
+                       int64_t n_rows, int32_t n_threads)
+{
+    if (!dims_ok(d) || !cu_q || !seqs_ok(batch, cu_q, cu_k) || !sel || !out || !k8 || !v8 ||
+        !k_scale || !v_scale || !rows_ok(cu_q, batch, rows, n_rows))
+        return -1;
+    row_job j;
+    memset(&j, 0, sizeof j);
+    j.op = 1;
+    j.d = d;
+    j.batch = batch;
+    j.cu_q = cu_q;
+    j.cu_k = cu_k;
+    j.q = q;
+    j.k.f8 = k8;
+    j.k.scale = k_scale;
+    j.v.f8 = v8;
+    j.v.scale = v_scale;
     j.sel_r = sel;
     j.out = out;
     j.lse = lse;

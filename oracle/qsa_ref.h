@@ -87,8 +87,26 @@ int qsa_ref_forward(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
                     double *out, double *lse, const int64_t *rows, int64_t n_rows,
                     int32_t n_threads);
 
-/* The bf16 rounding the oracle uses (exposed so tests can pin it). */
+/* FP8 KV cache: K and V as OCP FP8 E4M3 bytes [Tk, Hkv, D] with one fp32 scale per
+ * (token, KV head) [Tk, Hkv]; a stored element means byte value * scale. The scale
+ * of a row is amax / 448 (1 for an all-zero row) and each byte is the E4M3 rounding
+ * (nearest, ties to even) of the fp32 quotient x / scale. This changes how K and V
+ * are stored, not what the attention computes: qsa_ref_attend_fp8 is qsa_ref_attend
+ * on the dequantized values. */
+int qsa_ref_quantize_kv(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_k,
+                        const uint16_t *k, const uint16_t *v, uint8_t *k8, uint8_t *v8,
+                        float *k_scale, float *v_scale);
+int qsa_ref_attend_fp8(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                       const int32_t *cu_k, const uint16_t *q, const uint8_t *k8,
+                       const uint8_t *v8, const float *k_scale, const float *v_scale,
+                       const int32_t *sel, double *out, double *lse, const int64_t *rows,
+                       int64_t n_rows, int32_t n_threads);
+
+/* The bf16 and E4M3 roundings the oracle uses and the E4M3 decoding (exposed so tests
+ * can pin them). E4M3 rounding saturates finite magnitudes beyond 448 to 448. */
 uint16_t qsa_ref_bf16_round(double x);
+uint8_t qsa_ref_e4m3_round(double x);
+double qsa_ref_e4m3_value(uint8_t b);
 
 #ifdef __cplusplus
 }

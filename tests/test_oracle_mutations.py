@@ -3,8 +3,8 @@
 Each case compiles a copy of the oracle with one planted mistake and runs the pin
 suite against it in a subprocess; the suite must fail. This shows the pins are
 sensitive to: the tie-break, the visibility rule, the raw tail, the relu, the
-weight index, the head grouping, the softmax scale, the bf16 rounding and the
-compression range.
+weight index, the head grouping, the softmax scale, the bf16 rounding, the
+compression range, and the FP8 cache's rounding, scale and dequantization.
 """
 import os
 import subprocess
@@ -33,6 +33,13 @@ MUTATIONS = {
                         "double r = ldexp(trunc(ldexp(x, -qe)), qe);"),
     "compress_three_tokens": ("for (int64_t i = 0; i < bs; ++i)\n                    s +=",
                               "for (int64_t i = 0; i < bs - 1; ++i)\n                    s +="),
+    "e4m3_quantum_halved": ("int qe = (e < -5 ? -5 : e) - 4;", "int qe = (e < -5 ? -5 : e) - 5;"),
+    "e4m3_truncation": ("double r = ldexp(nearbyint(ldexp(a, -qe)), qe);",
+                        "double r = ldexp(trunc(ldexp(a, -qe)), qe);"),
+    "fp8_scale_ignored": ("return e4m3_value(s->f8[r * D + c]) * (double)s->scale[r];",
+                          "return e4m3_value(s->f8[r * D + c]);"),
+    "fp8_amax_over_256": ("float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;",
+                          "float s = amax > 0.0 ? (float)(amax / 256.0) : 1.0f;"),
 }
 
 

@@ -348,3 +348,91 @@ def test_ragged_batch_rows_independent():
         _, sel1, out1, _ = oracle.forward(dims, cu, cu, p.q[k0:k1], p.k[k0:k1], p.v[k0:k1],
                                           p.q_idx[k0:k1], p.w[k0:k1], p.k_idx[k0:k1])
         assert np.array_equal(sel[k0:k1], sel1) and np.array_equal(out[k0:k1], out1)
+
+
+# ----------------------------------------------------------------- FP8 KV cache
+
+def _e4m3_probe_values():
+    rng = np.random.default_rng(50)
+    return np.concatenate([
+        rng.uniform(-464.0, 464.0, 20000),          # every binade of the normal range
+        rng.normal(0.0, 0.01, 20000),               # subnormals and small normals
+        np.arange(-464.0, 464.5, 0.5),              # exact ties in the top binades
+        np.ldexp(np.arange(0, 64), -12),            # ties between subnormal steps
+    ]).astype(np.float32)
+
+
+def test_e4m3_round_matches_torch():
+    """FP8 rounding (nearest, ties to even, subnormals) equals torch's float8_e4m3fn
+    cast on fp32 values up to 464 (catches a wrong quantum, truncation, a wrong bias)."""
+    vals = _e4m3_probe_values()
+    ours = np.array([oracle.e4m3_round(float(x)) for x in vals], dtype=np.uint8)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3_decode_all_codes():
+    """The value of every E4M3 byte equals torch's decoding (NaN codes included)."""
+    ours = np.array([oracle.e4m3_value(b) for b in range(256)])
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    ref = ref.numpy()
+    assert np.all((ours == ref) | (np.isnan(ours) & np.isnan(ref)))
+
+
+def test_quantize_kv_matches_library_cast():
+    """Per (token, KV head) row: scale = fp32(amax / 448) and bytes = float8_e4m3fn cast
+    of the fp32 quotient x / scale, recomputed with torch; every nonzero row reaches 448;
+    all-zero rows get scale 1 and zero bytes."""
+    dims = oracle.Dims()
+    p = gen.make_problem([37, 9], seed=51, qkv_scale=0.5, outlier_frac=0.1)
+    p.k[5] = 0                                     # an all-zero token (both heads)
+    k8, v8, ks, vs = oracle.quantize_kv(dims, p.cu_k, p.k, p.v)
+    for x, q8, sc in ((p.k, k8, ks), (p.v, v8, vs)):
+        xf = torch.from_numpy(bf16_to_f32(x).reshape(-1, dims.head_dim))
+        amax = xf.abs().amax(dim=1)
+        s_ref = torch.where(amax > 0, amax / torch.tensor(448.0, dtype=torch.float32),
+                            torch.ones_like(amax))
+        assert np.array_equal(sc.reshape(-1), s_ref.numpy())
+        q_ref = (xf / s_ref[:, None]).to(torch.float8_e4m3fn)
+        assert np.array_equal(q8.reshape(-1, dims.head_dim), q_ref.view(torch.uint8).numpy())
+        dec = q_ref.to(torch.float64).abs().amax(dim=1).numpy()
+        assert np.all(dec[amax.numpy() > 0] == 448.0)
+    assert np.all(k8[5] == 0) and np.all(ks[5] == 1.0)
+
+
+def test_attend_fp8_lossless_case_equals_bf16():
+    """Integer K/V in [-7, 7] with a +-7 in every (token, head) row quantize exactly
+    (scale 2^-6, bytes 64*x), so FP8 attention equals bf16 attention bit for bit."""
+    dims = oracle.Dims(topk_blocks=5)
+    p = gen.make_problem([61, 40], q_lens=[61, 3], seed=52)
+    rng = np.random.default_rng(52)
+    for name in ("k", "v"):
+        x = rng.integers(-7, 8, size=getattr(p, name).shape).astype(np.float32)
+        x[..., 0] = np.where(rng.random(x.shape[:-1]) < 0.5, 7.0, -7.0)
+        setattr(p, name, bf(x))
+    kb = oracle.compress(dims, p.cu_k, p.k_idx)
+    sel = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb)
+    k8, v8, ks, vs = oracle.quantize_kv(dims, p.cu_k, p.k, p.v)
+    assert np.all(ks == 2.0 ** -6) and np.all(vs == 2.0 ** -6)
+    out, lse = oracle.attend(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel)
+    out8, lse8 = oracle.attend_fp8(dims, p.cu_q, p.cu_k, p.q, k8, v8, ks, vs, sel)
+    assert np.array_equal(out, out8) and np.array_equal(lse, lse8)
+
+
+def test_attend_fp8_matches_masked_attention_on_dequantized_values():
+    """FP8 attention of sparse rows equals dense GQA attention (scipy) restricted to the
+    attended tokens, computed on the dequantized K and V."""
+    dims = oracle.Dims(topk_blocks=4)
+    p = gen.make_problem([90], seed=53)
+    kb = oracle.compress(dims, p.cu_k, p.k_idx)
+    sel = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb)
+    k8, v8, ks, vs = oracle.quantize_kv(dims, p.cu_k, p.k, p.v)
+    deq = lambda q8, s: (torch.from_numpy(q8).view(torch.float8_e4m3fn).to(torch.float64)
+                         .numpy() * s[..., None].astype(np.float64))
+    kd, vd = deq(k8, ks), deq(v8, vs)
+    out8, lse8 = oracle.attend_fp8(dims, p.cu_q, p.cu_k, p.q, k8, v8, ks, vs, sel)
+    mask = attended_mask(list(range(90)), sel, 90, dims.block_size)
+    assert (mask.sum(axis=1)[40:] >= 16).all()     # rows past 19 tokens are sparse
+    ref_out, ref_lse = masked_gqa_attention(as_f64(p.q), kd, vd, mask,
+                                            1.0 / math.sqrt(dims.head_dim))
+    assert np.max(np.abs(out8 - ref_out)) < 1e-12 and np.max(np.abs(lse8 - ref_lse)) < 1e-12
