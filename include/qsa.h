@@ -150,6 +150,35 @@ qsa_status qsa_forward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf1
                        const float *w, const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel,
                        float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- FP8 KV cache
+ * A storage variant of the attention's K and V (the pages' FP8 builds are of the
+ * model, blog.compendialabs.org, "What This Means"; here FP8 halves the bytes the
+ * attention gathers): K and V as OCP FP8 E4M3 bytes, layout k8 / v8 [Tk, 2, 128], with
+ * one fp32 scale per (token, KV head), k_scale / v_scale [Tk, 2]. A stored element
+ * stands for byte value * scale; the attention is the same computation on those
+ * values. Selection does not read K or V and is unchanged. */
+
+/* Builds the FP8 cache of bf16 K and V: for each (token, KV head) row x of 128 values,
+ * scale = fp32(amax|x| / 448) (1 for an all-zero row) and byte i = E4M3 rounding
+ * (nearest, ties to even; magnitudes beyond 448 saturate) of the fp32 quotient
+ * x[i] / scale. cu_q is not read. No workspace. */
+qsa_status qsa_quantize_kv(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *k,
+                           const qsa_bf16 *v, uint8_t *k8, uint8_t *v8, float *k_scale,
+                           float *v_scale, void *stream);
+
+/* qsa_attend over the FP8 cache. All pointers 16-byte aligned. */
+qsa_status qsa_attend_fp8(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                          const uint8_t *k8, const uint8_t *v8, const float *k_scale,
+                          const float *v_scale, const int32_t *sel, float *out, float *lse,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* qsa_forward over the FP8 cache (compress and selection as in qsa_forward). */
+qsa_status qsa_forward_fp8(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                           const uint8_t *k8, const uint8_t *v8, const float *k_scale,
+                           const float *v_scale, const qsa_bf16 *q_idx, const float *w,
+                           const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel, float *out,
+                           float *lse, void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- diagnostics
  * Per-kernel timing with HIP events, for benchmarks and profiling. Between
  * qsa_trace_begin and qsa_trace_end on one host thread, each kernel the library

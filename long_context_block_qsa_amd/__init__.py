@@ -55,6 +55,10 @@ _SIGS = {
     "qsa_select": ([ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "qsa_attend": ([ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "qsa_forward": ([ctypes.c_void_p] * 13 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "qsa_quantize_kv": ([ctypes.c_void_p] * 9, ctypes.c_int),
+    "qsa_attend_fp8": ([ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "qsa_forward_fp8": ([ctypes.c_void_p] * 15 + [ctypes.c_size_t, ctypes.c_void_p],
+                        ctypes.c_int),
     "qsa_trace_begin": ([ctypes.c_int32], ctypes.c_int),
     "qsa_trace_end": ([ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int32),
     "qsa_kernel_name": ([ctypes.c_int32], ctypes.c_char_p),
@@ -213,6 +217,57 @@ def forward(seqs: Seqs, q, k, v, q_idx, w, k_idx, k_blk, sel, out, lse, ws, topk
                              _ptr(lse, "lse", 4, (seqs.n_q, HQ)),
                              _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
            "qsa_forward")
+
+
+def quantize_kv(seqs: Seqs, k, v, k8, v8, k_scale, v_scale, stream=None):
+    """FP8 KV cache of bf16 K and V: E4M3 bytes k8 / v8 [Tk, 2, 128] (uint8) and fp32
+    scales [Tk, 2] per (token, KV head)."""
+    d = make_dims()
+    _check(lib().qsa_quantize_kv(ctypes.byref(d), ctypes.byref(seqs.c),
+                                 _ptr(k, "k", 2, (seqs.n_k, HKV, D)),
+                                 _ptr(v, "v", 2, (seqs.n_k, HKV, D)),
+                                 _ptr(k8, "k8", 1, (seqs.n_k, HKV, D)),
+                                 _ptr(v8, "v8", 1, (seqs.n_k, HKV, D)),
+                                 _ptr(k_scale, "k_scale", 4, (seqs.n_k, HKV)),
+                                 _ptr(v_scale, "v_scale", 4, (seqs.n_k, HKV)), _stream(stream)),
+           "qsa_quantize_kv")
+
+
+def attend_fp8(seqs: Seqs, q, k8, v8, k_scale, v_scale, sel, out, lse, ws, topk: int = KMAX,
+               softmax_scale=0.0, stream=None):
+    d = make_dims(topk, softmax_scale)
+    _check(lib().qsa_attend_fp8(ctypes.byref(d), ctypes.byref(seqs.c),
+                                _ptr(q, "q", 2, (seqs.n_q, HQ, D)),
+                                _ptr(k8, "k8", 1, (seqs.n_k, HKV, D)),
+                                _ptr(v8, "v8", 1, (seqs.n_k, HKV, D)),
+                                _ptr(k_scale, "k_scale", 4, (seqs.n_k, HKV)),
+                                _ptr(v_scale, "v_scale", 4, (seqs.n_k, HKV)),
+                                _ptr(sel, "sel", 4, (seqs.n_q, topk)),
+                                _ptr(out, "out", 4, (seqs.n_q, HQ, D)),
+                                _ptr(lse, "lse", 4, (seqs.n_q, HQ)),
+                                _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "qsa_attend_fp8")
+
+
+def forward_fp8(seqs: Seqs, q, k8, v8, k_scale, v_scale, q_idx, w, k_idx, k_blk, sel, out, lse,
+                ws, topk: int = KMAX, softmax_scale=0.0, stream=None):
+    """forward() with K and V from the FP8 cache."""
+    d = make_dims(topk, softmax_scale)
+    _check(lib().qsa_forward_fp8(ctypes.byref(d), ctypes.byref(seqs.c),
+                                 _ptr(q, "q", 2, (seqs.n_q, HQ, D)),
+                                 _ptr(k8, "k8", 1, (seqs.n_k, HKV, D)),
+                                 _ptr(v8, "v8", 1, (seqs.n_k, HKV, D)),
+                                 _ptr(k_scale, "k_scale", 4, (seqs.n_k, HKV)),
+                                 _ptr(v_scale, "v_scale", 4, (seqs.n_k, HKV)),
+                                 _ptr(q_idx, "q_idx", 2, (seqs.n_q, HI, DI)),
+                                 _ptr(w, "w", 4, (seqs.n_q, HI)),
+                                 _ptr(k_idx, "k_idx", 2, (seqs.n_k, DI)),
+                                 _ptr(k_blk, "k_blk", 2, (seqs.n_blocks, DI)),
+                                 _ptr(sel, "sel", 4, (seqs.n_q, topk)),
+                                 _ptr(out, "out", 4, (seqs.n_q, HQ, D)),
+                                 _ptr(lse, "lse", 4, (seqs.n_q, HQ)),
+                                 _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "qsa_forward_fp8")
 
 
 class trace:

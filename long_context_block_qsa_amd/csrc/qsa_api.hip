@@ -281,12 +281,74 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
 }
 
 qsa_status run_attend(const Plan &p, const qsa_bf16 *q, const qsa_bf16 *k, const qsa_bf16 *v,
-                      const int32_t *sel, float *out, float *lse, void *ws, hipStream_t st) {
+                      const qsa::Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
+                      void *ws, hipStream_t st) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
     float *part = ws_at<float>(ws, p.off_union);
     QSA_TRY(qsa::launch_attend(tab, p.use_dec ? &p.dec : nullptr, p.batch, p.topk, p.scale, q,
-                               k, v, sel, out, lse, part, p.nsplit, p.tq, st));
+                               k, v, fp8, sel, out, lse, part, p.nsplit, p.tq, st));
     return QSA_OK;
+}
+
+qsa_status attend_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                         const qsa_bf16 *k, const qsa_bf16 *v, const qsa::Fp8Kv *fp8,
+                         const int32_t *sel, float *out, float *lse, void *ws, size_t ws_bytes,
+                         void *stream) {
+    Plan p;
+    qsa_status st = make_plan(dims, seqs, true, &p);
+    if (st != QSA_OK) return st;
+    if (p.tq == 0) return QSA_OK;
+    if (!q || !sel || !out) return QSA_ERR_NULL;
+    if (fp8 ? (!fp8->k8 || !fp8->v8 || !fp8->k_scale || !fp8->v_scale) : (!k || !v))
+        return QSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(sel) ||
+        (fp8 ? (!aligned16(fp8->k8) || !aligned16(fp8->v8) || !aligned16(fp8->k_scale) ||
+                !aligned16(fp8->v_scale))
+             : (!aligned16(k) || !aligned16(v))))
+        return QSA_ERR_SHAPE;
+    if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    if (!p.use_dec)
+        QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
+                                 ws_at<SeqInfo>(ws, p.off_tab), hs));
+    return run_attend(p, q, k, v, fp8, sel, out, lse, ws, hs);
+}
+
+qsa_status forward_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                          const qsa_bf16 *k, const qsa_bf16 *v, const qsa::Fp8Kv *fp8,
+                          const qsa_bf16 *q_idx, const float *w, const qsa_bf16 *k_idx,
+                          qsa_bf16 *k_blk, int32_t *sel, float *out, float *lse, void *ws,
+                          size_t ws_bytes, void *stream) {
+    Plan p;
+    qsa_status st = make_plan(dims, seqs, true, &p);
+    if (st != QSA_OK) return st;
+    if (p.tq == 0) return QSA_OK;
+    if (!q || !out) return QSA_ERR_NULL;
+    if (fp8 ? (!fp8->k8 || !fp8->v8 || !fp8->k_scale || !fp8->v_scale) : (!k || !v))
+        return QSA_ERR_NULL;
+    if (p.n_tiles > 0 && (!q_idx || !w)) return QSA_ERR_NULL;
+    if ((p.n_tiles > 0 || (k_idx && p.max_cmp_incr > 0)) && !k_blk) return QSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || (q_idx && !aligned16(q_idx)) ||
+        (w && !aligned16(w)) || (k_idx && !aligned16(k_idx)) || (k_blk && !aligned16(k_blk)) ||
+        (sel && !aligned16(sel)) ||
+        (fp8 ? (!aligned16(fp8->k8) || !aligned16(fp8->v8) || !aligned16(fp8->k_scale) ||
+                !aligned16(fp8->v_scale))
+             : (!aligned16(k) || !aligned16(v))))
+        return QSA_ERR_SHAPE;
+    if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    int32_t *sel_use = sel ? sel : ws_at<int32_t>(ws, p.off_sel);
+    SeqInfo *tab = p.use_dec ? nullptr : ws_at<SeqInfo>(ws, p.off_tab);
+    const bool fused = p.use_dec && p.fuse_compress && k_idx && p.n_tiles > 0;
+    if (k_idx && p.max_cmp_incr > 0 && !fused)   // compress the new blocks (and build the table)
+        QSA_TRY(qsa::launch_compress(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.max_cmp_incr,
+                                     k_idx, k_blk, 1, tab, p.topk, hs));
+    else if (!p.use_dec)
+        QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk, tab, hs));
+    if ((st = run_select(p, seqs, q_idx, w, fused ? k_idx : nullptr, k_blk, sel_use, ws, hs)) !=
+        QSA_OK)
+        return st;
+    return run_attend(p, q, k, v, fp8, sel_use, out, lse, ws, hs);
 }
 
 }  // namespace
@@ -353,50 +415,50 @@ qsa_status qsa_select(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16
 qsa_status qsa_attend(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
                       const qsa_bf16 *k, const qsa_bf16 *v, const int32_t *sel, float *out,
                       float *lse, void *ws, size_t ws_bytes, void *stream) {
-    Plan p;
-    qsa_status st = make_plan(dims, seqs, true, &p);
-    if (st != QSA_OK) return st;
-    if (p.tq == 0) return QSA_OK;
-    if (!q || !k || !v || !sel || !out) return QSA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(sel))
-        return QSA_ERR_SHAPE;
-    if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
-    hipStream_t hs = (hipStream_t)stream;
-    if (!p.use_dec)
-        QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
-                                 ws_at<SeqInfo>(ws, p.off_tab), hs));
-    return run_attend(p, q, k, v, sel, out, lse, ws, hs);
+    return attend_common(dims, seqs, q, k, v, nullptr, sel, out, lse, ws, ws_bytes, stream);
 }
 
 qsa_status qsa_forward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
                        const qsa_bf16 *k, const qsa_bf16 *v, const qsa_bf16 *q_idx,
                        const float *w, const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel,
                        float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    return forward_common(dims, seqs, q, k, v, nullptr, q_idx, w, k_idx, k_blk, sel, out, lse,
+                          ws, ws_bytes, stream);
+}
+
+qsa_status qsa_quantize_kv(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *k,
+                           const qsa_bf16 *v, uint8_t *k8, uint8_t *v8, float *k_scale,
+                           float *v_scale, void *stream) {
     Plan p;
-    qsa_status st = make_plan(dims, seqs, true, &p);
+    qsa_status st = make_plan(dims, seqs, false, &p);
     if (st != QSA_OK) return st;
-    if (p.tq == 0) return QSA_OK;
-    if (!q || !k || !v || !out) return QSA_ERR_NULL;
-    if (p.n_tiles > 0 && (!q_idx || !w)) return QSA_ERR_NULL;
-    if ((p.n_tiles > 0 || (k_idx && p.max_cmp_incr > 0)) && !k_blk) return QSA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        (q_idx && !aligned16(q_idx)) || (w && !aligned16(w)) || (k_idx && !aligned16(k_idx)) ||
-        (k_blk && !aligned16(k_blk)) || (sel && !aligned16(sel)))
+    if (p.tk == 0) return QSA_OK;
+    if (!k || !v || !k8 || !v8 || !k_scale || !v_scale) return QSA_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k8) || !aligned16(v8) ||
+        !aligned16(k_scale) || !aligned16(v_scale))
         return QSA_ERR_SHAPE;
-    if ((st = check_ws(p, ws, ws_bytes)) != QSA_OK) return st;
-    hipStream_t hs = (hipStream_t)stream;
-    int32_t *sel_use = sel ? sel : ws_at<int32_t>(ws, p.off_sel);
-    SeqInfo *tab = p.use_dec ? nullptr : ws_at<SeqInfo>(ws, p.off_tab);
-    const bool fused = p.use_dec && p.fuse_compress && k_idx && p.n_tiles > 0;
-    if (k_idx && p.max_cmp_incr > 0 && !fused)   // compress the new blocks (and build the table)
-        QSA_TRY(qsa::launch_compress(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.max_cmp_incr,
-                                     k_idx, k_blk, 1, tab, p.topk, hs));
-    else if (!p.use_dec)
-        QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk, tab, hs));
-    if ((st = run_select(p, seqs, q_idx, w, fused ? k_idx : nullptr, k_blk, sel_use, ws, hs)) !=
-        QSA_OK)
-        return st;
-    return run_attend(p, q, k, v, sel_use, out, lse, ws, hs);
+    QSA_TRY(qsa::launch_quantize_kv(k, v, k8, v8, k_scale, v_scale, p.tk * qsa::HKV,
+                                    (hipStream_t)stream));
+    return QSA_OK;
+}
+
+qsa_status qsa_attend_fp8(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                          const uint8_t *k8, const uint8_t *v8, const float *k_scale,
+                          const float *v_scale, const int32_t *sel, float *out, float *lse,
+                          void *ws, size_t ws_bytes, void *stream) {
+    const qsa::Fp8Kv f = {k8, v8, k_scale, v_scale};
+    return attend_common(dims, seqs, q, nullptr, nullptr, &f, sel, out, lse, ws, ws_bytes,
+                         stream);
+}
+
+qsa_status qsa_forward_fp8(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                           const uint8_t *k8, const uint8_t *v8, const float *k_scale,
+                           const float *v_scale, const qsa_bf16 *q_idx, const float *w,
+                           const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel, float *out,
+                           float *lse, void *ws, size_t ws_bytes, void *stream) {
+    const qsa::Fp8Kv f = {k8, v8, k_scale, v_scale};
+    return forward_common(dims, seqs, q, nullptr, nullptr, &f, q_idx, w, k_idx, k_blk, sel,
+                          out, lse, ws, ws_bytes, stream);
 }
 
 qsa_status qsa_trace_begin(int32_t max_kernels) {

@@ -2,6 +2,8 @@
 // kernels (gfx950, wave64). Internal to the library.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,6 +27,7 @@ constexpr int WAVE = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Per-sequence bookkeeping, built once per call into the workspace.
@@ -728,6 +731,40 @@ __device__ __forceinline__ int block_topk_regs(const uint32_t (&x)[PER], int n, 
     *first = block_excl_scan_i32<NT>(nt, sm.scan, &tot);
     *kept = mask;
     return tot;
+}
+
+// ---------------------------------------------------------------- FP8 (OCP E4M3)
+
+// 8 E4M3 bytes -> 8 bf16 (exact: E4M3 values have 4 significant bits and a narrower
+// exponent range than bf16), in the byte order of the input.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint2 b) {
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w = h ? b.y : b.x;
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+        r[2 * h] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+        r[2 * h + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+    }
+    return r;
+}
+
+// E4M3 rounding of an fp32 value: nearest, ties to even; finite magnitudes beyond 448
+// saturate to 448. The quantum is 2^(e-3) for |y| = 1.f * 2^e in the normal range
+// (|y| >= 2^-6) and 2^-9 below it.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (!(a > 0.f)) return sign;
+    const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+    const int qe = (e < -6 ? -6 : e) - 3;
+    float r = ldexpf(rintf(ldexpf(a, -qe)), qe);
+    r = fminf(r, 448.0f);
+    if (r < 0x1p-6f) return sign | (uint32_t)(r * 512.0f);
+    const uint32_t rb = __float_as_uint(r);
+    const uint32_t eb = ((rb >> 23) & 0xffu) - 120u;   // unbiased + 7
+    return sign | (eb << 3) | ((rb >> 20) & 7u);
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {

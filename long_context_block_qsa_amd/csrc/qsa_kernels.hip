@@ -738,6 +738,8 @@ struct AttnArgs {
     int topk;
     float scale_log2;  // softmax scale * log2(e)
     const uint16_t *q, *k, *v;
+    const uint8_t *k8, *v8;      // FP8 KV cache (E4M3 bytes) and its per-row scales
+    const float *k_scale, *v_scale;
     const int32_t *sel;
     float *out, *lse;
     float *part;
@@ -754,9 +756,19 @@ struct KVTile {
     u32x4 vr[8];     // V rows of the lane's 8 P keys, dims 8col .. 8col+7
     uint32_t valid;  // bit 4u+i: key j0 + 16u + 4gr + i is attended
 };
+// The same tile from the FP8 KV cache: 8 E4M3 bytes per load, and the K and V scales
+// of the lane's 8 P keys (the logit and probability of key e are scaled by them).
+struct KVTile8 {
+    uint2 kr[2][4];
+    uint2 vr[8];
+    float ks[8], vs[8];
+    uint32_t valid;
+};
 
+template <bool FP8>
 __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv, int64_t row,
                                             int g, int sp) {
+    using Tile = typename std::conditional<FP8, KVTile8, KVTile>::type;
     const int64_t t = rv.t;
     const int64_t nv = nvis_of(t);
     const int ntail = (int)(t + 1 - BS * nv);
@@ -807,8 +819,8 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
         ok = sl == nsel && ntail > 0;
         return kv0 + (int64_t)BS * nv;
     };
-    auto load_tile = [&](int j0, int32_t cur) -> KVTile {
-        KVTile T;
+    auto load_tile = [&](int j0, int32_t cur) -> Tile {
+        Tile T;
         T.valid = 0;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -817,9 +829,16 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
             int64_t tok = slot_token0(p >> 2, cur, ok) + (p & 3);
             ok = ok && p < p_hi && ((p >> 2) < nsel || (p & 3) < ntail);
             if (!ok) tok = safe_tok;
-            const uint16_t *kp = kbase + tok * (HKV * HD) + 8 * gr;
+            if constexpr (FP8) {
+                const uint8_t *kp = a.k8 + tok * (HKV * HD) + g * HD + 8 * gr;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) T.kr[u][m] = load16(kp + 32 * m);
+                for (int m = 0; m < 4; ++m)
+                    T.kr[u][m] = *reinterpret_cast<const uint2 *>(kp + 32 * m);
+            } else {
+                const uint16_t *kp = kbase + tok * (HKV * HD) + 8 * gr;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) T.kr[u][m] = load16(kp + 32 * m);
+            }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -831,7 +850,14 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
                 const int p = 4 * sl + i;
                 const bool ok = okb && p < p_hi && (sl < nsel || i < ntail);
                 const int64_t tok = ok ? tok0 + i : safe_tok;
-                T.vr[4 * h + i] = load16(vbase + tok * (HKV * HD) + 8 * col);
+                if constexpr (FP8) {
+                    T.vr[4 * h + i] = *reinterpret_cast<const uint2 *>(
+                        a.v8 + tok * (HKV * HD) + g * HD + 8 * col);
+                    T.ks[4 * h + i] = a.k_scale[tok * HKV + g];
+                    T.vs[4 * h + i] = a.v_scale[tok * HKV + g];
+                } else {
+                    T.vr[4 * h + i] = load16(vbase + tok * (HKV * HD) + 8 * col);
+                }
                 if (ok) T.valid |= 1u << (4 * h + i);
             }
         }
@@ -845,10 +871,10 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
 #pragma unroll
     for (int j = 1; j < KMAX / WAVE; ++j)
         if (cur_grp == j) cur = v[j];
-    KVTile nxt;
+    Tile nxt;
     if (p_lo < p_hi) nxt = load_tile(p_lo, cur);
     for (int j0 = p_lo; j0 < p_hi; j0 += 32) {
-        const KVTile T = nxt;
+        const Tile T = nxt;
         const int jn = j0 + 32;
         if (jn < p_hi) {
             if ((jn >> 8) != cur_grp) { cur_grp = jn >> 8; cur = group_ids(cur_grp); }
@@ -861,11 +887,16 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
         for (int u = 0; u < 2; ++u) {
             f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) c4 = mfma_bf16_16x16x32(T.kr[u][m], qb[m], c4);
+            for (int m = 0; m < 4; ++m) {
+                if constexpr (FP8) c4 = mfma_bf16_16x16x32(e4m3x8_to_bf16x8(T.kr[u][m]), qb[m], c4);
+                else c4 = mfma_bf16_16x16x32(T.kr[u][m], qb[m], c4);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool ok = (T.valid >> (4 * u + i)) & 1u;
-                z[4 * u + i] = ok ? c4[i] * a.scale_log2 : -INFINITY;
+                float zz = c4[i] * a.scale_log2;
+                if constexpr (FP8) zz *= T.ks[4 * u + i];
+                z[4 * u + i] = ok ? zz : -INFINITY;
                 mx = fmaxf(mx, z[4 * u + i]);
             }
         }
@@ -885,14 +916,28 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) acc[mt] *= alpha;
 
+        // FP8: the V scale of each key multiplies its probability (the denominator l
+        // keeps the unscaled ones)
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (FP8) pv[e] = p[e] * T.vs[e];
+            else pv[e] = p[e];
+        }
         u32x4 ph, pl;
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
-            const uint32_t h0 = f32_to_bf16_rne(p[2 * q2]), h1 = f32_to_bf16_rne(p[2 * q2 + 1]);
-            const float r0 = p[2 * q2] - __uint_as_float(h0 << 16);
-            const float r1 = p[2 * q2 + 1] - __uint_as_float(h1 << 16);
+            const uint32_t h0 = f32_to_bf16_rne(pv[2 * q2]), h1 = f32_to_bf16_rne(pv[2 * q2 + 1]);
+            const float r0 = pv[2 * q2] - __uint_as_float(h0 << 16);
+            const float r1 = pv[2 * q2 + 1] - __uint_as_float(h1 << 16);
             ph[q2] = h0 | (h1 << 16);
             pl[q2] = f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16);
+        }
+        u32x4 vb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (FP8) vb[e] = e4m3x8_to_bf16x8(T.vr[e]);
+            else vb[e] = T.vr[e];
         }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
@@ -900,7 +945,7 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
             u32x4 va;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const uint32_t x0 = T.vr[2 * kk][q2], x1 = T.vr[2 * kk + 1][q2];
+                const uint32_t x0 = vb[2 * kk][q2], x1 = vb[2 * kk + 1][q2];
                 va[kk] = (mt & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u))
                                   : ((x0 & 0xffffu) | (x1 << 16));
             }
@@ -950,14 +995,16 @@ __device__ __forceinline__ bool attend_item(const AttnArgs &a, int64_t &row, int
     return row < a.nrows;
 }
 
+template <bool FP8>
 __global__ void __launch_bounds__(ATT_NT)
 attend_kernel(AttnArgs a) {
     int64_t row;
     int g, sp;
     if (!attend_item(a, row, g, sp)) return;
-    attend_body(a, tab_row(a.tab, a.batch, a.topk, row), row, g, sp);
+    attend_body<FP8>(a, tab_row(a.tab, a.batch, a.topk, row), row, g, sp);
 }
 
+template <bool FP8>
 __global__ void __launch_bounds__(ATT_NT)
 attend_dec_kernel(AttnArgs a, DecodeTables d) {
     int64_t row;
@@ -965,7 +1012,7 @@ attend_dec_kernel(AttnArgs a, DecodeTables d) {
     if (!attend_item(a, row, g, sp)) return;
     const DecRow r = d.row[row];
     const RowView rv = {r.k0, r.t, r.blk0, r.slot};
-    attend_body(a, rv, row, g, sp);
+    attend_body<FP8>(a, rv, row, g, sp);
 }
 
 // =============================================================== combine
@@ -1012,6 +1059,55 @@ combine_kernel(const float *__restrict__ part, int nsplit, int64_t nrows,
     o[2 * l + 1] = o1 * inv;
     if (lse && l == 0)
         lse[row * HQ + head] = Lsum > 0.f ? M * 0.69314718055994531f + logf(Lsum) : -INFINITY;
+}
+
+// =============================================================== FP8 KV cache
+// Row = (token, KV head) of K or V, 128 bf16 values: 16 lanes per row (8 values, one
+// 16-byte load each), 16 rows per workgroup; grid y = 0 for K, 1 for V. The row's
+// scale is amax / 448 (1 for an all-zero row) and each byte the E4M3 rounding of the
+// fp32 quotient x / scale (IEEE divisions, as in the definition).
+constexpr int QNT_NT = 256;
+
+__global__ void __launch_bounds__(QNT_NT)
+quantize_kv_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                   uint8_t *__restrict__ k8, uint8_t *__restrict__ v8,
+                   float *__restrict__ k_scale, float *__restrict__ v_scale, int64_t rows) {
+    const int64_t r = (int64_t)blockIdx.x * (QNT_NT / 16) + threadIdx.x / 16;
+    if (r >= rows) return;   // whole 16-lane groups leave together
+    const int c = threadIdx.x % 16;
+    const uint16_t *src = blockIdx.y ? v : k;
+    uint8_t *dst = blockIdx.y ? v8 : k8;
+    float *sc = blockIdx.y ? v_scale : k_scale;
+    const u32x4 x4 = load16(src + r * HD + 8 * c);
+    float x[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        x[2 * q] = bf16_lo(x4[q]);
+        x[2 * q + 1] = bf16_hi(x4[q]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+    for (int dd = 1; dd < 16; dd <<= 1) amax = fmaxf(amax, __shfl_xor(amax, dd));
+    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lo |= e4m3_rne(x[e] / s) << (8 * e);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hi |= e4m3_rne(x[4 + e] / s) << (8 * e);
+    *reinterpret_cast<uint2 *>(dst + r * HD + 8 * c) = uint2{lo, hi};
+    if (c == 0) sc[r] = s;
+}
+
+hipError_t launch_quantize_kv(const uint16_t *k, const uint16_t *v, uint8_t *k8, uint8_t *v8,
+                              float *k_scale, float *v_scale, int64_t rows, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    const int64_t gx = (rows + QNT_NT / 16 - 1) / (QNT_NT / 16);
+    trace_before(1, st);
+    hipLaunchKernelGGL(quantize_kv_kernel, dim3((unsigned)gx, 2), dim3(QNT_NT), 0, st, k, v, k8,
+                       v8, k_scale, v_scale, rows);
+    return trace_after(st, hipGetLastError());
 }
 
 // =============================================================== launchers
@@ -1111,21 +1207,29 @@ hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, i
 
 hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         const int32_t *sel, float *out, float *lse, float *part, int nsplit,
-                         int64_t n_rows, hipStream_t st) {
+                         const Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
+                         float *part, int nsplit, int64_t n_rows, hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
     AttnArgs a;
     a.tab = tab; a.batch = batch; a.topk = topk;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q = q; a.k = k; a.v = v; a.sel = sel; a.out = out; a.lse = lse; a.part = part;
+    a.k8 = fp8 ? fp8->k8 : nullptr; a.v8 = fp8 ? fp8->v8 : nullptr;
+    a.k_scale = fp8 ? fp8->k_scale : nullptr; a.v_scale = fp8 ? fp8->v_scale : nullptr;
     a.nsplit = nsplit; a.nrows = n_rows;
     const int64_t waves = n_rows * HKV * nsplit;
     const int64_t wgs = (waves + ATT_NT / WAVE - 1) / (ATT_NT / WAVE);
     trace_before(4, st);
-    if (d)
-        hipLaunchKernelGGL(attend_dec_kernel, dim3((unsigned)wgs), dim3(ATT_NT), 0, st, a, *d);
+    if (d && fp8)
+        hipLaunchKernelGGL(attend_dec_kernel<true>, dim3((unsigned)wgs), dim3(ATT_NT), 0, st, a,
+                           *d);
+    else if (d)
+        hipLaunchKernelGGL(attend_dec_kernel<false>, dim3((unsigned)wgs), dim3(ATT_NT), 0, st, a,
+                           *d);
+    else if (fp8)
+        hipLaunchKernelGGL(attend_kernel<true>, dim3((unsigned)wgs), dim3(ATT_NT), 0, st, a);
     else
-        hipLaunchKernelGGL(attend_kernel, dim3((unsigned)wgs), dim3(ATT_NT), 0, st, a);
+        hipLaunchKernelGGL(attend_kernel<false>, dim3((unsigned)wgs), dim3(ATT_NT), 0, st, a);
     hipError_t e = trace_after(st, hipGetLastError());
     if (e != hipSuccess || nsplit == 1) return e;
     const int64_t cw = (n_rows * HQ + CMB_NT / WAVE - 1) / (CMB_NT / WAVE);

@@ -9,6 +9,12 @@ namespace qsa {
 struct SeqInfo;
 struct DecodeTables;
 
+// FP8 KV cache operands: E4M3 bytes [Tk, 2, 128] and fp32 scales [Tk, 2].
+struct Fp8Kv {
+    const uint8_t *k8, *v8;
+    const float *k_scale, *v_scale;
+};
+
 // Optional per-kernel event trace (thread-local; see qsa_trace_begin).
 void trace_before(int kind, hipStream_t st);
 hipError_t trace_after(hipStream_t st, hipError_t launch_status);
@@ -34,7 +40,9 @@ hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, i
                          int dense_only, hipStream_t st);
 hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         const int32_t *sel, float *out, float *lse, float *part, int nsplit,
-                         int64_t n_rows, hipStream_t st);
+                         const Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
+                         float *part, int nsplit, int64_t n_rows, hipStream_t st);
+hipError_t launch_quantize_kv(const uint16_t *k, const uint16_t *v, uint8_t *k8, uint8_t *v8,
+                              float *k_scale, float *v_scale, int64_t rows, hipStream_t st);
 
 }  // namespace qsa

@@ -30,6 +30,7 @@ def test_exports_every_declared_symbol():
     names = qsa.header_functions()
     assert set(names) == {"qsa_abi_version", "qsa_status_string", "qsa_workspace_size",
                           "qsa_compress", "qsa_select", "qsa_attend", "qsa_forward",
+                          "qsa_quantize_kv", "qsa_attend_fp8", "qsa_forward_fp8",
                           "qsa_trace_begin", "qsa_trace_end", "qsa_kernel_name"}
     out = subprocess.run(["nm", "-D", "--defined-only", qsa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -96,6 +97,29 @@ def test_null_pointers_rejected():
     assert L.qsa_select(ctypes.byref(d), ctypes.byref(s), f, f, f, None, f, nbytes,
                         None) == qsa.QSA_ERR_NULL
     assert L.qsa_compress(ctypes.byref(d), ctypes.byref(s), None, f, None) == qsa.QSA_ERR_NULL
+
+
+def test_fp8_entry_points_validate_first():
+    """FP8 entry points reject missing or misaligned operands before any device call."""
+    d = qsa.make_dims()
+    L = qsa.lib()
+    s = _seqs([0, 1], [0, 40])
+    st, nbytes = _ws(d, s)
+    assert st == 0
+    f = ctypes.c_void_p(FAKE)
+    odd = ctypes.c_void_p(FAKE + 4)
+    assert L.qsa_quantize_kv(ctypes.byref(d), ctypes.byref(s), f, f, None, f, f, f,
+                             None) == qsa.QSA_ERR_NULL
+    assert L.qsa_quantize_kv(ctypes.byref(d), ctypes.byref(s), f, f, f, f, odd, f,
+                             None) == qsa.QSA_ERR_SHAPE
+    assert L.qsa_attend_fp8(ctypes.byref(d), ctypes.byref(s), f, f, f, None, f, f, f, f, f,
+                            nbytes, None) == qsa.QSA_ERR_NULL
+    assert L.qsa_attend_fp8(ctypes.byref(d), ctypes.byref(s), f, odd, f, f, f, f, f, f, f,
+                            nbytes, None) == qsa.QSA_ERR_SHAPE
+    assert L.qsa_forward_fp8(ctypes.byref(d), ctypes.byref(s), f, f, None, f, f, f, f, f, f,
+                             f, f, f, f, nbytes, None) == qsa.QSA_ERR_NULL
+    assert L.qsa_forward_fp8(ctypes.byref(d), ctypes.byref(s), f, f, f, f, f, f, f, f, f,
+                             f, f, f, f, nbytes - 1, None) == qsa.QSA_ERR_WORKSPACE
 
 
 def test_workspace_checks():
