@@ -64,6 +64,7 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context decode line")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV cache lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--trace-steps", type=int, default=8)
@@ -185,9 +186,54 @@ def run_decode(args, torch, qsa, gen):
             step(i)
     torch.cuda.synchronize()
     long_ctx = None if args.no_1m else run_decode_1m(args, torch, qsa, gen, k, v, k_idx, sets)
+    fp8 = None if args.no_fp8 else run_decode_fp8(args, torch, qsa, seqs, k, v, k_idx, sets)
     return dict(p=p, batch=batch, ctx=ctx, wall_s=wall, gpu_ms=gpu_ms,
                 kernels=tr.mean_ms(), kernel_total=tr.total_ms(), seqs=seqs, sets=sets,
-                long_ctx=long_ctx)
+                long_ctx=long_ctx, fp8=fp8)
+
+
+def run_decode_fp8(args, torch, qsa, seqs, k, v, k_idx, sets):
+    """The decode workload with K and V read from the FP8 cache (built once, outside the
+    timed region, like the compressed indexer keys)."""
+    nk = seqs.n_k
+    k8 = torch.empty((nk, HKV, D), dtype=torch.uint8, device="cuda")
+    v8 = torch.empty_like(k8)
+    ks = torch.empty((nk, HKV), dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    qsa.quantize_kv(seqs, k, v, k8, v8, ks, vs)
+    ws = qsa.alloc_workspace(seqs, TOPK)
+    R = len(sets)
+
+    def step(i):
+        s = sets[i % R]
+        qsa.forward_fp8(seqs, s["q"], k8, v8, ks, vs, s["q_idx"], s["w"], k_idx, s["k_blk"],
+                        s["sel"], s["out"], s["lse"], ws, TOPK)
+
+    for i in range(max(args.warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(R, args.steps // R * R)
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    with qsa.trace(64) as tr:
+        for i in range(R):
+            step(i)
+    torch.cuda.synchronize()
+    batch = seqs.n_q
+    nblk = seqs.n_blocks // batch
+    nbytes = batch * (nblk * DI * 2 + HI * DI * 2 + HI * 4) + \
+        batch * (TOPK * BS * HKV * (2 * D + 2 * 4) + HQ * D * 2 + HQ * D * 4)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"decode fp8: {n} steps, {ms * 1e3:.1f} us/step")
+    del k8, v8, ks, vs
+    return {"workload": "decode as above, K/V from the FP8 (E4M3 + per-row scale) cache",
+            "steps": n, "launch": "eager", "ms_per_step": round(ms, 5),
+            "query_tokens_per_s": round(batch / (ms / 1e3), 1), "algorithmic_bytes": nbytes,
+            "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel_mean_ms": {k2: round(v2, 5) for k2, v2 in tr.mean_ms().items()}}
 
 
 def run_decode_1m(args, torch, qsa, gen, k, v, k_idx, sets):
@@ -279,7 +325,37 @@ def run_prefill(args, torch, qsa, gen):
     score_flop = scored * HI * DI * 2
     km = tr.mean_ms()
     att_ms = km.get("attend", float("nan")) + km.get("combine", 0.0)
+    fp8 = None
+    if not args.no_fp8:
+        k8 = torch.empty((seqs.n_k, HKV, D), dtype=torch.uint8, device="cuda")
+        v8 = torch.empty_like(k8)
+        ks = torch.empty((seqs.n_k, HKV), dtype=torch.float32, device="cuda")
+        vs = torch.empty_like(ks)
+        qsa.quantize_kv(seqs, k, v, k8, v8, ks, vs)
+
+        def step8():
+            qsa.forward_fp8(seqs, q, k8, v8, ks, vs, q_idx, w, k_idx, k_blk, sel, out, lse, ws,
+                            TOPK)
+
+        step8()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step8()
+        torch.cuda.synchronize()
+        ms8 = (time.perf_counter() - t0) * 1e3 / n
+        with qsa.trace(64) as tr8:
+            step8()
+        torch.cuda.synchronize()
+        km8 = tr8.mean_ms()
+        att8 = km8.get("attend", float("nan")) + km8.get("combine", 0.0)
+        fp8 = {"ms_per_step": round(ms8, 3),
+               "query_tokens_per_s": round(seqs.n_q / (ms8 / 1e3), 1),
+               "kernel_ms": {k2: round(v2, 4) for k2, v2 in km8.items()},
+               "attention_tflops": round(att_flop / (att8 / 1e3) / 1e12, 2),
+               "attention_gather_gbs": round(pairs * HKV * (2 * D + 8) / (att8 / 1e3) / 1e9, 1)}
     return {
+        "fp8_kv": fp8,
         "workload": "ragged prefill 65,535/40,001/8,190/3 tokens, budget 512 blocks",
         "ms_per_step": round(ms, 3),
         "query_tokens_per_s": round(seqs.n_q / (ms / 1e3), 1),
@@ -377,6 +453,8 @@ def main():
     }
     if d["long_ctx"] is not None:
         line["decode_1m"] = d["long_ctx"]
+    if d["fp8"] is not None:
+        line["decode_fp8"] = d["fp8"]
     if not args.no_prefill:
         log("prefill workload")
         line["prefill"] = run_prefill(args, torch, qsa, gen)
