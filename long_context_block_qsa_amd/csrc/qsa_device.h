@@ -9,11 +9,10 @@
 
 namespace qsa {
 
-// The layer's fixed shape: 24 query heads over 2 key/value heads of width 128
-// ("24 query heads paired with only 2 key-value (KV) heads", axbrief.com,
-// "Shifting from Tokens to Micro-Blocks"), a 4-head x 64 indexer, 4-token
-// micro-blocks (hellomarvisaitoday.com, FAQ) and a budget of at most 512 blocks
-// (elzobrito.github.io, "Linear attention carries the stream; sparse attention
+// The layer's fixed shape: 24 query heads sharing 2 key/value heads of width 128
+// (axbrief.com, "Shifting from Tokens to Micro-Blocks"), a 4-head x 64 indexer,
+// 4-token micro-blocks (hellomarvisaitoday.com, FAQ) and a budget of at most 512
+// blocks (elzobrito.github.io, "Linear attention carries the stream; sparse attention
 // retrieves detail").
 constexpr int HQ = 24;
 constexpr int HKV = 2;

@@ -163,8 +163,8 @@ static int64_t visible_blocks(const qsa_ref_dims *d, int64_t t)
 
 /* ------------------------------------------------------------- step 1 */
 
-/* Compressed key blocks. The pages say the indexer scores "compressed key
- * blocks" of 4-token micro-blocks but do not give the operator (elzobrito.github.io,
+/* Compressed key blocks. The pages have the indexer score compressed key blocks of
+ * 4-token micro-blocks but do not give the operator (elzobrito.github.io,
  * "Linear attention carries the stream; sparse attention retrieves detail").
  * Reading R1: the block key is the sum of the block's indexer keys, taken in token
  * order and stored as bf16. Only complete blocks are compressed; the trailing
@@ -288,10 +288,10 @@ static void select_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
 /* ------------------------------------------------------------- step 4 */
 
 /* Attention of one query row. Keys: the tokens of the kept blocks, in ascending
- * order, then the raw tokens after the last complete block (reading R4: "the
- * final incomplete block remains uncompressed", elzobrito.github.io). Query head h
- * reads key/value head h / (Hq/Hkv): "24 query heads paired with only 2 key-value
- * (KV) heads" (axbrief.com, "Shifting from Tokens to Micro-Blocks"), a 12:1 ratio
+ * order, then the raw tokens after the last complete block (reading R4: the last,
+ * incomplete block is attended without compression, elzobrito.github.io). Query head
+ * h reads key/value head h / (Hq/Hkv): the 24 query heads share 2 key/value heads
+ * (axbrief.com, "Shifting from Tokens to Micro-Blocks"), twelve per KV head
  * (blog.compendialabs.org, "Qwen Sparse Attention -- Full Attention When It
  * Counts"). Softmax with a max shift, then normalisation; lse = m + ln(l) of the
  * scaled logits. */
