@@ -547,6 +547,96 @@ int qsa_ref_attend_fp8(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
     return 0;
 }
 
+/* ------------------------------------------------------------- backward */
+
+/* Gradients of the attention over fixed selections: for the scalar
+ * sum_{t,h,c} dout[t,h,c] * out[t,h,c], with out as in qsa_ref_attend, the partial
+ * derivatives with respect to q, k and v. The selection is a fixed input (it is not
+ * differentiable; the pages give no training objective for the indexer). Per row and
+ * head, with z_j = scale * q.k_j and p = softmax(z) over the attended tokens J(t):
+ *   dP_j = dout . v_j,  dS_j = p_j * (dP_j - sum_i p_i dP_i),
+ *   dq += scale * sum_j dS_j k_j,  dk_j += scale * dS_j q,  dv_j += p_j dout,
+ * with dk, dv summed over every (row, head) that attends the token (row order). */
+int qsa_ref_attend_backward(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
+                            const int32_t *cu_k, const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const int32_t *sel, const double *dout,
+                            double *dq, double *dk, double *dv)
+{
+    if (!dims_ok(d) || !cu_q || !seqs_ok(batch, cu_q, cu_k) || !q || !k || !v || !sel ||
+        !dout || !dq || !dk || !dv)
+        return -1;
+    const int64_t Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
+    const int64_t bs = d->block_size, kb = d->topk_blocks;
+    const double scale = d->softmax_scale > 0 ? d->softmax_scale : 1.0 / sqrt((double)D);
+    const int64_t tq = cu_q[batch], tk = cu_k[batch];
+    memset(dq, 0, (size_t)(tq * Hq * D) * sizeof *dq);
+    memset(dk, 0, (size_t)(tk * Hkv * D) * sizeof *dk);
+    memset(dv, 0, (size_t)(tk * Hkv * D) * sizeof *dv);
+    int64_t *J = (int64_t *)malloc((size_t)(kb * bs + bs) * sizeof *J);
+    double *z = (double *)malloc((size_t)(kb * bs + bs) * sizeof *z);
+    double *dp = (double *)malloc((size_t)(kb * bs + bs) * sizeof *dp);
+    if (!J || !z || !dp) {
+        free(J), free(z), free(dp);
+        return -1;
+    }
+    for (int64_t row = 0; row < tq; ++row) {
+        row_pos p = locate_row(d, batch, cu_q, cu_k, row);
+        const int64_t nv = visible_blocks(d, p.t);
+        const int32_t *sel_row = sel + row * kb;
+        int64_t n_sel = 0;
+        while (n_sel < kb && sel_row[n_sel] >= 0)
+            ++n_sel;
+        int64_t nj = 0;
+        for (int64_t i = 0; i < n_sel; ++i)
+            for (int64_t j = 0; j < bs; ++j)
+                J[nj++] = p.key0 + (int64_t)sel_row[i] * bs + j;
+        for (int64_t j = nv * bs; j <= p.t; ++j)
+            J[nj++] = p.key0 + j;
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t g = h / (Hq / Hkv);
+            const uint16_t *qh = q + (row * Hq + h) * D;
+            const double *go = dout + (row * Hq + h) * D;
+            double m = -INFINITY;
+            for (int64_t i = 0; i < nj; ++i) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < D; ++c)
+                    dot += bf16_value(qh[c]) * bf16_value(k[(J[i] * Hkv + g) * D + c]);
+                z[i] = dot * scale;
+                if (z[i] > m)
+                    m = z[i];
+            }
+            double l = 0.0;
+            for (int64_t i = 0; i < nj; ++i) {
+                z[i] = exp(z[i] - m);
+                l += z[i];
+            }
+            double pdp = 0.0;
+            for (int64_t i = 0; i < nj; ++i) {
+                z[i] /= l; /* p_i */
+                double s = 0.0;
+                for (int64_t c = 0; c < D; ++c)
+                    s += go[c] * bf16_value(v[(J[i] * Hkv + g) * D + c]);
+                dp[i] = s;
+                pdp += z[i] * s;
+            }
+            double *gq = dq + (row * Hq + h) * D;
+            for (int64_t i = 0; i < nj; ++i) {
+                const double ds = z[i] * (dp[i] - pdp);
+                const int64_t r = J[i] * Hkv + g;
+                for (int64_t c = 0; c < D; ++c) {
+                    gq[c] += scale * ds * bf16_value(k[r * D + c]);
+                    dk[r * D + c] += scale * ds * bf16_value(qh[c]);
+                    dv[r * D + c] += z[i] * go[c];
+                }
+            }
+        }
+    }
+    free(J);
+    free(z);
+    free(dp);
+    return 0;
+}
+
 int qsa_ref_forward(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
                     const int32_t *cu_k, const uint16_t *q, const uint16_t *k,
                     const uint16_t *v, const uint16_t *q_idx, const float *w,

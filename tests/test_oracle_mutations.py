@@ -4,7 +4,8 @@ Each case compiles a copy of the oracle with one planted mistake and runs the pi
 suite against it in a subprocess; the suite must fail. This shows the pins are
 sensitive to: the tie-break, the visibility rule, the raw tail, the relu, the
 weight index, the head grouping, the softmax scale, the bf16 rounding, the
-compression range, and the FP8 cache's rounding, scale and dequantization.
+compression range, the FP8 cache's rounding, scale and dequantization, and the
+attention backward's softmax Jacobian and scale.
 """
 import os
 import subprocess
@@ -40,6 +41,10 @@ MUTATIONS = {
                           "return e4m3_value(s->f8[r * D + c]);"),
     "fp8_amax_over_256": ("float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;",
                           "float s = amax > 0.0 ? (float)(amax / 256.0) : 1.0f;"),
+    "backward_no_softmax_jacobian": ("const double ds = z[i] * (dp[i] - pdp);",
+                                     "const double ds = z[i] * dp[i];"),
+    "backward_dk_unscaled": ("dk[r * D + c] += scale * ds * bf16_value(qh[c]);",
+                             "dk[r * D + c] += ds * bf16_value(qh[c]);"),
 }
 
 

@@ -436,3 +436,57 @@ def test_attend_fp8_matches_masked_attention_on_dequantized_values():
     ref_out, ref_lse = masked_gqa_attention(as_f64(p.q), kd, vd, mask,
                                             1.0 / math.sqrt(dims.head_dim))
     assert np.max(np.abs(out8 - ref_out)) < 1e-12 and np.max(np.abs(lse8 - ref_lse)) < 1e-12
+
+
+# ----------------------------------------------------------------- attention backward
+
+def _torch_masked_gqa(q, k, v, allowed, scale):
+    """Masked dense GQA attention in float64 torch (query head h reads KV head h // 12)."""
+    hq, hkv = q.shape[1], k.shape[1]
+    kr = k.repeat_interleave(hq // hkv, dim=1)
+    vr = v.repeat_interleave(hq // hkv, dim=1)
+    logits = torch.einsum("qhd,khd->hqk", q, kr) * scale
+    logits = logits.masked_fill(~allowed[None], float("-inf"))
+    p = torch.softmax(logits, dim=-1)
+    return torch.einsum("hqk,khd->qhd", p, vr)
+
+
+def test_backward_matches_torch_autograd():
+    """dq, dk, dv equal torch autograd (float64) of sum(dout * out) through masked dense
+    GQA attention restricted to each row's kept blocks and raw tail (catches a dropped
+    softmax-Jacobian term, a wrong scale, a wrong head group, a missing raw tail)."""
+    dims = oracle.Dims(topk_blocks=3)
+    p = gen.make_problem([45, 30], q_lens=[45, 4], seed=60)
+    kb = oracle.compress(dims, p.cu_k, p.k_idx)
+    sel = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb)
+    dout = np.random.default_rng(60).normal(0.0, 1.0, (p.n_q, 24, 128))
+    dq, dk, dv = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel, dout)
+    scale = 1.0 / math.sqrt(128)
+    for b in range(2):
+        k0, k1 = int(p.cu_k[b]), int(p.cu_k[b + 1])
+        q0, q1 = int(p.cu_q[b]), int(p.cu_q[b + 1])
+        L, nq = k1 - k0, q1 - q0
+        ts = list(range(L - nq, L))
+        mask = torch.from_numpy(attended_mask(ts, sel[q0:q1], L, 4))
+        qt = torch.tensor(as_f64(p.q[q0:q1]), requires_grad=True)
+        kt = torch.tensor(as_f64(p.k[k0:k1]), requires_grad=True)
+        vt = torch.tensor(as_f64(p.v[k0:k1]), requires_grad=True)
+        out = _torch_masked_gqa(qt, kt, vt, mask, scale)
+        (out * torch.from_numpy(dout[q0:q1])).sum().backward()
+        assert np.max(np.abs(dq[q0:q1] - qt.grad.numpy())) < 1e-10
+        assert np.max(np.abs(dk[k0:k1] - kt.grad.numpy())) < 1e-10
+        assert np.max(np.abs(dv[k0:k1] - vt.grad.numpy())) < 1e-10
+        assert np.abs(kt.grad.numpy()).max() > 1e-3   # the check is not vacuous
+
+
+def test_backward_single_key_closed_form():
+    """Row t = 0 attends only token 0: the softmax is constant, so dq = 0 and token 0
+    gets dv = sum over the row's heads of its group of dout, dk = 0 from that row."""
+    dims = oracle.Dims(topk_blocks=2)
+    p = gen.make_problem([1], seed=61)
+    sel = np.full((1, 2), -1, np.int32)
+    dout = np.random.default_rng(61).normal(0.0, 1.0, (1, 24, 128))
+    dq, dk, dv = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel, dout)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    for g in range(2):
+        assert np.allclose(dv[0, g], dout[0, 12 * g:12 * (g + 1)].sum(axis=0), atol=1e-12)
