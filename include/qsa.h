@@ -179,6 +179,37 @@ qsa_status qsa_forward_fp8(const qsa_dims *dims, const qsa_seqs *seqs, const qsa
                            const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel, float *out,
                            float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- backward
+ * Gradients of the attention over FIXED selections: the pages speak of how the model
+ * was trained (axbrief.com, "Shifting from Tokens to Micro-Blocks", its optimizers) but
+ * give no training objective for the indexer,
+ * so only the attention is differentiated; selection and compression have no
+ * gradient. For a loss whose gradient with respect to out is dout, with P the softmax
+ * of the scaled logits of a (row, head) over its attended keys (its selected blocks'
+ * tokens and its raw tail, as in qsa_attend) and D = sum_d dout * out of that
+ * (row, head):
+ *   dP = dout . v_j,   dS = P * (dP - D),
+ *   dq = scale * sum_j dS_j k_j,   dk_j = scale * sum dS_j q,   dv_j = sum P_j dout,
+ * the last two summed over every (row, head of the key's KV group) that attends key j.
+ * Layouts: q, sel, out, lse as in qsa_attend (out and lse as qsa_attend wrote them);
+ * dout [Tq, 24, 128] bf16; dq [Tq, 24, 128] fp32; dk, dv [Tk, 2, 128] fp32, written for
+ * every key (0 where no row attends it). Results are deterministic: no gradient is
+ * accumulated with atomics. The workspace (its own size, below) starts with the same
+ * 4 KiB control block as the forward's, which this call does not touch, so one
+ * allocation of the larger size serves both. All pointers 16-byte aligned. */
+
+/* Bytes of workspace qsa_attend_backward needs (about 4 * Tq * (topk + 1) for the
+ * block -> rows lists plus small tables). Host-only. QSA_ERR_UNSUPPORTED when
+ * Tq * (topk + 1) exceeds INT32_MAX. */
+qsa_status qsa_backward_workspace_size(const qsa_dims *dims, const qsa_seqs *seqs,
+                                       size_t *bytes);
+
+qsa_status qsa_attend_backward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                               const qsa_bf16 *k, const qsa_bf16 *v, const int32_t *sel,
+                               const float *out, const float *lse, const qsa_bf16 *dout,
+                               float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
+                               void *stream);
+
 /* ---------------------------------------------------------------- diagnostics
  * Per-kernel timing with HIP events, for benchmarks and profiling. Between
  * qsa_trace_begin and qsa_trace_end on one host thread, each kernel the library
@@ -195,7 +226,15 @@ enum {
     QSA_KERNEL_SCORE = 2,
     QSA_KERNEL_SELECT = 3,
     QSA_KERNEL_ATTEND = 4,
-    QSA_KERNEL_COMBINE = 5
+    QSA_KERNEL_COMBINE = 5,
+    QSA_KERNEL_BWD_PREP = 6,
+    QSA_KERNEL_BWD_ROWS = 7,
+    QSA_KERNEL_BWD_COUNT = 8,
+    QSA_KERNEL_BWD_COLSCAN = 9,
+    QSA_KERNEL_BWD_SCAN = 10,
+    QSA_KERNEL_BWD_FILL = 11,
+    QSA_KERNEL_BWD_DQ = 12,
+    QSA_KERNEL_BWD_DKV = 13
 };
 qsa_status qsa_trace_begin(int32_t max_kernels);
 int32_t qsa_trace_end(int32_t max_out, int32_t *kind_out, float *ms_out);

@@ -59,6 +59,10 @@ _SIGS = {
     "qsa_attend_fp8": ([ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "qsa_forward_fp8": ([ctypes.c_void_p] * 15 + [ctypes.c_size_t, ctypes.c_void_p],
                         ctypes.c_int),
+    "qsa_backward_workspace_size": ([ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "qsa_attend_backward": ([ctypes.c_void_p] * 13 + [ctypes.c_size_t, ctypes.c_void_p],
+                            ctypes.c_int),
     "qsa_trace_begin": ([ctypes.c_int32], ctypes.c_int),
     "qsa_trace_end": ([ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int32),
     "qsa_kernel_name": ([ctypes.c_int32], ctypes.c_char_p),
@@ -268,6 +272,45 @@ def forward_fp8(seqs: Seqs, q, k8, v8, k_scale, v_scale, q_idx, w, k_idx, k_blk,
                                  _ptr(lse, "lse", 4, (seqs.n_q, HQ)),
                                  _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
            "qsa_forward_fp8")
+
+
+def backward_workspace_size(seqs: Seqs, topk: int = KMAX) -> int:
+    d = make_dims(topk)
+    n = ctypes.c_size_t(0)
+    _check(lib().qsa_backward_workspace_size(ctypes.byref(d), ctypes.byref(seqs.c),
+                                             ctypes.byref(n)), "qsa_backward_workspace_size")
+    return int(n.value)
+
+
+def alloc_backward_workspace(seqs: Seqs, topk: int = KMAX, device="cuda"):
+    """A zero-filled device buffer of qsa_backward_workspace_size() bytes, 256-byte
+    aligned."""
+    import torch
+    n = backward_workspace_size(seqs, topk)
+    buf = torch.zeros(n + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + n] if n > 0 else buf[off:off + 1]
+
+
+def attend_backward(seqs: Seqs, q, k, v, sel, out, lse, dout, dq, dk, dv, ws, topk: int = KMAX,
+                    softmax_scale=0.0, stream=None):
+    """Gradients dq [Tq, 24, 128], dk, dv [Tk, 2, 128] (fp32) of the attention over the
+    fixed selection sel, given its out and lse and the bf16 gradient dout of out."""
+    d = make_dims(topk, softmax_scale)
+    _check(lib().qsa_attend_backward(ctypes.byref(d), ctypes.byref(seqs.c),
+                                     _ptr(q, "q", 2, (seqs.n_q, HQ, D)),
+                                     _ptr(k, "k", 2, (seqs.n_k, HKV, D)),
+                                     _ptr(v, "v", 2, (seqs.n_k, HKV, D)),
+                                     _ptr(sel, "sel", 4, (seqs.n_q, topk)),
+                                     _ptr(out, "out", 4, (seqs.n_q, HQ, D)),
+                                     _ptr(lse, "lse", 4, (seqs.n_q, HQ)),
+                                     _ptr(dout, "dout", 2, (seqs.n_q, HQ, D)),
+                                     _ptr(dq, "dq", 4, (seqs.n_q, HQ, D)),
+                                     _ptr(dk, "dk", 4, (seqs.n_k, HKV, D)),
+                                     _ptr(dv, "dv", 4, (seqs.n_k, HKV, D)),
+                                     _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                                     _stream(stream)),
+           "qsa_attend_backward")
 
 
 class trace:

@@ -351,6 +351,45 @@ qsa_status forward_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_
     return run_attend(p, q, k, v, fp8, sel_use, out, lse, ws, hs);
 }
 
+// Attention backward: per-sequence table, D, nsel, list offsets, block totals, count
+// matrices and block -> rows lists after the control block.
+struct BwdPlan {
+    Plan p;
+    int64_t n_chunks = 0, nkb_total = 0, mat_entries = 0, max_entries = 0;
+    size_t off_seq = 0, off_delta = 0, off_nsel = 0, off_off = 0, off_tot = 0, off_mat = 0,
+           off_list = 0, ws_bytes = 0;
+};
+
+qsa_status make_bwd_plan(const qsa_dims *d, const qsa_seqs *s, BwdPlan *bp) {
+    qsa_status st = make_plan(d, s, true, &bp->p);
+    if (st != QSA_OK) return st;
+    const int32_t *ck = s->cu_k_host, *cq = s->cu_q_host;
+    for (int b = 0; b < s->batch; ++b) {
+        const int64_t L = (int64_t)ck[b + 1] - ck[b], nq = (int64_t)cq[b + 1] - cq[b];
+        const int64_t nkb = (L + qsa::BS - 1) / qsa::BS, nch = (nq + qsa::BWD_CH - 1) / qsa::BWD_CH;
+        bp->nkb_total += nkb;
+        bp->n_chunks += nch;
+        bp->mat_entries += nkb * nch;
+    }
+    // every row attends at most topk selected blocks and its raw tail: list positions,
+    // block offsets and counts stay within int32
+    bp->max_entries = bp->p.tq * (int64_t)(bp->p.topk + 1);
+    if (bp->max_entries > INT32_MAX || bp->nkb_total >= INT32_MAX ||
+        bp->n_chunks > INT32_MAX)
+        return QSA_ERR_UNSUPPORTED;
+    const size_t ctl_b = (size_t)qsa::CTL_WORDS * sizeof(uint32_t);
+    size_t o = ctl_b;
+    bp->off_seq = o;   o += align_up((size_t)std::max(s->batch, 1) * sizeof(qsa::BwdSeq));
+    bp->off_delta = o; o += align_up((size_t)bp->p.tq * qsa::HQ * sizeof(float));
+    bp->off_nsel = o;  o += align_up((size_t)bp->p.tq * sizeof(int32_t));
+    bp->off_off = o;   o += align_up((size_t)(bp->nkb_total + 1) * sizeof(int32_t));
+    bp->off_tot = o;   o += align_up((size_t)bp->nkb_total * sizeof(int32_t));
+    bp->off_mat = o;   o += align_up((size_t)bp->mat_entries * sizeof(int32_t));
+    bp->off_list = o;  o += align_up((size_t)bp->max_entries * sizeof(int32_t));
+    bp->ws_bytes = o;
+    return QSA_OK;
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -461,6 +500,49 @@ qsa_status qsa_forward_fp8(const qsa_dims *dims, const qsa_seqs *seqs, const qsa
                           out, lse, ws, ws_bytes, stream);
 }
 
+qsa_status qsa_backward_workspace_size(const qsa_dims *dims, const qsa_seqs *seqs,
+                                       size_t *bytes) {
+    if (!bytes) return QSA_ERR_NULL;
+    BwdPlan bp;
+    qsa_status st = make_bwd_plan(dims, seqs, &bp);
+    if (st != QSA_OK) return st;
+    *bytes = bp.ws_bytes;
+    return QSA_OK;
+}
+
+qsa_status qsa_attend_backward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                               const qsa_bf16 *k, const qsa_bf16 *v, const int32_t *sel,
+                               const float *out, const float *lse, const qsa_bf16 *dout,
+                               float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
+                               void *stream) {
+    BwdPlan bp;
+    qsa_status st = make_bwd_plan(dims, seqs, &bp);
+    if (st != QSA_OK) return st;
+    const Plan &p = bp.p;
+    if (p.tq == 0 && p.tk == 0) return QSA_OK;
+    if (p.tk > 0 && (!k || !v || !dk || !dv)) return QSA_ERR_NULL;
+    if (p.tq > 0 && (!q || !sel || !out || !lse || !dout || !dq)) return QSA_ERR_NULL;
+    if ((q && !aligned16(q)) || (k && !aligned16(k)) || (v && !aligned16(v)) ||
+        (sel && !aligned16(sel)) || (out && !aligned16(out)) || (lse && !aligned16(lse)) ||
+        (dout && !aligned16(dout)) || (dq && !aligned16(dq)) || (dk && !aligned16(dk)) ||
+        (dv && !aligned16(dv)))
+        return QSA_ERR_SHAPE;
+    if (!ws) return QSA_ERR_NULL;
+    if (((uintptr_t)ws % kAlign) != 0 || ws_bytes < bp.ws_bytes) return QSA_ERR_WORKSPACE;
+    qsa::BwdBuffers b;
+    b.seq = ws_at<qsa::BwdSeq>(ws, bp.off_seq);
+    b.delta = ws_at<float>(ws, bp.off_delta);
+    b.nsel = ws_at<int32_t>(ws, bp.off_nsel);
+    b.off = ws_at<int32_t>(ws, bp.off_off);
+    b.tot = ws_at<int32_t>(ws, bp.off_tot);
+    b.mat = ws_at<int32_t>(ws, bp.off_mat);
+    b.list = ws_at<int32_t>(ws, bp.off_list);
+    QSA_TRY(qsa::launch_backward(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk, p.scale, p.tq,
+                                 bp.n_chunks, bp.nkb_total, q, k, v, sel, out, lse, dout, dq,
+                                 dk, dv, b, (hipStream_t)stream));
+    return QSA_OK;
+}
+
 qsa_status qsa_trace_begin(int32_t max_kernels) {
     qsa::Trace &t = qsa::g_trace;
     if (t.open || max_kernels < 1 || max_kernels > (1 << 20)) return QSA_ERR_SHAPE;
@@ -508,8 +590,11 @@ int32_t qsa_trace_end(int32_t max_out, int32_t *kind_out, float *ms_out) {
 }
 
 const char *qsa_kernel_name(int32_t kind) {
-    static const char *names[] = {"prep", "compress", "score", "select", "attend", "combine"};
-    return (kind >= 0 && kind < 6) ? names[kind] : "unknown";
+    static const char *names[] = {"prep",     "compress",    "score",    "select",
+                                  "attend",   "combine",     "bwd_prep", "bwd_rows",
+                                  "bwd_count", "bwd_colscan", "bwd_scan", "bwd_fill",
+                                  "bwd_dq",   "bwd_dkv"};
+    return (kind >= 0 && kind < 14) ? names[kind] : "unknown";
 }
 
 }  // extern "C"

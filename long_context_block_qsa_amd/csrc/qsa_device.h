@@ -40,6 +40,20 @@ struct SeqInfo {
     int64_t s0;     // first score slot
 };
 
+// Per-sequence table of the attention backward. Key blocks are the ceil(L/4) groups of
+// 4 tokens of a sequence (the last one may be partial: it is only attended raw); query
+// rows are cut into chunks of BWD_CH consecutive rows of one sequence.
+constexpr int BWD_CH = 256;
+constexpr int BWD_CAP = 16384;  // key blocks counted per LDS pass of the index kernels
+struct BwdSeq {
+    int32_t q0, nq, k0, L;
+    int32_t kb0;   // first key block (global numbering over all sequences)
+    int32_t nkb;   // ceil(L / 4)
+    int32_t ch0;   // first row chunk
+    int32_t nch;   // ceil(nq / BWD_CH)
+    int64_t m0;    // first entry of the sequence's [nch][nkb] count matrix
+};
+
 // Host-computed row and tile tables passed as kernel arguments when a call has few
 // query rows (decode): no table kernel and no device-side sequence lookup.
 constexpr int DEC_MAX = 64;

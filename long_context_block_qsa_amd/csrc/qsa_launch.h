@@ -42,6 +42,23 @@ hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, i
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
                          float *part, int nsplit, int64_t n_rows, hipStream_t st);
+// Attention backward over fixed selections (qsa_backward.hip).
+struct BwdSeq;
+struct BwdBuffers {
+    BwdSeq *seq;      // [batch]
+    float *delta;     // [Tq, 24]
+    int32_t *nsel;    // [Tq]
+    int32_t *off;     // [nkb_total + 1]
+    int32_t *tot;     // [nkb_total]
+    int32_t *mat;     // count matrices of all sequences
+    int32_t *list;    // block -> rows lists
+};
+hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, int batch, int topk,
+                           float scale, int64_t n_rows, int64_t n_chunks, int64_t nkb_total,
+                           const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const int32_t *sel, const float *out, const float *lse,
+                           const uint16_t *dout, float *dq, float *dk, float *dv,
+                           const BwdBuffers &b, hipStream_t st);
 hipError_t launch_quantize_kv(const uint16_t *k, const uint16_t *v, uint8_t *k8, uint8_t *v8,
                               float *k_scale, float *v_scale, int64_t rows, hipStream_t st);
 

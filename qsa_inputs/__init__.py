@@ -39,6 +39,7 @@ _SRC = os.path.join(_HERE, "qsa_gen.c")
 _LIB_PATH = os.path.join(_HERE, "libqsa_gen.so")
 
 TID_Q, TID_K, TID_V, TID_QIDX, TID_KIDX, TID_W, TID_NEEDLE, TID_OUTLIER = 1, 2, 3, 4, 5, 6, 7, 8
+TID_DOUT = 9
 
 HQ, HKV, D, HI, DI, BS, TOPK = 24, 2, 128, 4, 64, 4, 512
 
@@ -206,6 +207,13 @@ def make_problem(lens, q_lens=None, seed=1234, qkv_scale=1.0, outlier_frac=0.0,
 
     return Problem(cu_q=cu_q, cu_k=cu_k, q=q, k=k, v=v, q_idx=q_idx, w=w, k_idx=k_idx,
                    topk=int(topk), needles=placed, name=name)
+
+
+def make_dout(p: "Problem", seed: int, scale: float = 1.0, threads=None) -> np.ndarray:
+    """Gradient of the attention output for a backward pass: bf16 ~N(0, scale^2) bits,
+    [Tq, HQ, D]."""
+    return normal_bf16(seed, TID_DOUT, p.n_q * HQ * D, scale,
+                       threads=_nthreads(threads)).reshape(p.n_q, HQ, D)
 
 
 CONFIGS = {

@@ -31,6 +31,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"qsa_abi_version", "qsa_status_string", "qsa_workspace_size",
                           "qsa_compress", "qsa_select", "qsa_attend", "qsa_forward",
                           "qsa_quantize_kv", "qsa_attend_fp8", "qsa_forward_fp8",
+                          "qsa_backward_workspace_size", "qsa_attend_backward",
                           "qsa_trace_begin", "qsa_trace_end", "qsa_kernel_name"}
     out = subprocess.run(["nm", "-D", "--defined-only", qsa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -122,6 +123,53 @@ def test_fp8_entry_points_validate_first():
                              f, f, f, f, nbytes - 1, None) == qsa.QSA_ERR_WORKSPACE
 
 
+def _bws(dims, seqs):
+    n = ctypes.c_size_t(0)
+    st = qsa.lib().qsa_backward_workspace_size(ctypes.byref(dims), ctypes.byref(seqs),
+                                               ctypes.byref(n))
+    return st, n.value
+
+
+def test_backward_entry_point_validates_first():
+    """qsa_attend_backward rejects missing, misaligned or undersized operands before any
+    device call; its workspace covers the block -> rows lists."""
+    d = qsa.make_dims()
+    L = qsa.lib()
+    s = _seqs([0, 40], [0, 40])
+    st, nbytes = _bws(d, s)
+    assert st == 0
+    assert nbytes >= 4 * 40 * (512 + 1)
+    f = ctypes.c_void_p(FAKE)
+    odd = ctypes.c_void_p(FAKE + 4)
+    args = [f] * 10   # q k v sel out lse dout dq dk dv
+    def call(a, ws=f, n=nbytes):
+        return L.qsa_attend_backward(ctypes.byref(d), ctypes.byref(s), *a, ws, n, None)
+    for i in range(10):
+        a = list(args)
+        a[i] = None
+        assert call(a) == qsa.QSA_ERR_NULL, i
+        a[i] = odd
+        assert call(a) == qsa.QSA_ERR_SHAPE, i
+    assert call(args, ws=None) == qsa.QSA_ERR_NULL
+    assert call(args, n=nbytes - 1) == qsa.QSA_ERR_WORKSPACE
+    assert call(args, ws=ctypes.c_void_p(FAKE + 16)) == qsa.QSA_ERR_WORKSPACE
+    # totals beyond int32 list positions are refused
+    big = _seqs([0, 2**22 + 8], [0, 2**22 + 8])
+    assert _bws(d, big)[0] == qsa.QSA_ERR_UNSUPPORTED
+    # dims are validated as in the forward
+    d2 = qsa.make_dims()
+    d2.head_dim = 64
+    assert _bws(d2, s)[0] == qsa.QSA_ERR_UNSUPPORTED
+
+
+def test_backward_workspace_grows_with_rows_and_budget():
+    d = qsa.make_dims(topk=512)
+    a = _bws(d, _seqs([0, 1000], [0, 1000]))[1]
+    b = _bws(d, _seqs([0, 4000], [0, 4000]))[1]
+    c = _bws(qsa.make_dims(topk=16), _seqs([0, 4000], [0, 4000]))[1]
+    assert b > a and b > c
+
+
 def test_workspace_checks():
     d = qsa.make_dims()
     s = _seqs([0, 40000], [0, 40000])
@@ -173,5 +221,7 @@ def test_trace_end_without_begin_and_names():
     L = qsa.lib()
     assert L.qsa_trace_end(0, None, None) == -1
     assert qsa.lib().qsa_kernel_name(2) == b"score"
+    assert qsa.lib().qsa_kernel_name(12) == b"bwd_dq"
+    assert qsa.lib().qsa_kernel_name(13) == b"bwd_dkv"
     assert qsa.lib().qsa_kernel_name(42) == b"unknown"
     assert L.qsa_trace_begin(0) == qsa.QSA_ERR_SHAPE
