@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context decode line")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV cache lines")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the prefill's attention backward line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--trace-steps", type=int, default=8)
@@ -354,8 +356,11 @@ def run_prefill(args, torch, qsa, gen):
                "kernel_ms": {k2: round(v2, 4) for k2, v2 in km8.items()},
                "attention_tflops": round(att_flop / (att8 / 1e3) / 1e12, 2),
                "attention_gather_gbs": round(pairs * HKV * (2 * D + 8) / (att8 / 1e3) / 1e9, 1)}
+    bwd = None if args.no_backward else run_prefill_backward(args, torch, qsa, gen, p, seqs, q, k,
+                                                             v, sel, out, lse, n, pairs)
     return {
         "fp8_kv": fp8,
+        "backward": bwd,
         "workload": "ragged prefill 65,535/40,001/8,190/3 tokens, budget 512 blocks",
         "ms_per_step": round(ms, 3),
         "query_tokens_per_s": round(seqs.n_q / (ms / 1e3), 1),
@@ -366,6 +371,44 @@ def run_prefill(args, torch, qsa, gen):
         "attention_gather_gbs": round(pairs * HKV * D * 2 * 2 / (att_ms / 1e3) / 1e9, 1),
         "score_tflops": round(score_flop / (km.get("score", float("nan")) / 1e3) / 1e12, 2),
     }
+
+
+def run_prefill_backward(args, torch, qsa, gen, p, seqs, q, k, v, sel, out, lse, n, pairs):
+    """Attention backward over the prefill's own selection, out and lse, with a seeded
+    bf16 dout: dq, dk, dv of all 113,729 rows."""
+    dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    dout = dev16(gen.make_dout(p, 900))
+    dq = torch.empty((seqs.n_q, HQ, D), dtype=torch.float32, device="cuda")
+    dk = torch.empty((seqs.n_k, HKV, D), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    bws = qsa.alloc_backward_workspace(seqs, TOPK)
+
+    def stepb():
+        qsa.attend_backward(seqs, q, k, v, sel, out, lse, dout, dq, dk, dv, bws, TOPK)
+
+    stepb()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        stepb()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    with qsa.trace(64) as tr:
+        stepb()
+    torch.cuda.synchronize()
+    km = tr.mean_ms()
+    # five contractions per attended (query head, key): S and dP recomputed, dQ, dK, dV
+    flop = pairs * HQ * D * 2 * 5
+    # rows x kept blocks per KV head (the dK/dV kernel's row visits)
+    return {"ms_per_step": round(ms, 3),
+            "query_tokens_per_s": round(seqs.n_q / (ms / 1e3), 1),
+            "kernel_ms": {k2: round(v2, 4) for k2, v2 in km.items()},
+            "tflops": round(flop / (ms / 1e3) / 1e12, 2),
+            "mfma_frac": round(flop / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "dq_gather_gbs": round(pairs * HKV * D * 2 * 2 / (km.get("bwd_dq", float("nan")) / 1e3)
+                                   / 1e9, 1),
+            "dkv_row_gbs": round(pairs / BS * HQ * D * 2 * 2 /
+                                 (km.get("bwd_dkv", float("nan")) / 1e3) / 1e9, 1)}
 
 
 # ---------------------------------------------------------------- CPU baseline

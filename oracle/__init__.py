@@ -82,7 +82,8 @@ def _load():
         lib.qsa_ref_quantize_kv.argtypes = [dp, i32, P, P, P, P, P, P, P]
         lib.qsa_ref_attend_fp8.argtypes = [dp, i32, P, P, P, P, P, P, P, P, P, P, P, i64,
                                            i32]
-        lib.qsa_ref_attend_backward.argtypes = [dp, i32, P, P, P, P, P, P, P, P, P, P]
+        lib.qsa_ref_attend_backward.argtypes = [dp, i32, P, P, P, P, P, P, P, P, P, P, P,
+                                                i64]
         lib.qsa_ref_bf16_round.argtypes = [ctypes.c_double]
         lib.qsa_ref_bf16_round.restype = ctypes.c_uint16
         lib.qsa_ref_e4m3_round.argtypes = [ctypes.c_double]
@@ -174,19 +175,22 @@ def attend_fp8(dims: Dims, cu_q, cu_k, q, k8, v8, k_scale, v_scale, sel, rows=No
     return out, lse
 
 
-def attend_backward(dims: Dims, cu_q, cu_k, q, k, v, sel, dout):
-    """Gradients (dq, dk, dv) of sum(dout * out) for attend() over fixed selections."""
+def attend_backward(dims: Dims, cu_q, cu_k, q, k, v, sel, dout, rows=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) for attend() over fixed selections.
+    With ``rows`` only those query rows contribute (dq of other rows stays 0, dk and dv
+    hold those rows' shares)."""
     cu_q, cu_k = _arr(cu_q, np.int32), _arr(cu_k, np.int32)
     q, k, v = _arr(q, np.uint16), _arr(k, np.uint16), _arr(v, np.uint16)
     sel, dout = _arr(sel, np.int32), _arr(dout, np.float64)
     dq = np.zeros(q.shape, dtype=np.float64)
     dk = np.zeros(k.shape, dtype=np.float64)
     dv = np.zeros(v.shape, dtype=np.float64)
+    r, nr = _rows(rows)
     d = dims._c()
     _check(_load().qsa_ref_attend_backward(ctypes.byref(d), len(cu_k) - 1, _ptr(cu_q),
                                            _ptr(cu_k), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
-                                           _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv)),
-           "attend_backward")
+                                           _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(r),
+                                           nr), "attend_backward")
     return dq, dk, dv
 
 

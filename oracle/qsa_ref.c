@@ -560,10 +560,11 @@ int qsa_ref_attend_fp8(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
 int qsa_ref_attend_backward(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
                             const int32_t *cu_k, const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, const int32_t *sel, const double *dout,
-                            double *dq, double *dk, double *dv)
+                            double *dq, double *dk, double *dv, const int64_t *rows,
+                            int64_t n_rows)
 {
     if (!dims_ok(d) || !cu_q || !seqs_ok(batch, cu_q, cu_k) || !q || !k || !v || !sel ||
-        !dout || !dq || !dk || !dv)
+        !dout || !dq || !dk || !dv || !rows_ok(cu_q, batch, rows, n_rows))
         return -1;
     const int64_t Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
     const int64_t bs = d->block_size, kb = d->topk_blocks;
@@ -579,7 +580,9 @@ int qsa_ref_attend_backward(const qsa_ref_dims *d, int32_t batch, const int32_t 
         free(J), free(z), free(dp);
         return -1;
     }
-    for (int64_t row = 0; row < tq; ++row) {
+    const int64_t n_loop = rows ? n_rows : tq;
+    for (int64_t ri = 0; ri < n_loop; ++ri) {
+        const int64_t row = rows ? rows[ri] : ri;
         row_pos p = locate_row(d, batch, cu_q, cu_k, row);
         const int64_t nv = visible_blocks(d, p.t);
         const int32_t *sel_row = sel + row * kb;

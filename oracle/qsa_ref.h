@@ -104,11 +104,14 @@ int qsa_ref_attend_fp8(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
 
 /* Backward of qsa_ref_attend over fixed selections: given dout [Tq, Hq, D], the
  * gradients dq [Tq, Hq, D], dk and dv [Tk, Hkv, D] of sum(dout * out). Single-threaded
- * (dk and dv accumulate across rows in row order). */
+ * (dk and dv accumulate across rows in the given row order). With rows != NULL only
+ * those query rows contribute: their dq, and their shares of dk and dv (every other
+ * entry is 0), so a key attended only by those rows gets its full gradient. */
 int qsa_ref_attend_backward(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
                             const int32_t *cu_k, const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, const int32_t *sel, const double *dout,
-                            double *dq, double *dk, double *dv);
+                            double *dq, double *dk, double *dv, const int64_t *rows,
+                            int64_t n_rows);
 
 /* The bf16 and E4M3 roundings the oracle uses and the E4M3 decoding (exposed so tests
  * can pin them). E4M3 rounding saturates finite magnitudes beyond 448 to 448. */

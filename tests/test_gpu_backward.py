@@ -113,3 +113,63 @@ def test_backward_is_deterministic():
     b = bp.backward()
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def _attending_rows(p, dims, kb, seq, blk):
+    """Rows of sequence `seq` that attend its key block `blk` by the oracle's own
+    selection: rows whose kept blocks hold it, and rows whose raw tail lies in it.
+    Returns (candidate rows, their oracle selections, attending rows)."""
+    q0, q1 = int(p.cu_q[seq]), int(p.cu_q[seq + 1])
+    L = int(p.cu_k[seq + 1] - p.cu_k[seq])
+    t0 = L - (q1 - q0)
+    cand = np.array([r for r in range(q0, q1) if t0 + (r - q0) >= 4 * blk], dtype=np.int64)
+    sel_c = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb, rows=cand)
+    att = []
+    for r in cand:
+        t = t0 + (r - q0)
+        nv = (t + 1) // 4
+        if blk in set(sel_c[r][sel_c[r] >= 0].tolist()) or (nv == blk and t + 1 > 4 * nv):
+            att.append(int(r))
+    return cand, sel_c, np.array(att, dtype=np.int64)
+
+
+def test_backward_config4_ragged_prefill_sampled():
+    """The ragged 4-sequence prefill (65535/40001/8190/3 tokens, budget 512) at full size:
+    dq on sampled rows, dk and dv on sampled key blocks (from the oracle over exactly the
+    rows that attend them: late blocks of each sequence, the partial final blocks)."""
+    _banner("backward config 4: ragged prefill 65535/40001/8190/3")
+    p = gen.config_problem(4)
+    bp = BwdProblem(p, 512)
+    _, sel, _, _ = bp.forward()
+    dq, dk, dv = bp.backward()
+    dims = oracle.Dims(topk_blocks=512)
+    kb = oracle.compress(dims, p.cu_k, p.k_idx)
+    dout = gen.bf16_to_f32(bp.dout_np).astype(np.float64)
+
+    cu = p.cu_q
+    rng = np.random.default_rng(45)
+    rows = set()
+    for b in range(4):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        rows.update(range(lo, min(hi, lo + 3)))
+        rows.update(range(max(lo, hi - 3), hi))
+        if hi - lo > 10:
+            rows.update(rng.integers(lo, hi, 6).tolist())
+    rows = np.array(sorted(rows), dtype=np.int64)
+    sel_r = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb, rows=rows)
+    assert np.array_equal(sel[rows], sel_r[rows])
+    dq_r, _, _ = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel_r, dout,
+                                        rows=rows)
+    _bars("cfg4 dq (sampled rows)", dq[rows], dq_r[rows])
+
+    for seq, blk in ((0, 16383), (0, 16150), (1, 9800), (2, 1950), (3, 0)):
+        cand, sel_c, att = _attending_rows(p, dims, kb, seq, blk)
+        assert np.array_equal(sel[cand], sel_c[cand]), (seq, blk)
+        assert att.size > 0
+        _, dk_r, dv_r = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel_c,
+                                               dout, rows=att)
+        k0 = int(p.cu_k[seq]) + 4 * blk
+        k1 = min(k0 + 4, int(p.cu_k[seq + 1]))
+        print(f"  block ({seq}, {blk}): {att.size} attending rows of {cand.size}", flush=True)
+        _bars(f"cfg4 dk block ({seq},{blk})", dk[k0:k1], dk_r[k0:k1])
+        _bars(f"cfg4 dv block ({seq},{blk})", dv[k0:k1], dv_r[k0:k1])

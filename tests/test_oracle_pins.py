@@ -490,3 +490,23 @@ def test_backward_single_key_closed_form():
     assert np.all(dq == 0.0) and np.all(dk == 0.0)
     for g in range(2):
         assert np.allclose(dv[0, g], dout[0, 12 * g:12 * (g + 1)].sum(axis=0), atol=1e-12)
+
+
+def test_backward_row_subsets_add_up():
+    """The loss sum(dout * out) is a sum over query rows, so the gradients restricted to
+    a partition of the rows add up to the full ones and each part's dq rows are the full
+    dq rows (pins the row-subset option the full-size GPU checks use)."""
+    dims = oracle.Dims(topk_blocks=4)
+    p = gen.make_problem([60, 23], q_lens=[60, 9], seed=62)
+    kb = oracle.compress(dims, p.cu_k, p.k_idx)
+    sel = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb)
+    dout = np.random.default_rng(62).normal(0.0, 1.0, (p.n_q, 24, 128))
+    full = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel, dout)
+    rows = np.random.default_rng(63).permutation(p.n_q)
+    a, b = np.sort(rows[:30]), rows[30:]
+    ga = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel, dout, rows=a)
+    gb = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel, dout, rows=b)
+    for f, x, y in zip(full, ga, gb):
+        assert np.max(np.abs(f - (x + y))) < 1e-10
+    assert np.array_equal(ga[0][a], full[0][a]) and np.all(ga[0][b] == 0.0)
+    assert np.abs(ga[1]).max() > 1e-3 and np.abs(gb[1]).max() > 1e-3
