@@ -301,8 +301,10 @@ __device__ __forceinline__ void select_keys(KP_T kk, IP_T ii, int64_t n, int top
 }
 
 // Level-one merges take at most MERGE_CHUNKS chunk lists (KP candidates each); rows
-// with more chunks first merge groups of MERGE_CHUNKS chunks, then the group lists
-// (topk entries each) of at most MAX_GROUPS groups.
+// with more chunks first merge G = ceil(nch / MERGE_CHUNKS) groups of ceil(nch / G)
+// consecutive chunks (balanced, so every group holds more than MERGE_CHUNKS / 2 chunk
+// lists: at least topk real candidates), then the group lists (topk entries each) of
+// at most MAX_GROUPS groups.
 constexpr int MERGE_CHUNKS = 64;
 constexpr int MAX_GROUPS = 4;
 
@@ -613,11 +615,12 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
     const int tid = threadIdx.x;
     const int nch = (int)((nv_max + a.ch - 1) / a.ch);
     const int ngroups = (nch + MERGE_CHUNKS - 1) / MERGE_CHUNKS;
+    const int gsize = (nch + ngroups - 1) / ngroups;   // chunks per group (balanced)
     // groups of chunks are merged separately when there are 2 .. MAX_GROUPS of them
     const bool grouped = ngroups > 1 && ngroups <= MAX_GROUPS;
     if (grouped) {
-        const int grp = chunk / MERGE_CHUNKS;
-        const int n_in = min(MERGE_CHUNKS, nch - grp * MERGE_CHUNKS);
+        const int grp = chunk / gsize;
+        const int n_in = min(gsize, nch - grp * gsize);
         if (tid == 0) {
             uint32_t *cnt = &a.ctl[CTL_GROUP + tile * MAX_GROUPS + grp];
             const uint32_t old = atomicAdd(cnt, 1u);
@@ -629,11 +632,11 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
         for (int rr = 0; rr < nrows; ++rr) {
             const int64_t nv = nvis_of(t0 + rr), row = row0 + rr;
             if (!cand_eligible(nv, a.topk, a.ch)) continue;   // uniform
-            const int64_t cbase = (row * a.max_chunks + grp * MERGE_CHUNKS) * KP;
+            const int64_t cbase = (row * a.max_chunks + grp * gsize) * KP;
             const int64_t gbase = (row * MAX_GROUPS + grp) * a.topk;
             const bool ok = merge_candidates<true>(
                 a.cand_key + cbase, a.cand_idx + cbase, n_in * KP, a.topk, a.glist_idx + gbase,
-                a.glist_key + gbase, nv, a.ch, grp * MERGE_CHUNKS, &sm.viol, &sm.tsm);
+                a.glist_key + gbase, nv, a.ch, grp * gsize, &sm.viol, &sm.tsm);
             if (!ok && tid == 0) store_wt(&a.ctl[CTL_EXACT + row], 1u);
         }
         wait_vmem();

@@ -139,6 +139,15 @@ def test_multi_query_long_rows_grouped():
     _check_rows("mq-grouped", DeviceProblem(p, 512), None, 512)
 
 
+@pytest.mark.parametrize("L", [266001, 526001])
+def test_decode_grouped_uneven_chunk_counts(L):
+    """65 and 129 chunks of 1024 blocks: the chunk groups are balanced (33 + 32, 3 x 43)
+    so every group merge sees at least topk real candidates."""
+    _banner(f"decode grouped, {L} tokens")
+    p = gen.make_problem([L], q_lens=[1], seed=20 + L % 7)
+    _check_rows(f"grouped-{L}", DeviceProblem(p, 512), None, 512)
+
+
 def test_grouped_merge_exact_fallback():
     """A grouped row (100,000 blocks) whose best blocks form one run of 300 blocks: the
     group merge finds a chunk with every candidate kept and the row is selected exactly."""
