@@ -396,7 +396,7 @@ def run_prefill_backward(args, torch, qsa, gen, p, seqs, q, k, v, sel, out, lse,
     with qsa.trace(64) as tr:
         stepb()
     torch.cuda.synchronize()
-    km = tr.mean_ms()
+    km = tr.total_ms()   # the dK/dV kernel runs once per row window
     # five contractions per attended (query head, key): S and dP recomputed, dQ, dK, dV
     flop = pairs * HQ * D * 2 * 5
     # rows x kept blocks per KV head (the dK/dV kernel's row visits)

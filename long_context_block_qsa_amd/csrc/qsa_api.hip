@@ -537,7 +537,8 @@ qsa_status qsa_attend_backward(const qsa_dims *dims, const qsa_seqs *seqs, const
     b.tot = ws_at<int32_t>(ws, bp.off_tot);
     b.mat = ws_at<int32_t>(ws, bp.off_mat);
     b.list = ws_at<int32_t>(ws, bp.off_list);
-    QSA_TRY(qsa::launch_backward(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk, p.scale, p.tq,
+    QSA_TRY(qsa::launch_backward(seqs->cu_q_dev, seqs->cu_k_dev, seqs->cu_q_host,
+                                 seqs->cu_k_host, p.batch, p.topk, p.scale, p.tq,
                                  bp.n_chunks, bp.nkb_total, q, k, v, sel, out, lse, dout, dq,
                                  dk, dv, b, (hipStream_t)stream));
     return QSA_OK;

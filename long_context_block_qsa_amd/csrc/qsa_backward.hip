@@ -312,7 +312,7 @@ struct DqTile {
     uint32_t valid;  // bit 4u+i: key j0 + 16u + 4gr + i is attended
 };
 
-__global__ void __launch_bounds__(BDQ_NT)
+__global__ void __launch_bounds__(BDQ_NT) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(DqArgs a) {
     const int64_t item = __builtin_amdgcn_readfirstlane(
         (int)((int64_t)blockIdx.x * (BDQ_NT / WAVE) + threadIdx.x / WAVE));
@@ -402,22 +402,33 @@ bwd_dq_kernel(DqArgs a) {
             }
         }
     };
-    auto group_ids = [=](int grp) -> int32_t { return srow[min(64 * grp + l, a.topk - 1)]; };
+    // block ids of slots 64*grp .. 64*grp+63 (lane i: slot 64*grp + i) held in registers,
+    // so the loop's only loads are the tiles: per iteration the current tile's K^T rows,
+    // then the next tile (past the end: the row's own key). The load counter completes
+    // in order, so the waits for the current tile and its K^T leave the next tile's
+    // loads in flight.
+    int32_t ids[KMAX / WAVE];
+#pragma unroll
+    for (int j = 0; j < KMAX / WAVE; ++j) ids[j] = srow[min(64 * j + l, a.topk - 1)];
+    auto group_ids = [&](int grp) -> int32_t {
+        int32_t c = ids[0];
+#pragma unroll
+        for (int j = 1; j < KMAX / WAVE; ++j)
+            if (grp == j) c = ids[j];
+        return c;
+    };
 
     int cur_grp = 0;
     int32_t cur = group_ids(0);
-    DqTile nxt;
-    if (npos > 0) nxt = load_tile(0, cur);
+    DqTile nxt = load_tile(0, cur);
     for (int j0 = 0; j0 < npos; j0 += 32) {
         const DqTile T = nxt;
         const int32_t cur_t = cur;
         const int jn = j0 + 32;
-        if (jn < npos) {
-            if ((jn >> 8) != cur_grp) { cur_grp = jn >> 8; cur = group_ids(cur_grp); }
-            nxt = load_tile(jn, cur);
-        }
         u32x4 kp[8];
         load_kt(j0, cur_t, kp);
+        if ((jn >> 8) != cur_grp) { cur_grp = jn >> 8; cur = group_ids(cur_grp); }
+        nxt = load_tile(jn, cur);
         float ds[8];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -448,11 +459,7 @@ bwd_dq_kernel(DqArgs a) {
             const int q2 = mt >> 1;
             u32x4 ka;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const uint32_t x0 = kp[2 * kk][q2], x1 = kp[2 * kk + 1][q2];
-                ka[kk] = (mt & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u))
-                                  : ((x0 & 0xffffu) | (x1 << 16));
-            }
+            for (int kk = 0; kk < 4; ++kk) ka[kk] = bf16_pair(kp[2 * kk][q2], kp[2 * kk + 1][q2], mt & 1);
             acc[mt] = mfma_bf16_16x16x32(ka, dh, acc[mt]);
             acc[mt] = mfma_bf16_16x16x32(ka, dl, acc[mt]);
         }
@@ -491,18 +498,21 @@ struct DkvArgs {
     const uint16_t *q, *k, *v, *dout;
     const float *lse, *delta;
     const int32_t *off, *list;
+    const int32_t *mat, *tot;   // chunk prefixes of each list, list lengths
     float *dk, *dv;
-    int64_t nkb_total;
+    int64_t kb_lo, kb_hi;       // global key blocks of this launch
     int64_t nrows;
+    int win;                    // row window: chunks [win * BWD_WCH, (win + 1) * BWD_WCH)
+    int skip_multi;             // skip sequences with more than one window
 };
 
 struct DkvRow {
     u32x4 qb[4], ob[4];
-    float lse2, del;
+    float lse, del;
     int64_t t;
 };
 
-__global__ void __launch_bounds__(BDKV_NT)
+__global__ void __launch_bounds__(BDKV_NT) __attribute__((amdgpu_waves_per_eu(3)))
 bwd_dkv_kernel(DkvArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sq[BDKV_NT / WAVE][GQ * QPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t so[BDKV_NT / WAVE][GQ * QPITCH];
@@ -511,12 +521,21 @@ bwd_dkv_kernel(DkvArgs a) {
     const int w = threadIdx.x / WAVE;
     const int64_t item = __builtin_amdgcn_readfirstlane(
         (int)((int64_t)blockIdx.x * (BDKV_NT / WAVE) + w));
-    const int64_t gb = item >> 1;
+    const int64_t gb = a.kb_lo + (item >> 1);
     const int g = (int)(item & 1);
-    if (gb >= a.nkb_total) return;
+    if (gb >= a.kb_hi) return;
     const int sb = find_seq(a.batch, gb, [&](int i) { return (int64_t)a.tab[i].kb0; });
     const BwdSeq S = a.tab[sb];
+    if (a.skip_multi && S.nch > BWD_WCH) return;
     const int b = (int)(gb - S.kb0);
+    // the block's list entries from the rows of this window (lists are in row order)
+    auto prefix = [&](int c) -> int32_t {
+        return c >= S.nch ? a.tot[gb] : a.mat[S.m0 + (int64_t)c * S.nkb + b];
+    };
+    const int c0 = min(a.win * BWD_WCH, S.nch);
+    const int32_t base = a.off[gb];
+    const int lo = base + prefix(c0), hi = base + prefix(min(c0 + BWD_WCH, S.nch));
+    if (a.win > 0 && lo >= hi) return;
     const int64_t tok0 = (int64_t)S.k0 + BS * b;
     const int nkeys = min(BS, S.L - BS * b);
     const int l = lane_id(), gr = l >> 4, col = l & 15;
@@ -529,7 +548,6 @@ bwd_dkv_kernel(DkvArgs a) {
         va[m] = load16(a.v + (tok * HKV + g) * HD + 32 * m + 8 * gr);
         if (col >= nkeys) ka[m] = va[m] = u32x4{0u, 0u, 0u, 0u};
     }
-    const int lo = a.off[gb], hi = a.off[gb + 1];
     const int64_t tbase = (int64_t)S.L - S.nq - S.q0;
     const int head = g * GQ + min(col, GQ - 1);
 
@@ -545,7 +563,7 @@ bwd_dkv_kernel(DkvArgs a) {
             R.qb[m] = load16(a.q + (row * HQ + head) * HD + 32 * m + 8 * gr);
             R.ob[m] = load16(a.dout + (row * HQ + head) * HD + 32 * m + 8 * gr);
         }
-        R.lse2 = a.lse[row * HQ + head] * 1.4426950408889634f;
+        R.lse = a.lse[row * HQ + head];
         R.del = a.delta[row * HQ + head];
         R.t = tbase + row;
         return R;
@@ -553,19 +571,7 @@ bwd_dkv_kernel(DkvArgs a) {
 
     uint16_t *wq = sq[w], *wo = so[w];
     float *wp = sp[w], *wds = sds[w];
-    int32_t rows = 0;  // list entries lo + 64k .. +63, lane i holds entry i
-    DkvRow nxt;
-    if (lo < hi) {
-        rows = a.list[min(lo + l, hi - 1)];
-        nxt = load_row(__shfl(rows, 0));
-    }
-    for (int e = lo; e < hi; ++e) {
-        const DkvRow R = nxt;
-        const int en = e + 1;
-        if (en < hi) {
-            if (((en - lo) & 63) == 0) rows = a.list[min(en + l, hi - 1)];
-            nxt = load_row(__shfl(rows, (en - lo) & 63));
-        }
+    auto process = [&](const DkvRow &R) {
         f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -574,11 +580,12 @@ bwd_dkv_kernel(DkvArgs a) {
         }
         // lanes (0, col < 12): keys i = 0..3 of head col
         if (gr == 0 && col < GQ) {
+            const float lse2 = R.lse * 1.4426950408889634f;
             f32x4 p4, ds4;
 #pragma unroll
             for (int i = 0; i < BS; ++i) {
                 const bool ok = BS * b + i <= R.t;
-                const float p = ok ? exp2f(s4[i] * a.scale_log2 - R.lse2) : 0.f;
+                const float p = ok ? exp2f(s4[i] * a.scale_log2 - lse2) : 0.f;
                 p4[i] = p;
                 ds4[i] = p * (d4[i] - R.del);
             }
@@ -610,19 +617,51 @@ bwd_dkv_kernel(DkvArgs a) {
             }
         }
         wave_lds_sync();
+    };
+    // Two row buffers used in turn (no register copies); each half-step loads the row
+    // id two entries ahead (one uniform dword) and the next row's operands before it
+    // processes the current row, so the waits leave the next row's loads in flight.
+    // Loads past the end repeat the last entry's row.
+    if (lo < hi) {
+        auto row_id = [&](int e) -> int32_t {
+            return __builtin_amdgcn_readfirstlane(a.list[min(e, hi - 1)]);
+        };
+        int32_t id1 = row_id(lo + 1);
+        DkvRow A = load_row(row_id(lo));
+        for (int e = lo; e < hi; e += 2) {
+            const int32_t id2 = row_id(e + 2);
+            const DkvRow B = load_row(id1);
+            __builtin_amdgcn_sched_barrier(0);   // issue B's loads before waiting for A
+            process(A);
+            if (e + 1 >= hi) break;
+            id1 = row_id(e + 3);
+            A = load_row(id2);
+            __builtin_amdgcn_sched_barrier(0);
+            process(B);
+        }
     }
+    // window 0 writes the block's gradients, later windows (later launches) add to them
 #pragma unroll
     for (int i = 0; i < BS; ++i) {
         if (i < nkeys) {
             const int64_t o = ((tok0 + i) * HKV + g) * HD + 2 * l;
-            *reinterpret_cast<float2 *>(a.dk + o) = float2{dk[i][0] * a.scale, dk[i][1] * a.scale};
-            *reinterpret_cast<float2 *>(a.dv + o) = float2{dv[i][0], dv[i][1]};
+            float2 k2 = float2{dk[i][0] * a.scale, dk[i][1] * a.scale};
+            float2 v2 = float2{dv[i][0], dv[i][1]};
+            if (a.win > 0) {
+                const float2 pk = *reinterpret_cast<const float2 *>(a.dk + o);
+                const float2 pv = *reinterpret_cast<const float2 *>(a.dv + o);
+                k2 = float2{pk.x + k2.x, pk.y + k2.y};
+                v2 = float2{pv.x + v2.x, pv.y + v2.y};
+            }
+            *reinterpret_cast<float2 *>(a.dk + o) = k2;
+            *reinterpret_cast<float2 *>(a.dv + o) = v2;
         }
     }
 }
 
 // =============================================================== launcher
-hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, int batch, int topk,
+hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, const int32_t *cu_q_host,
+                           const int32_t *cu_k_host, int batch, int topk,
                            float scale, int64_t n_rows, int64_t n_chunks, int64_t nkb_total,
                            const uint16_t *q, const uint16_t *k, const uint16_t *v,
                            const int32_t *sel, const float *out, const float *lse,
@@ -678,12 +717,28 @@ hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, int batch, 
         a.tab = bb.seq; a.batch = batch;
         a.scale = scale; a.scale_log2 = scale * 1.4426950408889634f;
         a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = bb.delta;
-        a.off = bb.off; a.list = bb.list; a.dk = dk; a.dv = dv; a.nkb_total = nkb_total;
-        a.nrows = n_rows;
-        const int64_t wg = (nkb_total * HKV + BDKV_NT / WAVE - 1) / (BDKV_NT / WAVE);
-        trace_before(13, st);
-        hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)wg), dim3(BDKV_NT), 0, st, a);
-        if ((e = trace_after(st, hipGetLastError())) != hipSuccess) return e;
+        a.off = bb.off; a.list = bb.list; a.mat = bb.mat; a.tot = bb.tot;
+        a.dk = dk; a.dv = dv; a.nrows = n_rows;
+        auto launch = [&](int64_t lo, int64_t hi, int win, int skip_multi) -> hipError_t {
+            a.kb_lo = lo; a.kb_hi = hi; a.win = win; a.skip_multi = skip_multi;
+            const int64_t wg = ((hi - lo) * HKV + BDKV_NT / WAVE - 1) / (BDKV_NT / WAVE);
+            trace_before(13, st);
+            hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)wg), dim3(BDKV_NT), 0, st, a);
+            return trace_after(st, hipGetLastError());
+        };
+        // one launch for every sequence with a single row window, then one launch per
+        // window of each longer sequence: the rows a launch gathers stay cache-resident
+        if ((e = launch(0, nkb_total, 0, 1)) != hipSuccess) return e;
+        int64_t kb0 = 0;
+        for (int s = 0; s < batch; ++s) {
+            const int64_t L = (int64_t)cu_k_host[s + 1] - cu_k_host[s];
+            const int64_t nq = (int64_t)cu_q_host[s + 1] - cu_q_host[s];
+            const int64_t nkb = (L + BS - 1) / BS, nch = (nq + BWD_CH - 1) / BWD_CH;
+            if (nch > BWD_WCH)
+                for (int w = 0; w * (int64_t)BWD_WCH < nch; ++w)
+                    if ((e = launch(kb0, kb0 + nkb, w, 0)) != hipSuccess) return e;
+            kb0 += nkb;
+        }
     }
     return hipSuccess;
 }

@@ -45,6 +45,7 @@ struct SeqInfo {
 // rows are cut into chunks of BWD_CH consecutive rows of one sequence.
 constexpr int BWD_CH = 256;
 constexpr int BWD_CAP = 16384;  // key blocks counted per LDS pass of the index kernels
+constexpr int BWD_WCH = 32;     // row chunks per window of the dK/dV kernel (8192 rows)
 struct BwdSeq {
     int32_t q0, nq, k0, L;
     int32_t kb0;   // first key block (global numbering over all sequences)
@@ -783,6 +784,12 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
 __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// The low (odd = false) or high (odd = true) bf16 halves of x0 and x1 as one pair
+// {x0 half, x1 half}: one byte permute.
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t x0, uint32_t x1, bool odd) {
+    return __builtin_amdgcn_perm(x1, x0, odd ? 0x07060302u : 0x05040100u);
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p) {

@@ -904,20 +904,25 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
             }
         }
         mx = wave_max_xor_16_32(mx);
-        const float m_new = fmaxf(m_run, mx);
-        if (m_new == -INFINITY) continue;  // no attended key yet (uniform over the wave)
-        const float alpha = exp2f(m_run - m_new);
+        if (mx == -INFINITY) continue;  // no attended key in the tile (uniform over the wave)
+        // the softmax reference m_run (with acc and l_run) moves only when some head's
+        // tile maximum exceeds it by more than 2^8, so most tiles skip rescaling the
+        // accumulators; every probability exp2(z - m_run) stays at most 2^8
+        if (__ballot(mx > m_run + 8.f)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) acc[mt] *= alpha;
+            m_run = m_new;
+        }
         float p[8], rs = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            p[e] = z[e] == -INFINITY ? 0.f : exp2f(z[e] - m_new);
+            p[e] = z[e] == -INFINITY ? 0.f : exp2f(z[e] - m_run);
             rs += p[e];
         }
-        rs = wave_sum_xor_16_32(rs);
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) acc[mt] *= alpha;
+        l_run += wave_sum_xor_16_32(rs);
 
         // FP8: the V scale of each key multiplies its probability (the denominator l
         // keeps the unscaled ones)
@@ -949,8 +954,7 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const uint32_t x0 = vb[2 * kk][q2], x1 = vb[2 * kk + 1][q2];
-                va[kk] = (mt & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u))
-                                  : ((x0 & 0xffffu) | (x1 << 16));
+                va[kk] = bf16_pair(x0, x1, mt & 1);
             }
             acc[mt] = mfma_bf16_16x16x32(va, ph, acc[mt]);
             acc[mt] = mfma_bf16_16x16x32(va, pl, acc[mt]);

@@ -53,7 +53,8 @@ struct BwdBuffers {
     int32_t *mat;     // count matrices of all sequences
     int32_t *list;    // block -> rows lists
 };
-hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, int batch, int topk,
+hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, const int32_t *cu_q_host,
+                           const int32_t *cu_k_host, int batch, int topk,
                            float scale, int64_t n_rows, int64_t n_chunks, int64_t nkb_total,
                            const uint16_t *q, const uint16_t *k, const uint16_t *v,
                            const int32_t *sel, const float *out, const float *lse,

@@ -99,6 +99,14 @@ def test_backward_two_lds_passes():
     _check("bwd-70001", BwdProblem(p, 512))
 
 
+def test_backward_row_windows():
+    """More than 8192 query rows in a sequence: dK/dV are summed over row windows in
+    successive launches (the second window adds to the first)."""
+    _banner("backward 9000-row prefill, two row windows")
+    p = gen.make_problem([9000, 50], seed=540)
+    _check("bwd-9000", BwdProblem(p, 8))
+
+
 def test_backward_is_deterministic():
     """Two calls give bit-identical gradients (no atomics in the accumulation)."""
     _banner("backward determinism")
