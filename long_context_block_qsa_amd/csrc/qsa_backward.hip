@@ -292,6 +292,8 @@ bwd_fill_kernel(const BwdSeq *__restrict__ tab, int batch, const int32_t *__rest
 //   head, dims 32m + 8gr .. +7), P = exp(scale S - lse), dS = P (dP - D);
 //   dQ^T [128 dims x 16 heads] += K^T dS^T, dS^T split into bf16 hi + lo (as P in the
 //   forward) and K^T rows permuted so that row r of dim tile mt is dim 8r + mt.
+// K and V are loaded as whole rows (16 lanes per row); the K rows are the K^T operand as
+// loaded and, like V, reach the S^T / dP^T operand layout through a per-wave LDS tile.
 constexpr int BDQ_NT = 256;
 
 struct DqArgs {
@@ -306,14 +308,21 @@ struct DqArgs {
     int64_t nrows;
 };
 
+// K and V rows of the lane's 8 dS keys (keys 4gr..4gr+3 and 16+4gr..16+4gr+3 of the tile),
+// dims 8col .. 8col+7: whole 256-byte rows per 16 lanes. K in this layout is the A operand
+// of dQ^T = K^T dS^T; K and V also pass through LDS into the layout of S^T and dP^T.
 struct DqTile {
-    u32x4 kr[2][4];  // K rows of keys j0 + 16u + col, dims 32m + 8gr
-    u32x4 vr[2][4];  // V rows, same keys and dims
+    u32x4 kt[8];
+    u32x4 vt[8];
     uint32_t valid;  // bit 4u+i: key j0 + 16u + 4gr + i is attended
 };
+constexpr int DQ_PITCH = 2 * HD + 16;          // LDS bytes per key row
+constexpr int DQ_LDS = 2 * 32 * DQ_PITCH;      // a wave's K and V tiles
 
 __global__ void __launch_bounds__(BDQ_NT) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(DqArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[(BDQ_NT / WAVE) * DQ_LDS];
+    uint8_t *klds = lds + (threadIdx.x / WAVE) * DQ_LDS, *vlds = klds + 32 * DQ_PITCH;
     const int64_t item = __builtin_amdgcn_readfirstlane(
         (int)((int64_t)blockIdx.x * (BDQ_NT / WAVE) + threadIdx.x / WAVE));
     const int64_t row = item >> 1;
@@ -361,35 +370,6 @@ bwd_dq_kernel(DqArgs a) {
         T.valid = 0;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int p = j0 + 16 * u + col;
-            bool ok;
-            int64_t tok = slot_token0(p >> 2, cur, ok) + (p & 3);
-            ok = ok && p < npos && ((p >> 2) < nsel || (p & 3) < ntail);
-            if (!ok) tok = safe_tok;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                T.kr[u][m] = load16(kbase + tok * (HKV * HD) + 32 * m + 8 * gr);
-                T.vr[u][m] = load16(vbase + tok * (HKV * HD) + 32 * m + 8 * gr);
-            }
-        }
-        // validity of the lane's 8 output keys j0 + 16u + 4gr + i (slot (j0>>2) + 4u + gr)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int sl = (j0 >> 2) + 4 * u + gr;
-            bool okb;
-            (void)slot_token0(sl, cur, okb);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int p = 4 * sl + i;
-                if (okb && p < npos && (sl < nsel || i < ntail)) T.valid |= 1u << (4 * u + i);
-            }
-        }
-        return T;
-    };
-    // K rows of the lane's 8 dS keys (as the forward's V^T operand), dims 8col .. +7
-    auto load_kt = [&](int j0, int32_t cur, u32x4 *kp) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
             const int sl = (j0 >> 2) + 4 * u + gr;
             bool okb;
             const int64_t tok0 = slot_token0(sl, cur, okb);
@@ -398,9 +378,12 @@ bwd_dq_kernel(DqArgs a) {
                 const int p = 4 * sl + i;
                 const bool ok = okb && p < npos && (sl < nsel || i < ntail);
                 const int64_t tok = ok ? tok0 + i : safe_tok;
-                kp[4 * u + i] = load16(kbase + tok * (HKV * HD) + 8 * col);
+                T.kt[4 * u + i] = load16(kbase + tok * (HKV * HD) + 8 * col);
+                T.vt[4 * u + i] = load16(vbase + tok * (HKV * HD) + 8 * col);
+                if (ok) T.valid |= 1u << (4 * u + i);
             }
         }
+        return T;
     };
     // block ids of slots 64*grp .. 64*grp+63 (lane i: slot 64*grp + i) held in registers,
     // so the loop's only loads are the tiles: per iteration the current tile's K^T rows,
@@ -423,20 +406,27 @@ bwd_dq_kernel(DqArgs a) {
     DqTile nxt = load_tile(0, cur);
     for (int j0 = 0; j0 < npos; j0 += 32) {
         const DqTile T = nxt;
-        const int32_t cur_t = cur;
         const int jn = j0 + 32;
-        u32x4 kp[8];
-        load_kt(j0, cur_t, kp);
         if ((jn >> 8) != cur_grp) { cur_grp = jn >> 8; cur = group_ids(cur_grp); }
         nxt = load_tile(jn, cur);
+        // K and V rows into the S^T / dP^T A layout (lane: key 16u + col, dims 32m + 8gr)
+        wave_lds_sync();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int off = (16 * (e >> 2) + 4 * gr + (e & 3)) * DQ_PITCH + 16 * col;
+            *reinterpret_cast<u32x4 *>(klds + off) = T.kt[e];
+            *reinterpret_cast<u32x4 *>(vlds + off) = T.vt[e];
+        }
+        wave_lds_sync();
         float ds[8];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                s4 = mfma_bf16_16x16x32(T.kr[u][m], qb[m], s4);
-                d4 = mfma_bf16_16x16x32(T.vr[u][m], ob[m], d4);
+                const int off = (16 * u + col) * DQ_PITCH + 2 * (32 * m + 8 * gr);
+                s4 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4 *>(klds + off), qb[m], s4);
+                d4 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4 *>(vlds + off), ob[m], d4);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -459,7 +449,8 @@ bwd_dq_kernel(DqArgs a) {
             const int q2 = mt >> 1;
             u32x4 ka;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) ka[kk] = bf16_pair(kp[2 * kk][q2], kp[2 * kk + 1][q2], mt & 1);
+            for (int kk = 0; kk < 4; ++kk)
+                ka[kk] = bf16_pair(T.kt[2 * kk][q2], T.kt[2 * kk + 1][q2], mt & 1);
             acc[mt] = mfma_bf16_16x16x32(ka, dh, acc[mt]);
             acc[mt] = mfma_bf16_16x16x32(ka, dl, acc[mt]);
         }

@@ -729,6 +729,8 @@ select_dec_kernel(SelectArgs a, DecodeTables d) {
 //   hi + lo parts (2 MFMAs) to keep ~16 bits; V^T rows are permuted so row r of
 //   dim-tile mt is dim 8r + mt, which lets each lane load 16 contiguous bytes of V per
 //   key.
+// K and V are loaded as whole rows (16 lanes per 256-byte row, the access the address
+// units coalesce); K then passes through a per-wave LDS tile into the MFMA layout.
 // Block ids of the row are held in registers (lane i: slot 64j + i) and broadcast with
 // shuffles, and each tile's K/V loads are issued one tile ahead of its MFMAs.
 // nsplit = 1: final output. nsplit > 1: unnormalised partial (acc, m, l) per split.
@@ -754,23 +756,29 @@ __device__ __forceinline__ int64_t part_stride_row(int nsplit) {
     return (int64_t)nsplit * HQ * PREC;
 }
 
+// K and V rows of the lane's 8 P keys (keys 4gr..4gr+3 and 16+4gr..16+4gr+3 of the tile),
+// dims 8col .. 8col+7: each load instruction reads whole 256-byte rows, one per 16 lanes.
 struct KVTile {
-    u32x4 kr[2][4];  // K rows of keys j0 + 16u + col, dims 32m + 8gr
-    u32x4 vr[8];     // V rows of the lane's 8 P keys, dims 8col .. 8col+7
+    u32x4 kt[8];
+    u32x4 vr[8];
     uint32_t valid;  // bit 4u+i: key j0 + 16u + 4gr + i is attended
 };
 // The same tile from the FP8 KV cache: 8 E4M3 bytes per load, and the K and V scales
 // of the lane's 8 P keys (the logit and probability of key e are scaled by them).
 struct KVTile8 {
-    uint2 kr[2][4];
+    uint2 kt[8];
     uint2 vr[8];
     float ks[8], vs[8];
     uint32_t valid;
 };
+// LDS row pitch (bytes) of the per-wave K tile that turns the row-per-16-lanes loads into
+// the MFMA operand layout (16 bytes of padding spread the rows over the banks)
+template <bool FP8> constexpr int kt_pitch() { return FP8 ? HD + 16 : 2 * HD + 16; }
+constexpr int KT_LDS_BYTES = 32 * (2 * HD + 16);   // one wave's tile (the larger, bf16)
 
 template <bool FP8>
 __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv, int64_t row,
-                                            int g, int sp) {
+                                            int g, int sp, uint8_t *klds) {
     using Tile = typename std::conditional<FP8, KVTile8, KVTile>::type;
     const int64_t t = rv.t;
     const int64_t nv = nvis_of(t);
@@ -826,24 +834,6 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
         Tile T;
         T.valid = 0;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int p = j0 + 16 * u + col;
-            bool ok;
-            int64_t tok = slot_token0(p >> 2, cur, ok) + (p & 3);
-            ok = ok && p < p_hi && ((p >> 2) < nsel || (p & 3) < ntail);
-            if (!ok) tok = safe_tok;
-            if constexpr (FP8) {
-                const uint8_t *kp = a.k8 + tok * (HKV * HD) + g * HD + 8 * gr;
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    T.kr[u][m] = *reinterpret_cast<const uint2 *>(kp + 32 * m);
-            } else {
-                const uint16_t *kp = kbase + tok * (HKV * HD) + 8 * gr;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) T.kr[u][m] = load16(kp + 32 * m);
-            }
-        }
-#pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int sl = (j0 >> 2) + 4 * h + gr;
             bool okb;
@@ -854,11 +844,14 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
                 const bool ok = okb && p < p_hi && (sl < nsel || i < ntail);
                 const int64_t tok = ok ? tok0 + i : safe_tok;
                 if constexpr (FP8) {
+                    T.kt[4 * h + i] = *reinterpret_cast<const uint2 *>(
+                        a.k8 + tok * (HKV * HD) + g * HD + 8 * col);
                     T.vr[4 * h + i] = *reinterpret_cast<const uint2 *>(
                         a.v8 + tok * (HKV * HD) + g * HD + 8 * col);
                     T.ks[4 * h + i] = a.k_scale[tok * HKV + g];
                     T.vs[4 * h + i] = a.v_scale[tok * HKV + g];
                 } else {
+                    T.kt[4 * h + i] = load16(kbase + tok * (HKV * HD) + 8 * col);
                     T.vr[4 * h + i] = load16(vbase + tok * (HKV * HD) + 8 * col);
                 }
                 if (ok) T.valid |= 1u << (4 * h + i);
@@ -886,13 +879,28 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
         // ---- logits S^T for keys j0 .. j0+31 (lane: keys j0+16u+4gr+i, head col)
         float z[8];
         float mx = -INFINITY;
+        // the K rows go through this wave's LDS tile into the MFMA A layout (lane: key
+        // 16u + col, dims 32m + 8gr)
+        constexpr int KP = kt_pitch<FP8>();
+        constexpr int EB = FP8 ? 1 : 2;   // bytes per element
+        wave_lds_sync();   // the previous tile's reads are done
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint8_t *dst = klds + (16 * (e >> 2) + 4 * gr + (e & 3)) * KP + 8 * EB * col;
+            if constexpr (FP8) *reinterpret_cast<uint2 *>(dst) = T.kt[e];
+            else *reinterpret_cast<u32x4 *>(dst) = T.kt[e];
+        }
+        wave_lds_sync();
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                if constexpr (FP8) c4 = mfma_bf16_16x16x32(e4m3x8_to_bf16x8(T.kr[u][m]), qb[m], c4);
-                else c4 = mfma_bf16_16x16x32(T.kr[u][m], qb[m], c4);
+                const uint8_t *src = klds + (16 * u + col) * KP + (32 * m + 8 * gr) * EB;
+                if constexpr (FP8)
+                    c4 = mfma_bf16_16x16x32(e4m3x8_to_bf16x8(*reinterpret_cast<const uint2 *>(src)),
+                                            qb[m], c4);
+                else c4 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4 *>(src), qb[m], c4);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1005,10 +1013,12 @@ __device__ __forceinline__ bool attend_item(const AttnArgs &a, int64_t &row, int
 template <bool FP8>
 __global__ void __launch_bounds__(ATT_NT)
 attend_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t klds[(ATT_NT / WAVE) * KT_LDS_BYTES];
     int64_t row;
     int g, sp;
     if (!attend_item(a, row, g, sp)) return;
-    attend_body<FP8>(a, tab_row(a.tab, a.batch, a.topk, row), row, g, sp);
+    attend_body<FP8>(a, tab_row(a.tab, a.batch, a.topk, row), row, g, sp,
+                     klds + (threadIdx.x / WAVE) * KT_LDS_BYTES);
 }
 
 template <bool FP8>
@@ -1017,9 +1027,10 @@ attend_dec_kernel(AttnArgs a, DecodeTables d) {
     int64_t row;
     int g, sp;
     if (!attend_item(a, row, g, sp)) return;
+    __shared__ __attribute__((aligned(16))) uint8_t klds[(ATT_NT / WAVE) * KT_LDS_BYTES];
     const DecRow r = d.row[row];
     const RowView rv = {r.k0, r.t, r.blk0, r.slot};
-    attend_body<FP8>(a, rv, row, g, sp);
+    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES);
 }
 
 // =============================================================== combine
