@@ -279,7 +279,6 @@ struct SelectArgs {
     const int32_t *cand_idx;
     int ch, max_chunks;  // ch = 0: no candidates
     int32_t *sel;
-    int64_t lds_cap;     // keys that fit the dynamic LDS
     int dense_only;      // only rows with at most topk visible blocks
 };
 
@@ -377,11 +376,11 @@ __device__ __forceinline__ bool merge_candidates(const uint32_t *ck, const int32
 }
 
 // One workgroup selects one query row from its full key row: rows within the budget
-// keep blocks 0..nvis-1, others get an exact radix select (keys staged in dynamic LDS
-// when they fit).
+// keep blocks 0..nvis-1, others get an exact radix select over the keys in global memory
+// (each pass re-reads them from L2; staging up to 64 KB of keys per row in LDS held
+// occupancy to two workgroups per CU and was a third slower).
 __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView rv, int64_t row,
-                                            uint32_t *dyn, uint32_t *hist, int32_t *scan_sh,
-                                            uint32_t *found) {
+                                            uint32_t *hist, int32_t *scan_sh, uint32_t *found) {
     const int64_t nv = nvis_of(rv.t);
     int32_t *out = a.sel + row * a.topk;
     const int tid = threadIdx.x;
@@ -390,25 +389,8 @@ __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView r
         return;
     }
     if (a.dense_only) return;
-    const uint32_t *rk = a.keys + rv.slot;
-    if (nv <= a.lds_cap) {
-        for (int64_t i0 = tid; i0 < nv; i0 += 8 * SEL_NT) {
-            uint32_t v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = rk[min<int64_t>(i0 + (int64_t)e * SEL_NT, nv - 1)];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t i = i0 + (int64_t)e * SEL_NT;
-                if (i < nv) dyn[i] = v[e];
-            }
-        }
-        __syncthreads();
-        select_keys<16>((const uint32_t *)dyn, (const int32_t *)nullptr, nv, a.topk, out, hist,
-                        scan_sh, found, nullptr, 1, 0);
-    } else {
-        select_keys<16>(rk, (const int32_t *)nullptr, nv, a.topk, out, hist, scan_sh, found,
-                        nullptr, 1, 0);
-    }
+    select_keys<16>(a.keys + rv.slot, (const int32_t *)nullptr, nv, a.topk, out, hist, scan_sh,
+                    found, nullptr, 1, 0);
 }
 
 struct LocalArgs {
@@ -695,24 +677,22 @@ score_local_kernel(LocalArgs a, DecodeTables d) {
 
 __global__ void __launch_bounds__(SEL_NT)
 select_kernel(SelectArgs a) {
-    extern __shared__ uint32_t dyn[];   // lds_cap words
-    __shared__ uint32_t hist[kHistBins];  // histograms; then per-chunk kept counts
+    __shared__ uint32_t hist[kHistBins];
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
     __shared__ uint32_t found[2];
     const int64_t row = blockIdx.x;
-    select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, dyn, hist, scan_sh, found);
+    select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, hist, scan_sh, found);
 }
 
 __global__ void __launch_bounds__(SEL_NT)
 select_dec_kernel(SelectArgs a, DecodeTables d) {
-    extern __shared__ uint32_t dyn[];
     __shared__ uint32_t hist[kHistBins];
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
     __shared__ uint32_t found[2];
     const int64_t row = blockIdx.x;
     const DecRow r = d.row[row];
     const RowView rv = {r.k0, r.t, r.blk0, r.slot};
-    select_body(a, rv, row, dyn, hist, scan_sh, found);
+    select_body(a, rv, row, hist, scan_sh, found);
 }
 
 // =============================================================== attend
@@ -1179,23 +1159,6 @@ hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
     return trace_after(st, hipGetLastError());
 }
 
-int64_t select_lds_cap_keys() {
-    static int64_t cap = -1;
-    if (cap < 0) {
-        int dev = 0, limit = 65536;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&limit, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-                hipSuccess)
-            limit = 65536;
-        // static LDS of select_kernel: histogram + small
-        const int64_t stat = kHistBins * 4 + 128;
-        int64_t c = (limit - stat) / 4;
-        c = c > 16384 ? 16384 : c;
-        cap = c < 0 ? 0 : c & ~(int64_t)255;
-    }
-    return cap;
-}
-
 hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          const uint32_t *keys, const uint32_t *cand_key, const int32_t *cand_idx,
                          int ch, int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
@@ -1205,21 +1168,12 @@ hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, i
     a.tab = tab; a.batch = batch; a.topk = topk; a.keys = keys;
     a.cand_key = cand_key; a.cand_idx = cand_idx; a.ch = ch; a.max_chunks = max_chunks;
     a.sel = sel; a.dense_only = dense_only;
-    const int64_t cap = dense_only ? 0 : select_lds_cap_keys();
-    int64_t want = max_nvis;
-    if (ch > 0) want = want > 2 * (int64_t)max_chunks * KP ? want : 2 * (int64_t)max_chunks * KP;
-    a.lds_cap = want < cap ? want : cap;
-    const size_t shmem = (size_t)a.lds_cap * 4;
-    const void *fn = d ? (const void *)select_dec_kernel : (const void *)select_kernel;
-    if (shmem > 65536) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-        if (e != hipSuccess) return e;
-    }
+    (void)max_nvis;
     trace_before(3, st);
     if (d)
-        hipLaunchKernelGGL(select_dec_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), shmem, st, a, *d);
+        hipLaunchKernelGGL(select_dec_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), 0, st, a, *d);
     else
-        hipLaunchKernelGGL(select_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), shmem, st, a);
+        hipLaunchKernelGGL(select_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), 0, st, a);
     return trace_after(st, hipGetLastError());
 }
 
