@@ -428,8 +428,14 @@ def run_cpu_baseline(args, d, oracle):
         el = time.perf_counter() - t0
         if el >= args.cpu_seconds or reps >= 50:
             break
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(reps * p.n_q / el, 3), "unit": "query-tokens/s", "cores": threads,
-            "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{reps} decode step(s) of 16 rows at 262,144 context (score + select + "
                       f"attend over the prebuilt compressed cache), {el:.1f} s wall"}
 
