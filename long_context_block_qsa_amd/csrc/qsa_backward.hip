@@ -474,10 +474,15 @@ bwd_dq_kernel(DqArgs a) {
 // =============================================================== bwd_dkv
 // One wave per (key block, KV head g), over the rows of the block's list in order. Per
 // row: S^T, dP^T [4 keys (of 16) x 12 heads (of 16)] by MFMA with the block's K and V
-// rows as the A operand (loaded once); P and dS go through LDS as per-(head, key)
-// values, the row's Q and dO through LDS as [head][dim]; then each lane accumulates
-// dK, dV of the 4 keys at dims 2l, 2l+1 with fp32 FMAs over the 12 heads. The next
-// row's Q, dO, lse and D are loaded while the current one is processed.
+// rows as the A operand (loaded once). The row's Q and dO are loaded as whole head rows
+// (16 lanes per 256-byte row, 3 loads each for the 12 heads) into LDS as [head][dim],
+// from where the MFMA B operands and the per-head values below are read; P and dS go
+// through LDS as per-(head, key) values. dK and dV of the 4 keys at
+// dims 2l, 2l+1 (register i: key i) are accumulated over the 12 heads with the fp32
+// 4x4x1 MFMA (16 blocks of 4 x 4): lane l of block l/4 multiplies the value of key i
+// held by lane 4(l/4) + i (dS or P, every block the same) by its own Q or dO element,
+// one fp32 product per output as a VALU FMA would form it, at twice the VALU rate.
+// The next row's Q, dO, lse and D are loaded while the current one is processed.
 constexpr int BDKV_NT = 256;
 constexpr int QPITCH = HD + 8;  // bf16 per LDS head row (272 bytes: 16-byte rows land on
                                 // distinct banks)
@@ -498,7 +503,7 @@ struct DkvArgs {
 };
 
 struct DkvRow {
-    u32x4 qb[4], ob[4];
+    u32x4 qr[3], orw[3];   // heads 4j + l/16 of the group, dims 8(l%16) .. +7
     float lse, del;
     int64_t t;
 };
@@ -542,17 +547,17 @@ bwd_dkv_kernel(DkvArgs a) {
     const int64_t tbase = (int64_t)S.L - S.nq - S.q0;
     const int head = g * GQ + min(col, GQ - 1);
 
-    float dk[BS][2], dv[BS][2];
-#pragma unroll
-    for (int i = 0; i < BS; ++i) dk[i][0] = dk[i][1] = dv[i][0] = dv[i][1] = 0.f;
+    // dk0[i], dk1[i]: dK of key i at dims 2l, 2l+1 (likewise dV)
+    f32x4 dk0 = {0.f, 0.f, 0.f, 0.f}, dk1 = dk0, dv0 = dk0, dv1 = dk0;
 
     auto load_row = [&](int64_t row) -> DkvRow {
         row = min<int64_t>(max<int64_t>(row, 0), a.nrows - 1);  // list entries are rows
         DkvRow R;
+        const int64_t rb = (row * HQ + g * GQ + (l >> 4)) * HD + 8 * (l & 15);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            R.qb[m] = load16(a.q + (row * HQ + head) * HD + 32 * m + 8 * gr);
-            R.ob[m] = load16(a.dout + (row * HQ + head) * HD + 32 * m + 8 * gr);
+        for (int j = 0; j < 3; ++j) {
+            R.qr[j] = load16(a.q + rb + (int64_t)4 * j * HD);
+            R.orw[j] = load16(a.dout + rb + (int64_t)4 * j * HD);
         }
         R.lse = a.lse[row * HQ + head];
         R.del = a.delta[row * HQ + head];
@@ -562,12 +567,22 @@ bwd_dkv_kernel(DkvArgs a) {
 
     uint16_t *wq = sq[w], *wo = so[w];
     float *wp = sp[w], *wds = sds[w];
+    const int hc = min(col, GQ - 1);   // head of the lane's S^T / dP^T column
     auto process = [&](const DkvRow &R) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int o = (4 * j + (l >> 4)) * QPITCH + 8 * (l & 15);
+            *reinterpret_cast<u32x4 *>(wq + o) = R.qr[j];
+            *reinterpret_cast<u32x4 *>(wo + o) = R.orw[j];
+        }
+        wave_lds_sync();
         f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            s4 = mfma_bf16_16x16x32(ka[m], R.qb[m], s4);
-            d4 = mfma_bf16_16x16x32(va[m], R.ob[m], d4);
+            const u32x4 qb = *reinterpret_cast<const u32x4 *>(wq + hc * QPITCH + 32 * m + 8 * gr);
+            const u32x4 ob = *reinterpret_cast<const u32x4 *>(wo + hc * QPITCH + 32 * m + 8 * gr);
+            s4 = mfma_bf16_16x16x32(ka[m], qb, s4);
+            d4 = mfma_bf16_16x16x32(va[m], ob, d4);
         }
         // lanes (0, col < 12): keys i = 0..3 of head col
         if (gr == 0 && col < GQ) {
@@ -583,29 +598,17 @@ bwd_dkv_kernel(DkvArgs a) {
             *reinterpret_cast<f32x4 *>(wp + 4 * col) = p4;
             *reinterpret_cast<f32x4 *>(wds + 4 * col) = ds4;
         }
-        if (col < GQ) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                *reinterpret_cast<u32x4 *>(wq + col * QPITCH + 32 * m + 8 * gr) = R.qb[m];
-                *reinterpret_cast<u32x4 *>(wo + col * QPITCH + 32 * m + 8 * gr) = R.ob[m];
-            }
-        }
         wave_lds_sync();
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
             const uint32_t qq = *reinterpret_cast<const uint32_t *>(wq + h * QPITCH + 2 * l);
             const uint32_t oo = *reinterpret_cast<const uint32_t *>(wo + h * QPITCH + 2 * l);
-            const f32x4 p4 = *reinterpret_cast<const f32x4 *>(wp + 4 * h);
-            const f32x4 ds4 = *reinterpret_cast<const f32x4 *>(wds + 4 * h);
-            const float q0 = bf16_lo(qq), q1 = bf16_hi(qq);
-            const float o0 = bf16_lo(oo), o1 = bf16_hi(oo);
-#pragma unroll
-            for (int i = 0; i < BS; ++i) {
-                dk[i][0] += ds4[i] * q0;
-                dk[i][1] += ds4[i] * q1;
-                dv[i][0] += p4[i] * o0;
-                dv[i][1] += p4[i] * o1;
-            }
+            const float pa = wp[4 * h + (l & 3)];    // P of key l % 4, head h
+            const float da = wds[4 * h + (l & 3)];   // dS of key l % 4, head h
+            dk0 = mfma_f32_4x4x1(da, bf16_lo(qq), dk0);
+            dk1 = mfma_f32_4x4x1(da, bf16_hi(qq), dk1);
+            dv0 = mfma_f32_4x4x1(pa, bf16_lo(oo), dv0);
+            dv1 = mfma_f32_4x4x1(pa, bf16_hi(oo), dv1);
         }
         wave_lds_sync();
     };
@@ -636,8 +639,8 @@ bwd_dkv_kernel(DkvArgs a) {
     for (int i = 0; i < BS; ++i) {
         if (i < nkeys) {
             const int64_t o = ((tok0 + i) * HKV + g) * HD + 2 * l;
-            float2 k2 = float2{dk[i][0] * a.scale, dk[i][1] * a.scale};
-            float2 v2 = float2{dv[i][0], dv[i][1]};
+            float2 k2 = float2{dk0[i] * a.scale, dk1[i] * a.scale};
+            float2 v2 = float2{dv0[i], dv1[i]};
             if (a.win > 0) {
                 const float2 pk = *reinterpret_cast<const float2 *>(a.dk + o);
                 const float2 pv = *reinterpret_cast<const float2 *>(a.dv + o);

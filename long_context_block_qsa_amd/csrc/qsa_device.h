@@ -781,6 +781,12 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
     return sign | (eb << 3) | ((rb >> 20) & 7u);
 }
 
+// 16 independent 4 x 4 fp32 outer products: lane l (block l/4, column l%4) adds
+// a[lane 4(l/4) + i] * b[lane l] to c[i].
+__device__ __forceinline__ f32x4 mfma_f32_4x4x1(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
