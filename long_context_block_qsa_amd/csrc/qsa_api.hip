@@ -552,7 +552,7 @@ qsa_status qsa_trace_begin(int32_t max_kernels) {
     for (auto &e : t.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             for (auto &x : t.ev)
-                if (x) hipEventDestroy(x);
+                if (x) (void)hipEventDestroy(x);   // best effort on the error path
             t.ev.clear();
             return QSA_ERR_DEVICE;
         }
@@ -582,7 +582,7 @@ int32_t qsa_trace_end(int32_t max_out, int32_t *kind_out, float *ms_out) {
             if (ms_out) ms_out[i] = ms;
         }
     }
-    for (auto &e : t.ev) hipEventDestroy(e);
+    for (auto &e : t.ev) (void)hipEventDestroy(e);   // nothing to report once the times are read
     t.ev.clear();
     t.kind.clear();
     t.open = false;

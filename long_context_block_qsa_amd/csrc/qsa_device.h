@@ -594,7 +594,7 @@ struct TopkSmem {
     uint32_t red[2][16];
     int32_t scan[16];
     int32_t found[4];
-    uint32_t bin_key[64];
+    __attribute__((aligned(16))) uint32_t bin_key[64];   // read 16 bytes at a time
     int32_t bin_pos[64];
     uint32_t take_bits[64];   // bit p: position p of the final bin is kept (n <= 2048)
 };
@@ -706,11 +706,15 @@ __device__ __forceinline__ int block_topk_regs(const uint32_t (&x)[PER], int n, 
             const int m = tot;
             const uint32_t kj = l < m ? sm.bin_key[l] : 0u;
             const int pj = l < m ? sm.bin_pos[l] : 0;
+            // rank = keys above kj plus equal keys earlier in position order (the
+            // compaction kept position order); the bin's keys are read 4 at a time by
+            // broadcast LDS reads
             int rank = 0;
-            for (int i = 0; i < m; ++i) {
-                const uint32_t ki = __builtin_amdgcn_readlane(kj, i);
-                const int pi = __builtin_amdgcn_readlane(pj, i);
-                rank += (ki > kj) || (ki == kj && pi < pj);
+            for (int i0 = 0; i0 < m; i0 += 4) {
+                const u32x4 k4 = *reinterpret_cast<const u32x4 *>(&sm.bin_key[i0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    rank += i0 + e < m && (k4[e] > kj || (k4[e] == kj && i0 + e < l));
             }
             if (l < m && rank < need) atomicOr(&sm.take_bits[pj >> 5], 1u << (pj & 31));
         }
