@@ -217,6 +217,48 @@ __device__ __forceinline__ void score_groups(const ScoreLane &sl, const uint16_t
 
 constexpr int SCORE_BATCH = 8;  // 16-block groups per wave in flight
 
+// score_groups with whole-block loads: each load instruction reads 8 complete 128-byte
+// blocks (lane 8j + q: the 16-byte chunk q of block j), the access the address units
+// coalesce, and each group's chunks reach the MFMA operand layout (lane (g, c): chunks
+// g and 4 + g of block c) through one of the wave's two LDS tiles (16 blocks, 144-byte
+// pitch: the 16 blocks' rows start on distinct 4-bank groups), used in turn.
+constexpr int SC_PITCH = 144;
+constexpr int SC_TILE = 16 * SC_PITCH;
+template <int NB>
+__device__ __forceinline__ void score_groups_lds(const ScoreLane &sl, const uint16_t *kb,
+                                                 int64_t b0, int64_t step, int64_t hi,
+                                                 uint32_t (&key)[NB], uint8_t *tiles) {
+    const int l = lane_id(), g = l >> 4, c = l & 15, bj = l >> 3, q = l & 7;
+    u32x4 b[NB][2];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t blk = b0 + u * step + 8 * h + bj;
+            b[u][h] = load16(kb + (blk < hi ? blk : hi - 1) * DI + 8 * q);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the MFMAs
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        uint8_t *t = tiles + (u & 1) * SC_TILE;
+        wave_lds_sync();   // this tile's reads of two groups ago are done
+        *reinterpret_cast<u32x4 *>(t + bj * SC_PITCH + 16 * q) = b[u][0];
+        *reinterpret_cast<u32x4 *>(t + (8 + bj) * SC_PITCH + 16 * q) = b[u][1];
+        wave_lds_sync();
+        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(t + c * SC_PITCH + 16 * g);
+        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(t + c * SC_PITCH + 64 + 16 * g);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma_bf16_16x16x32(sl.qa[0], x0, acc);
+        acc = mfma_bf16_16x16x32(sl.qa[1], x1, acc);
+        float sc = sl.wr[0] * fmaxf(acc[0], 0.f);
+        sc += sl.wr[1] * fmaxf(acc[1], 0.f);
+        sc += sl.wr[2] * fmaxf(acc[2], 0.f);
+        sc += sl.wr[3] * fmaxf(acc[3], 0.f);
+        key[u] = score_key(sc);
+    }
+}
+
 constexpr int SCORE_NT = 256;
 
 // Whole rows: grid x = tile, y = chunk of `chunk_blocks` blocks.
@@ -235,10 +277,11 @@ score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
         ti.s.s0 + slots_before(ti.t0 + g) - slots_before(ti.ts));
     const uint16_t *kb = k_blk + (int64_t)ti.s.blk0 * DI;
     const int c = lane_id() & 15;
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[SCORE_NT / WAVE][2 * SC_TILE];
     constexpr int64_t step = 16 * (SCORE_NT / WAVE);
     for (int64_t b0 = lo + 16 * (threadIdx.x / WAVE); b0 < hi; b0 += step * SCORE_BATCH) {
         uint32_t key[SCORE_BATCH];
-        score_groups<SCORE_BATCH>(sl, kb, b0, step, hi, key);
+        score_groups_lds<SCORE_BATCH>(sl, kb, b0, step, hi, key, tiles[threadIdx.x / WAVE]);
 #pragma unroll
         for (int u = 0; u < SCORE_BATCH; ++u) {
             const int64_t blk = b0 + u * step + c;
@@ -472,6 +515,7 @@ struct ScoreSmem {
     uint32_t found[2];
     int viol, s_last, exact[4];
     TopkSmem tsm;
+    __attribute__((aligned(16))) uint8_t tiles[LOC_NT / WAVE][2 * SC_TILE];  // score_groups_lds
 };
 
 // One scoring workgroup: chunk `chunk` of tile `tile`. Returns true in the workgroup
@@ -512,7 +556,8 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
     for (int h = 0; h < 2; ++h) {
         uint32_t kk[SCORE_BATCH];
         if (wlo + 16 * SCORE_BATCH * h < whi) {
-            score_groups<SCORE_BATCH>(sl, kb, wlo + 16 * SCORE_BATCH * h, 16, whi, kk);
+            score_groups_lds<SCORE_BATCH>(sl, kb, wlo + 16 * SCORE_BATCH * h, 16, whi, kk,
+                                          sm.tiles[w]);
         } else {
 #pragma unroll
             for (int u = 0; u < SCORE_BATCH; ++u) kk[u] = 0u;
