@@ -330,58 +330,93 @@ __device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
     *need_out = need;
 }
 
-// Ordered pass after radix_kth: walks the n keys in position order and keeps every
-// key above theta and the first `need` keys equal to it, writing their ids
-// (idx[i], or i when idx is null, plus idx_base) and optionally keys to consecutive
-// output slots
-// (at most cap). Optionally counts kept entries per group of `group` positions in
-// LDS (group_cnt). Returns the number kept. All NT threads must call it.
-template <int NT, int PER, typename KeyPtr, typename IdxPtr>
-__device__ __forceinline__ int64_t emit_kept(KeyPtr keys, IdxPtr idx,
-                                             int64_t n, uint32_t theta, int64_t need,
-                                             int32_t *out_idx, uint32_t *out_key, int64_t cap,
-                                             int32_t *scan_sh, uint32_t *group_cnt,
-                                             int group, int32_t idx_base = 0) {
-    const int tid = threadIdx.x;
+// Number of lanes below this one whose bit is set in mask.
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Ordered pass after radix_kth: keeps every key above theta and the first `need` keys
+// equal to it (by position), writing their positions in ascending order to out_idx (at
+// most cap); returns the number kept. Thread t reads element e of a batch at position
+// base + e*NT + t, so every load instruction reads consecutive keys. A kept key's slot is
+// its rank in position order: the kept keys of earlier elements, of earlier waves at the
+// same element, and of lower lanes (a ballot). Per-(wave, element) counts of equal and of
+// kept keys go through `cnt` (LDS, 4 * (NT/64) * PER ints; two barriers per batch, the
+// two halves used by alternate batches). All NT threads must call it.
+template <int NT, int PER, typename KeyPtr>
+__device__ __forceinline__ int64_t emit_kept(KeyPtr keys, int64_t n, uint32_t theta,
+                                             int64_t need, int32_t *out_idx, int64_t cap,
+                                             int32_t *cnt) {
+    constexpr int NW = NT / WAVE;
+    static_assert(PER <= WAVE, "one lane per element writes the wave's counts");
+    const int tid = threadIdx.x, w = tid / WAVE, l = lane_id();
     int64_t run_eq = 0, run_sel = 0;
+    int par = 0;
 #pragma unroll 1
-    for (int64_t base = 0; base < n; base += (int64_t)NT * PER) {
-        const int64_t i0 = base + (int64_t)tid * PER;
+    for (int64_t base = 0; base < n; base += (int64_t)NT * PER, par ^= 1) {
+        int32_t *ceq = cnt + par * 2 * NW * PER;   // [wave][element]: keys equal to theta
+        int32_t *ctk = ceq + NW * PER;             // [wave][element]: kept keys
         uint32_t kk[PER];
-        int n_eq = 0;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const bool valid = i0 + e < n;
-            kk[e] = valid ? keys[i0 + e] : 0u;
-            n_eq += (valid && kk[e] == theta);
+            const int64_t i = base + (int64_t)e * NT + tid;
+            kk[e] = i < n ? keys[i] : 0u;
         }
-        int32_t tot_eq;
-        int64_t eq_run = run_eq + block_excl_scan_i32<NT>(n_eq, scan_sh, &tot_eq);
-        int n_take = 0;
-        uint32_t take_mask = 0;
+        unsigned long long beq[PER];
+        int v = 0;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const bool valid = i0 + e < n;
-            const bool eq = valid && kk[e] == theta;
-            const bool take = (valid && kk[e] > theta) || (eq && eq_run < need);
-            eq_run += eq;
-            if (take) { take_mask |= 1u << e; ++n_take; }
+            beq[e] = __ballot(base + (int64_t)e * NT + tid < n && kk[e] == theta);
+            v = l == e ? (int)__popcll(beq[e]) : v;
         }
-        int32_t tot_take;
-        int64_t pos = run_sel + block_excl_scan_i32<NT>(n_take, scan_sh, &tot_take);
+        if (l < PER) ceq[w * PER + l] = v;
+        __syncthreads();
+        // equal keys before each element of this lane; then which keys are kept
+        int64_t eq_pre = run_eq;
+        int eq_tot = 0;
+        unsigned long long btk[PER];
+        v = 0;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            if (take_mask & (1u << e)) {
-                if (pos < cap) {
-                    out_idx[pos] = (idx ? idx[i0 + e] : (int32_t)(i0 + e)) + idx_base;
-                    if (out_key) out_key[pos] = kk[e];
-                }
-                if (group_cnt) atomicAdd(&group_cnt[(i0 + e) / group], 1u);
-                ++pos;
+            int before_w = 0, col = 0;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const int c = ceq[i * PER + e];
+                before_w += i < w ? c : 0;
+                col += c;
             }
+            const bool valid = base + (int64_t)e * NT + tid < n;
+            const bool eq = (beq[e] >> l) & 1ull;
+            const bool take = (valid && kk[e] > theta) ||
+                              (eq && eq_pre + before_w + lanes_below(beq[e]) < need);
+            btk[e] = __ballot(take);
+            v = l == e ? (int)__popcll(btk[e]) : v;
+            eq_pre += col;
+            eq_tot += col;
         }
-        run_eq += tot_eq;
-        run_sel += tot_take;
+        if (l < PER) ctk[w * PER + l] = v;
+        __syncthreads();
+        int64_t pos = run_sel;
+        int tk_tot = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            int before_w = 0, col = 0;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const int c = ctk[i * PER + e];
+                before_w += i < w ? c : 0;
+                col += c;
+            }
+            if ((btk[e] >> l) & 1ull) {
+                const int64_t slot = pos + before_w + lanes_below(btk[e]);
+                if (slot < cap) out_idx[slot] = (int32_t)(base + (int64_t)e * NT + tid);
+            }
+            pos += col;
+            tk_tot += col;
+        }
+        run_eq += eq_tot;
+        run_sel += tk_tot;
     }
     return run_sel;
 }
@@ -413,10 +448,6 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 }
 
 // Lanes below this one in a ballot mask.
-__device__ __forceinline__ int lanes_below(unsigned long long mask) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
 
 // Wave-wide max / min of uint32 with DPP row shifts and row broadcasts (the result is
 // complete in lane 63 and read from there).

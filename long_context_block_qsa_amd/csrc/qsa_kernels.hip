@@ -325,21 +325,16 @@ struct SelectArgs {
     int dense_only;      // only rows with at most topk visible blocks
 };
 
-// Top-k of n keys at `kk` (LDS or global), ids from `ii` (or positions), written to
-// out in ascending order.
-template <int PER, typename KP_T, typename IP_T>
-__device__ __forceinline__ void select_keys(KP_T kk, IP_T ii, int64_t n, int topk,
-                                            int32_t *out, uint32_t *hist, int32_t *scan_sh,
-                                            uint32_t *found, uint32_t *grp_cnt, int group,
-                                            int64_t ngroups) {
+// Top-k of the n keys at `kk` (global memory): their positions, ascending, to out.
+// hist: LDS, kHistBins entries (the radix histogram, then the emit pass's counts).
+template <int PER, typename KP_T>
+__device__ __forceinline__ void select_keys(KP_T kk, int64_t n, int topk, int32_t *out,
+                                            uint32_t *hist, int32_t *scan_sh, uint32_t *found) {
     uint32_t theta;
     int64_t need;
     radix_kth<SEL_NT>(kk, n, topk, kWide, hist, scan_sh, found, &theta, &need);
-    if (grp_cnt) {
-        for (int64_t i = threadIdx.x; i < ngroups; i += SEL_NT) grp_cnt[i] = 0u;
-        __syncthreads();
-    }
-    emit_kept<SEL_NT, PER>(kk, ii, n, theta, need, out, nullptr, topk, scan_sh, grp_cnt, group);
+    static_assert(4 * (SEL_NT / WAVE) * PER <= kHistBins, "emit counts fit the histogram");
+    emit_kept<SEL_NT, PER>(kk, n, theta, need, out, topk, reinterpret_cast<int32_t *>(hist));
 }
 
 // Level-one merges take at most MERGE_CHUNKS chunk lists (KP candidates each); rows
@@ -432,8 +427,7 @@ __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView r
         return;
     }
     if (a.dense_only) return;
-    select_keys<16>(a.keys + rv.slot, (const int32_t *)nullptr, nv, a.topk, out, hist, scan_sh,
-                    found, nullptr, 1, 0);
+    select_keys<16>(a.keys + rv.slot, nv, a.topk, out, hist, scan_sh, found);
 }
 
 struct LocalArgs {
@@ -499,9 +493,8 @@ __device__ __forceinline__ void select_tile_exact(const LocalArgs &a, const Deco
     for (int rr = 0; rr < nrows; ++rr) {
         if (!exact[rr]) continue;   // uniform (LDS)
         const DecRow r = d.row[row0 + rr];
-        select_keys<16>((const uint32_t *)(a.keys + r.slot), (const int32_t *)nullptr,
-                        nvis_of(r.t), a.topk, a.sel + (row0 + rr) * a.topk, hist, scan_sh,
-                        found, nullptr, 1, 0);
+        select_keys<16>((const uint32_t *)(a.keys + r.slot), nvis_of(r.t), a.topk,
+                        a.sel + (row0 + rr) * a.topk, hist, scan_sh, found);
     }
 }
 
