@@ -289,7 +289,11 @@ static void select_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
 
 /* Attention of one query row. Keys: the tokens of the kept blocks, in ascending
  * order, then the raw tokens after the last complete block (reading R4: the last,
- * incomplete block is attended without compression, elzobrito.github.io). Query head
+ * incomplete block is attended without compression, elzobrito.github.io). A row's
+ * selection is read up to its first negative entry; entries naming a block that is not
+ * visible at t (b >= nvis(t): reading R6, only complete blocks at or before t are
+ * candidates) are not attended, so a selection supplied from outside can never reach
+ * past the row's position. Query head
  * h reads key/value head h / (Hq/Hkv): the 24 query heads share 2 key/value heads
  * (axbrief.com, "Shifting from Tokens to Micro-Blocks"), twelve per KV head
  * (blog.compendialabs.org, "Qwen Sparse Attention -- Full Attention When It
@@ -324,16 +328,17 @@ static void attend_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
     int64_t nv = visible_blocks(d, p.t);
 
     /* the attended positions J(t), ascending */
-    int64_t n_sel = 0;
+    int64_t n_sel = 0, n_vis = 0;
     while (n_sel < kb && sel_row[n_sel] >= 0)
-        ++n_sel;
+        n_vis += sel_row[n_sel++] < nv;
     int64_t n_tail = p.t + 1 - nv * bs;
-    int64_t nj = n_sel * bs + n_tail;
+    int64_t nj = n_vis * bs + n_tail;
     int64_t *J = (int64_t *)malloc((size_t)nj * sizeof *J);
     int64_t n = 0;
     for (int64_t i = 0; i < n_sel; ++i)
-        for (int64_t j = 0; j < bs; ++j)
-            J[n++] = (int64_t)sel_row[i] * bs + j;
+        if (sel_row[i] < nv)
+            for (int64_t j = 0; j < bs; ++j)
+                J[n++] = (int64_t)sel_row[i] * bs + j;
     for (int64_t j = nv * bs; j <= p.t; ++j)
         J[n++] = j;
 
@@ -591,8 +596,9 @@ int qsa_ref_attend_backward(const qsa_ref_dims *d, int32_t batch, const int32_t 
             ++n_sel;
         int64_t nj = 0;
         for (int64_t i = 0; i < n_sel; ++i)
-            for (int64_t j = 0; j < bs; ++j)
-                J[nj++] = p.key0 + (int64_t)sel_row[i] * bs + j;
+            if (sel_row[i] < nv)   /* as in the forward: invisible blocks are not attended */
+                for (int64_t j = 0; j < bs; ++j)
+                    J[nj++] = p.key0 + (int64_t)sel_row[i] * bs + j;
         for (int64_t j = nv * bs; j <= p.t; ++j)
             J[nj++] = p.key0 + j;
         for (int64_t h = 0; h < Hq; ++h) {

@@ -48,3 +48,29 @@ def causal_mask(t_list, L):
     for i, t in enumerate(t_list):
         m[i, :t + 1] = True
     return m
+
+
+def row_positions(cu_q, cu_k):
+    """Position t of every query row: a sequence's queries are its last tokens."""
+    ts = []
+    for b in range(len(cu_q) - 1):
+        L, nq = int(cu_k[b + 1] - cu_k[b]), int(cu_q[b + 1] - cu_q[b])
+        ts.extend(range(L - nq, L))
+    return ts
+
+
+def supplied_selection(ts, topk, seed):
+    """A selection as a caller might supply it (topk >= 6): per row up to 3 visible blocks
+    (ascending), then an id of a block that is not visible at the row's position, a -1 and
+    one more visible id after it. Returns (selection, the same with only the blocks that
+    count, -1 padded)."""
+    rng = np.random.default_rng(seed)
+    sel = np.full((len(ts), topk), -1, np.int32)
+    clean = np.full((len(ts), topk), -1, np.int32)
+    for i, t in enumerate(ts):
+        nv = (t + 1) // 4
+        vis = sorted(rng.choice(nv, size=min(nv, 3), replace=False).tolist()) if nv else []
+        row = vis + [nv + 2 + t % 3, -1] + ([0] if nv else [])
+        sel[i, :len(row)] = row
+        clean[i, :len(vis)] = vis
+    return sel, clean

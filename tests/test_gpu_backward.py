@@ -15,6 +15,7 @@ import long_context_block_qsa_amd as qsa
 import oracle
 import qsa_inputs as gen
 from tests.gpu_helpers import MAX_ABS, MEAN_ABS, DeviceProblem, dev16, errs
+from tests.refmath import row_positions, supplied_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -181,3 +182,21 @@ def test_backward_config4_ragged_prefill_sampled():
         print(f"  block ({seq}, {blk}): {att.size} attending rows of {cand.size}", flush=True)
         _bars(f"cfg4 dk block ({seq},{blk})", dk[k0:k1], dk_r[k0:k1])
         _bars(f"cfg4 dv block ({seq},{blk})", dv[k0:k1], dv_r[k0:k1])
+
+
+def test_backward_supplied_selection_invalid_entries():
+    """Gradients over a caller's selection with an invisible block id and entries after a
+    -1: only the blocks that count are differentiated, like the oracle."""
+    _banner("backward over a supplied selection with invalid entries")
+    p = gen.make_problem([1200, 700, 5], q_lens=[1200, 3, 5], seed=570)
+    bp = BwdProblem(p, 8)
+    sel, clean = supplied_selection(row_positions(p.cu_q, p.cu_k), 8, 15)
+    bp.sel.copy_(torch.from_numpy(sel).cuda())
+    bp.attend()
+    dq, dk, dv = bp.backward()
+    dims = oracle.Dims(topk_blocks=8)
+    dout = gen.bf16_to_f32(bp.dout_np).astype(np.float64)
+    dq_r, dk_r, dv_r = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, clean, dout)
+    _bars("supplied dq", dq, dq_r)
+    _bars("supplied dk", dk, dk_r)
+    _bars("supplied dv", dv, dv_r)

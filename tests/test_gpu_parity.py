@@ -11,6 +11,7 @@ import torch
 import long_context_block_qsa_amd as qsa
 import oracle
 import qsa_inputs as gen
+from tests.refmath import row_positions, supplied_selection
 from tests.gpu_helpers import LSE_ABS, MAX_ABS, MEAN_ABS, DeviceProblem, errs, host16
 
 pytestmark = pytest.mark.gpu
@@ -334,3 +335,19 @@ def test_select_and_attend_entry_points():
     out_r, lse_r = oracle.attend(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, custom)
     mx, mean = errs(out_c, out_r)
     assert mx <= MAX_ABS and mean <= MEAN_ABS
+
+
+def test_attend_supplied_selection_invalid_entries():
+    """A caller's selection with an id of a block not yet visible at the row's position
+    and entries after a -1: the library attends only the blocks that count, like the
+    oracle (prefill rows in one split each; decode rows split over many waves)."""
+    _banner("attend over a supplied selection with invalid entries")
+    p = gen.make_problem([2000, 3000, 9], q_lens=[2000, 2, 9], seed=13)
+    dp = DeviceProblem(p, 16)
+    sel, clean = supplied_selection(row_positions(p.cu_q, p.cu_k), 16, 14)
+    out, lse = dp.attend(sel)
+    dims = oracle.Dims(topk_blocks=16)
+    out_r, lse_r = oracle.attend(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, clean)
+    mx, mean = errs(out, out_r)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+    assert np.max(np.abs(lse - lse_r)) <= 1e-4

@@ -16,7 +16,8 @@ import torch
 import oracle
 import qsa_inputs as gen
 from qsa_inputs import bf16_to_f32, f32_to_bf16_exact
-from tests.refmath import as_f64, attended_mask, causal_mask, masked_gqa_attention
+from tests.refmath import (as_f64, attended_mask, causal_mask, masked_gqa_attention,
+                          supplied_selection)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -272,6 +273,28 @@ def test_sparse_rows_match_masked_attention():
     assert np.max(np.abs(out - ro)) < 1e-12 and np.max(np.abs(lse - rl)) < 1e-12
     assert mask.sum(axis=1).max() <= 3 * 4 + 3
     assert (mask.sum(axis=1)[15:] >= 12).all()
+
+
+def test_supplied_selection_reads_to_first_negative_and_skips_invisible_blocks():
+    """attend() over a selection from outside: a row's entries are read up to its first
+    negative one, and an entry naming a block that is not visible at the row's position
+    (reading R6) is not attended. Pinned against masked attention over the blocks that
+    count."""
+    dims = oracle.Dims(topk_blocks=6)
+    L = 45
+    p = gen.make_problem([L], seed=29)
+    sel, clean = supplied_selection(range(L), 6, 7)
+    out, lse = oracle.attend(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel)
+    mask = attended_mask(range(L), clean, L, 4)
+    ro, rl = masked_gqa_attention(as_f64(p.q), as_f64(p.k), as_f64(p.v), mask,
+                                  1 / math.sqrt(128))
+    assert np.max(np.abs(out - ro)) < 1e-12 and np.max(np.abs(lse - rl)) < 1e-12
+    # the backward takes the same attended set
+    dout = gen.bf16_to_f32(gen.make_dout(p, 3)).astype(np.float64)
+    g_sup = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel, dout)
+    g_cln = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, clean, dout)
+    for a, b in zip(g_sup, g_cln):
+        assert np.array_equal(a, b)
 
 
 def test_first_token_attends_only_itself():
