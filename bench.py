@@ -105,11 +105,11 @@ def decode_algorithmic_bytes(batch, ctx):
 
 
 def run_decode(args, torch, qsa, gen):
-    cfg = gen.CONFIGS[3]
+    cfg = gen.WORKLOADS["decode_16x262144"]
     lens, batch = cfg["lens"], len(cfg["lens"])
     ctx = lens[0]
     t0 = time.time()
-    p = gen.config_problem(3)
+    p = gen.workload_problem("decode_16x262144")
     log(f"generated decode inputs in {time.time() - t0:.1f}s")
     dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
     seqs = qsa.Seqs(p.cu_q, p.cu_k)
@@ -290,7 +290,7 @@ def run_decode_1m(args, torch, qsa, gen, k, v, k_idx, sets):
 # ---------------------------------------------------------------- prefill workload
 
 def run_prefill(args, torch, qsa, gen):
-    p = gen.config_problem(4)
+    p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
     dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
     seqs = qsa.Seqs(p.cu_q, p.cu_k)
     q, k, v, q_idx, k_idx = (dev16(x) for x in (p.q, p.k, p.v, p.q_idx, p.k_idx))
@@ -450,8 +450,9 @@ def traffic_of(kernel):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs "
-                                   "are not part of this build", "n_gpus": args.gpus}),
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the library "
+                                   "has no multi-GPU path (its sharding is a design only)",
+                          "n_gpus": args.gpus}),
               flush=True)
         sys.exit(2)
     import torch

@@ -9,17 +9,18 @@ The five workloads (sizes and value laws of the layer's published shape: 24 quer
 heads over 2 KV heads of 128, a 4-head x 64 indexer, 4-token blocks, a 512-block
 budget, 256K native context):
 
-====  ===========================================  =====================================
-cfg   shape                                        values / structure
-====  ===========================================  =====================================
-0     prefill, 1 x 1,024 tokens                    Q,K,V ~ N(0,1); indexer ints U{-3..3};
-                                                   w in {1,2}; every row dense
-1     decode, 1 x 32,768 context                   as 0, plus 16 needle blocks
-2     prefill, 1 x 16,384 tokens                   as 0
-3     decode, 16 x 262,144 context                 as 0, plus 32 needle blocks / sequence
-4     ragged prefill 65,535 / 40,001 / 8,190 / 3   Q,K,V ~ N(0, 0.5^2); 5% of K rows
-                                                   (token, kv-head) scaled x8
-====  ===========================================  =====================================
+=================================  ===========================  ================================
+workload (seed)                    shape                        values / structure
+=================================  ===========================  ================================
+prefill_1x1024 (1000)              prefill, 1 x 1,024 tokens    Q,K,V ~ N(0,1); indexer ints
+                                                                U{-3..3}; w in {1,2}; all dense
+decode_1x32768 (1001)              decode, 1 x 32,768 context   as above, plus 16 needle blocks
+prefill_1x16384 (1002)             prefill, 1 x 16,384 tokens   as above
+decode_16x262144 (1003)            decode, 16 x 262,144 ctx     as above, plus 32 needle blocks
+                                                                per sequence
+prefill_ragged_65535_40001_8190_3  ragged prefill 65,535 /      Q,K,V ~ N(0, 0.5^2); 5% of K
+(1004)                             40,001 / 8,190 / 3           rows (token, kv-head) scaled x8
+=================================  ===========================  ================================
 
 A needle block of a decode sequence gets indexer keys +3 * sgn(u) on all its tokens,
 u = sum_h w_h * q_idx[h] of that sequence's query (sgn(0) = +1), so its score is at
@@ -216,19 +217,20 @@ def make_dout(p: "Problem", seed: int, scale: float = 1.0, threads=None) -> np.n
                        threads=_nthreads(threads)).reshape(p.n_q, HQ, D)
 
 
-CONFIGS = {
-    0: dict(name="prefill 1x1024", lens=[1024]),
-    1: dict(name="decode 1x32768", lens=[32768], q_lens=[1], needles=16),
-    2: dict(name="prefill 1x16384", lens=[16384]),
-    3: dict(name="decode 16x262144", lens=[262144] * 16, q_lens=[1] * 16, needles=32),
-    4: dict(name="ragged prefill 65535/40001/8190/3", lens=[65535, 40001, 8190, 3],
-            qkv_scale=0.5, outlier_frac=0.05, outlier_mul=8.0),
+# The benchmark and parity workloads, by name, each with its own seed.
+WORKLOADS = {
+    "prefill_1x1024": dict(seed=1000, lens=[1024]),
+    "decode_1x32768": dict(seed=1001, lens=[32768], q_lens=[1], needles=16),
+    "prefill_1x16384": dict(seed=1002, lens=[16384]),
+    "decode_16x262144": dict(seed=1003, lens=[262144] * 16, q_lens=[1] * 16, needles=32),
+    "prefill_ragged_65535_40001_8190_3": dict(seed=1004, lens=[65535, 40001, 8190, 3],
+                                              qkv_scale=0.5, outlier_frac=0.05,
+                                              outlier_mul=8.0),
 }
 
 
-def config_problem(index: int, seed: int | None = None, threads=None) -> Problem:
-    """The workload of config ``index`` with seed 1000 + index (unless given)."""
-    c = dict(CONFIGS[index])
-    name = c.pop("name")
-    return make_problem(seed=1000 + index if seed is None else seed, threads=threads,
-                        name=name, **c)
+def workload_problem(name: str, seed: int | None = None, threads=None) -> Problem:
+    """The named workload with its own seed (unless one is given)."""
+    c = dict(WORKLOADS[name])
+    s0 = c.pop("seed")
+    return make_problem(seed=s0 if seed is None else seed, threads=threads, name=name, **c)

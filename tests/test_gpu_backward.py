@@ -142,12 +142,12 @@ def _attending_rows(p, dims, kb, seq, blk):
     return cand, sel_c, np.array(att, dtype=np.int64)
 
 
-def test_backward_config4_ragged_prefill_sampled():
+def test_backward_prefill_ragged_64k_sampled():
     """The ragged 4-sequence prefill (65535/40001/8190/3 tokens, budget 512) at full size:
     dq on sampled rows, dk and dv on sampled key blocks (from the oracle over exactly the
     rows that attend them: late blocks of each sequence, the partial final blocks)."""
-    _banner("backward config 4: ragged prefill 65535/40001/8190/3")
-    p = gen.config_problem(4)
+    _banner("backward: ragged prefill 65535/40001/8190/3")
+    p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
     bp = BwdProblem(p, 512)
     _, sel, _, _ = bp.forward()
     dq, dk, dv = bp.backward()
@@ -169,7 +169,7 @@ def test_backward_config4_ragged_prefill_sampled():
     assert np.array_equal(sel[rows], sel_r[rows])
     dq_r, _, _ = oracle.attend_backward(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel_r, dout,
                                         rows=rows)
-    _bars("cfg4 dq (sampled rows)", dq[rows], dq_r[rows])
+    _bars("ragged-64k dq (sampled rows)", dq[rows], dq_r[rows])
 
     for seq, blk in ((0, 16383), (0, 16150), (1, 9800), (2, 1950), (3, 0)):
         cand, sel_c, att = _attending_rows(p, dims, kb, seq, blk)
@@ -180,8 +180,8 @@ def test_backward_config4_ragged_prefill_sampled():
         k0 = int(p.cu_k[seq]) + 4 * blk
         k1 = min(k0 + 4, int(p.cu_k[seq + 1]))
         print(f"  block ({seq}, {blk}): {att.size} attending rows of {cand.size}", flush=True)
-        _bars(f"cfg4 dk block ({seq},{blk})", dk[k0:k1], dk_r[k0:k1])
-        _bars(f"cfg4 dv block ({seq},{blk})", dv[k0:k1], dv_r[k0:k1])
+        _bars(f"ragged-64k dk block ({seq},{blk})", dk[k0:k1], dk_r[k0:k1])
+        _bars(f"ragged-64k dv block ({seq},{blk})", dv[k0:k1], dv_r[k0:k1])
 
 
 def test_backward_supplied_selection_invalid_entries():

@@ -89,17 +89,17 @@ def test_fp8_quantize_outliers_and_zero_rows():
     _check("fp8-outliers", Fp8Problem(p, 128))
 
 
-def test_fp8_config3_decode_256k_x16():
-    _banner("fp8 config 3: decode 16x262144")
-    p = gen.config_problem(3)
+def test_fp8_decode_16x262144():
+    _banner("fp8: decode 16x262144")
+    p = gen.workload_problem("decode_16x262144")
     sel, _ = _check("fp8-cfg3", Fp8Problem(p))
     for b, needles in p.needles.items():
         assert set(needles) <= set(sel[b].tolist())
 
 
-def test_fp8_config4_ragged_prefill_sampled():
-    _banner("fp8 config 4: ragged prefill 65535/40001/8190/3")
-    p = gen.config_problem(4)
+def test_fp8_prefill_ragged_64k_sampled():
+    _banner("fp8: ragged prefill 65535/40001/8190/3")
+    p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
     cu = p.cu_q
     rng = np.random.default_rng(44)
     rows = set()
@@ -109,7 +109,7 @@ def test_fp8_config4_ragged_prefill_sampled():
         rows.update(range(max(lo, hi - 4), hi))
         if hi - lo > 10:
             rows.update(rng.integers(lo, hi, 40).tolist())
-    _check("fp8-cfg4", Fp8Problem(p), sorted(rows))
+    _check("fp8-ragged-64k", Fp8Problem(p), sorted(rows))
 
 
 def test_fp8_forward_equals_select_then_attend():

@@ -72,39 +72,39 @@ def test_multi_query_rows_per_sequence():
 
 # ----------------------------------------------------------------- configurations
 
-def test_config0_prefill_1k_dense():
-    _banner("config 0: prefill 1x1024")
-    p = gen.config_problem(0)
+def test_prefill_1x1024_dense():
+    _banner("prefill 1x1024")
+    p = gen.workload_problem("prefill_1x1024")
     _check_rows("cfg0", DeviceProblem(p), None, 512)
 
 
-def test_config1_decode_32k_needles():
-    _banner("config 1: decode 1x32768")
-    p = gen.config_problem(1)
+def test_decode_1x32768_needles():
+    _banner("decode 1x32768")
+    p = gen.workload_problem("decode_1x32768")
     sel, _ = _check_rows("cfg1", DeviceProblem(p), None, 512)
     assert set(p.needles[0]) <= set(sel[0].tolist())
 
 
-def test_config2_prefill_16k_sampled():
-    _banner("config 2: prefill 1x16384")
-    p = gen.config_problem(2)
+def test_prefill_1x16384_sampled():
+    _banner("prefill 1x16384")
+    p = gen.workload_problem("prefill_1x16384")
     rows = sorted(set([0, 1, 2, 3, 4, 2047, 2048, 2049, 2050, 2051, 2052, 2053, 2054, 2055]
                       + list(range(16384 - 40, 16384))
                       + np.random.default_rng(2).integers(0, 16384, 200).tolist()))
     _check_rows("cfg2", DeviceProblem(p), rows, 512)
 
 
-def test_config3_decode_256k_x16_full():
-    _banner("config 3: decode 16x262144")
-    p = gen.config_problem(3)
+def test_decode_16x262144_full():
+    _banner("decode 16x262144")
+    p = gen.workload_problem("decode_16x262144")
     sel, _ = _check_rows("cfg3", DeviceProblem(p), None, 512)
     for b, needles in p.needles.items():
         assert set(needles) <= set(sel[b].tolist()), f"needles of sequence {b} missing"
 
 
-def test_config4_ragged_prefill_sampled():
-    _banner("config 4: ragged prefill 65535/40001/8190/3")
-    p = gen.config_problem(4)
+def test_prefill_ragged_64k_sampled():
+    _banner("ragged prefill 65535/40001/8190/3")
+    p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
     cu = p.cu_q
     rng = np.random.default_rng(4)
     rows = set()
@@ -117,7 +117,7 @@ def test_config4_ragged_prefill_sampled():
                 rows.add(lo + t)
         if hi - lo > 10:
             rows.update(rng.integers(lo, hi, 60).tolist())
-    _check_rows("cfg4", DeviceProblem(p), sorted(rows), 512)
+    _check_rows("ragged-64k", DeviceProblem(p), sorted(rows), 512)
 
 
 # ----------------------------------------------------------------- long contexts

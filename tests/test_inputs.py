@@ -43,7 +43,7 @@ def test_outlier_rows_scaled_by_eight():
 
 
 def test_needle_blocks_point_along_query():
-    p = gen.config_problem(1)
+    p = gen.workload_problem("decode_1x32768")
     assert len(p.needles[0]) == 16 and len(set(p.needles[0])) == 16
     u = (bf16_to_f32(p.q_idx[0]) * p.w[0][:, None]).sum(axis=0)
     sgn = np.where(u >= 0, 3.0, -3.0)

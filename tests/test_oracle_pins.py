@@ -220,8 +220,8 @@ def test_select_scale_invariance():
 
 
 def test_needles_selected_decode_32k():
-    """Config 1: every needle block must be among the 512 kept blocks."""
-    p = gen.config_problem(1)
+    """Decode 1 x 32,768: every needle block must be among the 512 kept blocks."""
+    p = gen.workload_problem("decode_1x32768")
     dims = oracle.Dims()
     kb = oracle.compress(dims, p.cu_k, p.k_idx)
     sel = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb)
@@ -251,9 +251,9 @@ def test_dense_equality_when_budget_covers_everything():
     assert np.max(np.abs(o - ro)) < 1e-12 and np.max(np.abs(l - rl)) < 1e-12
 
 
-def test_dense_equality_config0_sampled_rows():
+def test_dense_equality_prefill_1x1024_sampled_rows():
     dims = oracle.Dims()
-    p = gen.config_problem(0)
+    p = gen.workload_problem("prefill_1x1024")
     rows = [0, 1, 2, 3, 4, 511, 512, 1022, 1023]
     o, l, ro, rl, _ = _prefill_dense_check(p, dims, rows)
     assert np.max(np.abs(o - ro)) < 1e-12 and np.max(np.abs(l - rl)) < 1e-12
