@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context decode line")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV cache lines")
+    ap.add_argument("--no-mtp", action="store_true",
+                    help="skip the multi-query decode line (4 query tokens per sequence)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the prefill's attention backward line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -188,10 +190,11 @@ def run_decode(args, torch, qsa, gen):
             step(i)
     torch.cuda.synchronize()
     long_ctx = None if args.no_1m else run_decode_1m(args, torch, qsa, gen, k, v, k_idx, sets)
+    mtp = None if args.no_mtp else run_decode_mtp(args, torch, qsa, gen, k, v, k_idx, sets)
     fp8 = None if args.no_fp8 else run_decode_fp8(args, torch, qsa, seqs, k, v, k_idx, sets)
     return dict(p=p, batch=batch, ctx=ctx, wall_s=wall, gpu_ms=gpu_ms,
                 kernels=tr.mean_ms(), kernel_total=tr.total_ms(), seqs=seqs, sets=sets,
-                long_ctx=long_ctx, fp8=fp8)
+                long_ctx=long_ctx, fp8=fp8, mtp=mtp)
 
 
 def run_decode_fp8(args, torch, qsa, seqs, k, v, k_idx, sets):
@@ -285,6 +288,63 @@ def run_decode_1m(args, torch, qsa, gen, k, v, k_idx, sets):
             "ms_per_step": round(ms, 5), "query_tokens_per_s": round(batch / (ms / 1e3), 1),
             "algorithmic_bytes": ab["total"], "achieved_gbs": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def run_decode_mtp(args, torch, qsa, gen, k, v, k_idx, sets, nq=4):
+    """Multi-query decode (several draft tokens verified per step): the resident
+    16 x 262,144-token K/V, indexer keys and compressed caches, with the last nq tokens of
+    every sequence as queries (fresh query tensors); the sequence's rows share the scan of
+    its compressed keys. Same rotation and timing protocol as the 1M line."""
+    batch, L = 16, 262144
+    if k.shape[0] != L * batch:
+        return None
+    dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    cu_k = np.arange(batch + 1, dtype=np.int32) * L
+    cu_q = np.arange(batch + 1, dtype=np.int32) * nq
+    seqs = qsa.Seqs(cu_q, cu_k)
+    rows = batch * nq
+    R = len(sets)
+    qs = []
+    for r in range(R):
+        s2 = 70_000 + r
+        qs.append(dict(
+            q=dev16(gen.normal_bf16(s2, gen.TID_Q, rows * HQ * D).reshape(rows, HQ, D)),
+            q_idx=dev16(gen.uniform_int_bf16(s2, gen.TID_QIDX, rows * HI * DI, -3, 3).reshape(
+                rows, HI, DI)),
+            w=torch.from_numpy(gen.weights(s2, gen.TID_W, rows * HI).reshape(rows, HI)).cuda(),
+            sel=torch.empty((rows, TOPK), dtype=torch.int32, device="cuda"),
+            out=torch.empty((rows, HQ, D), dtype=torch.float32, device="cuda"),
+            lse=torch.empty((rows, HQ), dtype=torch.float32, device="cuda")))
+    ws = qsa.alloc_workspace(seqs, TOPK)
+
+    def step(i):
+        s, kb = qs[i % R], sets[i % R]["k_blk"]
+        qsa.forward(seqs, s["q"], k, v, s["q_idx"], s["w"], k_idx, kb, s["sel"], s["out"],
+                    s["lse"], ws, TOPK)
+
+    for i in range(max(args.warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(R, args.steps // 2 // R * R)
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    with qsa.trace(64) as tr:
+        for i in range(R):
+            step(i)
+    torch.cuda.synchronize()
+    one = decode_algorithmic_bytes(batch, L)
+    nbytes = one["score"] + batch * (nq - 1) * (HI * DI * 2 + HI * 4) + nq * one["attend"]
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"decode {nq} queries/sequence: {n} steps, {ms * 1e3:.1f} us/step")
+    return {"workload": f"decode: 16 sequences x 262,144 tokens of context, {nq} query tokens "
+                        "each (the last ones), budget 512 blocks", "steps": n, "launch": "eager",
+            "ms_per_step": round(ms, 5), "query_tokens_per_s": round(rows / (ms / 1e3), 1),
+            "algorithmic_bytes": nbytes, "achieved_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel_mean_ms": {k2: round(v2, 5) for k2, v2 in tr.mean_ms().items()}}
 
 
 # ---------------------------------------------------------------- prefill workload
@@ -503,6 +563,8 @@ def main():
     }
     if d["long_ctx"] is not None:
         line["decode_1m"] = d["long_ctx"]
+    if d["mtp"] is not None:
+        line["decode_multi_query"] = d["mtp"]
     if d["fp8"] is not None:
         line["decode_fp8"] = d["fp8"]
     if not args.no_prefill:

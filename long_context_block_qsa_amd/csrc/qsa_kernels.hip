@@ -560,10 +560,58 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
     }
 
     // each tile row whose selection can come from chunk candidates gets this chunk's
-    // KP best (key, block) pairs, in ascending block order, padded with key 0: the top
-    // KP of each wave's blocks, then the top KP of those 4 x KP
+    // KP best (key, block) pairs, in ascending block order, padded with key 0. One row:
+    // the top KP of each wave's blocks, then the top KP of those 4 x KP. Several rows: the
+    // rows' keys go through LDS (the scoring tiles are free by then) and wave w takes the
+    // top KP of row w over the whole chunk, all rows at once. (The rows' merges below stay
+    // one after another in the whole workgroup: one wave per row was not faster.)
+    const bool par_local = nrows > 1;
+    if (par_local) {
+        uint32_t *rk = reinterpret_cast<uint32_t *>(&sm.tiles[0][0]);   // [row][1024 entries]
+        static_assert(sizeof(sm.tiles) >= 4 * 4 * 256 * sizeof(uint32_t), "row keys fit");
+        __syncthreads();   // every wave is done with its scoring tiles
+#pragma unroll
+        for (int u = 0; u < 2 * SCORE_BATCH; ++u) rk[g * 1024 + w * 256 + 16 * u + c] = key[u];
+        __syncthreads();
+        const int rr = w;
+        if (rr < nrows && cand_eligible(nvis_of(t0 + rr), a.topk, a.ch)) {   // uniform per wave
+            // lane l: entries 16l .. 16l+15 = wave quarter l/16, blocks 16(l%16) + i of it
+            const int64_t vhi = min<int64_t>(hi, nvis_of(t0 + rr));
+            const int qw = l >> 4, u0 = 16 * (l & 15);
+            uint32_t x[16];
+            bool ok[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const u32x4 v4 = *reinterpret_cast<const u32x4 *>(rk + rr * 1024 + 16 * l + 4 * q4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[4 * q4 + e] = v4[e];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                ok[i] = u0 + i < span && lo + (int64_t)qw * span + u0 + i < vhi;
+            const uint32_t mask = wave_topk_hist<16>(x, ok, KP, sm.whist[w]);
+            const int cnt = __popc(mask);
+            const int incl = wave_incl_scan_i32(cnt);
+            const int tot = __builtin_amdgcn_readlane(incl, WAVE - 1);
+            int pos = incl - cnt;
+            uint32_t *ck = a.cand_key + ((row0 + rr) * a.max_chunks + chunk) * KP;
+            int32_t *ci = a.cand_idx + ((row0 + rr) * a.max_chunks + chunk) * KP;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (mask & (1u << i)) {
+                    store_wt(ck + pos, x[i]);
+                    store_wt(ci + pos, (int32_t)(lo + (int64_t)qw * span + u0 + i));
+                    ++pos;
+                }
+            }
+            if (l >= tot && l < KP) {
+                store_wt(ck + l, 0u);
+                store_wt(ci + l, -1);
+            }
+        }
+    }
     uint32_t *wk = sm.whist[w];
-    for (int rr = 0; rr < nrows; ++rr) {
+    for (int rr = 0; !par_local && rr < nrows; ++rr) {
         const int64_t nv = nvis_of(t0 + rr);
         if (!cand_eligible(nv, a.topk, a.ch)) continue;   // uniform over the workgroup
         // the row's keys, position 16u + c, move to lanes as positions 4l .. 4l+3
