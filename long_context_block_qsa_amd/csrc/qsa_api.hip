@@ -87,6 +87,7 @@ struct Plan {
     size_t ws_bytes = 0;
     bool use_dec = false;       // few rows: row/tile tables travel as kernel arguments
     bool fuse_compress = false; // decode: scoring workgroups compress the new blocks
+    bool merge_launch = false;  // decode: some tile's rows are merged by their own launch
     qsa::DecodeTables dec;
 };
 
@@ -103,7 +104,7 @@ void build_decode_tables(const int32_t *cq, const int32_t *ck, int batch, int to
             x.k0 = ck[b];
             x.t = (int32_t)t;
             x.blk0 = (int32_t)blk;
-            x.pad = 0;
+            x.tile = -1;
             x.slot = t >= ts ? slots + h_slots_before(t) - h_slots_before(ts) : 0;
         }
         if (ts < L) {
@@ -114,6 +115,7 @@ void build_decode_tables(const int32_t *cq, const int32_t *ck, int batch, int to
                 y.nrows = (int32_t)std::min<int64_t>(4, L - (ts + 4 * i));
                 y.new_lo = (int32_t)((L - nq) / qsa::BS);
                 y.new_hi = (int32_t)(L / qsa::BS);
+                for (int32_t rr = 0; rr < y.nrows; ++rr) d->row[y.row0 + rr].tile = (int32_t)(tiles + i);
             }
             tiles += nt;
             slots += h_slots_before(L) - h_slots_before(ts);
@@ -191,6 +193,12 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
         p->local_ch = ch;
         p->max_chunks = (int)((p->max_score_blocks + ch - 1) / ch);
         if (p->max_chunks > kMaxGridY) return QSA_ERR_UNSUPPORTED;
+        // the merge launch serves tiles whose chunks fit one merge
+        for (int64_t i = 0; i < p->n_tiles && !p->merge_launch; ++i) {
+            const qsa::DecTile &tl = p->dec.tile[i];
+            const int64_t nv_max = ((int64_t)p->dec.row[tl.row0].t + tl.nrows) / qsa::BS;
+            p->merge_launch = (nv_max + ch - 1) / ch <= qsa::MERGE_CHUNKS;
+        }
     }
     // score grid: enough workgroups to fill the chip when few tiles exist
     if (p->n_tiles > 0 && p->local_ch == 0) {
@@ -264,6 +272,10 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
                                         cand_key, cand_idx, p.local_ch, p.max_chunks, sel,
                                         glist_key, glist_idx, ws_at<uint32_t>(ws, p.off_ctl),
                                         st));
+        // rows whose chunks fit one merge are merged one workgroup per row
+        if (p.merge_launch)
+            QSA_TRY(qsa::launch_merge_dec(p.dec, p.tq, p.topk, q_idx, w, k_blk, keys, cand_key,
+                                          cand_idx, p.local_ch, p.max_chunks, sel, st));
         if (p.n_dense > 0)
             QSA_TRY(qsa::launch_select(tab, &p.dec, p.batch, p.topk, keys, cand_key, cand_idx,
                                        p.local_ch, p.max_chunks, sel, p.tq, p.max_score_blocks,

@@ -72,7 +72,7 @@ struct DecRow {
     int32_t k0;     // first key row of the row's sequence
     int32_t t;      // position of the query token
     int32_t blk0;   // first compressed-block row of the sequence
-    int32_t pad;
+    int32_t tile;   // score tile of the row (-1: not scored)
     int64_t slot;   // first score slot of the row (rows with nvis > topk)
 };
 struct DecTile {

@@ -292,17 +292,18 @@ score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
 
 // =============================================================== score_local + select
 // Decode-shaped launches: grid x = chunk of CH blocks, y = tile, so workgroups are
-// dispatched (and their loads largely served) row by row: a row's chunks complete
-// together and its selection overlaps the scoring of later rows. Each workgroup
-// scores its chunk for the tile's rows into LDS and, for each row whose selection can
-// come from chunk candidates, writes the chunk's KP best (key, block) pairs in
-// ascending block order to cand[row][chunk][0..KP), padded with key 0 (below every
-// real key). The local top-KP is exact and needs no workgroup-wide histogram: each
-// wave takes the top KP of its 256 positions with a wave-private radix select, and
-// one wave takes the top KP of those 4 x KP. Candidates are written through to the
-// coherence point; the workgroup that completes the tile's last chunk (per-tile
-// arrival counter in the control block, reset by that workgroup) then selects every
-// row of the tile (select_tile below).
+// dispatched (and their loads largely served) row by row. Each workgroup scores its
+// chunk for the tile's rows and, for each row whose selection can come from chunk
+// candidates, writes the chunk's KP best (key, block) pairs in ascending block order to
+// cand[row][chunk][0..KP), padded with key 0 (below every real key). The local top-KP
+// is exact and needs no workgroup-wide histogram: each wave takes the top KP of its 256
+// positions with a wave-private radix select, and one wave takes the top KP of those
+// 4 x KP (tiles of several rows: one wave per row over the whole chunk). Rows whose
+// tile has at most MERGE_CHUNKS chunks are then merged by merge_dec_kernel, one
+// workgroup per row. Longer rows merge groups of chunks inside this kernel: candidates
+// are written through to the coherence point, and the workgroup that completes a group
+// (then the tile) behind an arrival counter in the control block (reset by that
+// workgroup) merges it.
 constexpr int LOC_NT = 256;
 constexpr int LOC_MAX_CH = 1024;
 constexpr int KP = 32;
@@ -337,12 +338,12 @@ __device__ __forceinline__ void select_keys(KP_T kk, int64_t n, int topk, int32_
     emit_kept<SEL_NT, PER>(kk, n, theta, need, out, topk, reinterpret_cast<int32_t *>(hist));
 }
 
-// Level-one merges take at most MERGE_CHUNKS chunk lists (KP candidates each); rows
-// with more chunks first merge G = ceil(nch / MERGE_CHUNKS) groups of ceil(nch / G)
-// consecutive chunks (balanced, so every group holds more than MERGE_CHUNKS / 2 chunk
+// Level-one merges take at most MERGE_CHUNKS chunk lists (KP candidates each; the
+// constant is shared with the host, qsa_launch.h); rows with more chunks first merge
+// G = ceil(nch / MERGE_CHUNKS) groups of ceil(nch / G) consecutive chunks (balanced,
+// so every group holds more than MERGE_CHUNKS / 2 chunk
 // lists: at least topk real candidates), then the group lists (topk entries each) of
 // at most MAX_GROUPS groups.
-constexpr int MERGE_CHUNKS = 64;
 constexpr int MAX_GROUPS = 4;
 
 // Top-k of the n <= 2048 candidates (key, id) at ck[0..n) / ci[0..n) (written by other
@@ -686,6 +687,10 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
     const int gsize = (nch + ngroups - 1) / ngroups;   // chunks per group (balanced)
     // groups of chunks are merged separately when there are 2 .. MAX_GROUPS of them
     const bool grouped = ngroups > 1 && ngroups <= MAX_GROUPS;
+    // rows whose chunks fit one merge are merged by merge_dec_kernel, one workgroup per
+    // row: the rows (of all tiles) merge at the same time, and this kernel ends with its
+    // last chunk instead of with a merge behind an arrival counter
+    if (ngroups == 1) return false;
     if (grouped) {
         const int grp = chunk / gsize;
         const int n_in = min(gsize, nch - grp * gsize);
@@ -752,6 +757,47 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
     __syncthreads();
     if (n_exact > 0) select_tile_exact(a, d, tile, sm.exact, sm.hist, sm.scan_sh, sm.found);
     return true;
+}
+
+// Exact selection of one decode row from its full key row, which this workgroup scores
+// itself into the row's slots of `keys` (the blocks its tile's tokens complete were
+// compressed by the scoring kernel, which has finished).
+__device__ __forceinline__ void select_row_exact(const LocalArgs &a, const DecodeTables &d,
+                                                 int64_t row, ScoreSmem &sm) {
+    const DecRow r = d.row[row];
+    const ScoreLane sl = score_lane_setup(a.q_idx, a.w, row, 1, r.t, r.slot);
+    uint32_t *keys = a.keys;
+    const int64_t slot = sl.slot;
+    score_range(sl, a.k_blk + (int64_t)r.blk0 * DI, 0, nvis_of(r.t),
+                [=](int, int64_t blk, uint32_t key) { keys[slot + blk] = key; });
+    wait_vmem();
+    __syncthreads();
+    select_keys<16>((const uint32_t *)(a.keys + r.slot), nvis_of(r.t), a.topk,
+                    a.sel + row * a.topk, sm.hist, sm.scan_sh, sm.found);
+}
+
+// One workgroup per decode row: rows whose tile's chunks fit one merge get their top-k
+// from the chunk candidates the scoring kernel wrote (or exactly, when a chunk may hide
+// a better block or the row has too few chunks for candidates).
+__global__ void __launch_bounds__(LOC_NT) merge_dec_kernel(LocalArgs a, DecodeTables d) {
+    __shared__ ScoreSmem sm;
+    const int64_t row = blockIdx.x;
+    const DecRow r = d.row[row];
+    if (r.tile < 0) return;
+    const DecTile tl = d.tile[r.tile];
+    const int64_t nv_max = nvis_of((int64_t)d.row[tl.row0].t + tl.nrows - 1);
+    const int64_t nch = (nv_max + a.ch - 1) / a.ch;
+    if (nch > MERGE_CHUNKS) return;   // groups of chunks: merged by the scoring kernel
+    const int64_t nv = nvis_of(r.t);
+    bool done = false;
+    if (cand_eligible(nv, a.topk, a.ch)) {
+        const int64_t cbase = row * a.max_chunks * KP;
+        const int nch_row = (int)((nv + a.ch - 1) / a.ch);
+        done = merge_candidates<false>(a.cand_key + cbase, a.cand_idx + cbase, nch_row * KP,
+                                       a.topk, a.sel + row * a.topk, nullptr, nv, a.ch, 0,
+                                       &sm.viol, &sm.tsm);
+    }
+    if (!done) select_row_exact(a, d, row, sm);   // uniform
 }
 
 // 4 waves per SIMD: the whole decode grid (rows x chunks) is resident at once
@@ -1242,6 +1288,20 @@ hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
     trace_before(2, st);
     hipLaunchKernelGGL(score_local_kernel, dim3((unsigned)max_chunks, (unsigned)n_tiles),
                        dim3(LOC_NT), 0, st, a, d);
+    return trace_after(st, hipGetLastError());
+}
+
+hipError_t launch_merge_dec(const DecodeTables &d, int64_t n_rows, int topk,
+                            const uint16_t *q_idx, const float *w, uint16_t *k_blk,
+                            uint32_t *keys, uint32_t *cand_key, int32_t *cand_idx, int ch,
+                            int max_chunks, int32_t *sel, hipStream_t st) {
+    if (n_rows <= 0) return hipSuccess;
+    LocalArgs a = {};
+    a.topk = topk; a.q_idx = q_idx; a.w = w; a.k_idx = nullptr; a.k_blk = k_blk; a.keys = keys;
+    a.cand_key = cand_key; a.cand_idx = cand_idx; a.ch = ch; a.max_chunks = max_chunks;
+    a.sel = sel;
+    trace_before(3, st);
+    hipLaunchKernelGGL(merge_dec_kernel, dim3((unsigned)n_rows), dim3(LOC_NT), 0, st, a, d);
     return trace_after(st, hipGetLastError());
 }
 

@@ -15,6 +15,9 @@ struct Fp8Kv {
     const float *k_scale, *v_scale;
 };
 
+// Chunk lists one decode merge takes (longer rows merge groups of chunks first).
+constexpr int MERGE_CHUNKS = 64;
+
 // Optional per-kernel event trace (thread-local; see qsa_trace_begin).
 void trace_before(int kind, hipStream_t st);
 hipError_t trace_after(hipStream_t st, hipError_t launch_status);
@@ -34,6 +37,12 @@ hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
                               int32_t *cand_idx, int ch, int max_chunks, int32_t *sel,
                               uint32_t *glist_key, int32_t *glist_idx, uint32_t *ctl,
                               hipStream_t st);
+// Selection of the decode rows whose tile's chunks fit one merge (the scoring kernel
+// leaves them to this launch: one workgroup per row).
+hipError_t launch_merge_dec(const DecodeTables &d, int64_t n_rows, int topk,
+                            const uint16_t *q_idx, const float *w, uint16_t *k_blk,
+                            uint32_t *keys, uint32_t *cand_key, int32_t *cand_idx, int ch,
+                            int max_chunks, int32_t *sel, hipStream_t st);
 hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          const uint32_t *keys, const uint32_t *cand_key, const int32_t *cand_idx,
                          int ch, int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
