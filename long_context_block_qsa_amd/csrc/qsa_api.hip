@@ -83,7 +83,8 @@ struct Plan {
     int max_chunks = 0;         // chunks of the longest scored row (decode path)
     int nsplit = 1;             // attention key splits per row
     int64_t n_dense = 0;        // query rows with at most topk visible blocks
-    size_t off_ctl = 0, off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, off_glist = 0;
+    size_t off_ctl = 0, off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, off_glist = 0,
+           off_part = 0;
     size_t ws_bytes = 0;
     bool use_dec = false;       // few rows: row/tile tables travel as kernel arguments
     bool fuse_compress = false; // decode: scoring workgroups compress the new blocks
@@ -213,6 +214,9 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     if (p->tq > 0) {
         int64_t ns = (1024 + 2 * p->tq - 1) / (2 * p->tq);
         p->nsplit = (int)std::min<int64_t>(64, std::max<int64_t>(1, ns));
+        // decode rows merged inside the attention: a workgroup's 4 waves (splits) must
+        // belong to one row, so the 2 * nsplit waves of a row come in whole workgroups
+        if (p->local_ch > 0 && p->nsplit > 1) p->nsplit += p->nsplit & 1;
     }
     // workspace: [control block][seq table][selection][scores | attention partials]
     const size_t ctl_b = (size_t)qsa::CTL_WORDS * sizeof(uint32_t);
@@ -232,7 +236,11 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     p->off_union = ctl_b + tab_b + sel_b;  // scores (+ candidates) while selecting, then partials
     p->off_cand = p->off_union + score_b;
     p->off_glist = p->off_cand + cand_b;
-    p->ws_bytes = p->off_union + std::max(score_b + cand_b + glist_b, part_b);
+    // decode (chunk candidates): the attention reads the candidates while it writes its
+    // partials, so they get their own space; otherwise the partials reuse the scores'
+    p->off_part = p->local_ch > 0 ? p->off_glist + glist_b : p->off_union;
+    p->ws_bytes = p->local_ch > 0 ? p->off_part + part_b
+                                  : p->off_union + std::max(score_b + cand_b + glist_b, part_b);
     return QSA_OK;
 }
 
@@ -254,9 +262,11 @@ qsa_status device_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_E
 template <typename T>
 T *ws_at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
 
+// merge_in_attend: the decode rows merged after scoring are merged by the attention
+// launch that follows (forward), not by a merge launch here.
 qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, const float *w,
                       const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel, void *ws,
-                      hipStream_t st) {
+                      hipStream_t st, bool merge_in_attend = false) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
     uint32_t *keys = ws_at<uint32_t>(ws, p.off_union);
     uint32_t *cand_key = nullptr;
@@ -273,7 +283,7 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
                                         glist_key, glist_idx, ws_at<uint32_t>(ws, p.off_ctl),
                                         st));
         // rows whose chunks fit one merge are merged one workgroup per row
-        if (p.merge_launch)
+        if (p.merge_launch && !merge_in_attend)
             QSA_TRY(qsa::launch_merge_dec(p.dec, p.tq, p.topk, q_idx, w, k_blk, keys, cand_key,
                                           cand_idx, p.local_ch, p.max_chunks, sel, st));
         if (p.n_dense > 0)
@@ -294,11 +304,11 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
 
 qsa_status run_attend(const Plan &p, const qsa_bf16 *q, const qsa_bf16 *k, const qsa_bf16 *v,
                       const qsa::Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
-                      void *ws, hipStream_t st) {
+                      void *ws, hipStream_t st, const qsa::AttnMerge *merge = nullptr) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
-    float *part = ws_at<float>(ws, p.off_union);
+    float *part = ws_at<float>(ws, p.off_part);
     QSA_TRY(qsa::launch_attend(tab, p.use_dec ? &p.dec : nullptr, p.batch, p.topk, p.scale, q,
-                               k, v, fp8, sel, out, lse, part, p.nsplit, p.tq, st));
+                               k, v, fp8, sel, out, lse, part, p.nsplit, p.tq, merge, st));
     return QSA_OK;
 }
 
@@ -357,10 +367,22 @@ qsa_status forward_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_
                                      k_idx, k_blk, 1, tab, p.topk, hs));
     else if (!p.use_dec)
         QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk, tab, hs));
-    if ((st = run_select(p, seqs, q_idx, w, fused ? k_idx : nullptr, k_blk, sel_use, ws, hs)) !=
-        QSA_OK)
+    // decode rows merged after scoring: the attention workgroups of a row merge its
+    // candidates themselves (no merge launch, no selection round trip through memory)
+    const bool merge_in_attend = p.use_dec && p.local_ch > 0 && p.merge_launch;
+    if ((st = run_select(p, seqs, q_idx, w, fused ? k_idx : nullptr, k_blk, sel_use, ws, hs,
+                         merge_in_attend)) != QSA_OK)
         return st;
-    return run_attend(p, q, k, v, fp8, sel_use, out, lse, ws, hs);
+    qsa::AttnMerge m = {};
+    if (merge_in_attend) {
+        m.q_idx = q_idx; m.w = w; m.k_blk = k_blk;
+        m.keys = ws_at<uint32_t>(ws, p.off_union);
+        m.cand_key = ws_at<uint32_t>(ws, p.off_cand);
+        m.cand_idx = reinterpret_cast<int32_t *>(m.cand_key + (size_t)p.tq * p.max_chunks * 32);
+        m.ch = p.local_ch; m.max_chunks = p.max_chunks;
+        m.sel = sel_use;
+    }
+    return run_attend(p, q, k, v, fp8, sel_use, out, lse, ws, hs, merge_in_attend ? &m : nullptr);
 }
 
 // Attention backward: per-sequence table, D, nsel, list offsets, block totals, count

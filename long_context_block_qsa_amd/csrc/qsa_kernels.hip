@@ -763,7 +763,8 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
 // itself into the row's slots of `keys` (the blocks its tile's tokens complete were
 // compressed by the scoring kernel, which has finished).
 __device__ __forceinline__ void select_row_exact(const LocalArgs &a, const DecodeTables &d,
-                                                 int64_t row, ScoreSmem &sm) {
+                                                 int64_t row, int32_t *out, uint32_t *hist,
+                                                 int32_t *scan_sh, uint32_t *found) {
     const DecRow r = d.row[row];
     const ScoreLane sl = score_lane_setup(a.q_idx, a.w, row, 1, r.t, r.slot);
     uint32_t *keys = a.keys;
@@ -772,8 +773,18 @@ __device__ __forceinline__ void select_row_exact(const LocalArgs &a, const Decod
                 [=](int, int64_t blk, uint32_t key) { keys[slot + blk] = key; });
     wait_vmem();
     __syncthreads();
-    select_keys<16>((const uint32_t *)(a.keys + r.slot), nvis_of(r.t), a.topk,
-                    a.sel + row * a.topk, sm.hist, sm.scan_sh, sm.found);
+    select_keys<16>((const uint32_t *)(a.keys + r.slot), nvis_of(r.t), a.topk, out, hist,
+                    scan_sh, found);
+}
+
+// The rows that are merged from chunk candidates outside the scoring kernel: those whose
+// tile has at most MERGE_CHUNKS chunks.
+__device__ __forceinline__ bool merged_after_scoring(const DecodeTables &d, const DecRow &r,
+                                                     int ch) {
+    if (r.tile < 0) return false;
+    const DecTile tl = d.tile[r.tile];
+    const int64_t nv_max = nvis_of((int64_t)d.row[tl.row0].t + tl.nrows - 1);
+    return (nv_max + ch - 1) / ch <= MERGE_CHUNKS;
 }
 
 // One workgroup per decode row: rows whose tile's chunks fit one merge get their top-k
@@ -783,11 +794,7 @@ __global__ void __launch_bounds__(LOC_NT) merge_dec_kernel(LocalArgs a, DecodeTa
     __shared__ ScoreSmem sm;
     const int64_t row = blockIdx.x;
     const DecRow r = d.row[row];
-    if (r.tile < 0) return;
-    const DecTile tl = d.tile[r.tile];
-    const int64_t nv_max = nvis_of((int64_t)d.row[tl.row0].t + tl.nrows - 1);
-    const int64_t nch = (nv_max + a.ch - 1) / a.ch;
-    if (nch > MERGE_CHUNKS) return;   // groups of chunks: merged by the scoring kernel
+    if (!merged_after_scoring(d, r, a.ch)) return;   // groups of chunks: scoring kernel
     const int64_t nv = nvis_of(r.t);
     bool done = false;
     if (cand_eligible(nv, a.topk, a.ch)) {
@@ -797,7 +804,8 @@ __global__ void __launch_bounds__(LOC_NT) merge_dec_kernel(LocalArgs a, DecodeTa
                                        a.topk, a.sel + row * a.topk, nullptr, nv, a.ch, 0,
                                        &sm.viol, &sm.tsm);
     }
-    if (!done) select_row_exact(a, d, row, sm);   // uniform
+    if (!done)   // uniform
+        select_row_exact(a, d, row, a.sel + row * a.topk, sm.hist, sm.scan_sh, sm.found);
 }
 
 // 4 waves per SIMD: the whole decode grid (rows x chunks) is resident at once
@@ -862,6 +870,8 @@ struct AttnArgs {
     float *part;
     int nsplit;
     int64_t nrows;
+    int merge;        // decode: merge the rows of short tiles here (operands in `loc`)
+    LocalArgs loc;
 };
 
 __device__ __forceinline__ int64_t part_stride_row(int nsplit) {
@@ -890,12 +900,12 @@ constexpr int KT_LDS_BYTES = 32 * (2 * HD + 16);   // one wave's tile (the large
 
 template <bool FP8>
 __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv, int64_t row,
-                                            int g, int sp, uint8_t *klds) {
+                                            int g, int sp, uint8_t *klds,
+                                            const int32_t *srow) {
     using Tile = typename std::conditional<FP8, KVTile8, KVTile>::type;
     const int64_t t = rv.t;
     const int64_t nv = nvis_of(t);
     const int ntail = (int)(t + 1 - BS * nv);
-    const int32_t *srow = a.sel + row * a.topk;
     const int l = lane_id(), gr = l >> 4, col = l & 15;
 
     // number of leading selected entries: 8 unconditional loads in flight, then ballots
@@ -1130,8 +1140,18 @@ attend_kernel(AttnArgs a) {
     int g, sp;
     if (!attend_item(a, row, g, sp)) return;
     attend_body<FP8>(a, tab_row(a.tab, a.batch, a.topk, row), row, g, sp,
-                     klds + (threadIdx.x / WAVE) * KT_LDS_BYTES);
+                     klds + (threadIdx.x / WAVE) * KT_LDS_BYTES, a.sel + row * a.topk);
 }
+
+// LDS of a decode attention workgroup that merges its row's candidates.
+struct AttnMergeSmem {
+    TopkSmem tsm;
+    int viol;
+    uint32_t hist[kHistBins];   // exact fallback: radix histogram, then the emit counts
+    int32_t scan_sh[SEL_NT / WAVE];
+    uint32_t found[2];
+    int32_t ids[KMAX];          // the row's kept block ids, ascending
+};
 
 template <bool FP8>
 __global__ void __launch_bounds__(ATT_NT)
@@ -1140,9 +1160,32 @@ attend_dec_kernel(AttnArgs a, DecodeTables d) {
     int g, sp;
     if (!attend_item(a, row, g, sp)) return;
     __shared__ __attribute__((aligned(16))) uint8_t klds[(ATT_NT / WAVE) * KT_LDS_BYTES];
+    __shared__ AttnMergeSmem ms;
     const DecRow r = d.row[row];
     const RowView rv = {r.k0, r.t, r.blk0, r.slot};
-    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES);
+    const int32_t *srow = a.sel + row * a.topk;
+    // rows merged from chunk candidates after scoring: every workgroup of the row (its
+    // waves are splits of one row) merges them into LDS, the row's first workgroup also
+    // writes the selection out
+    if (a.merge && merged_after_scoring(d, r, a.loc.ch)) {   // uniform over the workgroup
+        const int64_t nv = nvis_of(r.t);
+        bool done = false;
+        if (cand_eligible(nv, a.topk, a.loc.ch)) {
+            const int64_t cbase = row * a.loc.max_chunks * KP;
+            const int nch_row = (int)((nv + a.loc.ch - 1) / a.loc.ch);
+            done = merge_candidates<false>(a.loc.cand_key + cbase, a.loc.cand_idx + cbase,
+                                           nch_row * KP, a.topk, ms.ids, nullptr, nv,
+                                           a.loc.ch, 0, &ms.viol, &ms.tsm);
+        }
+        if (!done)   // uniform
+            select_row_exact(a.loc, d, row, ms.ids, ms.hist, ms.scan_sh, ms.found);
+        __syncthreads();
+        const int64_t item0 = (int64_t)blockIdx.x * (ATT_NT / WAVE);
+        if (item0 % (HKV * a.nsplit) == 0)
+            for (int i = threadIdx.x; i < a.topk; i += ATT_NT) a.loc.sel[row * a.topk + i] = ms.ids[i];
+        srow = ms.ids;
+    }
+    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES, srow);
 }
 
 // =============================================================== combine
@@ -1326,9 +1369,17 @@ hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, i
 hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
-                         float *part, int nsplit, int64_t n_rows, hipStream_t st) {
+                         float *part, int nsplit, int64_t n_rows, const AttnMerge *merge,
+                         hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
-    AttnArgs a;
+    AttnArgs a = {};
+    a.merge = merge != nullptr && d != nullptr;
+    if (a.merge) {
+        a.loc.topk = topk; a.loc.q_idx = merge->q_idx; a.loc.w = merge->w; a.loc.k_idx = nullptr;
+        a.loc.k_blk = merge->k_blk; a.loc.keys = merge->keys; a.loc.cand_key = merge->cand_key;
+        a.loc.cand_idx = merge->cand_idx; a.loc.ch = merge->ch; a.loc.max_chunks = merge->max_chunks;
+        a.loc.sel = merge->sel;
+    }
     a.tab = tab; a.batch = batch; a.topk = topk;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q = q; a.k = k; a.v = v; a.sel = sel; a.out = out; a.lse = lse; a.part = part;

@@ -47,10 +47,22 @@ hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, i
                          const uint32_t *keys, const uint32_t *cand_key, const int32_t *cand_idx,
                          int ch, int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
                          int dense_only, hipStream_t st);
+// Decode rows whose tile's chunks fit one merge, merged by the attention workgroups
+// themselves (each workgroup of a row merges its candidates into LDS first).
+struct AttnMerge {
+    const uint16_t *q_idx;
+    const float *w;
+    uint16_t *k_blk;
+    uint32_t *keys, *cand_key;
+    int32_t *cand_idx;
+    int ch, max_chunks;
+    int32_t *sel;   // where the merged selections are written out (the one attend reads)
+};
 hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
-                         float *part, int nsplit, int64_t n_rows, hipStream_t st);
+                         float *part, int nsplit, int64_t n_rows, const AttnMerge *merge,
+                         hipStream_t st);
 // Attention backward over fixed selections (qsa_backward.hip).
 struct BwdSeq;
 struct BwdBuffers {
