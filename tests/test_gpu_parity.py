@@ -62,6 +62,25 @@ def test_small_decode(lens, topk):
     _check_rows(f"decode{lens}/k{topk}", DeviceProblem(p, topk), None, topk)
 
 
+@pytest.mark.parametrize("topk", [512, 100])
+def test_decode_odd_split_counts(topk):
+    """9 decode rows: ceil(1024 / 18) = 57 key splits per (row, KV head) are rounded up to an
+    even count, so the workgroups of the attention (4 splits each) never straddle two rows;
+    the rows mix scored contexts (more blocks than the budget) with short ones."""
+    lens = [5000, 3000, 2100, 9000, 4097, 2049, 600, 12000, 7777]
+    _banner(f"decode 9 rows topk={topk}")
+    p = gen.make_problem(lens, q_lens=[1] * len(lens), seed=311 + topk)
+    _check_rows(f"decode9/k{topk}", DeviceProblem(p, topk), None, topk)
+
+
+def test_multi_query_odd_split_counts():
+    """11 query rows (4 + 4 + 3): 47 splits rounded up to 48."""
+    lens, q_lens = [6000, 3001, 2500], [4, 4, 3]
+    _banner("multi-query decode, 11 rows")
+    p = gen.make_problem(lens, q_lens=q_lens, seed=317)
+    _check_rows("multi-query-11", DeviceProblem(p, 512), None, 512)
+
+
 def test_multi_query_rows_per_sequence():
     """2-4 query tokens per sequence (the last tokens), ragged lengths."""
     _banner("multi-query decode")
