@@ -436,17 +436,6 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d));
-    return v;
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d));
-    return v;
-}
-
 // Lanes below this one in a ballot mask.
 
 // Wave-wide max / min of uint32 with DPP row shifts and row broadcasts (the result is
