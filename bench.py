@@ -37,7 +37,7 @@ HQ, HKV, D, HI, DI, BS, TOPK = 24, 2, 128, 4, 64, 4, 512
 # reads on a plain 512 MiB copy) from rocprofv3 --pmc runs of this benchmark, with the
 # fingerprint of the kernel sources they were taken on; reported only while it matches.
 TRAFFIC = {
-    "score": {"bytes": 135_080_000, "sources_sha256": "b8bd3c4dd27145e9d8cd1796438465a6a8bfeec7625e168746828779e4e6c4a6"},
+    "score": {"bytes": 135_080_000, "sources_sha256": "ed8549b398cc8cdd4f8153c3ef6564e38bb32af532bc19b81f08f2a57e00e32c"},
 }
 
 

@@ -299,8 +299,9 @@ score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
 // is exact and needs no workgroup-wide histogram: each wave takes the top KP of its 256
 // positions with a wave-private radix select, and one wave takes the top KP of those
 // 4 x KP (tiles of several rows: one wave per row over the whole chunk). Rows whose
-// tile has at most MERGE_CHUNKS chunks are then merged by merge_dec_kernel, one
-// workgroup per row. Longer rows merge groups of chunks inside this kernel: candidates
+// tile has at most MERGE_CHUNKS chunks are then merged after this kernel: in a forward
+// step by the decode attention's workgroups, after a selection alone by merge_dec_kernel
+// (one workgroup per row). Longer rows merge groups of chunks inside this kernel: candidates
 // are written through to the coherence point, and the workgroup that completes a group
 // (then the tile) behind an arrival counter in the control block (reset by that
 // workgroup) merges it.
