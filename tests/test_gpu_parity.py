@@ -121,6 +121,14 @@ def test_decode_16x262144_full():
         assert set(needles) <= set(sel[b].tolist()), f"needles of sequence {b} missing"
 
 
+def test_decode_multi_query_16x262144_full():
+    """The multi-query decode line at its size: 16 sequences of 262,144 tokens, 4 query
+    tokens each (tiles of 4 rows sharing the compressed-key scan), all 64 rows."""
+    _banner("decode 16x262144, 4 query tokens per sequence")
+    p = gen.make_problem([262144] * 16, q_lens=[4] * 16, seed=1003, needles=32)
+    _check_rows("cfg3-mq4", DeviceProblem(p), None, 512)
+
+
 def test_prefill_ragged_64k_sampled():
     _banner("ragged prefill 65535/40001/8190/3")
     p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
