@@ -159,6 +159,16 @@ def test_decode_1m_context_grouped_merge():
     assert set(p.needles[0]) <= set(sel[0].tolist())
 
 
+def test_decode_4x1m_full():
+    """The 1M decode line's shape: 4 sequences of 1,048,576 tokens, one query each (4 score
+    tiles, each merging 4 groups of 64 chunks inside the scoring kernel), all rows."""
+    _banner("decode 4x1M")
+    p = gen.make_problem([1 << 20] * 4, q_lens=[1] * 4, seed=23, needles=16)
+    sel, _ = _check_rows("4x1M", DeviceProblem(p), None, 512)
+    for b, needles in p.needles.items():
+        assert set(needles) <= set(sel[b].tolist()), f"needles of sequence {b} missing"
+
+
 def test_multi_query_long_rows_grouped():
     """Three query tokens of one 300,001-token sequence (one tile, 74 chunks, 2 groups)
     plus a short sequence."""
