@@ -92,7 +92,7 @@ def test_fp8_quantize_outliers_and_zero_rows():
 def test_fp8_decode_16x262144():
     _banner("fp8: decode 16x262144")
     p = gen.workload_problem("decode_16x262144")
-    sel, _ = _check("fp8-cfg3", Fp8Problem(p))
+    sel, _ = _check("fp8-decode-16x262144", Fp8Problem(p))
     for b, needles in p.needles.items():
         assert set(needles) <= set(sel[b].tolist())
 

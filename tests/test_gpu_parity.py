@@ -94,13 +94,13 @@ def test_multi_query_rows_per_sequence():
 def test_prefill_1x1024_dense():
     _banner("prefill 1x1024")
     p = gen.workload_problem("prefill_1x1024")
-    _check_rows("cfg0", DeviceProblem(p), None, 512)
+    _check_rows("prefill-1x1024", DeviceProblem(p), None, 512)
 
 
 def test_decode_1x32768_needles():
     _banner("decode 1x32768")
     p = gen.workload_problem("decode_1x32768")
-    sel, _ = _check_rows("cfg1", DeviceProblem(p), None, 512)
+    sel, _ = _check_rows("decode-1x32768", DeviceProblem(p), None, 512)
     assert set(p.needles[0]) <= set(sel[0].tolist())
 
 
@@ -110,13 +110,13 @@ def test_prefill_1x16384_sampled():
     rows = sorted(set([0, 1, 2, 3, 4, 2047, 2048, 2049, 2050, 2051, 2052, 2053, 2054, 2055]
                       + list(range(16384 - 40, 16384))
                       + np.random.default_rng(2).integers(0, 16384, 200).tolist()))
-    _check_rows("cfg2", DeviceProblem(p), rows, 512)
+    _check_rows("prefill-1x16384", DeviceProblem(p), rows, 512)
 
 
 def test_decode_16x262144_full():
     _banner("decode 16x262144")
     p = gen.workload_problem("decode_16x262144")
-    sel, _ = _check_rows("cfg3", DeviceProblem(p), None, 512)
+    sel, _ = _check_rows("decode-16x262144", DeviceProblem(p), None, 512)
     for b, needles in p.needles.items():
         assert set(needles) <= set(sel[b].tolist()), f"needles of sequence {b} missing"
 
@@ -126,7 +126,7 @@ def test_decode_multi_query_16x262144_full():
     tokens each (tiles of 4 rows sharing the compressed-key scan), all 64 rows."""
     _banner("decode 16x262144, 4 query tokens per sequence")
     p = gen.make_problem([262144] * 16, q_lens=[4] * 16, seed=1003, needles=32)
-    _check_rows("cfg3-mq4", DeviceProblem(p), None, 512)
+    _check_rows("decode-16x262144-4q", DeviceProblem(p), None, 512)
 
 
 def test_prefill_ragged_64k_sampled():
