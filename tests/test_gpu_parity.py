@@ -81,6 +81,16 @@ def test_multi_query_odd_split_counts():
     _check_rows("multi-query-11", DeviceProblem(p, 512), None, 512)
 
 
+def test_decode_65_rows_split_combine():
+    """65 decode rows, one more than the decode tables hold: the per-sequence table path
+    with 8 key splits per (row, KV head) and the combine kernel (mixed lengths, some rows
+    within the budget)."""
+    lens = [3000 + 37 * i for i in range(60)] + [100, 2048, 2051, 900, 5]
+    _banner("decode 65 rows")
+    p = gen.make_problem(lens, q_lens=[1] * len(lens), seed=331)
+    _check_rows("decode-65-rows", DeviceProblem(p, 512), None, 512)
+
+
 def test_multi_query_rows_per_sequence():
     """2-4 query tokens per sequence (the last tokens), ragged lengths."""
     _banner("multi-query decode")
