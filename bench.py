@@ -197,6 +197,33 @@ def run_decode(args, torch, qsa, gen):
                 long_ctx=long_ctx, fp8=fp8, mtp=mtp)
 
 
+def time_steps(args, torch, step, R, n):
+    """Runs n steps (a multiple of R) and returns (ms per step, launch mode): replays of one
+    HIP graph holding R consecutive steps, as for the main decode line, or with --no-graph
+    launches from Python."""
+    if args.no_graph:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            step(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n, "eager"
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(R):
+            step(r)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n // R):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    del graph
+    return ms, "hip graph replay"
+
+
 def run_decode_fp8(args, torch, qsa, seqs, k, v, k_idx, sets):
     """The decode workload with K and V read from the FP8 cache (built once, outside the
     timed region, like the compressed indexer keys)."""
@@ -218,11 +245,7 @@ def run_decode_fp8(args, torch, qsa, seqs, k, v, k_idx, sets):
         step(i)
     torch.cuda.synchronize()
     n = max(R, args.steps // R * R)
-    t0 = time.perf_counter()
-    for i in range(n):
-        step(i)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / n
+    ms, mode = time_steps(args, torch, step, R, n)
     with qsa.trace(64) as tr:
         for i in range(R):
             step(i)
@@ -235,7 +258,7 @@ def run_decode_fp8(args, torch, qsa, seqs, k, v, k_idx, sets):
     log(f"decode fp8: {n} steps, {ms * 1e3:.1f} us/step")
     del k8, v8, ks, vs
     return {"workload": "decode as above, K/V from the FP8 (E4M3 + per-row scale) cache",
-            "steps": n, "launch": "eager", "ms_per_step": round(ms, 5),
+            "steps": n, "launch": mode, "ms_per_step": round(ms, 5),
             "query_tokens_per_s": round(batch / (ms / 1e3), 1), "algorithmic_bytes": nbytes,
             "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "kernel_mean_ms": {k2: round(v2, 5) for k2, v2 in tr.mean_ms().items()}}
@@ -275,16 +298,12 @@ def run_decode_1m(args, torch, qsa, gen, k, v, k_idx, sets):
         step(i)
     torch.cuda.synchronize()
     n = max(R, args.steps // 2 // R * R)
-    t0 = time.perf_counter()
-    for i in range(n):
-        step(i)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / n
+    ms, mode = time_steps(args, torch, step, R, n)
     ab = decode_algorithmic_bytes(batch, L)
     gbs = ab["total"] / (ms / 1e3) / 1e9
     log(f"decode 1M: {n} steps, {ms * 1e3:.1f} us/step")
     return {"workload": "decode: 4 sequences x 1,048,576 tokens of context, 1 query token "
-                        "each, budget 512 blocks", "steps": n, "launch": "eager",
+                        "each, budget 512 blocks", "steps": n, "launch": mode,
             "ms_per_step": round(ms, 5), "query_tokens_per_s": round(batch / (ms / 1e3), 1),
             "algorithmic_bytes": ab["total"], "achieved_gbs": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -326,11 +345,7 @@ def run_decode_mtp(args, torch, qsa, gen, k, v, k_idx, sets, nq=4):
         step(i)
     torch.cuda.synchronize()
     n = max(R, args.steps // 2 // R * R)
-    t0 = time.perf_counter()
-    for i in range(n):
-        step(i)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / n
+    ms, mode = time_steps(args, torch, step, R, n)
     with qsa.trace(64) as tr:
         for i in range(R):
             step(i)
@@ -340,7 +355,7 @@ def run_decode_mtp(args, torch, qsa, gen, k, v, k_idx, sets, nq=4):
     gbs = nbytes / (ms / 1e3) / 1e9
     log(f"decode {nq} queries/sequence: {n} steps, {ms * 1e3:.1f} us/step")
     return {"workload": f"decode: 16 sequences x 262,144 tokens of context, {nq} query tokens "
-                        "each (the last ones), budget 512 blocks", "steps": n, "launch": "eager",
+                        "each (the last ones), budget 512 blocks", "steps": n, "launch": mode,
             "ms_per_step": round(ms, 5), "query_tokens_per_s": round(rows / (ms / 1e3), 1),
             "algorithmic_bytes": nbytes, "achieved_gbs": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
