@@ -7,16 +7,21 @@
  * order in which the pages describe the layer: compress key blocks, score them
  * with the indexer, keep the best blocks, attend over the kept tokens.
  *
- * Readings taken where the pages are silent (each is restated at its step):
- *   R1 compression of a micro-block = sum of its indexer keys, stored as bf16;
- *   R2 score = sum_h w[t,h] * relu(q_idx[t,h] . K^[b]) with relu(x) = x>0 ? x : +0;
- *   R3 order = score descending, ties to the lower block index;
- *   R4 a block is a candidate once all of its tokens are at or before the query;
- *      the tokens after the last complete block (0..bs-1 of them) are attended raw,
- *      on top of the block budget;
- *   R5 query head h uses key/value head h / (Hq/Hkv) (contiguous groups);
- *   R6 one selection per query token, shared by every head;
- *   R7 softmax scale 1/sqrt(D) unless given; output and log-sum-exp per head.
+ * Readings taken where the pages are silent (each is restated at its step; the
+ * numbers are the ones the design notes use for the same readings):
+ *   R1  compression of a micro-block = sum of its indexer keys, stored as bf16;
+ *   R3  score = sum_h w[t,h] * relu(q_idx[t,h] . K^[b]) with relu(x) = x>0 ? x : +0;
+ *   R4  order = score descending, ties to the lower block index;
+ *   R5  the budget counts compressed blocks only: the raw tail is attended on top;
+ *   R6  a block is a candidate once all of its tokens are at or before the query;
+ *       the tokens after the last complete block (0..bs-1 of them) are attended raw;
+ *   R8  query head h uses key/value head h / (Hq/Hkv) (contiguous groups);
+ *   R9  softmax scale 1/sqrt(D) unless given;
+ *   R10 output and log-sum-exp per head;
+ *   R11 a query with no more visible blocks than the budget keeps all of them;
+ *   R14 one selection per query token, shared by every head;
+ *   R18 FP8 cache: E4M3 bytes with one fp32 scale per (token, KV head) row;
+ *   R19 the backward differentiates the attention over fixed selections.
  */
 #include "qsa_ref.h"
 
@@ -155,7 +160,7 @@ static row_pos locate_row(const qsa_ref_dims *d, int32_t batch, const int32_t *c
     return p;
 }
 
-/* Reading R4: blocks whose every token is at or before t. */
+/* Reading R6: blocks whose every token is at or before t. */
 static int64_t visible_blocks(const qsa_ref_dims *d, int64_t t)
 {
     return (t + 1) / d->block_size;
@@ -197,20 +202,33 @@ static double relu(double x) { return x > 0.0 ? x : 0.0; }
 
 /* Indexer score of block `blk` for one query row. The pages describe a small
  * indexer whose query heads share one key ("MQA indexer", aiany.app, "Key
- * Capabilities") scoring compressed blocks. Reading R2:
+ * Capabilities") scoring compressed blocks. Reading R3:
  *     s = sum_h w[h] * relu(q_idx[h] . K^[blk]). */
-static double block_score(const qsa_ref_dims *d, const uint16_t *qi_row, const float *w_row,
-                          const uint16_t *kb)
+static double block_score(const qsa_ref_dims *d, const double *qi_row, const float *w_row,
+                          const uint16_t *kb, double *kd)
 {
     const int64_t Hi = d->n_idx_heads, Di = d->idx_dim;
+    for (int64_t j = 0; j < Di; ++j)
+        kd[j] = bf16_value(kb[j]);
     double s = 0.0;
     for (int64_t h = 0; h < Hi; ++h) {
         double dot = 0.0;
         for (int64_t j = 0; j < Di; ++j)
-            dot += bf16_value(qi_row[h * Di + j]) * bf16_value(kb[j]);
+            dot += qi_row[h * Di + j] * kd[j];
         s += (double)w_row[h] * relu(dot);
     }
     return s;
+}
+
+/* The indexer query of one row as doubles (exact), [Hi * Di]. NULL if out of memory. */
+static double *widen_row(const qsa_ref_dims *d, const uint16_t *qi_row)
+{
+    const int64_t n = (int64_t)d->n_idx_heads * d->idx_dim;
+    double *qd = (double *)malloc((size_t)(n + d->idx_dim) * sizeof *qd);
+    if (qd)
+        for (int64_t i = 0; i < n; ++i)
+            qd[i] = bf16_value(qi_row[i]);
+    return qd;
 }
 
 int qsa_ref_row_scores(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
@@ -224,9 +242,13 @@ int qsa_ref_row_scores(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
     row_pos p = locate_row(d, batch, cu_q, cu_k, row);
     int64_t nv = visible_blocks(d, p.t);
     const int64_t Hi = d->n_idx_heads, Di = d->idx_dim;
+    double *qd = widen_row(d, q_idx + row * Hi * Di);
+    if (!qd)
+        return -1;
     for (int64_t blk = 0; blk < nv; ++blk)
-        scores[blk] = block_score(d, q_idx + row * Hi * Di, w + row * Hi,
-                                  k_blk + (p.blk0 + blk) * Di);
+        scores[blk] = block_score(d, qd, w + row * Hi, k_blk + (p.blk0 + blk) * Di,
+                                  qd + Hi * Di);
+    free(qd);
     *n_out = nv;
     return 0;
 }
@@ -238,7 +260,7 @@ typedef struct {
     int32_t blk;
 } scored_block;
 
-/* Reading R3: higher score first; equal scores go to the lower block index. */
+/* Reading R4: higher score first; equal scores go to the lower block index. */
 static int by_score_then_index(const void *a, const void *b)
 {
     const scored_block *x = (const scored_block *)a, *y = (const scored_block *)b;
@@ -253,10 +275,11 @@ static int by_index(const void *a, const void *b)
     return (x > y) - (x < y);
 }
 
-/* Keep the budget of best blocks: "the published budget is 512 blocks,
- * corresponding to 2,048 tokens" (elzobrito.github.io). A query with no more
- * visible blocks than the budget keeps all of them. The kept ids are written in
- * ascending order and the row is padded with -1. */
+/* Keep the budget of best blocks: the pages give the budget as 512 blocks, i.e.
+ * 2,048 tokens per query (elzobrito.github.io, "Linear attention carries the stream;
+ * sparse attention retrieves detail"). Reading R11: a query with no more visible
+ * blocks than the budget keeps all of them. The kept ids are written in ascending
+ * order and the row is padded with -1. */
 static void select_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q,
                        const int32_t *cu_k, const uint16_t *q_idx, const float *w,
                        const uint16_t *k_blk, int64_t row, int32_t *sel_row)
@@ -270,11 +293,13 @@ static void select_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
             sel_row[i] = (int32_t)i;
     } else {
         scored_block *c = (scored_block *)malloc((size_t)nv * sizeof *c);
+        double *qd = widen_row(d, q_idx + row * Hi * Di);
         for (int64_t blk = 0; blk < nv; ++blk) {
-            c[blk].s = block_score(d, q_idx + row * Hi * Di, w + row * Hi,
-                                   k_blk + (p.blk0 + blk) * Di);
+            c[blk].s = block_score(d, qd, w + row * Hi, k_blk + (p.blk0 + blk) * Di,
+                                   qd + Hi * Di);
             c[blk].blk = (int32_t)blk;
         }
+        free(qd);
         qsort(c, (size_t)nv, sizeof *c, by_score_then_index);
         for (int64_t i = 0; i < k; ++i)
             sel_row[i] = c[i].blk;
@@ -288,12 +313,12 @@ static void select_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
 /* ------------------------------------------------------------- step 4 */
 
 /* Attention of one query row. Keys: the tokens of the kept blocks, in ascending
- * order, then the raw tokens after the last complete block (reading R4: the last,
- * incomplete block is attended without compression, elzobrito.github.io). A row's
- * selection is read up to its first negative entry; entries naming a block that is not
- * visible at t (b >= nvis(t): reading R6, only complete blocks at or before t are
- * candidates) are not attended, so a selection supplied from outside can never reach
- * past the row's position. Query head
+ * order, then the raw tokens after the last complete block (readings R5 and R6: the
+ * last, incomplete block is attended without compression, elzobrito.github.io). A
+ * row's selection is read up to its first negative entry; entries naming a block that
+ * is not visible at t (b >= nvis(t): reading R6, only complete blocks at or before t
+ * are candidates) are not attended, so a selection supplied from outside can never
+ * reach past the row's position. Query head
  * h reads key/value head h / (Hq/Hkv): the 24 query heads share 2 key/value heads
  * (axbrief.com, "Shifting from Tokens to Micro-Blocks"), twelve per KV head
  * (blog.compendialabs.org, "Qwen Sparse Attention -- Full Attention When It
@@ -342,15 +367,28 @@ static void attend_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
     for (int64_t j = nv * bs; j <= p.t; ++j)
         J[n++] = j;
 
+    /* the attended K and V rows of a key/value head, widened once for the query heads
+     * that read it */
     double *z = (double *)malloc((size_t)nj * sizeof *z);
+    double *kd = (double *)malloc((size_t)(nj * D + 1) * sizeof *kd);
+    double *vd = (double *)malloc((size_t)(nj * D + 1) * sizeof *vd);
+    int64_t g_wide = -1;
     for (int64_t h = 0; h < Hq; ++h) {
         int64_t g = h / (Hq / Hkv);
+        if (g != g_wide) {
+            for (int64_t i = 0; i < nj; ++i)
+                for (int64_t c = 0; c < D; ++c) {
+                    kd[i * D + c] = kv_value(k, p.key0 + J[i], g, Hkv, D, c);
+                    vd[i * D + c] = kv_value(v, p.key0 + J[i], g, Hkv, D, c);
+                }
+            g_wide = g;
+        }
         const uint16_t *qh = q + (row * Hq + h) * D;
         double m = -INFINITY;
         for (int64_t i = 0; i < nj; ++i) {
             double dot = 0.0;
             for (int64_t c = 0; c < D; ++c)
-                dot += bf16_value(qh[c]) * kv_value(k, p.key0 + J[i], g, Hkv, D, c);
+                dot += bf16_value(qh[c]) * kd[i * D + c];
             z[i] = dot * scale;
             if (z[i] > m)
                 m = z[i];
@@ -365,12 +403,14 @@ static void attend_row(const qsa_ref_dims *d, int32_t batch, const int32_t *cu_q
             o[c] = 0.0;
         for (int64_t i = 0; i < nj; ++i)
             for (int64_t c = 0; c < D; ++c)
-                o[c] += z[i] * kv_value(v, p.key0 + J[i], g, Hkv, D, c);
+                o[c] += z[i] * vd[i * D + c];
         for (int64_t c = 0; c < D; ++c)
             o[c] /= l;
         if (lse_row)
             lse_row[h] = m + log(l);
     }
+    free(vd);
+    free(kd);
     free(z);
     free(J);
 }
@@ -389,14 +429,14 @@ typedef struct {
     const int32_t *sel_r;
     double *out, *lse;
     const int64_t *rows;
-    int64_t lo, hi;
+    int64_t lo, hi, step;
 } row_job;
 
 static void *run_rows(void *arg)
 {
     row_job *j = (row_job *)arg;
     const int64_t kb = j->d->topk_blocks, Hq = j->d->n_q_heads, D = j->d->head_dim;
-    for (int64_t i = j->lo; i < j->hi; ++i) {
+    for (int64_t i = j->lo; i < j->hi; i += j->step) {
         int64_t r = j->rows ? j->rows[i] : i;
         if (j->op == 0)
             select_row(j->d, j->batch, j->cu_q, j->cu_k, j->q_idx, j->w, j->k_blk, r,
@@ -421,8 +461,9 @@ static void for_rows(row_job proto, int64_t n_rows, int32_t n_threads)
     row_job jobs[256];
     for (int32_t i = 0; i < n_threads; ++i) {
         jobs[i] = proto;
-        jobs[i].lo = n_rows * i / n_threads;
-        jobs[i].hi = n_rows * (i + 1) / n_threads;
+        jobs[i].lo = i;             /* rows i, i + n_threads, ...: costs grow with t */
+        jobs[i].hi = n_rows;
+        jobs[i].step = n_threads;
     }
     for (int32_t i = 1; i < n_threads; ++i)
         pthread_create(&tid[i], NULL, run_rows, &jobs[i]);
