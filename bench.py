@@ -387,7 +387,7 @@ def run_prefill(args, torch, qsa, gen):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / n
-    with qsa.trace(64) as tr:
+    with qsa.trace(4096) as tr:
         step()
     torch.cuda.synchronize()
     # algorithmic work: attended (query, key) pairs and scored (query, block) pairs
@@ -400,7 +400,7 @@ def run_prefill(args, torch, qsa, gen):
             scored += nv if nv > TOPK else 0
     att_flop = pairs * HQ * D * 4
     score_flop = scored * HI * DI * 2
-    km = tr.mean_ms()
+    km = tr.total_ms()   # score and select run once per pass of score tiles
     att_ms = km.get("attend", float("nan")) + km.get("combine", 0.0)
     fp8 = None
     if not args.no_fp8:
@@ -421,10 +421,10 @@ def run_prefill(args, torch, qsa, gen):
             step8()
         torch.cuda.synchronize()
         ms8 = (time.perf_counter() - t0) * 1e3 / n
-        with qsa.trace(64) as tr8:
+        with qsa.trace(4096) as tr8:
             step8()
         torch.cuda.synchronize()
-        km8 = tr8.mean_ms()
+        km8 = tr8.total_ms()
         att8 = km8.get("attend", float("nan")) + km8.get("combine", 0.0)
         fp8 = {"ms_per_step": round(ms8, 3),
                "query_tokens_per_s": round(seqs.n_q / (ms8 / 1e3), 1),

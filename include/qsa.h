@@ -126,6 +126,22 @@ qsa_status qsa_select(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16
                       const float *w, const qsa_bf16 *k_blk, int32_t *sel, void *ws,
                       size_t ws_bytes, void *stream);
 
+/* The indexer scores alone, for the listed query rows: the scoring half of
+ * qsa_select (the small MQA indexer of aiany.app, "Key Capabilities", scoring the
+ * compressed key blocks of elzobrito.github.io, "Linear attention carries the stream;
+ * sparse attention retrieves detail"), computed by the same MFMA code (bf16 products,
+ * fp32 sums; exact when the indexer data are small integers).
+ *   rows    DEVICE int64 [n_rows]: query rows, each in [0, Tq)
+ *   scores  DEVICE fp32 [n_rows, ld], row-major: scores[i][b] = s[t,b] =
+ *           sum_h w[t,h] * relu(q_idx[t,h] . K^[b]) for the visible blocks b < nvis(t)
+ *           of row rows[i] (a score of -0 is written as +0), -INFINITY for
+ *           nvis(t) <= b < ld; a row id outside [0, Tq) gets NaN in every column.
+ * ld must be at least the largest floor(L_b/4) (QSA_ERR_SHAPE otherwise); n_rows in
+ * [0, INT32_MAX]. k_blk must hold the listed rows' visible blocks. No workspace. */
+qsa_status qsa_score(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q_idx,
+                     const float *w, const qsa_bf16 *k_blk, const int64_t *rows, int64_t n_rows,
+                     float *scores, int64_t ld, void *stream);
+
 /* Grouped-query attention of every query row over the tokens of its selected blocks
  * plus its raw tail (24 query heads paired with 2 KV heads, axbrief.com "Shifting
  * from Tokens to Micro-Blocks"; blog.compendialabs.org "Qwen Sparse Attention --
@@ -137,7 +153,13 @@ qsa_status qsa_attend(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16
                       const qsa_bf16 *k, const qsa_bf16 *v, const int32_t *sel, float *out,
                       float *lse, void *ws, size_t ws_bytes, void *stream);
 
-/* The whole layer step: compress -> select -> attend on one stream.
+/* The whole layer step of the pages' sparse attention, compress -> select -> attend
+ * on one stream: compressed key blocks scored by the MQA indexer, the best 512 blocks
+ * (2,048 tokens) kept while the final incomplete block stays raw (elzobrito.github.io,
+ * "Linear attention carries the stream; sparse attention retrieves detail"; aiany.app,
+ * "Key Capabilities"), then attention of the 24 query heads over 2 KV heads on the kept
+ * tokens (axbrief.com, "Shifting from Tokens to Micro-Blocks"; blog.compendialabs.org,
+ * "Qwen Sparse Attention -- Full Attention When It Counts").
  * If k_idx is not NULL, the blocks that contain at least one query token
  * (blocks floor((L_b - q_b)/4) .. floor(L_b/4)-1 of each sequence) are (re)compressed
  * from k_idx into k_blk first; earlier blocks must already be valid in k_blk (a cache

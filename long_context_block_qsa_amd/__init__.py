@@ -53,6 +53,8 @@ _SIGS = {
                             ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "qsa_compress": ([ctypes.c_void_p] * 5, ctypes.c_int),
     "qsa_select": ([ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "qsa_score": ([ctypes.c_void_p] * 6 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_void_p], ctypes.c_int),
     "qsa_attend": ([ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "qsa_forward": ([ctypes.c_void_p] * 13 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "qsa_quantize_kv": ([ctypes.c_void_p] * 9, ctypes.c_int),
@@ -188,6 +190,21 @@ def select(seqs: Seqs, q_idx, w, k_blk, sel, ws, topk: int = KMAX, stream=None):
                             _ptr(sel, "sel", 4, (seqs.n_q, topk)),
                             _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
            "qsa_select")
+
+
+def score(seqs: Seqs, q_idx, w, k_blk, rows, scores, topk: int = KMAX, stream=None):
+    """Indexer scores of the query rows listed in ``rows`` (int64 device tensor) into
+    ``scores`` [len(rows), ld] fp32 (-inf past a row's visible blocks)."""
+    d = make_dims(topk)
+    if rows.dtype.itemsize != 8 or scores.dim() != 2 or scores.shape[0] != rows.numel():
+        raise ValueError("rows: int64 [n]; scores: fp32 [n, ld]")
+    _check(lib().qsa_score(ctypes.byref(d), ctypes.byref(seqs.c),
+                           _ptr(q_idx, "q_idx", 2, (seqs.n_q, HI, DI)),
+                           _ptr(w, "w", 4, (seqs.n_q, HI)),
+                           _ptr(k_blk, "k_blk", 2, (seqs.n_blocks, DI)),
+                           _ptr(rows, "rows", 8), rows.numel(), _ptr(scores, "scores", 4),
+                           scores.shape[1], _stream(stream)),
+           "qsa_score")
 
 
 def attend(seqs: Seqs, q, k, v, sel, out, lse, ws, topk: int = KMAX, softmax_scale=0.0,

@@ -68,6 +68,21 @@ int64_t h_first_scored_pos(int64_t L, int64_t nq, int64_t topk) {
     return std::max(L - nq, 4 * topk + 3);
 }
 
+// Prefill-shaped calls select in passes: a pass is a run of whole score tiles (with the
+// rows they cover and the unscored rows before them) whose score keys fit kKeyBudget
+// slots. Each pass is scored, then selected, before the next one reuses the keys
+// buffer, so the workspace does not grow with the square of the context and the
+// select re-reads keys that the Infinity Cache still holds.
+constexpr int64_t kKeyBudget = int64_t(1) << 25;   // slots (uint32 keys): 128 MiB
+
+struct Pass {
+    int64_t tile_lo = 0, tile_hi = 0;   // score tiles
+    int64_t row_lo = 0, row_hi = 0;     // query rows selected after the pass is scored
+    int64_t slot_lo = 0, slot_hi = 0;   // score slots (keys[s - slot_lo])
+    int64_t max_blocks = 0;             // most blocks a row of the pass sees
+    int64_t chunk = 0;                  // blocks per scoring workgroup
+};
+
 struct Plan {
     int batch = 0;
     int topk = 0;
@@ -78,7 +93,6 @@ struct Plan {
     int64_t max_score_blocks = 0;
     int64_t max_cmp_full = 0;   // most complete blocks in a sequence
     int64_t max_cmp_incr = 0;   // most blocks holding a query token
-    int64_t score_chunk = 0;    // blocks per score workgroup (whole-row path)
     int local_ch = 0;           // > 0: decode path, blocks per chunk
     int max_chunks = 0;         // chunks of the longest scored row (decode path)
     int nsplit = 1;             // attention key splits per row
@@ -90,7 +104,57 @@ struct Plan {
     bool fuse_compress = false; // decode: scoring workgroups compress the new blocks
     bool merge_launch = false;  // decode: some tile's rows are merged by their own launch
     qsa::DecodeTables dec;
+    std::vector<Pass> passes;   // prefill-shaped calls
+    int64_t pass_slots = 0;     // largest pass (slots of the keys buffer)
 };
+
+// Cuts the score tiles of a prefill-shaped call into passes of at most `budget` slots
+// (a single tile larger than the budget gets a pass of its own). Tiles, rows and
+// slots are numbered as on the device: sequences in order, a sequence's tiles cover
+// its rows at t >= first scored position, 4 rows each.
+qsa_status build_passes(const int32_t *cq, const int32_t *ck, int batch, int topk,
+                        int64_t budget, Plan *p) {
+    Pass cur;
+    int64_t tile = 0, slot = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t L = (int64_t)ck[b + 1] - ck[b], nq = (int64_t)cq[b + 1] - cq[b];
+        const int64_t ts = h_first_scored_pos(L, nq, topk);
+        for (int64_t t0 = ts; t0 < L; t0 += 4, ++tile) {
+            const int64_t nr = std::min<int64_t>(4, L - t0);
+            const int64_t row0 = cq[b] + (t0 - (L - nq));
+            const int64_t ns = h_slots_before(t0 + nr) - h_slots_before(t0);
+            if (cur.slot_hi > cur.slot_lo && cur.slot_hi - cur.slot_lo + ns > budget) {
+                cur.tile_hi = tile;
+                cur.row_hi = row0;
+                p->passes.push_back(cur);
+                cur = Pass();
+                cur.tile_lo = tile;
+                cur.row_lo = row0;
+                cur.slot_lo = cur.slot_hi = slot;
+            }
+            slot += ns;
+            cur.slot_hi = slot;
+            cur.max_blocks = std::max(cur.max_blocks, (t0 + nr) / qsa::BS);
+        }
+    }
+    cur.tile_hi = tile;
+    cur.row_hi = cq[batch];
+    p->passes.push_back(cur);
+    for (Pass &ps : p->passes) {
+        p->pass_slots = std::max(p->pass_slots, ps.slot_hi - ps.slot_lo);
+        const int64_t nt = ps.tile_hi - ps.tile_lo;
+        if (nt <= 0) continue;
+        // enough workgroups to fill the chip when the pass has few tiles
+        int64_t gy = std::max<int64_t>(1, (2048 + nt - 1) / nt);
+        gy = std::min<int64_t>(gy, std::max<int64_t>(1, ps.max_blocks / 256));
+        int64_t chunk = (ps.max_blocks + gy - 1) / gy;
+        chunk = (chunk + 63) / 64 * 64;
+        ps.chunk = chunk;
+        if ((ps.max_blocks + chunk - 1) / chunk > kMaxGridY || nt > INT32_MAX)
+            return QSA_ERR_UNSUPPORTED;
+    }
+    return QSA_OK;
+}
 
 // Row and tile tables of a call with at most DEC_MAX query rows and score tiles.
 void build_decode_tables(const int32_t *cq, const int32_t *ck, int batch, int topk,
@@ -201,14 +265,10 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
             p->merge_launch = (nv_max + ch - 1) / ch <= qsa::MERGE_CHUNKS;
         }
     }
-    // score grid: enough workgroups to fill the chip when few tiles exist
-    if (p->n_tiles > 0 && p->local_ch == 0) {
-        int64_t gy = std::max<int64_t>(1, (2048 + p->n_tiles - 1) / p->n_tiles);
-        gy = std::min<int64_t>(gy, std::max<int64_t>(1, p->max_score_blocks / 256));
-        int64_t chunk = (p->max_score_blocks + gy - 1) / gy;
-        chunk = (chunk + 63) / 64 * 64;
-        p->score_chunk = chunk;
-        if ((p->max_score_blocks + chunk - 1) / chunk > kMaxGridY) return QSA_ERR_UNSUPPORTED;
+    // prefill-shaped calls: passes of whole score tiles under the key budget
+    if (cq && !p->use_dec) {
+        const qsa_status ps = build_passes(cq, ck, p->batch, p->topk, kKeyBudget, p);
+        if (ps != QSA_OK) return ps;
     }
     // attention splits: aim at ~1024 waves when rows are few
     if (p->tq > 0) {
@@ -222,7 +282,8 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     const size_t ctl_b = (size_t)qsa::CTL_WORDS * sizeof(uint32_t);
     const size_t tab_b = align_up((size_t)std::max(p->batch, 1) * sizeof(SeqInfo));
     const size_t sel_b = align_up((size_t)p->tq * (size_t)p->topk * sizeof(int32_t));
-    const size_t score_b = align_up((size_t)p->n_slots * sizeof(uint32_t));
+    const size_t score_b = align_up((size_t)(p->use_dec ? p->n_slots : p->pass_slots) *
+                                    sizeof(uint32_t));
     const size_t cand_b = p->local_ch > 0
         ? align_up((size_t)p->tq * p->max_chunks * kKP * 2 * sizeof(uint32_t)) : 0;
     // group merge results of rows with more than 64 chunks (at most 4 groups of topk)
@@ -287,17 +348,25 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
             QSA_TRY(qsa::launch_merge_dec(p.dec, p.tq, p.topk, q_idx, w, k_blk, keys, cand_key,
                                           cand_idx, p.local_ch, p.max_chunks, sel, st));
         if (p.n_dense > 0)
-            QSA_TRY(qsa::launch_select(tab, &p.dec, p.batch, p.topk, keys, cand_key, cand_idx,
-                                       p.local_ch, p.max_chunks, sel, p.tq, p.max_score_blocks,
-                                       1, st));
+            QSA_TRY(qsa::launch_select(tab, &p.dec, p.batch, p.topk, keys, 0, cand_key,
+                                       cand_idx, p.local_ch, p.max_chunks, sel, 0, p.tq, 1,
+                                       st));
         return QSA_OK;
     }
-    if (p.n_tiles > 0)
-        QSA_TRY(qsa::launch_score(tab, p.batch, p.topk, q_idx, w, k_blk, keys, p.n_tiles,
-                                  p.max_score_blocks, p.score_chunk, st));
-    QSA_TRY(qsa::launch_select(tab, p.use_dec ? &p.dec : nullptr, p.batch, p.topk, keys,
-                               cand_key, cand_idx, p.local_ch, p.max_chunks, sel, p.tq,
-                               p.max_score_blocks, 0, st));
+    if (p.use_dec) {   // decode-shaped call without scored rows
+        QSA_TRY(qsa::launch_select(tab, &p.dec, p.batch, p.topk, keys, 0, nullptr, nullptr, 0,
+                                   0, sel, 0, p.tq, 0, st));
+        return QSA_OK;
+    }
+    // prefill: score one pass of tiles into the keys buffer, select its rows, next pass
+    for (const Pass &ps : p.passes) {
+        if (ps.tile_hi > ps.tile_lo)
+            QSA_TRY(qsa::launch_score(tab, p.batch, p.topk, q_idx, w, k_blk, keys, ps.tile_lo,
+                                      ps.tile_hi - ps.tile_lo, ps.slot_lo, ps.max_blocks,
+                                      ps.chunk, st));
+        QSA_TRY(qsa::launch_select(tab, nullptr, p.batch, p.topk, keys, ps.slot_lo, nullptr,
+                                   nullptr, 0, 0, sel, ps.row_lo, ps.row_hi - ps.row_lo, 0, st));
+    }
     (void)s;
     return QSA_OK;
 }
@@ -483,6 +552,24 @@ qsa_status qsa_select(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16
         QSA_TRY(qsa::launch_prep(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, p.topk,
                                  ws_at<SeqInfo>(ws, p.off_tab), hs));
     return run_select(p, seqs, q_idx, w, nullptr, const_cast<qsa_bf16 *>(k_blk), sel, ws, hs);
+}
+
+qsa_status qsa_score(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q_idx,
+                     const float *w, const qsa_bf16 *k_blk, const int64_t *rows, int64_t n_rows,
+                     float *scores, int64_t ld, void *stream) {
+    Plan p;
+    qsa_status st = make_plan(dims, seqs, true, &p);
+    if (st != QSA_OK) return st;
+    if (n_rows < 0 || n_rows > INT32_MAX || ld < 0) return QSA_ERR_SHAPE;
+    if (n_rows == 0) return QSA_OK;
+    if (p.tq == 0 || ld < p.max_cmp_full) return QSA_ERR_SHAPE;
+    if (ld == 0) return QSA_OK;
+    if (!rows || !scores || !q_idx || !w || (p.max_cmp_full > 0 && !k_blk)) return QSA_ERR_NULL;
+    if (!aligned16(q_idx) || !aligned16(w) || (k_blk && !aligned16(k_blk)))
+        return QSA_ERR_SHAPE;
+    QSA_TRY(qsa::launch_score_rows(seqs->cu_q_dev, seqs->cu_k_dev, p.batch, rows, n_rows, q_idx,
+                                   w, k_blk, scores, ld, (hipStream_t)stream));
+    return QSA_OK;
 }
 
 qsa_status qsa_attend(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,

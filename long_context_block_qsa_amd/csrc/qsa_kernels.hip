@@ -8,6 +8,8 @@
 //   attend            sparse GQA attention over gathered micro-blocks (MFMA, online
 //                     softmax), split over keys when rows are few
 //   combine           log-sum-exp merge of the key splits
+#include <algorithm>
+
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -261,20 +263,22 @@ __device__ __forceinline__ void score_groups_lds(const ScoreLane &sl, const uint
 
 constexpr int SCORE_NT = 256;
 
-// Whole rows: grid x = tile, y = chunk of `chunk_blocks` blocks.
+// Whole rows: grid x = tile (tile_base + x), y = chunk of `chunk_blocks` blocks. The
+// keys of score slot s go to keys[s - slot_base]: a call scores its tiles in passes
+// whose keys fit one buffer, selecting each pass's rows before the next pass.
 __global__ void __launch_bounds__(SCORE_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
              const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
              const uint16_t *__restrict__ k_blk, uint32_t *__restrict__ keys,
-             int64_t chunk_blocks) {
-    const TileInfo ti = tile_info(tab, batch, topk, blockIdx.x);
+             int64_t chunk_blocks, int64_t tile_base, int64_t slot_base) {
+    const TileInfo ti = tile_info(tab, batch, topk, tile_base + blockIdx.x);
     const int64_t lo = (int64_t)blockIdx.y * chunk_blocks;
     const int64_t hi = min<int64_t>(ti.nv_max, lo + chunk_blocks);
     if (lo >= hi) return;
     const int g = lane_id() >> 4;
     const ScoreLane sl = score_lane_setup(
         q_idx, w, ti.row0, ti.nrows, ti.t0,
-        ti.s.s0 + slots_before(ti.t0 + g) - slots_before(ti.ts));
+        ti.s.s0 + slots_before(ti.t0 + g) - slots_before(ti.ts) - slot_base);
     const uint16_t *kb = k_blk + (int64_t)ti.s.blk0 * DI;
     const int c = lane_id() & 15;
     __shared__ __attribute__((aligned(16))) uint8_t tiles[SCORE_NT / WAVE][2 * SC_TILE];
@@ -286,6 +290,57 @@ score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
         for (int u = 0; u < SCORE_BATCH; ++u) {
             const int64_t blk = b0 + u * step + c;
             if (blk < hi && blk < sl.nv_row) keys[sl.slot + blk] = key[u];
+        }
+    }
+}
+
+// Scores of listed rows on their own (the scoring step without the selection): grid x =
+// listed row, y = chunk of `chunk_blocks` of the ld columns. The row's sequence comes
+// from cu_q, its first block row from a workgroup sum over cu_k. Visible blocks get the
+// fp32 score the selection ranks (the order key turned back into its float), columns
+// from nvis(t) to ld get -inf, and a listed row outside [0, Tq) gets NaN everywhere.
+__device__ __forceinline__ float key_score(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__global__ void __launch_bounds__(SCORE_NT)
+score_rows_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int batch,
+                  const int64_t *__restrict__ rows, const uint16_t *__restrict__ q_idx,
+                  const float *__restrict__ w, const uint16_t *__restrict__ k_blk,
+                  float *__restrict__ scores, int64_t ld, int64_t chunk_blocks) {
+    __shared__ int64_t red[SCORE_NT / WAVE + 1];
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[SCORE_NT / WAVE][2 * SC_TILE];
+    const int64_t i = blockIdx.x;
+    const int64_t lo = (int64_t)blockIdx.y * chunk_blocks;
+    const int64_t hi = min<int64_t>(ld, lo + chunk_blocks);
+    float *out = scores + i * ld;
+    const int64_t r = rows[i];
+    if (r < 0 || r >= cu_q[batch]) {   // uniform: a bad row id is reported, not followed
+        for (int64_t b = lo + threadIdx.x; b < hi; b += SCORE_NT) out[b] = __int_as_float(0x7fc00000);
+        return;
+    }
+    const int sb = find_seq(batch, r, [&](int j) { return (int64_t)cu_q[j]; });
+    int64_t part = 0;
+    for (int j = threadIdx.x; j < sb; j += SCORE_NT) part += (cu_k[j + 1] - cu_k[j]) / BS;
+    int64_t blk0;
+    (void)block_excl_scan<int64_t, SCORE_NT>(part, red, &blk0);
+    const int64_t L = cu_k[sb + 1] - cu_k[sb], nq = cu_q[sb + 1] - cu_q[sb];
+    const int64_t t = L - nq + (r - cu_q[sb]);
+    const int64_t nv = nvis_of(t);
+    for (int64_t b = max(lo, nv) + threadIdx.x; b < hi; b += SCORE_NT) out[b] = -INFINITY;
+    const int64_t shi = min(hi, nv);
+    if (lo >= shi) return;
+    const ScoreLane sl = score_lane_setup(q_idx, w, r, 1, t, 0);
+    const uint16_t *kb = k_blk + blk0 * DI;
+    const int g = lane_id() >> 4, c = lane_id() & 15;
+    constexpr int64_t step = 16 * (SCORE_NT / WAVE);
+    for (int64_t b0 = lo + 16 * (threadIdx.x / WAVE); b0 < shi; b0 += step * SCORE_BATCH) {
+        uint32_t key[SCORE_BATCH];
+        score_groups_lds<SCORE_BATCH>(sl, kb, b0, step, shi, key, tiles[threadIdx.x / WAVE]);
+#pragma unroll
+        for (int u = 0; u < SCORE_BATCH; ++u) {
+            const int64_t blk = b0 + u * step + c;
+            if (g == 0 && blk < shi) out[blk] = key_score(key[u]);
         }
     }
 }
@@ -319,7 +374,9 @@ __device__ __forceinline__ bool cand_eligible(int64_t nv, int topk, int ch) {
 struct SelectArgs {
     const SeqInfo *tab;
     int batch, topk;
-    const uint32_t *keys;
+    const uint32_t *keys;    // score slot s at keys[s - slot_base]
+    int64_t slot_base;
+    int64_t row_base;        // prefill: workgroup x selects row row_base + x
     const uint32_t *cand_key;
     const int32_t *cand_idx;
     int ch, max_chunks;  // ch = 0: no candidates
@@ -429,7 +486,7 @@ __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView r
         return;
     }
     if (a.dense_only) return;
-    select_keys<16>(a.keys + rv.slot, nv, a.topk, out, hist, scan_sh, found);
+    select_keys<16>(a.keys + (rv.slot - a.slot_base), nv, a.topk, out, hist, scan_sh, found);
 }
 
 struct LocalArgs {
@@ -821,7 +878,7 @@ select_kernel(SelectArgs a) {
     __shared__ uint32_t hist[kHistBins];
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
     __shared__ uint32_t found[2];
-    const int64_t row = blockIdx.x;
+    const int64_t row = a.row_base + blockIdx.x;
     select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, hist, scan_sh, found);
 }
 
@@ -1308,13 +1365,30 @@ hipError_t launch_compress(const int32_t *cu_q, const int32_t *cu_k, int batch,
 
 hipError_t launch_score(const SeqInfo *tab, int batch, int topk, const uint16_t *q_idx,
                         const float *w, const uint16_t *k_blk, uint32_t *keys,
-                        int64_t n_tiles, int64_t max_blocks, int64_t chunk_blocks,
-                        hipStream_t st) {
+                        int64_t tile_base, int64_t n_tiles, int64_t slot_base,
+                        int64_t max_blocks, int64_t chunk_blocks, hipStream_t st) {
     if (n_tiles <= 0) return hipSuccess;
     const int64_t gy = (max_blocks + chunk_blocks - 1) / chunk_blocks;
     trace_before(2, st);
     hipLaunchKernelGGL(score_kernel, dim3((unsigned)n_tiles, (unsigned)gy), dim3(SCORE_NT), 0, st,
-                       tab, batch, topk, q_idx, w, k_blk, keys, chunk_blocks);
+                       tab, batch, topk, q_idx, w, k_blk, keys, chunk_blocks, tile_base,
+                       slot_base);
+    return trace_after(st, hipGetLastError());
+}
+
+hipError_t launch_score_rows(const int32_t *cu_q, const int32_t *cu_k, int batch,
+                             const int64_t *rows, int64_t n_rows, const uint16_t *q_idx,
+                             const float *w, const uint16_t *k_blk, float *scores, int64_t ld,
+                             hipStream_t st) {
+    if (n_rows <= 0 || ld <= 0) return hipSuccess;
+    int64_t gy = std::max<int64_t>(1, (2048 + n_rows - 1) / n_rows);
+    gy = std::min<int64_t>(gy, std::max<int64_t>(1, ld / 256));
+    int64_t chunk = (ld + gy - 1) / gy;
+    chunk = (chunk + 63) / 64 * 64;
+    gy = (ld + chunk - 1) / chunk;
+    trace_before(2, st);
+    hipLaunchKernelGGL(score_rows_kernel, dim3((unsigned)n_rows, (unsigned)gy), dim3(SCORE_NT), 0,
+                       st, cu_q, cu_k, batch, rows, q_idx, w, k_blk, scores, ld, chunk);
     return trace_after(st, hipGetLastError());
 }
 
@@ -1350,15 +1424,15 @@ hipError_t launch_merge_dec(const DecodeTables &d, int64_t n_rows, int topk,
 }
 
 hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
-                         const uint32_t *keys, const uint32_t *cand_key, const int32_t *cand_idx,
-                         int ch, int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
-                         int dense_only, hipStream_t st) {
+                         const uint32_t *keys, int64_t slot_base, const uint32_t *cand_key,
+                         const int32_t *cand_idx, int ch, int max_chunks, int32_t *sel,
+                         int64_t row_base, int64_t n_rows, int dense_only, hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
     SelectArgs a;
-    a.tab = tab; a.batch = batch; a.topk = topk; a.keys = keys;
+    a.tab = tab; a.batch = batch; a.topk = topk; a.keys = keys; a.slot_base = slot_base;
+    a.row_base = row_base;
     a.cand_key = cand_key; a.cand_idx = cand_idx; a.ch = ch; a.max_chunks = max_chunks;
     a.sel = sel; a.dense_only = dense_only;
-    (void)max_nvis;
     trace_before(3, st);
     if (d)
         hipLaunchKernelGGL(select_dec_kernel, dim3((unsigned)n_rows), dim3(SEL_NT), 0, st, a, *d);

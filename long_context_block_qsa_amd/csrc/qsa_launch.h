@@ -27,10 +27,17 @@ hipError_t launch_prep(const int32_t *cu_q, const int32_t *cu_k, int batch, int 
 hipError_t launch_compress(const int32_t *cu_q, const int32_t *cu_k, int batch,
                            int64_t max_blocks, const uint16_t *k_idx, uint16_t *k_blk,
                            int incremental, SeqInfo *tab, int topk, hipStream_t st);
+// Prefill scoring of tiles [tile_base, tile_base + n_tiles); slot s goes to
+// keys[s - slot_base].
 hipError_t launch_score(const SeqInfo *tab, int batch, int topk, const uint16_t *q_idx,
                         const float *w, const uint16_t *k_blk, uint32_t *keys,
-                        int64_t n_tiles, int64_t max_blocks, int64_t chunk_blocks,
-                        hipStream_t st);
+                        int64_t tile_base, int64_t n_tiles, int64_t slot_base,
+                        int64_t max_blocks, int64_t chunk_blocks, hipStream_t st);
+// Scores of the listed rows (fp32, -inf past the row's visible blocks), [n_rows, ld].
+hipError_t launch_score_rows(const int32_t *cu_q, const int32_t *cu_k, int batch,
+                             const int64_t *rows, int64_t n_rows, const uint16_t *q_idx,
+                             const float *w, const uint16_t *k_blk, float *scores, int64_t ld,
+                             hipStream_t st);
 hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
                               const uint16_t *q_idx, const float *w, const uint16_t *k_idx,
                               uint16_t *k_blk, uint32_t *keys, uint32_t *cand_key,
@@ -43,10 +50,12 @@ hipError_t launch_merge_dec(const DecodeTables &d, int64_t n_rows, int topk,
                             const uint16_t *q_idx, const float *w, uint16_t *k_blk,
                             uint32_t *keys, uint32_t *cand_key, int32_t *cand_idx, int ch,
                             int max_chunks, int32_t *sel, hipStream_t st);
+// Selection of rows [row_base, row_base + n_rows) (decode tables: rows 0..n_rows-1)
+// from their score keys (slot s at keys[s - slot_base]).
 hipError_t launch_select(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
-                         const uint32_t *keys, const uint32_t *cand_key, const int32_t *cand_idx,
-                         int ch, int max_chunks, int32_t *sel, int64_t n_rows, int64_t max_nvis,
-                         int dense_only, hipStream_t st);
+                         const uint32_t *keys, int64_t slot_base, const uint32_t *cand_key,
+                         const int32_t *cand_idx, int ch, int max_chunks, int32_t *sel,
+                         int64_t row_base, int64_t n_rows, int dense_only, hipStream_t st);
 // Decode rows whose tile's chunks fit one merge, merged by the attention workgroups
 // themselves (each workgroup of a row merges its candidates into LDS first).
 struct AttnMerge {

@@ -226,6 +226,8 @@ WORKLOADS = {
     "prefill_ragged_65535_40001_8190_3": dict(seed=1004, lens=[65535, 40001, 8190, 3],
                                               qkv_scale=0.5, outlier_frac=0.05,
                                               outlier_mul=8.0),
+    # one prefill at the native context (values as prefill_1x1024)
+    "prefill_1x262144": dict(seed=1005, lens=[262144]),
 }
 
 

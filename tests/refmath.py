@@ -1,4 +1,5 @@
-"""Independent numpy/scipy formulations used to pin the oracle (tests only).
+"""Independent numpy/scipy formulations used to pin the oracle, and the row samplers
+of the parity tests (tests only).
 
 Each function restates a special case through a library routine: masked softmax
 attention through scipy's ``softmax``/``logsumexp`` on dense matrices, block keys
@@ -74,3 +75,20 @@ def supplied_selection(ts, topk, seed):
         sel[i, :len(row)] = row
         clean[i, :len(vis)] = vis
     return sel, clean
+
+
+def stratified_rows(cu_q, cu_k, every=64, edge=8, boundary=(2040, 2062)):
+    """Every `every`-th query row, plus each sequence's first and last `edge` rows and
+    the rows around the dense/sparse boundary (positions 2,040..2,061: 2,051 is the
+    first position with more visible blocks than the 512-block budget)."""
+    rows = set(range(0, int(cu_q[-1]), every))
+    for b in range(len(cu_q) - 1):
+        lo, hi = int(cu_q[b]), int(cu_q[b + 1])
+        L = int(cu_k[b + 1] - cu_k[b])
+        rows.update(range(lo, min(hi, lo + edge)))
+        rows.update(range(max(lo, hi - edge), hi))
+        for t in range(*boundary):
+            r = lo + t - (L - (hi - lo))
+            if lo <= r < hi:
+                rows.add(r)
+    return sorted(rows)

@@ -29,7 +29,8 @@ def _ws(dims, seqs):
 def test_exports_every_declared_symbol():
     names = qsa.header_functions()
     assert set(names) == {"qsa_abi_version", "qsa_status_string", "qsa_workspace_size",
-                          "qsa_compress", "qsa_select", "qsa_attend", "qsa_forward",
+                          "qsa_compress", "qsa_select", "qsa_score", "qsa_attend",
+                          "qsa_forward",
                           "qsa_quantize_kv", "qsa_attend_fp8", "qsa_forward_fp8",
                           "qsa_backward_workspace_size", "qsa_attend_backward",
                           "qsa_trace_begin", "qsa_trace_end", "qsa_kernel_name"}
@@ -225,3 +226,43 @@ def test_trace_end_without_begin_and_names():
     assert qsa.lib().qsa_kernel_name(13) == b"bwd_dkv"
     assert qsa.lib().qsa_kernel_name(42) == b"unknown"
     assert L.qsa_trace_begin(0) == qsa.QSA_ERR_SHAPE
+
+
+def test_prefill_workspace_bounded_by_key_budget():
+    """Prefill scores are kept one pass of score tiles at a time (at most 2^25 keys of
+    4 bytes), so the workspace of a 262,144-token or a 1,048,576-token prefill is the
+    selection (4 * 512 bytes per query row, linear in the length) plus at most 128 MiB
+    of keys, while the sum of its score slots (F(L) - F(2051)) would be 34 GB and
+    550 GB."""
+    d = qsa.make_dims(topk=512)
+    F = lambda t: 2 * (t // 4) * (t // 4 - 1) + (t // 4) * (t % 4 + 1)
+    for L in (65535, 262144, 1 << 20):
+        st, n = _ws(d, _seqs([0, L], [0, L]))
+        assert st == 0
+        assert n <= 4 * 512 * L + 4 * 2**25 + 2**20, (L, n)
+        if L >= 262144:
+            assert 4 * (F(L) - F(2051)) > 30 * n
+    # a call whose keys fit one pass keeps all of them (as before)
+    st, n = _ws(d, _seqs([0, 4096], [0, 4096]))
+    assert n >= 4 * (F(4096) - F(2051))
+
+
+def test_score_entry_point_validates_first():
+    """qsa_score: ld below the longest sequence's block count, no query rows, null or
+    misaligned operands are refused before any device call."""
+    d = qsa.make_dims()
+    L = qsa.lib()
+    s = _seqs([0, 3], [0, 4001])            # 1000 complete blocks
+    f, odd = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 2)
+    call = lambda qi, w, kb, rows, n, sc, ld: L.qsa_score(ctypes.byref(d), ctypes.byref(s), qi,
+                                                           w, kb, rows, n, sc, ld, None)
+    assert call(f, f, f, f, 3, f, 999) == qsa.QSA_ERR_SHAPE
+    assert call(f, f, f, f, -1, f, 1000) == qsa.QSA_ERR_SHAPE
+    assert call(f, f, f, None, 3, f, 1000) == qsa.QSA_ERR_NULL
+    assert call(f, f, f, f, 3, None, 1000) == qsa.QSA_ERR_NULL
+    assert call(f, None, f, f, 3, f, 1000) == qsa.QSA_ERR_NULL
+    assert call(odd, f, f, f, 3, f, 1000) == qsa.QSA_ERR_SHAPE
+    assert call(None, None, None, None, 0, None, 0) == qsa.QSA_OK
+    empty = _seqs([0, 0], [0, 50])
+    assert L.qsa_score(ctypes.byref(d), ctypes.byref(empty), f, f, f, f, 1, f, 100,
+                       None) == qsa.QSA_ERR_SHAPE

@@ -11,7 +11,7 @@ import torch
 import long_context_block_qsa_amd as qsa
 import oracle
 import qsa_inputs as gen
-from tests.refmath import row_positions, supplied_selection
+from tests.refmath import row_positions, stratified_rows, supplied_selection
 from tests.gpu_helpers import LSE_ABS, MAX_ABS, MEAN_ABS, DeviceProblem, errs, host16
 
 pytestmark = pytest.mark.gpu
@@ -114,13 +114,33 @@ def test_decode_1x32768_needles():
     assert set(p.needles[0]) <= set(sel[0].tolist())
 
 
-def test_prefill_1x16384_sampled():
+def _check_all_selections(name, dp, attend_rows, topk=512, threads=None):
+    """Compressed keys and the selection of EVERY row bit-exact against the oracle;
+    out and lse on attend_rows (None: every row) within the forward's bars."""
+    p = dp.p
+    dims = oracle.Dims(topk_blocks=topk)
+    k_blk, sel, out, lse = dp.forward()
+    kb_r = oracle.compress(dims, p.cu_k, p.k_idx)
+    assert np.array_equal(k_blk, kb_r), f"{name}: compressed keys differ"
+    sel_r = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb_r, threads=threads)
+    bad = np.nonzero(~np.all(sel == sel_r, axis=1))[0]
+    assert bad.size == 0, f"{name}: selection differs on {bad.size} rows, first {bad[:10]}"
+    out_r, lse_r = oracle.attend(dims, p.cu_q, p.cu_k, p.q, p.k, p.v, sel_r, rows=attend_rows,
+                                 threads=threads)
+    rows = np.arange(p.n_q) if attend_rows is None else np.asarray(attend_rows)
+    mx, mean = errs(out[rows], out_r[rows])
+    lmx, _ = errs(lse[rows], lse_r[rows])
+    print(f"[{name}] selections: all {p.n_q} rows equal; attention rows={len(rows)} "
+          f"max_abs={mx:.3e} mean_abs={mean:.3e} lse={lmx:.3e}", flush=True)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and lmx <= LSE_ABS
+    return sel, out
+
+
+def test_prefill_1x16384_all_rows():
+    """Every one of the 16,384 rows: selection bit-exact, out and lse within the bars."""
     _banner("prefill 1x16384")
     p = gen.workload_problem("prefill_1x16384")
-    rows = sorted(set([0, 1, 2, 3, 4, 2047, 2048, 2049, 2050, 2051, 2052, 2053, 2054, 2055]
-                      + list(range(16384 - 40, 16384))
-                      + np.random.default_rng(2).integers(0, 16384, 200).tolist()))
-    _check_rows("prefill-1x16384", DeviceProblem(p), rows, 512)
+    _check_all_selections("prefill-1x16384", DeviceProblem(p), None)
 
 
 def test_decode_16x262144_full():
@@ -139,22 +159,64 @@ def test_decode_multi_query_16x262144_full():
     _check_rows("decode-16x262144-4q", DeviceProblem(p), None, 512)
 
 
-def test_prefill_ragged_64k_sampled():
+def test_prefill_ragged_64k_all_selections():
+    """Selections of all 113,729 rows bit-exact; out and lse on every 56th row plus each
+    sequence's ends and its dense/sparse boundary (over 2,000 rows)."""
     _banner("ragged prefill 65535/40001/8190/3")
     p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
-    cu = p.cu_q
-    rng = np.random.default_rng(4)
-    rows = set()
-    for b in range(4):
-        lo, hi = int(cu[b]), int(cu[b + 1])
-        rows.update(range(lo, min(hi, lo + 6)))
-        rows.update(range(max(lo, hi - 6), hi))
-        for t in (2049, 2050, 2051, 2052):
-            if lo + t < hi:
-                rows.add(lo + t)
-        if hi - lo > 10:
-            rows.update(rng.integers(lo, hi, 60).tolist())
-    _check_rows("ragged-64k", DeviceProblem(p), sorted(rows), 512)
+    rows = stratified_rows(p.cu_q, p.cu_k, every=56)
+    assert len(rows) >= 2000
+    _check_all_selections("ragged-64k", DeviceProblem(p), rows)
+
+
+def test_prefill_1x262144_bounded_workspace():
+    """One prefill at the native context, 262,144 tokens: its 8.6e9 score slots (34 GB
+    of keys if kept whole) are scored and selected in passes of at most 2^25 keys, in a
+    workspace of the selection plus 128 MiB. 300 rows (spread over the sequence, its
+    last rows and the dense/sparse boundary): selections bit-exact, out and lse within
+    the bars."""
+    _banner("prefill 1x262144")
+    L = 262144
+    p = gen.workload_problem("prefill_1x262144")
+    dp = DeviceProblem(p)
+    assert dp.ws.numel() <= 4 * 512 * L + 4 * 2**25 + 2**20
+    rows = sorted(set(np.linspace(0, L - 1, 268).astype(int).tolist())
+                  | set(range(2044, 2060)) | set(range(L - 16, L)))
+    _check_rows("prefill-1x262144", dp, rows, 512)
+
+
+def test_indexer_scores_bit_exact():
+    """qsa_score on whole rows: with integer indexer data every fp32 score is exact, so
+    the GPU's scores equal the oracle's double scores bit for bit (-inf past the row's
+    visible blocks). Rows of the ragged prefill (each sequence's last row, rows at the
+    dense/sparse boundary and inside, the length-3 sequence with no blocks) and all 16
+    decode rows at 262,144 tokens (65,536 blocks each)."""
+    _banner("indexer scores")
+    dims = oracle.Dims()
+    cases = []
+    p4 = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
+    cu = p4.cu_q
+    rows4 = [int(cu[1]) - 1, int(cu[2]) - 1, int(cu[3]) - 1, int(cu[3]), int(cu[4]) - 1,
+             2050, 2051, 30000, int(cu[1]) + 12345, int(cu[2]) + 4099]
+    cases.append(("ragged-64k", p4, rows4))
+    p3 = gen.workload_problem("decode_16x262144")
+    cases.append(("decode-16x262144", p3, list(range(16))))
+    for name, p, rows in cases:
+        dp = DeviceProblem(p)
+        ld = int((np.diff(p.cu_k.astype(np.int64)) // 4).max()) + 3
+        rows_d = torch.tensor(rows, dtype=torch.int64, device="cuda")
+        sc = torch.full((len(rows), ld), 7.0, dtype=torch.float32, device="cuda")
+        qsa.score(dp.seqs, dp.q_idx, dp.w, dp.k_blk, rows_d, sc)
+        torch.cuda.synchronize()
+        got = sc.cpu().numpy()
+        kb = oracle.compress(dims, p.cu_k, p.k_idx)
+        for i, r in enumerate(rows):
+            ref = oracle.row_scores(dims, p.cu_q, p.cu_k, p.q_idx, p.w, kb, r)
+            n = ref.size
+            assert np.array_equal(got[i, :n].astype(np.float64), ref), \
+                f"{name}: scores of row {r} differ at {np.nonzero(got[i, :n] != ref)[0][:8]}"
+            assert np.all(np.isneginf(got[i, n:])), f"{name}: row {r} past its blocks"
+        print(f"[{name}] scores of {len(rows)} rows bit-exact", flush=True)
 
 
 # ----------------------------------------------------------------- long contexts
