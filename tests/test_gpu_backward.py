@@ -3,9 +3,10 @@
 The GPU forward gives sel, out and lse; the GPU backward takes those and a seeded bf16
 dout. The oracle selects on its own (the selections must be bit-identical) and
 differentiates its fp64 attention over that selection. Bars: dq, dk and dv within
-max-abs 2e-3 * s and mean-abs 2e-4 * s of the oracle's, with s = max(1, max |oracle|)
-per tensor (the forward's absolute bars, scaled when a gradient is larger than 1: the
-GPU sums in fp32, so its error grows with the magnitude of the sum).
+max-abs 5e-4 and mean-abs 2e-5 of the oracle's, absolute. Measured on every case here
+(gradients up to 25 in magnitude, sums of up to ~10^5 fp32 terms): max-abs at most
+1.0e-4 and mean-abs at most 6e-7, so the bars sit 5x and 30x above the worst measured
+errors and a regression of one order of magnitude fails.
 """
 import numpy as np
 import pytest
@@ -14,7 +15,7 @@ import torch
 import long_context_block_qsa_amd as qsa
 import oracle
 import qsa_inputs as gen
-from tests.gpu_helpers import MAX_ABS, MEAN_ABS, DeviceProblem, dev16, errs
+from tests.gpu_helpers import DeviceProblem, dev16, errs
 from tests.refmath import row_positions, supplied_selection
 
 pytestmark = pytest.mark.gpu
@@ -42,15 +43,17 @@ class BwdProblem(DeviceProblem):
         return self.dq.cpu().numpy(), self.dk.cpu().numpy(), self.dv.cpu().numpy()
 
 
+GRAD_MAX_ABS, GRAD_MEAN_ABS = 5e-4, 2e-5
+
+
 def _bars(name, got, ref, mask=None):
     if mask is not None:
         got, ref = got[mask], ref[mask]
-    s = max(1.0, float(np.abs(ref).max(initial=0.0)))
     mx, mean = errs(got, ref)
     print(f"[{name}] max|ref|={np.abs(ref).max(initial=0.0):.3e} max_abs={mx:.3e} "
           f"mean_abs={mean:.3e}", flush=True)
     assert np.isfinite(got).all(), f"{name}: non-finite values"
-    assert mx <= MAX_ABS * s and mean <= MEAN_ABS * s, name
+    assert mx <= GRAD_MAX_ABS and mean <= GRAD_MEAN_ABS, name
 
 
 def _check(name, bp):
