@@ -172,6 +172,23 @@ qsa_status qsa_forward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf1
                        const float *w, const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel,
                        float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): qsa_forward without a workspace
+ * argument. Its workspace is a scratch array of QSA_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * inside the library, one per GPU, held until the process ends; the call allocates
+ * nothing. Calls whose qsa_workspace_size exceeds that return QSA_ERR_WORKSPACE before
+ * any device call (a decode batch of 16 x 262,144 tokens needs under 8 MiB; a prefill
+ * needs its selection when sel is NULL plus its score keys). Every call on a GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller. The array's control block
+ * is zero before the first call and every call leaves it zero. Other arguments and
+ * results as qsa_forward. */
+#define QSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+qsa_status qsa_forward_noalloc(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                               const qsa_bf16 *k, const qsa_bf16 *v, const qsa_bf16 *q_idx,
+                               const float *w, const qsa_bf16 *k_idx, qsa_bf16 *k_blk,
+                               int32_t *sel, float *out, float *lse, void *stream);
+
 /* ---------------------------------------------------------------- FP8 KV cache
  * A storage variant of the attention's K and V (the pages' FP8 builds are of the
  * model, blog.compendialabs.org, "What This Means"; here FP8 halves the bytes the

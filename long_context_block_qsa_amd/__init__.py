@@ -57,6 +57,7 @@ _SIGS = {
                                            ctypes.c_void_p], ctypes.c_int),
     "qsa_attend": ([ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "qsa_forward": ([ctypes.c_void_p] * 13 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "qsa_forward_noalloc": ([ctypes.c_void_p] * 13, ctypes.c_int),
     "qsa_quantize_kv": ([ctypes.c_void_p] * 9, ctypes.c_int),
     "qsa_attend_fp8": ([ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "qsa_forward_fp8": ([ctypes.c_void_p] * 15 + [ctypes.c_size_t, ctypes.c_void_p],
@@ -238,6 +239,28 @@ def forward(seqs: Seqs, q, k, v, q_idx, w, k_idx, k_blk, sel, out, lse, ws, topk
                              _ptr(lse, "lse", 4, (seqs.n_q, HQ)),
                              _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
            "qsa_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_noalloc(seqs: Seqs, q, k, v, q_idx, w, k_idx, k_blk, sel, out, lse,
+                    topk: int = KMAX, softmax_scale=0.0, stream=None):
+    """forward() without a workspace: the library's per-GPU scratch array serves as the
+    workspace (calls needing more than NOALLOC_SCRATCH_BYTES are refused)."""
+    d = make_dims(topk, softmax_scale)
+    _check(lib().qsa_forward_noalloc(ctypes.byref(d), ctypes.byref(seqs.c),
+                                     _ptr(q, "q", 2, (seqs.n_q, HQ, D)),
+                                     _ptr(k, "k", 2, (seqs.n_k, HKV, D)),
+                                     _ptr(v, "v", 2, (seqs.n_k, HKV, D)),
+                                     _ptr(q_idx, "q_idx", 2, (seqs.n_q, HI, DI)),
+                                     _ptr(w, "w", 4, (seqs.n_q, HI)),
+                                     _ptr(k_idx, "k_idx", 2, (seqs.n_k, DI)),
+                                     _ptr(k_blk, "k_blk", 2, (seqs.n_blocks, DI)),
+                                     _ptr(sel, "sel", 4, (seqs.n_q, topk)),
+                                     _ptr(out, "out", 4, (seqs.n_q, HQ, D)),
+                                     _ptr(lse, "lse", 4, (seqs.n_q, HQ)), _stream(stream)),
+           "qsa_forward_noalloc")
 
 
 def quantize_kv(seqs: Seqs, k, v, k8, v8, k_scale, v_scale, stream=None):

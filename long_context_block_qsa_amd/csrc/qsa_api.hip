@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #pragma GCC visibility push(default)
@@ -493,6 +494,38 @@ qsa_status make_bwd_plan(const qsa_dims *d, const qsa_seqs *s, BwdPlan *bp) {
     return QSA_OK;
 }
 
+// ------------------------------------------------- scratch of qsa_forward_noalloc
+// The workspace of the no-allocation entry point: one array per GPU, part of the
+// library's code object (it exists on every device the library is loaded on, until
+// the process ends). In host code `scratch` only names the symbol: its device address
+// comes from hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[QSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // per device, guarded by g_scratch_mu
+
+// The current device's scratch address. On the first call for a device its control
+// block is cleared by a kernel on `st` (the array is zero when the code object is
+// loaded; the clear makes that explicit, and in a captured graph it is a kernel node).
+qsa_status noalloc_scratch(hipStream_t st, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QSA_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return QSA_ERR_DEVICE;
+        if (qsa::launch_zero_words(static_cast<uint32_t *>(ptr), qsa::CTL_WORDS, st) !=
+            hipSuccess)
+            return QSA_ERR_DEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return QSA_OK;
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -584,6 +617,23 @@ qsa_status qsa_forward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf1
                        float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
     return forward_common(dims, seqs, q, k, v, nullptr, q_idx, w, k_idx, k_blk, sel, out, lse,
                           ws, ws_bytes, stream);
+}
+
+qsa_status qsa_forward_noalloc(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
+                               const qsa_bf16 *k, const qsa_bf16 *v, const qsa_bf16 *q_idx,
+                               const float *w, const qsa_bf16 *k_idx, qsa_bf16 *k_blk,
+                               int32_t *sel, float *out, float *lse, void *stream) {
+    // the call's workspace must fit the scratch; checked before any device call
+    Plan p;
+    qsa_status st = make_plan(dims, seqs, true, &p);
+    if (st != QSA_OK) return st;
+    if (p.tq == 0) return QSA_OK;
+    if (p.ws_bytes > (size_t)QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_WORKSPACE;
+    if (!q || !out) return QSA_ERR_NULL;
+    void *ws = nullptr;
+    if ((st = noalloc_scratch((hipStream_t)stream, &ws)) != QSA_OK) return st;
+    return forward_common(dims, seqs, q, k, v, nullptr, q_idx, w, k_idx, k_blk, sel, out, lse,
+                          ws, (size_t)QSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 qsa_status qsa_quantize_kv(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *k,

@@ -1341,6 +1341,21 @@ hipError_t launch_quantize_kv(const uint16_t *k, const uint16_t *v, uint8_t *k8,
     return trace_after(st, hipGetLastError());
 }
 
+// =============================================================== zero fill
+// Clears n 32-bit words (a kernel rather than a memset, so that a launch recorded in
+// a HIP graph is a kernel node).
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t *__restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p,
+                       n);
+    return hipGetLastError();
+}
+
 // =============================================================== launchers
 
 hipError_t launch_prep(const int32_t *cu_q, const int32_t *cu_k, int batch, int topk,

@@ -90,6 +90,8 @@ hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, const int32
                            const int32_t *sel, const float *out, const float *lse,
                            const uint16_t *dout, float *dq, float *dk, float *dv,
                            const BwdBuffers &b, hipStream_t st);
+// Clears n 32-bit words with a kernel.
+hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t st);
 hipError_t launch_quantize_kv(const uint16_t *k, const uint16_t *v, uint8_t *k8, uint8_t *v8,
                               float *k_scale, float *v_scale, int64_t rows, hipStream_t st);
 

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
     names = qsa.header_functions()
     assert set(names) == {"qsa_abi_version", "qsa_status_string", "qsa_workspace_size",
                           "qsa_compress", "qsa_select", "qsa_score", "qsa_attend",
-                          "qsa_forward",
+                          "qsa_forward", "qsa_forward_noalloc",
                           "qsa_quantize_kv", "qsa_attend_fp8", "qsa_forward_fp8",
                           "qsa_backward_workspace_size", "qsa_attend_backward",
                           "qsa_trace_begin", "qsa_trace_end", "qsa_kernel_name"}
@@ -266,3 +266,22 @@ def test_score_entry_point_validates_first():
     empty = _seqs([0, 0], [0, 50])
     assert L.qsa_score(ctypes.byref(d), ctypes.byref(empty), f, f, f, f, 1, f, 100,
                        None) == qsa.QSA_ERR_SHAPE
+
+
+def test_noalloc_entry_point_validates_first():
+    """qsa_forward_noalloc refuses, before any device call, a call whose workspace would
+    exceed its scratch (QSA_ERR_WORKSPACE) and invalid arguments as qsa_forward does."""
+    d = qsa.make_dims()
+    L = qsa.lib()
+    f = ctypes.c_void_p(FAKE)
+    big = _seqs([0, 65535], [0, 65535])
+    assert _ws(d, big)[1] > qsa.NOALLOC_SCRATCH_BYTES
+    assert L.qsa_forward_noalloc(ctypes.byref(d), ctypes.byref(big), f, f, f, f, f, f, f, f, f,
+                                 f, None) == qsa.QSA_ERR_WORKSPACE
+    small = _seqs([0, 1], [0, 40])
+    assert L.qsa_forward_noalloc(ctypes.byref(d), ctypes.byref(small), None, f, f, f, f, f, f,
+                                 f, f, f, None) == qsa.QSA_ERR_NULL
+    bad = qsa.make_dims()
+    bad.head_dim = 64
+    assert L.qsa_forward_noalloc(ctypes.byref(bad), ctypes.byref(small), f, f, f, f, f, f, f,
+                                 f, f, f, None) == qsa.QSA_ERR_UNSUPPORTED
