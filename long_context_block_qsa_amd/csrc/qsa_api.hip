@@ -71,10 +71,10 @@ int64_t h_first_scored_pos(int64_t L, int64_t nq, int64_t topk) {
 
 // Prefill-shaped calls select in passes: a pass is a run of whole score tiles (with the
 // rows they cover and the unscored rows before them) whose score keys fit kKeyBudget
-// slots. Each pass is scored, then selected, before the next one reuses the keys
-// buffer, so the workspace does not grow with the square of the context and the
-// select re-reads keys that the Infinity Cache still holds.
-constexpr int64_t kKeyBudget = int64_t(1) << 25;   // slots (uint32 keys): 128 MiB
+// slots. Two key buffers alternate: one launch selects the rows of pass p from one
+// buffer while it scores pass p + 1 into the other, so the workspace does not grow
+// with the square of the context and no pass ends with its own tail.
+constexpr int64_t kKeyBudget = int64_t(1) << 25;   // slots (uint32 keys) per buffer: 128 MiB
 
 struct Pass {
     int64_t tile_lo = 0, tile_hi = 0;   // score tiles
@@ -283,8 +283,10 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     const size_t ctl_b = (size_t)qsa::CTL_WORDS * sizeof(uint32_t);
     const size_t tab_b = align_up((size_t)std::max(p->batch, 1) * sizeof(SeqInfo));
     const size_t sel_b = align_up((size_t)p->tq * (size_t)p->topk * sizeof(int32_t));
-    const size_t score_b = align_up((size_t)(p->use_dec ? p->n_slots : p->pass_slots) *
-                                    sizeof(uint32_t));
+    // prefill: two key buffers when there is more than one pass
+    const size_t score_b = p->use_dec
+        ? align_up((size_t)p->n_slots * sizeof(uint32_t))
+        : align_up((size_t)p->pass_slots * sizeof(uint32_t)) * (p->passes.size() > 1 ? 2 : 1);
     const size_t cand_b = p->local_ch > 0
         ? align_up((size_t)p->tq * p->max_chunks * kKP * 2 * sizeof(uint32_t)) : 0;
     // group merge results of rows with more than 64 chunks (at most 4 groups of topk)
@@ -359,14 +361,18 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
                                    0, sel, 0, p.tq, 0, st));
         return QSA_OK;
     }
-    // prefill: score one pass of tiles into the keys buffer, select its rows, next pass
-    for (const Pass &ps : p.passes) {
-        if (ps.tile_hi > ps.tile_lo)
-            QSA_TRY(qsa::launch_score(tab, p.batch, p.topk, q_idx, w, k_blk, keys, ps.tile_lo,
-                                      ps.tile_hi - ps.tile_lo, ps.slot_lo, ps.max_blocks,
-                                      ps.chunk, st));
-        QSA_TRY(qsa::launch_select(tab, nullptr, p.batch, p.topk, keys, ps.slot_lo, nullptr,
-                                   nullptr, 0, 0, sel, ps.row_lo, ps.row_hi - ps.row_lo, 0, st));
+    // prefill: launch i scores pass i into buffer i % 2 and selects the rows of pass
+    // i - 1 from buffer (i - 1) % 2
+    uint32_t *buf[2] = {keys, keys + align_up((size_t)p.pass_slots * sizeof(uint32_t)) / 4};
+    const size_t np = p.passes.size();
+    for (size_t i = 0; i <= np; ++i) {
+        const Pass *sc = i < np ? &p.passes[i] : nullptr;
+        const Pass *se = i > 0 ? &p.passes[i - 1] : nullptr;
+        QSA_TRY(qsa::launch_score_select(
+            tab, p.batch, p.topk, q_idx, w, k_blk, buf[i % 2], sc ? sc->tile_lo : 0,
+            sc ? sc->tile_hi - sc->tile_lo : 0, sc ? sc->slot_lo : 0, sc ? sc->max_blocks : 0,
+            sc ? sc->chunk : 1, buf[(i + 1) % 2], se ? se->slot_lo : 0, sel,
+            se ? se->row_lo : 0, se ? se->row_hi - se->row_lo : 0, st));
     }
     (void)s;
     return QSA_OK;
@@ -765,8 +771,8 @@ const char *qsa_kernel_name(int32_t kind) {
     static const char *names[] = {"prep",     "compress",    "score",    "select",
                                   "attend",   "combine",     "bwd_prep", "bwd_rows",
                                   "bwd_count", "bwd_colscan", "bwd_scan", "bwd_fill",
-                                  "bwd_dq",   "bwd_dkv"};
-    return (kind >= 0 && kind < 14) ? names[kind] : "unknown";
+                                  "bwd_dq",   "bwd_dkv",     "score_select"};
+    return (kind >= 0 && kind < 15) ? names[kind] : "unknown";
 }
 
 }  // extern "C"

@@ -263,29 +263,40 @@ __device__ __forceinline__ void score_groups_lds(const ScoreLane &sl, const uint
 
 constexpr int SCORE_NT = 256;
 
-// Whole rows: grid x = tile (tile_base + x), y = chunk of `chunk_blocks` blocks. The
-// keys of score slot s go to keys[s - slot_base]: a call scores its tiles in passes
-// whose keys fit one buffer, selecting each pass's rows before the next pass.
-__global__ void __launch_bounds__(SCORE_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
-score_kernel(const SeqInfo *__restrict__ tab, int batch, int topk,
-             const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
-             const uint16_t *__restrict__ k_blk, uint32_t *__restrict__ keys,
-             int64_t chunk_blocks, int64_t tile_base, int64_t slot_base) {
-    const TileInfo ti = tile_info(tab, batch, topk, tile_base + blockIdx.x);
-    const int64_t lo = (int64_t)blockIdx.y * chunk_blocks;
-    const int64_t hi = min<int64_t>(ti.nv_max, lo + chunk_blocks);
+// Whole rows of one tile, blocks [chunk * chunk_blocks, +chunk_blocks): keys of score
+// slot s go to keys[s - slot_base]. A call scores its tiles in passes whose keys fit one
+// buffer; a pass's rows are selected while the next pass is scored into the other one.
+struct ScorePass {
+    const SeqInfo *tab;
+    int batch, topk;
+    const uint16_t *q_idx;
+    const float *w;
+    const uint16_t *k_blk;
+    uint32_t *keys;
+    int64_t chunk_blocks, tile_base, slot_base;
+    int gy;   // chunks per tile
+};
+
+constexpr int SC_LDS_BYTES = (SCORE_NT / WAVE) * 2 * SC_TILE;
+
+__device__ __forceinline__ void score_tile_body(const ScorePass &sp, int64_t tile, int chunk,
+                                                uint8_t *smem) {
+    const TileInfo ti = tile_info(sp.tab, sp.batch, sp.topk, tile);
+    const int64_t lo = (int64_t)chunk * sp.chunk_blocks;
+    const int64_t hi = min<int64_t>(ti.nv_max, lo + sp.chunk_blocks);
     if (lo >= hi) return;
     const int g = lane_id() >> 4;
     const ScoreLane sl = score_lane_setup(
-        q_idx, w, ti.row0, ti.nrows, ti.t0,
-        ti.s.s0 + slots_before(ti.t0 + g) - slots_before(ti.ts) - slot_base);
-    const uint16_t *kb = k_blk + (int64_t)ti.s.blk0 * DI;
+        sp.q_idx, sp.w, ti.row0, ti.nrows, ti.t0,
+        ti.s.s0 + slots_before(ti.t0 + g) - slots_before(ti.ts) - sp.slot_base);
+    const uint16_t *kb = sp.k_blk + (int64_t)ti.s.blk0 * DI;
     const int c = lane_id() & 15;
-    __shared__ __attribute__((aligned(16))) uint8_t tiles[SCORE_NT / WAVE][2 * SC_TILE];
+    uint8_t *tiles = smem + (threadIdx.x / WAVE) * 2 * SC_TILE;
+    uint32_t *keys = sp.keys;
     constexpr int64_t step = 16 * (SCORE_NT / WAVE);
     for (int64_t b0 = lo + 16 * (threadIdx.x / WAVE); b0 < hi; b0 += step * SCORE_BATCH) {
         uint32_t key[SCORE_BATCH];
-        score_groups_lds<SCORE_BATCH>(sl, kb, b0, step, hi, key, tiles[threadIdx.x / WAVE]);
+        score_groups_lds<SCORE_BATCH>(sl, kb, b0, step, hi, key, tiles);
 #pragma unroll
         for (int u = 0; u < SCORE_BATCH; ++u) {
             const int64_t blk = b0 + u * step + c;
@@ -882,6 +893,30 @@ select_kernel(SelectArgs a) {
     select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, hist, scan_sh, found);
 }
 
+// One launch per pass boundary: workgroups [0, n_sel) select the rows of the previous
+// pass (its keys complete since the previous launch), the others score the tiles of the
+// next pass into the other keys buffer (workgroup n_sel + s: tile s / gy, chunk s % gy).
+// The two roles touch disjoint buffers; the latency-bound selections and the MFMA
+// scoring share the machine instead of each ending with its own tail.
+static_assert(SEL_NT == SCORE_NT, "one block size for both roles");
+constexpr int SS_LDS_BYTES = SC_LDS_BYTES > (kHistBins + SEL_NT / WAVE + 2) * 4
+                                 ? SC_LDS_BYTES : (kHistBins + SEL_NT / WAVE + 2) * 4;
+
+__global__ void __launch_bounds__(SCORE_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
+score_select_kernel(ScorePass sp, SelectArgs a, int n_sel) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SS_LDS_BYTES];
+    if ((int)blockIdx.x < n_sel) {   // uniform over the workgroup
+        uint32_t *hist = reinterpret_cast<uint32_t *>(smem);
+        int32_t *scan_sh = reinterpret_cast<int32_t *>(hist + kHistBins);
+        uint32_t *found = reinterpret_cast<uint32_t *>(scan_sh + SEL_NT / WAVE);
+        const int64_t row = a.row_base + blockIdx.x;
+        select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, hist, scan_sh, found);
+        return;
+    }
+    const int64_t s = (int64_t)blockIdx.x - n_sel;
+    score_tile_body(sp, sp.tile_base + s / sp.gy, (int)(s % sp.gy), smem);
+}
+
 __global__ void __launch_bounds__(SEL_NT)
 select_dec_kernel(SelectArgs a, DecodeTables d) {
     __shared__ uint32_t hist[kHistBins];
@@ -1378,16 +1413,25 @@ hipError_t launch_compress(const int32_t *cu_q, const int32_t *cu_k, int batch,
     return trace_after(st, hipGetLastError());
 }
 
-hipError_t launch_score(const SeqInfo *tab, int batch, int topk, const uint16_t *q_idx,
-                        const float *w, const uint16_t *k_blk, uint32_t *keys,
-                        int64_t tile_base, int64_t n_tiles, int64_t slot_base,
-                        int64_t max_blocks, int64_t chunk_blocks, hipStream_t st) {
-    if (n_tiles <= 0) return hipSuccess;
-    const int64_t gy = (max_blocks + chunk_blocks - 1) / chunk_blocks;
-    trace_before(2, st);
-    hipLaunchKernelGGL(score_kernel, dim3((unsigned)n_tiles, (unsigned)gy), dim3(SCORE_NT), 0, st,
-                       tab, batch, topk, q_idx, w, k_blk, keys, chunk_blocks, tile_base,
-                       slot_base);
+hipError_t launch_score_select(const SeqInfo *tab, int batch, int topk, const uint16_t *q_idx,
+                               const float *w, const uint16_t *k_blk, uint32_t *score_keys,
+                               int64_t tile_base, int64_t n_tiles, int64_t score_slot_base,
+                               int64_t max_blocks, int64_t chunk_blocks,
+                               const uint32_t *sel_keys, int64_t sel_slot_base, int32_t *sel,
+                               int64_t row_base, int64_t n_rows, hipStream_t st) {
+    ScorePass sp = {};
+    sp.tab = tab; sp.batch = batch; sp.topk = topk; sp.q_idx = q_idx; sp.w = w; sp.k_blk = k_blk;
+    sp.keys = score_keys; sp.chunk_blocks = chunk_blocks; sp.tile_base = tile_base;
+    sp.slot_base = score_slot_base;
+    sp.gy = n_tiles > 0 ? (int)((max_blocks + chunk_blocks - 1) / chunk_blocks) : 0;
+    SelectArgs a = {};
+    a.tab = tab; a.batch = batch; a.topk = topk; a.keys = sel_keys; a.slot_base = sel_slot_base;
+    a.row_base = row_base; a.sel = sel;
+    const int64_t n_wg = n_rows + n_tiles * sp.gy;
+    if (n_wg <= 0) return hipSuccess;
+    trace_before(14, st);
+    hipLaunchKernelGGL(score_select_kernel, dim3((unsigned)n_wg), dim3(SCORE_NT), 0, st, sp, a,
+                       (int)n_rows);
     return trace_after(st, hipGetLastError());
 }
 

@@ -27,12 +27,16 @@ hipError_t launch_prep(const int32_t *cu_q, const int32_t *cu_k, int batch, int 
 hipError_t launch_compress(const int32_t *cu_q, const int32_t *cu_k, int batch,
                            int64_t max_blocks, const uint16_t *k_idx, uint16_t *k_blk,
                            int incremental, SeqInfo *tab, int topk, hipStream_t st);
-// Prefill scoring of tiles [tile_base, tile_base + n_tiles); slot s goes to
-// keys[s - slot_base].
-hipError_t launch_score(const SeqInfo *tab, int batch, int topk, const uint16_t *q_idx,
-                        const float *w, const uint16_t *k_blk, uint32_t *keys,
-                        int64_t tile_base, int64_t n_tiles, int64_t slot_base,
-                        int64_t max_blocks, int64_t chunk_blocks, hipStream_t st);
+// One prefill launch: selection of rows [row_base, row_base + n_rows) from sel_keys
+// (slot s at sel_keys[s - sel_slot_base]) and, at the same time, scoring of tiles
+// [tile_base, tile_base + n_tiles) into score_keys (slot s at score_keys[s -
+// score_slot_base]); either part may be empty.
+hipError_t launch_score_select(const SeqInfo *tab, int batch, int topk, const uint16_t *q_idx,
+                               const float *w, const uint16_t *k_blk, uint32_t *score_keys,
+                               int64_t tile_base, int64_t n_tiles, int64_t score_slot_base,
+                               int64_t max_blocks, int64_t chunk_blocks,
+                               const uint32_t *sel_keys, int64_t sel_slot_base, int32_t *sel,
+                               int64_t row_base, int64_t n_rows, hipStream_t st);
 // Scores of the listed rows (fp32, -inf past the row's visible blocks), [n_rows, ld].
 hipError_t launch_score_rows(const int32_t *cu_q, const int32_t *cu_k, int batch,
                              const int64_t *rows, int64_t n_rows, const uint16_t *q_idx,

@@ -224,22 +224,23 @@ def test_trace_end_without_begin_and_names():
     assert qsa.lib().qsa_kernel_name(2) == b"score"
     assert qsa.lib().qsa_kernel_name(12) == b"bwd_dq"
     assert qsa.lib().qsa_kernel_name(13) == b"bwd_dkv"
+    assert qsa.lib().qsa_kernel_name(14) == b"score_select"
     assert qsa.lib().qsa_kernel_name(42) == b"unknown"
     assert L.qsa_trace_begin(0) == qsa.QSA_ERR_SHAPE
 
 
 def test_prefill_workspace_bounded_by_key_budget():
     """Prefill scores are kept one pass of score tiles at a time (at most 2^25 keys of
-    4 bytes), so the workspace of a 262,144-token or a 1,048,576-token prefill is the
-    selection (4 * 512 bytes per query row, linear in the length) plus at most 128 MiB
-    of keys, while the sum of its score slots (F(L) - F(2051)) would be 34 GB and
-    550 GB."""
+    4 bytes, in two alternating buffers), so the workspace of a 262,144-token or a
+    1,048,576-token prefill is the selection (4 * 512 bytes per query row, linear in the
+    length) plus at most 256 MiB of keys, while the sum of its score slots
+    (F(L) - F(2051)) would be 34 GB and 550 GB."""
     d = qsa.make_dims(topk=512)
     F = lambda t: 2 * (t // 4) * (t // 4 - 1) + (t // 4) * (t % 4 + 1)
     for L in (65535, 262144, 1 << 20):
         st, n = _ws(d, _seqs([0, L], [0, L]))
         assert st == 0
-        assert n <= 4 * 512 * L + 4 * 2**25 + 2**20, (L, n)
+        assert n <= 4 * 512 * L + 8 * 2**25 + 2**20, (L, n)
         if L >= 262144:
             assert 4 * (F(L) - F(2051)) > 30 * n
     # a call whose keys fit one pass keeps all of them (as before)
