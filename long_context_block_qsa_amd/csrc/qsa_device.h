@@ -264,17 +264,25 @@ constexpr DigitPlan kWide = {3, {21, 10, 0, 0}, {11, 11, 10, 0}};
 constexpr int kHistBins = 2048;
 constexpr DigitPlan kNarrow = {4, {24, 16, 8, 0}, {8, 8, 8, 8}};
 
+// Words of the `found` LDS array radix_kth needs with NT threads.
+template <int NT> constexpr int radix_found_words() { return 2 + 2 * (NT / 64); }
+
 // The k-th largest of n keys (1 <= k <= n) by a most-significant-digit radix select
 // with LDS histograms. Returns theta (that key) and `need`, how many keys equal to
-// theta belong to the k largest (ties go to the lowest positions). All NT threads
-// of the workgroup must call it. hist: LDS, 2^max(width) entries; scan_sh: LDS,
-// NT/64+1 entries; found: LDS, 2 entries.
+// theta belong to the k largest (ties go to the lowest positions). Each pass also
+// ORs and ANDs the keys it counts: when they agree on every bit below the pass's digit,
+// the bin found holds a single key value and the select stops there (scores of small-
+// integer indexer data leave the low bits of their keys constant, so the last of the
+// three passes is skipped). All NT threads of the workgroup must call it. hist: LDS,
+// 2^max(width) entries; scan_sh: LDS, NT/64+1 entries; found: LDS,
+// radix_found_words<NT>() entries.
 template <int NT, typename KeyPtr>
 __device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
                                           const DigitPlan &plan, uint32_t *hist,
                                           int32_t *scan_sh, uint32_t *found,
                                           uint32_t *theta_out, int64_t *need_out) {
     static_assert(NT == 256, "bin ownership assumes 256 threads");
+    constexpr int NW = NT / WAVE;
     const int tid = threadIdx.x;
     uint32_t prefix = 0, pmask = 0;
     int64_t need = k;
@@ -286,6 +294,7 @@ __device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
         if (tid == 0) { found[0] = 0u; found[1] = 0u; }
         __syncthreads();
         // keys are read in batches of 8 before their atomics, so the loads overlap
+        uint32_t k_or = 0u, k_and = 0xffffffffu;
         for (int64_t i0 = tid; i0 < n; i0 += 8 * NT) {
             uint32_t kk[8];
 #pragma unroll
@@ -296,9 +305,21 @@ __device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int64_t i = i0 + (int64_t)e * NT;
-                if (i < n && (kk[e] & pmask) == prefix)
+                if (i < n && (kk[e] & pmask) == prefix) {
                     atomicAdd(&hist[(kk[e] >> shift) & dmask], 1u);
+                    k_or |= kk[e];
+                    k_and &= kk[e];
+                }
             }
+        }
+#pragma unroll
+        for (int d = 1; d < WAVE; d <<= 1) {
+            k_or |= (uint32_t)__shfl_xor((int)k_or, d);
+            k_and &= (uint32_t)__shfl_xor((int)k_and, d);
+        }
+        if (lane_id() == 0) {
+            found[2 + tid / WAVE] = k_or;
+            found[2 + NW + tid / WAVE] = k_and;
         }
         __syncthreads();
         // thread j owns `per` consecutive bins ending at nb - per*j (highest bins first)
@@ -324,7 +345,18 @@ __device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
         need -= (int64_t)found[1];
         prefix |= found[0] << shift;
         pmask |= dmask << shift;
+        uint32_t b_or = 0u, b_and = 0xffffffffu;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            b_or |= found[2 + i];
+            b_and &= found[2 + NW + i];
+        }
         __syncthreads();
+        const uint32_t low = (1u << shift) - 1u;   // bits below this pass's digit
+        if (((b_or ^ b_and) & low) == 0u) {        // uniform: every thread read the same words
+            prefix |= b_or & low;
+            break;
+        }
     }
     *theta_out = prefix;
     *need_out = need;

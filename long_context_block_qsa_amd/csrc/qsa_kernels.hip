@@ -575,7 +575,7 @@ struct ScoreSmem {
     int32_t wl_pos[LOC_NT / WAVE][KP];
     uint32_t hist[kHistBins];
     int32_t scan_sh[SEL_NT / WAVE];
-    uint32_t found[2];
+    uint32_t found[radix_found_words<SEL_NT>()];
     int viol, s_last, exact[4];
     TopkSmem tsm;
     __attribute__((aligned(16))) uint8_t tiles[LOC_NT / WAVE][2 * SC_TILE];  // score_groups_lds
@@ -888,7 +888,7 @@ __global__ void __launch_bounds__(SEL_NT)
 select_kernel(SelectArgs a) {
     __shared__ uint32_t hist[kHistBins];
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
-    __shared__ uint32_t found[2];
+    __shared__ uint32_t found[radix_found_words<SEL_NT>()];
     const int64_t row = a.row_base + blockIdx.x;
     select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, hist, scan_sh, found);
 }
@@ -899,8 +899,8 @@ select_kernel(SelectArgs a) {
 // The two roles touch disjoint buffers; the latency-bound selections and the MFMA
 // scoring share the machine instead of each ending with its own tail.
 static_assert(SEL_NT == SCORE_NT, "one block size for both roles");
-constexpr int SS_LDS_BYTES = SC_LDS_BYTES > (kHistBins + SEL_NT / WAVE + 2) * 4
-                                 ? SC_LDS_BYTES : (kHistBins + SEL_NT / WAVE + 2) * 4;
+constexpr int SEL_LDS_WORDS = kHistBins + SEL_NT / WAVE + radix_found_words<SEL_NT>();
+constexpr int SS_LDS_BYTES = SC_LDS_BYTES > SEL_LDS_WORDS * 4 ? SC_LDS_BYTES : SEL_LDS_WORDS * 4;
 
 __global__ void __launch_bounds__(SCORE_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 score_select_kernel(ScorePass sp, SelectArgs a, int n_sel) {
@@ -921,7 +921,7 @@ __global__ void __launch_bounds__(SEL_NT)
 select_dec_kernel(SelectArgs a, DecodeTables d) {
     __shared__ uint32_t hist[kHistBins];
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
-    __shared__ uint32_t found[2];
+    __shared__ uint32_t found[radix_found_words<SEL_NT>()];
     const int64_t row = blockIdx.x;
     const DecRow r = d.row[row];
     const RowView rv = {r.k0, r.t, r.blk0, r.slot};
@@ -1242,7 +1242,7 @@ struct AttnMergeSmem {
     int viol;
     uint32_t hist[kHistBins];   // exact fallback: radix histogram, then the emit counts
     int32_t scan_sh[SEL_NT / WAVE];
-    uint32_t found[2];
+    uint32_t found[radix_found_words<SEL_NT>()];
     int32_t ids[KMAX];          // the row's kept block ids, ascending
 };
 
