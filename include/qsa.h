@@ -274,7 +274,8 @@ enum {
     QSA_KERNEL_BWD_FILL = 11,
     QSA_KERNEL_BWD_DQ = 12,
     QSA_KERNEL_BWD_DKV = 13,
-    QSA_KERNEL_SCORE_SELECT = 14   /* prefill: one pass's selection + the next pass's scoring */
+    QSA_KERNEL_SCORE_SELECT = 14,  /* prefill: one pass's selection + the next pass's scoring */
+    QSA_KERNEL_ATTEND_DENSE = 15   /* prefill rows that keep every visible block (causal) */
 };
 qsa_status qsa_trace_begin(int32_t max_kernels);
 int32_t qsa_trace_end(int32_t max_out, int32_t *kind_out, float *ms_out);

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqsa.so")
-SOURCES = ["qsa_kernels.hip", "qsa_backward.hip", "qsa_api.hip"]
+SOURCES = ["qsa_kernels.hip", "qsa_dense.hip", "qsa_backward.hip", "qsa_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -98,6 +98,7 @@ struct Plan {
     int max_chunks = 0;         // chunks of the longest scored row (decode path)
     int nsplit = 1;             // attention key splits per row
     int64_t n_dense = 0;        // query rows with at most topk visible blocks
+    int64_t n_dense_tiles = 0;  // their tiles of DN_ROWS rows (per sequence)
     size_t off_ctl = 0, off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, off_glist = 0,
            off_part = 0;
     size_t ws_bytes = 0;
@@ -226,7 +227,11 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
         if (nq > 0)
             p->max_cmp_incr = std::max(p->max_cmp_incr, L / qsa::BS - (L - nq) / qsa::BS);
         const int64_t ts = h_first_scored_pos(L, nq, p->topk);
-        if (cq) p->n_dense += std::min(nq, std::max<int64_t>(0, ts - (L - nq)));
+        if (cq) {
+            const int64_t nd = std::max<int64_t>(0, std::min(ts, L) - (L - nq));
+            p->n_dense += nd;
+            p->n_dense_tiles += (nd + qsa::DN_ROWS - 1) / qsa::DN_ROWS;
+        }
         if (cq && ts < L) {
             p->n_tiles += (L - ts + 3) / 4;
             p->n_slots += h_slots_before(L) - h_slots_before(ts);
@@ -378,13 +383,23 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
     return QSA_OK;
 }
 
+// dense_tiles: the selection is the library's own (a forward step), so rows with at
+// most topk visible blocks keep them all and are attended by the dense-regime kernel.
 qsa_status run_attend(const Plan &p, const qsa_bf16 *q, const qsa_bf16 *k, const qsa_bf16 *v,
                       const qsa::Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
-                      void *ws, hipStream_t st, const qsa::AttnMerge *merge = nullptr) {
+                      void *ws, hipStream_t st, const qsa::AttnMerge *merge = nullptr,
+                      bool dense_tiles = false) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
     float *part = ws_at<float>(ws, p.off_part);
-    QSA_TRY(qsa::launch_attend(tab, p.use_dec ? &p.dec : nullptr, p.batch, p.topk, p.scale, q,
-                               k, v, fp8, sel, out, lse, part, p.nsplit, p.tq, merge, st));
+    const bool dense = dense_tiles && !fp8 && !p.use_dec && p.nsplit == 1 &&
+                       p.n_dense_tiles > 0;
+    if (dense)
+        QSA_TRY(qsa::launch_attend_dense(tab, p.batch, p.topk, p.scale, q, k, v, out, lse,
+                                         p.n_dense_tiles, st));
+    if (!dense || p.n_dense < p.tq)
+        QSA_TRY(qsa::launch_attend(tab, p.use_dec ? &p.dec : nullptr, p.batch, p.topk, p.scale,
+                                   q, k, v, fp8, sel, out, lse, part, p.nsplit, p.tq, merge,
+                                   dense, st));
     return QSA_OK;
 }
 
@@ -458,7 +473,8 @@ qsa_status forward_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_
         m.ch = p.local_ch; m.max_chunks = p.max_chunks;
         m.sel = sel_use;
     }
-    return run_attend(p, q, k, v, fp8, sel_use, out, lse, ws, hs, merge_in_attend ? &m : nullptr);
+    return run_attend(p, q, k, v, fp8, sel_use, out, lse, ws, hs, merge_in_attend ? &m : nullptr,
+                      true);
 }
 
 // Attention backward: per-sequence table, D, nsel, list offsets, block totals, count
@@ -771,8 +787,8 @@ const char *qsa_kernel_name(int32_t kind) {
     static const char *names[] = {"prep",     "compress",    "score",    "select",
                                   "attend",   "combine",     "bwd_prep", "bwd_rows",
                                   "bwd_count", "bwd_colscan", "bwd_scan", "bwd_fill",
-                                  "bwd_dq",   "bwd_dkv",     "score_select"};
-    return (kind >= 0 && kind < 15) ? names[kind] : "unknown";
+                                  "bwd_dq",   "bwd_dkv",     "score_select", "attend_dense"};
+    return (kind >= 0 && kind < 16) ? names[kind] : "unknown";
 }
 
 }  // extern "C"

@@ -38,7 +38,13 @@ struct SeqInfo {
     int32_t blk0;   // first compressed-block row
     int32_t tile0;  // first score tile (4 query rows that need scoring)
     int64_t s0;     // first score slot
+    int32_t dtile0; // first dense tile (DN_ROWS query rows that keep every visible block)
+    int32_t pad_;
 };
+
+// Query rows per tile of the dense-regime attention (rows with no more visible blocks
+// than the budget attend every token up to their own position).
+constexpr int DN_ROWS = 16;
 
 // Per-sequence table of the attention backward. Key blocks are the ceil(L/4) groups of
 // 4 tokens of a sequence (the last one may be partial: it is only attended raw); query
@@ -106,6 +112,13 @@ __device__ __forceinline__ int64_t slots_before(int64_t t) {
 __device__ __forceinline__ int64_t first_scored_pos(int32_t L, int32_t nq, int32_t topk) {
     int64_t a = (int64_t)L - nq, b = 4 * (int64_t)topk + 3;
     return a > b ? a : b;
+}
+
+// Query rows of a sequence in the dense regime: positions L - nq .. first scored - 1.
+__device__ __forceinline__ int64_t dense_rows_of(int32_t L, int32_t nq, int32_t topk) {
+    const int64_t ts = first_scored_pos(L, nq, topk), e = ts < L ? ts : L;
+    const int64_t n = e - ((int64_t)L - nq);
+    return n > 0 ? n : 0;
 }
 
 // Largest b with key(b) <= x over a non-decreasing table (x >= key(0)).

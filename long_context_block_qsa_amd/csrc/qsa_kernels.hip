@@ -22,11 +22,11 @@ namespace qsa {
 template <int NT>
 __device__ void prep_body(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
                           int batch, int topk, SeqInfo *__restrict__ tab, int64_t *sh) {
-    int64_t carry_blk = 0, carry_tile = 0, carry_slot = 0;
+    int64_t carry_blk = 0, carry_tile = 0, carry_slot = 0, carry_dt = 0;
     for (int base = 0; base < batch; base += NT) {
         const int b = base + threadIdx.x;
         int32_t q0 = 0, nq = 0, k0 = 0, L = 0;
-        int64_t nblk = 0, ntile = 0, nslot = 0;
+        int64_t nblk = 0, ntile = 0, nslot = 0, ndt = 0;
         if (b < batch) {
             q0 = cu_q[b]; nq = cu_q[b + 1] - q0;
             k0 = cu_k[b]; L = cu_k[b + 1] - k0;
@@ -36,20 +36,24 @@ __device__ void prep_body(const int32_t *__restrict__ cu_q, const int32_t *__res
                 ntile = (L - ts + 3) / 4;
                 nslot = slots_before(L) - slots_before(ts);
             }
+            ndt = (dense_rows_of(L, nq, topk) + DN_ROWS - 1) / DN_ROWS;
         }
-        int64_t tot_b, tot_t, tot_s;
+        int64_t tot_b, tot_t, tot_s, tot_d;
         const int64_t eb = block_excl_scan<int64_t, NT>(nblk, sh, &tot_b);
         const int64_t et = block_excl_scan<int64_t, NT>(ntile, sh, &tot_t);
         const int64_t es = block_excl_scan<int64_t, NT>(nslot, sh, &tot_s);
+        const int64_t ed = block_excl_scan<int64_t, NT>(ndt, sh, &tot_d);
         if (b < batch) {
             SeqInfo s;
             s.q0 = q0; s.nq = nq; s.k0 = k0; s.L = L;
             s.blk0 = (int32_t)(carry_blk + eb);
             s.tile0 = (int32_t)(carry_tile + et);
             s.s0 = carry_slot + es;
+            s.dtile0 = (int32_t)(carry_dt + ed);
+            s.pad_ = 0;
             tab[b] = s;
         }
-        carry_blk += tot_b; carry_tile += tot_t; carry_slot += tot_s;
+        carry_blk += tot_b; carry_tile += tot_t; carry_slot += tot_s; carry_dt += tot_d;
     }
 }
 
@@ -963,6 +967,7 @@ struct AttnArgs {
     float *part;
     int nsplit;
     int64_t nrows;
+    int skip_dense;   // rows with at most topk visible blocks are left to the dense kernel
     int merge;        // decode: merge the rows of short tiles here (operands in `loc`)
     LocalArgs loc;
 };
@@ -1232,8 +1237,10 @@ attend_kernel(AttnArgs a) {
     int64_t row;
     int g, sp;
     if (!attend_item(a, row, g, sp)) return;
-    attend_body<FP8>(a, tab_row(a.tab, a.batch, a.topk, row), row, g, sp,
-                     klds + (threadIdx.x / WAVE) * KT_LDS_BYTES, a.sel + row * a.topk);
+    const RowView rv = tab_row(a.tab, a.batch, a.topk, row);
+    if (a.skip_dense && nvis_of(rv.t) <= a.topk) return;   // uniform over the wave
+    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES,
+                     a.sel + row * a.topk);
 }
 
 // LDS of a decode attention workgroup that merges its row's candidates.
@@ -1504,7 +1511,7 @@ hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, i
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
                          float *part, int nsplit, int64_t n_rows, const AttnMerge *merge,
-                         hipStream_t st) {
+                         bool skip_dense, hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
     AttnArgs a = {};
     a.merge = merge != nullptr && d != nullptr;
@@ -1520,6 +1527,7 @@ hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, i
     a.k8 = fp8 ? fp8->k8 : nullptr; a.v8 = fp8 ? fp8->v8 : nullptr;
     a.k_scale = fp8 ? fp8->k_scale : nullptr; a.v_scale = fp8 ? fp8->v_scale : nullptr;
     a.nsplit = nsplit; a.nrows = n_rows;
+    a.skip_dense = skip_dense && !d && nsplit == 1;
     const int64_t waves = n_rows * HKV * nsplit;
     const int64_t wgs = (waves + ATT_NT / WAVE - 1) / (ATT_NT / WAVE);
     trace_before(4, st);

@@ -71,11 +71,18 @@ struct AttnMerge {
     int ch, max_chunks;
     int32_t *sel;   // where the merged selections are written out (the one attend reads)
 };
+// skip_dense (prefill, nsplit 1): rows with at most topk visible blocks are left to
+// launch_attend_dense.
 hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
                          float *part, int nsplit, int64_t n_rows, const AttnMerge *merge,
-                         hipStream_t st);
+                         bool skip_dense, hipStream_t st);
+// Causal attention of the rows in the dense regime (every visible block kept), in tiles
+// of DN_ROWS rows sharing their keys through LDS (qsa_dense.hip).
+hipError_t launch_attend_dense(const SeqInfo *tab, int batch, int topk, float scale,
+                               const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               float *out, float *lse, int64_t n_tiles, hipStream_t st);
 // Attention backward over fixed selections (qsa_backward.hip).
 struct BwdSeq;
 struct BwdBuffers {
