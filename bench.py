@@ -8,9 +8,13 @@ Inputs are seeded and synthetic and sit in HBM before timing starts. Consecutive
 rotate over R distinct query sets and R copies of the compressed-key cache, so that a
 step never finds the previous step's 168 MB working set in the 256 MB Infinity Cache.
 
-Prints one JSON line: throughput (query-tokens/s), a roofline entry for the dominant
-kernel (algorithmic bytes / its mean HIP-event duration), the CPU oracle timed on a
-bounded sample, and a secondary prefill measurement (ragged 65,535/40,001/8,190/3).
+Prints one JSON line: throughput (query-tokens/s), the median and minimum step times, a
+roofline entry for the dominant kernel (algorithmic bytes / its mean HIP-event duration)
+and the whole step's HBM fraction, the CPU oracle timed on a bounded sample, and the
+other measurements: decode at 1M tokens, with 4 query tokens per sequence and from the
+FP8 cache; compression of the full 16 x 262,144-token key cache; the ragged
+65,535/40,001/8,190/3 prefill (with its FP8 and backward variants and its own oracle
+baseline); and the 1x1024, 1x16384 and 1x262144 prefills and the 1x32768 decode.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -63,6 +67,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=4, help="distinct query sets / cache copies")
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the lines of the other workloads (1x1024, 1x32768 decode, "
+                         "1x16384, 1x262144)")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context decode line")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 KV cache lines")
     ap.add_argument("--no-mtp", action="store_true",
@@ -183,6 +190,18 @@ def run_decode(args, torch, qsa, gen):
     gpu_ms = ev0.elapsed_time(ev1)
     log(f"decode: {args.steps} steps ({'eager' if graph is None else 'graph replay'}), "
         f"wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+    # per-step distribution (outside the timed region): HIP events around each replay of
+    # R steps, or around each eager step
+    if graph is None:
+        ctr = [0]
+
+        def one():
+            step(ctr[0])
+            ctr[0] += 1
+
+        per_step = event_times(torch, one, args.steps)
+    else:
+        per_step = [t / R for t in event_times(torch, graph.replay, max(1, args.steps // R))]
 
     # instrumented pass: per-kernel durations with HIP events on the library's stream
     with qsa.trace(4096) as tr:
@@ -194,7 +213,7 @@ def run_decode(args, torch, qsa, gen):
     fp8 = None if args.no_fp8 else run_decode_fp8(args, torch, qsa, seqs, k, v, k_idx, sets)
     return dict(p=p, batch=batch, ctx=ctx, wall_s=wall, gpu_ms=gpu_ms,
                 kernels=tr.mean_ms(), kernel_total=tr.total_ms(), seqs=seqs, sets=sets,
-                long_ctx=long_ctx, fp8=fp8, mtp=mtp)
+                long_ctx=long_ctx, fp8=fp8, mtp=mtp, per_step=per_step, k_idx=k_idx)
 
 
 def time_steps(args, torch, step, R, n):
@@ -362,10 +381,55 @@ def run_decode_mtp(args, torch, qsa, gen, k, v, k_idx, sets, nq=4):
             "kernel_mean_ms": {k2: round(v2, 5) for k2, v2 in tr.mean_ms().items()}}
 
 
-# ---------------------------------------------------------------- prefill workload
+# ---------------------------------------------------------------- prefill workloads
 
-def run_prefill(args, torch, qsa, gen):
-    p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
+# Random 256-byte row gathers from a 67 MB table, measured on this part with a probe
+# kernel of the attention's access shape (16 lanes per row): the beyond-L2 ceiling the
+# sparse rows' gathers are compared against.
+GATHER_CEILING_GBS = 7900.0
+
+
+def step_stats(ms_list):
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"n": int(a.size), "median_ms": round(float(np.median(a)), 5),
+            "min_ms": round(float(a.min()), 5), "mean_ms": round(float(a.mean()), 5)}
+
+
+def event_times(torch, fn, n):
+    """HIP-event time of each of n calls of fn on torch's current stream (ms)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def prefill_work(cu_k):
+    """Attended (query, key) pairs of a prefill (every token a query), split into rows
+    that keep every visible block (dense) and the others, and scored (query, block)
+    pairs."""
+    dense = sparse = scored = 0
+    for L in np.diff(np.asarray(cu_k, dtype=np.int64)):
+        t = np.arange(int(L), dtype=np.int64)
+        nv = (t + 1) // BS
+        keys = np.minimum(nv, TOPK) * BS + (t + 1 - BS * nv)
+        dm = nv <= TOPK
+        dense += int(keys[dm].sum())
+        sparse += int(keys[~dm].sum())
+        scored += int(nv[~dm].sum())
+    return dense, sparse, scored
+
+
+def measure_prefill(args, torch, qsa, gen, name, steps, extras=False):
+    """One prefill workload through qsa_forward (compress, score + select in passes,
+    attention): step times by HIP events, per-kernel totals of one traced step, the
+    attention's MFMA fraction (attended pairs x 12,288 flop) and its gather rate."""
+    t0 = time.time()
+    p = gen.workload_problem(name)
+    log(f"{name}: inputs generated in {time.time() - t0:.1f}s")
     dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
     seqs = qsa.Seqs(p.cu_q, p.cu_k)
     q, k, v, q_idx, k_idx = (dev16(x) for x in (p.q, p.k, p.v, p.q_idx, p.k_idx))
@@ -381,74 +445,132 @@ def run_prefill(args, torch, qsa, gen):
 
     step()
     torch.cuda.synchronize()
-    n = max(1, args.prefill_steps)
-    t0 = time.perf_counter()
-    for _ in range(n):
+    times = event_times(torch, step, max(1, steps))
+    with qsa.trace(8192) as tr:
         step()
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / n
-    with qsa.trace(4096) as tr:
-        step()
-    torch.cuda.synchronize()
-    # algorithmic work: attended (query, key) pairs and scored (query, block) pairs
-    pairs, scored = 0, 0
-    for b in range(len(p.cu_k) - 1):
-        L = int(p.cu_k[b + 1] - p.cu_k[b])
-        for t in range(L):
-            nv = (t + 1) // BS
-            pairs += min(nv, TOPK) * BS + (t + 1 - BS * nv)
-            scored += nv if nv > TOPK else 0
+    km = tr.total_ms()
+    dense, sparse, scored = prefill_work(p.cu_k)
+    pairs = dense + sparse
     att_flop = pairs * HQ * D * 4
-    score_flop = scored * HI * DI * 2
-    km = tr.total_ms()   # score and select run once per pass of score tiles
-    att_ms = km.get("attend", float("nan")) + km.get("combine", 0.0)
-    fp8 = None
-    if not args.no_fp8:
-        k8 = torch.empty((seqs.n_k, HKV, D), dtype=torch.uint8, device="cuda")
-        v8 = torch.empty_like(k8)
-        ks = torch.empty((seqs.n_k, HKV), dtype=torch.float32, device="cuda")
-        vs = torch.empty_like(ks)
-        qsa.quantize_kv(seqs, k, v, k8, v8, ks, vs)
-
-        def step8():
-            qsa.forward_fp8(seqs, q, k8, v8, ks, vs, q_idx, w, k_idx, k_blk, sel, out, lse, ws,
-                            TOPK)
-
-        step8()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n):
-            step8()
-        torch.cuda.synchronize()
-        ms8 = (time.perf_counter() - t0) * 1e3 / n
-        with qsa.trace(4096) as tr8:
-            step8()
-        torch.cuda.synchronize()
-        km8 = tr8.total_ms()
-        att8 = km8.get("attend", float("nan")) + km8.get("combine", 0.0)
-        fp8 = {"ms_per_step": round(ms8, 3),
-               "query_tokens_per_s": round(seqs.n_q / (ms8 / 1e3), 1),
-               "kernel_ms": {k2: round(v2, 4) for k2, v2 in km8.items()},
-               "attention_tflops": round(att_flop / (att8 / 1e3) / 1e12, 2),
-               "attention_gather_gbs": round(pairs * HKV * (2 * D + 8) / (att8 / 1e3) / 1e9, 1)}
-    bwd = None if args.no_backward else run_prefill_backward(args, torch, qsa, gen, p, seqs, q, k,
-                                                             v, sel, out, lse, n, pairs)
-    return {
-        "fp8_kv": fp8,
-        "backward": bwd,
-        "workload": "ragged prefill 65,535/40,001/8,190/3 tokens, budget 512 blocks",
-        "ms_per_step": round(ms, 3),
-        "query_tokens_per_s": round(seqs.n_q / (ms / 1e3), 1),
+    att_ms = km.get("attend", 0.0) + km.get("attend_dense", 0.0) + km.get("combine", 0.0)
+    sparse_ms = km.get("attend", 0.0) + km.get("combine", 0.0)
+    st = step_stats(times)
+    res = {
+        "workload": name, "ms_per_step": st["median_ms"], "step_ms": st,
+        "query_tokens_per_s": round(seqs.n_q / (st["median_ms"] / 1e3), 1),
         "kernel_ms": {k2: round(v2, 4) for k2, v2 in km.items()},
-        "attention_pairs": pairs,
+        "attention_pairs": {"dense_rows": dense, "sparse_rows": sparse},
         "attention_tflops": round(att_flop / (att_ms / 1e3) / 1e12, 2),
         "attention_mfma_frac": round(att_flop / (att_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "attention_gather_gbs": round(pairs * HKV * D * 2 * 2 / (att_ms / 1e3) / 1e9, 1),
-        # score and select of the passes run in the same launches
-        "score_select_ms": round(km.get("score_select", float("nan")), 4),
-        "score_tflops_incl_select": round(score_flop / (km.get("score_select", float("nan")) / 1e3)
-                                          / 1e12, 2),
+        "score_select_ms": round(km.get("score_select", 0.0), 4),
+        "score_tflops_incl_select": (round(scored * HI * DI * 2 / (km["score_select"] / 1e3) / 1e12,
+                                           2) if km.get("score_select") else None),
+        "workspace_bytes": int(ws.numel()),
     }
+    if dense and km.get("attend_dense"):
+        f = dense * HQ * D * 4 / (km["attend_dense"] / 1e3) / 1e12
+        res["dense_rows_tflops"] = round(f, 2)
+        res["dense_rows_mfma_frac"] = round(f / MFMA_BF16_PEAK_TFLOPS, 4)
+    if sparse and sparse_ms > 0:
+        g = sparse * HKV * D * 2 * 2 / (sparse_ms / 1e3) / 1e9   # K and V rows of both heads
+        res["sparse_rows_gather_gbs"] = round(g, 1)
+        res["sparse_rows_gather_frac"] = round(g / GATHER_CEILING_GBS, 4)
+    log(f"{name}: {st['median_ms']:.3f} ms per step (median of {st['n']})")
+    if extras:
+        res["fp8_kv"] = None if args.no_fp8 else run_prefill_fp8(
+            args, torch, qsa, seqs, q, k, v, q_idx, w, k_idx, k_blk, sel, out, lse, ws, steps,
+            att_flop, sparse)
+        res["backward"] = None if args.no_backward else run_prefill_backward(
+            args, torch, qsa, gen, p, seqs, q, k, v, sel, out, lse, steps, pairs)
+    return res
+
+
+def run_prefill_fp8(args, torch, qsa, seqs, q, k, v, q_idx, w, k_idx, k_blk, sel, out, lse, ws,
+                    steps, att_flop, sparse):
+    """The same prefill with K and V read from the FP8 (E4M3 + per-row scale) cache."""
+    k8 = torch.empty((seqs.n_k, HKV, D), dtype=torch.uint8, device="cuda")
+    v8 = torch.empty_like(k8)
+    ks = torch.empty((seqs.n_k, HKV), dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    qsa.quantize_kv(seqs, k, v, k8, v8, ks, vs)
+
+    def step8():
+        qsa.forward_fp8(seqs, q, k8, v8, ks, vs, q_idx, w, k_idx, k_blk, sel, out, lse, ws, TOPK)
+
+    step8()
+    torch.cuda.synchronize()
+    st = step_stats(event_times(torch, step8, max(1, steps)))
+    with qsa.trace(8192) as tr8:
+        step8()
+    torch.cuda.synchronize()
+    km8 = tr8.total_ms()
+    att8 = km8.get("attend", float("nan")) + km8.get("combine", 0.0)
+    return {"ms_per_step": st["median_ms"], "step_ms": st,
+            "query_tokens_per_s": round(seqs.n_q / (st["median_ms"] / 1e3), 1),
+            "kernel_ms": {k2: round(v2, 4) for k2, v2 in km8.items()},
+            "attention_tflops": round(att_flop / (att8 / 1e3) / 1e12, 2),
+            "attention_gather_gbs": round(sparse * HKV * (2 * D + 8) / (att8 / 1e3) / 1e9, 1)}
+
+
+def run_decode_32k(args, torch, qsa, gen):
+    """Decode of one sequence at 32,768 tokens of context (16 needle blocks): each step
+    replays one HIP graph of the forward; its 3.2 MB working set stays in the caches
+    between steps, so this is a latency figure."""
+    p = gen.workload_problem("decode_1x32768")
+    dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    seqs = qsa.Seqs(p.cu_q, p.cu_k)
+    q, k, v, q_idx, k_idx = (dev16(x) for x in (p.q, p.k, p.v, p.q_idx, p.k_idx))
+    w = torch.from_numpy(p.w).cuda()
+    k_blk = torch.empty((seqs.n_blocks, DI), dtype=torch.int16, device="cuda")
+    qsa.compress(seqs, k_idx, k_blk)
+    sel = torch.empty((1, TOPK), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, HQ, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, HQ), dtype=torch.float32, device="cuda")
+    ws = qsa.alloc_workspace(seqs, TOPK)
+
+    def step():
+        qsa.forward(seqs, q, k, v, q_idx, w, k_idx, k_blk, sel, out, lse, ws, TOPK)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    st = step_stats(event_times(torch, g.replay, max(8, args.steps)))
+    if not set(p.needles[0]) <= set(sel.cpu().numpy()[0].tolist()):
+        raise RuntimeError("decode_1x32768: needle blocks not selected")
+    nbytes = decode_algorithmic_bytes(1, 32768)["total"]
+    with qsa.trace(64) as tr:
+        step()
+    torch.cuda.synchronize()
+    return {"workload": "decode_1x32768", "launch": "hip graph replay",
+            "ms_per_step": st["median_ms"], "step_ms": st,
+            "query_tokens_per_s": round(1 / (st["median_ms"] / 1e3), 1),
+            "algorithmic_bytes": nbytes,
+            "achieved_gbs": round(nbytes / (st["median_ms"] / 1e3) / 1e9, 1),
+            "kernel_ms": {k2: round(v2, 5) for k2, v2 in tr.total_ms().items()}}
+
+
+def run_compress_full(torch, qsa, d):
+    """Compression of the whole 16 x 262,144-token indexer-key cache (4,194,304 tokens ->
+    1,048,576 blocks): 512 B read and 128 B written per block."""
+    seqs, k_idx = d["seqs"], d["k_idx"]
+    k_blk = torch.empty((seqs.n_blocks, DI), dtype=torch.int16, device="cuda")
+
+    def run():
+        qsa.compress(seqs, k_idx, k_blk)
+
+    run()
+    torch.cuda.synchronize()
+    st = step_stats(event_times(torch, run, 10))
+    nbytes = seqs.n_blocks * (BS * DI * 2 + DI * 2)
+    gbs = nbytes / (st["median_ms"] / 1e3) / 1e9
+    return {"workload": "compress of the decode_16x262144 indexer keys (full context)",
+            "algorithmic_bytes": nbytes, "ms": st["median_ms"], "step_ms": st,
+            "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def run_prefill_backward(args, torch, qsa, gen, p, seqs, q, k, v, sel, out, lse, n, pairs):
@@ -466,11 +588,8 @@ def run_prefill_backward(args, torch, qsa, gen, p, seqs, q, k, v, sel, out, lse,
 
     stepb()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(n):
-        stepb()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / n
+    st = step_stats(event_times(torch, stepb, max(1, n)))
+    ms = st["median_ms"]
     with qsa.trace(64) as tr:
         stepb()
     torch.cuda.synchronize()
@@ -478,7 +597,7 @@ def run_prefill_backward(args, torch, qsa, gen, p, seqs, q, k, v, sel, out, lse,
     # five contractions per attended (query head, key): S and dP recomputed, dQ, dK, dV
     flop = pairs * HQ * D * 2 * 5
     # rows x kept blocks per KV head (the dK/dV kernel's row visits)
-    return {"ms_per_step": round(ms, 3),
+    return {"ms_per_step": round(ms, 3), "step_ms": st,
             "query_tokens_per_s": round(seqs.n_q / (ms / 1e3), 1),
             "kernel_ms": {k2: round(v2, 4) for k2, v2 in km.items()},
             "tflops": round(flop / (ms / 1e3) / 1e12, 2),
@@ -516,6 +635,23 @@ def run_cpu_baseline(args, d, oracle):
             "cpu_model": model, "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{reps} decode step(s) of 16 rows at 262,144 context (score + select + "
                       f"attend over the prebuilt compressed cache), {el:.1f} s wall"}
+
+
+def run_cpu_baseline_prefill(args, oracle, gen, stride=64):
+    """The oracle on a bounded sample of the ragged 64K prefill: every stride-th query row
+    (compress of all blocks, then score + select + attend of the sampled rows)."""
+    p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
+    rows = np.arange(0, p.n_q, stride, dtype=np.int64)
+    threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.forward(oracle.Dims(), p.cu_q, p.cu_k, p.q, p.k, p.v, p.q_idx, p.w, p.k_idx,
+                   rows=rows, threads=threads)
+    el = time.perf_counter() - t0
+    return {"value": round(rows.size / el, 3), "unit": "query-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"every {stride}th row of the ragged 65,535/40,001/8,190/3 prefill "
+                      f"({rows.size} rows: compress of every block, then score, select and "
+                      f"attend of those rows), {el:.1f} s wall"}
 
 
 def traffic_of(kernel):
@@ -577,6 +713,7 @@ def main():
         "roofline": roofline,
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_gbs": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "step_ms": step_stats(d["per_step"]),
         "kernel_mean_ms": {k2: round(v2, 5) for k2, v2 in kern.items()},
     }
     if d["long_ctx"] is not None:
@@ -585,13 +722,27 @@ def main():
         line["decode_multi_query"] = d["mtp"]
     if d["fp8"] is not None:
         line["decode_fp8"] = d["fp8"]
+    line["compress_full_context"] = run_compress_full(torch, qsa, d)
     if not args.no_prefill:
-        log("prefill workload")
-        line["prefill"] = run_prefill(args, torch, qsa, gen)
+        log("prefill workloads")
+        line["prefill"] = measure_prefill(args, torch, qsa, gen,
+                                          "prefill_ragged_65535_40001_8190_3",
+                                          args.prefill_steps, extras=True)
+    if not args.no_workloads:
+        w = {"decode_1x32768": run_decode_32k(args, torch, qsa, gen)}
+        for name, n in (("prefill_1x1024", 20), ("prefill_1x16384", 5),
+                        ("prefill_1x262144", 2)):
+            if name == "prefill_1x262144" and args.no_prefill:
+                continue
+            w[name] = measure_prefill(args, torch, qsa, gen, name, n)
+            torch.cuda.empty_cache()
+        line["workloads"] = w
     if not args.no_cpu_baseline:
         import oracle
         log("CPU oracle baseline")
         line["cpu_baseline"] = run_cpu_baseline(args, d, oracle)
+        if not args.no_prefill:
+            line["cpu_baseline_prefill"] = run_cpu_baseline_prefill(args, oracle, gen)
     print(json.dumps(line), flush=True)
 
 

@@ -255,12 +255,15 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
         }
     }
     // decode path: few score tiles over long rows -> chunked scoring with local
-    // candidates; the chunk shrinks until the longest row has 16 full chunks
+    // candidates; the chunk shrinks until the longest row's full chunks offer twice the
+    // budget in candidates (with exactly the budget every candidate would be kept, which
+    // the merge cannot tell from a chunk hiding better blocks: the row would always take
+    // the exact path)
     constexpr int kKP = 32;
     // (rows with too few chunks for candidates are selected from their full key row)
     if (p->use_dec && p->n_tiles > 0) {
         int ch = 1024;
-        while (ch > 64 && (p->max_score_blocks / ch) * kKP < p->topk) ch /= 2;
+        while (ch > 64 && (p->max_score_blocks / ch) * kKP < 2 * (int64_t)p->topk) ch /= 2;
         p->local_ch = ch;
         p->max_chunks = (int)((p->max_score_blocks + ch - 1) / ch);
         if (p->max_chunks > kMaxGridY) return QSA_ERR_UNSUPPORTED;
@@ -280,9 +283,12 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     if (p->tq > 0) {
         int64_t ns = (1024 + 2 * p->tq - 1) / (2 * p->tq);
         p->nsplit = (int)std::min<int64_t>(64, std::max<int64_t>(1, ns));
-        // decode rows merged inside the attention: a workgroup's 4 waves (splits) must
-        // belong to one row, so the 2 * nsplit waves of a row come in whole workgroups
-        if (p->local_ch > 0 && p->nsplit > 1) p->nsplit += p->nsplit & 1;
+        // a workgroup's 4 waves are consecutive splits of one (row, KV head) when nsplit
+        // is a multiple of 4: they merge their partials through LDS first (4x fewer
+        // partials for the combine). Decode rows merged inside the attention need at
+        // least whole rows per workgroup (nsplit even).
+        if (p->nsplit >= 4) p->nsplit = (p->nsplit + 3) / 4 * 4;
+        else if (p->local_ch > 0 && p->nsplit > 1) p->nsplit += p->nsplit & 1;
     }
     // workspace: [control block][seq table][selection][scores | attention partials]
     const size_t ctl_b = (size_t)qsa::CTL_WORDS * sizeof(uint32_t);

@@ -427,7 +427,7 @@ constexpr int MAX_GROUPS = 4;
 // the KP-entry lists of chunks c0, c0+1, ... of a row with nv visible blocks: returns
 // false if a chunk holding more than KP of the row's blocks had all KP candidates kept
 // (only such a chunk can hide a better block, so only then can the result be inexact).
-template <bool WT_OUT>
+template <bool WT_OUT, bool WT_IN = true>
 __device__ __forceinline__ bool merge_candidates(const uint32_t *ck, const int32_t *ci, int n,
                                                  int k, int32_t *out_idx, uint32_t *out_key,
                                                  int64_t nv, int ch, int c0, int *viol,
@@ -439,8 +439,13 @@ __device__ __forceinline__ bool merge_candidates(const uint32_t *ck, const int32
     const bool have = 8 * tid < n;
 #pragma unroll
     for (int v4 = 0; v4 < 2; ++v4) {
-        kq[v4] = have ? load16_wt(ck + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
-        iq[v4] = have ? load16_wt(ci + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
+        if (WT_IN) {   // written by other workgroups of this kernel
+            kq[v4] = have ? load16_wt(ck + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
+            iq[v4] = have ? load16_wt(ci + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
+        } else {       // written by an earlier kernel
+            kq[v4] = have ? load16(ck + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
+            iq[v4] = have ? load16(ci + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
 #pragma unroll
     for (int v4 = 0; v4 < 2; ++v4) {
@@ -873,9 +878,9 @@ __global__ void __launch_bounds__(LOC_NT) merge_dec_kernel(LocalArgs a, DecodeTa
     if (cand_eligible(nv, a.topk, a.ch)) {
         const int64_t cbase = row * a.max_chunks * KP;
         const int nch_row = (int)((nv + a.ch - 1) / a.ch);
-        done = merge_candidates<false>(a.cand_key + cbase, a.cand_idx + cbase, nch_row * KP,
-                                       a.topk, a.sel + row * a.topk, nullptr, nv, a.ch, 0,
-                                       &sm.viol, &sm.tsm);
+        done = merge_candidates<false, false>(a.cand_key + cbase, a.cand_idx + cbase,
+                                              nch_row * KP, a.topk, a.sel + row * a.topk,
+                                              nullptr, nv, a.ch, 0, &sm.viol, &sm.tsm);
     }
     if (!done)   // uniform
         select_row_exact(a, d, row, a.sel + row * a.topk, sm.hist, sm.scan_sh, sm.found);
@@ -968,6 +973,7 @@ struct AttnArgs {
     int nsplit;
     int64_t nrows;
     int skip_dense;   // rows with at most topk visible blocks are left to the dense kernel
+    int wg_combine;   // nsplit % 4 == 0: a workgroup's 4 split waves merge into 1 partial
     int merge;        // decode: merge the rows of short tiles here (operands in `loc`)
     LocalArgs loc;
 };
@@ -995,10 +1001,12 @@ struct KVTile8 {
 // the MFMA operand layout (16 bytes of padding spread the rows over the banks)
 template <bool FP8> constexpr int kt_pitch() { return FP8 ? HD + 16 : 2 * HD + 16; }
 constexpr int KT_LDS_BYTES = 32 * (2 * HD + 16);   // one wave's tile (the larger, bf16)
+// the workgroup combine reuses the 4 tiles for 4 x 12 head records of 128 floats + (m, l)
+static_assert(4 * GQ * (HD + 2) * 4 <= 4 * KT_LDS_BYTES, "combine records fit the K tiles");
 
 template <bool FP8>
 __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv, int64_t row,
-                                            int g, int sp, uint8_t *klds,
+                                            int g, int sp, uint8_t *klds, uint8_t *wg_lds,
                                             const int32_t *srow) {
     using Tile = typename std::conditional<FP8, KVTile8, KVTile>::type;
     const int64_t t = rv.t;
@@ -1190,6 +1198,46 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
     }
 
     // lane (gr, col): acc[mt][i] = O[head col][dim 8*(4gr+i) + mt]
+    if (a.wg_combine) {
+        // the workgroup's 4 waves are splits 4j .. 4j+3 of (row, g): they merge their
+        // (m, l, acc) through LDS and write one partial, split j of nsplit / 4
+        const int w = threadIdx.x / WAVE;
+        float *rec = reinterpret_cast<float *>(wg_lds);             // [wave][head][128]
+        float *ml = rec + (ATT_NT / WAVE) * GQ * HD;               // [wave][head][2]
+        __syncthreads();   // every wave is done with its K tile (the LDS is reused)
+        if (col < GQ) {
+            float *r = rec + (w * GQ + col) * HD;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 8 * (4 * gr + i);
+                *reinterpret_cast<f32x4 *>(r + d0) = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+                *reinterpret_cast<f32x4 *>(r + d0 + 4) =
+                    f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+            }
+            if (gr == 0) { ml[(w * GQ + col) * 2] = m_run; ml[(w * GQ + col) * 2 + 1] = l_run; }
+        }
+        __syncthreads();
+        const int nsw = a.nsplit / 4;
+        for (int hh = 0; hh < GQ / 4; ++hh) {   // wave w: heads 3w .. 3w+2, lane l: dims 2l, 2l+1
+            const int h = (GQ / 4) * w + hh;
+            float mw[4], M = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { mw[i] = ml[(i * GQ + h) * 2]; M = fmaxf(M, mw[i]); }
+            float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float f = mw[i] == -INFINITY ? 0.f : exp2f(mw[i] - M);
+                L += ml[(i * GQ + h) * 2 + 1] * f;
+                const float2 x = *reinterpret_cast<const float2 *>(rec + (i * GQ + h) * HD + 2 * l);
+                o0 += x.x * f;
+                o1 += x.y * f;
+            }
+            float *pp = a.part + row * part_stride_row(nsw) + ((int64_t)(sp / 4) * HQ + g * GQ + h) * PREC;
+            *reinterpret_cast<float2 *>(pp + 2 * l) = float2{o0, o1};
+            if (l == 0) { pp[HD] = M; pp[HD + 1] = L; }
+        }
+        return;
+    }
     if (col >= GQ) return;
     if (a.nsplit == 1) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -1239,7 +1287,7 @@ attend_kernel(AttnArgs a) {
     if (!attend_item(a, row, g, sp)) return;
     const RowView rv = tab_row(a.tab, a.batch, a.topk, row);
     if (a.skip_dense && nvis_of(rv.t) <= a.topk) return;   // uniform over the wave
-    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES,
+    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES, klds,
                      a.sel + row * a.topk);
 }
 
@@ -1273,9 +1321,10 @@ attend_dec_kernel(AttnArgs a, DecodeTables d) {
         if (cand_eligible(nv, a.topk, a.loc.ch)) {
             const int64_t cbase = row * a.loc.max_chunks * KP;
             const int nch_row = (int)((nv + a.loc.ch - 1) / a.loc.ch);
-            done = merge_candidates<false>(a.loc.cand_key + cbase, a.loc.cand_idx + cbase,
-                                           nch_row * KP, a.topk, ms.ids, nullptr, nv,
-                                           a.loc.ch, 0, &ms.viol, &ms.tsm);
+            done = merge_candidates<false, false>(a.loc.cand_key + cbase,
+                                                  a.loc.cand_idx + cbase, nch_row * KP, a.topk,
+                                                  ms.ids, nullptr, nv, a.loc.ch, 0, &ms.viol,
+                                                  &ms.tsm);
         }
         if (!done)   // uniform
             select_row_exact(a.loc, d, row, ms.ids, ms.hist, ms.scan_sh, ms.found);
@@ -1285,7 +1334,7 @@ attend_dec_kernel(AttnArgs a, DecodeTables d) {
             for (int i = threadIdx.x; i < a.topk; i += ATT_NT) a.loc.sel[row * a.topk + i] = ms.ids[i];
         srow = ms.ids;
     }
-    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES, srow);
+    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES, klds, srow);
 }
 
 // =============================================================== combine
@@ -1528,6 +1577,7 @@ hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, i
     a.k_scale = fp8 ? fp8->k_scale : nullptr; a.v_scale = fp8 ? fp8->v_scale : nullptr;
     a.nsplit = nsplit; a.nrows = n_rows;
     a.skip_dense = skip_dense && !d && nsplit == 1;
+    a.wg_combine = nsplit >= 4 && nsplit % 4 == 0;
     const int64_t waves = n_rows * HKV * nsplit;
     const int64_t wgs = (waves + ATT_NT / WAVE - 1) / (ATT_NT / WAVE);
     trace_before(4, st);
@@ -1545,8 +1595,8 @@ hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, i
     if (e != hipSuccess || nsplit == 1) return e;
     const int64_t cw = (n_rows * HQ + CMB_NT / WAVE - 1) / (CMB_NT / WAVE);
     trace_before(5, st);
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)cw), dim3(CMB_NT), 0, st, part, nsplit,
-                       n_rows, out, lse);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)cw), dim3(CMB_NT), 0, st, part,
+                       a.wg_combine ? nsplit / 4 : nsplit, n_rows, out, lse);
     return trace_after(st, hipGetLastError());
 }
 
