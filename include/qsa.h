@@ -73,7 +73,8 @@ typedef enum {
     QSA_ERR_NULL = 1,        /* a required pointer is NULL                         */
     QSA_ERR_SHAPE = 2,       /* cu_* not starting at 0, decreasing, q_b > L_b,
                                 totals beyond int32, topk outside [1, 512]          */
-    QSA_ERR_UNSUPPORTED = 3, /* dims other than 24 / 2 / 128 / 4 / 64 / block 4    */
+    QSA_ERR_UNSUPPORTED = 3, /* dims other than 24 / 2 / 128 / 4 / 64 / block 4;
+                                attention calls: a sequence over 4,194,304 tokens  */
     QSA_ERR_WORKSPACE = 4,   /* ws_bytes smaller than qsa_workspace_size()          */
     QSA_ERR_DEVICE = 5       /* a launch failed (hipGetLastError)                   */
 } qsa_status;

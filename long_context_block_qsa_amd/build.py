@@ -20,6 +20,9 @@ FLAGS = [
     "-fvisibility=hidden",
     # keep fp32 arithmetic out of packed (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the attention rescales them with VALU
+    # instructions, which cannot address AGPRs (every tile would copy them back and forth)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wall", "-Wno-unused-result",
 ]
 

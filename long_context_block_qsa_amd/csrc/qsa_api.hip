@@ -92,6 +92,7 @@ struct Plan {
     int64_t n_tiles = 0;        // score tiles (4 query rows each)
     int64_t n_slots = 0;        // fp32 score slots
     int64_t max_score_blocks = 0;
+    int64_t max_len = 0;        // longest sequence
     int64_t max_cmp_full = 0;   // most complete blocks in a sequence
     int64_t max_cmp_incr = 0;   // most blocks holding a query token
     int local_ch = 0;           // > 0: decode path, blocks per chunk
@@ -223,6 +224,7 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
             nq = (int64_t)cq[b + 1] - cq[b];
             if (nq < 0 || nq > L) return QSA_ERR_SHAPE;
         }
+        p->max_len = std::max(p->max_len, L);
         p->max_cmp_full = std::max(p->max_cmp_full, L / qsa::BS);
         if (nq > 0)
             p->max_cmp_incr = std::max(p->max_cmp_incr, L / qsa::BS - (L - nq) / qsa::BS);
@@ -409,6 +411,9 @@ qsa_status run_attend(const Plan &p, const qsa_bf16 *q, const qsa_bf16 *k, const
     return QSA_OK;
 }
 
+// The attention addresses a sequence's K and V with 32-bit byte offsets.
+constexpr int64_t kMaxAttendLen = int64_t(1) << 22;
+
 qsa_status attend_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
                          const qsa_bf16 *k, const qsa_bf16 *v, const qsa::Fp8Kv *fp8,
                          const int32_t *sel, float *out, float *lse, void *ws, size_t ws_bytes,
@@ -416,6 +421,7 @@ qsa_status attend_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_b
     Plan p;
     qsa_status st = make_plan(dims, seqs, true, &p);
     if (st != QSA_OK) return st;
+    if (p.max_len > kMaxAttendLen) return QSA_ERR_UNSUPPORTED;
     if (p.tq == 0) return QSA_OK;
     if (!q || !sel || !out) return QSA_ERR_NULL;
     if (fp8 ? (!fp8->k8 || !fp8->v8 || !fp8->k_scale || !fp8->v_scale) : (!k || !v))
@@ -441,6 +447,7 @@ qsa_status forward_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_
     Plan p;
     qsa_status st = make_plan(dims, seqs, true, &p);
     if (st != QSA_OK) return st;
+    if (p.max_len > kMaxAttendLen) return QSA_ERR_UNSUPPORTED;
     if (p.tq == 0) return QSA_OK;
     if (!q || !out) return QSA_ERR_NULL;
     if (fp8 ? (!fp8->k8 || !fp8->v8 || !fp8->k_scale || !fp8->v_scale) : (!k || !v))
@@ -655,6 +662,7 @@ qsa_status qsa_forward_noalloc(const qsa_dims *dims, const qsa_seqs *seqs, const
     Plan p;
     qsa_status st = make_plan(dims, seqs, true, &p);
     if (st != QSA_OK) return st;
+    if (p.max_len > kMaxAttendLen) return QSA_ERR_UNSUPPORTED;
     if (p.tq == 0) return QSA_OK;
     if (p.ws_bytes > (size_t)QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_WORKSPACE;
     if (!q || !out) return QSA_ERR_NULL;

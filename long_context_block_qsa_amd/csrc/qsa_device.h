@@ -155,6 +155,17 @@ __device__ __forceinline__ int find_seq(int n, int64_t x, F key) {
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+// Two fp32 values as one word of bf16 (low half = a), round to nearest even: the
+// gfx950 conversion instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+    const bf16x2_t h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Third word of a raw buffer resource (gfx9 family: untyped 32-bit data, no swizzle).
+constexpr int kBufWord3 = 0x00020000;
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);

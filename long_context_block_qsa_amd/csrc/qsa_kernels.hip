@@ -984,8 +984,9 @@ __device__ __forceinline__ int64_t part_stride_row(int nsplit) {
 
 // K and V rows of the lane's 8 P keys (keys 4gr..4gr+3 and 16+4gr..16+4gr+3 of the tile),
 // dims 8col .. 8col+7: each load instruction reads whole 256-byte rows, one per 16 lanes.
+// bf16: K goes from memory straight into the wave's LDS tile (buffer loads with an LDS
+// destination), V into registers.
 struct KVTile {
-    u32x4 kt[8];
     u32x4 vr[8];
     uint32_t valid;  // bit 4u+i: key j0 + 16u + 4gr + i is attended
 };
@@ -997,12 +998,28 @@ struct KVTile8 {
     float ks[8], vs[8];
     uint32_t valid;
 };
-// LDS row pitch (bytes) of the per-wave K tile that turns the row-per-16-lanes loads into
-// the MFMA operand layout (16 bytes of padding spread the rows over the banks)
+// LDS row pitch (bytes) of the per-wave FP8 K tile that turns the row-per-16-lanes loads
+// into the MFMA operand layout (16 bytes of padding spread the rows over the banks)
 template <bool FP8> constexpr int kt_pitch() { return FP8 ? HD + 16 : 2 * HD + 16; }
-constexpr int KT_LDS_BYTES = 32 * (2 * HD + 16);   // one wave's tile (the larger, bf16)
+// bf16 K tiles: two per wave (the tile being processed and the next one, 8 KiB each).
+// Load instruction e (key e & 3 of the lane group's slot of tile half e >> 2) writes
+// 1 KiB: lane (gr, c) -> bytes e * 1024 + gr * 256 + c * 16 of the tile. The lane loads
+// 16-byte piece c ^ (4 * (e & 3) + gr) of its key's 256-byte row, so that the MFMA
+// operand reads (16 lanes reading 16 different keys' same piece) spread over all banks.
+constexpr int KT_TILE_BYTES = 32 * 2 * HD;
+constexpr int KT_LDS_BYTES = 2 * KT_TILE_BYTES;   // one wave's tiles (larger than FP8's)
+static_assert(32 * (HD + 16) <= KT_LDS_BYTES, "the FP8 tile fits");
 // the workgroup combine reuses the 4 tiles for 4 x 12 head records of 128 floats + (m, l)
 static_assert(4 * GQ * (HD + 2) * 4 <= 4 * KT_LDS_BYTES, "combine records fit the K tiles");
+
+// Waits until at most N vector memory operations of this wave are outstanding (they
+// complete in issue order); used for buffer loads whose destination is LDS, which the
+// compiler does not track.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
 
 template <bool FP8>
 __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv, int64_t row,
@@ -1043,46 +1060,89 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
     for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
+    // K and V are read through buffer resources spanning the tokens 0..t of the row's
+    // sequence (the only keys it may attend): offsets are 32-bit byte offsets from the
+    // sequence start (t < 2^23, checked by the host), a slot's 4 keys sit at immediate
+    // offsets of 512 bytes, and anything outside (unused slots, keys past t) reads 0.
     const int64_t kv0 = rv.k0;
-    const int64_t safe_tok = kv0 + t;  // always a valid key row
-    const uint16_t *kbase = a.k + g * HD;
-    const uint16_t *vbase = a.v + g * HD;
+    const uint32_t kv_bytes = (uint32_t)((t + 1) * (FP8 ? HKV * HD : HKV * HD * 2));
+    const __amdgpu_buffer_rsrc_t kres = FP8
+        ? __builtin_amdgcn_make_buffer_rsrc((void *)(a.k8 + kv0 * HKV * HD), 0, (int)kv_bytes, kBufWord3)
+        : __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + kv0 * HKV * HD), 0, (int)kv_bytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t vres = FP8
+        ? __builtin_amdgcn_make_buffer_rsrc((void *)(a.v8 + kv0 * HKV * HD), 0, (int)kv_bytes, kBufWord3)
+        : __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + kv0 * HKV * HD), 0, (int)kv_bytes, kBufWord3);
+    const uint32_t sc_bytes = (uint32_t)((t + 1) * HKV * 4);
+    const __amdgpu_buffer_rsrc_t ksres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(FP8 ? a.k_scale + kv0 * HKV : nullptr), 0, FP8 ? (int)sc_bytes : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t vsres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(FP8 ? a.v_scale + kv0 * HKV : nullptr), 0, FP8 ? (int)sc_bytes : 0, kBufWord3);
+    constexpr uint32_t TOK_BYTES = FP8 ? HKV * HD : HKV * HD * 2;    // one token's K (or V) row
+    constexpr uint32_t OFF_NONE = 0xfffff000u;                       // beyond every buffer
 
-    // first token of slot sl (block ids of the current 64-slot group held in `cur`)
-    auto slot_token0 = [&](int sl, int32_t cur, bool &ok) -> int64_t {
+    // slot sl (block ids of the current 64-slot group held in `cur`): its first token and
+    // which of its 4 keys are attended (bits), given the split's positions [p_lo, p_hi)
+    auto slot_first = [&](int sl, int32_t cur, uint32_t &bits) -> int64_t {
         const int32_t bid = __shfl(cur, sl & 63);
+        bits = 0u;
+        if (4 * sl >= p_hi) return -1;
         if (sl < nsel) {
-            ok = bid >= 0 && bid < nv;
-            return kv0 + (int64_t)BS * bid;
+            if (bid >= 0 && bid < nv) { bits = 0xfu; return (int64_t)BS * bid; }
+            return -1;
         }
-        ok = sl == nsel && ntail > 0;
-        return kv0 + (int64_t)BS * nv;
+        if (sl == nsel && ntail > 0) { bits = (1u << ntail) - 1u; return (int64_t)BS * nv; }
+        return -1;
     };
-    auto load_tile = [&](int j0, int32_t cur) -> Tile {
+    // bf16 K: the lane's byte offset of piece c ^ (4i + gr) within a key row, for key i
+    uint32_t kswz[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kswz[i] = 16u * (uint32_t)(col ^ (4 * i + gr));
+    auto load_tile = [&](int j0, int32_t cur, int buf) -> Tile {
         Tile T;
         T.valid = 0;
+        uint32_t ob[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int sl = (j0 >> 2) + 4 * h + gr;
-            bool okb;
-            const int64_t tok0 = slot_token0(sl, cur, okb);
+            uint32_t bits;
+            const int64_t f = slot_first(sl, cur, bits);
+            T.valid |= bits << (4 * h);
+            ob[h] = f >= 0 ? (uint32_t)f * TOK_BYTES + g * HD * (FP8 ? 1 : 2) : OFF_NONE;
+        }
+        if constexpr (!FP8) {
+            // K: 8 loads into the LDS tile (every K load of a tile precedes its V loads)
+            typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int p = 4 * sl + i;
-                const bool ok = okb && p < p_hi && (sl < nsel || i < ntail);
-                const int64_t tok = ok ? tok0 + i : safe_tok;
-                if constexpr (FP8) {
-                    T.kt[4 * h + i] = *reinterpret_cast<const uint2 *>(
-                        a.k8 + tok * (HKV * HD) + g * HD + 8 * col);
-                    T.vr[4 * h + i] = *reinterpret_cast<const uint2 *>(
-                        a.v8 + tok * (HKV * HD) + g * HD + 8 * col);
-                    T.ks[4 * h + i] = a.k_scale[tok * HKV + g];
-                    T.vs[4 * h + i] = a.v_scale[tok * HKV + g];
-                } else {
-                    T.kt[4 * h + i] = load16(kbase + tok * (HKV * HD) + 8 * col);
-                    T.vr[4 * h + i] = load16(vbase + tok * (HKV * HD) + 8 * col);
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        kres, (lds_void *)(klds + buf * KT_TILE_BYTES + (4 * h + i) * 1024), 16,
+                        ob[h] + i * TOK_BYTES + kswz[i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if constexpr (FP8) {
+                const uint32_t o = ob[h] + 8 * col;
+                const uint32_t os = ob[h] != OFF_NONE ? (ob[h] - g * HD) / TOK_BYTES * (HKV * 4) + g * 4
+                                                      : OFF_NONE;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    T.kt[4 * h + i] = __builtin_bit_cast(
+                        uint2, __builtin_amdgcn_raw_buffer_load_b64(kres, o + i * TOK_BYTES, 0, 0));
+                    T.vr[4 * h + i] = __builtin_bit_cast(
+                        uint2, __builtin_amdgcn_raw_buffer_load_b64(vres, o + i * TOK_BYTES, 0, 0));
+                    T.ks[4 * h + i] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(ksres, os + i * HKV * 4, 0, 0));
+                    T.vs[4 * h + i] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(vsres, os + i * HKV * 4, 0, 0));
                 }
-                if (ok) T.valid |= 1u << (4 * h + i);
+            } else {
+                const uint32_t o = ob[h] + 16 * col;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    T.vr[4 * h + i] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, o + i * TOK_BYTES, 0, 0));
             }
         }
         return T;
@@ -1095,40 +1155,45 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
 #pragma unroll
     for (int j = 1; j < KMAX / WAVE; ++j)
         if (cur_grp == j) cur = v[j];
-    Tile nxt;
-    if (p_lo < p_hi) nxt = load_tile(p_lo, cur);
-    for (int j0 = p_lo; j0 < p_hi; j0 += 32) {
-        const Tile T = nxt;
-        const int jn = j0 + 32;
-        if (jn < p_hi) {
-            if ((jn >> 8) != cur_grp) { cur_grp = jn >> 8; cur = group_ids(cur_grp); }
-            nxt = load_tile(jn, cur);
-        }
+    // the tiles alternate between two register sets (ta, tb) so that the next tile's
+    // loads never need a copy of the one being processed
+    // next_loaded: the next tile's loads were issued after this tile's (bf16: its K tile
+    // in LDS is complete once at most that tile's 16 loads are outstanding)
+    auto process = [&](const Tile &T, int j0, int buf, bool next_loaded) {
         // ---- logits S^T for keys j0 .. j0+31 (lane: keys j0+16u+4gr+i, head col)
         float z[8];
         float mx = -INFINITY;
-        // the K rows go through this wave's LDS tile into the MFMA A layout (lane: key
-        // 16u + col, dims 32m + 8gr)
+        // the K rows reach the MFMA A layout (lane: key 16u + col, dims 32m + 8gr)
+        // through this wave's LDS tile
         constexpr int KP = kt_pitch<FP8>();
-        constexpr int EB = FP8 ? 1 : 2;   // bytes per element
-        wave_lds_sync();   // the previous tile's reads are done
+        if constexpr (FP8) {
+            wave_lds_sync();   // the previous tile's reads are done
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint8_t *dst = klds + (16 * (e >> 2) + 4 * gr + (e & 3)) * KP + 8 * EB * col;
-            if constexpr (FP8) *reinterpret_cast<uint2 *>(dst) = T.kt[e];
-            else *reinterpret_cast<u32x4 *>(dst) = T.kt[e];
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<uint2 *>(klds + (16 * (e >> 2) + 4 * gr + (e & 3)) * KP + 8 * col) =
+                    T.kt[e];
+            wave_lds_sync();
+        } else {
+            if (next_loaded) wait_vmcnt<16>();
+            else wait_vmcnt<0>();
         }
-        wave_lds_sync();
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const uint8_t *src = klds + (16 * u + col) * KP + (32 * m + 8 * gr) * EB;
-                if constexpr (FP8)
+                if constexpr (FP8) {
+                    const uint8_t *src = klds + (16 * u + col) * KP + 32 * m + 8 * gr;
                     c4 = mfma_bf16_16x16x32(e4m3x8_to_bf16x8(*reinterpret_cast<const uint2 *>(src)),
                                             qb[m], c4);
-                else c4 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4 *>(src), qb[m], c4);
+                } else {
+                    // key 16u + col = instruction 4u + (col & 3), lane group col >> 2;
+                    // piece 4m + gr sits at column (4m + gr) ^ (4 (col & 3) + (col >> 2))
+                    const int e = 4 * u + (col & 3), kg = col >> 2;
+                    const int cc = (4 * m + gr) ^ (4 * (col & 3) + kg);
+                    const uint8_t *src = klds + buf * KT_TILE_BYTES + e * 1024 + kg * 256 + 16 * cc;
+                    c4 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4 *>(src), qb[m], c4);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1140,7 +1205,7 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
             }
         }
         mx = wave_max_xor_16_32(mx);
-        if (mx == -INFINITY) continue;  // no attended key in the tile (uniform over the wave)
+        if (mx == -INFINITY) return;  // no attended key in the tile (uniform over the wave)
         // the softmax reference m_run (with acc and l_run) moves only when some head's
         // tile maximum exceeds it by more than 2^8, so most tiles skip rescaling the
         // accumulators; every probability exp2(z - m_run) stays at most 2^8
@@ -1155,7 +1220,8 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
         float p[8], rs = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            p[e] = z[e] == -INFINITY ? 0.f : exp2f(z[e] - m_run);
+            // z - m_run <= 8; results below 2^-126 may flush to 0 (negligible weights)
+            p[e] = z[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[e] - m_run);
             rs += p[e];
         }
         l_run += wave_sum_xor_16_32(rs);
@@ -1171,11 +1237,11 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
         u32x4 ph, pl;
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
-            const uint32_t h0 = f32_to_bf16_rne(pv[2 * q2]), h1 = f32_to_bf16_rne(pv[2 * q2 + 1]);
-            const float r0 = pv[2 * q2] - __uint_as_float(h0 << 16);
-            const float r1 = pv[2 * q2 + 1] - __uint_as_float(h1 << 16);
-            ph[q2] = h0 | (h1 << 16);
-            pl[q2] = f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16);
+            const uint32_t hh = pack_bf16x2_rne(pv[2 * q2], pv[2 * q2 + 1]);
+            const float r0 = pv[2 * q2] - __uint_as_float(hh << 16);
+            const float r1 = pv[2 * q2 + 1] - __uint_as_float(hh & 0xffff0000u);
+            ph[q2] = hh;
+            pl[q2] = pack_bf16x2_rne(r0, r1);
         }
         u32x4 vb[8];
 #pragma unroll
@@ -1195,6 +1261,27 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
             acc[mt] = mfma_bf16_16x16x32(va, ph, acc[mt]);
             acc[mt] = mfma_bf16_16x16x32(va, pl, acc[mt]);
         }
+    };
+    auto next_ids = [&](int jn) {
+        if ((jn >> 8) != cur_grp) { cur_grp = jn >> 8; cur = group_ids(cur_grp); }
+    };
+    // (the scheduling barriers keep each tile's loads together and in program order, which
+    // the LDS-destination waits count on)
+    Tile ta, tb;
+    if (p_lo < p_hi) ta = load_tile(p_lo, cur, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int j0 = p_lo; j0 < p_hi; j0 += 64) {
+        const bool n1 = j0 + 32 < p_hi;
+        if (n1) { next_ids(j0 + 32); tb = load_tile(j0 + 32, cur, 1); }
+        __builtin_amdgcn_sched_barrier(0);
+        process(ta, j0, 0, n1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!n1) break;
+        const bool n2 = j0 + 64 < p_hi;
+        if (n2) { next_ids(j0 + 64); ta = load_tile(j0 + 64, cur, 0); }
+        __builtin_amdgcn_sched_barrier(0);
+        process(tb, j0 + 32, 1, n2);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // lane (gr, col): acc[mt][i] = O[head col][dim 8*(4gr+i) + mt]
@@ -1339,8 +1426,11 @@ attend_dec_kernel(AttnArgs a, DecodeTables d) {
 
 // =============================================================== combine
 // One wave per (row, head): lane s reads split s's (m, l); the merged output is the
-// weighted sum of the split accumulators in split order (deterministic).
+// weighted sum of the split accumulators in split order (deterministic). Every load is
+// issued before the first reduction (the accumulators do not depend on the weights), so
+// the kernel waits for memory once.
 constexpr int CMB_NT = 256;
+constexpr int CMB_MAXS = 16;   // splits per (row, head) the combine reads in registers
 
 __global__ void __launch_bounds__(CMB_NT)
 combine_kernel(const float *__restrict__ part, int nsplit, int64_t nrows,
@@ -1352,27 +1442,51 @@ combine_kernel(const float *__restrict__ part, int nsplit, int64_t nrows,
     const int l = lane_id();
     const float *pr = part + row * part_stride_row(nsplit) + (int64_t)head * PREC;
     const int64_t sstride = (int64_t)HQ * PREC;
-    const float ms = l < nsplit ? pr[l * sstride + HD] : -INFINITY;
-    const float ls = l < nsplit ? pr[l * sstride + HD + 1] : 0.f;
-    float M = ms;
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
-    const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    float Lsum = ls * f;
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) Lsum += __shfl_xor(Lsum, d);
+    float ms = -INFINITY, ls = 0.f;
+    if (l < nsplit) { ms = pr[l * sstride + HD]; ls = pr[l * sstride + HD + 1]; }
     float o0 = 0.f, o1 = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += 16) {
-        float2 v[16];
+    float M = -INFINITY, Lsum = 0.f;
+    if (nsplit <= CMB_MAXS) {
+        float2 v[CMB_MAXS];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            v[j] = s0 + j < nsplit ? *reinterpret_cast<const float2 *>(pr + (s0 + j) * sstride + 2 * l)
-                                   : float2{0.f, 0.f};
+        for (int j = 0; j < CMB_MAXS; ++j)
+            v[j] = j < nsplit ? *reinterpret_cast<const float2 *>(pr + j * sstride + 2 * l)
+                              : float2{0.f, 0.f};
+        M = ms;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float fs = __shfl(f, (s0 + j) & 63);
+        for (int d = 1; d < CMB_MAXS; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
+        M = __shfl(M, 0);
+        const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+        Lsum = ls * f;
+#pragma unroll
+        for (int d = 1; d < CMB_MAXS; d <<= 1) Lsum += __shfl_xor(Lsum, d);
+        Lsum = __shfl(Lsum, 0);
+#pragma unroll
+        for (int j = 0; j < CMB_MAXS; ++j) {
+            const float fs = __shfl(f, j);
             o0 += v[j].x * fs;
             o1 += v[j].y * fs;
+        }
+    } else {
+        M = ms;
+#pragma unroll
+        for (int d = 1; d < WAVE; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
+        const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+        Lsum = ls * f;
+#pragma unroll
+        for (int d = 1; d < WAVE; d <<= 1) Lsum += __shfl_xor(Lsum, d);
+        for (int s0 = 0; s0 < nsplit; s0 += 16) {
+            float2 v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                v[j] = s0 + j < nsplit ? *reinterpret_cast<const float2 *>(pr + (s0 + j) * sstride + 2 * l)
+                                       : float2{0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float fs = __shfl(f, (s0 + j) & 63);
+                o0 += v[j].x * fs;
+                o1 += v[j].y * fs;
+            }
         }
     }
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
