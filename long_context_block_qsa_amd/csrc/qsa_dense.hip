@@ -9,18 +9,18 @@
 // instead of gathering them row by row they are staged once per workgroup in LDS and
 // shared by DN_ROWS consecutive query rows x the 12 query heads of one KV head.
 //
-// Workgroup = (dense tile of DN_ROWS = 16 rows, KV head g); 4 waves of 4 rows each.
-// A wave's 48 query vectors (4 rows x 12 heads) are 3 MFMA column tiles of 16. Per
-// tile of 32 keys:
-//   S^T[32 keys x 48] = K (A operand from LDS, bf16) x Q^T (B operand, registers):
-//     3 column tiles x 2 key halves x 4 steps of MFMA 16x16x32 over the 128 dims;
+// Workgroup = (dense tile of DN_ROWS = 16 rows, KV head g): its 192 query vectors (16
+// rows x 12 heads, vector v = row * 12 + head) are 12 MFMA column tiles of 16, two per
+// wave (6 waves). Per tile of 32 keys, each wave computes
+//   S^T[32 keys x 32] = K (A operand from LDS, bf16) x Q^T (B operand, registers):
+//     2 column tiles x 2 key halves x 4 steps of MFMA 16x16x32 over the 128 dims;
 //   online softmax per query vector in base 2 (the reference maximum moves only when a
 //     vector's maximum grows by more than 2^8, so probabilities stay at most 2^8);
-//   O^T[128 dims x 48] += V^T (A operand, fp16 rows staged in LDS) x P^T (fp16):
-//     8 dim tiles x 3 column tiles of MFMA 16x16x32 f16. V is converted bf16 -> fp16
-//     once, when the workgroup stages it (bf16 values of N(0,1)-sized data are exact
-//     in fp16 unless tinier than 2^-14, where the fp16 step is 2^-24); P in fp16 keeps
-//     11 bits.
+//   O^T[128 dims x 32] += V^T (A operand, bf16 rows staged in LDS) x P^T: P is split
+//     into bf16 hi + lo parts (about 16 significant bits), 2 x 8 dim tiles x 2 column
+//     tiles of MFMA 16x16x32 bf16 (the same precision as the sparse rows' kernel; P in
+//     fp16 alone left errors of 5e-4 in the outputs, which the attention backward, fed
+//     these outputs, carries into its gradients).
 // Key order within the MFMA contraction is permuted as in the sparse kernel (k-slot
 // 8gr + i holds key 4gr + i for i < 4 and 16 + 4gr + i - 4 otherwise), identically on
 // both operands. Tiles are numbered from the end so that the longest rows start first.
@@ -29,26 +29,14 @@
 
 namespace qsa {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4 mfma_f16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// Two fp32 values as one word of fp16 (round to nearest even).
-__device__ __forceinline__ uint32_t pack_f16(float x, float y) {
-    const f16x2 h = {(_Float16)x, (_Float16)y};
-    return __builtin_bit_cast(uint32_t, h);
-}
-
-constexpr int DN_NT = 256;
+constexpr int DN_NQ = 2;                  // column tiles of 16 query vectors per wave
+constexpr int DN_WAVES = DN_ROWS * GQ / 16 / DN_NQ;   // 6
+constexpr int DN_NT = DN_WAVES * WAVE;
 constexpr int DN_KEYS = 32;
-constexpr int DN_NQ = 3;                  // column tiles of 16 query vectors per wave
 constexpr int DN_PITCH = 2 * HD + 16;     // LDS row pitch (bytes) of the K and V tiles
-static_assert(DN_ROWS == 4 * (DN_NT / WAVE), "4 rows per wave");
-static_assert(DN_NQ * 16 == 4 * GQ, "a wave's 4 rows x 12 heads fill 3 column tiles");
+constexpr int DN_STAGE_NT = DN_KEYS * 8;  // threads that stage a tile (32 bytes of K and V each)
+static_assert(DN_ROWS * GQ == 16 * DN_NQ * DN_WAVES, "column tiles split evenly over waves");
+static_assert(DN_STAGE_NT <= DN_NT, "enough threads to stage a tile");
 
 struct DenseArgs {
     const SeqInfo *tab;
@@ -59,7 +47,7 @@ struct DenseArgs {
     int64_t n_tiles;
 };
 
-__global__ void __launch_bounds__(DN_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(DN_NT)
 attend_dense_kernel(DenseArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t ks[DN_KEYS * DN_PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t vs[DN_KEYS * DN_PITCH];
@@ -74,23 +62,23 @@ attend_dense_kernel(DenseArgs a) {
     const int64_t row0 = s.q0 + i0;
     const int64_t t_last = t0 + nrows - 1;
     const int tid = threadIdx.x, w = tid / WAVE, l = lane_id(), gr = l >> 4, col = l & 15;
-    const int wrows = min(4, nrows - 4 * w);                  // this wave's rows (may be <= 0)
+    // this wave's rows: those of its query vectors 32w .. 32w + 31
+    const int r_lo = (16 * DN_NQ * w) / GQ, r_hi = (16 * DN_NQ * (w + 1) - 1) / GQ;
 
-    // Q^T operands: column tile nt, lane column col -> query vector 16nt + col = (row
-    // 4w + v / 12, head v % 12); dims 32m + 8gr .. +7 of step m
+    // Q^T operands: column tile nt, lane column col -> query vector v = 16 (DN_NQ w + nt)
+    // + col = (row v / 12, head v % 12); dims 32m + 8gr .. +7 of step m
     u32x4 qb[DN_NQ][4];
     int64_t tpos[DN_NQ];
 #pragma unroll
     for (int nt = 0; nt < DN_NQ; ++nt) {
-        const int vq = 16 * nt + col, rr = vq / GQ, hh = vq % GQ;
-        const bool ok = rr < wrows;
-        tpos[nt] = ok ? t0 + 4 * w + rr : -1;
-        const uint16_t *qp =
-            a.q + ((row0 + (ok ? 4 * w + rr : 0)) * HQ + g * GQ + hh) * HD + 8 * gr;
+        const int vq = 16 * (DN_NQ * w + nt) + col, rr = vq / GQ, hh = vq % GQ;
+        const bool ok = rr < nrows;
+        tpos[nt] = ok ? t0 + rr : -1;
+        const uint16_t *qp = a.q + ((row0 + (ok ? rr : 0)) * HQ + g * GQ + hh) * HD + 8 * gr;
 #pragma unroll
         for (int m = 0; m < 4; ++m) qb[nt][m] = ok ? load16(qp + 32 * m) : u32x4{0u, 0u, 0u, 0u};
     }
-    const int64_t wave_tmax = wrows > 0 ? t0 + 4 * w + wrows - 1 : -1;
+    const int64_t wave_tmax = r_lo < nrows ? t0 + min(r_hi, nrows - 1) : -1;
 
     f32x4 acc[DN_NQ][8];
 #pragma unroll
@@ -101,8 +89,10 @@ attend_dense_kernel(DenseArgs a) {
 #pragma unroll
     for (int nt = 0; nt < DN_NQ; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
 
-    // staging: thread -> (key tid / 8, 32-byte piece tid % 8) of the K and V rows
-    const int sk = tid >> 3, sp = tid & 7;
+    // staging: thread < DN_STAGE_NT -> (key tid / 8, 32-byte piece tid % 8) of the K and V
+    // rows
+    const bool stager = tid < DN_STAGE_NT;
+    const int sk = (tid >> 3) & (DN_KEYS - 1), sp = tid & 7;
     const uint16_t *kbase = a.k + (int64_t)s.k0 * (HKV * HD) + g * HD + 16 * sp;
     const uint16_t *vbase = a.v + (int64_t)s.k0 * (HKV * HD) + g * HD + 16 * sp;
     auto load_stage = [&](int64_t j0, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
@@ -117,22 +107,19 @@ attend_dense_kernel(DenseArgs a) {
         uint8_t *vd = vs + sk * DN_PITCH + 32 * sp;
         *reinterpret_cast<u32x4 *>(kd) = kr[0];
         *reinterpret_cast<u32x4 *>(kd + 16) = kr[1];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            u32x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = pack_f16(bf16_lo(vr[h][e]), bf16_hi(vr[h][e]));
-            *reinterpret_cast<u32x4 *>(vd + 16 * h) = o;
-        }
+        *reinterpret_cast<u32x4 *>(vd) = vr[0];
+        *reinterpret_cast<u32x4 *>(vd + 16) = vr[1];
     };
 
     u32x4 kr[2], vr[2];
-    load_stage(0, kr, vr);
-    store_stage(kr, vr);
+    if (stager) {
+        load_stage(0, kr, vr);
+        store_stage(kr, vr);
+    }
     __syncthreads();
     for (int64_t j0 = 0; j0 <= t_last; j0 += DN_KEYS) {
         const bool more = j0 + DN_KEYS <= t_last;
-        if (more) load_stage(j0 + DN_KEYS, kr, vr);   // next tile in flight during compute
+        if (more && stager) load_stage(j0 + DN_KEYS, kr, vr);   // next tile in flight
         if (j0 <= wave_tmax) {                         // uniform over the wave
             // ---- S^T: lane (gr, col) of column tile nt holds keys j0 + 16u + 4gr + i
             float z[DN_NQ][8];
@@ -156,8 +143,23 @@ attend_dense_kernel(DenseArgs a) {
                         z[nt][4 * u + i] = j <= tpos[nt] ? c[nt][i] * a.scale_log2 : -INFINITY;
                     }
             }
-            // ---- online softmax per query vector (column), P^T in fp16
-            u32x4 ph[DN_NQ];
+            // ---- V^T operands of the 8 dim tiles: lane rows are dims 8col + mt, its
+            // k-slot keys as above
+            u32x4 va[8];
+            {
+                u32x4 vrow[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    vrow[e] = *reinterpret_cast<const u32x4 *>(
+                        vs + (16 * (e >> 2) + 4 * gr + (e & 3)) * DN_PITCH + 16 * col);
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        va[mt][kk] = bf16_pair(vrow[2 * kk][mt >> 1], vrow[2 * kk + 1][mt >> 1], mt & 1);
+            }
+            // ---- per column tile: online softmax per query vector, P^T as bf16 hi + lo,
+            // O^T += V^T P^T
 #pragma unroll
             for (int nt = 0; nt < DN_NQ; ++nt) {
                 float mx = -INFINITY;
@@ -175,41 +177,37 @@ attend_dense_kernel(DenseArgs a) {
                 float p[8], rs = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    p[e] = z[nt][e] == -INFINITY ? 0.f : exp2f(z[nt][e] - m_run[nt]);
+                    p[e] = z[nt][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[nt][e] - m_run[nt]);
                     rs += p[e];
                 }
                 l_run[nt] += wave_sum_xor_16_32(rs);
+                u32x4 ph, pl;
 #pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2) ph[nt][q2] = pack_f16(p[2 * q2], p[2 * q2 + 1]);
-            }
-            // ---- O^T += V^T P^T: lane rows are dims 8col + mt, its k-slot keys as above
-            u32x4 vrow[8];
+                for (int q2 = 0; q2 < 4; ++q2) {
+                    const uint32_t hh = pack_bf16x2_rne(p[2 * q2], p[2 * q2 + 1]);
+                    ph[q2] = hh;
+                    pl[q2] = pack_bf16x2_rne(p[2 * q2] - __uint_as_float(hh << 16),
+                                             p[2 * q2 + 1] - __uint_as_float(hh & 0xffff0000u));
+                }
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                vrow[e] = *reinterpret_cast<const u32x4 *>(
-                    vs + (16 * (e >> 2) + 4 * gr + (e & 3)) * DN_PITCH + 16 * col);
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                u32x4 va;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    va[kk] = bf16_pair(vrow[2 * kk][mt >> 1], vrow[2 * kk + 1][mt >> 1], mt & 1);
-#pragma unroll
-                for (int nt = 0; nt < DN_NQ; ++nt)
-                    acc[nt][mt] = mfma_f16_16x16x32(va, ph[nt], acc[nt][mt]);
+                for (int mt = 0; mt < 8; ++mt) {
+                    acc[nt][mt] = mfma_bf16_16x16x32(va[mt], ph, acc[nt][mt]);
+                    acc[nt][mt] = mfma_bf16_16x16x32(va[mt], pl, acc[nt][mt]);
+                }
             }
         }
         __syncthreads();   // every wave is done with this tile
-        if (more) store_stage(kr, vr);
+        if (more && stager) store_stage(kr, vr);
         __syncthreads();
     }
 
-    // lane (gr, col), column tile nt: acc[nt][mt][i] = O[vector 16nt + col][dim 8(4gr+i) + mt]
+    // lane (gr, col), column tile nt: acc[nt][mt][i] = O[vector 16(DN_NQ w + nt) + col]
+    // [dim 8(4gr+i) + mt]
 #pragma unroll
     for (int nt = 0; nt < DN_NQ; ++nt) {
-        const int vq = 16 * nt + col, rr = vq / GQ, hh = vq % GQ;
-        if (rr >= wrows) continue;
-        const int64_t row = row0 + 4 * w + rr;
+        const int vq = 16 * (DN_NQ * w + nt) + col, rr = vq / GQ, hh = vq % GQ;
+        if (rr >= nrows) continue;
+        const int64_t row = row0 + rr;
         const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
         float *o = a.out + (row * HQ + g * GQ + hh) * HD;
 #pragma unroll

@@ -1007,10 +1007,12 @@ template <bool FP8> constexpr int kt_pitch() { return FP8 ? HD + 16 : 2 * HD + 1
 // 16-byte piece c ^ (4 * (e & 3) + gr) of its key's 256-byte row, so that the MFMA
 // operand reads (16 lanes reading 16 different keys' same piece) spread over all banks.
 constexpr int KT_TILE_BYTES = 32 * 2 * HD;
-constexpr int KT_LDS_BYTES = 2 * KT_TILE_BYTES;   // one wave's tiles (larger than FP8's)
-static_assert(32 * (HD + 16) <= KT_LDS_BYTES, "the FP8 tile fits");
-// the workgroup combine reuses the 4 tiles for 4 x 12 head records of 128 floats + (m, l)
-static_assert(4 * GQ * (HD + 2) * 4 <= 4 * KT_LDS_BYTES, "combine records fit the K tiles");
+// The two tiles of every wave live in two separate LDS arrays (kt0, kt1: one tile per
+// wave each), so that alias analysis can tell a read of one from a load in flight into
+// the other (the compiler then waits only for the loads the read depends on).
+static_assert(32 * (HD + 16) <= KT_TILE_BYTES, "the FP8 tile fits");
+// the workgroup combine reuses kt0 for 4 x 12 head records of 128 floats + (m, l)
+static_assert(4 * GQ * (HD + 2) * 4 <= 4 * KT_TILE_BYTES, "combine records fit the K tiles");
 
 // Waits until at most N vector memory operations of this wave are outstanding (they
 // complete in issue order); used for buffer loads whose destination is LDS, which the
@@ -1023,7 +1025,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <bool FP8>
 __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv, int64_t row,
-                                            int g, int sp, uint8_t *klds, uint8_t *wg_lds,
+                                            int g, int sp, uint8_t *kt0, uint8_t *kt1,
+                                            uint8_t *wg_lds,
                                             const int32_t *srow) {
     using Tile = typename std::conditional<FP8, KVTile8, KVTile>::type;
     const int64_t t = rv.t;
@@ -1100,12 +1103,13 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
     auto load_tile = [&](int j0, int32_t cur, int buf) -> Tile {
         Tile T;
         T.valid = 0;
-        uint32_t ob[2];
+        uint32_t ob[2], bits_h[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int sl = (j0 >> 2) + 4 * h + gr;
             uint32_t bits;
             const int64_t f = slot_first(sl, cur, bits);
+            bits_h[h] = bits;
             T.valid |= bits << (4 * h);
             ob[h] = f >= 0 ? (uint32_t)f * TOK_BYTES + g * HD * (FP8 ? 1 : 2) : OFF_NONE;
         }
@@ -1117,25 +1121,46 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        kres, (lds_void *)(klds + buf * KT_TILE_BYTES + (4 * h + i) * 1024), 16,
+                        kres, (lds_void *)((buf ? kt1 : kt0) + (4 * h + i) * 1024), 16,
                         ob[h] + i * TOK_BYTES + kswz[i], 0, 0, 0);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             if constexpr (FP8) {
                 const uint32_t o = ob[h] + 8 * col;
-                const uint32_t os = ob[h] != OFF_NONE ? (ob[h] - g * HD) / TOK_BYTES * (HKV * 4) + g * 4
-                                                      : OFF_NONE;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     T.kt[4 * h + i] = __builtin_bit_cast(
                         uint2, __builtin_amdgcn_raw_buffer_load_b64(kres, o + i * TOK_BYTES, 0, 0));
                     T.vr[4 * h + i] = __builtin_bit_cast(
                         uint2, __builtin_amdgcn_raw_buffer_load_b64(vres, o + i * TOK_BYTES, 0, 0));
-                    T.ks[4 * h + i] = __builtin_bit_cast(
-                        float, __builtin_amdgcn_raw_buffer_load_b32(ksres, os + i * HKV * 4, 0, 0));
-                    T.vs[4 * h + i] = __builtin_bit_cast(
-                        float, __builtin_amdgcn_raw_buffer_load_b32(vsres, os + i * HKV * 4, 0, 0));
+                }
+                // scales of the slot's first token (both heads, 8 bytes per token)
+                const uint32_t os = ob[h] != OFF_NONE ? (ob[h] - g * HD) / TOK_BYTES * (HKV * 4)
+                                                      : OFF_NONE;
+                if (bits_h[h] == 0xfu) {
+                    // a whole block: its 4 tokens' K and V scales are 32 contiguous bytes each
+                    // (one line), read with two 16-byte loads instead of four scattered ones
+                    const u32x4 k01 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ksres, os, 0, 0));
+                    const u32x4 k23 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ksres, os + 16, 0, 0));
+                    const u32x4 v01 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vsres, os, 0, 0));
+                    const u32x4 v23 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vsres, os + 16, 0, 0));
+                    T.ks[4 * h + 0] = __uint_as_float(g ? k01[1] : k01[0]);
+                    T.ks[4 * h + 1] = __uint_as_float(g ? k01[3] : k01[2]);
+                    T.ks[4 * h + 2] = __uint_as_float(g ? k23[1] : k23[0]);
+                    T.ks[4 * h + 3] = __uint_as_float(g ? k23[3] : k23[2]);
+                    T.vs[4 * h + 0] = __uint_as_float(g ? v01[1] : v01[0]);
+                    T.vs[4 * h + 1] = __uint_as_float(g ? v01[3] : v01[2]);
+                    T.vs[4 * h + 2] = __uint_as_float(g ? v23[1] : v23[0]);
+                    T.vs[4 * h + 3] = __uint_as_float(g ? v23[3] : v23[2]);
+                } else {   // the raw tail (tokens past t read 0) or no slot
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        T.ks[4 * h + i] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(ksres, os + i * HKV * 4 + g * 4, 0, 0));
+                        T.vs[4 * h + i] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(vsres, os + i * HKV * 4 + g * 4, 0, 0));
+                    }
                 }
             } else {
                 const uint32_t o = ob[h] + 16 * col;
@@ -1157,9 +1182,11 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
         if (cur_grp == j) cur = v[j];
     // the tiles alternate between two register sets (ta, tb) so that the next tile's
     // loads never need a copy of the one being processed
-    // next_loaded: the next tile's loads were issued after this tile's (bf16: its K tile
-    // in LDS is complete once at most that tile's 16 loads are outstanding)
-    auto process = [&](const Tile &T, int j0, int buf, bool next_loaded) {
+    // issue_next(): issues the next tile's loads once this tile's logits are computed, so
+    // that they are in flight during its softmax and PV products; until then nothing but
+    // this tile's loads is outstanding, and the bf16 K tile in LDS is complete once none
+    // is (the compiler waits for every LDS-destination load before such an LDS read)
+    auto process = [&](const Tile &T, int j0, int buf, auto &&issue_next) {
         // ---- logits S^T for keys j0 .. j0+31 (lane: keys j0+16u+4gr+i, head col)
         float z[8];
         float mx = -INFINITY;
@@ -1170,12 +1197,11 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
             wave_lds_sync();   // the previous tile's reads are done
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<uint2 *>(klds + (16 * (e >> 2) + 4 * gr + (e & 3)) * KP + 8 * col) =
+                *reinterpret_cast<uint2 *>(kt0 + (16 * (e >> 2) + 4 * gr + (e & 3)) * KP + 8 * col) =
                     T.kt[e];
             wave_lds_sync();
         } else {
-            if (next_loaded) wait_vmcnt<16>();
-            else wait_vmcnt<0>();
+            wait_vmcnt<0>();
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -1183,7 +1209,7 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 if constexpr (FP8) {
-                    const uint8_t *src = klds + (16 * u + col) * KP + 32 * m + 8 * gr;
+                    const uint8_t *src = kt0 + (16 * u + col) * KP + 32 * m + 8 * gr;
                     c4 = mfma_bf16_16x16x32(e4m3x8_to_bf16x8(*reinterpret_cast<const uint2 *>(src)),
                                             qb[m], c4);
                 } else {
@@ -1191,7 +1217,7 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
                     // piece 4m + gr sits at column (4m + gr) ^ (4 (col & 3) + (col >> 2))
                     const int e = 4 * u + (col & 3), kg = col >> 2;
                     const int cc = (4 * m + gr) ^ (4 * (col & 3) + kg);
-                    const uint8_t *src = klds + buf * KT_TILE_BYTES + e * 1024 + kg * 256 + 16 * cc;
+                    const uint8_t *src = (buf ? kt1 : kt0) + e * 1024 + kg * 256 + 16 * cc;
                     c4 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4 *>(src), qb[m], c4);
                 }
             }
@@ -1204,6 +1230,9 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
                 mx = fmaxf(mx, z[4 * u + i]);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_next();
+        __builtin_amdgcn_sched_barrier(0);
         mx = wave_max_xor_16_32(mx);
         if (mx == -INFINITY) return;  // no attended key in the tile (uniform over the wave)
         // the softmax reference m_run (with acc and l_run) moves only when some head's
@@ -1267,20 +1296,23 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
     };
     // (the scheduling barriers keep each tile's loads together and in program order, which
     // the LDS-destination waits count on)
+    // (tiles in ascending order: waves of nearby rows then reach the blocks that many rows
+    // select at about the same time, and share their lines in the caches; a row-dependent
+    // rotation of the start measured 37% slower on the ragged 64K prefill)
     Tile ta, tb;
     if (p_lo < p_hi) ta = load_tile(p_lo, cur, 0);
     __builtin_amdgcn_sched_barrier(0);
     for (int j0 = p_lo; j0 < p_hi; j0 += 64) {
         const bool n1 = j0 + 32 < p_hi;
-        if (n1) { next_ids(j0 + 32); tb = load_tile(j0 + 32, cur, 1); }
-        __builtin_amdgcn_sched_barrier(0);
-        process(ta, j0, 0, n1);
+        process(ta, j0, 0, [&] {
+            if (n1) { next_ids(j0 + 32); tb = load_tile(j0 + 32, cur, 1); }
+        });
         __builtin_amdgcn_sched_barrier(0);
         if (!n1) break;
         const bool n2 = j0 + 64 < p_hi;
-        if (n2) { next_ids(j0 + 64); ta = load_tile(j0 + 64, cur, 0); }
-        __builtin_amdgcn_sched_barrier(0);
-        process(tb, j0 + 32, 1, n2);
+        process(tb, j0 + 32, 1, [&] {
+            if (n2) { next_ids(j0 + 64); ta = load_tile(j0 + 64, cur, 0); }
+        });
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -1368,13 +1400,15 @@ __device__ __forceinline__ bool attend_item(const AttnArgs &a, int64_t &row, int
 template <bool FP8>
 __global__ void __launch_bounds__(ATT_NT)
 attend_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t klds[(ATT_NT / WAVE) * KT_LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t kt0[(ATT_NT / WAVE) * KT_TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t kt1[(ATT_NT / WAVE) * KT_TILE_BYTES];
     int64_t row;
     int g, sp;
     if (!attend_item(a, row, g, sp)) return;
     const RowView rv = tab_row(a.tab, a.batch, a.topk, row);
     if (a.skip_dense && nvis_of(rv.t) <= a.topk) return;   // uniform over the wave
-    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES, klds,
+    const int w = threadIdx.x / WAVE;
+    attend_body<FP8>(a, rv, row, g, sp, kt0 + w * KT_TILE_BYTES, kt1 + w * KT_TILE_BYTES, kt0,
                      a.sel + row * a.topk);
 }
 
@@ -1394,7 +1428,8 @@ attend_dec_kernel(AttnArgs a, DecodeTables d) {
     int64_t row;
     int g, sp;
     if (!attend_item(a, row, g, sp)) return;
-    __shared__ __attribute__((aligned(16))) uint8_t klds[(ATT_NT / WAVE) * KT_LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t kt0[(ATT_NT / WAVE) * KT_TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t kt1[(ATT_NT / WAVE) * KT_TILE_BYTES];
     __shared__ AttnMergeSmem ms;
     const DecRow r = d.row[row];
     const RowView rv = {r.k0, r.t, r.blk0, r.slot};
@@ -1421,7 +1456,8 @@ attend_dec_kernel(AttnArgs a, DecodeTables d) {
             for (int i = threadIdx.x; i < a.topk; i += ATT_NT) a.loc.sel[row * a.topk + i] = ms.ids[i];
         srow = ms.ids;
     }
-    attend_body<FP8>(a, rv, row, g, sp, klds + (threadIdx.x / WAVE) * KT_LDS_BYTES, klds, srow);
+    const int w = threadIdx.x / WAVE;
+    attend_body<FP8>(a, rv, row, g, sp, kt0 + w * KT_TILE_BYTES, kt1 + w * KT_TILE_BYTES, kt0, srow);
 }
 
 // =============================================================== combine

@@ -286,3 +286,24 @@ def test_noalloc_entry_point_validates_first():
     bad.head_dim = 64
     assert L.qsa_forward_noalloc(ctypes.byref(bad), ctypes.byref(small), f, f, f, f, f, f, f,
                                  f, f, f, None) == qsa.QSA_ERR_UNSUPPORTED
+
+
+def test_attention_length_limit():
+    """Attention calls address a sequence's K and V with 32-bit byte offsets: sequences over
+    4,194,304 tokens are refused (QSA_ERR_UNSUPPORTED) before any device call; scoring and
+    compression are not limited."""
+    d = qsa.make_dims()
+    L = qsa.lib()
+    f = ctypes.c_void_p(FAKE)
+    n = 4194304
+    ok = _seqs([0, 1], [0, n])
+    big = _seqs([0, 1], [0, n + 1])
+    st, nbytes = _ws(d, big)
+    assert st == 0
+    for s, expect in ((big, qsa.QSA_ERR_UNSUPPORTED), (ok, qsa.QSA_ERR_WORKSPACE)):
+        assert L.qsa_attend(ctypes.byref(d), ctypes.byref(s), f, f, f, f, f, f, f, 0,
+                            None) == expect
+        assert L.qsa_forward(ctypes.byref(d), ctypes.byref(s), f, f, f, f, f, f, f, f, f, f, f,
+                             0, None) == expect
+    assert L.qsa_forward_noalloc(ctypes.byref(d), ctypes.byref(big), f, f, f, f, f, f, f, f, f,
+                                 f, None) == qsa.QSA_ERR_UNSUPPORTED
