@@ -101,8 +101,10 @@ typedef struct {
 /* QSA_ABI_VERSION of the built library. */
 int32_t qsa_abi_version(void);
 
-/* Static, human-readable name of a status. */
-const char *qsa_status_string(qsa_status s);
+/* Static, human-readable name of a status value (a qsa_status; the parameter is a plain
+ * int so that any value a C caller passes is well defined: others name no status and
+ * give "unknown qsa_status"). */
+const char *qsa_status_string(int32_t status);
 
 /* Bytes of device workspace that qsa_select, qsa_attend and qsa_forward need for
  * these dims and sequences (one size serves all three). Host-only, no device call. */

@@ -48,7 +48,7 @@ _lib = None
 
 _SIGS = {
     "qsa_abi_version": ([], ctypes.c_int32),
-    "qsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "qsa_status_string": ([ctypes.c_int32], ctypes.c_char_p),
     "qsa_workspace_size": ([ctypes.c_void_p, ctypes.c_void_p,
                             ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "qsa_compress": ([ctypes.c_void_p] * 5, ctypes.c_int),

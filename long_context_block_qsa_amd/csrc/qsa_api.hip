@@ -568,7 +568,7 @@ extern "C" {
 
 int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
 
-const char *qsa_status_string(qsa_status s) {
+const char *qsa_status_string(int32_t s) {
     switch (s) {
     case QSA_OK: return "QSA_OK";
     case QSA_ERR_NULL: return "QSA_ERR_NULL: a required pointer is NULL";

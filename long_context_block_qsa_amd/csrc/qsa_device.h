@@ -630,10 +630,28 @@ __device__ __forceinline__ int wave_excl_small(int cnt) {
 
 // ---------------------------------------------------------------- write-through access
 // Data handed from one workgroup to another inside a kernel (possibly on another
-// XCD, whose L2 is not coherent with this one) is stored and loaded at agent scope:
-// the stores write through to the coherence point and the loads read from it. The
-// producer waits for its stores to complete before it signals (s_waitcnt), so no
-// cache-wide release fence is needed.
+// XCD, whose L2 is not coherent with this one) is stored and loaded at agent scope.
+//
+// The hand-off protocol (producer: store_wt of the data, wait_vmem, __syncthreads, one
+// relaxed agent-scope atomicAdd on a counter; consumer: the atomicAdd that completes
+// the count, __syncthreads, load_wt of the data) uses relaxed atomics only, so the HIP
+// memory model alone does not order it: the order comes from the CDNA hardware, by
+// these facts of the gfx9 (CDNA3/CDNA4) ISA and of the compiler's atomic lowering:
+//   1. an agent-scope atomic store or load is issued with device-scope cache bits, so
+//      the store is written through every non-coherent cache level (the XCD's L2
+//      included) and the load is served from the device-coherent level, never from a
+//      stale line in this XCD's L2;
+//   2. on gfx9, vector stores count in vmcnt and a store leaves the count only once it
+//      is acknowledged at the scope it was issued with, so after `s_waitcnt vmcnt(0)`
+//      every store_wt of the wave is visible device-wide;
+//   3. the counter atomic is performed at the device-coherent level and is issued after
+//      the barrier that follows every wave's wait, so a consumer that sees its count
+//      complete issues its loads after all the producers' data is visible.
+// A release/acquire atomic at agent scope would give the same order by the memory
+// model, at the cost of a write-back of the whole L2 (release) and an invalidation of
+// it (acquire) per hand-off; the data stored this way is exactly what needs no such
+// write-back. Code that hands data over must keep to the protocol: only store_wt /
+// load_wt / load16_wt on the handed-over words, and the wait before the barrier.
 __device__ __forceinline__ void store_wt(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

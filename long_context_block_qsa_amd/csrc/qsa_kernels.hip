@@ -754,6 +754,8 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
         if (rr + 1 < nrows) lds_barrier();   // wave lists are reused by the next row
     }
 
+    // (the order of this hand-off rests on the hardware facts listed with store_wt in
+    // qsa_device.h: candidates stored write-through, waited for, then counted)
     // hand over: the workgroup that completes the tile's last chunk merges the rows'
     // candidates; rows with more than MERGE_CHUNKS chunks merge groups of chunks first
     // (the last chunk of each group), then the group lists (the tile's last group)

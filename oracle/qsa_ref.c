@@ -78,15 +78,20 @@ static double e4m3_value(uint8_t b)
 
 double qsa_ref_e4m3_value(uint8_t b) { return e4m3_value(b); }
 
-/* Round x to the nearest E4M3 value, ties to even; finite magnitudes beyond 448
- * saturate to 448. The rounding quantum is 2^(e-4) for |x| = m * 2^e with
- * 0.5 <= m < 1, never finer than the subnormal step 2^-9. */
+/* Round x to the nearest E4M3 value, ties to even; magnitudes beyond 448 (infinities
+ * included) saturate to 448 and NaN gives the format's NaN pattern (quantization only
+ * ever rounds finite quotients). The rounding quantum is 2^(e-4) for |x| = m * 2^e
+ * with 0.5 <= m < 1, never finer than the subnormal step 2^-9. */
 uint8_t qsa_ref_e4m3_round(double x)
 {
     uint8_t sign = signbit(x) ? 0x80u : 0x00u;
     double a = fabs(x);
+    if (isnan(x))
+        return (uint8_t)(sign | 0x7Fu);
     if (a == 0.0)
         return sign;
+    if (a > 448.0)
+        a = 448.0;
     int e;
     (void)frexp(a, &e);
     int qe = (e < -5 ? -5 : e) - 4;

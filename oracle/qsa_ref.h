@@ -114,7 +114,8 @@ int qsa_ref_attend_backward(const qsa_ref_dims *d, int32_t batch, const int32_t 
                             int64_t n_rows);
 
 /* The bf16 and E4M3 roundings the oracle uses and the E4M3 decoding (exposed so tests
- * can pin them). E4M3 rounding saturates finite magnitudes beyond 448 to 448. */
+ * can pin them). E4M3 rounding saturates magnitudes beyond 448 (infinities too) to 448
+ * and maps NaN to the NaN pattern 0x7F (with the sign bit of x). */
 uint16_t qsa_ref_bf16_round(double x);
 uint8_t qsa_ref_e4m3_round(double x);
 double qsa_ref_e4m3_value(uint8_t b);

@@ -533,3 +533,12 @@ def test_backward_row_subsets_add_up():
         assert np.max(np.abs(f - (x + y))) < 1e-10
     assert np.array_equal(ga[0][a], full[0][a]) and np.all(ga[0][b] == 0.0)
     assert np.abs(ga[1]).max() > 1e-3 and np.abs(gb[1]).max() > 1e-3
+
+
+def test_e4m3_round_non_finite():
+    """Outside the quantizer's domain: infinities saturate like large finite values (to
+    +-448, bytes 0x7E / 0xFE) and NaN gives the NaN pattern with its sign."""
+    assert oracle.e4m3_round(float("inf")) == 0x7E
+    assert oracle.e4m3_round(float("-inf")) == 0xFE
+    assert oracle.e4m3_round(1e300) == 0x7E
+    assert oracle.e4m3_round(float("nan")) == 0x7F
