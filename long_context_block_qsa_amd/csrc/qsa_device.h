@@ -515,103 +515,87 @@ __device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
 }
 
-// Exact top-k (1 <= k) of the valid keys one wave holds in registers, with no
-// workgroup barrier: lane l holds positions PER*l .. PER*l+PER-1 (REG_MAJOR: positions
-// e*64 + l), ok[e] marks the valid ones. Order: key descending, equal keys by
-// ascending position. Radix select with
-// 8-bit digits over a wave-private 256-bin LDS histogram (`hist`), starting at the
-// highest bit where the keys differ and stopping as soon as the bin that holds the
-// k-th key is kept whole; when the digits run out, that bin is one key value and its
-// keys are kept by position. Returns this lane's kept mask (bit e); all valid keys
-// when there are at most k.
-template <int PER, bool REG_MAJOR = false>
-__device__ __forceinline__ uint32_t wave_topk_hist(const uint32_t (&x)[PER],
-                                                   const bool (&ok)[PER], int k,
-                                                   uint32_t *__restrict__ hist) {
-    const int l = lane_id();
+// Wave-wide OR / AND of uint32 (DPP row shifts and broadcasts, result from lane 63).
+__device__ __forceinline__ uint32_t wave_or_dpp(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
+}
+__device__ __forceinline__ uint32_t wave_and_dpp(uint32_t v) {
+    v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xf, 0xf, false);
+    v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xf, 0xf, false);
+    v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xf, 0xf, false);
+    v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xf, 0xf, false);
+    v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xa, 0xf, false);
+    v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xc, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
+}
+
+// Exact top-k (1 <= k) of the valid keys one wave holds in registers: lane l holds
+// positions PER*l .. PER*l+PER-1, ok[e] marks the valid ones. Order: key descending,
+// equal keys by ascending position. Returns this lane's kept mask (bit e); all valid
+// keys when there are at most k.
+// Method: a bitwise search for the k-th largest key theta, from the highest bit where
+// the keys differ down, over the bits that differ between some keys only (the others
+// are the same in every key, theta's included): a bit is set in theta when at least k
+// keys reach it, counted with ballots (no LDS, no atomics), and the search stops as
+// soon as exactly k keys reach theta. Keys above theta are kept, then keys equal to
+// theta by position while fewer than k are kept. (A histogram radix select was several
+// times slower: with small-integer scores many keys share a bin and its LDS atomics
+// serialize.)
+template <int PER>
+__device__ __forceinline__ uint32_t wave_topk_bits(const uint32_t (&x)[PER],
+                                                   const bool (&ok)[PER], int k) {
+    unsigned long long okm[PER];
     int nvalid = 0;
-    uint32_t mx = 0u, mn = 0xffffffffu, all = 0u;
+    uint32_t o = 0u, an = 0xffffffffu, all = 0u;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        nvalid += __popcll(__ballot(ok[e]));
-        if (ok[e]) { mx = max(mx, x[e]); mn = min(mn, x[e]); all |= 1u << e; }
+        okm[e] = __ballot(ok[e]);
+        nvalid += __popcll(okm[e]);
+        if (ok[e]) { o |= x[e]; an &= x[e]; all |= 1u << e; }
     }
     if (nvalid <= k) return all;
-    mx = wave_max_dpp(mx);
-    mn = wave_min_dpp(mn);
-    const uint32_t diff = mx ^ mn;
-    int hb = diff ? 32 - __builtin_clz(diff) : 0;   // low bits that vary
-    uint32_t pmask = hb >= 32 ? 0u : ~((1u << hb) - 1u);
-    uint32_t prefix = mx & pmask;
-    int need = k;
-    bool whole = false;   // the final bin is kept whole
-    while (hb > 0) {
-        const int shift = hb > 8 ? hb - 8 : 0;
-        const int nb = 1 << (hb - shift);
-        const uint32_t dmask = (uint32_t)nb - 1u;
-        *reinterpret_cast<u32x4 *>(&hist[4 * l]) = u32x4{0u, 0u, 0u, 0u};
-        wave_lds_sync();
+    o = wave_or_dpp(o);
+    an = wave_and_dpp(an);
+    uint32_t theta = an;      // every key has the bits set in all keys
+    uint32_t rem = o ^ an;    // bits that differ between keys, searched high to low
+    bool exact = false;       // exactly k keys are >= theta
+    while (rem) {
+        const uint32_t bit = 1u << (31 - __builtin_clz(rem));
+        rem ^= bit;
+        const uint32_t c = theta | bit;
+        int cnt = 0;
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-            if (ok[e] && (x[e] & pmask) == prefix)
-                atomicAdd(&hist[(x[e] >> shift) & dmask], 1u);
-        wave_lds_sync();
-        // lane l owns bins nb-1-4l .. nb-4-4l (highest first)
-        int h[4], local = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int b = nb - 1 - 4 * l - i;
-            h[i] = b >= 0 ? (int)hist[b] : 0;
-            local += h[i];
+        for (int e = 0; e < PER; ++e) cnt += __popcll(__ballot(x[e] >= c) & okm[e]);
+        if (cnt >= k) {
+            theta = c;
+            if (cnt == k) { exact = true; break; }
         }
-        const int incl = wave_incl_scan_i32(local);
-        const int above = incl - local;
-        const bool cross = above < need && need <= incl;
-        int digit = 0, run = above, m = 0;
-        if (cross) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (run + h[i] >= need) { digit = nb - 1 - 4 * l - i; m = h[i]; break; }
-                run += h[i];
-            }
-        }
-        const int src = (int)__builtin_ctzll(__ballot(cross));
-        digit = __builtin_amdgcn_readlane(digit, src);
-        run = __builtin_amdgcn_readlane(run, src);
-        m = __builtin_amdgcn_readlane(m, src);
-        need -= run;
-        prefix |= (uint32_t)digit << shift;
-        pmask |= dmask << shift;
-        hb = shift;
-        wave_lds_sync();  // the histogram is cleared again by the next pass
-        if (m == need) { whole = true; break; }
     }
     uint32_t mask = 0u;
-    if (REG_MAJOR) {
-        // equal keys before (e, l): all lanes at e' < e, then lanes below l at e
-        int eq_run = 0;
+    if (exact) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const uint32_t hi_bits = x[e] & pmask;
-            const bool eq = ok[e] && !whole && hi_bits == prefix;
-            const unsigned long long b = __ballot(eq);
-            if (ok[e] && (hi_bits > prefix || (whole && hi_bits == prefix))) mask |= 1u << e;
-            else if (eq && eq_run + lanes_below(b) < need) mask |= 1u << e;
-            eq_run += __popcll(b);
-        }
+        for (int e = 0; e < PER; ++e)
+            if (ok[e] && x[e] >= theta) mask |= 1u << e;
         return mask;
     }
-    int eq_below = 0;
-    if (!whole) {
+    int gt = 0, eq_below = 0;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) eq_below += lanes_below(__ballot(ok[e] && x[e] == prefix));
+    for (int e = 0; e < PER; ++e) {
+        gt += __popcll(__ballot(x[e] > theta) & okm[e]);
+        eq_below += lanes_below(__ballot(x[e] == theta) & okm[e]);
     }
+    const int need = k - gt;   // keys equal to theta to keep, the first by position
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
         if (!ok[e]) continue;
-        const uint32_t hi_bits = x[e] & pmask;
-        if (hi_bits > prefix || (whole && hi_bits == prefix)) mask |= 1u << e;
-        else if (hi_bits == prefix) {
+        if (x[e] > theta) mask |= 1u << e;
+        else if (x[e] == theta) {
             if (eq_below < need) mask |= 1u << e;
             ++eq_below;
         }
@@ -682,167 +666,131 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 
 // ---------------------------------------------------------------- block top-k (registers)
 
-// LDS of block_topk_regs.
+// LDS of block_topk_radix.
 struct TopkSmem {
-    uint32_t hist[256];
+    uint32_t hist[3][256];
     uint32_t red[2][16];
     int32_t scan[16];
-    int32_t found[4];
-    __attribute__((aligned(16))) uint32_t bin_key[64];   // read 16 bytes at a time
-    int32_t bin_pos[64];
-    uint32_t take_bits[64];   // bit p: position p of the final bin is kept (n <= 2048)
 };
 
-// Top-k of n keys (1 <= k <= n <= 2048) that the NT threads of a workgroup hold in
+// Top-k of n keys (1 <= k, n <= 2048) that the 256 threads of a workgroup hold in
 // registers: thread t holds positions PER*t .. PER*t+PER-1 (positions >= n are
 // ignored). Order: key descending, equal keys by ascending position. Sets bit e of
-// *kept when position PER*t+e is among the k, and *first to this thread's rank
-// among kept positions (kept positions ordered by position); returns k.
-// Method: a histogram of up to DB bits (the highest bits where the keys differ; DB
-// = 8 uses sm.hist, DB = 11 the caller's 2048-word `wide` array) finds the bin that
-// holds the k-th key; bins above it are kept whole. When that bin holds at most 64
-// keys they are ranked exactly by one wave (all pairs); otherwise the bin is refined
-// with the next 8 bits, down to single key values, where equal keys are kept by
-// position.
-template <int NT, int PER, int DB = 8>
-__device__ __forceinline__ int block_topk_regs(const uint32_t (&x)[PER], int n, int k,
-                                               TopkSmem &sm, uint32_t *kept, int *first,
-                                               uint32_t *wide = nullptr) {
-    static_assert(NT == 256, "bins are owned by threads in groups of nb / 256");
-    static_assert(DB == 8 || DB == 11, "digit widths: 8 or 11 bits");
+// *kept when position PER*t+e is among the k, and *first to this thread's rank among
+// kept positions (kept positions ordered by position); returns the number kept
+// (min(k, n)).
+// Method: radix select with 8-bit digits over the bits that differ between keys (an
+// OR / AND of all keys gives them; lower bits that never differ are not refined), one
+// workgroup barrier per digit: the threads add their keys to a 256-bin LDS histogram,
+// and after the barrier every wave scans the bins itself (so all waves find the bin
+// holding the k-th key without another barrier). Three histograms rotate: a pass
+// fills one and clears the one the next pass fills, which no wave reads any more.
+// Bins above the k-th key's are kept whole, as is its own bin once all of it fits;
+// otherwise its keys are equal and the first by position are kept. One scan of packed
+// per-thread counts then ranks the kept positions.
+template <int NT, int PER>
+__device__ __forceinline__ int block_topk_radix(const uint32_t (&x)[PER], int n, int k,
+                                                TopkSmem &sm, uint32_t *kept, int *first) {
+    static_assert(NT == 256, "one histogram bin per thread");
+    static_assert(NT * PER <= 2048, "packed 16-bit counts");
     constexpr int NW = NT / WAVE;
     const int tid = threadIdx.x, l = lane_id(), w = tid / WAVE;
-
-    // common high bits of all valid keys
-    uint32_t mx = 0u, mn = 0xffffffffu;
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-        if (PER * tid + e < n) { mx = max(mx, x[e]); mn = min(mn, x[e]); }
-    mx = wave_max_dpp(mx);
-    mn = wave_min_dpp(mn);
-    if (l == 0) { sm.red[0][w] = mx; sm.red[1][w] = mn; }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NW; ++i) { mx = max(mx, sm.red[0][i]); mn = min(mn, sm.red[1][i]); }
-    const uint32_t diff = mx ^ mn;
-    int hb = diff ? 32 - __builtin_clz(diff) : 0;
-    uint32_t pmask = hb >= 32 ? 0u : ~((1u << hb) - 1u);
-    uint32_t prefix = mx & pmask;
-    int need = k;
-    int mode = 0;   // 1: keep the whole final bin, 2: ranked bitmap, 3: equal keys by position
-    bool first_pass = true;
-
-    while (true) {
-        if (hb == 0) { mode = 3; break; }            // the final bin is one key value
-        const int width = (DB == 11 && first_pass) ? 11 : 8;
-        uint32_t *hist = (DB == 11 && first_pass) ? wide : sm.hist;
-        const int shift = hb > width ? hb - width : 0;
-        const int nb = 1 << (hb - shift);
-        const int bpt = nb > NT ? nb / NT : 1;        // bins per thread
-        const uint32_t dmask = (uint32_t)nb - 1u;
-        for (int i = tid; i < nb; i += NT) hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-            if (PER * tid + e < n && (x[e] & pmask) == prefix)
-                atomicAdd(&hist[(x[e] >> shift) & dmask], 1u);
-        __syncthreads();
-        // thread t owns bins nb-bpt*(t+1) .. nb-1-bpt*t (highest bins first)
-        const int top = nb - bpt * tid;
-        int local = 0;
-        for (int i = 1; i <= bpt; ++i) local += top - i >= 0 ? (int)hist[top - i] : 0;
-        int tot;
-        const int above = block_excl_scan_i32<NT>(local, sm.scan, &tot);
-        if (top > 0 && above < need && need <= above + local) {
-            int run = above;
-            for (int i = 1; i <= bpt; ++i) {
-                const int b = top - i;
-                const int h = (int)hist[b];
-                if (run + h >= need) {
-                    sm.found[0] = b;
-                    sm.found[1] = run;
-                    sm.found[2] = h;
-                    break;
-                }
-                run += h;
-            }
-        }
-        __syncthreads();
-        const int T = sm.found[0], A = sm.found[1], m = sm.found[2];
-        need -= A;
-        prefix |= (uint32_t)T << shift;
-        pmask |= dmask << shift;
-        hb = shift;
-        first_pass = false;
-        __syncthreads();
-        if (m == need) { mode = 1; break; }
-        if (m <= 64) { mode = 2; break; }
-    }
-
-    if (mode == 2) {
-        // compact the final bin's keys in position order, rank them in one wave
-        int c = 0;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) c += (PER * tid + e < n && (x[e] & pmask) == prefix);
-        int tot;
-        int off = block_excl_scan_i32<NT>(c, sm.scan, &tot);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            if (PER * tid + e < n && (x[e] & pmask) == prefix) {
-                sm.bin_key[off] = x[e];
-                sm.bin_pos[off] = PER * tid + e;
-                ++off;
-            }
-        }
-        for (int i = tid; i < 64; i += NT) sm.take_bits[i] = 0u;
-        __syncthreads();
-        if (w == 0) {
-            const int m = tot;
-            const uint32_t kj = l < m ? sm.bin_key[l] : 0u;
-            const int pj = l < m ? sm.bin_pos[l] : 0;
-            // rank = keys above kj plus equal keys earlier in position order (the
-            // compaction kept position order); the bin's keys are read 4 at a time by
-            // broadcast LDS reads
-            int rank = 0;
-            for (int i0 = 0; i0 < m; i0 += 4) {
-                const u32x4 k4 = *reinterpret_cast<const u32x4 *>(&sm.bin_key[i0]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    rank += i0 + e < m && (k4[e] > kj || (k4[e] == kj && i0 + e < l));
-            }
-            if (l < m && rank < need) atomicOr(&sm.take_bits[pj >> 5], 1u << (pj & 31));
-        }
-        __syncthreads();
-    }
-
-    // mode 3: among the (equal) keys of the final bin keep the first `need` by position
-    int eq_before = 0;
-    if (mode == 3) {
-        int c = 0;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) c += (PER * tid + e < n && (x[e] & pmask) == prefix);
-        int tot;
-        eq_before = block_excl_scan_i32<NT>(c, sm.scan, &tot);
-    }
-    uint32_t mask = 0u;
-    int nt = 0;
+    bool ok[PER];
+    uint32_t o = 0u, an = 0xffffffffu;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const int pos = PER * tid + e;
-        if (pos >= n) continue;
-        const uint32_t hi_bits = x[e] & pmask;
-        bool take = hi_bits > prefix;
-        if (hi_bits == prefix) {
-            if (mode == 1) take = true;
-            else if (mode == 2) take = (sm.take_bits[pos >> 5] >> (pos & 31)) & 1u;
-            else { take = eq_before < need; ++eq_before; }
+        ok[e] = PER * tid + e < n;
+        if (ok[e]) { o |= x[e]; an &= x[e]; }
+    }
+    if (n <= k) {   // every valid position is kept (uniform)
+        uint32_t m = 0u;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) m |= ok[e] ? 1u << e : 0u;
+        *kept = m;
+        *first = min(PER * tid, max(n, 0));
+        return max(n, 0);
+    }
+    sm.hist[0][tid] = 0u;
+    o = wave_or_dpp(o);
+    an = wave_and_dpp(an);
+    if (l == 0) { sm.red[0][w] = o; sm.red[1][w] = an; }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) { o |= sm.red[0][i]; an &= sm.red[1][i]; }
+    const uint32_t vary = o ^ an;
+    int hb = vary ? 32 - __builtin_clz(vary) : 0;       // bits >= hb: the same in all keys
+    const int lo = vary ? __builtin_ctz(vary) : 0;      // bits < lo: the same in all keys
+    uint32_t pmask = hb >= 32 ? 0u : ~((1u << hb) - 1u);
+    uint32_t prefix = o & pmask;
+    int need = k;
+    bool whole = false;   // the final bin is kept whole
+    for (int pass = 0; hb > lo; ++pass) {   // uniform over the workgroup
+        const int shift = max(hb - 8, lo);
+        const int nb = 1 << (hb - shift);
+        const uint32_t dmask = (uint32_t)nb - 1u;
+        uint32_t *h = sm.hist[pass % 3];
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            if (ok[e] && (x[e] & pmask) == prefix) atomicAdd(&h[(x[e] >> shift) & dmask], 1u);
+        sm.hist[(pass + 1) % 3][tid] = 0u;
+        __syncthreads();
+        // lane l of every wave owns bins nb-1-4l .. nb-4-4l (highest first)
+        int hc[4], local = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int bn = nb - 1 - 4 * l - i;
+            hc[i] = bn >= 0 ? (int)h[bn] : 0;
+            local += hc[i];
         }
-        if (take) { mask |= 1u << e; ++nt; }
+        const int incl = wave_incl_scan_i32(local);
+        const int above = incl - local;
+        const bool cross = above < need && need <= incl;
+        int digit = 0, run = above, m = 0;
+        if (cross) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (run + hc[i] >= need) { digit = nb - 1 - 4 * l - i; m = hc[i]; break; }
+                run += hc[i];
+            }
+        }
+        const int src = (int)__builtin_ctzll(__ballot(cross));
+        digit = __builtin_amdgcn_readlane(digit, src);
+        run = __builtin_amdgcn_readlane(run, src);
+        m = __builtin_amdgcn_readlane(m, src);
+        need -= run;
+        prefix |= (uint32_t)digit << shift;
+        pmask |= dmask << shift;
+        hb = shift;
+        if (m == need) { whole = true; break; }
+    }
+    // per thread: keys kept outright (high bits above the prefix, or equal to it when
+    // the final bin is kept whole) and keys equal to the final value, packed for one scan
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        if (!ok[e]) continue;
+        const uint32_t hi = x[e] & pmask;
+        n_gt += hi > prefix || (whole && hi == prefix);
+        n_eq += !whole && hi == prefix;
     }
     int tot;
-    *first = block_excl_scan_i32<NT>(nt, sm.scan, &tot);
+    const int before = block_excl_scan_i32<NT>((n_gt << 16) | n_eq, sm.scan, &tot);
+    const int take = k - (tot >> 16);   // keys of the final value kept, the first by position
+    int eq_before = before & 0xffff;
+    *first = (before >> 16) + min(take, eq_before);
+    uint32_t mask = 0u;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        if (!ok[e]) continue;
+        const uint32_t hi = x[e] & pmask;
+        if (hi > prefix || (whole && hi == prefix)) mask |= 1u << e;
+        else if (hi == prefix) {
+            if (eq_before < take) mask |= 1u << e;
+            ++eq_before;
+        }
+    }
     *kept = mask;
-    return tot;
+    return k;
 }
 
 // ---------------------------------------------------------------- FP8 (OCP E4M3)

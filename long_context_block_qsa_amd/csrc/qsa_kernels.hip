@@ -367,8 +367,8 @@ score_rows_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ 
 // candidates, writes the chunk's KP best (key, block) pairs in ascending block order to
 // cand[row][chunk][0..KP), padded with key 0 (below every real key). The local top-KP
 // is exact and needs no workgroup-wide histogram: each wave takes the top KP of its 256
-// positions with a wave-private radix select, and one wave takes the top KP of those
-// 4 x KP (tiles of several rows: one wave per row over the whole chunk). Rows whose
+// positions with a wave-level bitwise search (ballot counts, no LDS), and one wave takes
+// the top KP of those 4 x KP (tiles of several rows: one wave per row over the whole chunk). Rows whose
 // tile has at most MERGE_CHUNKS chunks are then merged after this kernel: in a forward
 // step by the decode attention's workgroups, after a selection alone by merge_dec_kernel
 // (one workgroup per row). Longer rows merge groups of chunks inside this kernel: candidates
@@ -458,7 +458,7 @@ __device__ __forceinline__ bool merge_candidates(const uint32_t *ck, const int32
     if (tid == 0) *viol = 0;
     uint32_t kept;
     int first;
-    const int tot = block_topk_regs<SEL_NT, 8>(x, n, k, *tsm, &kept, &first);
+    const int tot = block_topk_radix<SEL_NT, 8>(x, n, k, *tsm, &kept, &first);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         if (kept & (1u << e)) {
@@ -579,7 +579,7 @@ __device__ __forceinline__ void select_tile_exact(const LocalArgs &a, const Deco
 
 // LDS of one scoring workgroup.
 struct ScoreSmem {
-    uint32_t whist[LOC_NT / WAVE][256];   // per-wave histograms (and key transposes)
+    uint32_t whist[LOC_NT / WAVE][256];   // per-wave key transposes
     uint32_t wl_key[LOC_NT / WAVE][KP];
     int32_t wl_pos[LOC_NT / WAVE][KP];
     uint32_t hist[kHistBins];
@@ -668,7 +668,7 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 ok[i] = u0 + i < span && lo + (int64_t)qw * span + u0 + i < vhi;
-            const uint32_t mask = wave_topk_hist<16>(x, ok, KP, sm.whist[w]);
+            const uint32_t mask = wave_topk_bits<16>(x, ok, KP);
             const int cnt = __popc(mask);
             const int incl = wave_incl_scan_i32(cnt);
             const int tot = __builtin_amdgcn_readlane(incl, WAVE - 1);
@@ -705,8 +705,7 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
         const int64_t nvw = min<int64_t>(whi, nv);
 #pragma unroll
         for (int e = 0; e < 4; ++e) { x[e] = q4[e]; ok[e] = wlo + 4 * l + e < nvw; }
-        wave_lds_sync();   // the histogram below reuses wk
-        const uint32_t mask = wave_topk_hist<4>(x, ok, KP, wk);
+        const uint32_t mask = wave_topk_bits<4>(x, ok, KP);
         const int cnt = __popc(mask);
         int pos = wave_excl_small<4>(cnt);
         const int tot = __builtin_amdgcn_readlane(pos + cnt, WAVE - 1);
@@ -732,7 +731,7 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
                 py[e] = sm.wl_pos[i / KP][i % KP];
                 oy[e] = y[e] != 0u;
             }
-            const uint32_t m2 = wave_topk_hist<2>(y, oy, KP, sm.whist[0]);
+            const uint32_t m2 = wave_topk_bits<2>(y, oy, KP);
             const int c2 = __popc(m2);
             int o = wave_excl_small<2>(c2);
             const int tot2 = __builtin_amdgcn_readlane(o + c2, WAVE - 1);
