@@ -36,6 +36,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16, 256 CU x 2.4 GHz x 4096 flop/clk
 
 HQ, HKV, D, HI, DI, BS, TOPK = 24, 2, 128, 4, 64, 4, 512
+HOST_THREADS = 16   # host threads for the oracle baseline: one GPU's share of the host
 
 # HBM bytes per dispatch (FETCH_SIZE + WRITE_SIZE, each scaled by the factor the counter
 # reads on a plain 512 MiB copy) from rocprofv3 --pmc runs of this benchmark, with the
@@ -616,7 +617,7 @@ def run_cpu_baseline(args, d, oracle):
     p = d["p"]
     dims = oracle.Dims()
     k_blk = oracle.compress(dims, p.cu_k, p.k_idx)
-    threads = min(os.cpu_count() or 1, p.n_q)
+    threads = min(os.cpu_count() or 1, p.n_q, HOST_THREADS)
     reps, t0 = 0, time.perf_counter()
     while True:
         sel = oracle.select(dims, p.cu_q, p.cu_k, p.q_idx, p.w, k_blk, threads=threads)
@@ -642,7 +643,7 @@ def run_cpu_baseline_prefill(args, oracle, gen, stride=64):
     (compress of all blocks, then score + select + attend of the sampled rows)."""
     p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
     rows = np.arange(0, p.n_q, stride, dtype=np.int64)
-    threads = os.cpu_count() or 1
+    threads = min(os.cpu_count() or 1, HOST_THREADS)
     t0 = time.perf_counter()
     oracle.forward(oracle.Dims(), p.cu_q, p.cu_k, p.q, p.k, p.v, p.q_idx, p.w, p.k_idx,
                    rows=rows, threads=threads)

@@ -110,7 +110,7 @@ def _arr(a, dtype):
 
 
 def _threads(n):
-    return int(n if n else min(os.cpu_count() or 1, 64))
+    return int(n if n else min(os.cpu_count() or 1, 16))   # one GPU's share of a shared host
 
 
 def _rows(rows):
