@@ -79,6 +79,7 @@ attend_dense_kernel(DenseArgs a) {
         for (int m = 0; m < 4; ++m) qb[nt][m] = ok ? load16(qp + 32 * m) : u32x4{0u, 0u, 0u, 0u};
     }
     const int64_t wave_tmax = r_lo < nrows ? t0 + min(r_hi, nrows - 1) : -1;
+    const int64_t wave_tmin = t0 + r_lo;   // tiles up to here need no causal mask
 
     f32x4 acc[DN_NQ][8];
 #pragma unroll
@@ -135,13 +136,20 @@ attend_dense_kernel(DenseArgs a) {
 #pragma unroll
                     for (int nt = 0; nt < DN_NQ; ++nt) c[nt] = mfma_bf16_16x16x32(ka, qb[nt][m], c[nt]);
                 }
+                if (j0 + DN_KEYS - 1 <= wave_tmin) {   // uniform: every key visible
 #pragma unroll
-                for (int nt = 0; nt < DN_NQ; ++nt)
+                    for (int nt = 0; nt < DN_NQ; ++nt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t j = j0 + 16 * u + 4 * gr + i;
-                        z[nt][4 * u + i] = j <= tpos[nt] ? c[nt][i] * a.scale_log2 : -INFINITY;
-                    }
+                        for (int i = 0; i < 4; ++i) z[nt][4 * u + i] = c[nt][i] * a.scale_log2;
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < DN_NQ; ++nt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int64_t j = j0 + 16 * u + 4 * gr + i;
+                            z[nt][4 * u + i] = j <= tpos[nt] ? c[nt][i] * a.scale_log2 : -INFINITY;
+                        }
+                }
             }
             // ---- V^T operands of the 8 dim tiles: lane rows are dims 8col + mt, its
             // k-slot keys as above
@@ -174,10 +182,13 @@ attend_dense_kernel(DenseArgs a) {
                     for (int mt = 0; mt < 8; ++mt) acc[nt][mt] *= alpha;
                     m_run[nt] = m_new;
                 }
+                // masked keys (z = -inf) give 0: a valid column's m_run is finite from
+                // its first tile on (key 0 is visible to every row); columns past the
+                // tile's rows may turn NaN, and are never written
                 float p[8], rs = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    p[e] = z[nt][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[nt][e] - m_run[nt]);
+                    p[e] = __builtin_amdgcn_exp2f(z[nt][e] - m_run[nt]);
                     rs += p[e];
                 }
                 l_run[nt] += wave_sum_xor_16_32(rs);

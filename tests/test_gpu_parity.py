@@ -107,6 +107,19 @@ def test_prefill_1x1024_dense():
     _check_rows("prefill-1x1024", DeviceProblem(p), None, 512)
 
 
+@pytest.mark.parametrize("lens,topk", [
+    ([700, 1500, 33], 512),   # ragged, every row dense
+    ([258, 258, 258], 64),    # dense rows t <= 258 at budget 64
+    ([2051], 512),            # the longest dense rows at the model's budget
+])
+def test_dense_prefills(lens, topk):
+    """All-dense prefills of several shapes (ragged tails, a smaller budget, the longest
+    dense rows): every row checked."""
+    _banner(f"dense prefill lens={lens} topk={topk}")
+    p = gen.make_problem(lens, seed=600 + sum(lens) + topk)
+    _check_rows(f"dense{lens}/k{topk}", DeviceProblem(p, topk), None, topk)
+
+
 def test_decode_1x32768_needles():
     _banner("decode 1x32768")
     p = gen.workload_problem("decode_1x32768")
