@@ -74,7 +74,10 @@ int64_t h_first_scored_pos(int64_t L, int64_t nq, int64_t topk) {
 // slots. Two key buffers alternate: one launch selects the rows of pass p from one
 // buffer while it scores pass p + 1 into the other, so the workspace does not grow
 // with the square of the context and no pass ends with its own tail.
-constexpr int64_t kKeyBudget = int64_t(1) << 25;   // slots (uint32 keys) per buffer: 128 MiB
+// slots (uint32 keys) per buffer: 256 MiB (2^25 took 47.5 ms of score + select for a
+// 262,144-token prefill, 2^26 39.9 ms, 2^27 41.2 ms: more rows per launch, until the two
+// buffers outgrow the Infinity Cache)
+constexpr int64_t kKeyBudget = int64_t(1) << 26;
 
 struct Pass {
     int64_t tile_lo = 0, tile_hi = 0;   // score tiles

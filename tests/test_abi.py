@@ -230,17 +230,17 @@ def test_trace_end_without_begin_and_names():
 
 
 def test_prefill_workspace_bounded_by_key_budget():
-    """Prefill scores are kept one pass of score tiles at a time (at most 2^25 keys of
+    """Prefill scores are kept one pass of score tiles at a time (at most 2^26 keys of
     4 bytes, in two alternating buffers), so the workspace of a 262,144-token or a
     1,048,576-token prefill is the selection (4 * 512 bytes per query row, linear in the
-    length) plus at most 256 MiB of keys, while the sum of its score slots
+    length) plus at most 512 MiB of keys, while the sum of its score slots
     (F(L) - F(2051)) would be 34 GB and 550 GB."""
     d = qsa.make_dims(topk=512)
     F = lambda t: 2 * (t // 4) * (t // 4 - 1) + (t // 4) * (t % 4 + 1)
     for L in (65535, 262144, 1 << 20):
         st, n = _ws(d, _seqs([0, L], [0, L]))
         assert st == 0
-        assert n <= 4 * 512 * L + 8 * 2**25 + 2**20, (L, n)
+        assert n <= 4 * 512 * L + 8 * 2**26 + 2**20, (L, n)
         if L >= 262144:
             assert 4 * (F(L) - F(2051)) > 30 * n
     # a call whose keys fit one pass keeps all of them (as before)

@@ -184,15 +184,15 @@ def test_prefill_ragged_64k_all_selections():
 
 def test_prefill_1x262144_bounded_workspace():
     """One prefill at the native context, 262,144 tokens: its 8.6e9 score slots (34 GB
-    of keys if kept whole) are scored and selected in passes of at most 2^25 keys, in a
-    workspace of the selection plus two 128 MiB key buffers. 300 rows (spread over the sequence, its
+    of keys if kept whole) are scored and selected in passes of at most 2^26 keys, in a
+    workspace of the selection plus two 256 MiB key buffers. 300 rows (spread over the sequence, its
     last rows and the dense/sparse boundary): selections bit-exact, out and lse within
     the bars."""
     _banner("prefill 1x262144")
     L = 262144
     p = gen.workload_problem("prefill_1x262144")
     dp = DeviceProblem(p)
-    assert dp.ws.numel() <= 4 * 512 * L + 8 * 2**25 + 2**20
+    assert dp.ws.numel() <= 4 * 512 * L + 8 * 2**26 + 2**20
     rows = sorted(set(np.linspace(0, L - 1, 268).astype(int).tolist())
                   | set(range(2044, 2060)) | set(range(L - 16, L)))
     _check_rows("prefill-1x262144", dp, rows, 512)
