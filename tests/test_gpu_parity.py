@@ -246,12 +246,15 @@ def test_decode_1m_context_grouped_merge():
 
 def test_decode_4x1m_full():
     """The 1M decode line's shape: 4 sequences of 1,048,576 tokens, one query each (4 score
-    tiles, each merging 4 groups of 64 chunks inside the scoring kernel), all rows."""
+    tiles, each merging 4 groups of 64 chunks inside the scoring kernel), all rows; the
+    selection alone equals the forward's."""
     _banner("decode 4x1M")
     p = gen.make_problem([1 << 20] * 4, q_lens=[1] * 4, seed=23, needles=16)
-    sel, _ = _check_rows("4x1M", DeviceProblem(p), None, 512)
+    dp = DeviceProblem(p)
+    sel, _ = _check_rows("4x1M", dp, None, 512)
     for b, needles in p.needles.items():
         assert set(needles) <= set(sel[b].tolist()), f"needles of sequence {b} missing"
+    assert np.array_equal(dp.select(), sel)
 
 
 def test_multi_query_long_rows_grouped():
@@ -259,7 +262,9 @@ def test_multi_query_long_rows_grouped():
     plus a short sequence."""
     _banner("multi-query grouped")
     p = gen.make_problem([300001, 7000], q_lens=[3, 2], seed=18)
-    _check_rows("mq-grouped", DeviceProblem(p, 512), None, 512)
+    dp = DeviceProblem(p, 512)
+    sel, _ = _check_rows("mq-grouped", dp, None, 512)
+    assert np.array_equal(dp.select(), sel)
 
 
 @pytest.mark.parametrize("L", [266001, 526001])
@@ -280,8 +285,10 @@ def test_grouped_merge_exact_fallback():
          gen.bf16_to_f32(p.q_idx[0]).astype(np.float64)).sum(axis=0)
     val = np.where(u >= 0, 0x4040, 0xC040).astype(np.uint16)
     p.k_idx[4 * 70000: 4 * 70300] = val[None, :]
-    sel, _ = _check_rows("grouped-fallback", DeviceProblem(p, 512), None, 512)
+    dp = DeviceProblem(p, 512)
+    sel, _ = _check_rows("grouped-fallback", dp, None, 512)
     assert set(range(70000, 70300)) <= set(sel[0].tolist())
+    assert np.array_equal(dp.select(), sel)
 
 
 # ----------------------------------------------------------------- edge cases / properties
