@@ -10,15 +10,15 @@
 // shared by DN_ROWS consecutive query rows x the 12 query heads of one KV head.
 //
 // Workgroup = (dense tile of DN_ROWS = 16 rows, KV head g): its 192 query vectors (16
-// rows x 12 heads, vector v = row * 12 + head) are 12 MFMA column tiles of 16, two per
-// wave (6 waves). Per tile of 32 keys, each wave computes
-//   S^T[32 keys x 32] = K (A operand from LDS, bf16) x Q^T (B operand, registers):
-//     2 column tiles x 2 key halves x 4 steps of MFMA 16x16x32 over the 128 dims;
+// rows x 12 heads, vector v = row * 12 + head) are 12 MFMA column tiles of 16, over 8
+// waves. Per tile of 32 keys, each wave computes, for each of its column tiles,
+//   S^T[32 keys x 16] = K (A operand from LDS, bf16) x Q^T (B operand, registers):
+//     2 key halves x 4 steps of MFMA 16x16x32 over the 128 dims;
 //   online softmax per query vector in base 2 (the reference maximum moves only when a
 //     vector's maximum grows by more than 2^8, so probabilities stay at most 2^8);
 //   O^T[128 dims x 32] += V^T (A operand, bf16 rows staged in LDS) x P^T: P is split
-//     into bf16 hi + lo parts (about 16 significant bits), 2 x 8 dim tiles x 2 column
-//     tiles of MFMA 16x16x32 bf16 (the same precision as the sparse rows' kernel; P in
+//     into bf16 hi + lo parts (about 16 significant bits), 2 x 8 dim tiles of MFMA
+//     16x16x32 bf16 (the same precision as the sparse rows' kernel; P in
 //     fp16 alone left errors of 5e-4 in the outputs, which the attention backward, fed
 //     these outputs, carries into its gradients).
 // Key order within the MFMA contraction is permuted as in the sparse kernel (k-slot
@@ -29,14 +29,18 @@
 
 namespace qsa {
 
-constexpr int DN_NQ = 2;                  // column tiles of 16 query vectors per wave
-constexpr int DN_WAVES = DN_ROWS * GQ / 16 / DN_NQ;   // 6
+// Column tiles: waves 0-3 take two each (tiles 2w, 2w + 1), waves 4-7 one each (tile 4 + w)
+// and also stage the K/V tiles, so that each SIMD (waves w and w + 4) carries three column
+// tiles of MFMA work per key tile.
+constexpr int DN_WAVES = 8;
 constexpr int DN_NT = DN_WAVES * WAVE;
 constexpr int DN_KEYS = 32;
 constexpr int DN_PITCH = 2 * HD + 16;     // LDS row pitch (bytes) of the K and V tiles
+constexpr int DN_TILE_BYTES = DN_KEYS * DN_PITCH;
 constexpr int DN_STAGE_NT = DN_KEYS * 8;  // threads that stage a tile (32 bytes of K and V each)
-static_assert(DN_ROWS * GQ == 16 * DN_NQ * DN_WAVES, "column tiles split evenly over waves");
-static_assert(DN_STAGE_NT <= DN_NT, "enough threads to stage a tile");
+constexpr int DN_STAGE_T0 = 4 * WAVE;     // first staging thread (waves 4-7)
+static_assert(DN_ROWS * GQ == 16 * (4 * 2 + 4 * 1), "12 column tiles over the 8 waves");
+static_assert(DN_STAGE_T0 + DN_STAGE_NT == DN_NT, "waves 4-7 stage a tile");
 
 struct DenseArgs {
     const SeqInfo *tab;
@@ -47,31 +51,32 @@ struct DenseArgs {
     int64_t n_tiles;
 };
 
-__global__ void __launch_bounds__(DN_NT)
-attend_dense_kernel(DenseArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t ks[DN_KEYS * DN_PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t vs[DN_KEYS * DN_PITCH];
-    const int g = blockIdx.y;
-    const int64_t tile = a.n_tiles - 1 - (int64_t)blockIdx.x;
-    const int sb = find_seq(a.batch, tile, [&](int i) { return (int64_t)a.tab[i].dtile0; });
-    const SeqInfo s = a.tab[sb];
-    const int64_t nd = dense_rows_of(s.L, s.nq, a.topk);
-    const int64_t i0 = (tile - s.dtile0) * DN_ROWS;          // first dense row of the tile
-    const int64_t t0 = (int64_t)s.L - s.nq + i0;              // its position
-    const int nrows = (int)min<int64_t>(DN_ROWS, nd - i0);
-    const int64_t row0 = s.q0 + i0;
-    const int64_t t_last = t0 + nrows - 1;
-    const int tid = threadIdx.x, w = tid / WAVE, l = lane_id(), gr = l >> 4, col = l & 15;
-    // this wave's rows: those of its query vectors 32w .. 32w + 31
-    const int r_lo = (16 * DN_NQ * w) / GQ, r_hi = (16 * DN_NQ * (w + 1) - 1) / GQ;
+// The workgroup's dense tile: its sequence, first row and position, row count.
+struct DenseTile {
+    SeqInfo s;
+    int64_t row0, t0, t_last;
+    int nrows;
+};
 
-    // Q^T operands: column tile nt, lane column col -> query vector v = 16 (DN_NQ w + nt)
-    // + col = (row v / 12, head v % 12); dims 32m + 8gr .. +7 of step m
-    u32x4 qb[DN_NQ][4];
-    int64_t tpos[DN_NQ];
+// One wave's part of a workgroup: NQ column tiles from column tile ct0 (query vectors
+// 16 ct0 .. 16 (ct0 + NQ) - 1), the key loop with the workgroup's barriers (every wave runs
+// the same number of iterations), and, for the staging waves, the K/V staging.
+template <int NQ, bool STAGE>
+__device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &dt, int g,
+                                           int ct0, uint8_t *ks0, uint8_t *vs0) {
+    const int tid = threadIdx.x, l = lane_id(), gr = l >> 4, col = l & 15;
+    const int64_t row0 = dt.row0, t0 = dt.t0, t_last = dt.t_last;
+    const int nrows = dt.nrows;
+    // this wave's rows: those of its query vectors
+    const int r_lo = (16 * ct0) / GQ, r_hi = (16 * (ct0 + NQ) - 1) / GQ;
+
+    // Q^T operands: column tile nt, lane column col -> query vector v = 16 (ct0 + nt) + col
+    // = (row v / 12, head v % 12); dims 32m + 8gr .. +7 of step m
+    u32x4 qb[NQ][4];
+    int64_t tpos[NQ];
 #pragma unroll
-    for (int nt = 0; nt < DN_NQ; ++nt) {
-        const int vq = 16 * (DN_NQ * w + nt) + col, rr = vq / GQ, hh = vq % GQ;
+    for (int nt = 0; nt < NQ; ++nt) {
+        const int vq = 16 * (ct0 + nt) + col, rr = vq / GQ, hh = vq % GQ;
         const bool ok = rr < nrows;
         tpos[nt] = ok ? t0 + rr : -1;
         const uint16_t *qp = a.q + ((row0 + (ok ? rr : 0)) * HQ + g * GQ + hh) * HD + 8 * gr;
@@ -81,21 +86,20 @@ attend_dense_kernel(DenseArgs a) {
     const int64_t wave_tmax = r_lo < nrows ? t0 + min(r_hi, nrows - 1) : -1;
     const int64_t wave_tmin = t0 + r_lo;   // tiles up to here need no causal mask
 
-    f32x4 acc[DN_NQ][8];
+    f32x4 acc[NQ][8];
 #pragma unroll
-    for (int nt = 0; nt < DN_NQ; ++nt)
+    for (int nt = 0; nt < NQ; ++nt)
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[DN_NQ], l_run[DN_NQ];
+    float m_run[NQ], l_run[NQ];
 #pragma unroll
-    for (int nt = 0; nt < DN_NQ; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
+    for (int nt = 0; nt < NQ; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
 
-    // staging: thread < DN_STAGE_NT -> (key tid / 8, 32-byte piece tid % 8) of the K and V
-    // rows
-    const bool stager = tid < DN_STAGE_NT;
-    const int sk = (tid >> 3) & (DN_KEYS - 1), sp = tid & 7;
-    const uint16_t *kbase = a.k + (int64_t)s.k0 * (HKV * HD) + g * HD + 16 * sp;
-    const uint16_t *vbase = a.v + (int64_t)s.k0 * (HKV * HD) + g * HD + 16 * sp;
+    // staging: thread DN_STAGE_T0 + i -> (key i / 8, 32-byte piece i % 8) of the K and V rows
+    const int st = tid - DN_STAGE_T0;
+    const int sk = (st >> 3) & (DN_KEYS - 1), sp = st & 7;
+    const uint16_t *kbase = a.k + (int64_t)dt.s.k0 * (HKV * HD) + g * HD + 16 * sp;
+    const uint16_t *vbase = a.v + (int64_t)dt.s.k0 * (HKV * HD) + g * HD + 16 * sp;
     auto load_stage = [&](int64_t j0, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
         const int64_t j = min<int64_t>(j0 + sk, t_last);   // keys past the tile's rows: masked
         kr[0] = load16(kbase + j * (HKV * HD));
@@ -103,47 +107,53 @@ attend_dense_kernel(DenseArgs a) {
         vr[0] = load16(vbase + j * (HKV * HD));
         vr[1] = load16(vbase + j * (HKV * HD) + 8);
     };
-    auto store_stage = [&](const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
-        uint8_t *kd = ks + sk * DN_PITCH + 32 * sp;
-        uint8_t *vd = vs + sk * DN_PITCH + 32 * sp;
+    auto store_stage = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
+        uint8_t *kd = ks0 + buf * DN_TILE_BYTES + sk * DN_PITCH + 32 * sp;
+        uint8_t *vd = vs0 + buf * DN_TILE_BYTES + sk * DN_PITCH + 32 * sp;
         *reinterpret_cast<u32x4 *>(kd) = kr[0];
         *reinterpret_cast<u32x4 *>(kd + 16) = kr[1];
         *reinterpret_cast<u32x4 *>(vd) = vr[0];
         *reinterpret_cast<u32x4 *>(vd + 16) = vr[1];
     };
 
+    // the tiles alternate between two LDS buffers: tile j + 1 is written while tile j is
+    // read, and one barrier per tile makes it visible (and frees tile j's buffer)
     u32x4 kr[2], vr[2];
-    if (stager) {
+    if constexpr (STAGE) {
         load_stage(0, kr, vr);
-        store_stage(kr, vr);
+        store_stage(0, kr, vr);
     }
     __syncthreads();
-    for (int64_t j0 = 0; j0 <= t_last; j0 += DN_KEYS) {
+    int buf = 0;
+    for (int64_t j0 = 0; j0 <= t_last; j0 += DN_KEYS, buf ^= 1) {
         const bool more = j0 + DN_KEYS <= t_last;
-        if (more && stager) load_stage(j0 + DN_KEYS, kr, vr);   // next tile in flight
+        if constexpr (STAGE)
+            if (more) load_stage(j0 + DN_KEYS, kr, vr);   // next tile in flight
+        const uint8_t *ks = ks0 + buf * DN_TILE_BYTES;
+        const uint8_t *vs = vs0 + buf * DN_TILE_BYTES;
         if (j0 <= wave_tmax) {                         // uniform over the wave
             // ---- S^T: lane (gr, col) of column tile nt holds keys j0 + 16u + 4gr + i
-            float z[DN_NQ][8];
+            float z[NQ][8];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                f32x4 c[DN_NQ];
+                f32x4 c[NQ];
 #pragma unroll
-                for (int nt = 0; nt < DN_NQ; ++nt) c[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int nt = 0; nt < NQ; ++nt) c[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const u32x4 ka = *reinterpret_cast<const u32x4 *>(
                         ks + (16 * u + col) * DN_PITCH + 2 * (32 * m + 8 * gr));
 #pragma unroll
-                    for (int nt = 0; nt < DN_NQ; ++nt) c[nt] = mfma_bf16_16x16x32(ka, qb[nt][m], c[nt]);
+                    for (int nt = 0; nt < NQ; ++nt) c[nt] = mfma_bf16_16x16x32(ka, qb[nt][m], c[nt]);
                 }
                 if (j0 + DN_KEYS - 1 <= wave_tmin) {   // uniform: every key visible
 #pragma unroll
-                    for (int nt = 0; nt < DN_NQ; ++nt)
+                    for (int nt = 0; nt < NQ; ++nt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) z[nt][4 * u + i] = c[nt][i] * a.scale_log2;
                 } else {
 #pragma unroll
-                    for (int nt = 0; nt < DN_NQ; ++nt)
+                    for (int nt = 0; nt < NQ; ++nt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int64_t j = j0 + 16 * u + 4 * gr + i;
@@ -169,7 +179,7 @@ attend_dense_kernel(DenseArgs a) {
             // ---- per column tile: online softmax per query vector, P^T as bf16 hi + lo,
             // O^T += V^T P^T
 #pragma unroll
-            for (int nt = 0; nt < DN_NQ; ++nt) {
+            for (int nt = 0; nt < NQ; ++nt) {
                 float mx = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) mx = fmaxf(mx, z[nt][e]);
@@ -207,16 +217,16 @@ attend_dense_kernel(DenseArgs a) {
                 }
             }
         }
-        __syncthreads();   // every wave is done with this tile
-        if (more && stager) store_stage(kr, vr);
-        __syncthreads();
+        if constexpr (STAGE)
+            if (more) store_stage(buf ^ 1, kr, vr);   // the buffer of tile j - 1, done with
+        __syncthreads();   // tile j + 1 staged, every wave done with tile j
     }
 
-    // lane (gr, col), column tile nt: acc[nt][mt][i] = O[vector 16(DN_NQ w + nt) + col]
+    // lane (gr, col), column tile nt: acc[nt][mt][i] = O[vector 16(ct0 + nt) + col]
     // [dim 8(4gr+i) + mt]
 #pragma unroll
-    for (int nt = 0; nt < DN_NQ; ++nt) {
-        const int vq = 16 * (DN_NQ * w + nt) + col, rr = vq / GQ, hh = vq % GQ;
+    for (int nt = 0; nt < NQ; ++nt) {
+        const int vq = 16 * (ct0 + nt) + col, rr = vq / GQ, hh = vq % GQ;
         if (rr >= nrows) continue;
         const int64_t row = row0 + rr;
         const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
@@ -235,6 +245,26 @@ attend_dense_kernel(DenseArgs a) {
             a.lse[row * HQ + g * GQ + hh] =
                 l_run[nt] > 0.f ? m_run[nt] * 0.69314718055994531f + logf(l_run[nt]) : -INFINITY;
     }
+}
+
+__global__ void __launch_bounds__(DN_NT)
+attend_dense_kernel(DenseArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t ks[2 * DN_TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t vs[2 * DN_TILE_BYTES];
+    const int g = blockIdx.y;
+    const int64_t tile = a.n_tiles - 1 - (int64_t)blockIdx.x;
+    const int sb = find_seq(a.batch, tile, [&](int i) { return (int64_t)a.tab[i].dtile0; });
+    DenseTile dt;
+    dt.s = a.tab[sb];
+    const int64_t nd = dense_rows_of(dt.s.L, dt.s.nq, a.topk);
+    const int64_t i0 = (tile - dt.s.dtile0) * DN_ROWS;       // first dense row of the tile
+    dt.t0 = (int64_t)dt.s.L - dt.s.nq + i0;                   // its position
+    dt.nrows = (int)min<int64_t>(DN_ROWS, nd - i0);
+    dt.row0 = dt.s.q0 + i0;
+    dt.t_last = dt.t0 + dt.nrows - 1;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+    if (w < 4) dense_wave<2, false>(a, dt, g, 2 * w, ks, vs);
+    else dense_wave<1, true>(a, dt, g, 4 + w, ks, vs);
 }
 
 hipError_t launch_attend_dense(const SeqInfo *tab, int batch, int topk, float scale,
