@@ -85,6 +85,7 @@ struct Pass {
     int64_t slot_lo = 0, slot_hi = 0;   // score slots (keys[s - slot_lo])
     int64_t max_blocks = 0;             // most blocks a row of the pass sees
     int64_t chunk = 0;                  // blocks per scoring workgroup
+    bool long_rows = false;             // max_blocks > SEL_LONG_KEYS: the long-row kernel
 };
 
 struct Plan {
@@ -150,8 +151,11 @@ qsa_status build_passes(const int32_t *cq, const int32_t *ck, int batch, int top
         p->pass_slots = std::max(p->pass_slots, ps.slot_hi - ps.slot_lo);
         const int64_t nt = ps.tile_hi - ps.tile_lo;
         if (nt <= 0) continue;
-        // enough workgroups to fill the chip when the pass has few tiles
-        int64_t gy = std::max<int64_t>(1, (2048 + nt - 1) / nt);
+        // enough workgroups to fill the chip when the pass has few tiles (the long-row
+        // kernel scores 4 tiles per workgroup)
+        ps.long_rows = ps.max_blocks > qsa::SEL_LONG_KEYS;
+        const int64_t ngr = ps.long_rows ? (nt + 3) / 4 : nt;
+        int64_t gy = std::max<int64_t>(1, (2048 + ngr - 1) / ngr);
         gy = std::min<int64_t>(gy, std::max<int64_t>(1, ps.max_blocks / 256));
         int64_t chunk = (ps.max_blocks + gy - 1) / gy;
         chunk = (chunk + 63) / 64 * 64;
@@ -388,7 +392,8 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
             tab, p.batch, p.topk, q_idx, w, k_blk, buf[i % 2], sc ? sc->tile_lo : 0,
             sc ? sc->tile_hi - sc->tile_lo : 0, sc ? sc->slot_lo : 0, sc ? sc->max_blocks : 0,
             sc ? sc->chunk : 1, buf[(i + 1) % 2], se ? se->slot_lo : 0, sel,
-            se ? se->row_lo : 0, se ? se->row_hi - se->row_lo : 0, st));
+            se ? se->row_lo : 0, se ? se->row_hi - se->row_lo : 0,
+            (sc && sc->long_rows) || (se && se->long_rows), st));
     }
     (void)s;
     return QSA_OK;

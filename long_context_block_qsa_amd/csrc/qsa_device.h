@@ -285,6 +285,8 @@ struct DigitPlan {
     int width[4];
 };
 constexpr DigitPlan kWide = {3, {21, 10, 0, 0}, {11, 11, 10, 0}};
+constexpr DigitPlan kWideFirst = {1, {21, 0, 0, 0}, {11, 0, 0, 0}};   // first digit only
+constexpr DigitPlan kWideRest = {2, {10, 0, 0, 0}, {11, 10, 0, 0}};   // after it
 constexpr int kHistBins = 2048;
 constexpr DigitPlan kNarrow = {4, {24, 16, 8, 0}, {8, 8, 8, 8}};
 
@@ -300,16 +302,23 @@ template <int NT> constexpr int radix_found_words() { return 2 + 2 * (NT / 64); 
 // three passes is skipped). All NT threads of the workgroup must call it. hist: LDS,
 // 2^max(width) entries; scan_sh: LDS, NT/64+1 entries; found: LDS,
 // radix_found_words<NT>() entries.
+// A select may also start below the first digit: prefix0 / pmask0 give the bits already
+// fixed (only keys matching them count) and k is then the rank among those keys. On
+// return *exact_out (if given) tells whether theta is the k-th key itself (every digit
+// refined, or the bin found held one key value) or only its bits under pmask so far.
 template <int NT, typename KeyPtr>
 __device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
                                           const DigitPlan &plan, uint32_t *hist,
                                           int32_t *scan_sh, uint32_t *found,
-                                          uint32_t *theta_out, int64_t *need_out) {
+                                          uint32_t *theta_out, int64_t *need_out,
+                                          uint32_t prefix0 = 0u, uint32_t pmask0 = 0u,
+                                          bool *exact_out = nullptr) {
     static_assert(NT == 256, "bin ownership assumes 256 threads");
     constexpr int NW = NT / WAVE;
     const int tid = threadIdx.x;
-    uint32_t prefix = 0, pmask = 0;
+    uint32_t prefix = prefix0, pmask = pmask0;
     int64_t need = k;
+    bool exact = false;
 #pragma unroll 1
     for (int pass = 0; pass < plan.n; ++pass) {
         const int shift = plan.shift[pass], nb = 1 << plan.width[pass];
@@ -379,11 +388,14 @@ __device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
         const uint32_t low = (1u << shift) - 1u;   // bits below this pass's digit
         if (((b_or ^ b_and) & low) == 0u) {        // uniform: every thread read the same words
             prefix |= b_or & low;
+            exact = true;
             break;
         }
+        if (shift == 0) exact = true;
     }
     *theta_out = prefix;
     *need_out = need;
+    if (exact_out) *exact_out = exact;
 }
 
 // Number of lanes below this one whose bit is set in mask.
@@ -475,6 +487,82 @@ __device__ __forceinline__ int64_t emit_kept(KeyPtr keys, int64_t n, uint32_t th
         run_sel += tk_tot;
     }
     return run_sel;
+}
+
+// Ordered pass that lists in LDS, by ascending position, the positions of the keys above
+// hi (a_pos) and the keys in [lo, hi] with their positions (c_key, c_pos); the caller
+// knows both counts fit. Element e of a batch is position base + e*NT + t, as in
+// emit_kept; a key's slot is the number of listed keys before it (earlier elements,
+// earlier waves at the same element, lower lanes). cnt: LDS, 4 * (NT/64) * PER ints (two
+// halves used by alternate batches, one barrier per batch). All NT threads must call it.
+template <int NT, int PER, typename KeyPtr>
+__device__ __forceinline__ void collect_bin(KeyPtr keys, int64_t n, uint32_t lo, uint32_t hi,
+                                            int32_t *a_pos, uint32_t *c_key, int32_t *c_pos,
+                                            int32_t *cnt) {
+    constexpr int NW = NT / WAVE;
+    static_assert(PER <= WAVE, "one lane per element writes the wave's counts");
+    const int tid = threadIdx.x, w = tid / WAVE, l = lane_id();
+    int run_a = 0, run_c = 0;
+    int par = 0;
+#pragma unroll 1
+    for (int64_t base = 0; base < n; base += (int64_t)NT * PER, par ^= 1) {
+        int32_t *ca = cnt + par * 2 * NW * PER;   // [wave][element]: keys above hi
+        int32_t *cc = ca + NW * PER;              // [wave][element]: keys in [lo, hi]
+        uint32_t kk[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int64_t i = base + (int64_t)e * NT + tid;
+            kk[e] = i < n ? keys[i] : 0u;
+        }
+        unsigned long long ba[PER], bc[PER];
+        int va = 0, vc = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const bool valid = base + (int64_t)e * NT + tid < n;
+            ba[e] = __ballot(valid && kk[e] > hi);
+            bc[e] = __ballot(valid && kk[e] >= lo && kk[e] <= hi);
+            va = l == e ? (int)__popcll(ba[e]) : va;
+            vc = l == e ? (int)__popcll(bc[e]) : vc;
+        }
+        if (l < PER) { ca[w * PER + l] = va; cc[w * PER + l] = vc; }
+        __syncthreads();
+        int pa = run_a, pc = run_c;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            int wa = 0, ta = 0, wc = 0, tc = 0;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const int xa = ca[i * PER + e], xc = cc[i * PER + e];
+                wa += i < w ? xa : 0;
+                ta += xa;
+                wc += i < w ? xc : 0;
+                tc += xc;
+            }
+            const int32_t pos = (int32_t)(base + (int64_t)e * NT + tid);
+            if ((ba[e] >> l) & 1ull) a_pos[pa + wa + lanes_below(ba[e])] = pos;
+            if ((bc[e] >> l) & 1ull) {
+                const int sl = pc + wc + lanes_below(bc[e]);
+                c_key[sl] = kk[e];
+                c_pos[sl] = pos;
+            }
+            pa += ta;
+            pc += tc;
+        }
+        run_a = pa;
+        run_c = pc;
+    }
+    __syncthreads();
+}
+
+// Number of entries of the ascending list v[0..n) below x.
+__device__ __forceinline__ int lower_bound_i32(const int32_t *v, int n, int32_t x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (v[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
 }
 
 // ---------------------------------------------------------------- wave-level select

@@ -278,7 +278,8 @@ struct ScorePass {
     const uint16_t *k_blk;
     uint32_t *keys;
     int64_t chunk_blocks, tile_base, slot_base;
-    int gy;   // chunks per tile
+    int64_t n_tiles;   // tiles of the pass
+    int gy;   // chunks per tile group
 };
 
 constexpr int SC_LDS_BYTES = (SCORE_NT / WAVE) * 2 * SC_TILE;
@@ -305,6 +306,118 @@ __device__ __forceinline__ void score_tile_body(const ScorePass &sp, int64_t til
         for (int u = 0; u < SCORE_BATCH; ++u) {
             const int64_t blk = b0 + u * step + c;
             if (blk < hi && blk < sl.nv_row) keys[sl.slot + blk] = key[u];
+        }
+    }
+}
+
+// Score tiles are taken SC_TG at a time: a workgroup scores the tiles of a group (up to
+// 16 consecutive rows of one sequence) over its chunk of blocks, and each 16-block group
+// of keys it stages in LDS feeds the MFMAs of every tile, so a block key is read once per
+// 16 rows instead of once per 4. A group that spans two sequences (their blocks differ)
+// scores its tiles one after another.
+constexpr int SC_TG = 4;
+constexpr int SC_GBATCH = 2;   // 16-block groups per wave in flight
+
+// Operands of one tile of a group (as ScoreLane; slot relative to the pass buffer and the
+// row's visible blocks fit 32 bits).
+struct GroupLane {
+    u32x4 qa[2];
+    float wr[HI];
+    int32_t slot, nv_row;
+};
+
+template <int NB>
+__device__ __forceinline__ void score_groups_lds_tg(const GroupLane (&sl)[SC_TG],
+                                                    const uint16_t *kb, int64_t b0, int64_t step,
+                                                    int64_t hi, uint32_t (&key)[NB][SC_TG],
+                                                    uint8_t *tiles) {
+    const int l = lane_id(), g = l >> 4, c = l & 15, bj = l >> 3, q = l & 7;
+    u32x4 b[NB][2];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t blk = b0 + u * step + 8 * h + bj;
+            b[u][h] = load16(kb + (blk < hi ? blk : hi - 1) * DI + 8 * q);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the MFMAs
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        uint8_t *t = tiles + (u & 1) * SC_TILE;
+        wave_lds_sync();   // this tile's reads of two groups ago are done
+        *reinterpret_cast<u32x4 *>(t + bj * SC_PITCH + 16 * q) = b[u][0];
+        *reinterpret_cast<u32x4 *>(t + (8 + bj) * SC_PITCH + 16 * q) = b[u][1];
+        wave_lds_sync();
+        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(t + c * SC_PITCH + 16 * g);
+        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(t + c * SC_PITCH + 64 + 16 * g);
+#pragma unroll
+        for (int nt = 0; nt < SC_TG; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mfma_bf16_16x16x32(sl[nt].qa[0], x0, acc);
+            acc = mfma_bf16_16x16x32(sl[nt].qa[1], x1, acc);
+            float sc = sl[nt].wr[0] * fmaxf(acc[0], 0.f);
+            sc += sl[nt].wr[1] * fmaxf(acc[1], 0.f);
+            sc += sl[nt].wr[2] * fmaxf(acc[2], 0.f);
+            sc += sl[nt].wr[3] * fmaxf(acc[3], 0.f);
+            key[u][nt] = score_key(sc);
+        }
+    }
+}
+
+// Tiles tile0 .. tile0 + ntg - 1 (1 <= ntg <= SC_TG) of a pass, blocks [chunk *
+// chunk_blocks, +chunk_blocks) of each.
+__device__ __forceinline__ void score_group_body(const ScorePass &sp, int64_t tile0, int ntg,
+                                                 int chunk, uint8_t *smem) {
+    const TileInfo ti = tile_info(sp.tab, sp.batch, sp.topk, tile0);
+    const int64_t seq_tiles = (ti.s.L - ti.ts + 3) / 4;
+    if (tile0 + ntg > ti.s.tile0 + seq_tiles) {   // uniform: the group spans two sequences
+        for (int j = 0; j < ntg; ++j) score_tile_body(sp, tile0 + j, chunk, smem);
+        return;
+    }
+    const int64_t t_last = min<int64_t>(ti.t0 + 4 * ntg, ti.s.L) - 1;   // last row's position
+    const int64_t lo = (int64_t)chunk * sp.chunk_blocks;
+    const int64_t hi = min<int64_t>(nvis_of(t_last), lo + sp.chunk_blocks);
+    if (lo >= hi) return;
+    const int g = lane_id() >> 4;
+    const int64_t slot_ts = slots_before(ti.ts);
+    GroupLane sl[SC_TG];
+#pragma unroll
+    for (int nt = 0; nt < SC_TG; ++nt) {
+        const int64_t t0 = ti.t0 + 4 * nt;
+        const int nrows = nt < ntg ? (int)min<int64_t>(4, ti.s.L - t0) : 0;
+        if (nrows > 0) {
+            const ScoreLane x = score_lane_setup(
+                sp.q_idx, sp.w, ti.row0 + 4 * nt, nrows, t0,
+                ti.s.s0 + slots_before(t0 + g) - slot_ts - sp.slot_base);
+            sl[nt].qa[0] = x.qa[0];
+            sl[nt].qa[1] = x.qa[1];
+#pragma unroll
+            for (int h = 0; h < HI; ++h) sl[nt].wr[h] = x.wr[h];
+            sl[nt].slot = (int32_t)x.slot;     // below the pass's key budget
+            sl[nt].nv_row = (int32_t)x.nv_row;
+        } else {   // no such tile: zero operands, nothing stored
+            sl[nt].qa[0] = sl[nt].qa[1] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int h = 0; h < HI; ++h) sl[nt].wr[h] = 0.f;
+            sl[nt].slot = 0;
+            sl[nt].nv_row = 0;
+        }
+    }
+    const uint16_t *kb = sp.k_blk + (int64_t)ti.s.blk0 * DI;
+    const int c = lane_id() & 15;
+    uint8_t *tiles = smem + (threadIdx.x / WAVE) * 2 * SC_TILE;
+    uint32_t *keys = sp.keys;
+    constexpr int64_t step = 16 * (SCORE_NT / WAVE);
+    for (int64_t b0 = lo + 16 * (threadIdx.x / WAVE); b0 < hi; b0 += step * SC_GBATCH) {
+        uint32_t key[SC_GBATCH][SC_TG];
+        score_groups_lds_tg<SC_GBATCH>(sl, kb, b0, step, hi, key, tiles);
+#pragma unroll
+        for (int u = 0; u < SC_GBATCH; ++u) {
+            const int64_t blk = b0 + u * step + c;
+#pragma unroll
+            for (int nt = 0; nt < SC_TG; ++nt)
+                if (blk < hi && blk < sl[nt].nv_row) keys[sl[nt].slot + (int32_t)blk] = key[u][nt];
         }
     }
 }
@@ -411,6 +524,78 @@ __device__ __forceinline__ void select_keys(KP_T kk, int64_t n, int topk, int32_
     emit_kept<SEL_NT, PER>(kk, n, theta, need, out, topk, reinterpret_cast<int32_t *>(hist));
 }
 
+// LDS of select_keys_bin (beside the radix histogram of select_keys).
+constexpr int SEL_CCAP = 2048;   // keys of the first digit's crossing bin listed in LDS
+constexpr int SEL_CPER = SEL_CCAP / SEL_NT;
+struct SelectLds {
+    int32_t a_pos[KMAX];        // positions of the keys above the bin, ascending
+    int32_t k2[KMAX];           // the bin's kept keys: their list slots, then positions
+    uint32_t c_key[SEL_CCAP];   // the bin's keys and positions, by position
+    int32_t c_pos[SEL_CCAP];
+};
+
+// select_keys with one global pass fewer when the first digit's crossing bin is small:
+// the first radix digit gives the bin holding the topk-th key (`need` of its keys are
+// kept, every key above it is); one ordered pass lists the positions of the keys above
+// the bin and the bin's keys in LDS; the bin's keys are ranked there (key descending,
+// position ascending), and the two ascending position lists are merged into out. A bin
+// of one key value needs no ranking (the emit pass follows the first digit directly);
+// a bin of more than SEL_CCAP keys takes the remaining radix digits over global memory.
+template <int PER, typename KP_T>
+__device__ __forceinline__ void select_keys_bin(KP_T kk, int64_t n, int topk, int32_t *out,
+                                                uint32_t *hist, int32_t *scan_sh,
+                                                uint32_t *found, SelectLds &xl) {
+    if (n <= SEL_LONG_KEYS) {   // uniform: a row whose keys the L2 keeps between passes
+        select_keys<PER>(kk, n, topk, out, hist, scan_sh, found);
+        return;
+    }
+    uint32_t theta;
+    int64_t need;
+    bool exact;
+    radix_kth<SEL_NT>(kk, n, topk, kWideFirst, hist, scan_sh, found, &theta, &need, 0u, 0u,
+                      &exact);
+    static_assert(4 * (SEL_NT / WAVE) * PER <= kHistBins, "emit counts fit the histogram");
+    if (exact) {   // uniform
+        emit_kept<SEL_NT, PER>(kk, n, theta, need, out, topk, reinterpret_cast<int32_t *>(hist));
+        return;
+    }
+    const uint32_t bin_mask = 0xffe00000u;   // the first digit (bits 21..31)
+    const int m = (int)hist[theta >> 21];     // keys in the bin
+    __syncthreads();                          // every thread has read it
+    if (m > SEL_CCAP) {   // uniform
+        radix_kth<SEL_NT>(kk, n, need, kWideRest, hist, scan_sh, found, &theta, &need, theta,
+                          bin_mask);
+        emit_kept<SEL_NT, PER>(kk, n, theta, need, out, topk, reinterpret_cast<int32_t *>(hist));
+        return;
+    }
+    const int n_above = topk - (int)need;
+    // (the first digit's histogram has been read: it holds the collect counts)
+    static_assert(4 * (SEL_NT / WAVE) * PER <= kHistBins, "collect counts fit the histogram");
+    collect_bin<SEL_NT, PER>(kk, n, theta, theta | ~bin_mask, xl.a_pos, xl.c_key, xl.c_pos,
+                             reinterpret_cast<int32_t *>(hist));
+    // rank the bin in LDS: the need-th of its keys, then its kept keys' list slots
+    uint32_t theta2;
+    int64_t need2;
+    radix_kth<SEL_NT>(xl.c_key, m, need, kWideRest, hist, scan_sh, found, &theta2, &need2,
+                      theta, bin_mask);
+    static_assert(4 * (SEL_NT / WAVE) * SEL_CPER <= kHistBins, "emit counts fit the histogram");
+    emit_kept<SEL_NT, SEL_CPER>(xl.c_key, m, theta2, need2, xl.k2, need,
+                                reinterpret_cast<int32_t *>(hist));
+    __syncthreads();
+    const int nk = (int)need;
+    for (int j = threadIdx.x; j < nk; j += SEL_NT) xl.k2[j] = xl.c_pos[xl.k2[j]];
+    __syncthreads();
+    // merge: an entry's output slot is its own index plus the other list's entries below it
+    for (int i = threadIdx.x; i < n_above; i += SEL_NT) {
+        const int32_t pos = xl.a_pos[i];
+        out[i + lower_bound_i32(xl.k2, nk, pos)] = pos;
+    }
+    for (int j = threadIdx.x; j < nk; j += SEL_NT) {
+        const int32_t pos = xl.k2[j];
+        out[j + lower_bound_i32(xl.a_pos, n_above, pos)] = pos;
+    }
+}
+
 // Level-one merges take at most MERGE_CHUNKS chunk lists (KP candidates each; the
 // constant is shared with the host, qsa_launch.h); rows with more chunks first merge
 // G = ceil(nch / MERGE_CHUNKS) groups of ceil(nch / G) consecutive chunks (balanced,
@@ -496,8 +681,10 @@ __device__ __forceinline__ bool merge_candidates(const uint32_t *ck, const int32
 // keep blocks 0..nvis-1, others get an exact radix select over the keys in global memory
 // (each pass re-reads them from L2; staging up to 64 KB of keys per row in LDS held
 // occupancy to two workgroups per CU and was a third slower).
+// xl: LDS lists for long rows (select_keys_bin), or null (select_keys).
 __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView rv, int64_t row,
-                                            uint32_t *hist, int32_t *scan_sh, uint32_t *found) {
+                                            uint32_t *hist, int32_t *scan_sh, uint32_t *found,
+                                            SelectLds *xl) {
     const int64_t nv = nvis_of(rv.t);
     int32_t *out = a.sel + row * a.topk;
     const int tid = threadIdx.x;
@@ -506,7 +693,11 @@ __device__ __forceinline__ void select_body(const SelectArgs &a, const RowView r
         return;
     }
     if (a.dense_only) return;
-    select_keys<16>(a.keys + (rv.slot - a.slot_base), nv, a.topk, out, hist, scan_sh, found);
+    if (xl)
+        select_keys_bin<16>(a.keys + (rv.slot - a.slot_base), nv, a.topk, out, hist, scan_sh,
+                            found, *xl);
+    else
+        select_keys<16>(a.keys + (rv.slot - a.slot_base), nv, a.topk, out, hist, scan_sh, found);
 }
 
 struct LocalArgs {
@@ -900,31 +1091,48 @@ select_kernel(SelectArgs a) {
     __shared__ int32_t scan_sh[SEL_NT / WAVE];
     __shared__ uint32_t found[radix_found_words<SEL_NT>()];
     const int64_t row = a.row_base + blockIdx.x;
-    select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, hist, scan_sh, found);
+    select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, hist, scan_sh, found, nullptr);
 }
 
 // One launch per pass boundary: workgroups [0, n_sel) select the rows of the previous
 // pass (its keys complete since the previous launch), the others score the tiles of the
-// next pass into the other keys buffer (workgroup n_sel + s: tile s / gy, chunk s % gy).
-// The two roles touch disjoint buffers; the latency-bound selections and the MFMA
-// scoring share the machine instead of each ending with its own tail.
+// next pass into the other keys buffer. The two roles touch disjoint buffers; the
+// latency-bound selections and the MFMA scoring share the machine instead of each ending
+// with its own tail. LONG (rows that see more than SEL_LONG_KEYS blocks): scoring
+// workgroup n_sel + s takes tile group s / gy (SC_TG tiles), chunk s % gy, and rows are
+// selected with their crossing bin listed in LDS; otherwise workgroup n_sel + s takes tile
+// s / gy alone and rows are selected in three global passes, in less LDS and fewer
+// registers (five waves per SIMD).
 static_assert(SEL_NT == SCORE_NT, "one block size for both roles");
 constexpr int SEL_LDS_WORDS = kHistBins + SEL_NT / WAVE + radix_found_words<SEL_NT>();
+constexpr int SEL_LONG_LDS_WORDS = SEL_LDS_WORDS + (int)(sizeof(SelectLds) / 4);
 constexpr int SS_LDS_BYTES = SC_LDS_BYTES > SEL_LDS_WORDS * 4 ? SC_LDS_BYTES : SEL_LDS_WORDS * 4;
+constexpr int SS_LONG_LDS_BYTES =
+    SC_LDS_BYTES > SEL_LONG_LDS_WORDS * 4 ? SC_LDS_BYTES : SEL_LONG_LDS_WORDS * 4;
 
+template <bool LONG>
 __global__ void __launch_bounds__(SCORE_NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 score_select_kernel(ScorePass sp, SelectArgs a, int n_sel) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[SS_LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[LONG ? SS_LONG_LDS_BYTES : SS_LDS_BYTES];
     if ((int)blockIdx.x < n_sel) {   // uniform over the workgroup
         uint32_t *hist = reinterpret_cast<uint32_t *>(smem);
         int32_t *scan_sh = reinterpret_cast<int32_t *>(hist + kHistBins);
         uint32_t *found = reinterpret_cast<uint32_t *>(scan_sh + SEL_NT / WAVE);
+        SelectLds *xl =
+            LONG ? reinterpret_cast<SelectLds *>(found + radix_found_words<SEL_NT>()) : nullptr;
         const int64_t row = a.row_base + blockIdx.x;
-        select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, hist, scan_sh, found);
+        select_body(a, tab_row(a.tab, a.batch, a.topk, row), row, hist, scan_sh, found, xl);
         return;
     }
     const int64_t s = (int64_t)blockIdx.x - n_sel;
-    score_tile_body(sp, sp.tile_base + s / sp.gy, (int)(s % sp.gy), smem);
+    if constexpr (LONG) {
+        const int64_t grp = s / sp.gy;
+        score_group_body(sp, sp.tile_base + SC_TG * grp,
+                         (int)min<int64_t>(SC_TG, sp.n_tiles - SC_TG * grp), (int)(s % sp.gy),
+                         smem);
+    } else {
+        score_tile_body(sp, sp.tile_base + s / sp.gy, (int)(s % sp.gy), smem);
+    }
 }
 
 __global__ void __launch_bounds__(SEL_NT)
@@ -935,7 +1143,7 @@ select_dec_kernel(SelectArgs a, DecodeTables d) {
     const int64_t row = blockIdx.x;
     const DecRow r = d.row[row];
     const RowView rv = {r.k0, r.t, r.blk0, r.slot};
-    select_body(a, rv, row, hist, scan_sh, found);
+    select_body(a, rv, row, hist, scan_sh, found, nullptr);
 }
 
 // =============================================================== attend
@@ -1625,20 +1833,27 @@ hipError_t launch_score_select(const SeqInfo *tab, int batch, int topk, const ui
                                int64_t tile_base, int64_t n_tiles, int64_t score_slot_base,
                                int64_t max_blocks, int64_t chunk_blocks,
                                const uint32_t *sel_keys, int64_t sel_slot_base, int32_t *sel,
-                               int64_t row_base, int64_t n_rows, hipStream_t st) {
+                               int64_t row_base, int64_t n_rows, bool long_rows,
+                               hipStream_t st) {
     ScorePass sp = {};
     sp.tab = tab; sp.batch = batch; sp.topk = topk; sp.q_idx = q_idx; sp.w = w; sp.k_blk = k_blk;
     sp.keys = score_keys; sp.chunk_blocks = chunk_blocks; sp.tile_base = tile_base;
     sp.slot_base = score_slot_base;
+    sp.n_tiles = n_tiles;
     sp.gy = n_tiles > 0 ? (int)((max_blocks + chunk_blocks - 1) / chunk_blocks) : 0;
     SelectArgs a = {};
     a.tab = tab; a.batch = batch; a.topk = topk; a.keys = sel_keys; a.slot_base = sel_slot_base;
     a.row_base = row_base; a.sel = sel;
-    const int64_t n_wg = n_rows + n_tiles * sp.gy;
+    const int64_t n_wg =
+        n_rows + (long_rows ? (n_tiles + SC_TG - 1) / SC_TG : n_tiles) * sp.gy;
     if (n_wg <= 0) return hipSuccess;
     trace_before(14, st);
-    hipLaunchKernelGGL(score_select_kernel, dim3((unsigned)n_wg), dim3(SCORE_NT), 0, st, sp, a,
-                       (int)n_rows);
+    if (long_rows)
+        hipLaunchKernelGGL(score_select_kernel<true>, dim3((unsigned)n_wg), dim3(SCORE_NT), 0,
+                           st, sp, a, (int)n_rows);
+    else
+        hipLaunchKernelGGL(score_select_kernel<false>, dim3((unsigned)n_wg), dim3(SCORE_NT), 0,
+                           st, sp, a, (int)n_rows);
     return trace_after(st, hipGetLastError());
 }
 

@@ -18,6 +18,11 @@ struct Fp8Kv {
 // Chunk lists one decode merge takes (longer rows merge groups of chunks first).
 constexpr int MERGE_CHUNKS = 64;
 
+// Prefill score + select launches whose rows see more blocks than this take the variant
+// for long rows (score tiles grouped 4 at a time, selections that list the first radix
+// digit's crossing bin in LDS); the others keep the leaner kernel, at more waves per SIMD.
+constexpr int64_t SEL_LONG_KEYS = 16384;
+
 // Optional per-kernel event trace (thread-local; see qsa_trace_begin).
 void trace_before(int kind, hipStream_t st);
 hipError_t trace_after(hipStream_t st, hipError_t launch_status);
@@ -36,7 +41,8 @@ hipError_t launch_score_select(const SeqInfo *tab, int batch, int topk, const ui
                                int64_t tile_base, int64_t n_tiles, int64_t score_slot_base,
                                int64_t max_blocks, int64_t chunk_blocks,
                                const uint32_t *sel_keys, int64_t sel_slot_base, int32_t *sel,
-                               int64_t row_base, int64_t n_rows, hipStream_t st);
+                               int64_t row_base, int64_t n_rows, bool long_rows,
+                               hipStream_t st);
 // Scores of the listed rows (fp32, -inf past the row's visible blocks), [n_rows, ld].
 hipError_t launch_score_rows(const int32_t *cu_q, const int32_t *cu_k, int batch,
                              const int64_t *rows, int64_t n_rows, const uint16_t *q_idx,

@@ -182,6 +182,22 @@ def test_prefill_ragged_64k_all_selections():
     _check_all_selections("ragged-64k", DeviceProblem(p), rows)
 
 
+def test_prefill_crowded_first_digit():
+    """Indexer values in [2, 3] keep every score of a row within about 10% of each other,
+    so the bin of the first 11-bit radix digit that holds the 512th key holds nearly all of
+    the row's keys (hundreds of distinct values, heavy ties). One 70,001-token sequence: rows
+    past position 65,539 see more than 16,384 blocks, so their launches take the long-row
+    select, whose LDS list cannot hold such a bin and which continues the radix digits over
+    global memory; earlier rows take the lean select. 160 rows across the sequence (both
+    sides of that boundary, and its last rows): selections bit-exact, out and lse within
+    the bars."""
+    _banner("prefill, crowded first radix digit")
+    p = gen.make_problem([70001], seed=23, idx_lo=2, idx_hi=3)
+    rows = sorted(set(np.linspace(0, 70000, 130).astype(int).tolist())
+                  | set(range(65530, 65550)) | set(range(69990, 70001)))
+    _check_rows("crowded-bins", DeviceProblem(p), rows, 512)
+
+
 def test_prefill_1x262144_bounded_workspace():
     """One prefill at the native context, 262,144 tokens: its 8.6e9 score slots (34 GB
     of keys if kept whole) are scored and selected in passes of at most 2^26 keys, in a
