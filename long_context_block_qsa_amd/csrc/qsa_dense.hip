@@ -29,18 +29,22 @@
 
 namespace qsa {
 
-// Column tiles: waves 0-3 take two each (tiles 2w, 2w + 1), waves 4-7 one each (tile 4 + w)
-// and also stage the K/V tiles, so that each SIMD (waves w and w + 4) carries three column
-// tiles of MFMA work per key tile.
-constexpr int DN_WAVES = 8;
-constexpr int DN_NT = DN_WAVES * WAVE;
+// The 12 column tiles of a (dense tile, KV head) go to CS workgroups of 12 / CS each.
+// CS = 1 (8 waves): waves 0-3 take two each (tiles 2w, 2w + 1), waves 4-7 one each (tile
+// 4 + w) and also stage the K/V tiles, so each SIMD (waves w and w + 4) carries three column
+// tiles of MFMA work per key tile. CS = 2 (4 waves, every thread staging, two key tiles in
+// flight): waves 0-1 take two tiles, waves 2-3 one, so no SIMD carries more than two; twice
+// the workgroups share each key tile (through the L2), for launches with too few dense tiles
+// to fill the machine.
 constexpr int DN_KEYS = 32;
 constexpr int DN_PITCH = 2 * HD + 16;     // LDS row pitch (bytes) of the K and V tiles
 constexpr int DN_TILE_BYTES = DN_KEYS * DN_PITCH;
 constexpr int DN_STAGE_NT = DN_KEYS * 8;  // threads that stage a tile (32 bytes of K and V each)
-constexpr int DN_STAGE_T0 = 4 * WAVE;     // first staging thread (waves 4-7)
+template <int CS> constexpr int dn_threads() { return CS == 1 ? 8 * WAVE : 4 * WAVE; }
+template <int CS> constexpr int dn_stage_t0() { return dn_threads<CS>() - DN_STAGE_NT; }
 static_assert(DN_ROWS * GQ == 16 * (4 * 2 + 4 * 1), "12 column tiles over the 8 waves");
-static_assert(DN_STAGE_T0 + DN_STAGE_NT == DN_NT, "waves 4-7 stage a tile");
+static_assert(DN_ROWS * GQ / 2 == 16 * (2 * 2 + 2 * 1), "6 column tiles over the 4 waves");
+static_assert(dn_stage_t0<1>() == 4 * WAVE && dn_stage_t0<2>() == 0, "the staging threads");
 
 struct DenseArgs {
     const SeqInfo *tab;
@@ -61,9 +65,11 @@ struct DenseTile {
 // One wave's part of a workgroup: NQ column tiles from column tile ct0 (query vectors
 // 16 ct0 .. 16 (ct0 + NQ) - 1), the key loop with the workgroup's barriers (every wave runs
 // the same number of iterations), and, for the staging waves, the K/V staging.
-template <int NQ, bool STAGE>
+// AHEAD: key tiles whose loads the staging threads keep in flight (1 or 2).
+template <int NQ, bool STAGE, int STAGE_T0, int AHEAD>
 __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &dt, int g,
                                            int ct0, uint8_t *ks0, uint8_t *vs0) {
+    static_assert(AHEAD == 1 || AHEAD == 2, "one or two tiles ahead");
     const int tid = threadIdx.x, l = lane_id(), gr = l >> 4, col = l & 15;
     const int64_t row0 = dt.row0, t0 = dt.t0, t_last = dt.t_last;
     const int nrows = dt.nrows;
@@ -95,8 +101,8 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
 #pragma unroll
     for (int nt = 0; nt < NQ; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
 
-    // staging: thread DN_STAGE_T0 + i -> (key i / 8, 32-byte piece i % 8) of the K and V rows
-    const int st = tid - DN_STAGE_T0;
+    // staging: thread STAGE_T0 + i -> (key i / 8, 32-byte piece i % 8) of the K and V rows
+    const int st = tid - STAGE_T0;
     const int sk = (st >> 3) & (DN_KEYS - 1), sp = st & 7;
     const uint16_t *kbase = a.k + (int64_t)dt.s.k0 * (HKV * HD) + g * HD + 16 * sp;
     const uint16_t *vbase = a.v + (int64_t)dt.s.k0 * (HKV * HD) + g * HD + 16 * sp;
@@ -117,18 +123,24 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
     };
 
     // the tiles alternate between two LDS buffers: tile j + 1 is written while tile j is
-    // read, and one barrier per tile makes it visible (and frees tile j's buffer)
-    u32x4 kr[2], vr[2];
+    // read, and one barrier per tile makes it visible (and frees tile j's buffer). The
+    // staging registers hold tile j + 1 (AHEAD = 1: loaded at the start of tile j), or
+    // tiles j + 1 and j + 2 (AHEAD = 2: tile i in set i % 2, tile j + 3 loaded once tile
+    // j + 1 is stored).
+    u32x4 kr0[2], vr0[2], kr1[2], vr1[2];
     if constexpr (STAGE) {
-        load_stage(0, kr, vr);
-        store_stage(0, kr, vr);
+        load_stage(0, kr0, vr0);
+        store_stage(0, kr0, vr0);
+        if constexpr (AHEAD == 2) {
+            if (DN_KEYS <= t_last) load_stage(DN_KEYS, kr1, vr1);
+            if (2 * DN_KEYS <= t_last) load_stage(2 * DN_KEYS, kr0, vr0);
+        }
     }
     __syncthreads();
-    int buf = 0;
-    for (int64_t j0 = 0; j0 <= t_last; j0 += DN_KEYS, buf ^= 1) {
+    auto step = [&](int64_t j0, int buf, u32x4 (&krn)[2], u32x4 (&vrn)[2]) {
         const bool more = j0 + DN_KEYS <= t_last;
-        if constexpr (STAGE)
-            if (more) load_stage(j0 + DN_KEYS, kr, vr);   // next tile in flight
+        if constexpr (STAGE && AHEAD == 1)
+            if (more) load_stage(j0 + DN_KEYS, krn, vrn);   // next tile in flight
         const uint8_t *ks = ks0 + buf * DN_TILE_BYTES;
         const uint8_t *vs = vs0 + buf * DN_TILE_BYTES;
         if (j0 <= wave_tmax) {                         // uniform over the wave
@@ -217,9 +229,22 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
                 }
             }
         }
-        if constexpr (STAGE)
-            if (more) store_stage(buf ^ 1, kr, vr);   // the buffer of tile j - 1, done with
+        if constexpr (STAGE) {
+            if (more) store_stage(buf ^ 1, krn, vrn);   // tile j + 1 into the buffer of j - 1
+            if constexpr (AHEAD == 2)
+                if (j0 + 3 * DN_KEYS <= t_last) load_stage(j0 + 3 * DN_KEYS, krn, vrn);
+        }
         __syncthreads();   // tile j + 1 staged, every wave done with tile j
+    };
+    if constexpr (AHEAD == 1) {
+        int buf = 0;
+        for (int64_t j0 = 0; j0 <= t_last; j0 += DN_KEYS, buf ^= 1) step(j0, buf, kr0, vr0);
+    } else {
+        for (int64_t j0 = 0; j0 <= t_last; j0 += 2 * DN_KEYS) {
+            step(j0, 0, kr1, vr1);
+            if (j0 + DN_KEYS > t_last) break;
+            step(j0 + DN_KEYS, 1, kr0, vr0);
+        }
     }
 
     // lane (gr, col), column tile nt: acc[nt][mt][i] = O[vector 16(ct0 + nt) + col]
@@ -247,11 +272,12 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
     }
 }
 
-__global__ void __launch_bounds__(DN_NT)
+template <int CS>
+__global__ void __launch_bounds__(dn_threads<CS>())
 attend_dense_kernel(DenseArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t ks[2 * DN_TILE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t vs[2 * DN_TILE_BYTES];
-    const int g = blockIdx.y;
+    const int g = blockIdx.y / CS, part = blockIdx.y % CS;
     const int64_t tile = a.n_tiles - 1 - (int64_t)blockIdx.x;
     const int sb = find_seq(a.batch, tile, [&](int i) { return (int64_t)a.tab[i].dtile0; });
     DenseTile dt;
@@ -263,8 +289,14 @@ attend_dense_kernel(DenseArgs a) {
     dt.row0 = dt.s.q0 + i0;
     dt.t_last = dt.t0 + dt.nrows - 1;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
-    if (w < 4) dense_wave<2, false>(a, dt, g, 2 * w, ks, vs);
-    else dense_wave<1, true>(a, dt, g, 4 + w, ks, vs);
+    if constexpr (CS == 1) {
+        if (w < 4) dense_wave<2, false, dn_stage_t0<1>(), 1>(a, dt, g, 2 * w, ks, vs);
+        else dense_wave<1, true, dn_stage_t0<1>(), 1>(a, dt, g, 4 + w, ks, vs);
+    } else {
+        const int c0 = 6 * part;
+        if (w < 2) dense_wave<2, true, dn_stage_t0<2>(), 2>(a, dt, g, c0 + 2 * w, ks, vs);
+        else dense_wave<1, true, dn_stage_t0<2>(), 2>(a, dt, g, c0 + 2 + w, ks, vs);
+    }
 }
 
 hipError_t launch_attend_dense(const SeqInfo *tab, int batch, int topk, float scale,
@@ -276,7 +308,13 @@ hipError_t launch_attend_dense(const SeqInfo *tab, int batch, int topk, float sc
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.n_tiles = n_tiles;
     trace_before(15, st);
-    hipLaunchKernelGGL(attend_dense_kernel, dim3((unsigned)n_tiles, HKV), dim3(DN_NT), 0, st, a);
+    // fewer dense tiles than the machine has CUs per KV head: split their column tiles
+    if (n_tiles * HKV < 256)
+        hipLaunchKernelGGL(attend_dense_kernel<2>, dim3((unsigned)n_tiles, HKV * 2),
+                           dim3(dn_threads<2>()), 0, st, a);
+    else
+        hipLaunchKernelGGL(attend_dense_kernel<1>, dim3((unsigned)n_tiles, HKV),
+                           dim3(dn_threads<1>()), 0, st, a);
     return trace_after(st, hipGetLastError());
 }
 
