@@ -198,6 +198,19 @@ def test_prefill_crowded_first_digit():
     _check_rows("crowded-bins", DeviceProblem(p), rows, 512)
 
 
+def test_prefill_long_rows_two_sequences():
+    """Two long sequences (70,001 and 66,001 tokens) whose rows see more than 16,384 blocks:
+    their launches score tiles 4 at a time, and the group holding the first sequence's last
+    3 tiles and the second sequence's first tile spans both sequences (scored tile by tile).
+    Both sides of that boundary, the first sequence's last rows and rows spread over both:
+    selections bit-exact, out and lse within the bars."""
+    _banner("prefill, two long sequences")
+    p = gen.make_problem([70001, 66001], seed=29)
+    rows = sorted(set(np.linspace(0, p.n_q - 1, 120).astype(int).tolist())
+                  | set(range(69980, 70001)) | set(range(70001 + 2040, 70001 + 2070)))
+    _check_rows("two-long", DeviceProblem(p), rows, 512)
+
+
 def test_prefill_1x262144_bounded_workspace():
     """One prefill at the native context, 262,144 tokens: its 8.6e9 score slots (34 GB
     of keys if kept whole) are scored and selected in passes of at most 2^26 keys, in a
