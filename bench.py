@@ -42,7 +42,7 @@ HOST_THREADS = 16   # host threads for the oracle baseline: one GPU's share of t
 # reads on a plain 512 MiB copy) from rocprofv3 --pmc runs of this benchmark, with the
 # fingerprint of the kernel sources they were taken on; reported only while it matches.
 TRAFFIC = {
-    "score": {"bytes": 135_050_000, "sources_sha256": "68b7e8b2b6985a0b1119edba1bcbc1963d67d911cd720f7da0853a895e061478"},
+    "score": {"bytes": 135_050_000, "sources_sha256": "5a49af688f82de3bc6677634ebcd936358fa5cebaed76fe761a02deb8d909804"},
 }
 
 
