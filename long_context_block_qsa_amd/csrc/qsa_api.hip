@@ -104,7 +104,7 @@ struct Plan {
     int nsplit = 1;             // attention key splits per row
     int64_t n_dense = 0;        // query rows with at most topk visible blocks
     int64_t n_dense_tiles = 0;  // their tiles of DN_ROWS rows (per sequence)
-    size_t off_ctl = 0, off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0, off_glist = 0,
+    size_t off_ctl = 0, off_tab = 0, off_sel = 0, off_union = 0, off_cand = 0,
            off_part = 0;
     size_t ws_bytes = 0;
     bool use_dec = false;       // few rows: row/tile tables travel as kernel arguments
@@ -280,7 +280,7 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
         for (int64_t i = 0; i < p->n_tiles && !p->merge_launch; ++i) {
             const qsa::DecTile &tl = p->dec.tile[i];
             const int64_t nv_max = ((int64_t)p->dec.row[tl.row0].t + tl.nrows) / qsa::BS;
-            p->merge_launch = (nv_max + ch - 1) / ch <= qsa::MERGE_CHUNKS;
+            p->merge_launch = (nv_max + ch - 1) / ch <= qsa::MERGE_CHUNKS_WIDE;
         }
     }
     // prefill-shaped calls: passes of whole score tiles under the key budget
@@ -309,9 +309,6 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
         : align_up((size_t)p->pass_slots * sizeof(uint32_t)) * (p->passes.size() > 1 ? 2 : 1);
     const size_t cand_b = p->local_ch > 0
         ? align_up((size_t)p->tq * p->max_chunks * kKP * 2 * sizeof(uint32_t)) : 0;
-    // group merge results of rows with more than 64 chunks (at most 4 groups of topk)
-    const size_t glist_b = p->local_ch > 0 && p->max_chunks > 64
-        ? align_up((size_t)p->tq * 4 * p->topk * 2 * sizeof(uint32_t)) : 0;
     const size_t part_b = p->nsplit > 1
         ? align_up((size_t)p->tq * p->nsplit * qsa::HQ * (qsa::HD + 4) * sizeof(float)) : 0;
     p->off_ctl = 0;
@@ -319,12 +316,11 @@ qsa_status make_plan(const qsa_dims *d, const qsa_seqs *s, bool need_q, Plan *p)
     p->off_sel = ctl_b + tab_b;
     p->off_union = ctl_b + tab_b + sel_b;  // scores (+ candidates) while selecting, then partials
     p->off_cand = p->off_union + score_b;
-    p->off_glist = p->off_cand + cand_b;
     // decode (chunk candidates): the attention reads the candidates while it writes its
     // partials, so they get their own space; otherwise the partials reuse the scores'
-    p->off_part = p->local_ch > 0 ? p->off_glist + glist_b : p->off_union;
+    p->off_part = p->local_ch > 0 ? p->off_cand + cand_b : p->off_union;
     p->ws_bytes = p->local_ch > 0 ? p->off_part + part_b
-                                  : p->off_union + std::max(score_b + cand_b + glist_b, part_b);
+                                  : p->off_union + std::max(score_b + cand_b, part_b);
     return QSA_OK;
 }
 
@@ -360,12 +356,9 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
         cand_idx = reinterpret_cast<int32_t *>(cand_key + (size_t)p.tq * p.max_chunks * 32);
         // scoring selects the scored rows itself; a select launch remains only for rows
         // within the budget
-        uint32_t *glist_key = ws_at<uint32_t>(ws, p.off_glist);
-        int32_t *glist_idx = reinterpret_cast<int32_t *>(glist_key + (size_t)p.tq * 4 * p.topk);
         QSA_TRY(qsa::launch_score_local(p.dec, p.n_tiles, p.topk, q_idx, w, k_idx, k_blk, keys,
                                         cand_key, cand_idx, p.local_ch, p.max_chunks, sel,
-                                        glist_key, glist_idx, ws_at<uint32_t>(ws, p.off_ctl),
-                                        st));
+                                        ws_at<uint32_t>(ws, p.off_ctl), st));
         // rows whose chunks fit one merge are merged one workgroup per row
         if (p.merge_launch && !merge_in_attend)
             QSA_TRY(qsa::launch_merge_dec(p.dec, p.tq, p.topk, q_idx, w, k_blk, keys, cand_key,

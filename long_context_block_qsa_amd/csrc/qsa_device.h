@@ -65,14 +65,12 @@ struct BwdSeq {
 // query rows (decode): no table kernel and no device-side sequence lookup.
 constexpr int DEC_MAX = 64;
 
-// Control block at the start of the workspace: counters through which workgroups of
-// one kernel hand work to each other. Zero before a call; every call leaves it zero.
-//   [0, 64)    per score tile: chunks (or chunk groups) merged so far
-//   [64, 320)  per (tile, group of chunks): chunks scored so far
-//   [320, 384) per query row: the row needs the exact selection
+// Control block at the start of the workspace: counters through which the workgroups of
+// one kernel learn which of them finishes a piece of work. Zero before a call; every call
+// leaves it zero.
+//   [0, 64)    per decode score tile: chunks scored so far (tiles of rows too long to be
+//              merged from chunk candidates, whose last workgroup selects them exactly)
 constexpr int CTL_TILE = 0;
-constexpr int CTL_GROUP = 64;
-constexpr int CTL_EXACT = 320;
 constexpr int CTL_WORDS = 1024;
 struct DecRow {
     int32_t k0;     // first key row of the row's sequence
@@ -700,52 +698,10 @@ __device__ __forceinline__ int wave_excl_small(int cnt) {
     return pre;
 }
 
-// ---------------------------------------------------------------- write-through access
-// Data handed from one workgroup to another inside a kernel (possibly on another
-// XCD, whose L2 is not coherent with this one) is stored and loaded at agent scope.
-//
-// The hand-off protocol (producer: store_wt of the data, wait_vmem, __syncthreads, one
-// relaxed agent-scope atomicAdd on a counter; consumer: the atomicAdd that completes
-// the count, __syncthreads, load_wt of the data) uses relaxed atomics only, so the HIP
-// memory model alone does not order it: the order comes from the CDNA hardware, by
-// these facts of the gfx9 (CDNA3/CDNA4) ISA and of the compiler's atomic lowering:
-//   1. an agent-scope atomic store or load is issued with device-scope cache bits, so
-//      the store is written through every non-coherent cache level (the XCD's L2
-//      included) and the load is served from the device-coherent level, never from a
-//      stale line in this XCD's L2;
-//   2. on gfx9, vector stores count in vmcnt and a store leaves the count only once it
-//      is acknowledged at the scope it was issued with, so after `s_waitcnt vmcnt(0)`
-//      every store_wt of the wave is visible device-wide;
-//   3. the counter atomic is performed at the device-coherent level and is issued after
-//      the barrier that follows every wave's wait, so a consumer that sees its count
-//      complete issues its loads after all the producers' data is visible.
-// A release/acquire atomic at agent scope would give the same order by the memory
-// model, at the cost of a write-back of the whole L2 (release) and an invalidation of
-// it (acquire) per hand-off; the data stored this way is exactly what needs no such
-// write-back. Code that hands data over must keep to the protocol: only store_wt /
-// load_wt / load16_wt on the handed-over words, and the wait before the barrier.
-__device__ __forceinline__ void store_wt(uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_wt(int32_t *p, int32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_wt(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t load_wt(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_wt(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// 16 bytes as two 8-byte agent-scope loads (p 16-byte aligned)
-__device__ __forceinline__ u32x4 load16_wt(const void *p) {
-    const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
-    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
-}
+// ---------------------------------------------------------------- memory waits
+// No kernel here passes data from one workgroup to another while both run: data one
+// workgroup writes is read by a later kernel, or by the same workgroup after a barrier.
+// (Between workgroups only arrival counts pass, by device-scope atomics.)
 // Waits until every vector memory operation this wave issued has completed (stores
 // included); the "memory" clobber keeps the compiler from moving memory accesses
 // across it.
@@ -761,7 +717,7 @@ struct TopkSmem {
     int32_t scan[16];
 };
 
-// Top-k of n keys (1 <= k, n <= 2048) that the 256 threads of a workgroup hold in
+// Top-k of n keys (1 <= k, n <= 256 * PER <= 8192) that the 256 threads of a workgroup hold in
 // registers: thread t holds positions PER*t .. PER*t+PER-1 (positions >= n are
 // ignored). Order: key descending, equal keys by ascending position. Sets bit e of
 // *kept when position PER*t+e is among the k, and *first to this thread's rank among
@@ -780,7 +736,7 @@ template <int NT, int PER>
 __device__ __forceinline__ int block_topk_radix(const uint32_t (&x)[PER], int n, int k,
                                                 TopkSmem &sm, uint32_t *kept, int *first) {
     static_assert(NT == 256, "one histogram bin per thread");
-    static_assert(NT * PER <= 2048, "packed 16-bit counts");
+    static_assert(NT * PER <= 8192, "packed 16-bit counts");
     constexpr int NW = NT / WAVE;
     const int tid = threadIdx.x, l = lane_id(), w = tid / WAVE;
     bool ok[PER];

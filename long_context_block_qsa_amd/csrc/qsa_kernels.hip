@@ -482,12 +482,11 @@ score_rows_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ 
 // is exact and needs no workgroup-wide histogram: each wave takes the top KP of its 256
 // positions with a wave-level bitwise search (ballot counts, no LDS), and one wave takes
 // the top KP of those 4 x KP (tiles of several rows: one wave per row over the whole chunk). Rows whose
-// tile has at most MERGE_CHUNKS chunks are then merged after this kernel: in a forward
-// step by the decode attention's workgroups, after a selection alone by merge_dec_kernel
-// (one workgroup per row). Longer rows merge groups of chunks inside this kernel: candidates
-// are written through to the coherence point, and the workgroup that completes a group
-// (then the tile) behind an arrival counter in the control block (reset by that
-// workgroup) merges it.
+// tile has at most MERGE_CHUNKS_WIDE chunks (1,048,576 tokens with chunks of 1,024 blocks)
+// are then merged after this kernel: in a forward step by the decode attention's
+// workgroups, after a selection alone by merge_dec_kernel (one workgroup per row). Longer
+// rows are selected exactly by the workgroup that completes their tile's last chunk
+// (an arrival counter in the control block, reset by that workgroup).
 constexpr int LOC_NT = 256;
 constexpr int LOC_MAX_CH = 1024;
 constexpr int KP = 32;
@@ -596,83 +595,51 @@ __device__ __forceinline__ void select_keys_bin(KP_T kk, int64_t n, int topk, in
     }
 }
 
-// Level-one merges take at most MERGE_CHUNKS chunk lists (KP candidates each; the
-// constant is shared with the host, qsa_launch.h); rows with more chunks first merge
-// G = ceil(nch / MERGE_CHUNKS) groups of ceil(nch / G) consecutive chunks (balanced,
-// so every group holds more than MERGE_CHUNKS / 2 chunk
-// lists: at least topk real candidates), then the group lists (topk entries each) of
-// at most MAX_GROUPS groups.
-constexpr int MAX_GROUPS = 4;
 
-// Top-k of the n <= 2048 candidates (key, id) at ck[0..n) / ci[0..n) (written by other
-// workgroups of this kernel: agent-scope loads); key 0 marks padding, which is never
-// kept because every caller has at least k real candidates. Kept ids go out in
-// position order: to out_idx with plain stores, or (WT_OUT) with their keys through to
-// the coherence point, padded with key 0 / id -1 up to k. When nv > 0 the positions are
-// the KP-entry lists of chunks c0, c0+1, ... of a row with nv visible blocks: returns
-// false if a chunk holding more than KP of the row's blocks had all KP candidates kept
-// (only such a chunk can hide a better block, so only then can the result be inexact).
-template <bool WT_OUT, bool WT_IN = true>
+// Top-k of the n <= 256 * PER candidates (key, id) at ck[0..n) / ci[0..n) (PER = 8: up to
+// 2,048, 32: up to 8,192), written by an earlier kernel; key 0 marks padding, which is never
+// kept because every caller has at least k real candidates. The kept ids go to out_idx in
+// position order. The positions are the KP-entry lists of the chunks of a row with nv
+// visible blocks: returns false if a chunk holding more than KP of the row's blocks had all
+// KP candidates kept (only such a chunk can hide a better block, so only then can the
+// result be inexact).
+template <int PER>
 __device__ __forceinline__ bool merge_candidates(const uint32_t *ck, const int32_t *ci, int n,
-                                                 int k, int32_t *out_idx, uint32_t *out_key,
-                                                 int64_t nv, int ch, int c0, int *viol,
-                                                 TopkSmem *tsm) {
+                                                 int k, int32_t *out_idx, int64_t nv, int ch,
+                                                 int *viol, TopkSmem *tsm) {
+    static_assert(PER % 4 == 0 && PER <= KP && KP % PER == 0, "whole lists per thread group");
+    constexpr int TPL = KP / PER;   // threads per chunk list
     const int tid = threadIdx.x;
-    uint32_t x[8];
-    int32_t id[8];
-    u32x4 kq[2], iq[2];
-    const bool have = 8 * tid < n;
+    uint32_t x[PER];
+    int32_t id[PER];
+    const bool have = PER * tid < n;
 #pragma unroll
-    for (int v4 = 0; v4 < 2; ++v4) {
-        if (WT_IN) {   // written by other workgroups of this kernel
-            kq[v4] = have ? load16_wt(ck + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
-            iq[v4] = have ? load16_wt(ci + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
-        } else {       // written by an earlier kernel
-            kq[v4] = have ? load16(ck + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
-            iq[v4] = have ? load16(ci + 8 * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-#pragma unroll
-    for (int v4 = 0; v4 < 2; ++v4) {
+    for (int v4 = 0; v4 < PER / 4; ++v4) {
+        const u32x4 kq = have ? load16(ck + PER * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 iq = have ? load16(ci + PER * tid + 4 * v4) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[4 * v4 + e] = kq[v4][e];
-            id[4 * v4 + e] = (int32_t)iq[v4][e];
+            x[4 * v4 + e] = kq[e];
+            id[4 * v4 + e] = (int32_t)iq[e];
         }
     }
     if (tid == 0) *viol = 0;
     uint32_t kept;
     int first;
-    const int tot = block_topk_radix<SEL_NT, 8>(x, n, k, *tsm, &kept, &first);
+    (void)block_topk_radix<SEL_NT, PER>(x, n, k, *tsm, &kept, &first);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < PER; ++e) {
         if (kept & (1u << e)) {
-            if (first < k) {
-                if (WT_OUT) {
-                    store_wt(out_key + first, x[e]);
-                    store_wt(out_idx + first, id[e]);
-                } else {
-                    out_idx[first] = id[e];
-                }
-            }
+            if (first < k) out_idx[first] = id[e];
             ++first;
         }
     }
-    if (WT_OUT) {
-        for (int i = tot + tid; i < k; i += SEL_NT) {
-            store_wt(out_key + i, 0u);
-            store_wt(out_idx + i, -1);
-        }
-    }
-    if (nv > 0) {
-        int kc = __popc(kept);
-        kc += __shfl_xor(kc, 1);
-        kc += __shfl_xor(kc, 2);
-        static_assert(KP == 32, "4 threads hold one chunk list");
-        const int c = c0 + tid / 4;
-        const int64_t nc = have ? min<int64_t>(ch, nv - (int64_t)c * ch) : 0;
-        if (nc > KP && kc >= KP) *viol = 1;
-    }
+    int kc = __popc(kept);
+#pragma unroll
+    for (int d = 1; d < TPL; d <<= 1) kc += __shfl_xor(kc, d);
+    const int c = tid / TPL;
+    const int64_t nc = have ? min<int64_t>(ch, nv - (int64_t)c * ch) : 0;
+    if (nc > KP && kc >= KP) *viol = 1;
     __syncthreads();
     return !*viol;
 }
@@ -711,9 +678,7 @@ struct LocalArgs {
     int32_t *cand_idx;
     int ch, max_chunks;
     int32_t *sel;
-    uint32_t *glist_key;     // [row][MAX_GROUPS][topk] group merge results
-    int32_t *glist_idx;
-    uint32_t *ctl;           // arrival counters and flags (zero between calls)
+    uint32_t *ctl;           // arrival counters (zero between calls)
 };
 
 // Scores blocks [lo, hi) of a tile; store(row, blk, key) is called for each block
@@ -869,14 +834,14 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 if (mask & (1u << i)) {
-                    store_wt(ck + pos, x[i]);
-                    store_wt(ci + pos, (int32_t)(lo + (int64_t)qw * span + u0 + i));
+                    ck[pos] = x[i];
+                    ci[pos] = (int32_t)(lo + (int64_t)qw * span + u0 + i);
                     ++pos;
                 }
             }
             if (l >= tot && l < KP) {
-                store_wt(ck + l, 0u);
-                store_wt(ci + l, -1);
+                ck[l] = 0u;
+                ci[l] = -1;
             }
         }
     }
@@ -931,101 +896,38 @@ __device__ __forceinline__ bool score_chunk(const LocalArgs &a, const DecodeTabl
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 if (m2 & (1u << e)) {
-                    store_wt(ck + o, y[e]);
-                    store_wt(ci + o, (int32_t)(lo + py[e]));
+                    ck[o] = y[e];
+                    ci[o] = (int32_t)(lo + py[e]);
                     ++o;
                 }
             }
             if (l >= tot2 && l < KP) {
-                store_wt(ck + l, 0u);
-                store_wt(ci + l, -1);
+                ck[l] = 0u;
+                ci[l] = -1;
             }
         }
         if (rr + 1 < nrows) lds_barrier();   // wave lists are reused by the next row
     }
 
-    // (the order of this hand-off rests on the hardware facts listed with store_wt in
-    // qsa_device.h: candidates stored write-through, waited for, then counted)
-    // hand over: the workgroup that completes the tile's last chunk merges the rows'
-    // candidates; rows with more than MERGE_CHUNKS chunks merge groups of chunks first
-    // (the last chunk of each group), then the group lists (the tile's last group)
-    wait_vmem();
-    __syncthreads();
+    // rows of tiles with at most MERGE_CHUNKS_WIDE chunks are merged from these candidates
+    // by a later kernel (the decode attention, or merge_dec_kernel after qsa_select): this
+    // workgroup is done, with no wait for its stores
     const int tid = threadIdx.x;
     const int nch = (int)((nv_max + a.ch - 1) / a.ch);
-    const int ngroups = (nch + MERGE_CHUNKS - 1) / MERGE_CHUNKS;
-    const int gsize = (nch + ngroups - 1) / ngroups;   // chunks per group (balanced)
-    // groups of chunks are merged separately when there are 2 .. MAX_GROUPS of them
-    const bool grouped = ngroups > 1 && ngroups <= MAX_GROUPS;
-    // rows whose chunks fit one merge are merged by merge_dec_kernel, one workgroup per
-    // row: the rows (of all tiles) merge at the same time, and this kernel ends with its
-    // last chunk instead of with a merge behind an arrival counter
-    if (ngroups == 1) return false;
-    if (grouped) {
-        const int grp = chunk / gsize;
-        const int n_in = min(gsize, nch - grp * gsize);
-        if (tid == 0) {
-            uint32_t *cnt = &a.ctl[CTL_GROUP + tile * MAX_GROUPS + grp];
-            const uint32_t old = atomicAdd(cnt, 1u);
-            sm.s_last = old + 1 == (uint32_t)n_in;
-            if (sm.s_last) store_wt(cnt, 0u);
-        }
-        __syncthreads();
-        if (!sm.s_last) return false;
-        for (int rr = 0; rr < nrows; ++rr) {
-            const int64_t nv = nvis_of(t0 + rr), row = row0 + rr;
-            if (!cand_eligible(nv, a.topk, a.ch)) continue;   // uniform
-            const int64_t cbase = (row * a.max_chunks + grp * gsize) * KP;
-            const int64_t gbase = (row * MAX_GROUPS + grp) * a.topk;
-            const bool ok = merge_candidates<true>(
-                a.cand_key + cbase, a.cand_idx + cbase, n_in * KP, a.topk, a.glist_idx + gbase,
-                a.glist_key + gbase, nv, a.ch, grp * gsize, &sm.viol, &sm.tsm);
-            if (!ok && tid == 0) store_wt(&a.ctl[CTL_EXACT + row], 1u);
-        }
-        wait_vmem();
-        __syncthreads();
-    }
-    // the tile counter counts merged groups, or chunks when no grouping is used
+    if (nch <= MERGE_CHUNKS_WIDE) return false;
+    // longer rows are selected exactly by the workgroup that completes the tile's last
+    // chunk (an arrival counter); it scores the rows again itself, so nothing but the count
+    // passes between workgroups
     if (tid == 0) {
         const uint32_t old = atomicAdd(&a.ctl[CTL_TILE + tile], 1u);
-        sm.s_last = old + 1 == (uint32_t)(grouped ? ngroups : nch);
-        if (sm.s_last) store_wt(&a.ctl[CTL_TILE + tile], 0u);
+        sm.s_last = old + 1 == (uint32_t)nch;
+        if (sm.s_last) atomicExch(&a.ctl[CTL_TILE + tile], 0u);   // zero for the next call
     }
     __syncthreads();
     if (!sm.s_last) return false;
-
-    // this workgroup selects the tile's rows
-    int n_exact = 0;
-    for (int rr = 0; rr < nrows; ++rr) {
-        const int64_t nv = nvis_of(t0 + rr), row = row0 + rr;
-        bool done = false;
-        if (cand_eligible(nv, a.topk, a.ch) && ngroups <= MAX_GROUPS) {
-            if (grouped) {
-                if (tid == 0) {
-                    sm.exact[rr] = load_wt(&a.ctl[CTL_EXACT + row]) != 0u;
-                    store_wt(&a.ctl[CTL_EXACT + row], 0u);
-                }
-                __syncthreads();
-                if (!sm.exact[rr]) {
-                    const int64_t gbase = row * MAX_GROUPS * a.topk;
-                    done = merge_candidates<false>(a.glist_key + gbase, a.glist_idx + gbase,
-                                                   ngroups * a.topk, a.topk, a.sel + row * a.topk,
-                                                   nullptr, 0, a.ch, 0, &sm.viol, &sm.tsm);
-                }
-            } else {
-                const int64_t cbase = row * a.max_chunks * KP;
-                const int nch_row = (int)((nv + a.ch - 1) / a.ch);
-                done = merge_candidates<false>(a.cand_key + cbase, a.cand_idx + cbase,
-                                               nch_row * KP, a.topk, a.sel + row * a.topk,
-                                               nullptr, nv, a.ch, 0, &sm.viol, &sm.tsm);
-            }
-        }
-        __syncthreads();
-        if (tid == 0) sm.exact[rr] = !done;
-        n_exact += !done;   // uniform
-    }
+    for (int rr = tid; rr < nrows; rr += LOC_NT) sm.exact[rr] = 1;
     __syncthreads();
-    if (n_exact > 0) select_tile_exact(a, d, tile, sm.exact, sm.hist, sm.scan_sh, sm.found);
+    select_tile_exact(a, d, tile, sm.exact, sm.hist, sm.scan_sh, sm.found);
     return true;
 }
 
@@ -1048,13 +950,23 @@ __device__ __forceinline__ void select_row_exact(const LocalArgs &a, const Decod
 }
 
 // The rows that are merged from chunk candidates outside the scoring kernel: those whose
-// tile has at most MERGE_CHUNKS chunks.
+// tile has at most MERGE_CHUNKS_WIDE chunks.
 __device__ __forceinline__ bool merged_after_scoring(const DecodeTables &d, const DecRow &r,
                                                      int ch) {
     if (r.tile < 0) return false;
     const DecTile tl = d.tile[r.tile];
     const int64_t nv_max = nvis_of((int64_t)d.row[tl.row0].t + tl.nrows - 1);
-    return (nv_max + ch - 1) / ch <= MERGE_CHUNKS;
+    return (nv_max + ch - 1) / ch <= MERGE_CHUNKS_WIDE;
+}
+
+// Top-k of a row merged after scoring from its nch chunk lists: 8 candidates per thread up
+// to 64 lists, 32 up to 256.
+__device__ __forceinline__ bool merge_row_lists(const uint32_t *ck, const int32_t *ci, int nch,
+                                                int k, int32_t *out_idx, int64_t nv, int ch,
+                                                int *viol, TopkSmem *tsm) {
+    if (nch <= MERGE_CHUNKS)   // uniform
+        return merge_candidates<8>(ck, ci, nch * KP, k, out_idx, nv, ch, viol, tsm);
+    return merge_candidates<32>(ck, ci, nch * KP, k, out_idx, nv, ch, viol, tsm);
 }
 
 // One workgroup per decode row: rows whose tile's chunks fit one merge get their top-k
@@ -1064,15 +976,14 @@ __global__ void __launch_bounds__(LOC_NT) merge_dec_kernel(LocalArgs a, DecodeTa
     __shared__ ScoreSmem sm;
     const int64_t row = blockIdx.x;
     const DecRow r = d.row[row];
-    if (!merged_after_scoring(d, r, a.ch)) return;   // groups of chunks: scoring kernel
+    if (!merged_after_scoring(d, r, a.ch)) return;   // selected by the scoring kernel
     const int64_t nv = nvis_of(r.t);
     bool done = false;
     if (cand_eligible(nv, a.topk, a.ch)) {
         const int64_t cbase = row * a.max_chunks * KP;
         const int nch_row = (int)((nv + a.ch - 1) / a.ch);
-        done = merge_candidates<false, false>(a.cand_key + cbase, a.cand_idx + cbase,
-                                              nch_row * KP, a.topk, a.sel + row * a.topk,
-                                              nullptr, nv, a.ch, 0, &sm.viol, &sm.tsm);
+        done = merge_row_lists(a.cand_key + cbase, a.cand_idx + cbase, nch_row, a.topk,
+                                      a.sel + row * a.topk, nv, a.ch, &sm.viol, &sm.tsm);
     }
     if (!done)   // uniform
         select_row_exact(a, d, row, a.sel + row * a.topk, sm.hist, sm.scan_sh, sm.found);
@@ -1652,10 +1563,9 @@ attend_dec_kernel(AttnArgs a, DecodeTables d) {
         if (cand_eligible(nv, a.topk, a.loc.ch)) {
             const int64_t cbase = row * a.loc.max_chunks * KP;
             const int nch_row = (int)((nv + a.loc.ch - 1) / a.loc.ch);
-            done = merge_candidates<false, false>(a.loc.cand_key + cbase,
-                                                  a.loc.cand_idx + cbase, nch_row * KP, a.topk,
-                                                  ms.ids, nullptr, nv, a.loc.ch, 0, &ms.viol,
-                                                  &ms.tsm);
+            done = merge_row_lists(a.loc.cand_key + cbase, a.loc.cand_idx + cbase,
+                                          nch_row, a.topk, ms.ids, nv, a.loc.ch, &ms.viol,
+                                          &ms.tsm);
         }
         if (!done)   // uniform
             select_row_exact(a.loc, d, row, ms.ids, ms.hist, ms.scan_sh, ms.found);
@@ -1877,13 +1787,12 @@ hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
                               const uint16_t *q_idx, const float *w, const uint16_t *k_idx,
                               uint16_t *k_blk, uint32_t *keys, uint32_t *cand_key,
                               int32_t *cand_idx, int ch, int max_chunks, int32_t *sel,
-                              uint32_t *glist_key, int32_t *glist_idx, uint32_t *ctl,
-                              hipStream_t st) {
+                              uint32_t *ctl, hipStream_t st) {
     if (n_tiles <= 0) return hipSuccess;
     LocalArgs a;
     a.topk = topk; a.q_idx = q_idx; a.w = w; a.k_idx = k_idx; a.k_blk = k_blk; a.keys = keys;
     a.cand_key = cand_key; a.cand_idx = cand_idx; a.ch = ch; a.max_chunks = max_chunks;
-    a.sel = sel; a.glist_key = glist_key; a.glist_idx = glist_idx; a.ctl = ctl;
+    a.sel = sel; a.ctl = ctl;
     trace_before(2, st);
     hipLaunchKernelGGL(score_local_kernel, dim3((unsigned)max_chunks, (unsigned)n_tiles),
                        dim3(LOC_NT), 0, st, a, d);

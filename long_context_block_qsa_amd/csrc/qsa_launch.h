@@ -15,8 +15,10 @@ struct Fp8Kv {
     const float *k_scale, *v_scale;
 };
 
-// Chunk lists one decode merge takes (longer rows merge groups of chunks first).
+// Chunk lists one decode merge takes with 8 candidates per thread; rows of up to
+// MERGE_CHUNKS_WIDE chunks are merged after scoring with 32 per thread.
 constexpr int MERGE_CHUNKS = 64;
+constexpr int MERGE_CHUNKS_WIDE = 256;
 
 // Prefill score + select launches whose rows see more blocks than this take the variant
 // for long rows (score tiles grouped 4 at a time, selections that list the first radix
@@ -52,8 +54,7 @@ hipError_t launch_score_local(const DecodeTables &d, int64_t n_tiles, int topk,
                               const uint16_t *q_idx, const float *w, const uint16_t *k_idx,
                               uint16_t *k_blk, uint32_t *keys, uint32_t *cand_key,
                               int32_t *cand_idx, int ch, int max_chunks, int32_t *sel,
-                              uint32_t *glist_key, int32_t *glist_idx, uint32_t *ctl,
-                              hipStream_t st);
+                              uint32_t *ctl, hipStream_t st);
 // Selection of the decode rows whose tile's chunks fit one merge (the scoring kernel
 // leaves them to this launch: one workgroup per row).
 hipError_t launch_merge_dec(const DecodeTables &d, int64_t n_rows, int topk,

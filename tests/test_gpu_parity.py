@@ -263,10 +263,10 @@ def test_indexer_scores_bit_exact():
 
 # ----------------------------------------------------------------- long contexts
 
-def test_decode_1m_context_grouped_merge():
-    """One decode row at 1,048,576 tokens (262,144 blocks, 256 chunks): candidates are
-    merged in 4 groups of 64 chunks, then across groups; bit-exact selection, needles
-    kept, outputs within tolerance."""
+def test_decode_1m_context():
+    """One decode row at 1,048,576 tokens (262,144 blocks, 256 chunks): the attention
+    workgroups merge its 8,192 chunk candidates (32 per thread); bit-exact selection,
+    needles kept, outputs within tolerance."""
     _banner("decode 1M context")
     p = gen.make_problem([1 << 20], q_lens=[1], seed=17, needles=32)
     sel, _ = _check_rows("decode-1M", DeviceProblem(p, 512), None, 512)
@@ -275,8 +275,8 @@ def test_decode_1m_context_grouped_merge():
 
 def test_decode_4x1m_full():
     """The 1M decode line's shape: 4 sequences of 1,048,576 tokens, one query each (4 score
-    tiles, each merging 4 groups of 64 chunks inside the scoring kernel), all rows; the
-    selection alone equals the forward's."""
+    tiles of 256 chunks, each row merged from 8,192 candidates), all rows; the selection
+    alone (merged by merge_dec_kernel) equals the forward's."""
     _banner("decode 4x1M")
     p = gen.make_problem([1 << 20] * 4, q_lens=[1] * 4, seed=23, needles=16)
     dp = DeviceProblem(p)
@@ -286,37 +286,53 @@ def test_decode_4x1m_full():
     assert np.array_equal(dp.select(), sel)
 
 
-def test_multi_query_long_rows_grouped():
-    """Three query tokens of one 300,001-token sequence (one tile, 74 chunks, 2 groups)
-    plus a short sequence."""
-    _banner("multi-query grouped")
+def test_multi_query_long_rows():
+    """Three query tokens of one 300,001-token sequence (one tile of 74 chunks: each row's
+    2,368 candidates take the wide merge) plus a short sequence."""
+    _banner("multi-query long rows")
     p = gen.make_problem([300001, 7000], q_lens=[3, 2], seed=18)
     dp = DeviceProblem(p, 512)
-    sel, _ = _check_rows("mq-grouped", dp, None, 512)
+    sel, _ = _check_rows("mq-long", dp, None, 512)
     assert np.array_equal(dp.select(), sel)
 
 
 @pytest.mark.parametrize("L", [266001, 526001])
-def test_decode_grouped_uneven_chunk_counts(L):
-    """65 and 129 chunks of 1024 blocks: the chunk groups are balanced (33 + 32, 3 x 43)
-    so every group merge sees at least topk real candidates."""
-    _banner(f"decode grouped, {L} tokens")
+def test_decode_chunk_counts_past_64(L):
+    """65 and 129 chunks of 1,024 blocks (the last one partial): the first chunk counts
+    past the 2,048-candidate merge, taken by the wide merge."""
+    _banner(f"decode, {L} tokens")
     p = gen.make_problem([L], q_lens=[1], seed=20 + L % 7)
-    _check_rows(f"grouped-{L}", DeviceProblem(p, 512), None, 512)
+    _check_rows(f"chunks-{L}", DeviceProblem(p, 512), None, 512)
 
 
-def test_grouped_merge_exact_fallback():
-    """A grouped row (100,000 blocks) whose best blocks form one run of 300 blocks: the
-    group merge finds a chunk with every candidate kept and the row is selected exactly."""
-    _banner("grouped exact fallback")
+def test_wide_merge_exact_fallback():
+    """A row of 100,000 blocks (98 chunks, the wide merge) whose best blocks form one run of
+    300 blocks: the merge finds a chunk with every candidate kept, and the row is selected
+    exactly."""
+    _banner("wide merge exact fallback")
     p = gen.make_problem([400000], q_lens=[1], seed=19)
     u = (p.w[0][:, None].astype(np.float64) *
          gen.bf16_to_f32(p.q_idx[0]).astype(np.float64)).sum(axis=0)
     val = np.where(u >= 0, 0x4040, 0xC040).astype(np.uint16)
     p.k_idx[4 * 70000: 4 * 70300] = val[None, :]
     dp = DeviceProblem(p, 512)
-    sel, _ = _check_rows("grouped-fallback", dp, None, 512)
+    sel, _ = _check_rows("wide-fallback", dp, None, 512)
     assert set(range(70000, 70300)) <= set(sel[0].tolist())
+    assert np.array_equal(dp.select(), sel)
+
+
+def test_decode_rows_past_1m_exact():
+    """Two query tokens of a 1,100,001-token sequence (275,000 blocks, 269 chunks: more than
+    one merge of chunk candidates takes) plus a short sequence: the workgroup that completes
+    the long tile's last chunk (arrival counter) scores its rows again and selects them
+    exactly; called twice, so the counter must be back at zero after the first call."""
+    _banner("decode rows past 1M tokens")
+    p = gen.make_problem([1100001, 9000], q_lens=[2, 1], seed=31, needles=8)
+    dp = DeviceProblem(p, 512)
+    sel, _ = _check_rows("past-1M", dp, None, 512)
+    assert set(p.needles[0]) <= set(sel[1].tolist())
+    _, sel2, _, _ = dp.forward()
+    assert np.array_equal(sel2, sel)
     assert np.array_equal(dp.select(), sel)
 
 
