@@ -26,12 +26,13 @@ def _noalloc(dp):
 
 
 @pytest.mark.parametrize("first,second", [
-    # a decode batch (score kernel hand-offs through the control block), then a smaller
+    # a decode batch (chunk candidates merged by the attention), then a smaller
     # prefill-shaped call
     (dict(lens=[60000, 30000, 9000], q_lens=[1, 1, 1], topk=512, seed=501),
      dict(lens=[3000, 700], q_lens=[40, 700], topk=64, seed=502)),
-    # 1M-token decode rows (grouped merges behind counters), then a short decode
-    (dict(lens=[1 << 20], q_lens=[1], topk=512, seed=503),
+    # a decode row past 1,048,576 tokens (selected exactly behind the tile's arrival
+    # counter in the control block), then a short decode
+    (dict(lens=[1100001], q_lens=[1], topk=512, seed=503),
      dict(lens=[5000], q_lens=[2], topk=128, seed=504)),
 ])
 def test_noalloc_matches_forward(first, second):
