@@ -276,7 +276,7 @@ __device__ __forceinline__ T block_excl_scan(T v, T *scratch, T *total) {
 // ---------------------------------------------------------------- selection
 
 // Digit plans of the radix select over 32-bit order keys (most significant first).
-// WIDE: 11 + 11 + 10 bits (2048-bin histograms) for long rows; NARROW: 4 x 8 bits.
+// WIDE: 11 + 11 + 10 bits (2048-bin histograms).
 struct DigitPlan {
     int n;
     int shift[4];
@@ -286,7 +286,6 @@ constexpr DigitPlan kWide = {3, {21, 10, 0, 0}, {11, 11, 10, 0}};
 constexpr DigitPlan kWideFirst = {1, {21, 0, 0, 0}, {11, 0, 0, 0}};   // first digit only
 constexpr DigitPlan kWideRest = {2, {10, 0, 0, 0}, {11, 10, 0, 0}};   // after it
 constexpr int kHistBins = 2048;
-constexpr DigitPlan kNarrow = {4, {24, 16, 8, 0}, {8, 8, 8, 8}};
 
 // Words of the `found` LDS array radix_kth needs with NT threads.
 template <int NT> constexpr int radix_found_words() { return 2 + 2 * (NT / 64); }
@@ -576,29 +575,6 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
-}
-
-// Lanes below this one in a ballot mask.
-
-// Wave-wide max / min of uint32 with DPP row shifts and row broadcasts (the result is
-// complete in lane 63 and read from there).
-__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
-}
-__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xf, 0xf, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xf, 0xf, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xf, 0xf, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xf, 0xf, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xa, 0xf, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xc, 0xf, false));
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
 }
 
 // Wave-wide OR / AND of uint32 (DPP row shifts and broadcasts, result from lane 63).

@@ -488,7 +488,6 @@ score_rows_kernel(const int32_t *__restrict__ cu_q, const int32_t *__restrict__ 
 // rows are selected exactly by the workgroup that completes their tile's last chunk
 // (an arrival counter in the control block, reset by that workgroup).
 constexpr int LOC_NT = 256;
-constexpr int LOC_MAX_CH = 1024;
 constexpr int KP = 32;
 constexpr int SEL_NT = 256;
 
