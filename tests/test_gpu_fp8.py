@@ -99,6 +99,15 @@ def test_fp8_decode_16x262144():
         assert set(needles) <= set(sel[b].tolist())
 
 
+def test_fp8_decode_long_rows():
+    """FP8 decode rows past 64 chunks (a 300,001-token row with 2 query tokens: 74 chunks,
+    merged from 2,368 candidates by the attention) and at 1,048,576 tokens (256 chunks)."""
+    _banner("fp8: long decode rows")
+    p = gen.make_problem([300001, 1 << 20], q_lens=[2, 1], seed=430, needles=8)
+    sel, _ = _check("fp8-long-decode", Fp8Problem(p))
+    assert set(p.needles[1]) <= set(sel[2].tolist())
+
+
 def test_fp8_prefill_ragged_64k():
     """Selections of all 113,729 rows bit-exact; attention on every 128th row plus each
     sequence's ends and its dense/sparse boundary."""
