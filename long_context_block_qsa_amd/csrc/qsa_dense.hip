@@ -308,7 +308,7 @@ hipError_t launch_attend_dense(const SeqInfo *tab, int batch, int topk, float sc
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.n_tiles = n_tiles;
     trace_before(15, st);
-    // fewer dense tiles than the machine has CUs per KV head: split their column tiles
+    // fewer (dense tile, KV head) workgroups than CUs: each tile's column tiles go to two
     if (n_tiles * HKV < 256)
         hipLaunchKernelGGL(attend_dense_kernel<2>, dim3((unsigned)n_tiles, HKV * 2),
                            dim3(dn_threads<2>()), 0, st, a);
