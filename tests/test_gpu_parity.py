@@ -401,6 +401,37 @@ def test_float_indexer_tie_tolerant():
     assert errs(lse, lse_r)[0] <= LSE_ABS
 
 
+def _random_case(i):
+    """Shape i of a fixed, seeded family: 1-4 sequences of 0-20,000 tokens, each a prefill,
+    a decode of 1-4 query tokens or without queries (at least one query in all), and a
+    budget of 1-512 blocks."""
+    rng = np.random.default_rng(7000 + i)
+    nb = int(rng.integers(1, 5))
+    lens, q_lens = [], []
+    for _ in range(nb):
+        L = int(rng.choice([int(rng.integers(0, 40)), int(rng.integers(40, 3000)),
+                            int(rng.integers(3000, 20001))]))
+        kind = rng.integers(0, 3)
+        q = L if kind == 0 else (min(L, int(rng.integers(1, 5))) if kind == 1 else 0)
+        lens.append(L)
+        q_lens.append(q)
+    if sum(q_lens) == 0:   # at least one query: a decode of the longest sequence
+        j = int(np.argmax(lens))
+        q_lens[j] = min(lens[j], 2)
+    topk = int(rng.choice([1, 3, 16, 64, 100, 512]))
+    return lens, q_lens, topk
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes(i):
+    """24 seeded shapes mixing prefills and decodes, ragged and empty sequences, tails of
+    0-3 tokens and budgets of 1-512 blocks: every row against the oracle."""
+    lens, q_lens, topk = _random_case(i)
+    _banner(f"random shape {i}: lens={lens} q_lens={q_lens} topk={topk}")
+    p = gen.make_problem(lens, q_lens=q_lens, seed=7100 + i)
+    _check_rows(f"random{i}", DeviceProblem(p, topk), None, topk)
+
+
 def test_deterministic_bitwise():
     _banner("determinism")
     p = gen.make_problem([9000, 4000], q_lens=[1, 1], seed=9)
