@@ -344,9 +344,17 @@ T *ws_at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *
 
 // merge_in_attend: the decode rows merged after scoring are merged by the attention
 // launch that follows (forward), not by a merge launch here.
+// The forward attends the rows in the dense regime with the dense-tile kernel (bf16 K/V,
+// prefill-shaped calls without attention splits); with no scored row at all, that kernel
+// also writes the selections and no select launch is needed.
+bool dense_tile_path(const Plan &p, bool fp8) {
+    return !fp8 && !p.use_dec && p.nsplit == 1 && p.n_dense_tiles > 0;
+}
+bool sel_by_dense_tiles(const Plan &p, bool fp8) { return dense_tile_path(p, fp8) && p.n_tiles == 0; }
+
 qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, const float *w,
                       const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel, void *ws,
-                      hipStream_t st, bool merge_in_attend = false) {
+                      hipStream_t st, bool merge_in_attend = false, bool sel_by_dense = false) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
     uint32_t *keys = ws_at<uint32_t>(ws, p.off_union);
     uint32_t *cand_key = nullptr;
@@ -374,6 +382,7 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
                                    0, sel, 0, p.tq, 0, st));
         return QSA_OK;
     }
+    if (sel_by_dense) return QSA_OK;
     // prefill: launch i scores pass i into buffer i % 2 and selects the rows of pass
     // i - 1 from buffer (i - 1) % 2
     uint32_t *buf[2] = {keys, keys + align_up((size_t)p.pass_slots * sizeof(uint32_t)) / 4};
@@ -393,18 +402,18 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
 }
 
 // dense_tiles: the selection is the library's own (a forward step), so rows with at
-// most topk visible blocks keep them all and are attended by the dense-regime kernel.
+// most topk visible blocks keep them all and are attended by the dense-regime kernel;
+// sel_out (not null) is where that kernel writes their selections.
 qsa_status run_attend(const Plan &p, const qsa_bf16 *q, const qsa_bf16 *k, const qsa_bf16 *v,
                       const qsa::Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
                       void *ws, hipStream_t st, const qsa::AttnMerge *merge = nullptr,
-                      bool dense_tiles = false) {
+                      bool dense_tiles = false, int32_t *sel_out = nullptr) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
     float *part = ws_at<float>(ws, p.off_part);
-    const bool dense = dense_tiles && !fp8 && !p.use_dec && p.nsplit == 1 &&
-                       p.n_dense_tiles > 0;
+    const bool dense = dense_tiles && dense_tile_path(p, fp8 != nullptr);
     if (dense)
         QSA_TRY(qsa::launch_attend_dense(tab, p.batch, p.topk, p.scale, q, k, v, out, lse,
-                                         p.n_dense_tiles, st));
+                                         sel_out, p.n_dense_tiles, st));
     if (!dense || p.n_dense < p.tq)
         QSA_TRY(qsa::launch_attend(tab, p.use_dec ? &p.dec : nullptr, p.batch, p.topk, p.scale,
                                    q, k, v, fp8, sel, out, lse, part, p.nsplit, p.tq, merge,
@@ -475,8 +484,9 @@ qsa_status forward_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_
     // decode rows merged after scoring: the attention workgroups of a row merge its
     // candidates themselves (no merge launch, no selection round trip through memory)
     const bool merge_in_attend = p.use_dec && p.local_ch > 0 && p.merge_launch;
+    const bool sel_by_dense = sel_by_dense_tiles(p, fp8 != nullptr);
     if ((st = run_select(p, seqs, q_idx, w, fused ? k_idx : nullptr, k_blk, sel_use, ws, hs,
-                         merge_in_attend)) != QSA_OK)
+                         merge_in_attend, sel_by_dense)) != QSA_OK)
         return st;
     qsa::AttnMerge m = {};
     if (merge_in_attend) {
@@ -488,7 +498,7 @@ qsa_status forward_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_
         m.sel = sel_use;
     }
     return run_attend(p, q, k, v, fp8, sel_use, out, lse, ws, hs, merge_in_attend ? &m : nullptr,
-                      true);
+                      true, sel_by_dense ? sel_use : nullptr);
 }
 
 // Attention backward: per-sequence table, D, nsel, list offsets, block totals, count

@@ -32,19 +32,24 @@ namespace qsa {
 // The 12 column tiles of a (dense tile, KV head) go to CS workgroups of 12 / CS each.
 // CS = 1 (8 waves): waves 0-3 take two each (tiles 2w, 2w + 1), waves 4-7 one each (tile
 // 4 + w) and also stage the K/V tiles, so each SIMD (waves w and w + 4) carries three column
-// tiles of MFMA work per key tile. CS = 2 (4 waves, every thread staging, two key tiles in
-// flight): waves 0-1 take two tiles, waves 2-3 one, so no SIMD carries more than two; twice
-// the workgroups share each key tile (through the L2), for launches with too few dense tiles
-// to fill the machine.
+// tiles of MFMA work per key tile. CS = 2 (every thread staging, two key tiles in flight):
+// 6 column tiles per workgroup, and twice the workgroups share each key tile (through the
+// L2), for launches with too few dense tiles to fill the machine. Their 8 waves are two
+// halves of 4 that take alternate key tiles (half h: tiles h, h + 2, h + 4, ...), so a
+// workgroup's chain of key tiles is half as long; at the end the second half hands its
+// running maxima, sums and accumulators to the first through LDS, which merges the two
+// softmax states and writes the rows. In half 0 waves 0-1 take two column tiles and waves
+// 2-3 one; half 1 the other way round, so every SIMD (waves w and w + 4) carries three.
 constexpr int DN_KEYS = 32;
 constexpr int DN_PITCH = 2 * HD + 16;     // LDS row pitch (bytes) of the K and V tiles
 constexpr int DN_TILE_BYTES = DN_KEYS * DN_PITCH;
 constexpr int DN_STAGE_NT = DN_KEYS * 8;  // threads that stage a tile (32 bytes of K and V each)
-template <int CS> constexpr int dn_threads() { return CS == 1 ? 8 * WAVE : 4 * WAVE; }
-template <int CS> constexpr int dn_stage_t0() { return dn_threads<CS>() - DN_STAGE_NT; }
+constexpr int DN_XCH = 34;                // floats per lane and column tile handed between halves
+constexpr int DN_NT = 8 * WAVE;          // threads of a workgroup (both variants)
 static_assert(DN_ROWS * GQ == 16 * (4 * 2 + 4 * 1), "12 column tiles over the 8 waves");
-static_assert(DN_ROWS * GQ / 2 == 16 * (2 * 2 + 2 * 1), "6 column tiles over the 4 waves");
-static_assert(dn_stage_t0<1>() == 4 * WAVE && dn_stage_t0<2>() == 0, "the staging threads");
+static_assert(DN_ROWS * GQ / 2 == 16 * (2 * 2 + 2 * 1), "6 column tiles over a half's 4 waves");
+static_assert(4 * WAVE == DN_STAGE_NT, "4 waves stage a tile");
+static_assert(6 * DN_XCH * WAVE * 4 <= 2 * 4 * DN_TILE_BYTES, "the hand-over fits the tiles");
 
 struct DenseArgs {
     const SeqInfo *tab;
@@ -52,6 +57,7 @@ struct DenseArgs {
     float scale_log2;
     const uint16_t *q, *k, *v;
     float *out, *lse;
+    int32_t *sel;   // not null: the tiles also write their rows' selections
     int64_t n_tiles;
 };
 
@@ -66,10 +72,16 @@ struct DenseTile {
 // 16 ct0 .. 16 (ct0 + NQ) - 1), the key loop with the workgroup's barriers (every wave runs
 // the same number of iterations), and, for the staging waves, the K/V staging.
 // AHEAD: key tiles whose loads the staging threads keep in flight (1 or 2).
-template <int NQ, bool STAGE, int STAGE_T0, int AHEAD>
+// KS: halves of the workgroup taking alternate key tiles (1 or 2); `half` is this wave's,
+// xch the LDS of the hand-over (it reuses the tile buffers) and c0 the workgroup's first
+// column tile.
+template <int NQ, bool STAGE, int STAGE_T0, int AHEAD, int KS>
 __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &dt, int g,
-                                           int ct0, uint8_t *ks0, uint8_t *vs0) {
+                                           int ct0, uint8_t *ks0, uint8_t *vs0, int half,
+                                           float *xch, int c0) {
     static_assert(AHEAD == 1 || AHEAD == 2, "one or two tiles ahead");
+    static_assert(KS == 1 || KS == 2, "one or two halves");
+    constexpr int STRIDE = KS * DN_KEYS;   // keys from one of this half's tiles to the next
     const int tid = threadIdx.x, l = lane_id(), gr = l >> 4, col = l & 15;
     const int64_t row0 = dt.row0, t0 = dt.t0, t_last = dt.t_last;
     const int nrows = dt.nrows;
@@ -97,9 +109,11 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
     for (int nt = 0; nt < NQ; ++nt)
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the reference maxima start at a finite floor: a vector whose keys in some tile are
+    // all masked (a row before the first key of its half's tiles) then gets p = 0, not NaN
     float m_run[NQ], l_run[NQ];
 #pragma unroll
-    for (int nt = 0; nt < NQ; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
+    for (int nt = 0; nt < NQ; ++nt) { m_run[nt] = -1e30f; l_run[nt] = 0.f; }
 
     // staging: thread STAGE_T0 + i -> (key i / 8, 32-byte piece i % 8) of the K and V rows
     const int st = tid - STAGE_T0;
@@ -122,25 +136,27 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
         *reinterpret_cast<u32x4 *>(vd + 16) = vr[1];
     };
 
-    // the tiles alternate between two LDS buffers: tile j + 1 is written while tile j is
-    // read, and one barrier per tile makes it visible (and frees tile j's buffer). The
-    // staging registers hold tile j + 1 (AHEAD = 1: loaded at the start of tile j), or
-    // tiles j + 1 and j + 2 (AHEAD = 2: tile i in set i % 2, tile j + 3 loaded once tile
-    // j + 1 is stored).
+    // a half's tiles (keys j0 = base + STRIDE i) alternate between its two LDS buffers:
+    // tile i + 1 is written while tile i is read, and one barrier per step makes it visible
+    // (and frees tile i's buffer). The staging registers hold tile i + 1 (AHEAD = 1: loaded
+    // at the start of tile i), or tiles i + 1 and i + 2 (AHEAD = 2: tile i in set i % 2,
+    // tile i + 3 loaded once tile i + 1 is stored). A half with no tile left at a step
+    // (the second half, when the tile count is odd) still takes part in its barrier.
+    const int64_t base = (int64_t)DN_KEYS * half;
     u32x4 kr0[2], vr0[2], kr1[2], vr1[2];
     if constexpr (STAGE) {
-        load_stage(0, kr0, vr0);
+        load_stage(base, kr0, vr0);   // past t_last (no tile for this half): clamped, unused
         store_stage(0, kr0, vr0);
         if constexpr (AHEAD == 2) {
-            if (DN_KEYS <= t_last) load_stage(DN_KEYS, kr1, vr1);
-            if (2 * DN_KEYS <= t_last) load_stage(2 * DN_KEYS, kr0, vr0);
+            if (base + STRIDE <= t_last) load_stage(base + STRIDE, kr1, vr1);
+            if (base + 2 * STRIDE <= t_last) load_stage(base + 2 * STRIDE, kr0, vr0);
         }
     }
     __syncthreads();
     auto step = [&](int64_t j0, int buf, u32x4 (&krn)[2], u32x4 (&vrn)[2]) {
-        const bool more = j0 + DN_KEYS <= t_last;
+        const bool more = j0 + STRIDE <= t_last;
         if constexpr (STAGE && AHEAD == 1)
-            if (more) load_stage(j0 + DN_KEYS, krn, vrn);   // next tile in flight
+            if (more) load_stage(j0 + STRIDE, krn, vrn);   // next tile in flight
         const uint8_t *ks = ks0 + buf * DN_TILE_BYTES;
         const uint8_t *vs = vs0 + buf * DN_TILE_BYTES;
         if (j0 <= wave_tmax) {                         // uniform over the wave
@@ -204,9 +220,7 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
                     for (int mt = 0; mt < 8; ++mt) acc[nt][mt] *= alpha;
                     m_run[nt] = m_new;
                 }
-                // masked keys (z = -inf) give 0: a valid column's m_run is finite from
-                // its first tile on (key 0 is visible to every row); columns past the
-                // tile's rows may turn NaN, and are never written
+                // masked keys (z = -inf) give 0, since m_run is always finite
                 float p[8], rs = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -230,20 +244,51 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
             }
         }
         if constexpr (STAGE) {
-            if (more) store_stage(buf ^ 1, krn, vrn);   // tile j + 1 into the buffer of j - 1
+            if (more) store_stage(buf ^ 1, krn, vrn);   // tile i + 1 into the buffer of i - 1
             if constexpr (AHEAD == 2)
-                if (j0 + 3 * DN_KEYS <= t_last) load_stage(j0 + 3 * DN_KEYS, krn, vrn);
+                if (j0 + 3 * STRIDE <= t_last) load_stage(j0 + 3 * STRIDE, krn, vrn);
         }
-        __syncthreads();   // tile j + 1 staged, every wave done with tile j
+        __syncthreads();   // tile i + 1 staged, every wave done with tile i
     };
+    // steps: the first half's tile count, the same in both halves
+    const int64_t n_steps = (t_last / DN_KEYS + KS) / KS;
     if constexpr (AHEAD == 1) {
         int buf = 0;
-        for (int64_t j0 = 0; j0 <= t_last; j0 += DN_KEYS, buf ^= 1) step(j0, buf, kr0, vr0);
+        for (int64_t i = 0; i < n_steps; ++i, buf ^= 1) step(base + STRIDE * i, buf, kr0, vr0);
     } else {
-        for (int64_t j0 = 0; j0 <= t_last; j0 += 2 * DN_KEYS) {
-            step(j0, 0, kr1, vr1);
-            if (j0 + DN_KEYS > t_last) break;
-            step(j0 + DN_KEYS, 1, kr0, vr0);
+        for (int64_t i = 0; i < n_steps; i += 2) {
+            step(base + STRIDE * i, 0, kr1, vr1);
+            if (i + 1 >= n_steps) break;
+            step(base + STRIDE * (i + 1), 1, kr0, vr0);
+        }
+    }
+
+    // two halves: the second hands its state to the first (the tile buffers are free after
+    // the last step's barrier), which merges: m = max(m0, m1), each half's sum and
+    // accumulators scaled by 2^(m_h - m). Layout: [column tile - c0][34 floats][64 lanes].
+    if constexpr (KS == 2) {
+        if (half == 1) {
+#pragma unroll
+            for (int nt = 0; nt < NQ; ++nt) {
+                float *x = xch + (ct0 + nt - c0) * DN_XCH * WAVE + l;
+#pragma unroll
+                for (int e = 0; e < 32; ++e) x[e * WAVE] = acc[nt][e >> 2][e & 3];
+                x[32 * WAVE] = m_run[nt];
+                x[33 * WAVE] = l_run[nt];
+            }
+        }
+        __syncthreads();
+        if (half == 1) return;
+#pragma unroll
+        for (int nt = 0; nt < NQ; ++nt) {
+            const float *x = xch + (ct0 + nt - c0) * DN_XCH * WAVE + l;
+            const float m1 = x[32 * WAVE], m = fmaxf(m_run[nt], m1);
+            const float s0 = exp2f(m_run[nt] - m), s1 = exp2f(m1 - m);
+            l_run[nt] = l_run[nt] * s0 + x[33 * WAVE] * s1;
+#pragma unroll
+            for (int e = 0; e < 32; ++e)
+                acc[nt][e >> 2][e & 3] = acc[nt][e >> 2][e & 3] * s0 + x[e * WAVE] * s1;
+            m_run[nt] = m;
         }
     }
 
@@ -273,10 +318,9 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
 }
 
 template <int CS>
-__global__ void __launch_bounds__(dn_threads<CS>())
-attend_dense_kernel(DenseArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t ks[2 * DN_TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t vs[2 * DN_TILE_BYTES];
+__global__ void __launch_bounds__(DN_NT) attend_dense_kernel(DenseArgs a) {
+    // CS = 1: two tile buffers of K and of V; CS = 2: two of each per half
+    __shared__ __attribute__((aligned(16))) uint8_t lds[CS * 4 * DN_TILE_BYTES];
     const int g = blockIdx.y / CS, part = blockIdx.y % CS;
     const int64_t tile = a.n_tiles - 1 - (int64_t)blockIdx.x;
     const int sb = find_seq(a.batch, tile, [&](int i) { return (int64_t)a.tab[i].dtile0; });
@@ -288,33 +332,53 @@ attend_dense_kernel(DenseArgs a) {
     dt.nrows = (int)min<int64_t>(DN_ROWS, nd - i0);
     dt.row0 = dt.s.q0 + i0;
     dt.t_last = dt.t0 + dt.nrows - 1;
+    // a call with no scored rows leaves the selections to this kernel: a dense row keeps
+    // every visible block (ascending), then -1 (one workgroup of the tile writes them)
+    if (a.sel && blockIdx.y == 0) {
+        for (int e = threadIdx.x; e < dt.nrows * a.topk; e += DN_NT) {
+            const int rr = e / a.topk, i = e - rr * a.topk;
+            a.sel[(dt.row0 + rr) * a.topk + i] = i < nvis_of(dt.t0 + rr) ? i : -1;
+        }
+    }
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     if constexpr (CS == 1) {
-        if (w < 4) dense_wave<2, false, dn_stage_t0<1>(), 1>(a, dt, g, 2 * w, ks, vs);
-        else dense_wave<1, true, dn_stage_t0<1>(), 1>(a, dt, g, 4 + w, ks, vs);
+        uint8_t *ks = lds, *vs = lds + 2 * DN_TILE_BYTES;
+        if (w < 4) dense_wave<2, false, 4 * WAVE, 1, 1>(a, dt, g, 2 * w, ks, vs, 0, nullptr, 0);
+        else dense_wave<1, true, 4 * WAVE, 1, 1>(a, dt, g, 4 + w, ks, vs, 0, nullptr, 0);
     } else {
-        const int c0 = 6 * part;
-        if (w < 2) dense_wave<2, true, dn_stage_t0<2>(), 2>(a, dt, g, c0 + 2 * w, ks, vs);
-        else dense_wave<1, true, dn_stage_t0<2>(), 2>(a, dt, g, c0 + 2 + w, ks, vs);
+        const int c0 = 6 * part, half = w >> 2, wl = w & 3;
+        uint8_t *ks = lds + half * 4 * DN_TILE_BYTES, *vs = ks + 2 * DN_TILE_BYTES;
+        float *xch = reinterpret_cast<float *>(lds);
+        if (half == 0) {
+            if (wl < 2) dense_wave<2, true, 0, 2, 2>(a, dt, g, c0 + 2 * wl, ks, vs, 0, xch, c0);
+            else dense_wave<1, true, 0, 2, 2>(a, dt, g, c0 + 2 + wl, ks, vs, 0, xch, c0);
+        } else {
+            if (wl < 2)
+                dense_wave<1, true, 4 * WAVE, 2, 2>(a, dt, g, c0 + 4 + wl, ks, vs, 1, xch, c0);
+            else
+                dense_wave<2, true, 4 * WAVE, 2, 2>(a, dt, g, c0 + 2 * (wl - 2), ks, vs, 1, xch,
+                                                    c0);
+        }
     }
 }
 
 hipError_t launch_attend_dense(const SeqInfo *tab, int batch, int topk, float scale,
                                const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                               float *out, float *lse, int64_t n_tiles, hipStream_t st) {
+                               float *out, float *lse, int32_t *sel, int64_t n_tiles,
+                               hipStream_t st) {
     if (n_tiles <= 0) return hipSuccess;
     DenseArgs a;
     a.tab = tab; a.batch = batch; a.topk = topk;
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.n_tiles = n_tiles;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.sel = sel; a.n_tiles = n_tiles;
     trace_before(15, st);
     // fewer (dense tile, KV head) workgroups than CUs: each tile's column tiles go to two
     if (n_tiles * HKV < 256)
         hipLaunchKernelGGL(attend_dense_kernel<2>, dim3((unsigned)n_tiles, HKV * 2),
-                           dim3(dn_threads<2>()), 0, st, a);
+                           dim3(DN_NT), 0, st, a);
     else
         hipLaunchKernelGGL(attend_dense_kernel<1>, dim3((unsigned)n_tiles, HKV),
-                           dim3(dn_threads<1>()), 0, st, a);
+                           dim3(DN_NT), 0, st, a);
     return trace_after(st, hipGetLastError());
 }
 

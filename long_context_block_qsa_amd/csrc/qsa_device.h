@@ -195,15 +195,27 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Max and sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes that hold one column
+// of an MFMA 16x16 result), in every lane of a full wave. gfx950's row-swap permutes do
+// the exchange in the VALU instead of an LDS permute: a 16-lane (32-lane) swap of a value
+// with itself leaves each lane the pair {v[l], v[l ^ 16]} ({v[l], v[l ^ 32]}) across its
+// two results, whichever way round, and both lanes of a pair add the same two operands,
+// so the result is the same in all four lanes and equals that of the LDS-permute sums.
 __device__ __forceinline__ float wave_max_xor_16_32(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_sum_xor_16_32(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -86,10 +86,12 @@ hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, i
                          float *part, int nsplit, int64_t n_rows, const AttnMerge *merge,
                          bool skip_dense, hipStream_t st);
 // Causal attention of the rows in the dense regime (every visible block kept), in tiles
-// of DN_ROWS rows sharing their keys through LDS (qsa_dense.hip).
+// of DN_ROWS rows sharing their keys through LDS (qsa_dense.hip). sel not null: the
+// kernel also writes these rows' selections (calls without scored rows).
 hipError_t launch_attend_dense(const SeqInfo *tab, int batch, int topk, float scale,
                                const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                               float *out, float *lse, int64_t n_tiles, hipStream_t st);
+                               float *out, float *lse, int32_t *sel, int64_t n_tiles,
+                               hipStream_t st);
 // Attention backward over fixed selections (qsa_backward.hip).
 struct BwdSeq;
 struct BwdBuffers {

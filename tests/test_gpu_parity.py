@@ -120,6 +120,20 @@ def test_dense_prefills(lens, topk):
     _check_rows(f"dense{lens}/k{topk}", DeviceProblem(p, topk), None, topk)
 
 
+@pytest.mark.parametrize("lens,q_lens,topk", [
+    ([100, 700, 2051, 37], [80, 650, 1000, 37], 512),   # few dense tiles (key halves)
+    ([700, 300], [690, 299], 64),                        # dense/sparse boundary inside
+    ([4100, 3000], [4090, 2900], 512),                   # 250 dense tiles
+])
+def test_dense_rows_after_cached_prefix(lens, q_lens, topk):
+    """Dense-regime rows that start after a cached prefix, at positions that are not
+    multiples of the key tile, so that a tile's early rows see none of the keys of some
+    of the tiles its later rows attend: every row checked."""
+    _banner(f"dense rows after a prefix lens={lens} q_lens={q_lens} topk={topk}")
+    p = gen.make_problem(lens, q_lens=q_lens, seed=650 + sum(q_lens) + topk)
+    _check_rows(f"dense-prefix{lens}/k{topk}", DeviceProblem(p, topk), None, topk)
+
+
 def test_decode_1x32768_needles():
     _banner("decode 1x32768")
     p = gen.workload_problem("decode_1x32768")
