@@ -16,9 +16,9 @@
 //     2 key halves x 4 steps of MFMA 16x16x32 over the 128 dims;
 //   online softmax per query vector in base 2 (the reference maximum moves only when a
 //     vector's maximum grows by more than 2^8, so probabilities stay at most 2^8);
-//   O^T[128 dims x 32] += V^T (A operand, bf16 rows staged in LDS) x P^T: P is split
-//     into bf16 hi + lo parts (about 16 significant bits), 2 x 8 dim tiles of MFMA
-//     16x16x32 bf16 (the same precision as the sparse rows' kernel; P in
+//   O^T[128 dims x 32] += V^T (A operand, bf16 rows staged in LDS and read back
+//     transposed, dim tile mt = dims 16mt .. 16mt + 15) x P^T: P is split into bf16 hi +
+//     lo parts (about 16 significant bits), 2 x 8 dim tiles of MFMA 16x16x32 bf16 (the same precision as the sparse rows' kernel; P in
 //     fp16 alone left errors of 5e-4 in the outputs, which the attention backward, fed
 //     these outputs, carries into its gradients).
 // Key order within the MFMA contraction is permuted as in the sparse kernel (k-slot
@@ -41,15 +41,20 @@ namespace qsa {
 // softmax states and writes the rows. In half 0 waves 0-1 take two column tiles and waves
 // 2-3 one; half 1 the other way round, so every SIMD (waves w and w + 4) carries three.
 constexpr int DN_KEYS = 32;
-constexpr int DN_PITCH = 2 * HD + 16;     // LDS row pitch (bytes) of the K and V tiles
-constexpr int DN_TILE_BYTES = DN_KEYS * DN_PITCH;
+// LDS row pitches (bytes): 68 dwords for K (the 16 lanes of a 16-byte row read cover the 64
+// banks), 72 for V (the transposing 8-byte reads of 32 lanes cover them)
+constexpr int DN_KPITCH = 2 * HD + 16;
+constexpr int DN_VPITCH = 2 * HD + 32;
+constexpr int DN_KTILE = DN_KEYS * DN_KPITCH;
+constexpr int DN_VTILE = DN_KEYS * DN_VPITCH;
+constexpr int DN_HALF_LDS = 2 * (DN_KTILE + DN_VTILE);   // two K and two V tile buffers
 constexpr int DN_STAGE_NT = DN_KEYS * 8;  // threads that stage a tile (32 bytes of K and V each)
 constexpr int DN_XCH = 34;                // floats per lane and column tile handed between halves
 constexpr int DN_NT = 8 * WAVE;          // threads of a workgroup (both variants)
 static_assert(DN_ROWS * GQ == 16 * (4 * 2 + 4 * 1), "12 column tiles over the 8 waves");
 static_assert(DN_ROWS * GQ / 2 == 16 * (2 * 2 + 2 * 1), "6 column tiles over a half's 4 waves");
 static_assert(4 * WAVE == DN_STAGE_NT, "4 waves stage a tile");
-static_assert(6 * DN_XCH * WAVE * 4 <= 2 * 4 * DN_TILE_BYTES, "the hand-over fits the tiles");
+static_assert(6 * DN_XCH * WAVE * 4 <= 2 * DN_HALF_LDS, "the hand-over fits the tiles");
 
 struct DenseArgs {
     const SeqInfo *tab;
@@ -128,8 +133,8 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
         vr[1] = load16(vbase + j * (HKV * HD) + 8);
     };
     auto store_stage = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
-        uint8_t *kd = ks0 + buf * DN_TILE_BYTES + sk * DN_PITCH + 32 * sp;
-        uint8_t *vd = vs0 + buf * DN_TILE_BYTES + sk * DN_PITCH + 32 * sp;
+        uint8_t *kd = ks0 + buf * DN_KTILE + sk * DN_KPITCH + 32 * sp;
+        uint8_t *vd = vs0 + buf * DN_VTILE + sk * DN_VPITCH + 32 * sp;
         *reinterpret_cast<u32x4 *>(kd) = kr[0];
         *reinterpret_cast<u32x4 *>(kd + 16) = kr[1];
         *reinterpret_cast<u32x4 *>(vd) = vr[0];
@@ -157,8 +162,8 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
         const bool more = j0 + STRIDE <= t_last;
         if constexpr (STAGE && AHEAD == 1)
             if (more) load_stage(j0 + STRIDE, krn, vrn);   // next tile in flight
-        const uint8_t *ks = ks0 + buf * DN_TILE_BYTES;
-        const uint8_t *vs = vs0 + buf * DN_TILE_BYTES;
+        const uint8_t *ks = ks0 + buf * DN_KTILE;
+        const uint8_t *vs = vs0 + buf * DN_VTILE;
         if (j0 <= wave_tmax) {                         // uniform over the wave
             // ---- S^T: lane (gr, col) of column tile nt holds keys j0 + 16u + 4gr + i
             float z[NQ][8];
@@ -170,7 +175,7 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const u32x4 ka = *reinterpret_cast<const u32x4 *>(
-                        ks + (16 * u + col) * DN_PITCH + 2 * (32 * m + 8 * gr));
+                        ks + (16 * u + col) * DN_KPITCH + 2 * (32 * m + 8 * gr));
 #pragma unroll
                     for (int nt = 0; nt < NQ; ++nt) c[nt] = mfma_bf16_16x16x32(ka, qb[nt][m], c[nt]);
                 }
@@ -189,20 +194,20 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
                         }
                 }
             }
-            // ---- V^T operands of the 8 dim tiles: lane rows are dims 8col + mt, its
-            // k-slot keys as above
+            // ---- V^T operands of the 8 dim tiles: lane (gr, col) of tile mt holds dim
+            // 16mt + col at k-slots 8gr .. 8gr + 7 (keys 4gr + r, then 16 + 4gr + r). Two
+            // transposing reads per tile: lane 4r + q of a 16-lane group addresses the 4 dims
+            // 16mt + 4q .. + 3 of key 4gr + r (+ 16), and lane col receives dim 16mt + col
+            // of those 4 keys.
             u32x4 va[8];
             {
-                u32x4 vrow[8];
+                const uint8_t *vb = vs + (4 * gr + (col >> 2)) * DN_VPITCH + 8 * (col & 3);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    vrow[e] = *reinterpret_cast<const u32x4 *>(
-                        vs + (16 * (e >> 2) + 4 * gr + (e & 3)) * DN_PITCH + 16 * col);
-#pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        va[mt][kk] = bf16_pair(vrow[2 * kk][mt >> 1], vrow[2 * kk + 1][mt >> 1], mt & 1);
+                for (int mt = 0; mt < 8; ++mt) {
+                    const uint2 k0 = lds_read_tr16(vb + 32 * mt);
+                    const uint2 k1 = lds_read_tr16(vb + 16 * DN_VPITCH + 32 * mt);
+                    va[mt] = u32x4{k0.x, k0.y, k1.x, k1.y};
+                }
             }
             // ---- per column tile: online softmax per query vector, P^T as bf16 hi + lo,
             // O^T += V^T P^T
@@ -293,7 +298,7 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
     }
 
     // lane (gr, col), column tile nt: acc[nt][mt][i] = O[vector 16(ct0 + nt) + col]
-    // [dim 8(4gr+i) + mt]
+    // [dim 16mt + 4gr + i]
 #pragma unroll
     for (int nt = 0; nt < NQ; ++nt) {
         const int vq = 16 * (ct0 + nt) + col, rr = vq / GQ, hh = vq % GQ;
@@ -302,15 +307,8 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
         const float inv = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
         float *o = a.out + (row * HQ + g * GQ + hh) * HD;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d0 = 8 * (4 * gr + i);
-            const f32x4 lo4 = {acc[nt][0][i] * inv, acc[nt][1][i] * inv, acc[nt][2][i] * inv,
-                               acc[nt][3][i] * inv};
-            const f32x4 hi4 = {acc[nt][4][i] * inv, acc[nt][5][i] * inv, acc[nt][6][i] * inv,
-                               acc[nt][7][i] * inv};
-            *reinterpret_cast<f32x4 *>(o + d0) = lo4;
-            *reinterpret_cast<f32x4 *>(o + d0 + 4) = hi4;
-        }
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<f32x4 *>(o + 16 * mt + 4 * gr) = acc[nt][mt] * inv;
         if (a.lse && gr == 0)
             a.lse[row * HQ + g * GQ + hh] =
                 l_run[nt] > 0.f ? m_run[nt] * 0.69314718055994531f + logf(l_run[nt]) : -INFINITY;
@@ -320,7 +318,7 @@ __device__ __forceinline__ void dense_wave(const DenseArgs &a, const DenseTile &
 template <int CS>
 __global__ void __launch_bounds__(DN_NT) attend_dense_kernel(DenseArgs a) {
     // CS = 1: two tile buffers of K and of V; CS = 2: two of each per half
-    __shared__ __attribute__((aligned(16))) uint8_t lds[CS * 4 * DN_TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[CS * DN_HALF_LDS];
     const int g = blockIdx.y / CS, part = blockIdx.y % CS;
     const int64_t tile = a.n_tiles - 1 - (int64_t)blockIdx.x;
     const int sb = find_seq(a.batch, tile, [&](int i) { return (int64_t)a.tab[i].dtile0; });
@@ -342,12 +340,12 @@ __global__ void __launch_bounds__(DN_NT) attend_dense_kernel(DenseArgs a) {
     }
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     if constexpr (CS == 1) {
-        uint8_t *ks = lds, *vs = lds + 2 * DN_TILE_BYTES;
+        uint8_t *ks = lds, *vs = lds + 2 * DN_KTILE;
         if (w < 4) dense_wave<2, false, 4 * WAVE, 1, 1>(a, dt, g, 2 * w, ks, vs, 0, nullptr, 0);
         else dense_wave<1, true, 4 * WAVE, 1, 1>(a, dt, g, 4 + w, ks, vs, 0, nullptr, 0);
     } else {
         const int c0 = 6 * part, half = w >> 2, wl = w & 3;
-        uint8_t *ks = lds + half * 4 * DN_TILE_BYTES, *vs = ks + 2 * DN_TILE_BYTES;
+        uint8_t *ks = lds + half * DN_HALF_LDS, *vs = ks + 2 * DN_KTILE;
         float *xch = reinterpret_cast<float *>(lds);
         if (half == 0) {
             if (wl < 2) dense_wave<2, true, 0, 2, 2>(a, dt, g, c0 + 2 * wl, ks, vs, 0, xch, c0);

@@ -876,6 +876,16 @@ __device__ __forceinline__ uint32_t bf16_pair(uint32_t x0, uint32_t x1, bool odd
     return __builtin_amdgcn_perm(x1, x0, odd ? 0x07060302u : 0x05040100u);
 }
 
+// Transposing LDS read of gfx950 (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
+// receives as its 16-bit element r (r = 0..3) element i % 4 of the four 16-bit values
+// that lane 4r + i / 4 of the group addresses (8 bytes, 8-byte aligned, in LDS).
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t *p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
 __device__ __forceinline__ u32x4 load16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
