@@ -325,6 +325,8 @@ __device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
     static_assert(NT == 256, "bin ownership assumes 256 threads");
     constexpr int NW = NT / WAVE;
     const int tid = threadIdx.x;
+    // a row holds fewer than 2^31 keys (its blocks of an int32 length): 32-bit positions
+    const uint32_t n32 = (uint32_t)n;
     uint32_t prefix = prefix0, pmask = pmask0;
     int64_t need = k;
     bool exact = false;
@@ -335,24 +337,34 @@ __device__ __forceinline__ void radix_kth(KeyPtr keys, int64_t n, int64_t k,
         for (int i = tid; i < nb; i += NT) hist[i] = 0u;
         if (tid == 0) { found[0] = 0u; found[1] = 0u; }
         __syncthreads();
-        // keys are read in batches of 8 before their atomics, so the loads overlap
+        // keys are read in batches of 8 before their atomics, so the loads overlap; whole
+        // batches need no bounds checks
         uint32_t k_or = 0u, k_and = 0xffffffffu;
-        for (int64_t i0 = tid; i0 < n; i0 += 8 * NT) {
+        auto count = [&](uint32_t x) {
+            if ((x & pmask) == prefix) {
+                atomicAdd(&hist[(x >> shift) & dmask], 1u);
+                k_or |= x;
+                k_and &= x;
+            }
+        };
+        uint32_t i0 = tid;
+        for (; i0 + 7u * NT < n32; i0 += 8 * NT) {
+            uint32_t kk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kk[e] = keys[i0 + (uint32_t)e * NT];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) count(kk[e]);
+        }
+        if (i0 < n32) {
             uint32_t kk[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int64_t i = i0 + (int64_t)e * NT;
-                kk[e] = i < n ? keys[i] : 0u;
+                const uint32_t i = i0 + (uint32_t)e * NT;
+                kk[e] = i < n32 ? keys[i] : 0u;
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t i = i0 + (int64_t)e * NT;
-                if (i < n && (kk[e] & pmask) == prefix) {
-                    atomicAdd(&hist[(kk[e] >> shift) & dmask], 1u);
-                    k_or |= kk[e];
-                    k_and &= kk[e];
-                }
-            }
+            for (int e = 0; e < 8; ++e)
+                if (i0 + (uint32_t)e * NT < n32) count(kk[e]);
         }
 #pragma unroll
         for (int d = 1; d < WAVE; d <<= 1) {
@@ -428,29 +440,32 @@ __device__ __forceinline__ int64_t emit_kept(KeyPtr keys, int64_t n, uint32_t th
     constexpr int NW = NT / WAVE;
     static_assert(PER <= WAVE, "one lane per element writes the wave's counts");
     const int tid = threadIdx.x, w = tid / WAVE, l = lane_id();
-    int64_t run_eq = 0, run_sel = 0;
+    // fewer than 2^31 keys, so positions, counts and slots are 32-bit
+    const uint32_t n32 = (uint32_t)n;
+    const int need32 = (int)need, cap32 = (int)min<int64_t>(cap, INT32_MAX);
+    int run_eq = 0, run_sel = 0;
     int par = 0;
 #pragma unroll 1
-    for (int64_t base = 0; base < n; base += (int64_t)NT * PER, par ^= 1) {
+    for (uint32_t base = 0; base < n32; base += (uint32_t)NT * PER, par ^= 1) {
         int32_t *ceq = cnt + par * 2 * NW * PER;   // [wave][element]: keys equal to theta
         int32_t *ctk = ceq + NW * PER;             // [wave][element]: kept keys
         uint32_t kk[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const int64_t i = base + (int64_t)e * NT + tid;
-            kk[e] = i < n ? keys[i] : 0u;
+            const uint32_t i = base + (uint32_t)(e * NT + tid);
+            kk[e] = i < n32 ? keys[i] : 0u;
         }
         unsigned long long beq[PER];
         int v = 0;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            beq[e] = __ballot(base + (int64_t)e * NT + tid < n && kk[e] == theta);
+            beq[e] = __ballot(base + (uint32_t)(e * NT + tid) < n32 && kk[e] == theta);
             v = l == e ? (int)__popcll(beq[e]) : v;
         }
         if (l < PER) ceq[w * PER + l] = v;
         __syncthreads();
         // equal keys before each element of this lane; then which keys are kept
-        int64_t eq_pre = run_eq;
+        int eq_pre = run_eq;
         int eq_tot = 0;
         unsigned long long btk[PER];
         v = 0;
@@ -463,10 +478,10 @@ __device__ __forceinline__ int64_t emit_kept(KeyPtr keys, int64_t n, uint32_t th
                 before_w += i < w ? c : 0;
                 col += c;
             }
-            const bool valid = base + (int64_t)e * NT + tid < n;
+            const bool valid = base + (uint32_t)(e * NT + tid) < n32;
             const bool eq = (beq[e] >> l) & 1ull;
             const bool take = (valid && kk[e] > theta) ||
-                              (eq && eq_pre + before_w + lanes_below(beq[e]) < need);
+                              (eq && eq_pre + before_w + lanes_below(beq[e]) < need32);
             btk[e] = __ballot(take);
             v = l == e ? (int)__popcll(btk[e]) : v;
             eq_pre += col;
@@ -474,7 +489,7 @@ __device__ __forceinline__ int64_t emit_kept(KeyPtr keys, int64_t n, uint32_t th
         }
         if (l < PER) ctk[w * PER + l] = v;
         __syncthreads();
-        int64_t pos = run_sel;
+        int pos = run_sel;
         int tk_tot = 0;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
@@ -486,8 +501,8 @@ __device__ __forceinline__ int64_t emit_kept(KeyPtr keys, int64_t n, uint32_t th
                 col += c;
             }
             if ((btk[e] >> l) & 1ull) {
-                const int64_t slot = pos + before_w + lanes_below(btk[e]);
-                if (slot < cap) out_idx[slot] = (int32_t)(base + (int64_t)e * NT + tid);
+                const int slot = pos + before_w + lanes_below(btk[e]);
+                if (slot < cap32) out_idx[slot] = (int32_t)(base + (uint32_t)(e * NT + tid));
             }
             pos += col;
             tk_tot += col;
@@ -513,21 +528,22 @@ __device__ __forceinline__ void collect_bin(KeyPtr keys, int64_t n, uint32_t lo,
     const int tid = threadIdx.x, w = tid / WAVE, l = lane_id();
     int run_a = 0, run_c = 0;
     int par = 0;
+    const uint32_t n32 = (uint32_t)n;   // fewer than 2^31 keys
 #pragma unroll 1
-    for (int64_t base = 0; base < n; base += (int64_t)NT * PER, par ^= 1) {
+    for (uint32_t base = 0; base < n32; base += (uint32_t)NT * PER, par ^= 1) {
         int32_t *ca = cnt + par * 2 * NW * PER;   // [wave][element]: keys above hi
         int32_t *cc = ca + NW * PER;              // [wave][element]: keys in [lo, hi]
         uint32_t kk[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const int64_t i = base + (int64_t)e * NT + tid;
-            kk[e] = i < n ? keys[i] : 0u;
+            const uint32_t i = base + (uint32_t)(e * NT + tid);
+            kk[e] = i < n32 ? keys[i] : 0u;
         }
         unsigned long long ba[PER], bc[PER];
         int va = 0, vc = 0;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const bool valid = base + (int64_t)e * NT + tid < n;
+            const bool valid = base + (uint32_t)(e * NT + tid) < n32;
             ba[e] = __ballot(valid && kk[e] > hi);
             bc[e] = __ballot(valid && kk[e] >= lo && kk[e] <= hi);
             va = l == e ? (int)__popcll(ba[e]) : va;
@@ -547,7 +563,7 @@ __device__ __forceinline__ void collect_bin(KeyPtr keys, int64_t n, uint32_t lo,
                 wc += i < w ? xc : 0;
                 tc += xc;
             }
-            const int32_t pos = (int32_t)(base + (int64_t)e * NT + tid);
+            const int32_t pos = (int32_t)(base + (uint32_t)(e * NT + tid));
             if ((ba[e] >> l) & 1ull) a_pos[pa + wa + lanes_below(ba[e])] = pos;
             if ((bc[e] >> l) & 1ull) {
                 const int sl = pc + wc + lanes_below(bc[e]);
