@@ -425,21 +425,41 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Per-(element, wave) counts of a batch of an ordered pass, c[e * NW + w] (element e of
+// wave w holds the keys at base + e * NT + 64 w + lane): their exclusive prefix in position
+// order (element-major, then wave) for this wave's elements into pre[] (wave-uniform), and
+// the batch total. Every wave derives it from the table itself: one LDS read per lane, a DPP
+// scan and register reads, instead of adding up the table per element.
+template <int NW, int PER>
+__device__ __forceinline__ int batch_prefix(const int32_t *c, int w, int (&pre)[PER]) {
+    constexpr int NC = NW * PER;
+    static_assert(NC <= WAVE, "a batch's counts fit one wave");
+    const int l = lane_id();
+    const int x = l < NC ? c[l] : 0;
+    const int incl = wave_incl_scan_i32(x);
+    const int excl = incl - x;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) pre[e] = __builtin_amdgcn_readlane(excl, e * NW + w);
+    return __builtin_amdgcn_readlane(incl, NC - 1);
+}
+
 // Ordered pass after radix_kth: keeps every key above theta and the first `need` keys
 // equal to it (by position), writing their positions in ascending order to out_idx (at
 // most cap); returns the number kept. Thread t reads element e of a batch at position
 // base + e*NT + t, so every load instruction reads consecutive keys. A kept key's slot is
 // its rank in position order: the kept keys of earlier elements, of earlier waves at the
-// same element, and of lower lanes (a ballot). Per-(wave, element) counts of equal and of
-// kept keys go through `cnt` (LDS, 4 * (NT/64) * PER ints; two barriers per batch, the
-// two halves used by alternate batches). All NT threads must call it.
+// same element (batch_prefix), and of lower lanes (a ballot). Per-(element, wave) counts of
+// equal and of kept keys go through `cnt` (LDS, 4 * (NT/64) * PER ints; two barriers per
+// batch, the two halves used by alternate batches). All NT threads must call it.
 template <int NT, int PER, typename KeyPtr>
 __device__ __forceinline__ int64_t emit_kept(KeyPtr keys, int64_t n, uint32_t theta,
                                              int64_t need, int32_t *out_idx, int64_t cap,
                                              int32_t *cnt) {
     constexpr int NW = NT / WAVE;
+    constexpr int NC = NW * PER;
     static_assert(PER <= WAVE, "one lane per element writes the wave's counts");
-    const int tid = threadIdx.x, w = tid / WAVE, l = lane_id();
+    const int tid = threadIdx.x, l = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
     // fewer than 2^31 keys, so positions, counts and slots are 32-bit
     const uint32_t n32 = (uint32_t)n;
     const int need32 = (int)need, cap32 = (int)min<int64_t>(cap, INT32_MAX);
@@ -447,8 +467,8 @@ __device__ __forceinline__ int64_t emit_kept(KeyPtr keys, int64_t n, uint32_t th
     int par = 0;
 #pragma unroll 1
     for (uint32_t base = 0; base < n32; base += (uint32_t)NT * PER, par ^= 1) {
-        int32_t *ceq = cnt + par * 2 * NW * PER;   // [wave][element]: keys equal to theta
-        int32_t *ctk = ceq + NW * PER;             // [wave][element]: kept keys
+        int32_t *ceq = cnt + par * 2 * NC;   // [element][wave]: keys equal to theta
+        int32_t *ctk = ceq + NC;             // [element][wave]: kept keys
         uint32_t kk[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
@@ -462,50 +482,31 @@ __device__ __forceinline__ int64_t emit_kept(KeyPtr keys, int64_t n, uint32_t th
             beq[e] = __ballot(base + (uint32_t)(e * NT + tid) < n32 && kk[e] == theta);
             v = l == e ? (int)__popcll(beq[e]) : v;
         }
-        if (l < PER) ceq[w * PER + l] = v;
+        if (l < PER) ceq[l * NW + w] = v;
         __syncthreads();
         // equal keys before each element of this lane; then which keys are kept
-        int eq_pre = run_eq;
-        int eq_tot = 0;
+        int pre[PER];
+        const int eq_tot = batch_prefix<NW, PER>(ceq, w, pre);
         unsigned long long btk[PER];
         v = 0;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            int before_w = 0, col = 0;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) {
-                const int c = ceq[i * PER + e];
-                before_w += i < w ? c : 0;
-                col += c;
-            }
             const bool valid = base + (uint32_t)(e * NT + tid) < n32;
             const bool eq = (beq[e] >> l) & 1ull;
             const bool take = (valid && kk[e] > theta) ||
-                              (eq && eq_pre + before_w + lanes_below(beq[e]) < need32);
+                              (eq && run_eq + pre[e] + lanes_below(beq[e]) < need32);
             btk[e] = __ballot(take);
             v = l == e ? (int)__popcll(btk[e]) : v;
-            eq_pre += col;
-            eq_tot += col;
         }
-        if (l < PER) ctk[w * PER + l] = v;
+        if (l < PER) ctk[l * NW + w] = v;
         __syncthreads();
-        int pos = run_sel;
-        int tk_tot = 0;
+        const int tk_tot = batch_prefix<NW, PER>(ctk, w, pre);
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            int before_w = 0, col = 0;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) {
-                const int c = ctk[i * PER + e];
-                before_w += i < w ? c : 0;
-                col += c;
-            }
             if ((btk[e] >> l) & 1ull) {
-                const int slot = pos + before_w + lanes_below(btk[e]);
+                const int slot = run_sel + pre[e] + lanes_below(btk[e]);
                 if (slot < cap32) out_idx[slot] = (int32_t)(base + (uint32_t)(e * NT + tid));
             }
-            pos += col;
-            tk_tot += col;
         }
         run_eq += eq_tot;
         run_sel += tk_tot;
@@ -524,15 +525,17 @@ __device__ __forceinline__ void collect_bin(KeyPtr keys, int64_t n, uint32_t lo,
                                             int32_t *a_pos, uint32_t *c_key, int32_t *c_pos,
                                             int32_t *cnt) {
     constexpr int NW = NT / WAVE;
+    constexpr int NC = NW * PER;
     static_assert(PER <= WAVE, "one lane per element writes the wave's counts");
-    const int tid = threadIdx.x, w = tid / WAVE, l = lane_id();
+    const int tid = threadIdx.x, l = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
     int run_a = 0, run_c = 0;
     int par = 0;
     const uint32_t n32 = (uint32_t)n;   // fewer than 2^31 keys
 #pragma unroll 1
     for (uint32_t base = 0; base < n32; base += (uint32_t)NT * PER, par ^= 1) {
-        int32_t *ca = cnt + par * 2 * NW * PER;   // [wave][element]: keys above hi
-        int32_t *cc = ca + NW * PER;              // [wave][element]: keys in [lo, hi]
+        int32_t *ca = cnt + par * 2 * NC;   // [element][wave]: keys above hi
+        int32_t *cc = ca + NC;              // [element][wave]: keys in [lo, hi]
         uint32_t kk[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
@@ -549,32 +552,23 @@ __device__ __forceinline__ void collect_bin(KeyPtr keys, int64_t n, uint32_t lo,
             va = l == e ? (int)__popcll(ba[e]) : va;
             vc = l == e ? (int)__popcll(bc[e]) : vc;
         }
-        if (l < PER) { ca[w * PER + l] = va; cc[w * PER + l] = vc; }
+        if (l < PER) { ca[l * NW + w] = va; cc[l * NW + w] = vc; }
         __syncthreads();
-        int pa = run_a, pc = run_c;
+        int pa[PER], pc[PER];
+        const int ta = batch_prefix<NW, PER>(ca, w, pa);
+        const int tc = batch_prefix<NW, PER>(cc, w, pc);
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            int wa = 0, ta = 0, wc = 0, tc = 0;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) {
-                const int xa = ca[i * PER + e], xc = cc[i * PER + e];
-                wa += i < w ? xa : 0;
-                ta += xa;
-                wc += i < w ? xc : 0;
-                tc += xc;
-            }
             const int32_t pos = (int32_t)(base + (uint32_t)(e * NT + tid));
-            if ((ba[e] >> l) & 1ull) a_pos[pa + wa + lanes_below(ba[e])] = pos;
+            if ((ba[e] >> l) & 1ull) a_pos[run_a + pa[e] + lanes_below(ba[e])] = pos;
             if ((bc[e] >> l) & 1ull) {
-                const int sl = pc + wc + lanes_below(bc[e]);
+                const int sl = run_c + pc[e] + lanes_below(bc[e]);
                 c_key[sl] = kk[e];
                 c_pos[sl] = pos;
             }
-            pa += ta;
-            pc += tc;
         }
-        run_a = pa;
-        run_c = pc;
+        run_a += ta;
+        run_c += tc;
     }
     __syncthreads();
 }
