@@ -840,14 +840,15 @@ __device__ __forceinline__ int block_topk_radix(const uint32_t (&x)[PER], int n,
 // 8 E4M3 bytes -> 8 bf16 (exact: E4M3 values have 4 significant bits and a narrower
 // exponent range than bf16), in the byte order of the input.
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint2 b) {
+    // gfx950's scaled conversion, scale 1: two E4M3 bytes (the low or the high pair of a
+    // word) to two bf16 in one instruction, exactly (every E4M3 value is a bf16 value)
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
     u32x4 r;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t w = h ? b.y : b.x;
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-        r[2 * h] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
-        r[2 * h + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+        r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+        r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
     }
     return r;
 }
