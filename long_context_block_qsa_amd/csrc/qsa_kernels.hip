@@ -1391,23 +1391,40 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
             ph[q2] = hh;
             pl[q2] = pack_bf16x2_rne(r0, r1);
         }
-        u32x4 vb[8];
+        if constexpr (FP8) {
+            // keys 2kk and 2kk + 1 at dims mt and mt + 1 (mt even): one byte permute puts
+            // the four E4M3 values in pair order, and each half converts to the bf16 pair
+            // of one dim tile
+            typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if constexpr (FP8) vb[e] = e4m3x8_to_bf16x8(T.vr[e]);
-            else vb[e] = T.vr[e];
-        }
+            for (int mp = 0; mp < 4; ++mp) {
+                u32x4 va0, va1;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const int q2 = mt >> 1;
-            u32x4 va;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const uint32_t x0 = vb[2 * kk][q2], x1 = vb[2 * kk + 1][q2];
-                va[kk] = bf16_pair(x0, x1, mt & 1);
+                for (int kk = 0; kk < 4; ++kk) {
+                    const uint32_t a0 = (mp >> 1) ? T.vr[2 * kk].y : T.vr[2 * kk].x;
+                    const uint32_t a1 = (mp >> 1) ? T.vr[2 * kk + 1].y : T.vr[2 * kk + 1].x;
+                    const uint32_t w4 = __builtin_amdgcn_perm(a1, a0, (mp & 1) ? 0x07030602u : 0x05010400u);
+                    va0[kk] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, false));
+                    va1[kk] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, true));
+                }
+                acc[2 * mp] = mfma_bf16_16x16x32(va0, ph, acc[2 * mp]);
+                acc[2 * mp] = mfma_bf16_16x16x32(va0, pl, acc[2 * mp]);
+                acc[2 * mp + 1] = mfma_bf16_16x16x32(va1, ph, acc[2 * mp + 1]);
+                acc[2 * mp + 1] = mfma_bf16_16x16x32(va1, pl, acc[2 * mp + 1]);
             }
-            acc[mt] = mfma_bf16_16x16x32(va, ph, acc[mt]);
-            acc[mt] = mfma_bf16_16x16x32(va, pl, acc[mt]);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const int q2 = mt >> 1;
+                u32x4 va;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const uint32_t x0 = T.vr[2 * kk][q2], x1 = T.vr[2 * kk + 1][q2];
+                    va[kk] = bf16_pair(x0, x1, mt & 1);
+                }
+                acc[mt] = mfma_bf16_16x16x32(va, ph, acc[mt]);
+                acc[mt] = mfma_bf16_16x16x32(va, pl, acc[mt]);
+            }
         }
     };
     auto next_ids = [&](int jn) {
