@@ -1092,6 +1092,7 @@ struct AttnArgs {
     int nsplit;
     int64_t nrows;
     int skip_dense;   // rows with at most topk visible blocks are left to the dense kernel
+    int head_major;   // nsplit 1: waves take every row of KV head 0, then of head 1
     int wg_combine;   // nsplit % 4 == 0: a workgroup's 4 split waves merge into 1 partial
     int merge;        // decode: merge the rows of short tiles here (operands in `loc`)
     LocalArgs loc;
@@ -1522,10 +1523,18 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
     }
 }
 
-// wave -> (row, kv head, split)
+// wave -> (row, kv head, split). head_major (one split per row): every row of KV head 0
+// first, then of head 1, so that the waves in flight read one head's K/V rows (its
+// half-size working set stays in the caches for long sequences)
 __device__ __forceinline__ bool attend_item(const AttnArgs &a, int64_t &row, int &g, int &sp) {
     const int64_t item = __builtin_amdgcn_readfirstlane(
         (int)((int64_t)blockIdx.x * (ATT_NT / WAVE) + threadIdx.x / WAVE));
+    if (a.head_major) {
+        g = (int)(item / a.nrows);
+        row = item - (int64_t)g * a.nrows;
+        sp = 0;
+        return g < HKV;
+    }
     row = item / (HKV * a.nsplit);
     const int rem = (int)(item % (HKV * a.nsplit));
     g = rem / a.nsplit;
@@ -1869,6 +1878,7 @@ hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, i
     a.nsplit = nsplit; a.nrows = n_rows;
     a.skip_dense = skip_dense && !d && nsplit == 1;
     a.wg_combine = nsplit >= 4 && nsplit % 4 == 0;
+    a.head_major = !d && nsplit == 1;
     const int64_t waves = n_rows * HKV * nsplit;
     const int64_t wgs = (waves + ATT_NT / WAVE - 1) / (ATT_NT / WAVE);
     trace_before(4, st);
