@@ -323,11 +323,13 @@ __global__ void __launch_bounds__(BDQ_NT) __attribute__((amdgpu_waves_per_eu(2))
 bwd_dq_kernel(DqArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[(BDQ_NT / WAVE) * DQ_LDS];
     uint8_t *klds = lds + (threadIdx.x / WAVE) * DQ_LDS, *vlds = klds + 32 * DQ_PITCH;
+    // waves in head-major order (every row of KV head 0, then of head 1): the waves in
+    // flight gather one head's K/V rows, half the lines
     const int64_t item = __builtin_amdgcn_readfirstlane(
         (int)((int64_t)blockIdx.x * (BDQ_NT / WAVE) + threadIdx.x / WAVE));
-    const int64_t row = item >> 1;
-    const int g = (int)(item & 1);
-    if (row >= a.nrows) return;
+    const int g = (int)(item / a.nrows);
+    const int64_t row = item - (int64_t)g * a.nrows;
+    if (g >= HKV) return;
     const int sb = find_seq(a.batch, row, [&](int i) { return (int64_t)a.tab[i].q0; });
     const BwdSeq S = a.tab[sb];
     const int64_t t = (int64_t)S.L - S.nq + (row - S.q0);
@@ -517,6 +519,8 @@ bwd_dkv_kernel(DkvArgs a) {
     const int w = threadIdx.x / WAVE;
     const int64_t item = __builtin_amdgcn_readfirstlane(
         (int)((int64_t)blockIdx.x * (BDKV_NT / WAVE) + w));
+    // (the two KV heads of a block on neighbouring waves: head-major order, which speeds
+    // up dQ, measured slower here)
     const int64_t gb = a.kb_lo + (item >> 1);
     const int g = (int)(item & 1);
     if (gb >= a.kb_hi) return;
