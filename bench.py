@@ -42,7 +42,7 @@ HOST_THREADS = 16   # host threads for the oracle baseline: one GPU's share of t
 # reads on a plain 512 MiB copy) from rocprofv3 --pmc runs of this benchmark, with the
 # fingerprint of the kernel sources they were taken on; reported only while it matches.
 TRAFFIC = {
-    "score": {"bytes": 134_760_000, "sources_sha256": "a56f94889d4224f46bfe324219dbe4751ef3dc439c77b7f12dd60b99797289f4"},
+    "score": {"bytes": 134_760_000, "sources_sha256": "12d0f1dcf87cdbd7c139e202cce203009477eb207a445dc2ed927d0fc0e17332"},
 }
 
 
