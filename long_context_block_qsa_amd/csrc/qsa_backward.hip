@@ -510,7 +510,7 @@ struct DkvRow {
     int64_t t;
 };
 
-__global__ void __launch_bounds__(BDKV_NT) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(BDKV_NT) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkv_kernel(DkvArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sq[BDKV_NT / WAVE][GQ * QPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t so[BDKV_NT / WAVE][GQ * QPITCH];
@@ -616,26 +616,28 @@ bwd_dkv_kernel(DkvArgs a) {
         }
         wave_lds_sync();
     };
-    // Two row buffers used in turn (no register copies); each half-step loads the row
-    // id two entries ahead (one uniform dword) and the next row's operands before it
-    // processes the current row, so the waits leave the next row's loads in flight.
-    // Loads past the end repeat the last entry's row.
+    // Three row buffers used in turn (no register copies): each step issues the loads of
+    // the row two entries ahead before it processes the current row, so the waits leave
+    // two rows' loads in flight (two waves per SIMD hold the registers). Loads past the
+    // end repeat the last entry's row.
     if (lo < hi) {
         auto row_id = [&](int e) -> int32_t {
             return __builtin_amdgcn_readfirstlane(a.list[min(e, hi - 1)]);
         };
-        int32_t id1 = row_id(lo + 1);
         DkvRow A = load_row(row_id(lo));
-        for (int e = lo; e < hi; e += 2) {
-            const int32_t id2 = row_id(e + 2);
-            const DkvRow B = load_row(id1);
-            __builtin_amdgcn_sched_barrier(0);   // issue B's loads before waiting for A
+        DkvRow B = load_row(row_id(lo + 1));
+        for (int e = lo; e < hi; e += 3) {
+            const DkvRow C = load_row(row_id(e + 2));
+            __builtin_amdgcn_sched_barrier(0);
             process(A);
             if (e + 1 >= hi) break;
-            id1 = row_id(e + 3);
-            A = load_row(id2);
+            A = load_row(row_id(e + 3));
             __builtin_amdgcn_sched_barrier(0);
             process(B);
+            if (e + 2 >= hi) break;
+            B = load_row(row_id(e + 4));
+            __builtin_amdgcn_sched_barrier(0);
+            process(C);
         }
     }
     // window 0 writes the block's gradients, later windows (later launches) add to them
