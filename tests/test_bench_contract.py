@@ -34,11 +34,14 @@ def test_traffic_fingerprint_follows_code_not_comments(tmp_path):
     shutil.copytree(src, dst)
     bench.ROOT = str(tmp_path)
     base = bench.sources_sha256()
-    f = dst / "qsa_dense.hip"
+    f = dst / "qsa_kernels.hip"
     text = f.read_text()
     f.write_text(text.replace("namespace qsa {", "namespace qsa {  // a comment\n/* and another */", 1))
     assert bench.sources_sha256() == base
-    f.write_text(text.replace("constexpr int DN_KEYS = 32;", "constexpr int DN_KEYS = 64;", 1))
+    other = dst / "qsa_backward.hip"   # another translation unit: not the scoring kernel's
+    other.write_text(other.read_text() + "\nnamespace qsa { constexpr int UNUSED_X = 1; }\n")
+    assert bench.sources_sha256() == base
+    f.write_text(text.replace("constexpr int SCORE_BATCH = 8;", "constexpr int SCORE_BATCH = 4;", 1))
     assert bench.sources_sha256() != base
     bench.TRAFFIC = {"score": {"bytes": 1, "sources_sha256": base}}
     assert bench.traffic_of("score") is None
