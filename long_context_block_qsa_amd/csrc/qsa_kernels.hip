@@ -1110,12 +1110,13 @@ struct KVTile {
     u32x4 vr[8];
     uint32_t valid;  // bit 4u+i: key j0 + 16u + 4gr + i is attended
 };
-// The same tile from the FP8 KV cache: 8 E4M3 bytes per load, and the K and V scales
-// of the lane's 8 P keys (the logit and probability of key e are scaled by them).
+// The same tile from the FP8 KV cache: 8 E4M3 bytes per load, and the K and V scales of
+// tile key l & 31 (lane l; key 16h + 4gr + i of the tile is that of lane group gr's slot
+// of half h, token i), which the lanes that use them fetch by lane permutes.
 struct KVTile8 {
     uint2 kt[8];
     uint2 vr[8];
-    float ks[8], vs[8];
+    float ks, vs;
     uint32_t valid;
 };
 // LDS row pitch (bytes) of the per-wave FP8 K tile that turns the row-per-16-lanes loads
@@ -1223,13 +1224,12 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
     auto load_tile = [&](int j0, int32_t cur, int buf) -> Tile {
         Tile T;
         T.valid = 0;
-        uint32_t ob[2], bits_h[2];
+        uint32_t ob[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int sl = (j0 >> 2) + 4 * h + gr;
             uint32_t bits;
             const int64_t f = slot_first(sl, cur, bits);
-            bits_h[h] = bits;
             T.valid |= bits << (4 * h);
             ob[h] = f >= 0 ? (uint32_t)f * TOK_BYTES + g * HD * (FP8 ? 1 : 2) : OFF_NONE;
         }
@@ -1255,33 +1255,6 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
                     T.vr[4 * h + i] = __builtin_bit_cast(
                         uint2, __builtin_amdgcn_raw_buffer_load_b64(vres, o + i * TOK_BYTES, 0, 0));
                 }
-                // scales of the slot's first token (both heads, 8 bytes per token)
-                const uint32_t os = ob[h] != OFF_NONE ? (ob[h] - g * HD) / TOK_BYTES * (HKV * 4)
-                                                      : OFF_NONE;
-                if (bits_h[h] == 0xfu) {
-                    // a whole block: its 4 tokens' K and V scales are 32 contiguous bytes each
-                    // (one line), read with two 16-byte loads instead of four scattered ones
-                    const u32x4 k01 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ksres, os, 0, 0));
-                    const u32x4 k23 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ksres, os + 16, 0, 0));
-                    const u32x4 v01 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vsres, os, 0, 0));
-                    const u32x4 v23 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vsres, os + 16, 0, 0));
-                    T.ks[4 * h + 0] = __uint_as_float(g ? k01[1] : k01[0]);
-                    T.ks[4 * h + 1] = __uint_as_float(g ? k01[3] : k01[2]);
-                    T.ks[4 * h + 2] = __uint_as_float(g ? k23[1] : k23[0]);
-                    T.ks[4 * h + 3] = __uint_as_float(g ? k23[3] : k23[2]);
-                    T.vs[4 * h + 0] = __uint_as_float(g ? v01[1] : v01[0]);
-                    T.vs[4 * h + 1] = __uint_as_float(g ? v01[3] : v01[2]);
-                    T.vs[4 * h + 2] = __uint_as_float(g ? v23[1] : v23[0]);
-                    T.vs[4 * h + 3] = __uint_as_float(g ? v23[3] : v23[2]);
-                } else {   // the raw tail (tokens past t read 0) or no slot
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        T.ks[4 * h + i] = __builtin_bit_cast(
-                            float, __builtin_amdgcn_raw_buffer_load_b32(ksres, os + i * HKV * 4 + g * 4, 0, 0));
-                        T.vs[4 * h + i] = __builtin_bit_cast(
-                            float, __builtin_amdgcn_raw_buffer_load_b32(vsres, os + i * HKV * 4 + g * 4, 0, 0));
-                    }
-                }
             } else {
                 const uint32_t o = ob[h] + 16 * col;
 #pragma unroll
@@ -1289,6 +1262,17 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
                     T.vr[4 * h + i] = __builtin_bit_cast(
                         u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, o + i * TOK_BYTES, 0, 0));
             }
+        }
+        if constexpr (FP8) {
+            // the tile's 32 K and 32 V scales (KV head g), one 4-byte load per lane each:
+            // lane l reads those of tile key l & 31 (lanes 32..63 repeat lanes 0..31). A
+            // key outside the sequence (the raw tail past t, no slot) reads 0 and is masked.
+            const int kk = l & 31;
+            uint32_t bits;
+            const int64_t f = slot_first((j0 >> 2) + 4 * (kk >> 4) + ((kk >> 2) & 3), cur, bits);
+            const uint32_t os = f >= 0 ? (uint32_t)(f + (kk & 3)) * (HKV * 4) + g * 4 : OFF_NONE;
+            T.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksres, os, 0, 0));
+            T.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsres, os, 0, 0));
         }
         return T;
     };
@@ -1345,7 +1329,7 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
             for (int i = 0; i < 4; ++i) {
                 const bool ok = (T.valid >> (4 * u + i)) & 1u;
                 float zz = c4[i] * a.scale_log2;
-                if constexpr (FP8) zz *= T.ks[4 * u + i];
+                if constexpr (FP8) zz *= __shfl(T.ks, 16 * u + 4 * gr + i);
                 z[4 * u + i] = ok ? zz : -INFINITY;
                 mx = fmaxf(mx, z[4 * u + i]);
             }
@@ -1380,7 +1364,7 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            if constexpr (FP8) pv[e] = p[e] * T.vs[e];
+            if constexpr (FP8) pv[e] = p[e] * __shfl(T.vs, 16 * (e >> 2) + 4 * gr + (e & 3));
             else pv[e] = p[e];
         }
         u32x4 ph, pl;
