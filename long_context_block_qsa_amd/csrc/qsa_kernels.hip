@@ -1114,14 +1114,14 @@ struct KVTile {
 // tile key l & 31 (lane l; key 16h + 4gr + i of the tile is that of lane group gr's slot
 // of half h, token i), which the lanes that use them fetch by lane permutes.
 struct KVTile8 {
-    uint2 kt[8];
     uint2 vr[8];
     float ks, vs;
     uint32_t valid;
 };
-// LDS row pitch (bytes) of the per-wave FP8 K tile that turns the row-per-16-lanes loads
-// into the MFMA operand layout (16 bytes of padding spread the rows over the banks)
-template <bool FP8> constexpr int kt_pitch() { return FP8 ? HD + 16 : 2 * HD + 16; }
+// FP8 K tiles (4 KiB, in the same two per-wave buffers): load instruction e (0..3) writes
+// 1 KiB, lane i -> bytes e * 1024 + 16 i, i.e. tile key kk = 8e + (i >> 3) at row kk of
+// 128 bytes, piece i & 7. The lane loads piece (i & 7) ^ (kk & 7) of the key's row, so
+// that the operand reads (16 lanes reading 16 keys' same dims) spread over the banks.
 // bf16 K tiles: two per wave (the tile being processed and the next one, 8 KiB each).
 // Load instruction e (key e & 3 of the lane group's slot of tile half e >> 2) writes
 // 1 KiB: lane (gr, c) -> bytes e * 1024 + gr * 256 + c * 16 of the tile. The lane loads
@@ -1131,7 +1131,7 @@ constexpr int KT_TILE_BYTES = 32 * 2 * HD;
 // The two tiles of every wave live in two separate LDS arrays (kt0, kt1: one tile per
 // wave each), so that alias analysis can tell a read of one from a load in flight into
 // the other (the compiler then waits only for the loads the read depends on).
-static_assert(32 * (HD + 16) <= KT_TILE_BYTES, "the FP8 tile fits");
+static_assert(32 * HD <= KT_TILE_BYTES, "the FP8 tile fits");
 // the workgroup combine reuses kt0 for 4 x 12 head records of 128 floats + (m, l)
 static_assert(4 * GQ * (HD + 2) * 4 <= 4 * KT_TILE_BYTES, "combine records fit the K tiles");
 
@@ -1233,9 +1233,9 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
             T.valid |= bits << (4 * h);
             ob[h] = f >= 0 ? (uint32_t)f * TOK_BYTES + g * HD * (FP8 ? 1 : 2) : OFF_NONE;
         }
+        typedef __attribute__((address_space(3))) void lds_void;
         if constexpr (!FP8) {
             // K: 8 loads into the LDS tile (every K load of a tile precedes its V loads)
-            typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1243,18 +1243,27 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
                         kres, (lds_void *)((buf ? kt1 : kt0) + (4 * h + i) * 1024), 16,
                         ob[h] + i * TOK_BYTES + kswz[i], 0, 0, 0);
+        } else {
+            // K: 4 loads into the LDS tile. Instruction e, lane l: tile key 8e + (l >> 3),
+            // i.e. half e >> 1, lane group 2 (e & 1) + (l >> 5) (whose slot offset that
+            // group's lanes hold), token (l >> 3) & 3, piece (l & 7) ^ ((l >> 3) & 7)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t os = (uint32_t)__shfl((int)ob[e >> 1], 16 * (2 * (e & 1) + (l >> 5)));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    kres, (lds_void *)((buf ? kt1 : kt0) + e * 1024), 16,
+                    os + (uint32_t)((l >> 3) & 3) * TOK_BYTES + 16u * (uint32_t)((l & 7) ^ ((l >> 3) & 7)),
+                    0, 0, 0);
+            }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             if constexpr (FP8) {
                 const uint32_t o = ob[h] + 8 * col;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    T.kt[4 * h + i] = __builtin_bit_cast(
-                        uint2, __builtin_amdgcn_raw_buffer_load_b64(kres, o + i * TOK_BYTES, 0, 0));
+                for (int i = 0; i < 4; ++i)
                     T.vr[4 * h + i] = __builtin_bit_cast(
                         uint2, __builtin_amdgcn_raw_buffer_load_b64(vres, o + i * TOK_BYTES, 0, 0));
-                }
             } else {
                 const uint32_t o = ob[h] + 16 * col;
 #pragma unroll
@@ -1296,24 +1305,17 @@ __device__ __forceinline__ void attend_body(const AttnArgs &a, const RowView rv,
         float mx = -INFINITY;
         // the K rows reach the MFMA A layout (lane: key 16u + col, dims 32m + 8gr)
         // through this wave's LDS tile
-        constexpr int KP = kt_pitch<FP8>();
-        if constexpr (FP8) {
-            wave_lds_sync();   // the previous tile's reads are done
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<uint2 *>(kt0 + (16 * (e >> 2) + 4 * gr + (e & 3)) * KP + 8 * col) =
-                    T.kt[e];
-            wave_lds_sync();
-        } else {
-            wait_vmcnt<0>();
-        }
+        wait_vmcnt<0>();
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 if constexpr (FP8) {
-                    const uint8_t *src = kt0 + (16 * u + col) * KP + 32 * m + 8 * gr;
+                    // dims 32m + 8gr .. +7: piece 2m + (gr >> 1) of key 16u + col, at
+                    // column (2m + (gr >> 1)) ^ (col & 7), its half gr & 1
+                    const uint8_t *src = (buf ? kt1 : kt0) + (16 * u + col) * HD +
+                                         16 * ((2 * m + (gr >> 1)) ^ (col & 7)) + 8 * (gr & 1);
                     c4 = mfma_bf16_16x16x32(e4m3x8_to_bf16x8(*reinterpret_cast<const uint2 *>(src)),
                                             qb[m], c4);
                 } else {
@@ -1526,19 +1528,28 @@ __device__ __forceinline__ bool attend_item(const AttnArgs &a, int64_t &row, int
     return row < a.nrows;
 }
 
+// LDS of the prefill attention: two K tiles per wave (FP8 tiles are half the size), the
+// first array also large enough for the workgroup combine's 4 x 12 head records. With FP8
+// tiles a CU holds three workgroups (the registers allow three waves per SIMD).
+template <bool FP8> constexpr int att_tile_bytes() { return FP8 ? 32 * HD : KT_TILE_BYTES; }
+template <bool FP8> constexpr int att_kt0_bytes() {
+    return (ATT_NT / WAVE) * att_tile_bytes<FP8>() > 4 * GQ * (HD + 2) * 4
+               ? (ATT_NT / WAVE) * att_tile_bytes<FP8>() : 4 * GQ * (HD + 2) * 4;
+}
+
 template <bool FP8>
 __global__ void __launch_bounds__(ATT_NT)
 attend_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t kt0[(ATT_NT / WAVE) * KT_TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t kt1[(ATT_NT / WAVE) * KT_TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t kt0[att_kt0_bytes<FP8>()];
+    __shared__ __attribute__((aligned(16))) uint8_t kt1[(ATT_NT / WAVE) * att_tile_bytes<FP8>()];
     int64_t row;
     int g, sp;
     if (!attend_item(a, row, g, sp)) return;
     const RowView rv = tab_row(a.tab, a.batch, a.topk, row);
     if (a.skip_dense && nvis_of(rv.t) <= a.topk) return;   // uniform over the wave
     const int w = threadIdx.x / WAVE;
-    attend_body<FP8>(a, rv, row, g, sp, kt0 + w * KT_TILE_BYTES, kt1 + w * KT_TILE_BYTES, kt0,
-                     a.sel + row * a.topk);
+    attend_body<FP8>(a, rv, row, g, sp, kt0 + w * att_tile_bytes<FP8>(),
+                     kt1 + w * att_tile_bytes<FP8>(), kt0, a.sel + row * a.topk);
 }
 
 // LDS of a decode attention workgroup that merges its row's candidates.
