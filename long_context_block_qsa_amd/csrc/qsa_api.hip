@@ -332,6 +332,41 @@ qsa_status check_ws(const Plan &p, void *ws, size_t ws_bytes) {
 }
 
 qsa_status device_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_DEVICE; }
+qsa_status device_status(qsa_status s) { return s; }
+
+// A second stream per host thread and device (default priority, created on first use and
+// kept), with events reused by this thread's calls: prefill forwards attend the rows of
+// each selection pass on it while the caller's stream scores and selects the next passes.
+// Events are only recorded and waited on, so the fork and join also record into a graph
+// the caller's stream is capturing.
+struct SideStreams {
+    std::vector<hipStream_t> stream;            // per device
+    std::vector<std::vector<hipEvent_t>> ev;    // per device
+};
+thread_local SideStreams tl_side;
+
+qsa_status side_stream(size_t n_events, hipStream_t *side, hipEvent_t **ev) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return QSA_ERR_DEVICE;
+    if ((size_t)dev >= tl_side.stream.size()) {
+        tl_side.stream.resize(dev + 1, nullptr);
+        tl_side.ev.resize(dev + 1);
+    }
+    if (!tl_side.stream[dev] &&
+        hipStreamCreateWithFlags(&tl_side.stream[dev], hipStreamNonBlocking) != hipSuccess) {
+        tl_side.stream[dev] = nullptr;
+        return QSA_ERR_DEVICE;
+    }
+    std::vector<hipEvent_t> &e = tl_side.ev[dev];
+    while (e.size() < n_events) {
+        hipEvent_t x;
+        if (hipEventCreateWithFlags(&x, hipEventDisableTiming) != hipSuccess) return QSA_ERR_DEVICE;
+        e.push_back(x);
+    }
+    *side = tl_side.stream[dev];
+    *ev = e.data();
+    return QSA_OK;
+}
 
 #define QSA_TRY(expr)                                  \
     do {                                               \
@@ -352,9 +387,13 @@ bool dense_tile_path(const Plan &p, bool fp8) {
 }
 bool sel_by_dense_tiles(const Plan &p, bool fp8) { return dense_tile_path(p, fp8) && p.n_tiles == 0; }
 
+// after_pass (prefill, not null): called once the launch that selects pass i's rows has
+// been enqueued, with i.
+template <class AfterPass = std::nullptr_t>
 qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, const float *w,
                       const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel, void *ws,
-                      hipStream_t st, bool merge_in_attend = false, bool sel_by_dense = false) {
+                      hipStream_t st, bool merge_in_attend = false, bool sel_by_dense = false,
+                      AfterPass after_pass = nullptr) {
     SeqInfo *tab = ws_at<SeqInfo>(ws, p.off_tab);
     uint32_t *keys = ws_at<uint32_t>(ws, p.off_union);
     uint32_t *cand_key = nullptr;
@@ -396,6 +435,8 @@ qsa_status run_select(const Plan &p, const qsa_seqs *s, const qsa_bf16 *q_idx, c
             sc ? sc->chunk : 1, buf[(i + 1) % 2], se ? se->slot_lo : 0, sel,
             se ? se->row_lo : 0, se ? se->row_hi - se->row_lo : 0,
             (sc && sc->long_rows) || (se && se->long_rows), st));
+        if constexpr (!std::is_same<AfterPass, std::nullptr_t>::value)
+            if (i > 0) QSA_TRY(after_pass(i - 1));
     }
     (void)s;
     return QSA_OK;
@@ -449,11 +490,13 @@ qsa_status attend_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_b
     return run_attend(p, q, k, v, fp8, sel, out, lse, ws, hs);
 }
 
+// overlap: prefill calls of several selection passes may attend each pass's rows on the
+// thread's side stream (not for callers that cannot allocate: creating it allocates).
 qsa_status forward_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
                           const qsa_bf16 *k, const qsa_bf16 *v, const qsa::Fp8Kv *fp8,
                           const qsa_bf16 *q_idx, const float *w, const qsa_bf16 *k_idx,
                           qsa_bf16 *k_blk, int32_t *sel, float *out, float *lse, void *ws,
-                          size_t ws_bytes, void *stream) {
+                          size_t ws_bytes, void *stream, bool overlap = true) {
     Plan p;
     qsa_status st = make_plan(dims, seqs, true, &p);
     if (st != QSA_OK) return st;
@@ -485,6 +528,43 @@ qsa_status forward_common(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_
     // candidates themselves (no merge launch, no selection round trip through memory)
     const bool merge_in_attend = p.use_dec && p.local_ch > 0 && p.merge_launch;
     const bool sel_by_dense = sel_by_dense_tiles(p, fp8 != nullptr);
+    // prefill in several selection passes: the rows of pass i are attended on the side
+    // stream as soon as the launch that selects them has run, while the caller's stream
+    // scores and selects the later passes (the attention reads only the selections of its
+    // own rows; the key buffers the later launches reuse are the selection's alone). Only
+    // where it pays: the FP8 attention (bound by its instruction issue as much as by its
+    // gathers) and prefills with long-row passes (rows of more than SEL_LONG_KEYS blocks);
+    // the bf16 attention of shorter rows is bound by the L2 requests of its gathers, and
+    // sharing the L2 with the selection passes made the whole step slower.
+    const bool long_passes = std::any_of(p.passes.begin(), p.passes.end(),
+                                         [](const Pass &ps) { return ps.long_rows; });
+    if (overlap && !p.use_dec && p.nsplit == 1 && p.passes.size() > 1 && !sel_by_dense &&
+        (fp8 != nullptr || long_passes)) {
+        hipStream_t side;
+        hipEvent_t *ev;
+        const size_t np = p.passes.size();
+        if ((st = side_stream(np + 1, &side, &ev)) != QSA_OK) return st;
+        const bool dense = dense_tile_path(p, fp8 != nullptr);
+        auto after_pass = [&](size_t i) -> qsa_status {
+            const Pass &ps = p.passes[i];
+            QSA_TRY(hipEventRecord(ev[i], hs));
+            QSA_TRY(hipStreamWaitEvent(side, ev[i], 0));
+            QSA_TRY(qsa::launch_attend(tab, nullptr, p.batch, p.topk, p.scale, q, k, v, fp8,
+                                       sel_use, out, lse, ws_at<float>(ws, p.off_part), 1,
+                                       ps.row_hi - ps.row_lo, nullptr, dense, side, ps.row_lo));
+            return QSA_OK;
+        };
+        st = run_select(p, seqs, q_idx, w, nullptr, k_blk, sel_use, ws, hs, false, false,
+                        after_pass);
+        // the dense-regime rows on the caller's stream meanwhile; then it waits for the side
+        // stream's attention (also after an error above, so nothing is left unjoined)
+        if (st == QSA_OK && dense)
+            st = device_status(qsa::launch_attend_dense(tab, p.batch, p.topk, p.scale, q, k, v,
+                                                        out, lse, nullptr, p.n_dense_tiles, hs));
+        const qsa_status jst = device_status(hipEventRecord(ev[np], side));
+        const qsa_status wst = jst == QSA_OK ? device_status(hipStreamWaitEvent(hs, ev[np], 0)) : jst;
+        return st != QSA_OK ? st : wst;
+    }
     if ((st = run_select(p, seqs, q_idx, w, fused ? k_idx : nullptr, k_blk, sel_use, ws, hs,
                          merge_in_attend, sel_by_dense)) != QSA_OK)
         return st;
@@ -680,7 +760,7 @@ qsa_status qsa_forward_noalloc(const qsa_dims *dims, const qsa_seqs *seqs, const
     void *ws = nullptr;
     if ((st = noalloc_scratch((hipStream_t)stream, &ws)) != QSA_OK) return st;
     return forward_common(dims, seqs, q, k, v, nullptr, q_idx, w, k_idx, k_blk, sel, out, lse,
-                          ws, (size_t)QSA_NOALLOC_SCRATCH_BYTES, stream);
+                          ws, (size_t)QSA_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 qsa_status qsa_quantize_kv(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *k,

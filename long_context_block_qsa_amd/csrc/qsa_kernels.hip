@@ -1091,6 +1091,7 @@ struct AttnArgs {
     float *part;
     int nsplit;
     int64_t nrows;
+    int64_t row0;     // first row of the launch (rows row0 .. row0 + nrows - 1)
     int skip_dense;   // rows with at most topk visible blocks are left to the dense kernel
     int head_major;   // nsplit 1: waves take every row of KV head 0, then of head 1
     int wg_combine;   // nsplit % 4 == 0: a workgroup's 4 split waves merge into 1 partial
@@ -1517,15 +1518,16 @@ __device__ __forceinline__ bool attend_item(const AttnArgs &a, int64_t &row, int
         (int)((int64_t)blockIdx.x * (ATT_NT / WAVE) + threadIdx.x / WAVE));
     if (a.head_major) {
         g = (int)(item / a.nrows);
-        row = item - (int64_t)g * a.nrows;
+        row = a.row0 + (item - (int64_t)g * a.nrows);
         sp = 0;
         return g < HKV;
     }
-    row = item / (HKV * a.nsplit);
+    const int64_t lr = item / (HKV * a.nsplit);
     const int rem = (int)(item % (HKV * a.nsplit));
     g = rem / a.nsplit;
     sp = rem % a.nsplit;
-    return row < a.nrows;
+    row = a.row0 + lr;
+    return lr < a.nrows;
 }
 
 // LDS of the prefill attention: two K tiles per wave (FP8 tiles are half the size), the
@@ -1855,9 +1857,11 @@ hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, i
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
                          float *part, int nsplit, int64_t n_rows, const AttnMerge *merge,
-                         bool skip_dense, hipStream_t st) {
+                         bool skip_dense, hipStream_t st, int64_t row0) {
     if (n_rows <= 0) return hipSuccess;
+    if (row0 != 0 && (nsplit != 1 || d)) return hipErrorInvalidValue;   // one split per row only
     AttnArgs a = {};
+    a.row0 = row0;
     a.merge = merge != nullptr && d != nullptr;
     if (a.merge) {
         a.loc.topk = topk; a.loc.q_idx = merge->q_idx; a.loc.w = merge->w; a.loc.k_idx = nullptr;

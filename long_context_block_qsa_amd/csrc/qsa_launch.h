@@ -79,12 +79,13 @@ struct AttnMerge {
     int32_t *sel;   // where the merged selections are written out (the one attend reads)
 };
 // skip_dense (prefill, nsplit 1): rows with at most topk visible blocks are left to
-// launch_attend_dense.
+// launch_attend_dense. row0: the launch attends rows row0 .. row0 + n_rows - 1 (nonzero
+// only for prefill launches with one split per row).
 hipError_t launch_attend(const SeqInfo *tab, const DecodeTables *d, int batch, int topk,
                          float scale, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const Fp8Kv *fp8, const int32_t *sel, float *out, float *lse,
                          float *part, int nsplit, int64_t n_rows, const AttnMerge *merge,
-                         bool skip_dense, hipStream_t st);
+                         bool skip_dense, hipStream_t st, int64_t row0 = 0);
 // Causal attention of the rows in the dense regime (every visible block kept), in tiles
 // of DN_ROWS rows sharing their keys through LDS (qsa_dense.hip). sel not null: the
 // kernel also writes these rows' selections (calls without scored rows).
