@@ -126,3 +126,35 @@ def test_fp8_forward_equals_select_then_attend():
     assert np.array_equal(fp.select(), sel)
     out2, lse2 = fp.attend_fp8()
     assert np.array_equal(out2, out) and np.array_equal(lse2, lse)
+
+
+def test_fp8_prefill_second_stream_equals_one_stream_and_graph():
+    """The ragged FP8 prefill forward attends each selection pass on a second stream while
+    the later passes are scored and selected: its outputs equal qsa_select followed by
+    qsa_attend_fp8 on one stream, bit for bit, and a HIP graph of the forward (the fork
+    and join recorded into it, captured after one eager call has created the second
+    stream) replays to the same result, with eager library work between the replays."""
+    _banner("fp8: ragged prefill, second stream vs one stream vs graph")
+    p = gen.workload_problem("prefill_ragged_65535_40001_8190_3")
+    fp = Fp8Problem(p)
+    sel, out, lse = fp.forward_fp8()
+    fp.sel.fill_(-9)
+    assert np.array_equal(fp.select(), sel)
+    out2, lse2 = fp.attend_fp8()
+    assert np.array_equal(out2, out) and np.array_equal(lse2, lse)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qsa.forward_fp8(fp.seqs, fp.q, fp.k8, fp.v8, fp.ks, fp.vs, fp.q_idx, fp.w, fp.k_idx,
+                        fp.k_blk, fp.sel, fp.out, fp.lse, fp.ws, fp.topk)
+    for i in range(3):
+        fp.sel.fill_(-7)
+        fp.out.fill_(float("nan"))
+        fp.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(fp.sel.cpu().numpy(), sel), f"replay {i}: selections differ"
+        assert np.array_equal(fp.out.cpu().numpy(), out), f"replay {i}: outputs differ"
+        assert np.array_equal(fp.lse.cpu().numpy(), lse), f"replay {i}: lse differs"
+        s2, o2, l2 = fp.forward_fp8()   # eager work between the replays
+        assert np.array_equal(o2, out) and np.array_equal(s2, sel)
