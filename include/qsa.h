@@ -169,7 +169,15 @@ qsa_status qsa_attend(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16
  * built by qsa_compress or by earlier steps). A prefill therefore compresses every
  * block, a decode step only the block its token completes. If k_idx is NULL, k_blk
  * must already be complete. If sel is NULL the selection is kept in the workspace.
- * lse may be NULL. */
+ * lse may be NULL.
+ * Streams: the work is ordered on `stream`: it starts after the work enqueued there
+ * before the call, and work enqueued there after the call starts after it. A prefill
+ * whose selection runs in several passes may attend each pass's rows on a second
+ * stream of the library's (one per host thread and device, default priority, created
+ * by the first such call and kept until the process ends), forked from and joined back
+ * into `stream` by events; both are recorded into a graph that `stream` captures, so
+ * capture such a call after one eager call on the same thread has created that
+ * stream. */
 qsa_status qsa_forward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
                        const qsa_bf16 *k, const qsa_bf16 *v, const qsa_bf16 *q_idx,
                        const float *w, const qsa_bf16 *k_idx, qsa_bf16 *k_blk, int32_t *sel,
@@ -184,8 +192,8 @@ qsa_status qsa_forward(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf1
  * needs its selection when sel is NULL plus its score keys). Every call on a GPU
  * shares that GPU's array: calls that overlap in time on one GPU (other streams, other
  * host threads) race and must be serialised by the caller. The array's control block
- * is zero before the first call and every call leaves it zero. Other arguments and
- * results as qsa_forward. */
+ * is zero before the first call and every call leaves it zero. All of its work runs on
+ * `stream` (no second stream). Other arguments and results as qsa_forward. */
 #define QSA_NOALLOC_SCRATCH_BYTES (64u << 20)
 qsa_status qsa_forward_noalloc(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
                                const qsa_bf16 *k, const qsa_bf16 *v, const qsa_bf16 *q_idx,
@@ -214,7 +222,7 @@ qsa_status qsa_attend_fp8(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_
                           const float *v_scale, const int32_t *sel, float *out, float *lse,
                           void *ws, size_t ws_bytes, void *stream);
 
-/* qsa_forward over the FP8 cache (compress and selection as in qsa_forward). */
+/* qsa_forward over the FP8 cache (compress, selection and streams as in qsa_forward). */
 qsa_status qsa_forward_fp8(const qsa_dims *dims, const qsa_seqs *seqs, const qsa_bf16 *q,
                            const uint8_t *k8, const uint8_t *v8, const float *k_scale,
                            const float *v_scale, const qsa_bf16 *q_idx, const float *w,
