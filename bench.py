@@ -584,6 +584,7 @@ def run_decode_32k(args, torch, qsa, gen):
             "query_tokens_per_s": round(1 / (st["median_ms"] / 1e3), 1),
             "algorithmic_bytes": nbytes,
             "achieved_gbs": round(nbytes / (st["median_ms"] / 1e3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (st["median_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_ms": {k2: round(v2, 5) for k2, v2 in tr.total_ms().items()}}
 
 
