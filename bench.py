@@ -636,8 +636,10 @@ def run_prefill_backward(args, torch, qsa, gen, p, seqs, q, k, v, sel, out, lse,
     km = tr.total_ms()   # the dK/dV kernel runs once per row window
     # five contractions per attended (query head, key): S and dP recomputed, dQ, dK, dV
     flop = pairs * HQ * D * 2 * 5
-    # rows x kept blocks per KV head (the dK/dV kernel's row visits)
-    return {"ms_per_step": round(ms, 3), "step_ms": st,
+    note = {"kernel_ms_note": "dQ ran on a second stream, concurrently with the dK/dV launches: "
+                              "kernel times overlap"} if overlapped(km, st) else {}
+    # dkv_row_gbs: rows x kept blocks per KV head (the dK/dV kernel's row visits)
+    return {**note, "ms_per_step": round(ms, 3), "step_ms": st,
             "query_tokens_per_s": round(seqs.n_q / (ms / 1e3), 1),
             "kernel_ms": {k2: round(v2, 4) for k2, v2 in km.items()},
             "tflops": round(flop / (ms / 1e3) / 1e12, 2),

@@ -249,7 +249,10 @@ qsa_status qsa_forward_fp8(const qsa_dims *dims, const qsa_seqs *seqs, const qsa
  * every key (0 where no row attends it). Results are deterministic: no gradient is
  * accumulated with atomics. The workspace (its own size, below) starts with the same
  * 4 KiB control block as the forward's, which this call does not touch, so one
- * allocation of the larger size serves both. All pointers 16-byte aligned. */
+ * allocation of the larger size serves both. All pointers 16-byte aligned.
+ * Streams: ordered on `stream` as qsa_forward; dq is computed on the library's second
+ * stream of this host thread and device (see qsa_forward), forked from and joined back
+ * into `stream` by events, while dk and dv are computed on `stream`. */
 
 /* Bytes of workspace qsa_attend_backward needs (about 4 * Tq * (topk + 1) for the
  * block -> rows lists plus small tables). Host-only. QSA_ERR_UNSUPPORTED when

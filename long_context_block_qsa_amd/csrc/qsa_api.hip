@@ -835,10 +835,14 @@ qsa_status qsa_attend_backward(const qsa_dims *dims, const qsa_seqs *seqs, const
     b.tot = ws_at<int32_t>(ws, bp.off_tot);
     b.mat = ws_at<int32_t>(ws, bp.off_mat);
     b.list = ws_at<int32_t>(ws, bp.off_list);
+    // dQ on the thread's side stream, concurrently with dK/dV on the caller's
+    hipStream_t side;
+    hipEvent_t *ev;
+    if ((st = side_stream(2, &side, &ev)) != QSA_OK) return st;
     QSA_TRY(qsa::launch_backward(seqs->cu_q_dev, seqs->cu_k_dev, seqs->cu_q_host,
                                  seqs->cu_k_host, p.batch, p.topk, p.scale, p.tq,
                                  bp.n_chunks, bp.nkb_total, q, k, v, sel, out, lse, dout, dq,
-                                 dk, dv, b, (hipStream_t)stream));
+                                 dk, dv, b, (hipStream_t)stream, side, ev[0], ev[1]));
     return QSA_OK;
 }
 

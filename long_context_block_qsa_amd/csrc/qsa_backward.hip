@@ -666,7 +666,8 @@ hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, const int32
                            const uint16_t *q, const uint16_t *k, const uint16_t *v,
                            const int32_t *sel, const float *out, const float *lse,
                            const uint16_t *dout, float *dq, float *dk, float *dv,
-                           const BwdBuffers &bb, hipStream_t st) {
+                           const BwdBuffers &bb, hipStream_t st, hipStream_t side,
+                           hipEvent_t fork, hipEvent_t join) {
     hipError_t e;
     trace_before(6, st);
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(BPREP_NT), 0, st, cu_q, cu_k, batch, bb.seq);
@@ -701,6 +702,15 @@ hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, const int32
                            (int32_t)(n_rows * (topk + 1)));
         if ((e = trace_after(st, hipGetLastError())) != hipSuccess) return e;
     }
+    // dQ (row-major, writes dq only) and dK/dV (key-major, writes dk and dv only) read the
+    // same inputs and the finished index: with a side stream they run concurrently
+    hipStream_t sq = st;
+    if (side && n_rows > 0 && nkb_total > 0) {
+        if ((e = hipEventRecord(fork, st)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return e;
+        sq = side;
+    }
+    hipError_t edq = hipSuccess;
     if (n_rows > 0) {
         DqArgs a;
         a.tab = bb.seq; a.batch = batch; a.topk = topk;
@@ -708,10 +718,13 @@ hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, const int32
         a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = bb.delta;
         a.sel = sel; a.nsel = bb.nsel; a.dq = dq; a.nrows = n_rows;
         const int64_t wg = (n_rows * HKV + BDQ_NT / WAVE - 1) / (BDQ_NT / WAVE);
-        trace_before(12, st);
-        hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)wg), dim3(BDQ_NT), 0, st, a);
-        if ((e = trace_after(st, hipGetLastError())) != hipSuccess) return e;
+        trace_before(12, sq);
+        hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)wg), dim3(BDQ_NT), 0, sq, a);
+        edq = trace_after(sq, hipGetLastError());
     }
+    // the dK/dV launches; then st waits for the side stream (also after an error)
+    auto run_dkv = [&]() -> hipError_t {
+    if (edq != hipSuccess) return edq;
     if (nkb_total > 0) {
         DkvArgs a;
         a.tab = bb.seq; a.batch = batch;
@@ -741,6 +754,14 @@ hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, const int32
         }
     }
     return hipSuccess;
+    };
+    const hipError_t ekv = run_dkv();
+    if (sq != st) {
+        const hipError_t ej = hipEventRecord(join, sq);
+        const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(st, join, 0) : ej;
+        if (ekv == hipSuccess && ew != hipSuccess) return ew;
+    }
+    return ekv;
 }
 
 }  // namespace qsa

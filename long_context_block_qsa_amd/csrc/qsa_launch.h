@@ -104,13 +104,17 @@ struct BwdBuffers {
     int32_t *mat;     // count matrices of all sequences
     int32_t *list;    // block -> rows lists
 };
+// side (not null): dQ runs on it, forked from st after the block -> rows index is built and
+// joined back into st by the two events, while st runs the dK/dV launches.
 hipError_t launch_backward(const int32_t *cu_q, const int32_t *cu_k, const int32_t *cu_q_host,
                            const int32_t *cu_k_host, int batch, int topk,
                            float scale, int64_t n_rows, int64_t n_chunks, int64_t nkb_total,
                            const uint16_t *q, const uint16_t *k, const uint16_t *v,
                            const int32_t *sel, const float *out, const float *lse,
                            const uint16_t *dout, float *dq, float *dk, float *dv,
-                           const BwdBuffers &b, hipStream_t st);
+                           const BwdBuffers &b, hipStream_t st,
+                           hipStream_t side = nullptr, hipEvent_t fork = nullptr,
+                           hipEvent_t join = nullptr);
 // Clears n 32-bit words with a kernel.
 hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t st);
 hipError_t launch_quantize_kv(const uint16_t *k, const uint16_t *v, uint8_t *k8, uint8_t *v8,
