@@ -42,7 +42,7 @@ HOST_THREADS = 16   # host threads for the oracle baseline: one GPU's share of t
 # reads on a plain 512 MiB copy) from rocprofv3 --pmc runs of this benchmark, with the
 # fingerprint of the kernel sources they were taken on; reported only while it matches.
 TRAFFIC = {
-    "score": {"bytes": 134_762_000, "sources_sha256": "a7aa4e9cb99c66fbb36414c34de974950d53d08e35939aad03d58b78ca2892f8"},
+    "score": {"bytes": 134_762_000, "sources_sha256": "de17aaecc9d0f5de9b401caaa2257983ffe1a8b2ef34d6ed03e08cf069885dc6"},
 }
 
 
